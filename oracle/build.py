@@ -1,0 +1,24 @@
+"""Build the CPU oracle shared library (test infrastructure only).
+
+Plain gcc, no fast-math: the oracle relies on IEEE round-to-nearest-even and x87 long double.
+"""
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "hq_oracle.c")
+LIB = os.path.join(HERE, "libhq_oracle.so")
+
+
+def build(verbose=False):
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+           "-fno-fast-math", SRC, "-o", LIB + ".tmp", "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))
