@@ -129,15 +129,24 @@ int hqo_rotate(const double *V, int64_t rows, int64_t cols, int rot, int k, doub
           R[i * cols + b * k + j] = (double)acc;
         }
   } else if (rot == HQO_ROT_LEFT) {
-#pragma omp parallel for schedule(static)
-    for (int64_t b = 0; b < rows / k; ++b)
-      for (int i = 0; i < k; ++i)
-        for (int64_t j = 0; j < cols; ++j) {
-          long double acc = 0.0L;
-          for (int t = 0; t < k; ++t)
-            acc += (long double)H[i * k + t] * (long double)V[(b * k + t) * cols + j];
-          R[(b * k + i) * cols + j] = (double)acc;
+    /* Same sums as R[b*k+i][j] = sum_t h(i,t) V[b*k+t][j], each taken over t in ascending
+     * order; the j loop runs innermost over a row accumulator so rows are read contiguously. */
+#pragma omp parallel
+    {
+      long double *acc = (long double *)malloc(sizeof(long double) * (size_t)(cols > 0 ? cols : 1));
+#pragma omp for schedule(static) collapse(2)
+      for (int64_t b = 0; b < rows / k; ++b)
+        for (int i = 0; i < k; ++i) {
+          for (int64_t j = 0; j < cols; ++j) acc[j] = 0.0L;
+          for (int t = 0; t < k; ++t) {
+            const long double h = (long double)H[i * k + t];
+            const double *vrow = V + (b * k + t) * cols;
+            for (int64_t j = 0; j < cols; ++j) acc[j] += h * (long double)vrow[j];
+          }
+          for (int64_t j = 0; j < cols; ++j) R[(b * k + i) * cols + j] = (double)acc[j];
         }
+      free(acc);
+    }
   } else if (rot == HQO_ROT_BOTH) {
     double *T = (double *)malloc(sizeof(double) * (size_t)(rows * cols));
     if (!T) { free(H); return -1; }
@@ -231,14 +240,18 @@ int hqo_rotate_i64(const int64_t *T, int64_t rows, int64_t cols, int rot, int k,
           R[i * cols + b * k + j] = acc;
         }
   } else if (rot == HQO_ROT_LEFT) {
-#pragma omp parallel for schedule(static)
+    /* R[b*k+i][j] = sum_t h(i,t) T[b*k+t][j] (exact integers; rows read contiguously) */
+#pragma omp parallel for schedule(static) collapse(2)
     for (int64_t b = 0; b < rows / k; ++b)
-      for (int i = 0; i < k; ++i)
-        for (int64_t j = 0; j < cols; ++j) {
-          int64_t acc = 0;
-          for (int t = 0; t < k; ++t) acc += (int64_t)H[i * k + t] * T[(b * k + t) * cols + j];
-          R[(b * k + i) * cols + j] = acc;
+      for (int i = 0; i < k; ++i) {
+        int64_t *out = R + (b * k + i) * cols;
+        for (int64_t j = 0; j < cols; ++j) out[j] = 0;
+        for (int t = 0; t < k; ++t) {
+          const int64_t h = (int64_t)H[i * k + t];
+          const int64_t *trow = T + (b * k + t) * cols;
+          for (int64_t j = 0; j < cols; ++j) out[j] += h * trow[j];
         }
+      }
   } else if (rot == HQO_ROT_BOTH) {
     int64_t *U = (int64_t *)malloc(sizeof(int64_t) * (size_t)(rows * cols));
     if (!U) { free(H); return -1; }
