@@ -1,0 +1,146 @@
+"""Thin ctypes binding of libhq (include/hq.h): the same entry-point names, argument
+marshalling only. Every step of the computation runs in the HIP kernels behind the C ABI;
+torch is used by the helpers below only to allocate device memory and to name streams.
+
+Loading fails loudly when the library is missing and cannot be built: there is no fallback.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhq.so")
+
+# enums of include/hq.h
+HQ_OK = 0
+STATUS_NAMES = {0: "HQ_OK", 1: "HQ_ERR_NULL", 2: "HQ_ERR_SHAPE", 3: "HQ_ERR_K", 4: "HQ_ERR_BITS",
+                5: "HQ_ERR_DTYPE", 6: "HQ_ERR_MODE", 7: "HQ_ERR_WORKSPACE", 8: "HQ_ERR_MISMATCH",
+                9: "HQ_ERR_DEVICE", 10: "HQ_ERR_LAUNCH", 11: "HQ_ERR_ALIGN"}
+HQ_F32, HQ_F16, HQ_BF16 = 0, 1, 2
+HQ_ROT_NONE, HQ_ROT_RIGHT, HQ_ROT_LEFT, HQ_ROT_BOTH = 0, 1, 2, 3
+HQ_SCALE_ABSMAX, HQ_SCALE_STEP = 0, 1
+HQ_VARIANT_HALO0, HQ_VARIANT_HQ, HQ_VARIANT_HALO2 = 0, 1, 2
+
+EXPORTS = ["hq_abi_version", "hq_status_string", "hq_code_pitch", "hq_workspace_bytes",
+           "hq_rotate_quantize", "hq_linear_fwd", "hq_linear_bwd_input", "hq_linear_bwd_weight",
+           "hq_fwht", "hq_gemm_i8_i32"]
+
+
+class hq_config(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_int32), ("bits", ctypes.c_int32),
+                ("scale_mode", ctypes.c_int32), ("variant", ctypes.c_int32)]
+
+
+class hq_qtensor(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("codes_t", ctypes.c_void_p),
+                ("scale", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("ld", ctypes.c_int64), ("ld_t", ctypes.c_int64), ("k", ctypes.c_int32),
+                ("bits", ctypes.c_int32), ("rot", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class HQError(RuntimeError):
+    def __init__(self, status, where=""):
+        self.status = status
+        super().__init__("%s: %s (%s)" % (where, STATUS_NAMES.get(status, status),
+                                          hq_status_string(status)))
+
+
+_lib = None
+
+
+def load(build_if_missing=True):
+    """Load libhq.so; build it first only when no built library exists."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        if not build_if_missing:
+            raise RuntimeError("libhq.so is not built (run hadamard_rotated_precision_amd/build.py)")
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(LIB_PATH)
+    i32, i64, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    P = ctypes.POINTER
+    lib.hq_abi_version.restype = i32
+    lib.hq_abi_version.argtypes = []
+    lib.hq_status_string.restype = ctypes.c_char_p
+    lib.hq_status_string.argtypes = [i32]
+    lib.hq_code_pitch.restype = i64
+    lib.hq_code_pitch.argtypes = [i64]
+    lib.hq_workspace_bytes.restype = sz
+    lib.hq_workspace_bytes.argtypes = [P(hq_config), i64, i64, i64]
+    lib.hq_rotate_quantize.restype = i32
+    lib.hq_rotate_quantize.argtypes = [vp, i32, i64, i64, i32, P(hq_config), vp, P(hq_qtensor),
+                                       vp, sz, vp]
+    lib.hq_linear_fwd.restype = i32
+    lib.hq_linear_fwd.argtypes = [vp, vp, i32, i64, i64, i64, P(hq_config), vp, vp, vp, vp, i32,
+                                  P(hq_qtensor), P(hq_qtensor), P(hq_qtensor), vp, sz, vp]
+    lib.hq_linear_bwd_input.restype = i32
+    lib.hq_linear_bwd_input.argtypes = [vp, i32, i64, i64, i64, P(hq_config), vp, P(hq_qtensor),
+                                        vp, i32, P(hq_qtensor), vp, sz, vp]
+    lib.hq_linear_bwd_weight.restype = i32
+    lib.hq_linear_bwd_weight.argtypes = [P(hq_qtensor), P(hq_qtensor), i64, i64, i64,
+                                         P(hq_config), vp, i32, vp, sz, vp]
+    lib.hq_fwht.restype = i32
+    lib.hq_fwht.argtypes = [vp, i32, vp, i32, i64, i64, i32, i32, vp]
+    lib.hq_gemm_i8_i32.restype = i32
+    lib.hq_gemm_i8_i32.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, vp]
+    _lib = lib
+    return lib
+
+
+def _ref(s):
+    return None if s is None else ctypes.byref(s)
+
+
+# ------------------------------------------------ entry points, same names as the C ABI
+def hq_abi_version():
+    return load().hq_abi_version()
+
+
+def hq_status_string(status):
+    return load().hq_status_string(status).decode()
+
+
+def hq_code_pitch(cols):
+    return load().hq_code_pitch(cols)
+
+
+def hq_workspace_bytes(cfg, N, C, D):
+    return load().hq_workspace_bytes(ctypes.byref(cfg), N, C, D)
+
+
+def hq_rotate_quantize(src, src_dtype, rows, cols, rot, cfg, step, out, ws, ws_bytes, stream):
+    return load().hq_rotate_quantize(src, src_dtype, rows, cols, rot, _ref(cfg), step, _ref(out),
+                                     ws, ws_bytes, stream)
+
+
+def hq_linear_fwd(x, w, in_dtype, N, C, D, cfg, step_x, step_w, step_xt, y, y_dtype, save_x,
+                  save_xt, save_w, ws, ws_bytes, stream):
+    return load().hq_linear_fwd(x, w, in_dtype, N, C, D, _ref(cfg), step_x, step_w, step_xt, y,
+                                y_dtype, _ref(save_x), _ref(save_xt), _ref(save_w), ws,
+                                ws_bytes, stream)
+
+
+def hq_linear_bwd_input(dy, dy_dtype, N, C, D, cfg, step_g, saved_w, dx, dx_dtype, save_g, ws,
+                        ws_bytes, stream):
+    return load().hq_linear_bwd_input(dy, dy_dtype, N, C, D, _ref(cfg), step_g, _ref(saved_w),
+                                      dx, dx_dtype, _ref(save_g), ws, ws_bytes, stream)
+
+
+def hq_linear_bwd_weight(saved_g, saved_x, N, C, D, cfg, dw, dw_dtype, ws, ws_bytes, stream):
+    return load().hq_linear_bwd_weight(_ref(saved_g), _ref(saved_x), N, C, D, _ref(cfg), dw,
+                                       dw_dtype, ws, ws_bytes, stream)
+
+
+def hq_fwht(src, src_dtype, dst, dst_dtype, rows, cols, rot, k, stream):
+    return load().hq_fwht(src, src_dtype, dst, dst_dtype, rows, cols, rot, k, stream)
+
+
+def hq_gemm_i8_i32(a, lda, b_t, ldb, c, M, N, K, stream):
+    return load().hq_gemm_i8_i32(a, lda, b_t, ldb, c, M, N, K, stream)
+
+
+def check(status, where=""):
+    if status != HQ_OK:
+        raise HQError(status, where)
+    return status

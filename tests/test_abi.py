@@ -1,0 +1,227 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol include/hq.h
+declares, and rejects every invalid argument before any HIP call.
+
+The pointers used here are fake addresses; every call below fails validation, which runs
+before the first HIP call, so nothing is ever dereferenced or launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from hadamard_rotated_precision_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000      # 16-byte aligned fake device address
+FAKE_MIS = 0x10004  # misaligned
+
+
+def declared_symbols():
+    with open(os.path.join(ROOT, "include", "hq.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(hq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = B.load()
+    syms = declared_symbols()
+    assert set(syms) == set(B.EXPORTS), syms
+    for s in syms:
+        assert hasattr(lib, s), s
+
+
+def test_version_status_pitch():
+    assert B.hq_abi_version() == 1
+    for code in range(12):
+        assert isinstance(B.hq_status_string(code), str) and B.hq_status_string(code)
+    assert B.hq_status_string(999) == "unknown status"
+    assert B.hq_code_pitch(0) == 0 and B.hq_code_pitch(1) == 16 and B.hq_code_pitch(32) == 32
+    assert B.hq_code_pitch(33) == 48
+
+
+def cfg(k=32, bits=8, mode=B.HQ_SCALE_ABSMAX, variant=B.HQ_VARIANT_HALO2):
+    c = B.hq_config()
+    c.k, c.bits, c.scale_mode, c.variant = k, bits, mode, variant
+    return c
+
+
+def qt(rows, cols, codes=FAKE, codes_t=FAKE, scale=FAKE, ld=None, ld_t=None, k=32, bits=8,
+       rot=B.HQ_ROT_RIGHT):
+    q = B.hq_qtensor()
+    q.codes, q.codes_t, q.scale = codes, codes_t, scale
+    q.rows, q.cols = rows, cols
+    q.ld = B.hq_code_pitch(cols) if ld is None else ld
+    q.ld_t = B.hq_code_pitch(rows) if ld_t is None else ld_t
+    q.k, q.bits, q.rot = k, bits, rot
+    return q
+
+
+def test_workspace_bytes():
+    assert B.hq_workspace_bytes(cfg(), 64, 64, 64) > 64 * 64 * 4
+    assert B.hq_workspace_bytes(cfg(k=3), 64, 64, 64) == 0
+    assert B.hq_workspace_bytes(cfg(), -1, 64, 64) == 0
+    a = B.hq_workspace_bytes(cfg(), 2048, 4096, 4096)
+    assert a >= 4096 * 4096 * 4
+
+
+def rq(**kw):
+    args = dict(src=FAKE, src_dtype=B.HQ_BF16, rows=64, cols=64, rot=B.HQ_ROT_RIGHT, cfg=cfg(),
+                step=None, out=qt(64, 64), ws=FAKE, ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return B.hq_rotate_quantize(**args)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(cfg=cfg(k=3)), "HQ_ERR_K"),
+    (dict(cfg=cfg(k=512)), "HQ_ERR_K"),
+    (dict(cfg=cfg(k=0)), "HQ_ERR_K"),
+    (dict(cfg=cfg(bits=5)), "HQ_ERR_BITS"),
+    (dict(cfg=cfg(mode=7)), "HQ_ERR_MODE"),
+    (dict(cfg=cfg(variant=3)), "HQ_ERR_MODE"),
+    (dict(src_dtype=9), "HQ_ERR_DTYPE"),
+    (dict(rot=4), "HQ_ERR_MODE"),
+    (dict(rows=-1), "HQ_ERR_SHAPE"),
+    (dict(cols=48), "HQ_ERR_SHAPE"),                       # 48 % 32 for a RIGHT rotation
+    (dict(rot=B.HQ_ROT_LEFT, rows=40), "HQ_ERR_SHAPE"),    # token axis not divisible by k
+    (dict(rot=B.HQ_ROT_BOTH, rows=40), "HQ_ERR_SHAPE"),
+    (dict(cfg=cfg(mode=B.HQ_SCALE_STEP)), "HQ_ERR_NULL"),  # STEP without a step
+    (dict(out=None), "HQ_ERR_NULL"),
+    (dict(out=qt(64, 64, scale=None)), "HQ_ERR_NULL"),
+    (dict(out=qt(64, 64, codes=None, codes_t=None)), "HQ_ERR_NULL"),
+    (dict(src=None), "HQ_ERR_NULL"),
+    (dict(out=qt(64, 64, codes=FAKE_MIS)), "HQ_ERR_ALIGN"),
+    (dict(out=qt(64, 64, ld=72)), "HQ_ERR_ALIGN"),
+    (dict(out=qt(64, 64, ld=48)), "HQ_ERR_SHAPE"),         # pitch shorter than cols
+    (dict(out=qt(64, 64, codes_t=None), rot=B.HQ_ROT_BOTH), "HQ_ERR_NULL"),
+    (dict(ws=None), "HQ_ERR_WORKSPACE"),
+    (dict(ws_bytes=100), "HQ_ERR_WORKSPACE"),
+    (dict(ws=FAKE_MIS), "HQ_ERR_ALIGN"),
+])
+def test_rotate_quantize_validation(kw, expect):
+    assert B.STATUS_NAMES[rq(**kw)] == expect
+
+
+def fwd(**kw):
+    N, C, D = kw.pop("N", 64), kw.pop("C", 64), kw.pop("D", 96)
+    args = dict(x=FAKE, w=FAKE, in_dtype=B.HQ_BF16, N=N, C=C, D=D, cfg=cfg(), step_x=None,
+                step_w=None, step_xt=None, y=FAKE, y_dtype=B.HQ_BF16, save_x=qt(N, C),
+                save_xt=qt(N, C, rot=B.HQ_ROT_BOTH), save_w=qt(D, C), ws=FAKE,
+                ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return B.hq_linear_fwd(**args)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(C=48), "HQ_ERR_SHAPE"),
+    (dict(N=48), "HQ_ERR_SHAPE"),            # HALO2 needs N % k for the saved Q(B_N X B_C)
+    (dict(y_dtype=5), "HQ_ERR_DTYPE"),
+    (dict(save_x=None), "HQ_ERR_NULL"),
+    (dict(save_w=qt(96, 64, codes=None)), "HQ_ERR_NULL"),
+    (dict(save_xt=qt(64, 64, codes_t=None)), "HQ_ERR_NULL"),
+    (dict(cfg=cfg(mode=B.HQ_SCALE_STEP), step_x=FAKE), "HQ_ERR_NULL"),
+    (dict(y=None), "HQ_ERR_NULL"),
+    (dict(ws_bytes=1024), "HQ_ERR_WORKSPACE"),
+    (dict(save_w=qt(96, 64, ld_t=72)), "HQ_ERR_ALIGN"),
+])
+def test_linear_fwd_validation(kw, expect):
+    assert B.STATUS_NAMES[fwd(**kw)] == expect
+
+
+def test_linear_fwd_halo2_without_xt_is_allowed_before_device():
+    # N = 48 is fine when the weight-gradient codes are not requested; the call then reaches
+    # the device check, which fails on a machine without a gfx950 GPU.
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("only meaningful without a GPU")
+    assert B.STATUS_NAMES[fwd(N=48, save_xt=None, save_x=qt(48, 64),
+                              ws_bytes=1 << 30)] == "HQ_ERR_DEVICE"
+
+
+def bwd_in(**kw):
+    N, C, D = 64, 64, 96
+    args = dict(dy=FAKE, dy_dtype=B.HQ_BF16, N=N, C=C, D=D, cfg=cfg(), step_g=None,
+                saved_w=qt(D, C), dx=FAKE, dx_dtype=B.HQ_BF16, save_g=qt(N, D, rot=B.HQ_ROT_LEFT),
+                ws=FAKE, ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return B.hq_linear_bwd_input(**args)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(saved_w=qt(96, 64, k=16)), "HQ_ERR_MISMATCH"),
+    (dict(saved_w=qt(96, 64, bits=4)), "HQ_ERR_MISMATCH"),
+    (dict(saved_w=qt(96, 64, rot=B.HQ_ROT_NONE)), "HQ_ERR_MISMATCH"),
+    (dict(saved_w=qt(64, 64)), "HQ_ERR_MISMATCH"),
+    (dict(saved_w=qt(96, 64, codes_t=None)), "HQ_ERR_NULL"),
+    (dict(saved_w=None), "HQ_ERR_NULL"),
+    (dict(save_g=None), "HQ_ERR_NULL"),
+    (dict(cfg=cfg(mode=B.HQ_SCALE_STEP)), "HQ_ERR_NULL"),
+    (dict(dx=None), "HQ_ERR_NULL"),
+    (dict(dy_dtype=-1), "HQ_ERR_DTYPE"),
+    (dict(ws=None), "HQ_ERR_WORKSPACE"),
+])
+def test_bwd_input_validation(kw, expect):
+    assert B.STATUS_NAMES[bwd_in(**kw)] == expect
+
+
+def bwd_w(**kw):
+    N, C, D = 64, 64, 96
+    args = dict(saved_g=qt(N, D, rot=B.HQ_ROT_LEFT), saved_x=qt(N, C, rot=B.HQ_ROT_BOTH), N=N,
+                C=C, D=D, cfg=cfg(), dw=FAKE, dw_dtype=B.HQ_F32, ws=FAKE, ws_bytes=1 << 30,
+                stream=None)
+    args.update(kw)
+    return B.hq_linear_bwd_weight(**args)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(saved_x=qt(64, 64, rot=B.HQ_ROT_RIGHT)), "HQ_ERR_MISMATCH"),  # HALO2 needs B_N X B_C
+    (dict(saved_g=qt(64, 96, rot=B.HQ_ROT_NONE)), "HQ_ERR_MISMATCH"),
+    (dict(cfg=cfg(variant=B.HQ_VARIANT_HQ)), "HQ_ERR_MISMATCH"),
+    (dict(saved_g=qt(64, 96, rot=B.HQ_ROT_LEFT, ld_t=8)), "HQ_ERR_ALIGN"),
+    (dict(dw=None), "HQ_ERR_NULL"),
+    (dict(N=40), "HQ_ERR_SHAPE"),
+])
+def test_bwd_weight_validation(kw, expect):
+    assert B.STATUS_NAMES[bwd_w(**kw)] == expect
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(k=6), "HQ_ERR_K"),
+    (dict(rot=B.HQ_ROT_BOTH), "HQ_ERR_MODE"),
+    (dict(cols=40), "HQ_ERR_SHAPE"),
+    (dict(src=None), "HQ_ERR_NULL"),
+    (dict(dst_dtype=3), "HQ_ERR_DTYPE"),
+])
+def test_fwht_validation(kw, expect):
+    args = dict(src=FAKE, src_dtype=B.HQ_F32, dst=FAKE, dst_dtype=B.HQ_F32, rows=32, cols=64,
+                rot=B.HQ_ROT_RIGHT, k=32, stream=None)
+    args.update(kw)
+    assert B.STATUS_NAMES[B.hq_fwht(**args)] == expect
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(lda=8), "HQ_ERR_SHAPE"),
+    (dict(lda=72, K=64), "HQ_ERR_ALIGN"),
+    (dict(a=FAKE_MIS), "HQ_ERR_ALIGN"),
+    (dict(c=None), "HQ_ERR_NULL"),
+    (dict(M=-1), "HQ_ERR_SHAPE"),
+])
+def test_gemm_validation(kw, expect):
+    args = dict(a=FAKE, lda=64, b_t=FAKE, ldb=64, c=FAKE, M=32, N=32, K=64, stream=None)
+    args.update(kw)
+    assert B.STATUS_NAMES[B.hq_gemm_i8_i32(**args)] == expect
+
+
+def test_empty_calls_return_ok_without_device():
+    # zero-size products have nothing to launch
+    assert B.hq_gemm_i8_i32(None, 16, None, 16, None, 0, 0, 0, None) == B.HQ_OK
+    assert B.hq_fwht(None, B.HQ_F32, None, B.HQ_F32, 0, 64, B.HQ_ROT_RIGHT, 32, None) == B.HQ_OK
+
+
+def test_no_compute_symbol_outside_header():
+    """Every exported hq_* function is declared in the header (no hidden entry points)."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = sorted(set(m for m in re.findall(r"\bT (hq_[a-z0-9_]+)\b", out)))
+    assert exported == declared_symbols()

@@ -1,0 +1,280 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the same seeded inputs.
+
+Sizes here run in seconds on the oracle and still span several kernel tiles plus ragged
+tails; the full workload sizes are covered by test_gpu_fullsize.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from hadamard_rotated_precision_amd import binding as B
+from hadamard_rotated_precision_amd import tensors as T
+from hadamard_rotated_precision_amd import workloads as WL
+
+from hq_testlib import (assert_codes, assert_scale, compare_layer, host, outputs_from_gpu_codes,
+                        rel_fro, rounded, run_gpu, run_oracle)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def banner(*a):
+    print("[case]", *a, flush=True)
+
+
+# ------------------------------------------------------------------ integer GEMM
+@pytest.mark.parametrize("M,N,K", [(1, 1, 16), (256, 256, 64), (300, 257, 1040), (513, 129, 4096),
+                                   (64, 700, 48), (256, 512, 0), (17, 33, 8)])
+def test_gemm_i8_i32_bitexact(M, N, K):
+    banner("gemm", M, N, K)
+    rng = np.random.default_rng(M * 7 + N * 3 + K)
+    lda = ldb = max(16, (K + 15) // 16 * 16)
+    A = np.zeros((M, lda), dtype=np.int8)
+    Bt = np.zeros((N, ldb), dtype=np.int8)
+    A[:, :K] = rng.integers(-128, 128, size=(M, K))
+    Bt[:, :K] = rng.integers(-128, 128, size=(N, K))
+    a = torch.from_numpy(A).to(DEV)
+    b = torch.from_numpy(Bt).to(DEV)
+    c = torch.full((M, N), 12345, dtype=torch.int32, device=DEV)
+    B.check(B.hq_gemm_i8_i32(a.data_ptr(), lda, b.data_ptr(), ldb, c.data_ptr(), M, N, K,
+                             T.stream_ptr()), "gemm")
+    torch.cuda.synchronize()
+    ref = O.gemm_i8(A[:, :K], K, 1, Bt[:, :K], 1, K, M, N, K) if K else np.zeros((M, N), np.int64)
+    np.testing.assert_array_equal(c.cpu().numpy().astype(np.int64), ref)
+
+
+def test_gemm_extremes_fit_int32():
+    """All -128 / 127 operands at the largest contraction of the workloads (13824)."""
+    K, M, N = 13824, 64, 64
+    A = np.full((M, K), -128, dtype=np.int8)
+    A[1::2] = 127
+    Bt = np.full((N, K), -128, dtype=np.int8)
+    a, b = torch.from_numpy(A).to(DEV), torch.from_numpy(Bt).to(DEV)
+    c = torch.empty((M, N), dtype=torch.int32, device=DEV)
+    B.check(B.hq_gemm_i8_i32(a.data_ptr(), K, b.data_ptr(), K, c.data_ptr(), M, N, K,
+                             T.stream_ptr()), "gemm")
+    torch.cuda.synchronize()
+    ref = A[:, :1].astype(np.int64) * -128 * K
+    np.testing.assert_array_equal(c.cpu().numpy()[:, :1], ref)
+
+
+# ------------------------------------------------------------------ FWHT (exact)
+@pytest.mark.parametrize("k", [1, 2, 4, 8, 16, 32, 64, 128, 256])
+@pytest.mark.parametrize("rot", [B.HQ_ROT_RIGHT, B.HQ_ROT_LEFT])
+@pytest.mark.parametrize("dt", [B.HQ_F32, B.HQ_BF16, B.HQ_F16])
+def test_fwht_exact_on_small_integers(k, rot, dt):
+    """Small-integer inputs make every partial sum exact in fp32, so the butterfly result must
+    equal the oracle's dense product with the explicit H bit for bit."""
+    banner("fwht", k, rot, dt)
+    rng = np.random.default_rng(k + 10 * rot + 100 * dt)
+    rows = 2 * max(k, 8) if rot == B.HQ_ROT_LEFT else 37
+    cols = 3 * max(k, 16) + (0 if rot == B.HQ_ROT_RIGHT else 5)
+    V = rng.integers(-8, 9, size=(rows, cols)).astype(np.float32)
+    bits = WL.to_dtype_bits(V.astype(np.float64), dt)
+    src = T.device_tensor_from_bits(bits, dt, DEV)
+    dst = torch.empty((rows, cols), dtype=torch.float32, device=DEV)
+    B.check(B.hq_fwht(src.data_ptr(), dt, dst.data_ptr(), B.HQ_F32, rows, cols, rot, k,
+                      T.stream_ptr()), "fwht")
+    torch.cuda.synchronize()
+    ref = O.rotate(V.astype(np.float64), rot, k)
+    np.testing.assert_array_equal(dst.cpu().numpy().astype(np.float64), ref)
+
+
+def test_fwht_output_dtypes():
+    rng = np.random.default_rng(3)
+    V = rng.standard_normal((64, 256)).astype(np.float32)
+    src = torch.from_numpy(V).to(DEV)
+    ref = O.rotate(V.astype(np.float64), O.ROT_RIGHT, 64)
+    for dt in (B.HQ_BF16, B.HQ_F16):
+        dst = torch.empty((64, 256), dtype=T.TORCH_DT[dt], device=DEV)
+        B.check(B.hq_fwht(src.data_ptr(), B.HQ_F32, dst.data_ptr(), dt, 64, 256, B.HQ_ROT_RIGHT,
+                          64, T.stream_ptr()), "fwht")
+        torch.cuda.synchronize()
+        got = O.decode(T.bits_of(dst), dt)
+        assert rel_fro(got, rounded(ref, dt)) < 1e-3
+
+
+# ---------------------------------------------------------- rotate + quantize
+def _rq(V_bits, dt, rows, cols, rot, k, bits, mode, step=None, codes=True, codes_t=True):
+    q = T.QTensor(rows, cols, codes=codes, codes_t=codes_t)
+    cfg = T.config(k, bits, mode, B.HQ_VARIANT_HQ)
+    ws_bytes = B.hq_workspace_bytes(cfg, rows, cols, cols)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    src = T.device_tensor_from_bits(V_bits, dt, DEV)
+    st = None if step is None else torch.tensor([step], dtype=torch.float32, device=DEV)
+    B.check(B.hq_rotate_quantize(src.data_ptr(), dt, rows, cols, rot, cfg, T.ptr(st), q.st,
+                                 ws.data_ptr(), ws_bytes, T.stream_ptr()), "rotate_quantize")
+    torch.cuda.synchronize()
+    return q
+
+
+@pytest.mark.parametrize("rot,k,rows,cols", [
+    (B.HQ_ROT_NONE, 1, 300, 100),
+    (B.HQ_ROT_RIGHT, 16, 300, 1040),
+    (B.HQ_ROT_RIGHT, 32, 77, 512),
+    (B.HQ_ROT_RIGHT, 256, 129, 768),
+    (B.HQ_ROT_RIGHT, 4, 33, 36),
+    (B.HQ_ROT_LEFT, 256, 512, 300),
+    (B.HQ_ROT_LEFT, 16, 48, 200),
+    (B.HQ_ROT_LEFT, 8, 24, 100),
+    (B.HQ_ROT_LEFT, 128, 256, 64),
+    (B.HQ_ROT_BOTH, 256, 512, 512),
+    (B.HQ_ROT_BOTH, 128, 256, 384),
+    (B.HQ_ROT_BOTH, 16, 64, 48),
+])
+@pytest.mark.parametrize("bits,mode", [(8, B.HQ_SCALE_ABSMAX), (4, B.HQ_SCALE_STEP)])
+@pytest.mark.parametrize("dt", [B.HQ_BF16, B.HQ_F16])
+def test_rotate_quantize_parity(rot, k, rows, cols, bits, mode, dt):
+    banner("rq", rot, k, rows, cols, bits, mode, dt)
+    rng = np.random.default_rng(rows * 31 + cols + k)
+    V = rng.standard_normal((rows, cols))
+    V[:, rng.choice(cols, max(1, cols // 100), replace=False)] *= 40.0   # outlier channels
+    vb = WL.to_dtype_bits(V, dt)
+    Vd = O.decode(vb, dt)
+    step = None
+    if mode == B.HQ_SCALE_STEP:
+        step = float(np.float32(2.0 * np.sqrt(k if rot != B.HQ_ROT_BOTH else k * k) *
+                                0.8 / np.sqrt(7.0)))
+    q = _rq(vb, dt, rows, cols, rot, k, bits, mode, step)
+    ref_codes, ref_s = O.quantize_tensor(Vd, rot, k, bits, O.STEP if step else O.ABSMAX, step)
+    got = q.codes_view().cpu().numpy()
+    assert_codes(got, ref_codes, "codes")
+    np.testing.assert_array_equal(q.codes_t_view().cpu().numpy(), got.T)
+    assert_scale(float(q.scale.cpu()[0]), ref_s, "scale")
+    # pitch padding is zero so whole 16-byte rows can be read by the GEMM
+    pad = q.codes.cpu().numpy()[:, cols:(cols + 15) // 16 * 16]
+    assert not pad.any()
+    pad_t = q.codes_t.cpu().numpy()[:, rows:(rows + 15) // 16 * 16]
+    assert not pad_t.any()
+    assert q.st.rows == rows and q.st.cols == cols and q.st.rot == rot and q.st.k == k
+
+
+@pytest.mark.parametrize("rot", [B.HQ_ROT_RIGHT, B.HQ_ROT_LEFT])
+def test_rotate_quantize_single_layout(rot):
+    """Only one code layout requested (the other is staged in the workspace)."""
+    rng = np.random.default_rng(5)
+    V = rng.standard_normal((256, 512))
+    vb = WL.to_dtype_bits(V, B.HQ_BF16)
+    ref, _ = O.quantize_tensor(O.decode(vb, B.HQ_BF16), rot, 32, 8)
+    q1 = _rq(vb, B.HQ_BF16, 256, 512, rot, 32, 8, B.HQ_SCALE_ABSMAX, codes=True, codes_t=False)
+    assert_codes(q1.codes_view().cpu().numpy(), ref, "rm only")
+    q2 = _rq(vb, B.HQ_BF16, 256, 512, rot, 32, 8, B.HQ_SCALE_ABSMAX, codes=False, codes_t=True)
+    assert_codes(q2.codes_t_view().cpu().numpy().T, ref, "t only")
+
+
+def test_quantize_degenerate_tensors():
+    """Zero tensor -> scale 0, codes 0; constant block -> energy in coefficient 0 only;
+    a single outlier -> spread at equal magnitude over its block (codes +-127)."""
+    rows, cols, k = 32, 256, 32
+    Z = np.zeros((rows, cols))
+    q = _rq(WL.to_dtype_bits(Z, B.HQ_BF16), B.HQ_BF16, rows, cols, B.HQ_ROT_RIGHT, k, 8,
+            B.HQ_SCALE_ABSMAX)
+    assert float(q.scale.cpu()[0]) == 0.0 and not q.codes_view().cpu().numpy().any()
+    Cst = np.full((rows, cols), 0.5)
+    q = _rq(WL.to_dtype_bits(Cst, B.HQ_BF16), B.HQ_BF16, rows, cols, B.HQ_ROT_RIGHT, k, 8,
+            B.HQ_SCALE_ABSMAX)
+    codes = q.codes_view().cpu().numpy()
+    assert (codes[:, ::k] == 127).all()
+    codes[:, ::k] = 0
+    assert not codes.any()
+    One = np.zeros((rows, cols))
+    One[3, 40] = 2.0
+    q = _rq(WL.to_dtype_bits(One, B.HQ_BF16), B.HQ_BF16, rows, cols, B.HQ_ROT_RIGHT, k, 8,
+            B.HQ_SCALE_ABSMAX)
+    codes = q.codes_view().cpu().numpy()
+    assert (np.abs(codes[3, 32:64]) == 127).all()
+    assert float(q.scale.cpu()[0]) == np.float32(2.0 / 127)
+
+
+def test_quantize_empty_tensor():
+    q = T.QTensor(0, 64)
+    q.scale.fill_(5.0)
+    cfg = T.config(32, 8, B.HQ_SCALE_ABSMAX, B.HQ_VARIANT_HQ)
+    ws_bytes = B.hq_workspace_bytes(cfg, 1, 64, 64)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    x = torch.empty((1, 64), dtype=torch.bfloat16, device=DEV)
+    B.check(B.hq_rotate_quantize(x.data_ptr(), B.HQ_BF16, 0, 64, B.HQ_ROT_RIGHT, cfg, None, q.st,
+                                 ws.data_ptr(), ws_bytes, T.stream_ptr()), "empty")
+    torch.cuda.synchronize()
+    assert float(q.scale.cpu()[0]) == 0.0
+
+
+# ------------------------------------------------------------- whole layer
+REDUCED = {
+    1: dict(),                                       # already small: 256 x 512 x 512
+    2: dict(N=512, C=1024, D=768),
+    3: dict(N=1000, C=1024, D=1000),                 # ragged token and output dims
+    4: dict(N=512, C=768, D=1100),
+    5: dict(N=256, C=1408, D=640),
+}
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_layer_parity_reduced(cid):
+    cfg = WL.config(cid, **REDUCED[cid])
+    banner("layer", cfg["name"], cfg["N"], cfg["C"], cfg["D"])
+    inputs = WL.make_inputs(cfg)
+    res = run_gpu(cfg, inputs)
+    h = host(res, cfg["out_dtype"])
+    ora = run_oracle(cfg, inputs)
+    stats = compare_layer(cfg, h, ora, cfg["out_dtype"])
+    print("stats", stats, flush=True)
+    # Same codes in, same products out: the GPU GEMM + epilogue against the oracle's products
+    # evaluated on the GPU's own codes and scales.
+    again = outputs_from_gpu_codes(cfg, h)
+    for name, ref in again.items():
+        err = rel_fro(h[name], rounded(ref, cfg["out_dtype"]))
+        assert err <= 2e-3 * (1 if cfg["out_dtype"] != O.F32 else 1e-2), (name, err)
+
+
+@pytest.mark.parametrize("cid", [2, 5])
+def test_layer_parity_fp32_outputs(cid):
+    """fp32 outputs: the GEMM + dequant + inverse rotation against the oracle's exact int64
+    inverse rotation on the GPU's own codes, to 1e-5."""
+    cfg = WL.config(cid, **REDUCED[cid])
+    inputs = WL.make_inputs(cfg)
+    res = run_gpu(cfg, inputs, out_dt=O.F32)
+    h = host(res, O.F32)
+    for name, ref in outputs_from_gpu_codes(cfg, h).items():
+        err = rel_fro(h[name], ref)
+        assert err <= 1e-5, (name, err)
+
+
+@pytest.mark.parametrize("variant", [B.HQ_VARIANT_HALO0, B.HQ_VARIANT_HQ, B.HQ_VARIANT_HALO2])
+@pytest.mark.parametrize("k", [1, 16, 64])
+def test_layer_variants_and_k(variant, k):
+    cfg = WL.config(2, N=256, C=320, D=192, k=k, variant=variant)
+    if variant == B.HQ_VARIANT_HALO0:
+        cfg["k"] = k
+    inputs = WL.make_inputs(cfg)
+    res = run_gpu(cfg, inputs)
+    h = host(res, cfg["out_dtype"])
+    ora = run_oracle(cfg, inputs)
+    compare_layer(cfg, h, ora, cfg["out_dtype"])
+
+
+def test_layer_deterministic():
+    cfg = WL.config(2, N=512, C=512, D=512)
+    inputs = WL.make_inputs(cfg)
+    a = host(run_gpu(cfg, inputs), cfg["out_dtype"])
+    b = host(run_gpu(cfg, inputs), cfg["out_dtype"])
+    for key in a:
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+
+
+def test_layer_empty_tokens():
+    """N = 0 tokens: nothing to compute, dW = 0 (no tokens to sum over)."""
+    N, C, D = 0, 256, 128
+    layer = T.Layer(N, C, D, 32, 8, B.HQ_SCALE_ABSMAX, B.HQ_VARIANT_HQ)
+    x = torch.empty((N, C), dtype=torch.bfloat16, device=DEV)
+    w = torch.randn((D, C), dtype=torch.bfloat16, device=DEV)
+    y = torch.empty((N, D), dtype=torch.bfloat16, device=DEV)
+    layer.fwd(x, w, y)
+    dy = torch.empty((N, D), dtype=torch.bfloat16, device=DEV)
+    dx = torch.empty((N, C), dtype=torch.bfloat16, device=DEV)
+    layer.bwd_input(dy, dx)
+    dw = torch.full((D, C), 7.0, dtype=torch.float32, device=DEV)
+    layer.bwd_weight(dw)
+    torch.cuda.synchronize()
+    assert float(dw.abs().max()) == 0.0
