@@ -1,0 +1,278 @@
+#!/usr/bin/env python3
+"""Benchmark: one HQ-MM linear-layer step (forward Y, input gradient dX, weight gradient dW,
+HALO-2 rotations, tensor-wise INT8) on one MI355X, through the C ABI of libhq.
+
+A step is the whole hot path on one batch: rotate+quantize X, W and dY, the three INT8 MFMA
+GEMMs with dequantization, and the output-side inverse rotations. Inputs are seeded synthetic
+tensors with the workload's shapes and distributions, resident in HBM before timing starts.
+
+Printed (one JSON line): effective TOPS = sum of 2*M*N*K over the three products / step
+time; the percentage of the INT8 MFMA peak; the roofline of the dominant kernel (the GEMM,
+timed with HIP events recorded on its own launch stream inside the timed region); the
+rotate+quantize bandwidth; an unrotated bf16 GEMM baseline of the same three products; and
+the CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0     # MI355X dense INT8 MFMA, 5.0 POP/s
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_hbm_traffic.json")
+GEMM_SOURCE = os.path.join(ROOT, "hadamard_rotated_precision_amd", "csrc", "hq_gemm.hip")
+
+
+def gemm_source_hash():
+    with open(GEMM_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def layer_ops(cfg):
+    N, C, D = cfg["N"], cfg["C"], cfg["D"]
+    ops = 0
+    if "fwd" in cfg["passes"]:
+        ops += 2 * N * D * C
+    if "dx" in cfg["passes"]:
+        ops += 2 * N * C * D
+    if "dw" in cfg["passes"]:
+        ops += 2 * D * C * N
+    return ops
+
+
+def prologue_bytes(cfg, in_bytes):
+    """Algorithmic bytes of the rotate+quantize stage of one step: each input read once, each
+    code tensor the method defines written once (X: qX and, under HALO-2, qXt)."""
+    from hadamard_rotated_precision_amd import workloads as WL
+    N, C, D = cfg["N"], cfg["C"], cfg["D"]
+    nx_codes = 2 if cfg["variant"] == WL.HALO2 else 1
+    b = N * C * (in_bytes + nx_codes) + D * C * (in_bytes + 1)
+    if "dx" in cfg["passes"] or "dw" in cfg["passes"]:
+        b += N * D * (in_bytes + 1)
+    return b
+
+
+def cpu_baseline(cfg_id, tokens):
+    """The oracle (plain C, OpenMP) on a bounded sample: the same workload with fewer tokens."""
+    import oracle as O
+    from hadamard_rotated_precision_amd import workloads as WL
+    cfg = WL.config(cfg_id)
+    k = cfg["k"]
+    tokens = max(k, tokens // k * k)
+    cfg = WL.config(cfg_id, N=tokens)
+    inputs = WL.make_inputs(cfg)
+    dt = cfg["in_dtype"]
+    X = O.decode(inputs["x"], dt)
+    W = O.decode(inputs["w"], dt)
+    dY = O.decode(inputs["dy"], dt) if inputs.get("dy") is not None else None
+    t0 = time.perf_counter()
+    O.linear(X, W, dY, k, cfg["bits"], cfg["variant"], cfg["mode"], inputs.get("steps"),
+             cfg["passes"])
+    dt_s = time.perf_counter() - t0
+    ops = layer_ops(cfg)
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": ops / dt_s / 1e12, "unit": "TOPS", "cores": cores, "kind": "oracle",
+            "sample": "%s with N=%d tokens (same C, D, k, distributions): rotate, quantize, "
+                      "int64 GEMMs, exact inverse rotations, dequantize for %s; %.2f s"
+                      % (cfg["name"], tokens, "+".join(cfg["passes"]), dt_s),
+            "seconds": dt_s}
+
+
+def bf16_baseline(cfg, steps, warmup, library):
+    """Three unrotated bf16 GEMMs of the same shapes (timing context only)."""
+    import torch
+    torch.backends.cuda.preferred_blas_library(library)
+    N, C, D = cfg["N"], cfg["C"], cfg["D"]
+    g = torch.Generator(device="cuda").manual_seed(0)
+    x = torch.randn((N, C), device="cuda", dtype=torch.bfloat16, generator=g)
+    w = torch.randn((D, C), device="cuda", dtype=torch.bfloat16, generator=g)
+    dy = torch.randn((N, D), device="cuda", dtype=torch.bfloat16, generator=g)
+
+    def run():
+        torch.mm(x, w.t())
+        torch.mm(dy, w)
+        torch.mm(dy.t(), x)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        run()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2,
+                    help="workload id (default 2: HALO-2 step, 2048 x 4096 x 4096, k=256)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bf16-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+    from hadamard_rotated_precision_amd import binding as B
+    from hadamard_rotated_precision_amd import tensors as T
+    from hadamard_rotated_precision_amd import workloads as WL
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    B.load()
+    cfg = WL.config(args.config)
+    N, C, D = cfg["N"], cfg["C"], cfg["D"]
+    in_dt, out_dt = cfg["in_dtype"], cfg["out_dtype"]
+    print("[bench] workload %s: generating inputs" % cfg["name"], file=sys.stderr, flush=True)
+    inputs = WL.make_inputs(cfg)
+    dev = "cuda"
+    x = T.device_tensor_from_bits(inputs["x"], in_dt, dev)
+    w = T.device_tensor_from_bits(inputs["w"], in_dt, dev)
+    has_bwd = "dx" in cfg["passes"] or "dw" in cfg["passes"]
+    dy = T.device_tensor_from_bits(inputs["dy"], in_dt, dev) if has_bwd else None
+    steps_t = None
+    if cfg["mode"] == WL.STEP:
+        steps_t = {n: torch.tensor([v], dtype=torch.float32, device=dev)
+                   for n, v in inputs["steps"].items()}
+    layer = T.Layer(N, C, D, cfg["k"], cfg["bits"], cfg["mode"], cfg["variant"], device=dev)
+    odt = T.TORCH_DT[out_dt]
+    y = torch.empty((N, D), dtype=odt, device=dev)
+    dx = torch.empty((N, C), dtype=odt, device=dev) if "dx" in cfg["passes"] else None
+    dw = torch.empty((D, C), dtype=odt, device=dev) if "dw" in cfg["passes"] else None
+    stream = torch.cuda.current_stream()
+
+    def step():
+        layer.fwd(x, w, y, steps_t, stream)
+        if dx is not None:
+            layer.bwd_input(dy, dx, steps_t, stream)
+        if dw is not None:
+            layer.bwd_weight(dw, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+
+    # ---- timed region: K steps; the GEMM launches are bracketed by HIP events on the stream
+    B.check(B.hq_profile_start(1 << B.HQ_KIND_GEMM), "profile")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = B.profile_stop_dict()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    ops = layer_ops(cfg)
+    eff_tops = ops / (ms_per_step * 1e-3) / 1e12
+    gcount, gms, gunits = prof["gemm"]
+    gemm_tops = gunits / (gms * 1e-3) / 1e12 if gms > 0 else None
+    gemm_avg_us = gms * 1e3 / gcount if gcount else None
+    print("[bench] timed region done: %.3f ms/step" % ms_per_step, file=sys.stderr, flush=True)
+
+    # ---- per-kind breakdown of the same step (all kinds bracketed; a separate pass)
+    B.check(B.hq_profile_start((1 << B.HQ_KIND_COUNT) - 1), "profile")
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    breakdown = B.profile_stop_dict()
+
+    # ---- rotate+quantize bandwidth: the prologue launches alone
+    in_bytes = 2 if in_dt != WL.F32 else 4
+    pro_bytes = prologue_bytes(cfg, in_bytes)
+    pro_kinds = (1 << B.HQ_KIND_ROT_ABSMAX) | (1 << B.HQ_KIND_ROT_QUANT) | \
+        (1 << B.HQ_KIND_TRANSPOSE) | (1 << B.HQ_KIND_MISC)
+    pro_ms = 0.0
+    for kind in ("rot_absmax", "rot_quant", "transpose", "misc"):
+        pro_ms += breakdown[kind][1]
+    # the two-sided rotation of X stages its column pass through a store pass
+    store_ms_prologue = None
+    if cfg["variant"] == WL.HALO2:
+        # measure the forward alone to split the store kind between prologue and epilogue
+        B.check(B.hq_profile_start(1 << B.HQ_KIND_ROT_STORE), "profile")
+        for _ in range(args.steps):
+            layer.fwd(x, w, y, steps_t, stream)
+        torch.cuda.synchronize()
+        store_ms_prologue = B.profile_stop_dict()["rot_store"][1]
+        pro_ms += store_ms_prologue
+    pro_ms_step = pro_ms / args.steps
+    rq_gbs = pro_bytes / (pro_ms_step * 1e-3) / 1e9 if pro_ms_step > 0 else None
+    _ = pro_kinds
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("gemm_source_sha256_16") == gemm_source_hash() and \
+                tr.get("workload") == cfg["name"]:
+            traffic = tr.get("bytes_per_launch")
+
+    result = {
+        "metric": "HQ-MM fwd+bwd effective TOPS and % of INT8 MFMA peak; rotate+quant GB/s",
+        "value": round(eff_tops, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": cfg["name"], "N": N, "C": C, "D": D, "k": cfg["k"],
+                   "bits": cfg["bits"], "variant": ["HALO0", "HQ", "HALO2"][cfg["variant"]],
+                   "in_dtype": WL.DTYPE_NAMES[in_dt], "out_dtype": WL.DTYPE_NAMES[out_dt],
+                   "passes": list(cfg["passes"]), "parallelism": "single GPU"},
+        "pct_int8_peak": round(100.0 * eff_tops / PEAK_INT8_TOPS, 2),
+        "gemm_tops": None if gemm_tops is None else round(gemm_tops, 1),
+        "rotate_quant_gbps": None if rq_gbs is None else round(rq_gbs, 1),
+        "rotate_quant_pct_hbm": None if rq_gbs is None else round(100 * rq_gbs / PEAK_HBM_GBS, 1),
+        "roofline": {
+            "kernel": "gemm_i8_kernel (int8 MFMA GEMM + dequant epilogue)",
+            "bound": "mfma",
+            "achieved": None if gemm_tops is None else round(gemm_tops, 1),
+            "peak": PEAK_INT8_TOPS,
+            "unit": "TOP/s",
+            "frac": None if gemm_tops is None else round(gemm_tops / PEAK_INT8_TOPS, 4),
+            "traffic": traffic,
+            "launches": gcount,
+            "avg_launch_us": None if gemm_avg_us is None else round(gemm_avg_us, 2),
+            "ops_per_launch": None if not gcount else gunits / gcount,
+        },
+        "breakdown_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in breakdown.items()},
+    }
+    if not args.no_bf16_baseline:
+        try:
+            ms_rb = bf16_baseline(cfg, args.steps, args.warmup, "cublas")
+            ms_lt = bf16_baseline(cfg, args.steps, args.warmup, "cublaslt")
+            result["bf16_baseline"] = {
+                "what": "three unrotated bf16 torch.mm of the same shapes (Y, dX, dW)",
+                "ms_rocblas": round(ms_rb, 4), "ms_hipblaslt": round(ms_lt, 4),
+                "speedup_vs_rocblas": round(ms_rb / ms_per_step, 3),
+                "speedup_vs_hipblaslt": round(ms_lt / ms_per_step, 3)}
+        except Exception as exc:  # report, do not fail the benchmark line
+            result["bf16_baseline"] = {"error": str(exc)}
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(args.config, args.cpu_sample_tokens)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

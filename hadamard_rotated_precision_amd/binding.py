@@ -22,7 +22,10 @@ HQ_VARIANT_HALO0, HQ_VARIANT_HQ, HQ_VARIANT_HALO2 = 0, 1, 2
 
 EXPORTS = ["hq_abi_version", "hq_status_string", "hq_code_pitch", "hq_workspace_bytes",
            "hq_rotate_quantize", "hq_linear_fwd", "hq_linear_bwd_input", "hq_linear_bwd_weight",
-           "hq_fwht", "hq_gemm_i8_i32"]
+           "hq_fwht", "hq_gemm_i8_i32", "hq_profile_start", "hq_profile_stop"]
+HQ_KIND_GEMM, HQ_KIND_ROT_ABSMAX, HQ_KIND_ROT_QUANT, HQ_KIND_ROT_STORE = 0, 1, 2, 3
+HQ_KIND_TRANSPOSE, HQ_KIND_MISC, HQ_KIND_COUNT = 4, 5, 6
+KIND_NAMES = ["gemm", "rot_absmax", "rot_quant", "rot_store", "transpose", "misc"]
 
 
 class hq_config(ctypes.Structure):
@@ -35,6 +38,11 @@ class hq_qtensor(ctypes.Structure):
                 ("scale", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
                 ("ld", ctypes.c_int64), ("ld_t", ctypes.c_int64), ("k", ctypes.c_int32),
                 ("bits", ctypes.c_int32), ("rot", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class hq_profile_stat(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("count", ctypes.c_int32),
+                ("total_ms", ctypes.c_double), ("units", ctypes.c_double)]
 
 
 class HQError(RuntimeError):
@@ -84,6 +92,10 @@ def load(build_if_missing=True):
     lib.hq_fwht.argtypes = [vp, i32, vp, i32, i64, i64, i32, i32, vp]
     lib.hq_gemm_i8_i32.restype = i32
     lib.hq_gemm_i8_i32.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, vp]
+    lib.hq_profile_start.restype = i32
+    lib.hq_profile_start.argtypes = [ctypes.c_uint32]
+    lib.hq_profile_stop.restype = i32
+    lib.hq_profile_stop.argtypes = [P(hq_profile_stat), i32]
     _lib = lib
     return lib
 
@@ -138,6 +150,22 @@ def hq_fwht(src, src_dtype, dst, dst_dtype, rows, cols, rot, k, stream):
 
 def hq_gemm_i8_i32(a, lda, b_t, ldb, c, M, N, K, stream):
     return load().hq_gemm_i8_i32(a, lda, b_t, ldb, c, M, N, K, stream)
+
+
+def hq_profile_start(kind_mask):
+    return load().hq_profile_start(kind_mask)
+
+
+def hq_profile_stop(stats, n_stats):
+    return load().hq_profile_stop(stats, n_stats)
+
+
+def profile_stop_dict():
+    """hq_profile_stop into a {kind name: (count, total_ms, units)} dict."""
+    arr = (hq_profile_stat * HQ_KIND_COUNT)()
+    check(hq_profile_stop(arr, HQ_KIND_COUNT), "hq_profile_stop")
+    return {KIND_NAMES[i]: (arr[i].count, arr[i].total_ms, arr[i].units)
+            for i in range(HQ_KIND_COUNT)}
 
 
 def check(status, where=""):

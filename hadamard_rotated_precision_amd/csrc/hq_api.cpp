@@ -371,64 +371,41 @@ hq_status hq_linear_bwd_input(const void* dy, int32_t dy_dtype, int64_t N, int64
                            save_g->codes, save_g->ld, save_g->codes_t, save_g->ld_t,
                            save_g->scale, wsp, 0, st));
   fill_meta(save_g, N, D, k, cfg->bits, rg);
+  // dX = [B_N] (qG qW) [B_C] sG sW / k^e, dequantized and inverse-rotated in the GEMM epilogue.
   GemmPass g;
-  g.a = save_g->codes;
-  g.lda = save_g->ld;
-  g.b = saved_w->codes_t;
-  g.ldb = saved_w->ld_t;
-  g.M = N;
-  g.N = C;
-  g.K = D;
   g.epi = hq::EPI_SCALE;
   g.sa = save_g->scale;
   g.sb = saved_w->scale;
+  g.c = dx;
+  g.out_dt = dx_dtype;
   g.ldc = C;
-  if (v == HQ_VARIANT_HALO0) {
-    g.c = dx;
-    g.out_dt = dx_dtype;
-    g.kmul = 1.0f;
-    HQ_TRY(hq::gemm_pass(g, st));
-    return HQ_OK;
-  }
-  g.c = wsp.fbuf;
-  g.out_dt = HQ_F32;
-  g.kmul = (v == HQ_VARIANT_HALO2) ? 1.0f / static_cast<float>(k * k) : 1.0f / static_cast<float>(k);
-  HQ_TRY(hq::gemm_pass(g, st));
-  if (N * C == 0) return HQ_OK;
-  RowPass r;
-  r.src = wsp.fbuf;
-  r.in_dt = HQ_F32;
-  r.rows = N;
-  r.cols = C;
-  r.k = k;
-  r.op = hq::OP_STORE;
+  g.K = D;
   if (v == HQ_VARIANT_HQ) {
-    r.dst = dx;
-    r.out_dt = dx_dtype;
-    HQ_TRY(hq::rows_pass(r, st));
-    return HQ_OK;
+    // only the columns (C) rotate: compute dX^T = qW^T qG^T so C is the tile's row axis,
+    // where the epilogue rotates in registers, and store it transposed
+    g.a = saved_w->codes_t;
+    g.lda = saved_w->ld_t;
+    g.b = save_g->codes;
+    g.ldb = save_g->ld;
+    g.M = C;
+    g.N = N;
+    g.km = k;
+    g.trans_out = true;
+    g.kmul = 1.0f / static_cast<float>(k);
+  } else {
+    g.a = save_g->codes;
+    g.lda = save_g->ld;
+    g.b = saved_w->codes_t;
+    g.ldb = saved_w->ld_t;
+    g.M = N;
+    g.N = C;
+    if (v == HQ_VARIANT_HALO2) {   // rows (tokens) and columns (C) both rotate
+      g.km = k;
+      g.kn = k;
+      g.kmul = 1.0f / static_cast<float>(k * k);
+    }
   }
-  r.dst = wsp.fbuf;   // in place: each lane rewrites exactly the elements it read
-  r.out_dt = HQ_F32;
-  HQ_TRY(hq::rows_pass(r, st));
-  ColPass c;
-  c.src = wsp.fbuf;
-  c.in_dt = HQ_F32;
-  c.rows = N;
-  c.cols = C;
-  c.k = k;
-  c.op = hq::OP_STORE;
-  c.dst = dx;
-  c.out_dt = dx_dtype;
-  if (k == 1) {
-    r.src = wsp.fbuf;
-    r.k = 1;
-    r.dst = dx;
-    r.out_dt = dx_dtype;
-    HQ_TRY(hq::rows_pass(r, st));
-    return HQ_OK;
-  }
-  HQ_TRY(hq::cols_pass(c, st));
+  HQ_TRY(hq::gemm_pass(g, st));
   return HQ_OK;
 }
 
@@ -448,40 +425,35 @@ hq_status hq_linear_bwd_weight(const hq_qtensor* saved_g, const hq_qtensor* save
   HQ_CHECK(device_ok());
   hipStream_t st = static_cast<hipStream_t>(stream);
   Ws wsp(ws);
+  // dW = (qG^T qX') [B_C] sG sX' / k^e. When C rotates, compute dW^T = qX'^T qG so C is the
+  // tile's row axis (rotated in registers) and store it transposed.
   GemmPass g;
-  g.a = saved_g->codes_t;
-  g.lda = saved_g->ld_t;
-  g.b = saved_x->codes_t;
-  g.ldb = saved_x->ld_t;
-  g.M = D;
-  g.N = C;
-  g.K = N;
   g.epi = hq::EPI_SCALE;
   g.sa = saved_g->scale;
   g.sb = saved_x->scale;
+  g.c = dw;
+  g.out_dt = dw_dtype;
   g.ldc = C;
+  g.K = N;
   if (v == HQ_VARIANT_HALO0) {
-    g.c = dw;
-    g.out_dt = dw_dtype;
-    g.kmul = 1.0f;
-    HQ_TRY(hq::gemm_pass(g, st));
-    return HQ_OK;
+    g.a = saved_g->codes_t;
+    g.lda = saved_g->ld_t;
+    g.b = saved_x->codes_t;
+    g.ldb = saved_x->ld_t;
+    g.M = D;
+    g.N = C;
+  } else {
+    g.a = saved_x->codes_t;
+    g.lda = saved_x->ld_t;
+    g.b = saved_g->codes_t;
+    g.ldb = saved_g->ld_t;
+    g.M = C;
+    g.N = D;
+    g.km = k;
+    g.trans_out = true;
+    g.kmul = (v == HQ_VARIANT_HALO2) ? 1.0f / static_cast<float>(k * k) : 1.0f / static_cast<float>(k);
   }
-  g.c = wsp.fbuf;
-  g.out_dt = HQ_F32;
-  g.kmul = (v == HQ_VARIANT_HALO2) ? 1.0f / static_cast<float>(k * k) : 1.0f / static_cast<float>(k);
   HQ_TRY(hq::gemm_pass(g, st));
-  if (D * C == 0) return HQ_OK;
-  RowPass r;
-  r.src = wsp.fbuf;
-  r.in_dt = HQ_F32;
-  r.rows = D;
-  r.cols = C;
-  r.k = k;
-  r.op = hq::OP_STORE;
-  r.dst = dw;
-  r.out_dt = dw_dtype;
-  HQ_TRY(hq::rows_pass(r, st));
   return HQ_OK;
 }
 

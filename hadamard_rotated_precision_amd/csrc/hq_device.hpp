@@ -94,6 +94,35 @@ __device__ inline void load16(const void* row, int64_t i0, int64_t n, bool vec, 
   }
 }
 
+// Store u[0..N) * alpha as N consecutive elements starting at element `off` of `base`;
+// only the first `nvalid` are written. Whole aligned runs use 16-byte stores.
+template <class T, int N>
+__device__ inline void store_run(void* base, int64_t off, int64_t nvalid, const float (&u)[N],
+                                 float alpha) {
+  char* p = static_cast<char*>(base) + off * T::bytes;
+  constexpr int PER16 = 16 / T::bytes;   // elements per 16-byte store
+  if (nvalid >= N && N % PER16 == 0 && (reinterpret_cast<uintptr_t>(p) & 15u) == 0) {
+#pragma unroll
+    for (int q = 0; q < N; q += PER16) {
+      if constexpr (T::bytes == 4) {
+        *reinterpret_cast<float4*>(p + 4 * q) =
+            make_float4(u[q] * alpha, u[q + 1] * alpha, u[q + 2] * alpha, u[q + 3] * alpha);
+      } else {
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          w[j] = static_cast<uint32_t>(T::to_bits(u[q + 2 * j] * alpha)) |
+                 (static_cast<uint32_t>(T::to_bits(u[q + 2 * j + 1] * alpha)) << 16);
+        *reinterpret_cast<uint4*>(p + 2 * q) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < N; ++q)
+      if (q < nvalid) T::store(base, off + q, u[q] * alpha);
+  }
+}
+
 // ---------------------------------------------------------------- butterflies
 // In-register stages of the unnormalized Walsh-Hadamard transform on N values that are N
 // consecutive elements of a k-block: stride h pairs (i, i+h) -> (a+b, a-b), for h < min(K, N).

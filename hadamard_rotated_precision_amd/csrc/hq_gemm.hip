@@ -1,18 +1,36 @@
-// hq_gemm.hip — INT8 x INT8 -> INT32 GEMM on gfx950 matrix cores, with a fused dequantizing
-// epilogue ("Training Transformers with 4-bit Integers", §3.1: the integer product is
-// accumulated in INT32 and dequantized back to floating point; §A.6: the integer GEMM reads
-// both operands contiguous along K).
+// hq_gemm.hip — INT8 x INT8 -> INT32 GEMM on gfx950 matrix cores with a fused epilogue that
+// dequantizes, applies the output-side inverse Walsh-Hadamard rotations and stores.
 //
-// c[m][n] = sum_k a[m][k] * b[n][k]; a is M x K and b is N x K, both K-contiguous int8.
-// Design for CDNA4:
-//   - 256 x 256 output tile per workgroup, 4 wave64s in a 2 x 2 grid, 128 x 128 per wave built
-//     from 4 x 4 blocks of v_mfma_i32_32x32x32_i8 (int32 accumulators, 256 per lane);
-//   - K advances 64 bytes per step through a double-buffered LDS stage (2 x 32 KB); global
-//     loads for step t+1 are issued before the MFMAs of step t;
+// "Training Transformers with 4-bit Integers", §3.1 (integer product accumulated in INT32,
+// dequantized back to floating point), §3.3 (the block-diagonal H_k transforms cancel, so the
+// output side multiplies by H_k once more per rotated axis), §A.6 (HQ-MM stages; the integer
+// GEMM reads both operands contiguous along K).
+//
+// c[m][n] = sum_k a[m][k] * b[n][k];  a: M x K, b: N x K, int8, K-contiguous.
+//
+// Main loop (CDNA4):
+//   - workgroup tile 256 x BN (BN = 256 or 128) from waves of 128 x 64 in a 2 x (BN/64) grid
+//     (8 or 4 wave64s), each built from 2 x 4 v_mfma_i32_32x32x32_i8 tiles with 128 int32
+//     accumulators in AGPRs, so two waves share each SIMD and one wave's LDS and memory waits
+//     are covered by the other's MFMAs;
+//   - K advances 64 bytes per step through three LDS buffers with one barrier per step; global
+//     loads run three steps ahead through two register stages, and the first fragments of the
+//     next step are read before the barrier, so the matrix pipe keeps busy across it;
 //   - LDS rows are 64 bytes; the 16-byte chunk index is XOR-swizzled with (row / 4) % 4 so the
-//     128-bit fragment reads of 16 consecutive rows hit 16 distinct bank groups;
-//   - workgroups are remapped so that consecutive tiles of a group land on one XCD (blocks are
-//     dispatched round-robin over the 8 XCDs) and tiles of a group share A rows in its L2.
+//     128-bit fragment reads of 16 consecutive rows touch 16 distinct bank groups;
+//   - workgroups are remapped so consecutive tiles land on one XCD (blocks are dispatched
+//     round-robin over the 8 XCDs) and a group of tiles shares A rows in that XCD's L2.
+//
+// Epilogue (EPI_OUT): acc -> fp32, then
+//   - rotation along M (rows) in registers: in the 32x32 accumulator layout a lane holds 16 rows
+//     of each of its 4 row blocks, so row bits 0,1,3,4 (register index) and 5,6 (block index) are
+//     in-lane butterflies, bit 2 is the lane half (v_permlane32_swap), bit 7 is the wave row
+//     (done in the LDS phase below);
+//   - the tile is staged through LDS 64 rows at a time (rows x and x+128 of the tile together,
+//     so the bit-7 butterfly is local), where the column rotation (along N) and the cast to the
+//     output dtype happen in a row-contiguous thread layout, and stores are coalesced; TRANS
+//     mode stores the transpose (the caller computes the transposed product when only the
+//     rows need rotating, which keeps that rotation in registers).
 #include "hq_device.hpp"
 #include "hq_internal.hpp"
 
@@ -21,9 +39,10 @@ namespace hq {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int GBM = 256, GBN = 256, GBK = 64;
-constexpr int kGemmThreads = 256;
+constexpr int GBM = 256, GBK = 64;
 constexpr int kGroupM = 8;
+constexpr int kBufferFlags = 0x00020000;   // raw untyped buffer, 32-bit records
+constexpr int kOutOfRange = 0x7FFFFFF0;    // an offset past any descriptor: the load reads 0
 
 struct GemmArgs {
   const int8_t* a;
@@ -42,12 +61,101 @@ __device__ inline int lds_off(int row, int chunk) {
   return row * GBK + ((chunk ^ ((row >> 2) & 3)) << 4);
 }
 
-template <class Out, int EPI>
-__global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) int8_t smem[2][(GBM + GBN) * GBK];
+// In-register butterflies along the tile's M axis for row bits 0,1,3,4 (register index) and
+// 5,6 (row-block index), restricted to strides < KM. v[bi][bj][r]: row = 32*bi + 8*(r/4) +
+// 4*(lane/32) + r%4 within the wave's 128 rows.
+template <int KM, int NB>
+__device__ inline void rows_fwht_inlane(float (&v)[4][NB][16]) {
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < NB; ++bj) {
+      // row strides 1, 2 <- register bits 0, 1; row strides 8, 16 <- register bits 2, 3
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const int stride = (rb < 2) ? (1 << rb) : (8 << (rb - 2));
+        if (stride < KM) {
+          const int h = 1 << rb;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if ((r & h) == 0) {
+              float a = v[bi][bj][r], b = v[bi][bj][r + h];
+              v[bi][bj][r] = a + b;
+              v[bi][bj][r + h] = a - b;
+            }
+        }
+      }
+    }
+  // row strides 32, 64 <- block bits 0, 1
+#pragma unroll
+  for (int hb = 1; hb <= 2; hb <<= 1) {
+    if (32 * hb < KM) {
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi)
+        if ((bi & hb) == 0)
+#pragma unroll
+          for (int bj = 0; bj < NB; ++bj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              float a = v[bi][bj][r], b = v[bi + hb][bj][r];
+              v[bi][bj][r] = a + b;
+              v[bi + hb][bj][r] = a - b;
+            }
+    }
+  }
+}
+
+// Row stride 4 <- lane bit 5: the pair lives in lanes l and l^32.
+template <int NB>
+__device__ inline void rows_fwht_lanehalf(float (&v)[4][NB][16], int lane) {
+  const float sgn = (lane & 32) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < NB; ++bj)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const unsigned x = __float_as_uint(v[bi][bj][r]);
+        // after the swap: .x = value of the lower lane of the pair, .y = of the upper lane
+        auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        const float lo = __uint_as_float(p[0]), hi = __uint_as_float(p[1]);
+        v[bi][bj][r] = __builtin_fmaf(hi, sgn, lo);   // lower lane: lo+hi, upper: lo-hi
+      }
+}
+
+// Butterfly stages over lanes l ^ m (m = 1, 2, 4) for N values.
+template <int N>
+__device__ inline void xlane_stage(float (&v)[N], int lane, int m) {
+  const bool upper = (lane & m) != 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    float p = __shfl_xor(v[i], m, 64);
+    v[i] = upper ? (p - v[i]) : (v[i] + p);
+  }
+}
+
+// Threads of a workgroup for a 256 x BN tile: waves of 128 x 64 in a 2 x (BN/64) grid.
+template <int BN> struct GemmShape {
+  static constexpr int NW = 2 * (BN / 64);
+  static constexpr int NT = 64 * NW;
+};
+
+template <int BN, class Out, int EPI, int KM, int KN, bool TRANS>
+__global__ __launch_bounds__(GemmShape<BN>::NT, 512 / GemmShape<BN>::NT) void gemm_i8_kernel(GemmArgs g) {
+  constexpr int NT = GemmShape<BN>::NT;   // 256 (BN=128) or 512 (BN=256): two waves per SIMD
+  constexpr int WN = 64;              // wave tile columns
+  constexpr int NB = WN / 32;         // 32x32 blocks per wave along N
+  constexpr int WCOLS = BN / WN;      // waves along N
+  constexpr int A_BYTES = GBM * GBK, B_BYTES = BN * GBK, STAGE = A_BYTES + B_BYTES;
+  constexpr int ALD = GBM * 4 / NT;   // 16-byte A chunks loaded per thread per step
+  constexpr int BLD = BN * 4 / NT;    // 16-byte B chunks loaded per thread per step
+  constexpr int EP = BN + 4;          // epilogue LDS row pitch (floats)
+  constexpr int EPI_BYTES = 64 * EP * 4;
+  constexpr int LDS_BYTES = (3 * STAGE > EPI_BYTES) ? 3 * STAGE : EPI_BYTES;
+  __shared__ __attribute__((aligned(16))) int8_t smem[LDS_BYTES];
 
   const int tiles_m = static_cast<int>((g.M + GBM - 1) / GBM);
-  const int tiles_n = static_cast<int>((g.N + GBN - 1) / GBN);
+  const int tiles_n = static_cast<int>((g.N + BN - 1) / BN);
   const int ntiles = tiles_m * tiles_n;
   int pid = blockIdx.x;
   if ((ntiles & 7) == 0) pid = (pid & 7) * (ntiles >> 3) + (pid >> 3);   // XCD-contiguous
@@ -56,124 +164,299 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_i8_kernel(GemmArgs g) {
   const int gsize = min(tiles_m - first_m, kGroupM);
   const int tm = first_m + (pid % (kGroupM * tiles_n)) % gsize;
   const int tn = (pid % (kGroupM * tiles_n)) / gsize;
-  const int64_t m0 = static_cast<int64_t>(tm) * GBM, n0 = static_cast<int64_t>(tn) * GBN;
+  const int64_t m0 = static_cast<int64_t>(tm) * GBM, n0 = static_cast<int64_t>(tn) * BN;
 
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / WCOLS, wn = w % WCOLS;
 
-  v16i acc[4][4];
+  v16i acc[4][NB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
   const int KT = static_cast<int>((g.K + GBK - 1) / GBK);
-  v4i stage[8];
-
-  auto load_tile = [&](int kt) {
-    const int64_t k0 = static_cast<int64_t>(kt) * GBK;
+  // Global loads are raw buffer loads from a descriptor rebased at this tile's first row:
+  // offsets past the tile's valid rows (or the sentinel used past K) read as zero, so edge
+  // tiles need no branches and the compiler can track each load's wait count exactly.
+  const int rows_a = static_cast<int>(min<int64_t>(GBM, g.M - m0));
+  const int rows_b = static_cast<int>(min<int64_t>(BN, g.N - n0));
+  const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(g.a + m0 * g.lda), 0, static_cast<int>(rows_a * g.lda), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(g.b + n0 * g.ldb), 0, static_cast<int>(rows_b * g.ldb), kBufferFlags);
+  int oa[ALD], ob[BLD], la[ALD], lb[BLD];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int q = t + kGemmThreads * j;
-      const int row = q >> 2, ch = q & 3;
-      const int64_t kk = k0 + 16 * ch;
-      const int64_t ga = m0 + row, gb = n0 + row;
-      v4i za = {0, 0, 0, 0}, zb = {0, 0, 0, 0};
-      if (ga < g.M && kk < g.K) za = *reinterpret_cast<const v4i*>(g.a + ga * g.lda + kk);
-      if (gb < g.N && kk < g.K) zb = *reinterpret_cast<const v4i*>(g.b + gb * g.ldb + kk);
-      stage[j] = za;
-      stage[4 + j] = zb;
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int q = t + kGemmThreads * j;
-      const int row = q >> 2, ch = q & 3;
-      *reinterpret_cast<v4i*>(&smem[buf][lds_off(row, ch)]) = stage[j];
-      *reinterpret_cast<v4i*>(&smem[buf][GBM * GBK + lds_off(row, ch)]) = stage[4 + j];
-    }
-  };
-
-  if (KT > 0) {
-    load_tile(0);
-    store_tile(0);
+  for (int j = 0; j < ALD; ++j) {
+    const int q = t + NT * j, row = q >> 2, ch = q & 3;
+    oa[j] = row * static_cast<int>(g.lda) + 16 * ch;
+    la[j] = lds_off(row, ch);
   }
-  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < BLD; ++j) {
+    const int q = t + NT * j, row = q >> 2, ch = q & 3;
+    ob[j] = row * static_cast<int>(g.ldb) + 16 * ch;
+    lb[j] = A_BYTES + lds_off(row, ch);
+  }
+  const int kch = 16 * (t & 3);   // k offset of this thread's chunk within a step
 
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) load_tile(kt + 1);
-    const int8_t* sa = smem[cur];
-    const int8_t* sb = smem[cur] + GBM * GBK;
+  v4i ra[2][ALD], rb[2][BLD];
+  auto load = [&](int kt, v4i (&xa)[ALD], v4i (&xb)[BLD]) {
+    const int k0 = kt * GBK;
+    const bool kin = (k0 + kch) < g.K;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int ch = 2 * ks + (lane >> 5);
-      v4i af[4], bf[4];
+    for (int j = 0; j < ALD; ++j)
+      xa[j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                                          rsa, kin ? oa[j] + k0 : kOutOfRange, 0, 0));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wm * 128 + i * 32 + (lane & 31);
-        af[i] = *reinterpret_cast<const v4i*>(sa + lds_off(row, ch));
+    for (int j = 0; j < BLD; ++j)
+      xb[j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                                          rsb, kin ? ob[j] + k0 : kOutOfRange, 0, 0));
+  };
+  auto store = [&](int buf, const v4i (&xa)[ALD], const v4i (&xb)[BLD]) {
+    int8_t* s = smem + buf * STAGE;
+#pragma unroll
+    for (int j = 0; j < ALD; ++j) *reinterpret_cast<v4i*>(s + la[j]) = xa[j];
+#pragma unroll
+    for (int j = 0; j < BLD; ++j) *reinterpret_cast<v4i*>(s + lb[j]) = xb[j];
+  };
+  // fragment registers: two sets (ping-pong between the two 32-byte halves of a K step)
+  v4i af[2][4], bf[2][NB];
+  auto frag = [&](int set, int buf, int ks) {
+    const int8_t* sa = smem + buf * STAGE;
+    const int8_t* sb = sa + A_BYTES;
+    const int ch = 2 * ks + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      af[set][i] = *reinterpret_cast<const v4i*>(sa + lds_off(wm * 128 + i * 32 + (lane & 31), ch));
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      bf[set][j] = *reinterpret_cast<const v4i*>(sb + lds_off(wn * WN + j * 32 + (lane & 31), ch));
+  };
+  auto mfma = [&](int set) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[set][i], bf[set][j], acc[i][j], 0, 0, 0);
+  };
+
+  // Pipeline: three LDS buffers, one barrier per K step.
+  //   At the start of step k, buffers k%3 and (k+1)%3 hold steps k and k+1 (visible), the
+  //   registers of stage (k+1)%2 hold the in-flight loads of step k+2, and fragment set 0 holds
+  //   step k's first half. Step k: issue the loads of step k+3 into stage k%2; read step k's
+  //   second half into set 1; MFMAs on set 0; read step k+1's first half into set 0 (its buffer
+  //   became visible at this step's barrier); MFMAs on set 1; write stage (k+1)%2 (step k+2)
+  //   into buffer (k+2)%3, which nobody reads any more; barrier.
+  // Loads and stores are unconditional: steps past K load zeros (out-of-range offsets), so
+  // every wait counts only the loads it needs.
+  auto step = [&](int k, v4i (&xa_new)[ALD], v4i (&xb_new)[BLD], const v4i (&xa_old)[ALD],
+                  const v4i (&xb_old)[BLD], int b0, int b1, int b2) {
+    load(k + 3, xa_new, xb_new);
+    frag(1, b0, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma(0);
+    __builtin_amdgcn_sched_barrier(0);
+    frag(0, b1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma(1);
+    __builtin_amdgcn_sched_barrier(0);
+    store(b2, xa_old, xb_old);
+    __syncthreads();
+  };
+
+  load(0, ra[0], rb[0]);
+  load(1, ra[1], rb[1]);
+  store(0, ra[0], rb[0]);
+  store(1, ra[1], rb[1]);
+  load(2, ra[1], rb[1]);
+  __syncthreads();
+  frag(0, 0, 0);
+  // unrolled by two so the register stage is static; an odd last step is peeled after the
+  // loop (the two-step body is unconditional, which keeps the accumulators in AGPRs)
+  int kt = 0, b0 = 0, b1 = 1, b2 = 2;
+  for (; kt + 1 < KT; kt += 2) {
+    step(kt, ra[0], rb[0], ra[1], rb[1], b0, b1, b2);
+    step(kt + 1, ra[1], rb[1], ra[0], rb[0], b1, b2, b0);
+    const int t0 = b0;   // advance the buffer rotation by two
+    b0 = b2;
+    b2 = b1;
+    b1 = t0;
+  }
+  if (kt < KT) {
+    frag(1, b0, 1);
+    mfma(0);
+    mfma(1);
+  }
+
+  if constexpr (EPI == EPI_I32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int64_t col = n0 + wn * WN + j * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          if (row < g.M && col < g.N) static_cast<int32_t*>(g.c)[row * g.ldc + col] = acc[i][j][r];
+        }
       }
+    return;
+  } else {
+    const float alpha = (*g.sa * *g.sb) * g.kmul;
+    // one 32-column block at a time: int32 -> fp32, row rotation in registers, and back into
+    // the accumulator registers as fp32 bit patterns (keeps the live set at one slice)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = wn * 128 + j * 32 + (lane & 31);
-        bf[j] = *reinterpret_cast<const v4i*>(sb + lds_off(row, ch));
+    for (int j = 0; j < NB; ++j) {
+      float v[4][1][16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[i][0][r] = static_cast<float>(acc[i][j][r]);
+      if constexpr (KM > 1) {
+        rows_fwht_inlane<KM, 1>(v);
+        if constexpr (KM > 4) rows_fwht_lanehalf<1>(v, lane);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = __float_as_int(v[i][0][r]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (kt + 1 < KT) store_tile(cur ^ 1);
-    __syncthreads();
-  }
-
-  // Epilogue. 32x32 accumulator layout: lane holds column (lane % 32) and, in register r,
-  // row 8*(r/4) + 4*(lane/32) + r%4 of its block.
-  float alpha = 1.0f;
-  if constexpr (EPI == EPI_SCALE) alpha = (*g.sa * *g.sb) * g.kmul;
+    float* ep = reinterpret_cast<float*>(smem);
+    // 4 chunks: chunk c holds tile rows 32c..32c+31 (local 0..31, wave row 0) and
+    // 128+32c..128+32c+31 (local 32..63, wave row 1)
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int c = 0; c < 4; ++c) {
+      __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = n0 + wn * 128 + j * 32 + (lane & 31);
+      for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row < g.M && col < g.N) {
-          if constexpr (EPI == EPI_I32) {
-            static_cast<int32_t*>(g.c)[row * g.ldc + col] = acc[i][j][r];
-          } else {
-            Out::store(g.c, row * g.ldc + col, static_cast<float>(acc[i][j][r]) * alpha);
+        for (int r = 0; r < 16; ++r) {
+          const int lr = wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          ep[lr * EP + wn * WN + j * 32 + (lane & 31)] = __int_as_float(acc[c][j][r]);
+        }
+      __syncthreads();
+      if constexpr (!TRANS) {
+        // thread: local row pair (x, x+32), columns [s*BN/8, (s+1)*BN/8)
+        constexpr int TPR = NT / 32;              // threads per row pair (8 or 16)
+        constexpr int SEG = BN / TPR;             // 16 columns each
+        const int x = t / TPR, s = t % TPR;
+        float u0[SEG], u1[SEG];
+#pragma unroll
+        for (int q = 0; q < SEG; q += 4) {
+          const float4 a0 = *reinterpret_cast<const float4*>(&ep[x * EP + s * SEG + q]);
+          const float4 a1 = *reinterpret_cast<const float4*>(&ep[(x + 32) * EP + s * SEG + q]);
+          u0[q] = a0.x; u0[q + 1] = a0.y; u0[q + 2] = a0.z; u0[q + 3] = a0.w;
+          u1[q] = a1.x; u1[q + 1] = a1.y; u1[q + 2] = a1.z; u1[q + 3] = a1.w;
+        }
+        if constexpr (KM > 128) {
+#pragma unroll
+          for (int q = 0; q < SEG; ++q) {
+            const float a = u0[q], b = u1[q];
+            u0[q] = a + b;
+            u1[q] = a - b;
           }
+        }
+        if constexpr (KN > 1) {
+          fwht_inreg<KN, SEG>(u0);
+          fwht_inreg<KN, SEG>(u1);
+#pragma unroll
+          for (int m = 1; SEG * m < KN; m <<= 1) {
+            xlane_stage<SEG>(u0, lane, m);
+            xlane_stage<SEG>(u1, lane, m);
+          }
+        }
+        const int64_t r0 = m0 + 32 * c + x, r1 = m0 + 128 + 32 * c + x;
+        const int64_t cb = n0 + s * SEG;
+        if (r0 < g.M) store_run<Out, SEG>(g.c, r0 * g.ldc + cb, g.N - cb, u0, alpha);
+        if (r1 < g.M) store_run<Out, SEG>(g.c, r1 * g.ldc + cb, g.N - cb, u1, alpha);
+      } else {
+        // transposed store: thread owns tile column j; output row n0+j, columns m (tile rows)
+        constexpr int TPC = NT / BN;                // threads per column (2)
+        constexpr int RPT = 32 / TPC;               // rows per thread in each half
+        const int j = t / TPC, h = t % TPC;
+        float u0[RPT], u1[RPT];
+#pragma unroll
+        for (int q = 0; q < RPT; ++q) {
+          u0[q] = ep[(h * RPT + q) * EP + j];
+          u1[q] = ep[(32 + h * RPT + q) * EP + j];
+        }
+        if constexpr (KM > 128) {
+#pragma unroll
+          for (int q = 0; q < RPT; ++q) {
+            const float a = u0[q], b = u1[q];
+            u0[q] = a + b;
+            u1[q] = a - b;
+          }
+        }
+        const int64_t orow = n0 + j;
+        const int64_t c0 = m0 + 32 * c + h * RPT, c1 = m0 + 128 + 32 * c + h * RPT;
+        if (orow < g.N) {
+          store_run<Out, RPT>(g.c, orow * g.ldc + c0, g.M - c0, u0, alpha);
+          store_run<Out, RPT>(g.c, orow * g.ldc + c1, g.M - c1, u1, alpha);
         }
       }
     }
+  }
 }
 
-template <class Out, int EPI>
-static hipError_t launch_gemm(const GemmArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_i8_kernel<Out, EPI>), dim3(grid), dim3(kGemmThreads), 0, st, a);
+template <int BN, class Out, int EPI, int KM, int KN, bool TRANS>
+static hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
+  const int64_t tiles = ((a.M + GBM - 1) / GBM) * ((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_i8_kernel<BN, Out, EPI, KM, KN, TRANS>), dim3(static_cast<int>(tiles)),
+                     dim3(GemmShape<BN>::NT), 0, st, a);
   return hipGetLastError();
+}
+
+template <int BN, class Out>
+static hipError_t launch_out(const GemmPass& p, const GemmArgs& a, hipStream_t st) {
+  if (p.trans_out) {
+    switch (p.km) {
+#define HQ_T(KK) case KK: return launch_gemm<BN, Out, EPI_SCALE, KK, 1, true>(a, st);
+      HQ_T(1) HQ_T(2) HQ_T(4) HQ_T(8) HQ_T(16) HQ_T(32) HQ_T(64) HQ_T(128) HQ_T(256)
+#undef HQ_T
+    }
+    return hipErrorInvalidValue;
+  }
+  if (p.km == 1 && p.kn == 1) return launch_gemm<BN, Out, EPI_SCALE, 1, 1, false>(a, st);
+  if (p.km != p.kn) return hipErrorInvalidValue;
+  if constexpr (BN == 256) {
+    switch (p.km) {
+#define HQ_B(KK) case KK: return launch_gemm<BN, Out, EPI_SCALE, KK, KK, false>(a, st);
+      HQ_B(2) HQ_B(4) HQ_B(8) HQ_B(16) HQ_B(32) HQ_B(64) HQ_B(128) HQ_B(256)
+#undef HQ_B
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t gemm_pass(const GemmPass& p, hipStream_t st) {
   GemmArgs a{p.a, p.lda, p.b, p.ldb, p.M, p.N, p.K, p.c, p.ldc, p.sa, p.sb, p.kmul};
-  const int64_t tiles = ((p.M + GBM - 1) / GBM) * ((p.N + GBN - 1) / GBN);
-  if (tiles == 0) return hipSuccess;
-  const int grid = static_cast<int>(tiles);
-  if (p.epi == EPI_I32) return launch_gemm<F32, EPI_I32>(a, grid, st);
-  switch (p.out_dt) {
-    case DT_F32: return launch_gemm<F32, EPI_SCALE>(a, grid, st);
-    case DT_F16: return launch_gemm<F16, EPI_SCALE>(a, grid, st);
-    case DT_BF16: return launch_gemm<BF16, EPI_SCALE>(a, grid, st);
+  if (p.M == 0 || p.N == 0) return hipSuccess;
+  // a tile's rows must be addressable by 32-bit buffer offsets
+  if (static_cast<int64_t>(GBM) * p.lda >= kOutOfRange || 256 * p.ldb >= kOutOfRange)
+    return hipErrorInvalidValue;
+  // 256-wide tiles unless that leaves most CUs idle and no column rotation needs the width
+  const int64_t tiles256 = ((p.M + GBM - 1) / GBM) * ((p.N + 255) / 256);
+  const bool narrow = p.kn <= 1 && tiles256 < 256;
+  const int tok = prof_begin(K_GEMM, 2.0 * p.M * p.N * p.K, st);
+  hipError_t e = hipErrorInvalidValue;
+  if (p.epi == EPI_I32) {
+    e = narrow ? launch_gemm<128, F32, EPI_I32, 1, 1, false>(a, st)
+               : launch_gemm<256, F32, EPI_I32, 1, 1, false>(a, st);
+  } else {
+    switch (p.out_dt) {
+      case DT_F32: e = narrow ? launch_out<128, F32>(p, a, st) : launch_out<256, F32>(p, a, st); break;
+      case DT_F16: e = narrow ? launch_out<128, F16>(p, a, st) : launch_out<256, F16>(p, a, st); break;
+      case DT_BF16: e = narrow ? launch_out<128, BF16>(p, a, st) : launch_out<256, BF16>(p, a, st); break;
+    }
   }
-  return hipErrorInvalidValue;
+  prof_end(tok, st);
+  return e;
 }
 
 }  // namespace hq

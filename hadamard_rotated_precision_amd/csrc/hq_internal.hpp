@@ -75,7 +75,16 @@ struct GemmPass {
   const float* sa = nullptr;   // EPI_SCALE: alpha = (*sa * *sb) * kmul
   const float* sb = nullptr;
   float kmul = 1.0f;
+  int km = 1;              // EPI_SCALE: inverse rotation block along M (rows), 1 = none
+  int kn = 1;              // EPI_SCALE: along N (columns); km == kn when both are set
+  bool trans_out = false;  // EPI_SCALE: store c^T (N x M, pitch ldc); requires kn == 1
 };
 hipError_t gemm_pass(const GemmPass& p, hipStream_t st);
+
+// Launch instrumentation (hq_profile.cpp): returns a token, or -1 when not recording.
+int prof_begin(int kind, double units, hipStream_t st);
+void prof_end(int token, hipStream_t st);
+enum Kind : int { K_GEMM = 0, K_ROT_ABSMAX = 1, K_ROT_QUANT = 2, K_ROT_STORE = 3,
+                  K_TRANSPOSE = 4, K_MISC = 5 };
 
 }  // namespace hq

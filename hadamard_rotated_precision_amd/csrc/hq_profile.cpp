@@ -1,0 +1,97 @@
+// hq_profile.cpp — optional launch instrumentation of libhq: when enabled for a set of kernel
+// kinds, each launch of those kinds is bracketed by two HIP events recorded on the launch's
+// own stream, and its algorithmic work (ops for the GEMM, bytes for streaming kernels) is
+// recorded with it. Nothing is recorded while disabled (the default).
+#include "../../include/hq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <vector>
+
+#include "hq_internal.hpp"
+
+namespace hq {
+namespace {
+
+struct Rec {
+  int kind;
+  double units;
+  hipEvent_t a, b;
+};
+
+std::mutex g_mu;
+bool g_on = false;
+uint32_t g_mask = 0;
+std::vector<Rec> g_recs;
+std::vector<hipEvent_t> g_pool;
+size_t g_next = 0;
+
+hipEvent_t take_event() {
+  if (g_next == g_pool.size()) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    g_pool.push_back(e);
+  }
+  return g_pool[g_next++];
+}
+
+}  // namespace
+
+int prof_begin(int kind, double units, hipStream_t st) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_on || !(g_mask & (1u << kind))) return -1;
+  Rec r{kind, units, take_event(), take_event()};
+  if (!r.a || !r.b || hipEventRecord(r.a, st) != hipSuccess) return -1;
+  g_recs.push_back(r);
+  return static_cast<int>(g_recs.size() - 1);
+}
+
+void prof_end(int idx, hipStream_t st) {
+  if (idx < 0) return;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (idx < static_cast<int>(g_recs.size())) hipEventRecord(g_recs[idx].b, st);
+}
+
+}  // namespace hq
+
+extern "C" {
+
+hq_status hq_profile_start(uint32_t kind_mask) {
+  std::lock_guard<std::mutex> lk(hq::g_mu);
+  hq::g_recs.clear();
+  hq::g_next = 0;
+  hq::g_mask = kind_mask;
+  hq::g_on = kind_mask != 0;
+  return HQ_OK;
+}
+
+hq_status hq_profile_stop(hq_profile_stat* stats, int32_t n_stats) {
+  std::lock_guard<std::mutex> lk(hq::g_mu);
+  hq::g_on = false;
+  if (!stats && n_stats > 0) return HQ_ERR_NULL;
+  for (int32_t i = 0; i < n_stats; ++i) {
+    stats[i].kind = i;
+    stats[i].count = 0;
+    stats[i].total_ms = 0.0;
+    stats[i].units = 0.0;
+  }
+  hq_status st = HQ_OK;
+  for (const auto& r : hq::g_recs) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
+      st = HQ_ERR_LAUNCH;
+      continue;
+    }
+    if (r.kind < n_stats) {
+      stats[r.kind].count += 1;
+      stats[r.kind].total_ms += ms;
+      stats[r.kind].units += r.units;
+    }
+  }
+  hq::g_recs.clear();
+  hq::g_next = 0;
+  return st;
+}
+
+}  // extern "C"

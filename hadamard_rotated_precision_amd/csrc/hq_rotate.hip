@@ -363,12 +363,25 @@ hipError_t rows_pass(const RowPass& p, hipStream_t st) {
   const int64_t items = p.rows * ((p.cols + 255) / 256) * 16;   // lanes of work
   int grid = (p.op == OP_ABSMAX) ? grid_for(items, kThreads, kMaxPartials)
                                  : grid_for(items, kThreads, 1 << 20);
+  const double in_b = static_cast<double>(p.rows) * p.cols * dt_bytes(p.in_dt);
+  hipError_t e = hipErrorInvalidValue;
+  int tok;
   switch (p.op) {
-    case OP_ABSMAX: return dispatch_rows<OP_ABSMAX>(p.in_dt, DT_F32, p.k, a, grid, st);
-    case OP_QUANT: return dispatch_rows<OP_QUANT>(p.in_dt, DT_F32, p.k, a, grid, st);
-    case OP_STORE: return dispatch_rows<OP_STORE>(p.in_dt, p.out_dt, p.k, a, grid, st);
+    case OP_ABSMAX:
+      tok = prof_begin(K_ROT_ABSMAX, in_b, st);
+      e = dispatch_rows<OP_ABSMAX>(p.in_dt, DT_F32, p.k, a, grid, st);
+      break;
+    case OP_QUANT:
+      tok = prof_begin(K_ROT_QUANT, in_b + static_cast<double>(p.rows) * p.cols, st);
+      e = dispatch_rows<OP_QUANT>(p.in_dt, DT_F32, p.k, a, grid, st);
+      break;
+    default:
+      tok = prof_begin(K_ROT_STORE, in_b + static_cast<double>(p.rows) * p.cols * dt_bytes(p.out_dt), st);
+      e = dispatch_rows<OP_STORE>(p.in_dt, p.out_dt, p.k, a, grid, st);
+      break;
   }
-  return hipErrorInvalidValue;
+  prof_end(tok, st);
+  return e;
 }
 
 int rows_pass_grid(const RowPass& p) {
@@ -397,12 +410,25 @@ hipError_t cols_pass(const ColPass& p, hipStream_t st) {
   const int nc = cols_tile_cols(p.k);
   const int64_t tiles = (p.rows / p.k) * ((p.cols + nc - 1) / nc);
   int grid = (p.op == OP_ABSMAX) ? grid_for(tiles, 1, kMaxPartials) : grid_for(tiles, 1, 1 << 20);
+  const double in_b = static_cast<double>(p.rows) * p.cols * dt_bytes(p.in_dt);
+  hipError_t e = hipErrorInvalidValue;
+  int tok;
   switch (p.op) {
-    case OP_ABSMAX: return dispatch_cols<OP_ABSMAX>(p.in_dt, DT_F32, p.k, a, grid, st);
-    case OP_QUANT: return dispatch_cols<OP_QUANT>(p.in_dt, DT_F32, p.k, a, grid, st);
-    case OP_STORE: return dispatch_cols<OP_STORE>(p.in_dt, p.out_dt, p.k, a, grid, st);
+    case OP_ABSMAX:
+      tok = prof_begin(K_ROT_ABSMAX, in_b, st);
+      e = dispatch_cols<OP_ABSMAX>(p.in_dt, DT_F32, p.k, a, grid, st);
+      break;
+    case OP_QUANT:
+      tok = prof_begin(K_ROT_QUANT, in_b + static_cast<double>(p.rows) * p.cols, st);
+      e = dispatch_cols<OP_QUANT>(p.in_dt, DT_F32, p.k, a, grid, st);
+      break;
+    default:
+      tok = prof_begin(K_ROT_STORE, in_b + static_cast<double>(p.rows) * p.cols * dt_bytes(p.out_dt), st);
+      e = dispatch_cols<OP_STORE>(p.in_dt, p.out_dt, p.k, a, grid, st);
+      break;
   }
-  return hipErrorInvalidValue;
+  prof_end(tok, st);
+  return e;
 }
 
 int cols_pass_grid(const ColPass& p) {
@@ -417,8 +443,10 @@ hipError_t transpose_i8(const int8_t* src, int64_t ld_src, int8_t* dst, int64_t 
   const int64_t tiles = ((rpad + 63) / 64) * ((cols + 63) / 64);
   if (tiles == 0) return hipSuccess;
   const int grid = grid_for(tiles, 1, 1 << 20);
+  const int tok = prof_begin(K_TRANSPOSE, 2.0 * rows * cols, st);
   hipLaunchKernelGGL(transpose_i8_kernel, dim3(grid), dim3(kThreads), 0, st, src, ld_src, dst,
                      ld_dst, rows, cols);
+  prof_end(tok, st);
   return hipGetLastError();
 }
 
@@ -426,12 +454,16 @@ hipError_t zero_pad(int8_t* p, int64_t nrows, int64_t ld, int64_t from, int64_t 
                     hipStream_t st) {
   if (to <= from || nrows == 0) return hipSuccess;
   const int grid = grid_for(nrows * (to - from), kThreads, 4096);
+  const int tok = prof_begin(K_MISC, static_cast<double>(nrows) * (to - from), st);
   hipLaunchKernelGGL(zero_pad_kernel, dim3(grid), dim3(kThreads), 0, st, p, nrows, ld, from, to);
+  prof_end(tok, st);
   return hipGetLastError();
 }
 
 hipError_t write_scale(float* scale, const float* step, hipStream_t st) {
+  const int tok = prof_begin(K_MISC, 4.0, st);
   hipLaunchKernelGGL(write_scale_kernel, dim3(1), dim3(1), 0, st, scale, step);
+  prof_end(tok, st);
   return hipGetLastError();
 }
 

@@ -193,6 +193,34 @@ hq_status hq_fwht(const void *src, int32_t src_dtype, void *dst, int32_t dst_dty
 hq_status hq_gemm_i8_i32(const int8_t *a, int64_t lda, const int8_t *b_t, int64_t ldb,
                          int32_t *c, int64_t M, int64_t N, int64_t K, void *stream);
 
+/* ---------------------------------------------------------------- instrumentation
+ * Optional timing of the library's own kernel launches, for benchmarks (no compute).
+ * hq_profile_start(mask) enables recording for the kernel kinds whose bit (1 << kind) is set:
+ * each such launch is bracketed by two HIP events recorded on its own stream, together with
+ * its algorithmic work in `units` (GEMM: 2*M*N*K integer ops; streaming kernels: bytes read
+ * once plus bytes written once). hq_profile_stop waits for the recorded events, fills
+ * stats[kind] for kind < n_stats (count, summed event time, summed units) and disables
+ * recording. Process-wide state; not meant for concurrent use from several threads. */
+typedef enum {
+  HQ_KIND_GEMM = 0,         /* integer MFMA GEMM + dequantizing epilogue */
+  HQ_KIND_ROT_ABSMAX = 1,   /* rotation + absmax partials */
+  HQ_KIND_ROT_QUANT = 2,    /* rotation + quantization to codes */
+  HQ_KIND_ROT_STORE = 3,    /* rotation to a floating-point output (inverse rotations, hq_fwht) */
+  HQ_KIND_TRANSPOSE = 4,    /* int8 code transpose */
+  HQ_KIND_MISC = 5,         /* scale writes, padding fills */
+  HQ_KIND_COUNT = 6
+} hq_kernel_kind;
+
+typedef struct {
+  int32_t kind;
+  int32_t count;
+  double total_ms;
+  double units;
+} hq_profile_stat;
+
+hq_status hq_profile_start(uint32_t kind_mask);
+hq_status hq_profile_stop(hq_profile_stat *stats, int32_t n_stats);
+
 #ifdef __cplusplus
 }
 #endif
