@@ -36,12 +36,8 @@ hq_status check_cfg(const hq_config* cfg) {
   return HQ_OK;
 }
 
-// fp32 scratch (elements) a call may need for a rows x cols tensor: the rotated values of a
-// two-sided rotation, an unfused output, or a row-major code buffer (as bytes).
-int64_t scratch_elems(int64_t rows, int64_t cols) {
-  return std::max<int64_t>(rows * cols, (rows * pitch16(cols) + 3) / 4);
-}
-size_t ws_need(int64_t elems) { return kPartialBytes + align_up(elems * sizeof(float), kAlign); }
+// Workspace: the absmax partial arrays plus one spare device float.
+size_t ws_need() { return kPartialBytes + kAlign; }
 
 hq_status check_ws(void* ws, size_t ws_bytes, size_t need) {
   if (need == 0) return HQ_OK;
@@ -52,11 +48,11 @@ hq_status check_ws(void* ws, size_t ws_bytes, size_t need) {
 
 struct Ws {
   float* part[4];
-  float* fbuf;
+  float* spare;
   explicit Ws(void* base) {
     char* b = static_cast<char*>(base);
     for (int i = 0; i < 4; ++i) part[i] = reinterpret_cast<float*>(b + i * hq::kMaxPartials * 4);
-    fbuf = reinterpret_cast<float*>(b + kPartialBytes);
+    spare = reinterpret_cast<float*>(b + kPartialBytes);
   }
 };
 
@@ -78,100 +74,83 @@ hq_status device_ok() {
     if ((expr) != hipSuccess) return HQ_ERR_LAUNCH;   \
   } while (0)
 
-// Rotate -> scale -> quantize one tensor into row-major and/or transposed codes.
+// Rotate -> scale -> quantize one tensor into row-major and/or transposed codes (one absmax
+// pass unless a step is given, then one quantize pass that writes both layouts).
 hq_status quantize_tensor(const void* src, int32_t dt, int64_t rows, int64_t cols, int32_t rot,
                           int32_t k, int32_t bits, const float* step, int8_t* codes, int64_t ld,
                           int8_t* codes_t, int64_t ld_t, float* scale, const Ws& ws,
                           int part_slot, hipStream_t st) {
-  const int qp = qmax(bits);
   if (rows * cols == 0) {   // empty tensor: scale = step (or 0); there are no codes to write
     HQ_TRY(hq::write_scale(scale, step, st));
     return HQ_OK;
   }
-  if (k == 1) rot = (rot == HQ_ROT_NONE || rot == HQ_ROT_LEFT) ? HQ_ROT_NONE : HQ_ROT_RIGHT;
-  float* part = ws.part[part_slot];
-  if (rot == HQ_ROT_NONE || rot == HQ_ROT_RIGHT) {
-    int8_t* rm = codes;
-    int64_t rm_ld = ld;
-    if (!rm) {   // only the transpose was asked for: stage row-major codes in the workspace
-      rm = reinterpret_cast<int8_t*>(ws.fbuf);
-      rm_ld = pitch16(cols);
-    }
-    RowPass p;
-    p.src = src;
-    p.in_dt = dt;
-    p.rows = rows;
-    p.cols = cols;
-    p.k = (rot == HQ_ROT_RIGHT) ? k : 1;
-    p.qp = qp;
-    int nparts = 0;
-    if (!step) {
-      p.op = hq::OP_ABSMAX;
-      p.partials = part;
-      nparts = hq::rows_pass_grid(p);
-      HQ_TRY(hq::rows_pass(p, st));
-    }
-    p.op = hq::OP_QUANT;
-    p.part_in = part;
-    p.nparts = nparts;
-    p.step = step;
+  if (k == 1) rot = HQ_ROT_NONE;
+  hq::ProPass p;
+  p.src = src;
+  p.in_dt = dt;
+  p.rows = rows;
+  p.cols = cols;
+  p.qp = qmax(bits);
+  p.partials = ws.part[part_slot];
+  p.step = step;
+  if (rot == HQ_ROT_BOTH) {
+    // the two-sided kernel also produces the right-only scale: park it in the workspace
+    p.kind = hq::PRO_BOTH;
+    p.k = k;
+    p.step2 = step;
+    p.scale_out = ws.spare;
+    p.scale_out2 = scale;
+    p.codes_t = codes_t;
+    p.ld_t = ld_t;
+    if (codes) return HQ_ERR_MODE;   // row-major codes of B V B are not produced
+  } else {
+    p.kind = (rot == HQ_ROT_LEFT) ? hq::PRO_LEFT : hq::PRO_RIGHT;
+    p.k = (rot == HQ_ROT_NONE) ? 1 : k;
     p.scale_out = scale;
-    p.codes = rm;
-    p.ld = rm_ld;
-    HQ_TRY(hq::rows_pass(p, st));
-    if (codes_t) HQ_TRY(hq::transpose_i8(rm, rm_ld, codes_t, ld_t, rows, cols, st));
+    p.codes = codes;
+    p.ld = ld;
+    p.codes_t = codes_t;
+    p.ld_t = ld_t;
+  }
+  if (!step) {
+    p.nparts = hq::pro_grid(p);
+    HQ_TRY(hq::pro_pass(p, hq::OP_ABSMAX, st));
+  }
+  HQ_TRY(hq::pro_pass(p, hq::OP_QUANT, st));
+  return HQ_OK;
+}
+
+// X under HALO-2: one pass pair writes Q(X B) row-major and Q(B X B) transposed.
+hq_status quantize_x_both(const void* src, int32_t dt, int64_t rows, int64_t cols, int32_t k,
+                          int32_t bits, const float* step_x, const float* step_xt,
+                          hq_qtensor* qx, hq_qtensor* qxt, const Ws& ws, hipStream_t st) {
+  if (rows * cols == 0) {
+    HQ_TRY(hq::write_scale(qx->scale, step_x, st));
+    HQ_TRY(hq::write_scale(qxt->scale, step_xt, st));
     return HQ_OK;
   }
-  // LEFT or BOTH: the token-axis transform writes transposed codes.
-  const void* lsrc = src;
-  int32_t ldt = dt;
-  if (rot == HQ_ROT_BOTH) {   // rotate along columns first, into fp32 scratch
-    RowPass p;
-    p.src = src;
-    p.in_dt = dt;
-    p.rows = rows;
-    p.cols = cols;
-    p.k = k;
-    p.op = hq::OP_STORE;
-    p.dst = ws.fbuf;
-    p.out_dt = HQ_F32;
-    HQ_TRY(hq::rows_pass(p, st));
-    lsrc = ws.fbuf;
-    ldt = HQ_F32;
+  hq::ProPass p;
+  p.kind = hq::PRO_BOTH;
+  p.src = src;
+  p.in_dt = dt;
+  p.rows = rows;
+  p.cols = cols;
+  p.k = k;
+  p.qp = qmax(bits);
+  p.partials = ws.part[0];
+  p.step = step_x;
+  p.step2 = step_xt;
+  p.scale_out = qx->scale;
+  p.scale_out2 = qxt->scale;
+  p.codes = qx->codes;
+  p.ld = qx->ld;
+  p.codes_t = qxt->codes_t;
+  p.ld_t = qxt->ld_t;
+  if (!step_x) {
+    p.nparts = hq::pro_grid(p);
+    HQ_TRY(hq::pro_pass(p, hq::OP_ABSMAX, st));
   }
-  int8_t* tcodes = codes_t;
-  int64_t tld = ld_t;
-  if (!tcodes) {
-    if (rot == HQ_ROT_BOTH) return HQ_ERR_NULL;   // scratch already holds the rotated values
-    tcodes = reinterpret_cast<int8_t*>(ws.fbuf);
-    tld = pitch16(rows);
-  }
-  ColPass c;
-  c.src = lsrc;
-  c.in_dt = ldt;
-  c.rows = rows;
-  c.cols = cols;
-  c.k = k;
-  c.qp = qp;
-  int nparts = 0;
-  if (!step) {
-    c.op = hq::OP_ABSMAX;
-    c.partials = part;
-    nparts = hq::cols_pass_grid(c);
-    HQ_TRY(hq::cols_pass(c, st));
-  }
-  c.op = hq::OP_QUANT;
-  c.part_in = part;
-  c.nparts = nparts;
-  c.step = step;
-  c.scale_out = scale;
-  c.codes_t = tcodes;
-  c.ld_t = tld;
-  HQ_TRY(hq::cols_pass(c, st));
-  // the token-axis transform writes columns [0, rows) of each transposed row; zero the pitch
-  // padding up to the next multiple of 16 so consumers can read whole 16-byte chunks
-  HQ_TRY(hq::zero_pad(tcodes, cols, tld, rows, pitch16(rows), st));
-  if (codes) HQ_TRY(hq::transpose_i8(tcodes, tld, codes, ld, cols, rows, st));
+  HQ_TRY(hq::pro_pass(p, hq::OP_QUANT, st));
   return HQ_OK;
 }
 
@@ -255,9 +234,7 @@ int64_t hq_code_pitch(int64_t cols) { return cols < 0 ? 0 : pitch16(cols); }
 
 size_t hq_workspace_bytes(const hq_config* cfg, int64_t N, int64_t C, int64_t D) {
   if (check_cfg(cfg) != HQ_OK || N < 0 || C < 0 || D < 0) return 0;
-  int64_t e = std::max({scratch_elems(N, C), scratch_elems(D, C), scratch_elems(N, D),
-                        scratch_elems(C, N), scratch_elems(C, D), scratch_elems(D, N)});
-  return ws_need(e);
+  return ws_need();
 }
 
 hq_status hq_rotate_quantize(const void* src, int32_t src_dtype, int64_t rows, int64_t cols,
@@ -274,7 +251,8 @@ hq_status hq_rotate_quantize(const void* src, int32_t src_dtype, int64_t rows, i
   if (rows * cols > 0 && !src) return HQ_ERR_NULL;
   HQ_CHECK(check_pitches(out, rows, cols));
   if (rot == HQ_ROT_BOTH && !out->codes_t && rows * cols > 0) return HQ_ERR_NULL;
-  HQ_CHECK(check_ws(ws, ws_bytes, ws_need(scratch_elems(rows, cols))));
+  if (rot == HQ_ROT_BOTH && out->codes && cfg->k > 1) return HQ_ERR_MODE;
+  HQ_CHECK(check_ws(ws, ws_bytes, ws_need()));
   HQ_CHECK(device_ok());
   hipStream_t st = static_cast<hipStream_t>(stream);
   Ws w(ws);
@@ -313,16 +291,21 @@ hq_status hq_linear_fwd(const void* x, const void* w, int32_t in_dtype, int64_t 
   hipStream_t st = static_cast<hipStream_t>(stream);
   Ws wsp(ws);
   const int32_t rx = x_rot(v);
-  HQ_CHECK(quantize_tensor(x, in_dtype, N, C, rx, k, cfg->bits, stepm ? step_x : nullptr,
-                           save_x->codes, save_x->ld, save_x->codes_t, save_x->ld_t,
-                           save_x->scale, wsp, 0, st));
-  fill_meta(save_x, N, C, k, cfg->bits, rx);
-  if (want_xt) {
-    HQ_CHECK(quantize_tensor(x, in_dtype, N, C, HQ_ROT_BOTH, k, cfg->bits,
-                             stepm ? step_xt : nullptr, save_xt->codes, save_xt->ld,
-                             save_xt->codes_t, save_xt->ld_t, save_xt->scale, wsp, 1, st));
-    fill_meta(save_xt, N, C, k, cfg->bits, HQ_ROT_BOTH);
+  if (want_xt && !save_x->codes_t && !save_xt->codes && k > 1) {
+    HQ_CHECK(quantize_x_both(x, in_dtype, N, C, k, cfg->bits, stepm ? step_x : nullptr,
+                             stepm ? step_xt : nullptr, save_x, save_xt, wsp, st));
+  } else {
+    HQ_CHECK(quantize_tensor(x, in_dtype, N, C, rx, k, cfg->bits, stepm ? step_x : nullptr,
+                             save_x->codes, save_x->ld, save_x->codes_t, save_x->ld_t,
+                             save_x->scale, wsp, 0, st));
+    if (want_xt)
+      HQ_CHECK(quantize_tensor(x, in_dtype, N, C, HQ_ROT_BOTH, k, cfg->bits,
+                               stepm ? step_xt : nullptr, k > 1 ? nullptr : save_xt->codes,
+                               save_xt->ld, save_xt->codes_t, save_xt->ld_t, save_xt->scale,
+                               wsp, 1, st));
   }
+  fill_meta(save_x, N, C, k, cfg->bits, rx);
+  if (want_xt) fill_meta(save_xt, N, C, k, cfg->bits, HQ_ROT_BOTH);
   HQ_CHECK(quantize_tensor(w, in_dtype, D, C, rx, k, cfg->bits, stepm ? step_w : nullptr,
                            save_w->codes, save_w->ld, save_w->codes_t, save_w->ld_t,
                            save_w->scale, wsp, 2, st));

@@ -50,6 +50,29 @@ struct ColPass {
   int out_dt = 0;
 };
 
+// Rotate -> scale -> quantize prologue (hq_prologue.hip).
+enum ProKind : int { PRO_RIGHT = 0, PRO_LEFT = 1, PRO_BOTH = 2 };
+struct ProPass {
+  int kind = PRO_RIGHT;
+  const void* src = nullptr;
+  int in_dt = 0;
+  int64_t rows = 0, cols = 0;
+  int k = 1;                         // 1 with PRO_RIGHT = no rotation
+  int qp = 127;
+  float* partials = nullptr;         // kMaxPartials floats
+  int nparts = 0;                    // QUANT: grid of the ABSMAX pass (pro_grid)
+  const float* step = nullptr;       // STEP mode (PRO_BOTH: step of X B)
+  const float* step2 = nullptr;      // PRO_BOTH, STEP mode: step of B X B
+  float* scale_out = nullptr;        // PRO_BOTH: scale of X B
+  float* scale_out2 = nullptr;       // PRO_BOTH: scale of B X B
+  int8_t* codes = nullptr;           // row-major codes (PRO_BOTH: of X B)
+  int64_t ld = 0;
+  int8_t* codes_t = nullptr;         // transposed codes (PRO_BOTH: of B X B; required)
+  int64_t ld_t = 0;
+};
+int pro_grid(const ProPass& p);
+hipError_t pro_pass(const ProPass& p, int op, hipStream_t st);
+
 hipError_t rows_pass(const RowPass& p, hipStream_t st);
 int rows_pass_grid(const RowPass& p);   // grid (= partial count) of the ABSMAX pass
 hipError_t cols_pass(const ColPass& p, hipStream_t st);

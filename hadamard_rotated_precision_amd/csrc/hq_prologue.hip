@@ -1,0 +1,465 @@
+// hq_prologue.hip — the rotate -> tensor-wise scale -> quantize prologue of HQ-MM for gfx950.
+//
+// "Training Transformers with 4-bit Integers", §3.3 (block-diagonal H_k transform before
+// quantization), §3.1 (symmetric integer grid, learned step), §A.6 (Hadamard multiplication,
+// quantization and packing before the integer GEMM; the GEMM wants K-contiguous operands, so
+// the transposed codes a backward product reads are written here rather than by a separate
+// transpose); "HALO: Hadamard-Assisted Lower-Precision Optimization for LLMs", Approach (right
+// rotation of X and W, left rotation of dY, one scale per tensor).
+//
+// Each kernel runs twice per tensor: an absmax pass (one partial max per workgroup, reduced by
+// the next pass, so no atomics and an order-independent result) and a quantize pass that
+// recomputes the rotation and writes codes. In STEP mode only the quantize pass runs.
+//
+//   right_kernel : rotation along the contiguous axis. Tile 64 rows x 256 columns; four lanes
+//                  share a row, each owning 64 consecutive columns, so strides < 64 are
+//                  in-register butterflies and strides 64, 128 are quad-lane DPP exchanges.
+//                  Transposed codes go through LDS as bytes and leave as 64-byte rows.
+//   left_kernel  : rotation along rows (the token axis). The tile (TR x 16384/TR) is staged in
+//                  LDS as fp32 with a column swizzle; a thread then owns 64 consecutive rows of
+//                  one column (in-register butterflies) and four lanes share a column.
+//   both_kernel  : X under HALO-2, 256 x 256 tiles, 512 threads: the right rotation (two rows
+//                  per thread) feeds the row-major codes of Q(X B); the same registers, staged
+//                  through LDS in two 128-column halves, feed the token-axis rotation (64 rows of
+//                  one column per thread) whose codes Q(B X B) are written transposed.
+#include "hq_device.hpp"
+#include "hq_internal.hpp"
+
+namespace hq {
+
+// Value of lane (lane ^ 1) / (lane ^ 2) within a quad, through DPP quad permutes.
+__device__ inline float quad_xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+__device__ inline float quad_xor2(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
+
+// Butterfly stage across the lanes of a quad (m = 1 or 2): the lane with bit m clear keeps
+// a + b, the other keeps a - b (a = lower lane's value, b = upper lane's value).
+template <int N>
+__device__ inline void quad_stage(float (&v)[N], int lane, int m) {
+  const float sgn = (lane & m) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float p = (m == 1) ? quad_xor1(v[i]) : quad_xor2(v[i]);
+    v[i] = __builtin_fmaf(v[i], sgn, p);   // lower: v + p, upper: p - v
+  }
+}
+
+// 64 consecutive elements starting at element c0 of a row with n valid elements.
+template <class T>
+__device__ inline void load64(const void* row, int64_t c0, int64_t n, bool vec, float (&v)[64]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float u[16];
+    load16<T>(row, c0 + 16 * q, n, vec && (c0 + 16 * q + 16 <= n), u);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[16 * q + j] = u[j];
+  }
+}
+
+// Pack 16 codes starting at v[i0] into a uint4.
+__device__ inline uint4 pack16(const float (&v)[64], int i0, float r, int qp) {
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    w[j] = pack4(quant_code(v[i0 + 4 * j], r, qp), quant_code(v[i0 + 4 * j + 1], r, qp),
+                 quant_code(v[i0 + 4 * j + 2], r, qp), quant_code(v[i0 + 4 * j + 3], r, qp));
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+struct ProArgs {
+  const void* src;
+  int64_t rows, cols;
+  bool vec;                 // 16-byte loads allowed (row pitch and base aligned)
+  float* partials;          // ABSMAX out (both_kernel: [0, grid) right, [grid, 2*grid) both)
+  const float* part_in;     // QUANT in
+  const float* part_in2;    // both_kernel QUANT: partials of the two-sided rotation
+  int nparts;
+  const float* step;        // QUANT, STEP mode (right / left rotation, or X B for both_kernel)
+  const float* step2;       // both_kernel, STEP mode: step of B X B
+  int qp;
+  float* scale_out;
+  float* scale_out2;        // both_kernel: scale of B X B
+  int8_t* codes;            // row-major codes (pitch ld) or nullptr
+  int64_t ld;
+  int8_t* codes_t;          // transposed codes (pitch ld_t) or nullptr
+  int64_t ld_t;
+};
+
+// ================================================================ right rotation
+constexpr int RT_ROWS = 64, RT_COLS = 256, RT_THREADS = 256;
+
+template <class In, int K, int OP>
+__global__ __launch_bounds__(RT_THREADS) void right_kernel(ProArgs a) {
+  __shared__ float red[32];
+  __shared__ __attribute__((aligned(16))) int8_t tcodes[RT_COLS][RT_ROWS + 16];
+  const int t = threadIdx.x, lane = t & 63;
+  const int r = t >> 2, s = t & 3;   // tile row, 64-column segment
+  const int64_t nrt = (a.rows + RT_ROWS - 1) / RT_ROWS, nct = (a.cols + RT_COLS - 1) / RT_COLS;
+  const int64_t tiles = nrt * nct;
+  float sc = 0.0f, rinv = 0.0f;
+  if constexpr (OP == OP_QUANT) {
+    tensor_scale(a.part_in, a.nparts, a.step, a.qp, red, sc, rinv);
+    if (blockIdx.x == 0 && t == 0) *a.scale_out = sc;
+  }
+  const int64_t rpad = (a.rows + 15) / 16 * 16;   // valid extent of a transposed row
+  float amax = 0.0f;
+  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+    const int64_t row0 = (tile / nct) * RT_ROWS, col0 = (tile % nct) * RT_COLS;
+    const int64_t grow = row0 + r, gc = col0 + 64 * s;
+    float v[64];
+    if (grow < a.rows && gc < a.cols) {
+      load64<In>(static_cast<const char*>(a.src) + grow * a.cols * In::bytes, gc, a.cols, a.vec, v);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 64; ++j) v[j] = 0.0f;
+    }
+    fwht_inreg<K, 64>(v);
+    if constexpr (K > 64) quad_stage<64>(v, lane, 1);
+    if constexpr (K > 128) quad_stage<64>(v, lane, 2);
+    if constexpr (OP == OP_ABSMAX) {
+#pragma unroll
+      for (int j = 0; j < 64; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    } else {
+      // row-major codes: 64 consecutive bytes, written up to the 16-byte-padded row end
+      if (a.codes && grow < a.rows) {
+        int8_t* dst = a.codes + grow * a.ld + gc;
+        const int64_t cpad = (a.cols + 15) / 16 * 16;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (gc + 16 * q < cpad) *reinterpret_cast<uint4*>(dst + 16 * q) = pack16(v, 16 * q, rinv, a.qp);
+      }
+      if (a.codes_t) {
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 64; ++j)
+          tcodes[64 * s + j][r] = static_cast<int8_t>(quant_code(v[j], rinv, a.qp));
+        __syncthreads();
+        // thread t writes transposed row col0 + t: 64 bytes = tile rows row0 .. row0+63
+        const int64_t orow = col0 + t;
+        if (orow < a.cols) {
+          int8_t* dst = a.codes_t + orow * a.ld_t + row0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (row0 + 16 * q < rpad)
+              *reinterpret_cast<uint4*>(dst + 16 * q) = *reinterpret_cast<const uint4*>(&tcodes[t][16 * q]);
+        }
+      }
+    }
+  }
+  if constexpr (OP == OP_ABSMAX) {
+    amax = block_max(amax, red);
+    if (t == 0) a.partials[blockIdx.x] = amax;
+  }
+}
+
+// ================================================================ left rotation
+constexpr int LT_THREADS = 256, LT_ELEMS = 16384;
+
+template <int KL> struct LeftShape {
+  static constexpr int TR = KL > 64 ? KL : 64;   // tile rows: whole k-blocks, >= 64
+  static constexpr int TC = LT_ELEMS / TR;       // tile columns
+  static constexpr int P = TR / 64;              // lanes sharing a column (1, 2 or 4)
+  static constexpr int PITCH = TC + 4;           // LDS row pitch (floats)
+};
+
+template <class In, int K, int OP>
+__global__ __launch_bounds__(LT_THREADS) void left_kernel(ProArgs a) {
+  using S = LeftShape<K>;
+  constexpr int TR = S::TR, TC = S::TC, P = S::P, PITCH = S::PITCH;
+  __shared__ __attribute__((aligned(16))) float tile[TR * PITCH];
+  __shared__ float red[32];
+  int8_t* bcodes = reinterpret_cast<int8_t*>(tile);   // reused for row-major codes: TR x (TC+16)
+  constexpr int BP = TC + 16;
+  const int t = threadIdx.x, lane = t & 63;
+  const int c = t / P, p = t % P;                     // column, 64-row part
+  const int64_t nrt = (a.rows + TR - 1) / TR, nct = (a.cols + TC - 1) / TC;
+  const int64_t tiles = nrt * nct;
+  float sc = 0.0f, rinv = 0.0f;
+  if constexpr (OP == OP_QUANT) {
+    tensor_scale(a.part_in, a.nparts, a.step, a.qp, red, sc, rinv);
+    if (blockIdx.x == 0 && t == 0) *a.scale_out = sc;
+  }
+  const int64_t rpad = (a.rows + 15) / 16 * 16, cpad = (a.cols + 15) / 16 * 16;
+  auto slot = [](int row, int col) { return row * PITCH + (col ^ ((64 / P) * (row >> 6))); };
+  float amax = 0.0f;
+  for (int64_t tl = blockIdx.x; tl < tiles; tl += gridDim.x) {
+    const int64_t row0 = (tl / nct) * TR, col0 = (tl % nct) * TC;
+    __syncthreads();
+    // stage the tile as fp32: 8 consecutive columns per thread per step
+    for (int q = t; q < TR * TC / 8; q += LT_THREADS) {
+      const int row = q / (TC / 8), cc = 8 * (q % (TC / 8));
+      const int64_t grow = row0 + row, gc = col0 + cc;
+      float f[8];
+      if (grow < a.rows && gc < a.cols) {
+        const char* rp = static_cast<const char*>(a.src) + grow * a.cols * In::bytes;
+        if (a.vec && gc + 8 <= a.cols) {
+          if constexpr (In::bytes == 4) {
+            const float4 x0 = *reinterpret_cast<const float4*>(rp + 4 * gc);
+            const float4 x1 = *reinterpret_cast<const float4*>(rp + 4 * gc + 16);
+            f[0] = x0.x; f[1] = x0.y; f[2] = x0.z; f[3] = x0.w;
+            f[4] = x1.x; f[5] = x1.y; f[6] = x1.z; f[7] = x1.w;
+          } else {
+            const uint4 u = *reinterpret_cast<const uint4*>(rp + 2 * gc);
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              f[2 * j] = In::from_bits(static_cast<uint16_t>(w[j] & 0xFFFFu));
+              f[2 * j + 1] = In::from_bits(static_cast<uint16_t>(w[j] >> 16));
+            }
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) f[j] = (gc + j < a.cols) ? In::load(rp, gc + j) : 0.0f;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f[j] = 0.0f;
+      }
+      *reinterpret_cast<float4*>(&tile[slot(row, cc)]) = make_float4(f[0], f[1], f[2], f[3]);
+      *reinterpret_cast<float4*>(&tile[slot(row, cc + 4)]) = make_float4(f[4], f[5], f[6], f[7]);
+    }
+    __syncthreads();
+    float v[64];
+#pragma unroll
+    for (int i = 0; i < 64; ++i) v[i] = tile[slot(64 * p + i, c)];
+    fwht_inreg<K, 64>(v);
+    if constexpr (K > 64) quad_stage<64>(v, lane, 1);
+    if constexpr (K > 128) quad_stage<64>(v, lane, 2);
+    const int64_t gcol = col0 + c;
+    if constexpr (OP == OP_ABSMAX) {
+#pragma unroll
+      for (int i = 0; i < 64; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    } else {
+      // transposed codes: 64 consecutive tokens of column gcol
+      if (a.codes_t && gcol < a.cols) {
+        int8_t* dst = a.codes_t + gcol * a.ld_t + row0 + 64 * p;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (row0 + 64 * p + 16 * q < rpad) *reinterpret_cast<uint4*>(dst + 16 * q) = pack16(v, 16 * q, rinv, a.qp);
+      }
+      if (a.codes) {
+        __syncthreads();   // the fp32 tile is dead: reuse it for the byte transpose
+#pragma unroll
+        for (int i = 0; i < 64; ++i)
+          bcodes[(64 * p + i) * BP + c] = static_cast<int8_t>(quant_code(v[i], rinv, a.qp));
+        __syncthreads();
+        for (int q = t; q < TR * TC / 16; q += LT_THREADS) {
+          const int row = q / (TC / 16), cc = 16 * (q % (TC / 16));
+          const int64_t grow = row0 + row, gc = col0 + cc;
+          if (grow < a.rows && gc < cpad)
+            *reinterpret_cast<uint4*>(a.codes + grow * a.ld + gc) =
+                *reinterpret_cast<const uint4*>(&bcodes[row * BP + cc]);
+        }
+      }
+    }
+  }
+  if constexpr (OP == OP_ABSMAX) {
+    amax = block_max(amax, red);
+    if (t == 0) a.partials[blockIdx.x] = amax;
+  }
+}
+
+// ================================================================ both (X under HALO-2)
+constexpr int BT = 256, BT_THREADS = 512, BT_HALF = 128, BT_PITCH = BT_HALF + 1;
+
+template <class In, int K, int OP>
+__global__ __launch_bounds__(BT_THREADS) void both_kernel(ProArgs a) {
+  __shared__ __attribute__((aligned(16))) float half[BT * BT_PITCH];
+  __shared__ float red[32];
+  const int t = threadIdx.x, lane = t & 63;
+  const int r = t >> 2, s = t & 3;        // row phase: tile rows r and r+128, 64-column segment
+  const int cp = t >> 2, pp = t & 3;      // column phase: column of the half, 64-row part
+  const int64_t nrt = (a.rows + BT - 1) / BT, nct = (a.cols + BT - 1) / BT;
+  const int64_t tiles = nrt * nct;
+  float s1 = 0.0f, r1 = 0.0f, s2 = 0.0f, r2 = 0.0f;
+  if constexpr (OP == OP_QUANT) {
+    tensor_scale(a.part_in, a.nparts, a.step, a.qp, red, s1, r1);
+    tensor_scale(a.part_in2, a.nparts, a.step2, a.qp, red, s2, r2);
+    if (blockIdx.x == 0 && t == 0) {
+      *a.scale_out = s1;
+      *a.scale_out2 = s2;
+    }
+  }
+  const int64_t rpad = (a.rows + 15) / 16 * 16, cpad = (a.cols + 15) / 16 * 16;
+  // element (row, col) of a 256 x 128 half lives at row*PITCH + (col ^ (16 * (row / 64))):
+  // with the odd pitch, a wave's 16 columns x 4 parts of the column phase hit distinct banks
+  float amax1 = 0.0f, amax2 = 0.0f;
+  for (int64_t tl = blockIdx.x; tl < tiles; tl += gridDim.x) {
+    const int64_t row0 = (tl / nct) * BT, col0 = (tl % nct) * BT;
+    const int64_t gc = col0 + 64 * s;
+    float v[2][64];
+#pragma unroll
+    for (int hr = 0; hr < 2; ++hr) {
+      const int64_t grow = row0 + r + 128 * hr;
+      if (grow < a.rows && gc < a.cols) {
+        load64<In>(static_cast<const char*>(a.src) + grow * a.cols * In::bytes, gc, a.cols, a.vec, v[hr]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 64; ++j) v[hr][j] = 0.0f;
+      }
+      fwht_inreg<K, 64>(v[hr]);
+      if constexpr (K > 64) quad_stage<64>(v[hr], lane, 1);
+      if constexpr (K > 128) quad_stage<64>(v[hr], lane, 2);
+      if constexpr (OP == OP_ABSMAX) {
+#pragma unroll
+        for (int j = 0; j < 64; ++j) amax1 = fmaxf(amax1, fabsf(v[hr][j]));
+      } else if (a.codes && grow < a.rows) {
+        int8_t* dst = a.codes + grow * a.ld + gc;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (gc + 16 * q < cpad) *reinterpret_cast<uint4*>(dst + 16 * q) = pack16(v[hr], 16 * q, r1, a.qp);
+      }
+    }
+    // token-axis rotation of the right-rotated tile, 128 columns at a time
+#pragma unroll 1
+    for (int h = 0; h < 2; ++h) {
+      __syncthreads();
+      if ((s >> 1) == h) {
+#pragma unroll
+        for (int hr = 0; hr < 2; ++hr) {
+          const int row = r + 128 * hr;
+          // 16-column blocks stay contiguous under the swizzle: one base per block
+#pragma unroll
+          for (int jb = 0; jb < 4; ++jb) {
+            float* dst = &half[row * BT_PITCH + 64 * (s & 1) + 16 * (jb ^ ((row >> 6) & 3))];
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) dst[jj] = v[hr][16 * jb + jj];
+          }
+        }
+      }
+      __syncthreads();
+      float u[64];
+      const float* src = &half[64 * pp * BT_PITCH + (cp ^ (16 * pp))];
+#pragma unroll
+      for (int i = 0; i < 64; ++i) u[i] = src[i * BT_PITCH];
+      fwht_inreg<K, 64>(u);
+      if constexpr (K > 64) quad_stage<64>(u, lane, 1);
+      if constexpr (K > 128) quad_stage<64>(u, lane, 2);
+      const int64_t gcol = col0 + BT_HALF * h + cp;
+      if constexpr (OP == OP_ABSMAX) {
+#pragma unroll
+        for (int i = 0; i < 64; ++i) amax2 = fmaxf(amax2, fabsf(u[i]));
+      } else if (gcol < a.cols) {
+        int8_t* dst = a.codes_t + gcol * a.ld_t + row0 + 64 * pp;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (row0 + 64 * pp + 16 * q < rpad) *reinterpret_cast<uint4*>(dst + 16 * q) = pack16(u, 16 * q, r2, a.qp);
+      }
+    }
+  }
+  if constexpr (OP == OP_ABSMAX) {
+    amax1 = block_max(amax1, red);
+    amax2 = block_max(amax2, red);
+    if (t == 0) {
+      a.partials[blockIdx.x] = amax1;
+      a.partials[gridDim.x + blockIdx.x] = amax2;
+    }
+  }
+}
+
+// ================================================================ launchers
+static int grid_cap(int64_t tiles, int cap) {
+  if (tiles < 1) tiles = 1;
+  return static_cast<int>(tiles < cap ? tiles : cap);
+}
+
+template <template <class, int, int> class KERN, int OP>
+struct Launch;
+
+#define HQ_PRO_DISPATCH(NAME, THREADS)                                                         \
+  template <class In, int OP>                                                                  \
+  static hipError_t NAME##_k(int k, const ProArgs& a, int grid, hipStream_t st) {             \
+    switch (k) {                                                                               \
+      case 1: hipLaunchKernelGGL((NAME<In, 1, OP>), dim3(grid), dim3(THREADS), 0, st, a); break;     \
+      case 2: hipLaunchKernelGGL((NAME<In, 2, OP>), dim3(grid), dim3(THREADS), 0, st, a); break;     \
+      case 4: hipLaunchKernelGGL((NAME<In, 4, OP>), dim3(grid), dim3(THREADS), 0, st, a); break;     \
+      case 8: hipLaunchKernelGGL((NAME<In, 8, OP>), dim3(grid), dim3(THREADS), 0, st, a); break;     \
+      case 16: hipLaunchKernelGGL((NAME<In, 16, OP>), dim3(grid), dim3(THREADS), 0, st, a); break;   \
+      case 32: hipLaunchKernelGGL((NAME<In, 32, OP>), dim3(grid), dim3(THREADS), 0, st, a); break;   \
+      case 64: hipLaunchKernelGGL((NAME<In, 64, OP>), dim3(grid), dim3(THREADS), 0, st, a); break;   \
+      case 128: hipLaunchKernelGGL((NAME<In, 128, OP>), dim3(grid), dim3(THREADS), 0, st, a); break; \
+      case 256: hipLaunchKernelGGL((NAME<In, 256, OP>), dim3(grid), dim3(THREADS), 0, st, a); break; \
+      default: return hipErrorInvalidValue;                                                    \
+    }                                                                                          \
+    return hipGetLastError();                                                                  \
+  }                                                                                            \
+  static hipError_t NAME##_launch(int in_dt, int op, int k, const ProArgs& a, int grid,        \
+                                  hipStream_t st) {                                            \
+    if (op == OP_ABSMAX) {                                                                     \
+      switch (in_dt) {                                                                         \
+        case DT_F32: return NAME##_k<F32, OP_ABSMAX>(k, a, grid, st);                          \
+        case DT_F16: return NAME##_k<F16, OP_ABSMAX>(k, a, grid, st);                          \
+        case DT_BF16: return NAME##_k<BF16, OP_ABSMAX>(k, a, grid, st);                        \
+      }                                                                                        \
+    } else {                                                                                   \
+      switch (in_dt) {                                                                         \
+        case DT_F32: return NAME##_k<F32, OP_QUANT>(k, a, grid, st);                           \
+        case DT_F16: return NAME##_k<F16, OP_QUANT>(k, a, grid, st);                           \
+        case DT_BF16: return NAME##_k<BF16, OP_QUANT>(k, a, grid, st);                         \
+      }                                                                                        \
+    }                                                                                          \
+    return hipErrorInvalidValue;                                                               \
+  }
+
+HQ_PRO_DISPATCH(right_kernel, RT_THREADS)
+HQ_PRO_DISPATCH(left_kernel, LT_THREADS)
+HQ_PRO_DISPATCH(both_kernel, BT_THREADS)
+#undef HQ_PRO_DISPATCH
+
+static int dtb(int dt) { return dt == DT_F32 ? 4 : 2; }
+
+static ProArgs pro_args(const ProPass& p) {
+  ProArgs a{};
+  a.src = p.src;
+  a.rows = p.rows;
+  a.cols = p.cols;
+  a.vec = (reinterpret_cast<uintptr_t>(p.src) & 15u) == 0 && (p.cols * dtb(p.in_dt)) % 16 == 0;
+  a.partials = p.partials;
+  a.part_in = p.partials;
+  a.part_in2 = p.partials + p.nparts;
+  a.nparts = p.nparts;
+  a.step = p.step;
+  a.step2 = p.step2;
+  a.qp = p.qp;
+  a.scale_out = p.scale_out;
+  a.scale_out2 = p.scale_out2;
+  a.codes = p.codes;
+  a.ld = p.ld;
+  a.codes_t = p.codes_t;
+  a.ld_t = p.ld_t;
+  return a;
+}
+
+int pro_grid(const ProPass& p) {
+  int64_t tiles;
+  if (p.kind == PRO_RIGHT) {
+    tiles = ((p.rows + RT_ROWS - 1) / RT_ROWS) * ((p.cols + RT_COLS - 1) / RT_COLS);
+  } else if (p.kind == PRO_LEFT) {
+    const int tr = p.k > 64 ? p.k : 64, tc = LT_ELEMS / tr;
+    tiles = ((p.rows + tr - 1) / tr) * ((p.cols + tc - 1) / tc);
+  } else {
+    tiles = ((p.rows + BT - 1) / BT) * ((p.cols + BT - 1) / BT);
+  }
+  return grid_cap(tiles, p.kind == PRO_BOTH ? kMaxPartials / 2 : kMaxPartials);
+}
+
+hipError_t pro_pass(const ProPass& p, int op, hipStream_t st) {
+  ProArgs a = pro_args(p);
+  const int grid = pro_grid(p);
+  const double elems = static_cast<double>(p.rows) * p.cols;
+  const double inb = elems * dtb(p.in_dt);
+  double outb = 0.0;
+  if (op == OP_QUANT) outb = elems * ((p.codes ? 1 : 0) + (p.codes_t ? 1 : 0));
+  const int tok = prof_begin(op == OP_ABSMAX ? K_ROT_ABSMAX : K_ROT_QUANT, inb + outb, st);
+  hipError_t e = hipErrorInvalidValue;
+  if (p.kind == PRO_RIGHT) e = right_kernel_launch(p.in_dt, op, p.k, a, grid, st);
+  else if (p.kind == PRO_LEFT) e = left_kernel_launch(p.in_dt, op, p.k, a, grid, st);
+  else e = both_kernel_launch(p.in_dt, op, p.k, a, grid, st);
+  prof_end(tok, st);
+  return e;
+}
+
+}  // namespace hq

@@ -135,7 +135,9 @@ size_t hq_workspace_bytes(const hq_config *cfg, int64_t N, int64_t C, int64_t D)
  *   out       host struct; out->codes and/or out->codes_t (at least one non-NULL) and
  *             out->scale are device buffers; the call fills rows, cols, k, bits, rot
  *   ws        workspace of ws_bytes (>= hq_workspace_bytes for a layer containing it)
- * Both code layouts carry the same rotation. */
+ * Both code layouts carry the same rotation. For rot BOTH only out->codes_t is produced (the
+ * transposed layout the weight-gradient product reads); out->codes must be NULL
+ * (HQ_ERR_MODE otherwise) unless k == 1. */
 hq_status hq_rotate_quantize(const void *src, int32_t src_dtype, int64_t rows, int64_t cols,
                              int32_t rot, const hq_config *cfg, const float *step,
                              hq_qtensor *out, void *ws, size_t ws_bytes, void *stream);
