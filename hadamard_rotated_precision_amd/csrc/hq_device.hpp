@@ -16,6 +16,7 @@ enum DType : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 struct F32 {
   using storage = float;
   static constexpr int bytes = 4;
+  static constexpr bool is_bf16 = false;
   __device__ static inline float load(const void* p, int64_t i) {
     return static_cast<const float*>(p)[i];
   }
@@ -27,6 +28,7 @@ struct F32 {
 struct F16 {
   using storage = uint16_t;
   static constexpr int bytes = 2;
+  static constexpr bool is_bf16 = false;
   __device__ static inline float from_bits(uint16_t b) {
     return static_cast<float>(__builtin_bit_cast(_Float16, b));
   }
@@ -45,6 +47,7 @@ struct F16 {
 struct BF16 {
   using storage = uint16_t;
   static constexpr int bytes = 2;
+  static constexpr bool is_bf16 = true;
   __device__ static inline float from_bits(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
   }
@@ -141,6 +144,22 @@ __device__ inline void fwht_inreg(float (&v)[N]) {
   }
 }
 
+// Stages of fwht_inreg from stride H0 on (the smaller strides already applied).
+template <int H0, int K, int N, class V>
+__device__ inline void fwht_from(V (&v)[N]) {
+#pragma unroll
+  for (int h = H0; h < N && h < K; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if ((i & h) == 0) {
+        V a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+}
+
 // Value of lane (lane ^ m) within the wave.
 __device__ inline float xor_lane(float x, int m) {
   return __shfl_xor(x, m, 64);
@@ -202,6 +221,20 @@ __device__ inline int quant_code(float v, float r, int qp) {
   const int base = 0x4B400000;       // bit pattern of 1.5 * 2^23
   bits = min(max(bits, base - qp), base + qp);
   return bits - base;
+}
+
+// The same quantizer kept in the float domain: fma(v, r, 1.5*2^23) clamped to
+// [1.5*2^23 - qp, 1.5*2^23 + qp] with med3; the low byte of the result's bit pattern is the
+// code in two's complement. lo/hi are the two clamp bounds (exact floats).
+__device__ inline uint32_t qbits(float v, float r, float lo, float hi) {
+  return __float_as_uint(__builtin_amdgcn_fmed3f(__builtin_fmaf(v, r, 12582912.0f), lo, hi));
+}
+__device__ inline float qlo(int qp) { return 12582912.0f - static_cast<float>(qp); }
+__device__ inline float qhi(int qp) { return 12582912.0f + static_cast<float>(qp); }
+
+// Four codes (low bytes of qbits results) packed little-endian into one dword.
+__device__ inline uint32_t qpack4(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3) {
+  return __builtin_amdgcn_perm(x1, x0, 0x0c0c0400u) | __builtin_amdgcn_perm(x3, x2, 0x04000c0cu);
 }
 
 // Pack 4 codes (already in [-127, 127]) into one little-endian dword.

@@ -263,90 +263,195 @@ __global__ __launch_bounds__(LT_THREADS) void left_kernel(ProArgs a) {
 }
 
 // ================================================================ both (X under HALO-2)
-constexpr int BT = 256, BT_THREADS = 512, BT_HALF = 128, BT_PITCH = BT_HALF + 1;
+constexpr int BT = 256, BT_THREADS = 512, BT_HALF = 128, BT_PITCH = BT_HALF + 4;
 
+// 64 consecutive elements starting at c0 of a row with n valid elements, with the stride-1
+// butterfly already applied (fp16 / bf16 pairs go through v_dot2 with (1, 1) and (1, -1)).
+template <class T>
+__device__ inline void load64_s1(const void* row, int64_t c0, int64_t n, bool vec, float (&v)[64]) {
+  if constexpr (T::bytes == 2) {
+    if (vec && c0 + 64 <= n) {
+      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(row) + c0);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint4 u = p[q];
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (T::is_bf16) {
+            typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+            const b2 x = __builtin_bit_cast(b2, w[j]);
+            v[8 * q + 2 * j] = __builtin_amdgcn_fdot2_f32_bf16(x, __builtin_bit_cast(b2, 0x3F803F80u), 0.0f, false);
+            v[8 * q + 2 * j + 1] = __builtin_amdgcn_fdot2_f32_bf16(x, __builtin_bit_cast(b2, 0xBF803F80u), 0.0f, false);
+          } else {
+            typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+            const h2 x = __builtin_bit_cast(h2, w[j]);
+            v[8 * q + 2 * j] = __builtin_amdgcn_fdot2(x, __builtin_bit_cast(h2, 0x3C003C00u), 0.0f, false);
+            v[8 * q + 2 * j + 1] = __builtin_amdgcn_fdot2(x, __builtin_bit_cast(h2, 0xBC003C00u), 0.0f, false);
+          }
+        }
+      }
+      return;
+    }
+  }
+  load64<T>(row, c0, n, vec, v);
+  fwht_inreg<2, 64>(v);
+}
+
+// f64 butterfly across the lanes of a quad (m = 1 or 2), as quad_stage.
+template <int M, int N>
+__device__ inline void quad_stage_f64(double (&u)[N], int lane) {
+  constexpr int ctrl = M == 1 ? 0xB1 : 0x4E;
+  const double sgn = (lane & M) ? -1.0 : 1.0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, u[i]);
+    const int lo = static_cast<int>(b), hi = static_cast<int>(b >> 32);
+    const int plo = __builtin_amdgcn_update_dpp(0, lo, ctrl, 0xF, 0xF, false);
+    const int phi = __builtin_amdgcn_update_dpp(0, hi, ctrl, 0xF, 0xF, false);
+    const double p = __builtin_bit_cast(double, (static_cast<uint64_t>(static_cast<uint32_t>(phi)) << 32) |
+                                                    static_cast<uint32_t>(plo));
+    u[i] = __builtin_fma(u[i], sgn, p);
+    if ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);   // bound the live DPP temporaries
+  }
+}
+
+// Work items of both_kernel: 128-column halves of 256 x 256 tiles. The two halves of a tile are
+// 8 items apart, so that they run on one XCD and the second read of the tile hits its L2.
+__host__ __device__ inline int64_t both_items(int64_t rows, int64_t cols) {
+  return 2 * ((rows + BT - 1) / BT) * ((cols + BT - 1) / BT);
+}
+
+// Per item: the tile rows rotated along the feature axis (X B in fp32, exact for 16-bit inputs;
+// with k = 256 both halves of a row are needed, otherwise only the item's own half is read) give
+// the row-major codes of X B; the item's half of X B is then staged through LDS (16-column
+// blocks XOR-swizzled by row / 64, so the column reads are conflict-free) and rotated along the
+// token axis in fp64, where sums of fp32 values are exact, so B X B is rounded to fp32 once, as
+// the exact sum would be, before its scale and codes are taken.
 template <class In, int K, int OP>
 __global__ __launch_bounds__(BT_THREADS) void both_kernel(ProArgs a) {
   __shared__ __attribute__((aligned(16))) float half[BT * BT_PITCH];
   __shared__ float red[32];
   const int t = threadIdx.x, lane = t & 63;
-  const int r = t >> 2, s = t & 3;        // row phase: tile rows r and r+128, 64-column segment
-  const int cp = t >> 2, pp = t & 3;      // column phase: column of the half, 64-row part
-  const int64_t nrt = (a.rows + BT - 1) / BT, nct = (a.cols + BT - 1) / BT;
-  const int64_t tiles = nrt * nct;
-  float s1 = 0.0f, r1 = 0.0f, s2 = 0.0f, r2 = 0.0f;
+  const int r = t >> 1, s2 = t & 1;      // row phase: row r, columns 64*s2 + [0, 64) of a half
+  const int cp = t >> 2, pp = t & 3;     // column phase: column cp of the half, rows 64*pp + [0, 64)
+  const int64_t nct = (a.cols + BT - 1) / BT;
+  const int64_t items = both_items(a.rows, a.cols);
+  float s1 = 0.0f, r1 = 0.0f, sc2 = 0.0f, r2 = 0.0f;
   if constexpr (OP == OP_QUANT) {
     tensor_scale(a.part_in, a.nparts, a.step, a.qp, red, s1, r1);
-    tensor_scale(a.part_in2, a.nparts, a.step2, a.qp, red, s2, r2);
+    tensor_scale(a.part_in2, a.nparts, a.step2, a.qp, red, sc2, r2);
     if (blockIdx.x == 0 && t == 0) {
       *a.scale_out = s1;
-      *a.scale_out2 = s2;
+      *a.scale_out2 = sc2;
     }
   }
+  const float lo = qlo(a.qp), hi = qhi(a.qp);
   const int64_t rpad = (a.rows + 15) / 16 * 16, cpad = (a.cols + 15) / 16 * 16;
-  // element (row, col) of a 256 x 128 half lives at row*PITCH + (col ^ (16 * (row / 64))):
-  // with the odd pitch, a wave's 16 columns x 4 parts of the column phase hit distinct banks
+  const char* src = static_cast<const char*>(a.src);
   float amax1 = 0.0f, amax2 = 0.0f;
-  for (int64_t tl = blockIdx.x; tl < tiles; tl += gridDim.x) {
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int64_t full = items / 16 * 16;
+    int64_t tl;
+    int h;
+    if (it < full) {
+      tl = (it / 16) * 8 + (it % 8);
+      h = static_cast<int>((it / 8) & 1);
+    } else {
+      tl = full / 2 + (it - full) / 2;
+      h = static_cast<int>((it - full) & 1);
+    }
     const int64_t row0 = (tl / nct) * BT, col0 = (tl % nct) * BT;
-    const int64_t gc = col0 + 64 * s;
-    float v[2][64];
+    const int64_t grow = row0 + r;
+    const bool rin = grow < a.rows;
+    const char* rowp = src + grow * a.cols * In::bytes;
+    // ---- row phase: this half of X B for row r, columns 64*s2 + [0, 64)
+    float w[64];
+    const int64_t gc = col0 + BT_HALF * h + 64 * s2;
+    if constexpr (K > 128) {
+      float v[2][64];
 #pragma unroll
-    for (int hr = 0; hr < 2; ++hr) {
-      const int64_t grow = row0 + r + 128 * hr;
-      if (grow < a.rows && gc < a.cols) {
-        load64<In>(static_cast<const char*>(a.src) + grow * a.cols * In::bytes, gc, a.cols, a.vec, v[hr]);
+      for (int hh = 0; hh < 2; ++hh) {
+        const int64_t c = col0 + BT_HALF * hh + 64 * s2;
+        if (rin && c < a.cols) {
+          load64_s1<In>(rowp, c, a.cols, a.vec, v[hh]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 64; ++j) v[hh][j] = 0.0f;
+        }
+        fwht_from<2, K, 64>(v[hh]);
+        quad_stage<64>(v[hh], lane, 1);
+      }
+      const float sg = h ? -1.0f : 1.0f;   // stride 128: the lower half keeps x + y, the upper x - y
+#pragma unroll
+      for (int j = 0; j < 64; ++j) w[j] = __builtin_fmaf(v[1][j], sg, v[0][j]);
+    } else {
+      if (rin && gc < a.cols) {
+        load64_s1<In>(rowp, gc, a.cols, a.vec, w);
       } else {
 #pragma unroll
-        for (int j = 0; j < 64; ++j) v[hr][j] = 0.0f;
+        for (int j = 0; j < 64; ++j) w[j] = 0.0f;
       }
-      fwht_inreg<K, 64>(v[hr]);
-      if constexpr (K > 64) quad_stage<64>(v[hr], lane, 1);
-      if constexpr (K > 128) quad_stage<64>(v[hr], lane, 2);
-      if constexpr (OP == OP_ABSMAX) {
-#pragma unroll
-        for (int j = 0; j < 64; ++j) amax1 = fmaxf(amax1, fabsf(v[hr][j]));
-      } else if (a.codes && grow < a.rows) {
-        int8_t* dst = a.codes + grow * a.ld + gc;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (gc + 16 * q < cpad) *reinterpret_cast<uint4*>(dst + 16 * q) = pack16(v[hr], 16 * q, r1, a.qp);
-      }
+      fwht_from<2, K, 64>(w);
+      if constexpr (K > 64) quad_stage<64>(w, lane, 1);
     }
-    // token-axis rotation of the right-rotated tile, 128 columns at a time
-#pragma unroll 1
-    for (int h = 0; h < 2; ++h) {
-      __syncthreads();
-      if ((s >> 1) == h) {
+    if constexpr (OP == OP_ABSMAX) {
 #pragma unroll
-        for (int hr = 0; hr < 2; ++hr) {
-          const int row = r + 128 * hr;
-          // 16-column blocks stay contiguous under the swizzle: one base per block
+      for (int j = 0; j < 64; ++j) amax1 = fmaxf(amax1, fabsf(w[j]));
+    } else if (a.codes && rin) {
+      int8_t* dst = a.codes + grow * a.ld + gc;
 #pragma unroll
-          for (int jb = 0; jb < 4; ++jb) {
-            float* dst = &half[row * BT_PITCH + 64 * (s & 1) + 16 * (jb ^ ((row >> 6) & 3))];
+      for (int q = 0; q < 4; ++q) {
+        if (gc + 16 * q < cpad) {
+          uint32_t x[4];
 #pragma unroll
-            for (int jj = 0; jj < 16; ++jj) dst[jj] = v[hr][16 * jb + jj];
+          for (int j = 0; j < 4; ++j) {
+            const int i = 16 * q + 4 * j;
+            x[j] = qpack4(qbits(w[i], r1, lo, hi), qbits(w[i + 1], r1, lo, hi),
+                          qbits(w[i + 2], r1, lo, hi), qbits(w[i + 3], r1, lo, hi));
           }
+          *reinterpret_cast<uint4*>(dst + 16 * q) = make_uint4(x[0], x[1], x[2], x[3]);
         }
       }
-      __syncthreads();
-      float u[64];
-      const float* src = &half[64 * pp * BT_PITCH + (cp ^ (16 * pp))];
+    }
+    // ---- column phase: the token-axis rotation of this half, in fp64
+    __syncthreads();
 #pragma unroll
-      for (int i = 0; i < 64; ++i) u[i] = src[i * BT_PITCH];
-      fwht_inreg<K, 64>(u);
-      if constexpr (K > 64) quad_stage<64>(u, lane, 1);
-      if constexpr (K > 128) quad_stage<64>(u, lane, 2);
-      const int64_t gcol = col0 + BT_HALF * h + cp;
-      if constexpr (OP == OP_ABSMAX) {
+    for (int jb = 0; jb < 4; ++jb) {
+      float* dst = &half[r * BT_PITCH + ((64 * s2 + 16 * jb) ^ (16 * (r >> 6)))];
 #pragma unroll
-        for (int i = 0; i < 64; ++i) amax2 = fmaxf(amax2, fabsf(u[i]));
-      } else if (gcol < a.cols) {
-        int8_t* dst = a.codes_t + gcol * a.ld_t + row0 + 64 * pp;
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(dst + 4 * q) =
+            make_float4(w[16 * jb + 4 * q], w[16 * jb + 4 * q + 1], w[16 * jb + 4 * q + 2], w[16 * jb + 4 * q + 3]);
+    }
+    __syncthreads();
+    double u[64];
+    const float* col = &half[64 * pp * BT_PITCH + (cp ^ (16 * pp))];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (row0 + 64 * pp + 16 * q < rpad) *reinterpret_cast<uint4*>(dst + 16 * q) = pack16(u, 16 * q, r2, a.qp);
+    for (int i = 0; i < 64; ++i) u[i] = static_cast<double>(col[i * BT_PITCH]);
+    fwht_from<1, K, 64>(u);
+    if constexpr (K > 64) quad_stage_f64<1, 64>(u, lane);
+    if constexpr (K > 128) quad_stage_f64<2, 64>(u, lane);
+    const int64_t gcol = col0 + BT_HALF * h + cp;
+    if constexpr (OP == OP_ABSMAX) {
+#pragma unroll
+      for (int i = 0; i < 64; ++i) amax2 = fmaxf(amax2, fabsf(static_cast<float>(u[i])));
+    } else if (gcol < a.cols) {
+      int8_t* dst = a.codes_t + gcol * a.ld_t + row0 + 64 * pp;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (row0 + 64 * pp + 16 * q < rpad) {
+          uint32_t x[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int i = 16 * q + 4 * j;
+            x[j] = qpack4(qbits(static_cast<float>(u[i]), r2, lo, hi),
+                          qbits(static_cast<float>(u[i + 1]), r2, lo, hi),
+                          qbits(static_cast<float>(u[i + 2]), r2, lo, hi),
+                          qbits(static_cast<float>(u[i + 3]), r2, lo, hi));
+          }
+          *reinterpret_cast<uint4*>(dst + 16 * q) = make_uint4(x[0], x[1], x[2], x[3]);
+        }
       }
     }
   }
@@ -441,9 +546,10 @@ int pro_grid(const ProPass& p) {
     const int tr = p.k > 64 ? p.k : 64, tc = LT_ELEMS / tr;
     tiles = ((p.rows + tr - 1) / tr) * ((p.cols + tc - 1) / tc);
   } else {
-    tiles = ((p.rows + BT - 1) / BT) * ((p.cols + BT - 1) / BT);
+    // one 135 KB workgroup per CU: at most one item per CU at a time
+    return grid_cap(both_items(p.rows, p.cols), 256);
   }
-  return grid_cap(tiles, p.kind == PRO_BOTH ? kMaxPartials / 2 : kMaxPartials);
+  return grid_cap(tiles, kMaxPartials);
 }
 
 hipError_t pro_pass(const ProPass& p, int op, hipStream_t st) {

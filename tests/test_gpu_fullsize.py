@@ -44,15 +44,15 @@ def test_fullsize_sampled(cid):
     X = O.decode(inputs["x"], in_dt)
     qx, sx, qxt, sxt = O.quantize_x(X, k, cfg["bits"], v, mode, steps.get("x"), steps.get("xt"))
     del X
-    assert_codes(L.qx.codes_view().cpu().numpy(), qx, "qX")
+    print("qX mismatch", assert_codes(L.qx.codes_view().cpu().numpy(), qx, "qX"), flush=True)
     assert_scale(float(L.qx.scale.cpu()[0]), sx, "sX")
     if L.qxt is not None:
-        assert_codes(L.qxt.codes_t_view().cpu().numpy().T, qxt, "qXt")
+        print("qXt mismatch", assert_codes(L.qxt.codes_t_view().cpu().numpy().T, qxt, "qXt"), flush=True)
         assert_scale(float(L.qxt.scale.cpu()[0]), sxt, "sXt")
     W = O.decode(inputs["w"], in_dt)
     qw, sw = O.quantize_w(W, k, cfg["bits"], v, mode, steps.get("w"))
     del W
-    assert_codes(L.qw.codes_view().cpu().numpy(), qw, "qW")
+    print("qW mismatch", assert_codes(L.qw.codes_view().cpu().numpy(), qw, "qW"), flush=True)
     assert_scale(float(L.qw.scale.cpu()[0]), sw, "sW")
     print("[step] forward codes compared", flush=True)
 
@@ -70,7 +70,7 @@ def test_fullsize_sampled(cid):
     G = O.decode(inputs["dy"], in_dt)
     qg, sg = O.quantize_g(G, k, cfg["bits"], v, mode, steps.get("g"))
     del G
-    assert_codes(L.qg.codes_view().cpu().numpy(), qg, "qG")
+    print("qG mismatch", assert_codes(L.qg.codes_view().cpu().numpy(), qg, "qG"), flush=True)
     assert_scale(float(L.qg.scale.cpu()[0]), sg, "sG")
     print("[step] gradient codes compared", flush=True)
 
