@@ -119,6 +119,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="before the steps, copy a buffer of this many MiB three times with a "
+                         "plain device copy (reference dispatches for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -162,6 +165,16 @@ def main():
         if dw is not None:
             layer.bwd_weight(dw, stream)
 
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print("[bench] copy calibration: 3 copies of %d bytes" % (4 * n), file=sys.stderr, flush=True)
+        del src, dst
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -194,24 +207,11 @@ def main():
     # ---- rotate+quantize bandwidth: the prologue launches alone
     in_bytes = 2 if in_dt != WL.F32 else 4
     pro_bytes = prologue_bytes(cfg, in_bytes)
-    pro_kinds = (1 << B.HQ_KIND_ROT_ABSMAX) | (1 << B.HQ_KIND_ROT_QUANT) | \
-        (1 << B.HQ_KIND_TRANSPOSE) | (1 << B.HQ_KIND_MISC)
     pro_ms = 0.0
     for kind in ("rot_absmax", "rot_quant", "transpose", "misc"):
         pro_ms += breakdown[kind][1]
-    # the two-sided rotation of X stages its column pass through a store pass
-    store_ms_prologue = None
-    if cfg["variant"] == WL.HALO2:
-        # measure the forward alone to split the store kind between prologue and epilogue
-        B.check(B.hq_profile_start(1 << B.HQ_KIND_ROT_STORE), "profile")
-        for _ in range(args.steps):
-            layer.fwd(x, w, y, steps_t, stream)
-        torch.cuda.synchronize()
-        store_ms_prologue = B.profile_stop_dict()["rot_store"][1]
-        pro_ms += store_ms_prologue
     pro_ms_step = pro_ms / args.steps
     rq_gbs = pro_bytes / (pro_ms_step * 1e-3) / 1e9 if pro_ms_step > 0 else None
-    _ = pro_kinds
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):

@@ -1,0 +1,153 @@
+"""Summaries of rocprofv3 CSV output for the profiles/ folder.
+
+  python -m hadamard_rotated_precision_amd.prof_summary stats DIR OUT.md --cmd "..."
+      per-kernel table from DIR/*kernel_stats.csv (calls, average and total duration).
+
+  python -m hadamard_rotated_precision_amd.prof_summary traffic FETCH_DIR WRITE_DIR \
+      --copy-bytes B --workload NAME --json OUT.json --md OUT.md --cmd "..."
+      HBM bytes per GEMM launch from two --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per
+      dispatch). Each counter is scaled by what it reads for the plain device copies of B
+      bytes the same run made (read B, write B), so the figure is in bytes of the copy's
+      own accounting.
+"""
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+GEMM_SOURCE = os.path.join(HERE, "csrc", "hq_gemm.hip")
+
+
+def _one(pattern):
+    files = sorted(glob.glob(pattern, recursive=True))
+    if not files:
+        raise SystemExit("no file matches %s" % pattern)
+    return files[0]
+
+
+def short_name(name):
+    name = re.sub(r"\(hq::\w+\)$", "", name)
+    name = name.replace("void ", "").replace("hq::", "")
+    return name[:100]
+
+
+def cmd_stats(args):
+    path = _one(os.path.join(args.dir, "**", "*kernel_stats.csv")) if not args.dir.endswith(".csv") \
+        else args.dir
+    rows = list(csv.DictReader(open(path)))
+    out = ["# Kernel durations: %s" % args.title, "",
+           "Command (from the repository root, rocprofv3 run in /tmp):", "",
+           "```", args.cmd, "```", "",
+           "| kernel | calls | avg us | total us | % |", "|---|---:|---:|---:|---:|"]
+    for r in rows:
+        out.append("| `%s` | %s | %.2f | %.1f | %.1f |" % (
+            short_name(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3,
+            float(r["TotalDurationNs"]) / 1e3, float(r["Percentage"])))
+    open(args.out, "w").write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
+def _counter_rows(d, counter):
+    path = _one(os.path.join(d, "**", "*counter_collection.csv"))
+    res = []
+    for r in csv.DictReader(open(path)):
+        if r.get("Counter_Name") != counter:
+            continue
+        res.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    res.sort()
+    return res
+
+
+def _is_copy(name):
+    n = name.lower()
+    return "copy" in n and "hq::" not in n
+
+
+def cmd_traffic(args):
+    fetch = _counter_rows(args.fetch_dir, "FETCH_SIZE")
+    write = _counter_rows(args.write_dir, "WRITE_SIZE")
+    cf = [v for _, n, v in fetch if _is_copy(n)]
+    cw = [v for _, n, v in write if _is_copy(n)]
+    if not cf or not cw:
+        raise SystemExit("no copy dispatches found for the calibration")
+    # the largest copies are the calibration copies of --copy-bytes
+    cf = sorted(cf)[-3:]
+    cw = sorted(cw)[-3:]
+    f_scale = (sum(cf) / len(cf)) * 1024.0 / args.copy_bytes
+    w_scale = (sum(cw) / len(cw)) * 1024.0 / args.copy_bytes
+
+    def per_kernel(rows, scale):
+        acc = {}
+        for _, n, v in rows:
+            if "hq::" not in n:
+                continue
+            key = short_name(n)
+            acc.setdefault(key, []).append(v * 1024.0 / scale)
+        return acc
+
+    kf = per_kernel(fetch, f_scale)
+    kw = per_kernel(write, w_scale)
+    gemm_f = [v for k, vs in kf.items() if "gemm_i8_kernel" in k for v in vs]
+    gemm_w = [v for k, vs in kw.items() if "gemm_i8_kernel" in k for v in vs]
+    if not gemm_f or not gemm_w:
+        raise SystemExit("no GEMM dispatches found")
+    fpl = sum(gemm_f) / len(gemm_f)
+    wpl = sum(gemm_w) / len(gemm_w)
+    with open(GEMM_SOURCE, "rb") as f:
+        src_hash = hashlib.sha256(f.read()).hexdigest()[:16]
+    doc = {"workload": args.workload, "gemm_source_sha256_16": src_hash,
+           "bytes_per_launch": round(fpl + wpl), "fetch_bytes_per_launch": round(fpl),
+           "write_bytes_per_launch": round(wpl), "gemm_launches_counted": len(gemm_f),
+           "calibration": {"copy_bytes": args.copy_bytes,
+                           "fetch_kib_per_copy": sum(cf) / len(cf),
+                           "write_kib_per_copy": sum(cw) / len(cw),
+                           "fetch_scale": f_scale, "write_scale": w_scale},
+           "command": args.cmd}
+    json.dump(doc, open(args.json, "w"), indent=1)
+    out = ["# HBM traffic per launch: %s" % args.workload, "",
+           "Two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch). Each counter",
+           "is divided by what it reads for a plain device copy of %d bytes in the same run" % args.copy_bytes,
+           "(fetch scale %.4f, write scale %.4f counted bytes per copied byte)." % (f_scale, w_scale), "",
+           "Commands (from the repository root, rocprofv3 run in /tmp):", "", "```", args.cmd, "```", "",
+           "| kernel | dispatches | read MB / launch | written MB / launch |", "|---|---:|---:|---:|"]
+    for k in sorted(set(kf) | set(kw)):
+        f = kf.get(k, [0.0])
+        w = kw.get(k, [0.0])
+        out.append("| `%s` | %d | %.2f | %.2f |" % (k, len(f), sum(f) / len(f) / 1e6, sum(w) / len(w) / 1e6))
+    out += ["", "GEMM average per launch: read %.2f MB, written %.2f MB, total %.2f MB "
+            "(source hash %s)." % (fpl / 1e6, wpl / 1e6, (fpl + wpl) / 1e6, src_hash)]
+    open(args.md, "w").write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    sub = ap.add_subparsers(dest="what", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("out")
+    s.add_argument("--cmd", required=True)
+    s.add_argument("--title", default="")
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_dir")
+    t.add_argument("write_dir")
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--json", required=True)
+    t.add_argument("--md", required=True)
+    t.add_argument("--cmd", required=True)
+    args = ap.parse_args(argv)
+    if args.what == "stats":
+        cmd_stats(args)
+    else:
+        cmd_traffic(args)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

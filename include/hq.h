@@ -36,7 +36,9 @@
  *     workspaces and outputs.
  *   - Numerics: inputs must be finite. H is the unnormalized Sylvester matrix in natural
  *     order, h(i,j) = (-1)^popcount(i&j); its 1/k factors go into the dequantization scalar.
- *     Rotations are computed in fp32. Quantization: s = absmax/Qp (fp32) or the given step,
+ *     Rotations are computed in fp32, except the token-axis rotation of the two-sided
+ *     transform (rot BOTH), which sums the fp32 values of V B exactly in fp64 and rounds the
+ *     result to fp32 once. Quantization: s = absmax/Qp (fp32) or the given step,
  *     code = clamp(RNE(v * fp32(1/s)), -Qp, Qp), Qp = 127 (bits 8) or 7 (bits 4); a zero
  *     tensor gets s = 0 and all-zero codes. Integer GEMMs accumulate exactly in int32.
  *     Outputs are rounded to their dtype with round-to-nearest-even.
