@@ -36,8 +36,19 @@ hq_status check_cfg(const hq_config* cfg) {
   return HQ_OK;
 }
 
-// Workspace: the absmax partial arrays plus one spare device float.
+// Workspace: the absmax partial arrays plus one spare device float, then (when the dX product
+// of a HALO-2 layer runs as two K halves) the split-K counters and partial tiles.
 size_t ws_need() { return kPartialBytes + kAlign; }
+
+int64_t dx_split_tiles(const hq_config* cfg, int64_t N, int64_t C, int64_t D) {
+  if (cfg->variant != HQ_VARIANT_HALO2 || cfg->k <= 1) return 0;
+  return hq::gemm_split_tiles(N, C, D, hq::EPI_SCALE, cfg->k, cfg->k, false);
+}
+
+size_t ws_need_layer(const hq_config* cfg, int64_t N, int64_t C, int64_t D) {
+  const int64_t split = dx_split_tiles(cfg, N, C, D);
+  return ws_need() + (split > 0 ? hq::gemm_split_bytes(split) : 0);
+}
 
 hq_status check_ws(void* ws, size_t ws_bytes, size_t need) {
   if (need == 0) return HQ_OK;
@@ -49,10 +60,12 @@ hq_status check_ws(void* ws, size_t ws_bytes, size_t need) {
 struct Ws {
   float* part[4];
   float* spare;
+  void* split;   // split-K area (only as large as the call's hq_workspace_bytes allows)
   explicit Ws(void* base) {
     char* b = static_cast<char*>(base);
     for (int i = 0; i < 4; ++i) part[i] = reinterpret_cast<float*>(b + i * hq::kMaxPartials * 4);
     spare = reinterpret_cast<float*>(b + kPartialBytes);
+    split = b + ws_need();
   }
 };
 
@@ -79,7 +92,8 @@ hq_status device_ok() {
 hq_status quantize_tensor(const void* src, int32_t dt, int64_t rows, int64_t cols, int32_t rot,
                           int32_t k, int32_t bits, const float* step, int8_t* codes, int64_t ld,
                           int8_t* codes_t, int64_t ld_t, float* scale, const Ws& ws,
-                          int part_slot, hipStream_t st) {
+                          int part_slot, hipStream_t st, int32_t* zero_ptr = nullptr,
+                          int64_t zero_n = 0) {
   if (rows * cols == 0) {   // empty tensor: scale = step (or 0); there are no codes to write
     HQ_TRY(hq::write_scale(scale, step, st));
     return HQ_OK;
@@ -93,6 +107,8 @@ hq_status quantize_tensor(const void* src, int32_t dt, int64_t rows, int64_t col
   p.qp = qmax(bits);
   p.partials = ws.part[part_slot];
   p.step = step;
+  p.zero_ptr = zero_ptr;
+  p.zero_n = zero_n;
   if (rot == HQ_ROT_BOTH) {
     // the two-sided kernel also produces the right-only scale: park it in the workspace
     p.kind = hq::PRO_BOTH;
@@ -234,7 +250,7 @@ int64_t hq_code_pitch(int64_t cols) { return cols < 0 ? 0 : pitch16(cols); }
 
 size_t hq_workspace_bytes(const hq_config* cfg, int64_t N, int64_t C, int64_t D) {
   if (check_cfg(cfg) != HQ_OK || N < 0 || C < 0 || D < 0) return 0;
-  return ws_need();
+  return ws_need_layer(cfg, N, C, D);
 }
 
 hq_status hq_rotate_quantize(const void* src, int32_t src_dtype, int64_t rows, int64_t cols,
@@ -350,9 +366,12 @@ hq_status hq_linear_bwd_input(const void* dy, int32_t dy_dtype, int64_t N, int64
   hipStream_t st = static_cast<hipStream_t>(stream);
   Ws wsp(ws);
   const int32_t rg = g_rot(v);
+  // a split dX product needs its arrival counters at zero: the quantize pass clears them
+  const int64_t split = dx_split_tiles(cfg, N, C, D);
   HQ_CHECK(quantize_tensor(dy, dy_dtype, N, D, rg, k, cfg->bits, stepm ? step_g : nullptr,
                            save_g->codes, save_g->ld, save_g->codes_t, save_g->ld_t,
-                           save_g->scale, wsp, 0, st));
+                           save_g->scale, wsp, 0, st,
+                           split > 0 ? static_cast<int32_t*>(wsp.split) : nullptr, split));
   fill_meta(save_g, N, D, k, cfg->bits, rg);
   // dX = [B_N] (qG qW) [B_C] sG sW / k^e, dequantized and inverse-rotated in the GEMM epilogue.
   GemmPass g;
@@ -386,6 +405,10 @@ hq_status hq_linear_bwd_input(const void* dy, int32_t dy_dtype, int64_t N, int64
       g.km = k;
       g.kn = k;
       g.kmul = 1.0f / static_cast<float>(k * k);
+      if (split > 0) {
+        g.split_ws = wsp.split;
+        g.split_cnt_zeroed = N * D > 0;   // the quantize pass above ran and cleared them
+      }
     }
   }
   HQ_TRY(hq::gemm_pass(g, st));

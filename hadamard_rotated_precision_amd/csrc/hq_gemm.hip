@@ -38,6 +38,7 @@ namespace hq {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 constexpr int GBM = 256, GBK = 64;
 constexpr int kGroupM = 8;
@@ -55,7 +56,16 @@ struct GemmArgs {
   const float* sa;
   const float* sb;
   float kmul;
+  int32_t* split_part;   // SPLIT: 2 int32 partial tiles per output tile
+  int32_t* split_cnt;    // SPLIT: arrival counter per output tile (zero on entry, left zero)
 };
+
+// One 16-byte buffer load per lane straight into LDS: lane l's bytes land at lds + 16 l
+// (the LDS base is wave-uniform and goes through M0).
+__device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t rs, int8_t* lds, int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voffset, 0, 0, 0);
+}
 
 __device__ inline int lds_off(int row, int chunk) {
   return row * GBK + ((chunk ^ ((row >> 2) & 3)) << 4);
@@ -140,25 +150,32 @@ template <int BN> struct GemmShape {
   static constexpr int NT = 64 * NW;
 };
 
-template <int BN, class Out, int EPI, int KM, int KN, bool TRANS>
+template <int BN, class Out, int EPI, int KM, int KN, bool TRANS, bool SPLIT>
 __global__ __launch_bounds__(GemmShape<BN>::NT, 512 / GemmShape<BN>::NT) void gemm_i8_kernel(GemmArgs g) {
   constexpr int NT = GemmShape<BN>::NT;   // 256 (BN=128) or 512 (BN=256): two waves per SIMD
+  constexpr int NW = GemmShape<BN>::NW;
   constexpr int WN = 64;              // wave tile columns
   constexpr int NB = WN / 32;         // 32x32 blocks per wave along N
   constexpr int WCOLS = BN / WN;      // waves along N
   constexpr int A_BYTES = GBM * GBK, B_BYTES = BN * GBK, STAGE = A_BYTES + B_BYTES;
-  constexpr int ALD = GBM * 4 / NT;   // 16-byte A chunks loaded per thread per step
-  constexpr int BLD = BN * 4 / NT;    // 16-byte B chunks loaded per thread per step
   constexpr int EP = BN + 4;          // epilogue LDS row pitch (floats)
-  constexpr int EPI_BYTES = 64 * EP * 4;
-  constexpr int LDS_BYTES = (3 * STAGE > EPI_BYTES) ? 3 * STAGE : EPI_BYTES;
-  __shared__ __attribute__((aligned(16))) int8_t smem[LDS_BYTES];
+  // Three LDS stages, each its own LDS object so the compiler tracks which direct-to-LDS
+  // loads a fragment read has to wait for; the epilogue reuses stages 0 and 1 (32 rows each).
+  constexpr int STAGE_ALLOC = (STAGE > 32 * EP * 4) ? STAGE : 32 * EP * 4;
+  __shared__ __attribute__((aligned(16))) int8_t st0[STAGE_ALLOC];
+  __shared__ __attribute__((aligned(16))) int8_t st1[STAGE_ALLOC];
+  __shared__ __attribute__((aligned(16))) int8_t st2[STAGE_ALLOC];
 
   const int tiles_m = static_cast<int>((g.M + GBM - 1) / GBM);
   const int tiles_n = static_cast<int>((g.N + BN - 1) / BN);
   const int ntiles = tiles_m * tiles_n;
+  const int nblocks = SPLIT ? 2 * ntiles : ntiles;
   int pid = blockIdx.x;
-  if ((ntiles & 7) == 0) pid = (pid & 7) * (ntiles >> 3) + (pid >> 3);   // XCD-contiguous
+  if ((nblocks & 7) == 0) pid = (pid & 7) * (nblocks >> 3) + (pid >> 3);   // XCD-contiguous
+  // split-K: the two K parts of a tile are consecutive, so they share an XCD
+  const int khalf = SPLIT ? (pid & 1) : 0;
+  if constexpr (SPLIT) pid >>= 1;
+  const int tile_id = pid;
   const int group = pid / (kGroupM * tiles_n);
   const int first_m = group * kGroupM;
   const int gsize = min(tiles_m - first_m, kGroupM);
@@ -178,55 +195,61 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 512 / GemmShape<BN>::NT) void ge
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-  const int KT = static_cast<int>((g.K + GBK - 1) / GBK);
-  // Global loads are raw buffer loads from a descriptor rebased at this tile's first row:
-  // offsets past the tile's valid rows (or the sentinel used past K) read as zero, so edge
-  // tiles need no branches and the compiler can track each load's wait count exactly.
+  // K range of this workgroup: all of K, or one 64-aligned part of it (SPLIT)
+  int kbeg = 0, kend = static_cast<int>(g.K);
+  if constexpr (SPLIT) {
+    // the first part is the shorter (27/64 of the steps), so it usually finishes first and
+    // publishes its partial while the second part still computes
+    const int steps = static_cast<int>((g.K + GBK - 1) / GBK);
+    const int cut = (steps * 27 / 64) * GBK;
+    kbeg = khalf ? cut : 0;
+    kend = khalf ? kend : cut;
+  }
+  const int KT = (kend - kbeg + GBK - 1) / GBK;
+  // Operands go straight from memory into LDS (buffer loads with the lds bit): each wave
+  // instruction fills 1 KB of LDS, lane l writing bytes 16l..16l+15, i.e. 16 rows of 64 bytes.
+  // A lane fetches the global 16-byte chunk that the XOR swizzle of its LDS slot calls for.
+  // Descriptors are rebased at the tile's first row: offsets past the valid rows (or the
+  // sentinel used past K) read as zero, so edge tiles need no branches.
   const int rows_a = static_cast<int>(min<int64_t>(GBM, g.M - m0));
   const int rows_b = static_cast<int>(min<int64_t>(BN, g.N - n0));
   const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t*>(g.a + m0 * g.lda), 0, static_cast<int>(rows_a * g.lda), kBufferFlags);
   const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t*>(g.b + n0 * g.ldb), 0, static_cast<int>(rows_b * g.ldb), kBufferFlags);
-  int oa[ALD], ob[BLD], la[ALD], lb[BLD];
+  constexpr int ABLK = GBM / 16 / NW;   // 1 KB blocks of A per wave per stage
+  constexpr int BBLK = BN / 16 / NW;
+  constexpr int NDMA = ABLK + BBLK;     // direct-to-LDS loads per wave per stage
+  int oa[ABLK], ob[BBLK], ka[ABLK], kb[BBLK];
+  {
+    const int rr = lane >> 2;
 #pragma unroll
-  for (int j = 0; j < ALD; ++j) {
-    const int q = t + NT * j, row = q >> 2, ch = q & 3;
-    oa[j] = row * static_cast<int>(g.lda) + 16 * ch;
-    la[j] = lds_off(row, ch);
+    for (int i = 0; i < ABLK; ++i) {
+      const int row = 16 * (w + NW * i) + rr;
+      const int lc = (lane & 3) ^ ((row >> 2) & 3);   // logical chunk held by this LDS slot
+      oa[i] = row * static_cast<int>(g.lda) + 16 * lc;
+      ka[i] = 16 * lc;
+    }
+#pragma unroll
+    for (int i = 0; i < BBLK; ++i) {
+      const int row = 16 * (w + NW * i) + rr;
+      const int lc = (lane & 3) ^ ((row >> 2) & 3);
+      ob[i] = row * static_cast<int>(g.ldb) + 16 * lc;
+      kb[i] = 16 * lc;
+    }
   }
+  auto dma = [&](int kt, int8_t* stg) {
+    const int k0 = kbeg + kt * GBK;
 #pragma unroll
-  for (int j = 0; j < BLD; ++j) {
-    const int q = t + NT * j, row = q >> 2, ch = q & 3;
-    ob[j] = row * static_cast<int>(g.ldb) + 16 * ch;
-    lb[j] = A_BYTES + lds_off(row, ch);
-  }
-  const int kch = 16 * (t & 3);   // k offset of this thread's chunk within a step
-
-  v4i ra[2][ALD], rb[2][BLD];
-  auto load = [&](int kt, v4i (&xa)[ALD], v4i (&xb)[BLD]) {
-    const int k0 = kt * GBK;
-    const bool kin = (k0 + kch) < g.K;
+    for (int i = 0; i < ABLK; ++i)
+      lds_dma16(rsa, stg + (w + NW * i) * 1024, (k0 + ka[i] < kend) ? oa[i] + k0 : kOutOfRange);
 #pragma unroll
-    for (int j = 0; j < ALD; ++j)
-      xa[j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
-                                          rsa, kin ? oa[j] + k0 : kOutOfRange, 0, 0));
-#pragma unroll
-    for (int j = 0; j < BLD; ++j)
-      xb[j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
-                                          rsb, kin ? ob[j] + k0 : kOutOfRange, 0, 0));
-  };
-  auto store = [&](int buf, const v4i (&xa)[ALD], const v4i (&xb)[BLD]) {
-    int8_t* s = smem + buf * STAGE;
-#pragma unroll
-    for (int j = 0; j < ALD; ++j) *reinterpret_cast<v4i*>(s + la[j]) = xa[j];
-#pragma unroll
-    for (int j = 0; j < BLD; ++j) *reinterpret_cast<v4i*>(s + lb[j]) = xb[j];
+    for (int i = 0; i < BBLK; ++i)
+      lds_dma16(rsb, stg + A_BYTES + (w + NW * i) * 1024, (k0 + kb[i] < kend) ? ob[i] + k0 : kOutOfRange);
   };
   // fragment registers: two sets (ping-pong between the two 32-byte halves of a K step)
   v4i af[2][4], bf[2][NB];
-  auto frag = [&](int set, int buf, int ks) {
-    const int8_t* sa = smem + buf * STAGE;
+  auto frag = [&](int set, const int8_t* sa, int ks) {
     const int8_t* sb = sa + A_BYTES;
     const int ch = 2 * ks + (lane >> 5);
 #pragma unroll
@@ -244,52 +267,110 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 512 / GemmShape<BN>::NT) void ge
         acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[set][i], bf[set][j], acc[i][j], 0, 0, 0);
   };
 
-  // Pipeline: three LDS buffers, one barrier per K step.
-  //   At the start of step k, buffers k%3 and (k+1)%3 hold steps k and k+1 (visible), the
-  //   registers of stage (k+1)%2 hold the in-flight loads of step k+2, and fragment set 0 holds
-  //   step k's first half. Step k: issue the loads of step k+3 into stage k%2; read step k's
-  //   second half into set 1; MFMAs on set 0; read step k+1's first half into set 0 (its buffer
-  //   became visible at this step's barrier); MFMAs on set 1; write stage (k+1)%2 (step k+2)
-  //   into buffer (k+2)%3, which nobody reads any more; barrier.
-  // Loads and stores are unconditional: steps past K load zeros (out-of-range offsets), so
-  // every wait counts only the loads it needs.
-  auto step = [&](int k, v4i (&xa_new)[ALD], v4i (&xb_new)[BLD], const v4i (&xa_old)[ALD],
-                  const v4i (&xb_old)[BLD], int b0, int b1, int b2) {
-    load(k + 3, xa_new, xb_new);
-    frag(1, b0, 1);
+  // Pipeline: three LDS stages, one barrier per K step. At the start of step k, stage k%3 is
+  // complete and visible, fragment set 0 holds step k's first half, and the loads of step
+  // k+1 are in flight. Step k: start the loads of step k+2 into stage (k+2)%3 (last read in
+  // step k-1, whose reads every wave finished before that step's barrier); read step k's
+  // second half into set 1; MFMAs on set 0; wait for this wave's loads of step k+1 and its
+  // own reads of stage k, barrier (stage k+1 is now complete for every wave); read step
+  // k+1's first half into set 0; MFMAs on set 1. Loads past K read zeros.
+  auto step = [&](int k, int8_t* cur, int8_t* nxt, int8_t* far) {
+    dma(k + 2, far);
+    frag(1, cur, 1);
     __builtin_amdgcn_sched_barrier(0);
     mfma(0);
     __builtin_amdgcn_sched_barrier(0);
-    frag(0, b1, 0);
+    if constexpr (NDMA == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    frag(0, nxt, 0);
     __builtin_amdgcn_sched_barrier(0);
     mfma(1);
     __builtin_amdgcn_sched_barrier(0);
-    store(b2, xa_old, xb_old);
-    __syncthreads();
+  };
+  auto last = [&](const int8_t* cur) {
+    frag(1, cur, 1);
+    mfma(0);
+    mfma(1);
   };
 
-  load(0, ra[0], rb[0]);
-  load(1, ra[1], rb[1]);
-  store(0, ra[0], rb[0]);
-  store(1, ra[1], rb[1]);
-  load(2, ra[1], rb[1]);
-  __syncthreads();
-  frag(0, 0, 0);
-  // unrolled by two so the register stage is static; an odd last step is peeled after the
-  // loop (the two-step body is unconditional, which keeps the accumulators in AGPRs)
-  int kt = 0, b0 = 0, b1 = 1, b2 = 2;
-  for (; kt + 1 < KT; kt += 2) {
-    step(kt, ra[0], rb[0], ra[1], rb[1], b0, b1, b2);
-    step(kt + 1, ra[1], rb[1], ra[0], rb[0], b1, b2, b0);
-    const int t0 = b0;   // advance the buffer rotation by two
-    b0 = b2;
-    b2 = b1;
-    b1 = t0;
+  if (KT > 0) {
+    dma(0, st0);
+    dma(1, st1);
+    if constexpr (NDMA == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    frag(0, st0, 0);
+    // unrolled by three so every stage is a static LDS object (the compiler then waits only
+    // for the loads a read depends on); the up to three trailing steps run with stage pointers
+    // picked at run time, and the last step has no successor
+    int kt = 0;
+    for (; kt + 3 < KT; kt += 3) {
+      step(kt, st0, st1, st2);
+      step(kt + 1, st1, st2, st0);
+      step(kt + 2, st2, st0, st1);
+    }
+    auto stg = [&](int i) { return i == 0 ? st0 : (i == 1 ? st1 : st2); };
+    for (; kt + 1 < KT; ++kt) step(kt, stg(kt % 3), stg((kt + 1) % 3), stg((kt + 2) % 3));
+    last(stg(kt % 3));
   }
-  if (kt < KT) {
-    frag(1, b0, 1);
-    mfma(0);
-    mfma(1);
+  // every direct-to-LDS load (including the zero-filled ones past K) has landed before the
+  // epilogue reuses the stages
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  if constexpr (SPLIT) {
+    // Which part finishes the tile, with no waiting. Each part has a flag bit (first part 1,
+    // second part 2). A part that finds its partner's bit set adds the partner's published
+    // partial and finishes; otherwise it publishes its own partial, sets its bit, and
+    // finishes only if the partner's bit appeared meanwhile (the partner then saw no bit and
+    // published instead of finishing). Exactly one part finishes; the finisher clears the
+    // flag. Partials move with device-coherent (sc1) buffer stores and loads: the stores are
+    // complete (s_waitcnt) before the flag's atomic, and the loads issue after it, so no
+    // cache-wide writeback or invalidate is needed.
+    __shared__ int s_state;
+    constexpr int SLOT = NT * 4 * NB * 16 * 4;   // bytes of one partial tile
+    constexpr int kDeviceScope = 16;             // cache policy: sc1
+    const __amdgpu_buffer_rsrc_t rsp = __builtin_amdgcn_make_buffer_rsrc(
+        g.split_part + 2 * static_cast<int64_t>(tile_id) * (SLOT / 4), 0, 2 * SLOT, kBufferFlags);
+    const int mybit = 1 << khalf, otherbit = 1 << (khalf ^ 1);
+    int* flag = &g.split_cnt[tile_id];
+    if (t == 0) s_state = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    bool finish = (s_state & otherbit) != 0;
+    if (!finish) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const v4i x = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(v4u, x), rsp, khalf * SLOT + (((i * NB + j) * 4 + q) * NT + t) * 16, 0,
+                kDeviceScope);
+          }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (t == 0)
+        s_state = __hip_atomic_fetch_or(flag, mybit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      finish = (s_state & otherbit) != 0;
+      if (!finish) return;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const v4i x = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
+              rsp, (khalf ^ 1) * SLOT + (((i * NB + j) * 4 + q) * NT + t) * 16, 0, kDeviceScope));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += x[e];
+        }
+    if (t == 0) __hip_atomic_store(flag, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   if constexpr (EPI == EPI_I32) {
@@ -326,9 +407,11 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 512 / GemmShape<BN>::NT) void ge
         for (int r = 0; r < 16; ++r) acc[i][j][r] = __float_as_int(v[i][0][r]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    float* ep = reinterpret_cast<float*>(smem);
-    // 4 chunks: chunk c holds tile rows 32c..32c+31 (local 0..31, wave row 0) and
-    // 128+32c..128+32c+31 (local 32..63, wave row 1)
+    // 4 chunks: chunk c holds tile rows 32c..32c+31 (local 0..31, wave row 0, in stage 0)
+    // and 128+32c..128+32c+31 (local 32..63, wave row 1, in stage 1)
+    float* ep0 = reinterpret_cast<float*>(st0);
+    float* ep1 = reinterpret_cast<float*>(st1);
+    float* epw = wm ? ep1 : ep0;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       __syncthreads();
@@ -336,8 +419,8 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 512 / GemmShape<BN>::NT) void ge
       for (int j = 0; j < NB; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int lr = wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          ep[lr * EP + wn * WN + j * 32 + (lane & 31)] = __int_as_float(acc[c][j][r]);
+          const int lr = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          epw[lr * EP + wn * WN + j * 32 + (lane & 31)] = __int_as_float(acc[c][j][r]);
         }
       __syncthreads();
       if constexpr (!TRANS) {
@@ -348,8 +431,8 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 512 / GemmShape<BN>::NT) void ge
         float u0[SEG], u1[SEG];
 #pragma unroll
         for (int q = 0; q < SEG; q += 4) {
-          const float4 a0 = *reinterpret_cast<const float4*>(&ep[x * EP + s * SEG + q]);
-          const float4 a1 = *reinterpret_cast<const float4*>(&ep[(x + 32) * EP + s * SEG + q]);
+          const float4 a0 = *reinterpret_cast<const float4*>(&ep0[x * EP + s * SEG + q]);
+          const float4 a1 = *reinterpret_cast<const float4*>(&ep1[x * EP + s * SEG + q]);
           u0[q] = a0.x; u0[q + 1] = a0.y; u0[q + 2] = a0.z; u0[q + 3] = a0.w;
           u1[q] = a1.x; u1[q + 1] = a1.y; u1[q + 2] = a1.z; u1[q + 3] = a1.w;
         }
@@ -382,8 +465,8 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 512 / GemmShape<BN>::NT) void ge
         float u0[RPT], u1[RPT];
 #pragma unroll
         for (int q = 0; q < RPT; ++q) {
-          u0[q] = ep[(h * RPT + q) * EP + j];
-          u1[q] = ep[(32 + h * RPT + q) * EP + j];
+          u0[q] = ep0[(h * RPT + q) * EP + j];
+          u1[q] = ep1[(h * RPT + q) * EP + j];
         }
         if constexpr (KM > 128) {
 #pragma unroll
@@ -404,11 +487,11 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 512 / GemmShape<BN>::NT) void ge
   }
 }
 
-template <int BN, class Out, int EPI, int KM, int KN, bool TRANS>
+template <int BN, class Out, int EPI, int KM, int KN, bool TRANS, bool SPLIT = false>
 static hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
   const int64_t tiles = ((a.M + GBM - 1) / GBM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_i8_kernel<BN, Out, EPI, KM, KN, TRANS>), dim3(static_cast<int>(tiles)),
-                     dim3(GemmShape<BN>::NT), 0, st, a);
+  hipLaunchKernelGGL((gemm_i8_kernel<BN, Out, EPI, KM, KN, TRANS, SPLIT>),
+                     dim3(static_cast<int>(SPLIT ? 2 * tiles : tiles)), dim3(GemmShape<BN>::NT), 0, st, a);
   return hipGetLastError();
 }
 
@@ -425,6 +508,13 @@ static hipError_t launch_out(const GemmPass& p, const GemmArgs& a, hipStream_t s
   if (p.km == 1 && p.kn == 1) return launch_gemm<BN, Out, EPI_SCALE, 1, 1, false>(a, st);
   if (p.km != p.kn) return hipErrorInvalidValue;
   if constexpr (BN == 256) {
+    if (a.split_part) {
+      switch (p.km) {
+#define HQ_S(KK) case KK: return launch_gemm<BN, Out, EPI_SCALE, KK, KK, false, true>(a, st);
+        HQ_S(2) HQ_S(4) HQ_S(8) HQ_S(16) HQ_S(32) HQ_S(64) HQ_S(128) HQ_S(256)
+#undef HQ_S
+      }
+    }
     switch (p.km) {
 #define HQ_B(KK) case KK: return launch_gemm<BN, Out, EPI_SCALE, KK, KK, false>(a, st);
       HQ_B(2) HQ_B(4) HQ_B(8) HQ_B(16) HQ_B(32) HQ_B(64) HQ_B(128) HQ_B(256)
@@ -434,9 +524,32 @@ static hipError_t launch_out(const GemmPass& p, const GemmArgs& a, hipStream_t s
   return hipErrorInvalidValue;
 }
 
+int64_t gemm_split_tiles(int64_t M, int64_t N, int64_t K, int epi, int km, int kn, bool trans_out) {
+  if (epi != EPI_SCALE || trans_out || km <= 1 || kn <= 1 || K < 1024) return 0;
+  const int64_t tiles = ((M + GBM - 1) / GBM) * ((N + 255) / 256);
+  return tiles < 256 ? tiles : 0;
+}
+
+size_t gemm_split_bytes(int64_t tiles) {
+  // counters (rounded to 256 B), then two partial tiles of 512 threads x 128 int32 per tile
+  return static_cast<size_t>((tiles * 4 + 255) / 256 * 256) +
+         static_cast<size_t>(tiles) * 2 * 512 * 128 * 4;
+}
+
 hipError_t gemm_pass(const GemmPass& p, hipStream_t st) {
-  GemmArgs a{p.a, p.lda, p.b, p.ldb, p.M, p.N, p.K, p.c, p.ldc, p.sa, p.sb, p.kmul};
+  GemmArgs a{p.a, p.lda, p.b, p.ldb, p.M, p.N, p.K, p.c, p.ldc, p.sa, p.sb, p.kmul,
+             nullptr, nullptr};
   if (p.M == 0 || p.N == 0) return hipSuccess;
+  const int64_t split = gemm_split_tiles(p.M, p.N, p.K, p.epi, p.km, p.kn, p.trans_out);
+  if (split > 0) {
+    if (!p.split_ws) return hipErrorInvalidValue;
+    a.split_cnt = static_cast<int32_t*>(p.split_ws);
+    a.split_part = reinterpret_cast<int32_t*>(static_cast<char*>(p.split_ws) + (split * 4 + 255) / 256 * 256);
+    if (!p.split_cnt_zeroed) {
+      const hipError_t e = zero_i32(a.split_cnt, split, st);
+      if (e != hipSuccess) return e;
+    }
+  }
   // a tile's rows must be addressable by 32-bit buffer offsets
   if (static_cast<int64_t>(GBM) * p.lda >= kOutOfRange || 256 * p.ldb >= kOutOfRange)
     return hipErrorInvalidValue;

@@ -69,6 +69,8 @@ struct ProPass {
   int64_t ld = 0;
   int8_t* codes_t = nullptr;         // transposed codes (PRO_BOTH: of B X B; required)
   int64_t ld_t = 0;
+  int32_t* zero_ptr = nullptr;       // QUANT pass also zeroes these ints (for a later launch)
+  int64_t zero_n = 0;
 };
 int pro_grid(const ProPass& p);
 hipError_t pro_pass(const ProPass& p, int op, hipStream_t st);
@@ -101,8 +103,16 @@ struct GemmPass {
   int km = 1;              // EPI_SCALE: inverse rotation block along M (rows), 1 = none
   int kn = 1;              // EPI_SCALE: along N (columns); km == kn when both are set
   bool trans_out = false;  // EPI_SCALE: store c^T (N x M, pitch ldc); requires kn == 1
+  void* split_ws = nullptr;       // split-K workspace (gemm_split_bytes) when the split applies
+  bool split_cnt_zeroed = false;  // its counters were zeroed by an earlier launch on the stream
 };
 hipError_t gemm_pass(const GemmPass& p, hipStream_t st);
+// Number of 256 x 256 tiles of a GEMM that runs as two K halves (0: no split). The split is
+// taken when the output rotates along both axes (so tiles stay 256 x 256) and the tiles alone
+// would leave most CUs idle.
+int64_t gemm_split_tiles(int64_t M, int64_t N, int64_t K, int epi, int km, int kn, bool trans_out);
+size_t gemm_split_bytes(int64_t tiles);
+hipError_t zero_i32(int32_t* p, int64_t n, hipStream_t st);
 
 // Launch instrumentation (hq_profile.cpp): returns a token, or -1 when not recording.
 int prof_begin(int kind, double units, hipStream_t st);

@@ -50,7 +50,7 @@ int prof_begin(int kind, double units, hipStream_t st) {
 void prof_end(int idx, hipStream_t st) {
   if (idx < 0) return;
   std::lock_guard<std::mutex> lk(g_mu);
-  if (idx < static_cast<int>(g_recs.size())) hipEventRecord(g_recs[idx].b, st);
+  if (idx < static_cast<int>(g_recs.size())) (void)hipEventRecord(g_recs[idx].b, st);
 }
 
 }  // namespace hq

@@ -86,7 +86,15 @@ struct ProArgs {
   int64_t ld;
   int8_t* codes_t;          // transposed codes (pitch ld_t) or nullptr
   int64_t ld_t;
+  int32_t* zero_ptr;        // QUANT: block 0 zeroes these ints for a later launch
+  int64_t zero_n;
 };
+
+// Counters a later launch on the stream needs at zero (the split-K arrivals of the GEMM).
+__device__ inline void zero_side(const ProArgs& a) {
+  if (a.zero_n > 0 && blockIdx.x == 0)
+    for (int64_t i = threadIdx.x; i < a.zero_n; i += blockDim.x) a.zero_ptr[i] = 0;
+}
 
 // ================================================================ right rotation
 constexpr int RT_ROWS = 64, RT_COLS = 256, RT_THREADS = 256;
@@ -102,6 +110,7 @@ __global__ __launch_bounds__(RT_THREADS) void right_kernel(ProArgs a) {
   float sc = 0.0f, rinv = 0.0f;
   if constexpr (OP == OP_QUANT) {
     tensor_scale(a.part_in, a.nparts, a.step, a.qp, red, sc, rinv);
+    zero_side(a);
     if (blockIdx.x == 0 && t == 0) *a.scale_out = sc;
   }
   const int64_t rpad = (a.rows + 15) / 16 * 16;   // valid extent of a transposed row
@@ -155,6 +164,231 @@ __global__ __launch_bounds__(RT_THREADS) void right_kernel(ProArgs a) {
   }
 }
 
+// ================================================================ right rotation, full tiles
+// Used when the tensor is whole 64 x 256 tiles with 16-byte aligned rows. Persistent
+// workgroups walk the tiles and load the next tile's row segment into registers before
+// working on the current one, so memory and ALU overlap.
+constexpr int RF_ROWS = 64, RF_COLS = 256, RF_THREADS = 256, RF_GRID = 512;
+
+// v += sgn * v[lane ^ M] in one DPP instruction per value (quad permute, M = 1 or 2). With
+// sgn = +1 on the lower lane of each pair and -1 on the upper, the lower lane gets a + b and
+// the upper lane b - a, the negation of its butterfly output: each cross-lane stage flips the
+// sign its upper lanes hold, and the caller folds that sign into the quantizer (a max of
+// magnitudes is unaffected). The s_nop covers the VALU-write -> DPP-read hazard of whatever
+// ran before the block.
+template <int M>
+__device__ inline void xstage8(float& v0, float& v1, float& v2, float& v3, float& v4, float& v5,
+                               float& v6, float& v7, float sgn) {
+  if constexpr (M == 1) {
+    asm("s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %0, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %2, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %3, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %4, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %5, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %6, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, %7, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+        : "+v"(v0), "+v"(v1), "+v"(v2), "+v"(v3), "+v"(v4), "+v"(v5), "+v"(v6), "+v"(v7)
+        : "v"(sgn));
+  } else {
+    asm("s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %0, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %2, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %3, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %4, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %5, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %6, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, %7, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+        : "+v"(v0), "+v"(v1), "+v"(v2), "+v"(v3), "+v"(v4), "+v"(v5), "+v"(v6), "+v"(v7)
+        : "v"(sgn));
+  }
+}
+
+template <int M>
+__device__ inline void xstage_signed(float (&v)[64], float sgn) {
+#pragma unroll
+  for (int i = 0; i < 64; i += 8)
+    xstage8<M>(v[i], v[i + 1], v[i + 2], v[i + 3], v[i + 4], v[i + 5], v[i + 6], v[i + 7], sgn);
+}
+
+// 64 raw elements (4*bytes uint4) to fp32, with the stride-1 butterfly applied when K >= 2
+// (v_dot2 on the packed pairs of 16-bit inputs).
+template <class In, int K>
+__device__ inline void unpack64(const uint4 (&c)[4 * In::bytes], float (&v)[64]) {
+  if constexpr (In::bytes == 2) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint32_t w[4] = {c[q].x, c[q].y, c[q].z, c[q].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float* o = &v[8 * q + 2 * j];
+        if constexpr (K >= 2) {
+          if constexpr (In::is_bf16) {
+            typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+            const b2 x = __builtin_bit_cast(b2, w[j]);
+            o[0] = __builtin_amdgcn_fdot2_f32_bf16(x, __builtin_bit_cast(b2, 0x3F803F80u), 0.0f, false);
+            o[1] = __builtin_amdgcn_fdot2_f32_bf16(x, __builtin_bit_cast(b2, 0xBF803F80u), 0.0f, false);
+          } else {
+            typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+            const h2 x = __builtin_bit_cast(h2, w[j]);
+            o[0] = __builtin_amdgcn_fdot2(x, __builtin_bit_cast(h2, 0x3C003C00u), 0.0f, false);
+            o[1] = __builtin_amdgcn_fdot2(x, __builtin_bit_cast(h2, 0xBC003C00u), 0.0f, false);
+          }
+        } else {
+          o[0] = In::from_bits(static_cast<uint16_t>(w[j] & 0xFFFFu));
+          o[1] = In::from_bits(static_cast<uint16_t>(w[j] >> 16));
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      v[4 * q] = __uint_as_float(c[q].x);
+      v[4 * q + 1] = __uint_as_float(c[q].y);
+      v[4 * q + 2] = __uint_as_float(c[q].z);
+      v[4 * q + 3] = __uint_as_float(c[q].w);
+    }
+    if constexpr (K >= 2) fwht_inreg<2, 64>(v);
+  }
+}
+
+__host__ __device__ inline bool right_fast_ok(int64_t rows, int64_t cols, bool vec) {
+  return vec && rows > 0 && cols > 0 && rows % RF_ROWS == 0 && cols % RF_COLS == 0 &&
+         (rows / RF_ROWS) * (cols / RF_COLS) < (int64_t(1) << 31);
+}
+
+// Tile 64 x 256. Thread (r = t/4, s = t%4) owns 64 elements of row r, interleaved so that
+// each load instruction reads 64 contiguous bytes per row: its v[8j + i] is column
+// 32j + 8s + i (j, i < 8). Butterfly strides 1, 2, 4 (column bits 0-2) and 32, 64, 128 (bits
+// 5-7) are in-register; strides 8 and 16 (bits 3, 4 = lane bits 0, 1) are quad DPP stages.
+// Transposed codes: the dwords of four codes along a row are transposed as 4x4 byte blocks
+// across the four lanes that hold rows 4i..4i+3 (DPP row_ror:8, then row_shl/shr:4 with bank
+// masks, each followed by a v_perm), which leaves each lane four consecutive rows of one
+// column; these go to LDS as dwords (16-byte chunks XOR-swizzled so that both the dword
+// writes and the 16-byte reads are conflict-free) and leave as 64-byte rows of the transpose.
+__device__ inline int rf_swz(int c) { return ((c >> 2) & 3) ^ ((c >> 4) & 3); }
+
+template <int K>
+__device__ inline void right_stages(float (&v)[64], float sg1, float sg2) {
+#pragma unroll
+  for (int h = 2; h <= 4; h <<= 1) {       // column strides 2, 4 (stride 1 came with the load)
+    if (h < K) {
+#pragma unroll
+      for (int i = 0; i < 64; ++i)
+        if ((i & h) == 0) {
+          const float a = v[i], b = v[i + h];
+          v[i] = a + b;
+          v[i + h] = a - b;
+        }
+    }
+  }
+  if constexpr (K > 8) xstage_signed<1>(v, sg1);    // column stride 8
+  if constexpr (K > 16) xstage_signed<2>(v, sg2);   // column stride 16
+#pragma unroll
+  for (int h = 8; h <= 32; h <<= 1) {      // column strides 32, 64, 128
+    if (4 * h < K) {
+#pragma unroll
+      for (int i = 0; i < 64; ++i)
+        if ((i & h) == 0) {
+          const float a = v[i], b = v[i + h];
+          v[i] = a + b;
+          v[i + h] = a - b;
+        }
+    }
+  }
+}
+
+template <class In, int K, int OP>
+__global__ __launch_bounds__(RF_THREADS) void right_fast_kernel(ProArgs a) {
+  __shared__ __attribute__((aligned(16))) uint32_t tc[RF_COLS * 16];
+  __shared__ float red[32];
+  const int t = threadIdx.x, lane = t & 63;
+  const int r = t >> 2, s = t & 3;
+  const uint32_t nct = static_cast<uint32_t>(a.cols / RF_COLS);
+  const uint32_t tiles = static_cast<uint32_t>(a.rows / RF_ROWS) * nct;   // < 2^31 (host checks)
+  float sc = 0.0f, rinv = 0.0f;
+  if constexpr (OP == OP_QUANT) {
+    tensor_scale(a.part_in, a.nparts, a.step, a.qp, red, sc, rinv);
+    zero_side(a);
+    if (blockIdx.x == 0 && t == 0) *a.scale_out = sc;
+  }
+  constexpr int XMASK = K > 16 ? 3 : (K > 8 ? 1 : 0);
+  const float rr = (__builtin_popcount(lane & XMASK) & 1) ? -rinv : rinv;
+  const float lo = qlo(a.qp), hi = qhi(a.qp);
+  const float sg1 = (lane & 1) ? -1.0f : 1.0f, sg2 = (lane & 2) ? -1.0f : 1.0f;
+  constexpr int NQ = 4 * In::bytes;      // 16-byte chunks per thread per tile
+  constexpr int PER = 16 / In::bytes;    // elements per chunk
+  const char* src = static_cast<const char*>(a.src);
+  auto issue = [&](uint32_t tl, uint4 (&raw)[NQ]) {
+    const uint32_t tr = tl / nct;
+    const int64_t row = static_cast<int64_t>(tr) * RF_ROWS + r;
+    const int64_t col = static_cast<int64_t>(tl - tr * nct) * RF_COLS + 8 * s;
+    const char* p = src + (row * a.cols + col) * In::bytes;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)   // chunk q: columns 32*(q*PER/8) + 8s + (q*PER)%8 ...
+      raw[q] = *reinterpret_cast<const uint4*>(p + (32 * ((q * PER) / 8) + (q * PER) % 8) * In::bytes);
+  };
+  uint4 raw[NQ];
+  uint32_t tl = blockIdx.x;
+  if (tl < tiles) issue(tl, raw);
+  float amax = 0.0f;
+  for (; tl < tiles; tl += gridDim.x) {
+    uint4 cur[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) cur[q] = raw[q];
+    issue(tl + gridDim.x < tiles ? tl + gridDim.x : tl, raw);   // unconditional: the last re-reads
+    float v[64];
+    unpack64<In, K>(cur, v);
+    right_stages<K>(v, sg1, sg2);
+    if constexpr (OP == OP_ABSMAX) {
+#pragma unroll
+      for (int j = 0; j < 64; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    } else {
+      uint32_t d[16];   // d[g]: columns 32(g/2) + 8s + 4(g%2) + 0..3
+#pragma unroll
+      for (int g = 0; g < 16; ++g)
+        d[g] = qpack4(qbits(v[4 * g], rr, lo, hi), qbits(v[4 * g + 1], rr, lo, hi),
+                      qbits(v[4 * g + 2], rr, lo, hi), qbits(v[4 * g + 3], rr, lo, hi));
+      const uint32_t tr = tl / nct;
+      const int64_t row0 = static_cast<int64_t>(tr) * RF_ROWS;
+      const int64_t col0 = static_cast<int64_t>(tl - tr * nct) * RF_COLS;
+      if (a.codes) {
+        int8_t* dst = a.codes + (row0 + r) * a.ld + col0 + 8 * s;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) *reinterpret_cast<uint2*>(dst + 32 * j) = make_uint2(d[2 * j], d[2 * j + 1]);
+      }
+      if (a.codes_t) {
+        const int b = (lane >> 2) & 3;                       // row within the 4-row block
+        const uint32_t selA = (b < 2) ? 0x05040100u : 0x03020706u;
+        const uint32_t selB = (b & 1) ? 0x03070105u : 0x06020400u;
+        __syncthreads();   // the previous tile's readers of tc are done
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+          const uint32_t p = __builtin_amdgcn_update_dpp(0u, d[g], 0x128, 0xF, 0xF, false);   // lane ^ 8
+          const uint32_t x = __builtin_amdgcn_perm(p, d[g], selA);
+          uint32_t q = __builtin_amdgcn_update_dpp(0u, x, 0x104, 0xF, 0x5, false);           // lane + 4
+          q = __builtin_amdgcn_update_dpp(q, x, 0x114, 0xF, 0xA, false);                     // lane - 4
+          const uint32_t e = __builtin_amdgcn_perm(q, x, selB);
+          const int c = 32 * (g >> 1) + 8 * s + 4 * (g & 1) + b;
+          tc[c * 16 + ((r >> 2) ^ (4 * rf_swz(c)))] = e;
+        }
+        __syncthreads();
+        const int x = rf_swz(t);
+        uint4* dst = reinterpret_cast<uint4*>(a.codes_t + (col0 + t) * a.ld_t + row0);
+        const uint4* sp = reinterpret_cast<const uint4*>(&tc[t * 16]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dst[j] = sp[j ^ x];
+      }
+    }
+  }
+  if constexpr (OP == OP_ABSMAX) {
+    amax = block_max(amax, red);
+    if (t == 0) a.partials[blockIdx.x] = amax;
+  }
+}
+
 // ================================================================ left rotation
 constexpr int LT_THREADS = 256, LT_ELEMS = 16384;
 
@@ -180,6 +414,7 @@ __global__ __launch_bounds__(LT_THREADS) void left_kernel(ProArgs a) {
   float sc = 0.0f, rinv = 0.0f;
   if constexpr (OP == OP_QUANT) {
     tensor_scale(a.part_in, a.nparts, a.step, a.qp, red, sc, rinv);
+    zero_side(a);
     if (blockIdx.x == 0 && t == 0) *a.scale_out = sc;
   }
   const int64_t rpad = (a.rows + 15) / 16 * 16, cpad = (a.cols + 15) / 16 * 16;
@@ -341,6 +576,7 @@ __global__ __launch_bounds__(BT_THREADS) void both_kernel(ProArgs a) {
   if constexpr (OP == OP_QUANT) {
     tensor_scale(a.part_in, a.nparts, a.step, a.qp, red, s1, r1);
     tensor_scale(a.part_in2, a.nparts, a.step2, a.qp, red, sc2, r2);
+    zero_side(a);
     if (blockIdx.x == 0 && t == 0) {
       *a.scale_out = s1;
       *a.scale_out2 = sc2;
@@ -510,6 +746,7 @@ struct Launch;
   }
 
 HQ_PRO_DISPATCH(right_kernel, RT_THREADS)
+HQ_PRO_DISPATCH(right_fast_kernel, RF_THREADS)
 HQ_PRO_DISPATCH(left_kernel, LT_THREADS)
 HQ_PRO_DISPATCH(both_kernel, BT_THREADS)
 #undef HQ_PRO_DISPATCH
@@ -535,12 +772,16 @@ static ProArgs pro_args(const ProPass& p) {
   a.ld = p.ld;
   a.codes_t = p.codes_t;
   a.ld_t = p.ld_t;
+  a.zero_ptr = p.zero_ptr;
+  a.zero_n = p.zero_n;
   return a;
 }
 
 int pro_grid(const ProPass& p) {
   int64_t tiles;
   if (p.kind == PRO_RIGHT) {
+    if (right_fast_ok(p.rows, p.cols, pro_args(p).vec))
+      return grid_cap((p.rows / RF_ROWS) * (p.cols / RF_COLS), RF_GRID);
     tiles = ((p.rows + RT_ROWS - 1) / RT_ROWS) * ((p.cols + RT_COLS - 1) / RT_COLS);
   } else if (p.kind == PRO_LEFT) {
     const int tr = p.k > 64 ? p.k : 64, tc = LT_ELEMS / tr;
@@ -561,7 +802,9 @@ hipError_t pro_pass(const ProPass& p, int op, hipStream_t st) {
   if (op == OP_QUANT) outb = elems * ((p.codes ? 1 : 0) + (p.codes_t ? 1 : 0));
   const int tok = prof_begin(op == OP_ABSMAX ? K_ROT_ABSMAX : K_ROT_QUANT, inb + outb, st);
   hipError_t e = hipErrorInvalidValue;
-  if (p.kind == PRO_RIGHT) e = right_kernel_launch(p.in_dt, op, p.k, a, grid, st);
+  if (p.kind == PRO_RIGHT && right_fast_ok(p.rows, p.cols, a.vec))
+    e = right_fast_kernel_launch(p.in_dt, op, p.k, a, grid, st);
+  else if (p.kind == PRO_RIGHT) e = right_kernel_launch(p.in_dt, op, p.k, a, grid, st);
   else if (p.kind == PRO_LEFT) e = left_kernel_launch(p.in_dt, op, p.k, a, grid, st);
   else e = both_kernel_launch(p.in_dt, op, p.k, a, grid, st);
   prof_end(tok, st);

@@ -260,6 +260,12 @@ __global__ __launch_bounds__(kThreads) void zero_pad_kernel(int8_t* p, int64_t n
     p[(i / w) * ld + from + i % w] = 0;
 }
 
+__global__ __launch_bounds__(kThreads) void zero_i32_kernel(int32_t* p, int64_t n) {
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * kThreads)
+    p[i] = 0;
+}
+
 __global__ void write_scale_kernel(float* scale, const float* step) {
   *scale = step ? *step : 0.0f;
 }
@@ -463,6 +469,16 @@ hipError_t zero_pad(int8_t* p, int64_t nrows, int64_t ld, int64_t from, int64_t 
 hipError_t write_scale(float* scale, const float* step, hipStream_t st) {
   const int tok = prof_begin(K_MISC, 4.0, st);
   hipLaunchKernelGGL(write_scale_kernel, dim3(1), dim3(1), 0, st, scale, step);
+  prof_end(tok, st);
+  return hipGetLastError();
+}
+
+hipError_t zero_i32(int32_t* p, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + kThreads - 1) / kThreads;
+  const int grid = static_cast<int>(blocks < 1024 ? blocks : 1024);
+  const int tok = prof_begin(K_MISC, 4.0 * n, st);
+  hipLaunchKernelGGL(zero_i32_kernel, dim3(grid), dim3(kThreads), 0, st, p, n);
   prof_end(tok, st);
   return hipGetLastError();
 }

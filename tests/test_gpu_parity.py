@@ -115,6 +115,10 @@ def _rq(V_bits, dt, rows, cols, rot, k, bits, mode, step=None, codes=True, codes
     (B.HQ_ROT_RIGHT, 32, 77, 512),
     (B.HQ_ROT_RIGHT, 256, 129, 768),
     (B.HQ_ROT_RIGHT, 4, 33, 36),
+    (B.HQ_ROT_RIGHT, 256, 128, 512),     # whole 64 x 256 tiles: the persistent kernel
+    (B.HQ_ROT_RIGHT, 128, 192, 1024),
+    (B.HQ_ROT_RIGHT, 64, 64, 256),
+    (B.HQ_ROT_NONE, 1, 64, 512),
     (B.HQ_ROT_LEFT, 256, 512, 300),
     (B.HQ_ROT_LEFT, 16, 48, 200),
     (B.HQ_ROT_LEFT, 8, 24, 100),
@@ -124,7 +128,7 @@ def _rq(V_bits, dt, rows, cols, rot, k, bits, mode, step=None, codes=True, codes
     (B.HQ_ROT_BOTH, 16, 64, 48),
 ])
 @pytest.mark.parametrize("bits,mode", [(8, B.HQ_SCALE_ABSMAX), (4, B.HQ_SCALE_STEP)])
-@pytest.mark.parametrize("dt", [B.HQ_BF16, B.HQ_F16])
+@pytest.mark.parametrize("dt", [B.HQ_BF16, B.HQ_F16, B.HQ_F32])
 def test_rotate_quantize_parity(rot, k, rows, cols, bits, mode, dt):
     banner("rq", rot, k, rows, cols, bits, mode, dt)
     rng = np.random.default_rng(rows * 31 + cols + k)
@@ -255,6 +259,22 @@ def test_layer_variants_and_k(variant, k):
     h = host(res, cfg["out_dtype"])
     ora = run_oracle(cfg, inputs)
     compare_layer(cfg, h, ora, cfg["out_dtype"])
+
+
+@pytest.mark.parametrize("k,N,C,D", [(256, 256, 512, 1024), (16, 256, 512, 1040), (128, 512, 768, 2048)])
+def test_layer_split_k_dx(k, N, C, D):
+    """HALO-2 dX with few 256 x 256 tiles and K >= 1024 runs as two K halves (the second to
+    finish adds the partner's partial); a ragged K puts a short last step in the second
+    half. Two layers in a row also check that the arrival counters are left at zero."""
+    for rep in range(2):
+        cfg = WL.config(2, N=N, C=C, D=D, k=k)
+        banner("split-k", k, N, C, D, rep)
+        inputs = WL.make_inputs(cfg)
+        res = run_gpu(cfg, inputs, out_dt=O.F32)
+        h = host(res, O.F32)
+        for name, ref in outputs_from_gpu_codes(cfg, h).items():
+            err = rel_fro(h[name], ref)
+            assert err <= 1e-5, (name, err)
 
 
 def test_layer_deterministic():
