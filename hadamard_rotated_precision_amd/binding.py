@@ -65,6 +65,11 @@ def load(build_if_missing=True):
             raise RuntimeError("libhq.so is not built (run hadamard_rotated_precision_amd/build.py)")
         from . import build as _build
         _build.build()
+    # The device buffers and streams handed to libhq come from torch's HIP runtime. torch
+    # ships its own libamdhip64 (same soname as the system one); loading torch first makes
+    # libhq bind to that copy, so the process holds one HIP runtime, not two that do not
+    # share allocations.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     i32, i64, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
     P = ctypes.POINTER

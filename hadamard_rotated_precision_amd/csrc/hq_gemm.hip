@@ -40,7 +40,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
-constexpr int GBM = 256, GBK = 64;
+constexpr int GBM = 256;
 constexpr int kGroupM = 8;
 constexpr int kBufferFlags = 0x00020000;   // raw untyped buffer, 32-bit records
 constexpr int kOutOfRange = 0x7FFFFFF0;    // an offset past any descriptor: the load reads 0
@@ -67,8 +67,13 @@ __device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t rs, int8_t* lds, int vof
                                            voffset, 0, 0, 0);
 }
 
+// LDS layout of an operand stage: rows of KB bytes (KB = K bytes per step), the 16-byte chunk
+// index XOR-swizzled so that the 128-bit fragment reads of 16 consecutive rows hit 16
+// distinct 16-byte bank groups.
+template <int KB>
 __device__ inline int lds_off(int row, int chunk) {
-  return row * GBK + ((chunk ^ ((row >> 2) & 3)) << 4);
+  const int swz = (KB == 64) ? ((row >> 2) & 3) : ((row >> 1) & 7);
+  return row * KB + ((chunk ^ swz) << 4);
 }
 
 // In-register butterflies along the tile's M axis for row bits 0,1,3,4 (register index) and
@@ -157,14 +162,21 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 512 / GemmShape<BN>::NT) void ge
   constexpr int WN = 64;              // wave tile columns
   constexpr int NB = WN / 32;         // 32x32 blocks per wave along N
   constexpr int WCOLS = BN / WN;      // waves along N
+  // K bytes per step and LDS stages: 128 and two stages for 256-wide tiles (one barrier per
+  // 32 MFMAs per wave), 64 and three stages for 128-wide tiles (two workgroups per CU)
+  constexpr int GBK = BN == 256 ? 128 : 64;
+  constexpr int NST = BN == 256 ? 2 : 3;
+  constexpr int KS = GBK / 32;        // 32-byte K slices per step (one MFMA group each)
+  constexpr int KC = GBK / 16;        // 16-byte chunks per LDS row
+  constexpr int RPB = 1024 / GBK;     // rows per 1 KB direct-to-LDS block
   constexpr int A_BYTES = GBM * GBK, B_BYTES = BN * GBK, STAGE = A_BYTES + B_BYTES;
   constexpr int EP = BN + 4;          // epilogue LDS row pitch (floats)
-  // Three LDS stages, each its own LDS object so the compiler tracks which direct-to-LDS
-  // loads a fragment read has to wait for; the epilogue reuses stages 0 and 1 (32 rows each).
+  // LDS stages, each its own LDS object so the compiler tracks which direct-to-LDS loads a
+  // fragment read has to wait for; the epilogue reuses stages 0 and 1 (32 rows each).
   constexpr int STAGE_ALLOC = (STAGE > 32 * EP * 4) ? STAGE : 32 * EP * 4;
   __shared__ __attribute__((aligned(16))) int8_t st0[STAGE_ALLOC];
   __shared__ __attribute__((aligned(16))) int8_t st1[STAGE_ALLOC];
-  __shared__ __attribute__((aligned(16))) int8_t st2[STAGE_ALLOC];
+  __shared__ __attribute__((aligned(16))) int8_t st2[NST == 3 ? STAGE_ALLOC : 16];
 
   const int tiles_m = static_cast<int>((g.M + GBM - 1) / GBM);
   const int tiles_n = static_cast<int>((g.N + BN - 1) / BN);
@@ -217,23 +229,24 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 512 / GemmShape<BN>::NT) void ge
       const_cast<int8_t*>(g.a + m0 * g.lda), 0, static_cast<int>(rows_a * g.lda), kBufferFlags);
   const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<int8_t*>(g.b + n0 * g.ldb), 0, static_cast<int>(rows_b * g.ldb), kBufferFlags);
-  constexpr int ABLK = GBM / 16 / NW;   // 1 KB blocks of A per wave per stage
-  constexpr int BBLK = BN / 16 / NW;
-  constexpr int NDMA = ABLK + BBLK;     // direct-to-LDS loads per wave per stage
+  constexpr int ABLK = GBM / RPB / NW;   // 1 KB blocks of A per wave per stage
+  constexpr int BBLK = BN / RPB / NW;
+  constexpr int NDMA = ABLK + BBLK;      // direct-to-LDS loads per wave per stage
   int oa[ABLK], ob[BBLK], ka[ABLK], kb[BBLK];
   {
-    const int rr = lane >> 2;
+    const int rr = lane / KC, pc = lane % KC;
 #pragma unroll
     for (int i = 0; i < ABLK; ++i) {
-      const int row = 16 * (w + NW * i) + rr;
-      const int lc = (lane & 3) ^ ((row >> 2) & 3);   // logical chunk held by this LDS slot
+      const int row = RPB * (w + NW * i) + rr;
+      // logical chunk whose swizzled slot is this lane's (lds_off(row, lc) == block + 16 lane)
+      const int lc = pc ^ ((lds_off<GBK>(row, 0) >> 4) & (KC - 1));
       oa[i] = row * static_cast<int>(g.lda) + 16 * lc;
       ka[i] = 16 * lc;
     }
 #pragma unroll
     for (int i = 0; i < BBLK; ++i) {
-      const int row = 16 * (w + NW * i) + rr;
-      const int lc = (lane & 3) ^ ((row >> 2) & 3);
+      const int row = RPB * (w + NW * i) + rr;
+      const int lc = pc ^ ((lds_off<GBK>(row, 0) >> 4) & (KC - 1));
       ob[i] = row * static_cast<int>(g.ldb) + 16 * lc;
       kb[i] = 16 * lc;
     }
@@ -254,10 +267,10 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 512 / GemmShape<BN>::NT) void ge
     const int ch = 2 * ks + (lane >> 5);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      af[set][i] = *reinterpret_cast<const v4i*>(sa + lds_off(wm * 128 + i * 32 + (lane & 31), ch));
+      af[set][i] = *reinterpret_cast<const v4i*>(sa + lds_off<GBK>(wm * 128 + i * 32 + (lane & 31), ch));
 #pragma unroll
     for (int j = 0; j < NB; ++j)
-      bf[set][j] = *reinterpret_cast<const v4i*>(sb + lds_off(wn * WN + j * 32 + (lane & 31), ch));
+      bf[set][j] = *reinterpret_cast<const v4i*>(sb + lds_off<GBK>(wn * WN + j * 32 + (lane & 31), ch));
   };
   auto mfma = [&](int set) {
 #pragma unroll
@@ -267,53 +280,70 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 512 / GemmShape<BN>::NT) void ge
         acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[set][i], bf[set][j], acc[i][j], 0, 0, 0);
   };
 
-  // Pipeline: three LDS stages, one barrier per K step. At the start of step k, stage k%3 is
-  // complete and visible, fragment set 0 holds step k's first half, and the loads of step
-  // k+1 are in flight. Step k: start the loads of step k+2 into stage (k+2)%3 (last read in
-  // step k-1, whose reads every wave finished before that step's barrier); read step k's
-  // second half into set 1; MFMAs on set 0; wait for this wave's loads of step k+1 and its
-  // own reads of stage k, barrier (stage k+1 is now complete for every wave); read step
-  // k+1's first half into set 0; MFMAs on set 1. Loads past K read zeros.
-  auto step = [&](int k, int8_t* cur, int8_t* nxt, int8_t* far) {
-    dma(k + 2, far);
-    frag(1, cur, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma(0);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (NDMA == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  // Pipeline, one barrier per K step. At the start of step k, stage k is complete and
+  // visible, fragment set 0 holds its first K slice, and (three stages) the loads of step k+1
+  // are in flight. Step k: start the loads of step k+NST-1 into the stage last read in step
+  // k-1 (whose reads every wave finished before that step's barrier); alternate between
+  // reading the next slice into one fragment set and MFMAs on the other; before the last
+  // slice's MFMAs, wait for this wave's loads of step k+1 and its own reads of stage k, then
+  // barrier (stage k+1 is now complete for every wave) and read step k+1's first slice.
+  // Loads past K read zeros.
+  auto wait_next = [&]() {
+    if constexpr (NST == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if constexpr (NDMA == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+  };
+  auto step = [&](int k, int8_t* cur, int8_t* nxt, int8_t* far) {
+    dma(k + NST - 1, NST == 2 ? nxt : far);
+#pragma unroll
+    for (int ks = 1; ks < KS; ++ks) {
+      frag(ks & 1, cur, ks);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma((ks - 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_next();
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     frag(0, nxt, 0);
     __builtin_amdgcn_sched_barrier(0);
-    mfma(1);
+    mfma((KS - 1) & 1);
     __builtin_amdgcn_sched_barrier(0);
   };
   auto last = [&](const int8_t* cur) {
-    frag(1, cur, 1);
-    mfma(0);
-    mfma(1);
+#pragma unroll
+    for (int ks = 1; ks < KS; ++ks) {
+      frag(ks & 1, cur, ks);
+      mfma((ks - 1) & 1);
+    }
+    mfma((KS - 1) & 1);
   };
 
   if (KT > 0) {
     dma(0, st0);
-    dma(1, st1);
-    if constexpr (NDMA == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+    if constexpr (NST == 3) dma(1, st1);
+    wait_next();
     __builtin_amdgcn_s_barrier();
     frag(0, st0, 0);
-    // unrolled by three so every stage is a static LDS object (the compiler then waits only
-    // for the loads a read depends on); the up to three trailing steps run with stage pointers
-    // picked at run time, and the last step has no successor
+    // unrolled over the stages so every stage is a static LDS object (the compiler then waits
+    // only for the loads a read depends on); the trailing steps run with stage pointers picked
+    // at run time, and the last step has no successor
     int kt = 0;
-    for (; kt + 3 < KT; kt += 3) {
-      step(kt, st0, st1, st2);
-      step(kt + 1, st1, st2, st0);
-      step(kt + 2, st2, st0, st1);
+    if constexpr (NST == 3) {
+      for (; kt + 3 < KT; kt += 3) {
+        step(kt, st0, st1, st2);
+        step(kt + 1, st1, st2, st0);
+        step(kt + 2, st2, st0, st1);
+      }
+    } else {
+      for (; kt + 2 < KT; kt += 2) {
+        step(kt, st0, st1, st2);
+        step(kt + 1, st1, st0, st2);
+      }
     }
     auto stg = [&](int i) { return i == 0 ? st0 : (i == 1 ? st1 : st2); };
-    for (; kt + 1 < KT; ++kt) step(kt, stg(kt % 3), stg((kt + 1) % 3), stg((kt + 2) % 3));
-    last(stg(kt % 3));
+    for (; kt + 1 < KT; ++kt) step(kt, stg(kt % NST), stg((kt + 1) % NST), stg((kt + 2) % NST));
+    last(stg(kt % NST));
   }
   // every direct-to-LDS load (including the zero-filled ones past K) has landed before the
   // epilogue reuses the stages

@@ -31,6 +31,19 @@ def test_library_loads_and_exports_every_declared_symbol():
         assert hasattr(lib, s), s
 
 
+def test_one_hip_runtime_in_process():
+    """libhq binds to the HIP runtime torch loaded (the buffers and streams it gets are
+    torch's), so the process maps exactly one libamdhip64."""
+    B.load()
+    maps = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            path = line.split()[-1]
+            if "libamdhip64" in path:
+                maps.add(os.path.realpath(path))
+    assert len(maps) == 1, maps
+
+
 def test_version_status_pitch():
     assert B.hq_abi_version() == 1
     for code in range(12):
