@@ -13,6 +13,8 @@ namespace hq {
 enum DType : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 
 // ----------------------------------------------------------------- element formats
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 struct F32 {
   using storage = float;
   static constexpr int bytes = 4;
@@ -42,6 +44,11 @@ struct F16 {
   __device__ static inline void store(void* p, int64_t i, float v) {
     static_cast<uint16_t*>(p)[i] = to_bits(v);
   }
+  // Two values, each rounded to nearest even, packed low-first (one v_cvt_pk_f16_f32).
+  __device__ static inline uint32_t pack2(float a, float b) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, h2));
+  }
 };
 
 struct BF16 {
@@ -62,6 +69,11 @@ struct BF16 {
   }
   __device__ static inline void store(void* p, int64_t i, float v) {
     static_cast<uint16_t*>(p)[i] = to_bits(v);
+  }
+  // Two values, each rounded to nearest even, packed low-first (one v_cvt_pk_bf16_f32).
+  __device__ static inline uint32_t pack2(float a, float b) {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, b2));
   }
 };
 
@@ -113,9 +125,7 @@ __device__ inline void store_run(void* base, int64_t off, int64_t nvalid, const 
       } else {
         uint32_t w[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          w[j] = static_cast<uint32_t>(T::to_bits(u[q + 2 * j] * alpha)) |
-                 (static_cast<uint32_t>(T::to_bits(u[q + 2 * j + 1] * alpha)) << 16);
+        for (int j = 0; j < 4; ++j) w[j] = T::pack2(u[q + 2 * j] * alpha, u[q + 2 * j + 1] * alpha);
         *reinterpret_cast<uint4*>(p + 2 * q) = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
@@ -174,6 +184,26 @@ __device__ inline void fwht_xlane(float (&v)[N], int lane, int m) {
   for (int i = 0; i < N; ++i) {
     float p = xor_lane(v[i], m);
     v[i] = upper ? (p - v[i]) : (v[i] + p);
+  }
+}
+
+// Value of lane (lane ^ 1) / (lane ^ 2) within a quad, through DPP quad permutes.
+__device__ inline float quad_xor1(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+__device__ inline float quad_xor2(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
+
+// Butterfly stage across the lanes of a quad (m = 1 or 2): the lane with bit m clear keeps
+// a + b, the other keeps a - b (a = lower lane's value, b = upper lane's value).
+template <int N>
+__device__ inline void quad_stage(float (&v)[N], int lane, int m) {
+  const float sgn = (lane & m) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float p = (m == 1) ? quad_xor1(v[i]) : quad_xor2(v[i]);
+    v[i] = __builtin_fmaf(v[i], sgn, p);   // lower: v + p, upper: p - v
   }
 }
 

@@ -38,6 +38,7 @@ namespace hq {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 constexpr int GBM = 256;
@@ -79,8 +80,8 @@ __device__ inline int lds_off(int row, int chunk) {
 // In-register butterflies along the tile's M axis for row bits 0,1,3,4 (register index) and
 // 5,6 (row-block index), restricted to strides < KM. v[bi][bj][r]: row = 32*bi + 8*(r/4) +
 // 4*(lane/32) + r%4 within the wave's 128 rows.
-template <int KM, int NB>
-__device__ inline void rows_fwht_inlane(float (&v)[4][NB][16]) {
+template <int KM, int NB, class V>
+__device__ inline void rows_fwht_inlane(V (&v)[4][NB]) {
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi)
 #pragma unroll
@@ -121,8 +122,8 @@ __device__ inline void rows_fwht_inlane(float (&v)[4][NB][16]) {
 }
 
 // Row stride 4 <- lane bit 5: the pair lives in lanes l and l^32.
-template <int NB>
-__device__ inline void rows_fwht_lanehalf(float (&v)[4][NB][16], int lane) {
+template <int NB, class V>
+__device__ inline void rows_fwht_lanehalf(V (&v)[4][NB], int lane) {
   const float sgn = (lane & 32) ? -1.0f : 1.0f;
 #pragma unroll
   for (int bi = 0; bi < 4; ++bi)
@@ -149,31 +150,33 @@ __device__ inline void xlane_stage(float (&v)[N], int lane, int m) {
   }
 }
 
-// Threads of a workgroup for a 256 x BN tile: waves of 128 x 64 in a 2 x (BN/64) grid.
+// Threads of a workgroup for a 256 x BN tile: eight waves of 128 x WN in a 2 x (BN/WN) grid
+// (WN = 64 for 256-wide tiles, 32 for 128-wide ones), two waves per SIMD.
 template <int BN> struct GemmShape {
-  static constexpr int NW = 2 * (BN / 64);
+  static constexpr int WN = BN == 256 ? 64 : 32;
+  static constexpr int NW = 2 * (BN / WN);
   static constexpr int NT = 64 * NW;
 };
 
 template <int BN, class Out, int EPI, int KM, int KN, bool TRANS, bool SPLIT>
-__global__ __launch_bounds__(GemmShape<BN>::NT, 512 / GemmShape<BN>::NT) void gemm_i8_kernel(GemmArgs g) {
-  constexpr int NT = GemmShape<BN>::NT;   // 256 (BN=128) or 512 (BN=256): two waves per SIMD
+__global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs g) {
+  constexpr int NT = GemmShape<BN>::NT;   // 512: two waves per SIMD
   constexpr int NW = GemmShape<BN>::NW;
-  constexpr int WN = 64;              // wave tile columns
+  constexpr int WN = GemmShape<BN>::WN;   // wave tile columns
   constexpr int NB = WN / 32;         // 32x32 blocks per wave along N
   constexpr int WCOLS = BN / WN;      // waves along N
-  // K bytes per step and LDS stages: 128 and two stages for 256-wide tiles (one barrier per
-  // 32 MFMAs per wave), 64 and three stages for 128-wide tiles (two workgroups per CU)
-  constexpr int GBK = BN == 256 ? 128 : 64;
+  // K bytes per step and LDS stages: 128 bytes in two 64 KB stages for 256-wide tiles, in
+  // three 48 KB stages for 128-wide ones (one barrier per 32 or 16 MFMAs per wave)
+  constexpr int GBK = 128;
   constexpr int NST = BN == 256 ? 2 : 3;
   constexpr int KS = GBK / 32;        // 32-byte K slices per step (one MFMA group each)
   constexpr int KC = GBK / 16;        // 16-byte chunks per LDS row
   constexpr int RPB = 1024 / GBK;     // rows per 1 KB direct-to-LDS block
   constexpr int A_BYTES = GBM * GBK, B_BYTES = BN * GBK, STAGE = A_BYTES + B_BYTES;
-  constexpr int EP = BN + 4;          // epilogue LDS row pitch (floats)
   // LDS stages, each its own LDS object so the compiler tracks which direct-to-LDS loads a
-  // fragment read has to wait for; the epilogue reuses stages 0 and 1 (32 rows each).
-  constexpr int STAGE_ALLOC = (STAGE > 32 * EP * 4) ? STAGE : 32 * EP * 4;
+  // fragment read has to wait for; the epilogue reuses stages 0 and 1 (64 rows x BN fp32 each).
+  constexpr int STAGE_ALLOC = STAGE;
+  static_assert(64 * BN * 4 <= STAGE, "an epilogue round must fit one stage");
   __shared__ __attribute__((aligned(16))) int8_t st0[STAGE_ALLOC];
   __shared__ __attribute__((aligned(16))) int8_t st1[STAGE_ALLOC];
   __shared__ __attribute__((aligned(16))) int8_t st2[NST == 3 ? STAGE_ALLOC : 16];
@@ -210,10 +213,10 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 512 / GemmShape<BN>::NT) void ge
   // K range of this workgroup: all of K, or one 64-aligned part of it (SPLIT)
   int kbeg = 0, kend = static_cast<int>(g.K);
   if constexpr (SPLIT) {
-    // the first part is the shorter (27/64 of the steps), so it usually finishes first and
+    // the first part is the shorter (28/64 of the steps), so it usually finishes and
     // publishes its partial while the second part still computes
     const int steps = static_cast<int>((g.K + GBK - 1) / GBK);
-    const int cut = (steps * 27 / 64) * GBK;
+    const int cut = (steps * 28 / 64) * GBK;
     kbeg = khalf ? cut : 0;
     kend = khalf ? kend : cut;
   }
@@ -288,9 +291,10 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 512 / GemmShape<BN>::NT) void ge
   // slice's MFMAs, wait for this wave's loads of step k+1 and its own reads of stage k, then
   // barrier (stage k+1 is now complete for every wave) and read step k+1's first slice.
   // Loads past K read zeros.
+  static_assert(NST == 2 || NDMA == 6 || NDMA == 3, "three-stage waits cover 3 or 6 loads per stage");
   auto wait_next = [&]() {
     if constexpr (NST == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else if constexpr (NDMA == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else if constexpr (NDMA == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
   };
   auto step = [&](int k, int8_t* cur, int8_t* nxt, int8_t* far) {
@@ -418,100 +422,167 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 512 / GemmShape<BN>::NT) void ge
     return;
   } else {
     const float alpha = (*g.sa * *g.sb) * g.kmul;
-    // one 32-column block at a time: int32 -> fp32, row rotation in registers, and back into
-    // the accumulator registers as fp32 bit patterns (keeps the live set at one slice)
+    // (1) int32 -> fp32 in place, then the row (M) stages inside the accumulator layout
+    v16f fa[4][NB];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      float v[4][1][16];
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) v[i][0][r] = static_cast<float>(acc[i][j][r]);
-      if constexpr (KM > 1) {
-        rows_fwht_inlane<KM, 1>(v);
-        if constexpr (KM > 4) rows_fwht_lanehalf<1>(v, lane);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = __float_as_int(v[i][0][r]);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int j = 0; j < NB; ++j) fa[i][j] = __builtin_convertvector(acc[i][j], v16f);
+    if constexpr (KM > 1) {
+      rows_fwht_inlane<KM, NB>(fa);
+      if constexpr (KM > 4) rows_fwht_lanehalf<NB>(fa, lane);
     }
-    // 4 chunks: chunk c holds tile rows 32c..32c+31 (local 0..31, wave row 0, in stage 0)
-    // and 128+32c..128+32c+31 (local 32..63, wave row 1, in stage 1)
-    float* ep0 = reinterpret_cast<float*>(st0);
-    float* ep1 = reinterpret_cast<float*>(st1);
-    float* epw = wm ? ep1 : ep0;
+    // (2) two rounds through LDS, each holding 64 rows of both wave rows: rows 64 cc + [0, 64)
+    // of wave row 0 in stage 0, the same rows of wave row 1 (tile rows + 128) in stage 1.
+    // After the round's barrier a lane reads eight consecutive values of one output row from
+    // each stage, so the row stride 128 is an in-register butterfly, and eight neighbouring
+    // lanes cover 64 consecutive outputs: each 16-byte store instruction writes whole 128-byte
+    // lines.
+    float* const ep0 = reinterpret_cast<float*>(st0);
+    float* const ep1 = reinterpret_cast<float*>(st1);
+    float* const epw = wm ? ep1 : ep0;
+    const int hh = lane >> 5, lq = lane & 31;
+    const int s8 = lane & 7;
+    auto bit7 = [&](float (&u0)[8], float (&u1)[8]) {
+      if constexpr (KM > 128) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int lr = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          epw[lr * EP + wn * WN + j * 32 + (lane & 31)] = __int_as_float(acc[c][j][r]);
+        for (int q = 0; q < 8; ++q) {
+          const float a = u0[q], b = u1[q];
+          u0[q] = a + b;
+          u1[q] = a - b;
         }
-      __syncthreads();
-      if constexpr (!TRANS) {
-        // thread: local row pair (x, x+32), columns [s*BN/8, (s+1)*BN/8)
-        constexpr int TPR = NT / 32;              // threads per row pair (8 or 16)
-        constexpr int SEG = BN / TPR;             // 16 columns each
-        const int x = t / TPR, s = t % TPR;
-        float u0[SEG], u1[SEG];
+      }
+    };
+    if constexpr (TRANS) {
+      // Column-major rounds: element (row p < 64, column n) at n*64 + 4*((p/4) ^ (n%16)) + p%4:
+      // a lane's four consecutive rows of the accumulator layout go in as one 16-byte write,
+      // and both the writes and the reads below meet distinct bank groups. Lane (column n,
+      // s8) then takes rows 8 s8 + [0, 8) of column n: eight elements of output row n0 + n.
+      constexpr int PASSES = BN / 64;
 #pragma unroll
-        for (int q = 0; q < SEG; q += 4) {
-          const float4 a0 = *reinterpret_cast<const float4*>(&ep0[x * EP + s * SEG + q]);
-          const float4 a1 = *reinterpret_cast<const float4*>(&ep1[x * EP + s * SEG + q]);
-          u0[q] = a0.x; u0[q + 1] = a0.y; u0[q + 2] = a0.z; u0[q + 3] = a0.w;
-          u1[q] = a1.x; u1[q + 1] = a1.y; u1[q + 2] = a1.z; u1[q + 3] = a1.w;
+      for (int cc = 0; cc < 2; ++cc) {
+        __syncthreads();
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            const int col = wn * WN + j * 32 + lq;
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+              const int gq = 8 * ib + 2 * rq + hh;
+              const float4 x = {fa[2 * cc + ib][j][4 * rq], fa[2 * cc + ib][j][4 * rq + 1],
+                                fa[2 * cc + ib][j][4 * rq + 2], fa[2 * cc + ib][j][4 * rq + 3]};
+              *reinterpret_cast<float4*>(&epw[col * 64 + 4 * (gq ^ (col & 15))]) = x;
+            }
+          }
+        __syncthreads();
+#pragma unroll
+        for (int ps = 0; ps < PASSES; ++ps) {
+          const int n = 64 * ps + 8 * w + (lane >> 3);
+          float u0[8], u1[8];
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const int off = n * 64 + 4 * ((2 * s8 + k) ^ (n & 15));
+            const float4 a = *reinterpret_cast<const float4*>(&ep0[off]);
+            const float4 b = *reinterpret_cast<const float4*>(&ep1[off]);
+            u0[4 * k] = a.x; u0[4 * k + 1] = a.y; u0[4 * k + 2] = a.z; u0[4 * k + 3] = a.w;
+            u1[4 * k] = b.x; u1[4 * k + 1] = b.y; u1[4 * k + 2] = b.z; u1[4 * k + 3] = b.w;
+          }
+          bit7(u0, u1);
+          const int64_t orow = n0 + n;
+          const int64_t c0 = m0 + 64 * cc + 8 * s8, c1 = c0 + 128;
+          if (orow < g.N) {
+            store_run<Out, 8>(g.c, orow * g.ldc + c0, g.M - c0, u0, alpha);
+            store_run<Out, 8>(g.c, orow * g.ldc + c1, g.M - c1, u1, alpha);
+          }
         }
+      }
+    } else {
+      // Four row-major rounds, one 32-row block of each wave row per round, rows padded to
+      // BN + 4 floats (the 16-byte reads of two neighbouring rows by sixteen lanes meet
+      // distinct bank groups, and every address is a lane base plus an immediate). Lane (row
+      // x, s8) of wave half hh takes columns 64 jj + 8 s8 + [0, 8) of tile row
+      // 32 cc + x + 128 hh: lanes l and l + 32 hold rows 128 apart (row stride 128 = one
+      // v_permlane32_swap per value); column strides 1, 2, 4 and 64, 128 are in-register
+      // butterflies, 8, 16 and 32 cross the eight lanes of a row (quad DPP, then a
+      // bank-masked row shift).
+      constexpr int NJ = BN / 64;
+      constexpr int RP = BN + 4;           // padded row pitch (floats)
+      const int x = 4 * w + (lq >> 3);
+      const float* const epr = hh ? ep1 : ep0;
+      const float hsgn = hh ? -1.0f : 1.0f;
+      auto store_rows = [&](int cc, const float (&u)[NJ][8]) {
+        const int64_t orow = m0 + 128 * hh + 32 * cc + x;
+        if (orow < g.M) {
+#pragma unroll
+          for (int jj = 0; jj < NJ; ++jj) {
+            const int64_t cb = n0 + 64 * jj + 8 * s8;
+            store_run<Out, 8>(g.c, orow * g.ldc + cb, g.N - cb, u[jj], alpha);
+          }
+        }
+      };
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const int col = wn * WN + j * 32 + lq;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int pr = 8 * (r >> 2) + 4 * hh + (r & 3);
+            epw[pr * RP + col] = fa[cc][j][r];
+          }
+        }
+        __syncthreads();
+        float u[NJ][8];
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const float4 a = *reinterpret_cast<const float4*>(&epr[x * RP + 64 * jj + 8 * s8 + 4 * k]);
+            u[jj][4 * k] = a.x; u[jj][4 * k + 1] = a.y; u[jj][4 * k + 2] = a.z; u[jj][4 * k + 3] = a.w;
+          }
+        float* const f = &u[0][0];
         if constexpr (KM > 128) {
 #pragma unroll
-          for (int q = 0; q < SEG; ++q) {
-            const float a = u0[q], b = u1[q];
-            u0[q] = a + b;
-            u1[q] = a - b;
+          for (int q = 0; q < 8 * NJ; ++q) {
+            const unsigned xv = __float_as_uint(f[q]);
+            auto pr = __builtin_amdgcn_permlane32_swap(xv, xv, false, false);
+            f[q] = __builtin_fmaf(__uint_as_float(pr[1]), hsgn, __uint_as_float(pr[0]));
           }
         }
         if constexpr (KN > 1) {
-          fwht_inreg<KN, SEG>(u0);
-          fwht_inreg<KN, SEG>(u1);
 #pragma unroll
-          for (int m = 1; SEG * m < KN; m <<= 1) {
-            xlane_stage<SEG>(u0, lane, m);
-            xlane_stage<SEG>(u1, lane, m);
+          for (int jj = 0; jj < NJ; ++jj) fwht_inreg<KN, 8>(u[jj]);
+          if constexpr (KN > 8) quad_stage<8 * NJ>(*reinterpret_cast<float(*)[8 * NJ]>(f), lane, 1);
+          if constexpr (KN > 16) quad_stage<8 * NJ>(*reinterpret_cast<float(*)[8 * NJ]>(f), lane, 2);
+          if constexpr (KN > 32) {
+            // stride 32 = lane bit 2: the partner is lane ^ 4 (row shifts by four lanes, each
+            // written to the banks whose partner it fetches)
+            const float sg = (lane & 4) ? -1.0f : 1.0f;
+#pragma unroll
+            for (int q = 0; q < 8 * NJ; ++q) {
+              const uint32_t xv = __float_as_uint(f[q]);
+              uint32_t pv = __builtin_amdgcn_update_dpp(0u, xv, 0x104, 0xF, 0x5, false);   // lane + 4
+              pv = __builtin_amdgcn_update_dpp(pv, xv, 0x114, 0xF, 0xA, false);            // lane - 4
+              f[q] = __builtin_fmaf(f[q], sg, __uint_as_float(pv));
+            }
           }
-        }
-        const int64_t r0 = m0 + 32 * c + x, r1 = m0 + 128 + 32 * c + x;
-        const int64_t cb = n0 + s * SEG;
-        if (r0 < g.M) store_run<Out, SEG>(g.c, r0 * g.ldc + cb, g.N - cb, u0, alpha);
-        if (r1 < g.M) store_run<Out, SEG>(g.c, r1 * g.ldc + cb, g.N - cb, u1, alpha);
-      } else {
-        // transposed store: thread owns tile column j; output row n0+j, columns m (tile rows)
-        constexpr int TPC = NT / BN;                // threads per column (2)
-        constexpr int RPT = 32 / TPC;               // rows per thread in each half
-        const int j = t / TPC, h = t % TPC;
-        float u0[RPT], u1[RPT];
 #pragma unroll
-        for (int q = 0; q < RPT; ++q) {
-          u0[q] = ep0[(h * RPT + q) * EP + j];
-          u1[q] = ep1[(h * RPT + q) * EP + j];
-        }
-        if constexpr (KM > 128) {
+          for (int hb = 1; hb < NJ; hb <<= 1)
+            if (64 * hb < KN) {
 #pragma unroll
-          for (int q = 0; q < RPT; ++q) {
-            const float a = u0[q], b = u1[q];
-            u0[q] = a + b;
-            u1[q] = a - b;
-          }
+              for (int jj = 0; jj < NJ; ++jj)
+                if ((jj & hb) == 0)
+#pragma unroll
+                  for (int q = 0; q < 8; ++q) {
+                    const float a = u[jj][q], b = u[jj + hb][q];
+                    u[jj][q] = a + b;
+                    u[jj + hb][q] = a - b;
+                  }
+            }
         }
-        const int64_t orow = n0 + j;
-        const int64_t c0 = m0 + 32 * c + h * RPT, c1 = m0 + 128 + 32 * c + h * RPT;
-        if (orow < g.N) {
-          store_run<Out, RPT>(g.c, orow * g.ldc + c0, g.M - c0, u0, alpha);
-          store_run<Out, RPT>(g.c, orow * g.ldc + c1, g.M - c1, u1, alpha);
-        }
+        store_rows(cc, u);
       }
     }
   }

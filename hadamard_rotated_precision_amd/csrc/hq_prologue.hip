@@ -27,26 +27,6 @@
 
 namespace hq {
 
-// Value of lane (lane ^ 1) / (lane ^ 2) within a quad, through DPP quad permutes.
-__device__ inline float quad_xor1(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
-}
-__device__ inline float quad_xor2(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
-}
-
-// Butterfly stage across the lanes of a quad (m = 1 or 2): the lane with bit m clear keeps
-// a + b, the other keeps a - b (a = lower lane's value, b = upper lane's value).
-template <int N>
-__device__ inline void quad_stage(float (&v)[N], int lane, int m) {
-  const float sgn = (lane & m) ? -1.0f : 1.0f;
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const float p = (m == 1) ? quad_xor1(v[i]) : quad_xor2(v[i]);
-    v[i] = __builtin_fmaf(v[i], sgn, p);   // lower: v + p, upper: p - v
-  }
-}
-
 // 64 consecutive elements starting at element c0 of a row with n valid elements.
 template <class T>
 __device__ inline void load64(const void* row, int64_t c0, int64_t n, bool vec, float (&v)[64]) {
