@@ -37,7 +37,7 @@ hq_status check_cfg(const hq_config* cfg) {
 }
 
 // Workspace: the absmax partial arrays plus one spare device float, then (when the dX product
-// of a HALO-2 layer runs as two K halves) the split-K counters and partial tiles.
+// of a HALO-2 layer runs on paired 256 x 128 tiles) the pair flags and published tiles.
 size_t ws_need() { return kPartialBytes + kAlign; }
 
 int64_t dx_split_tiles(const hq_config* cfg, int64_t N, int64_t C, int64_t D) {
@@ -366,7 +366,7 @@ hq_status hq_linear_bwd_input(const void* dy, int32_t dy_dtype, int64_t N, int64
   hipStream_t st = static_cast<hipStream_t>(stream);
   Ws wsp(ws);
   const int32_t rg = g_rot(v);
-  // a split dX product needs its arrival counters at zero: the quantize pass clears them
+  // paired dX tiles need their arrival flags at zero: the quantize pass clears them
   const int64_t split = dx_split_tiles(cfg, N, C, D);
   HQ_CHECK(quantize_tensor(dy, dy_dtype, N, D, rg, k, cfg->bits, stepm ? step_g : nullptr,
                            save_g->codes, save_g->ld, save_g->codes_t, save_g->ld_t,

@@ -57,8 +57,8 @@ struct GemmArgs {
   const float* sa;
   const float* sb;
   float kmul;
-  int32_t* split_part;   // SPLIT: 2 int32 partial tiles per output tile
-  int32_t* split_cnt;    // SPLIT: arrival counter per output tile (zero on entry, left zero)
+  float* pair_part;      // PAIR: 2 fp32 partial tiles per pair of 256 x 128 tiles
+  int32_t* pair_cnt;     // PAIR: arrival flags per pair (zero on entry, left zero)
 };
 
 // One 16-byte buffer load per lane straight into LDS: lane l's bytes land at lds + 16 l
@@ -158,7 +158,7 @@ template <int BN> struct GemmShape {
   static constexpr int NT = 64 * NW;
 };
 
-template <int BN, class Out, int EPI, int KM, int KN, bool TRANS, bool SPLIT>
+template <int BN, class Out, int EPI, int KM, int KN, bool TRANS, bool PAIR>
 __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs g) {
   constexpr int NT = GemmShape<BN>::NT;   // 512: two waves per SIMD
   constexpr int NW = GemmShape<BN>::NW;
@@ -184,13 +184,8 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs 
   const int tiles_m = static_cast<int>((g.M + GBM - 1) / GBM);
   const int tiles_n = static_cast<int>((g.N + BN - 1) / BN);
   const int ntiles = tiles_m * tiles_n;
-  const int nblocks = SPLIT ? 2 * ntiles : ntiles;
   int pid = blockIdx.x;
-  if ((nblocks & 7) == 0) pid = (pid & 7) * (nblocks >> 3) + (pid >> 3);   // XCD-contiguous
-  // split-K: the two K parts of a tile are consecutive, so they share an XCD
-  const int khalf = SPLIT ? (pid & 1) : 0;
-  if constexpr (SPLIT) pid >>= 1;
-  const int tile_id = pid;
+  if ((ntiles & 7) == 0) pid = (pid & 7) * (ntiles >> 3) + (pid >> 3);   // XCD-contiguous
   const int group = pid / (kGroupM * tiles_n);
   const int first_m = group * kGroupM;
   const int gsize = min(tiles_m - first_m, kGroupM);
@@ -210,16 +205,7 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-  // K range of this workgroup: all of K, or one 64-aligned part of it (SPLIT)
-  int kbeg = 0, kend = static_cast<int>(g.K);
-  if constexpr (SPLIT) {
-    // the first part is the shorter (28/64 of the steps), so it usually finishes and
-    // publishes its partial while the second part still computes
-    const int steps = static_cast<int>((g.K + GBK - 1) / GBK);
-    const int cut = (steps * 28 / 64) * GBK;
-    kbeg = khalf ? cut : 0;
-    kend = khalf ? kend : cut;
-  }
+  const int kbeg = 0, kend = static_cast<int>(g.K);
   const int KT = (kend - kbeg + GBK - 1) / GBK;
   // Operands go straight from memory into LDS (buffer loads with the lds bit): each wave
   // instruction fills 1 KB of LDS, lane l writing bytes 16l..16l+15, i.e. 16 rows of 64 bytes.
@@ -354,59 +340,6 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  if constexpr (SPLIT) {
-    // Which part finishes the tile, with no waiting. Each part has a flag bit (first part 1,
-    // second part 2). A part that finds its partner's bit set adds the partner's published
-    // partial and finishes; otherwise it publishes its own partial, sets its bit, and
-    // finishes only if the partner's bit appeared meanwhile (the partner then saw no bit and
-    // published instead of finishing). Exactly one part finishes; the finisher clears the
-    // flag. Partials move with device-coherent (sc1) buffer stores and loads: the stores are
-    // complete (s_waitcnt) before the flag's atomic, and the loads issue after it, so no
-    // cache-wide writeback or invalidate is needed.
-    __shared__ int s_state;
-    constexpr int SLOT = NT * 4 * NB * 16 * 4;   // bytes of one partial tile
-    constexpr int kDeviceScope = 16;             // cache policy: sc1
-    const __amdgpu_buffer_rsrc_t rsp = __builtin_amdgcn_make_buffer_rsrc(
-        g.split_part + 2 * static_cast<int64_t>(tile_id) * (SLOT / 4), 0, 2 * SLOT, kBufferFlags);
-    const int mybit = 1 << khalf, otherbit = 1 << (khalf ^ 1);
-    int* flag = &g.split_cnt[tile_id];
-    if (t == 0) s_state = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    bool finish = (s_state & otherbit) != 0;
-    if (!finish) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const v4i x = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-            __builtin_amdgcn_raw_buffer_store_b128(
-                __builtin_bit_cast(v4u, x), rsp, khalf * SLOT + (((i * NB + j) * 4 + q) * NT + t) * 16, 0,
-                kDeviceScope);
-          }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (t == 0)
-        s_state = __hip_atomic_fetch_or(flag, mybit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __syncthreads();
-      finish = (s_state & otherbit) != 0;
-      if (!finish) return;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const v4i x = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(
-              rsp, (khalf ^ 1) * SLOT + (((i * NB + j) * 4 + q) * NT + t) * 16, 0, kDeviceScope));
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += x[e];
-        }
-    if (t == 0) __hip_atomic_store(flag, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-
   if constexpr (EPI == EPI_I32) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -511,16 +444,18 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs 
       const int x = 4 * w + (lq >> 3);
       const float* const epr = hh ? ep1 : ep0;
       const float hsgn = hh ? -1.0f : 1.0f;
-      auto store_rows = [&](int cc, const float (&u)[NJ][8]) {
+      // (store_rows: dn shifts the columns, for the pair finisher's lower / upper halves)
+      auto store_rows = [&](int cc, const float (&u)[NJ][8], int dn) {
         const int64_t orow = m0 + 128 * hh + 32 * cc + x;
         if (orow < g.M) {
 #pragma unroll
           for (int jj = 0; jj < NJ; ++jj) {
-            const int64_t cb = n0 + 64 * jj + 8 * s8;
+            const int64_t cb = n0 + dn + 64 * jj + 8 * s8;
             store_run<Out, 8>(g.c, orow * g.ldc + cb, g.N - cb, u[jj], alpha);
           }
         }
       };
+      float res[PAIR ? 4 : 1][NJ][8];   // PAIR: this tile's rotated values, kept for the exchange
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
         __syncthreads();
@@ -582,17 +517,95 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs 
                   }
             }
         }
-        store_rows(cc, u);
+        if constexpr (PAIR) {
+#pragma unroll
+          for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) res[cc][jj][q] = u[jj][q];
+        } else {
+          store_rows(cc, u, 0);
+        }
+      }
+      if constexpr (PAIR) {
+        // Column stride 128 of a 256-column rotation block spans the two 256 x 128 tiles of a
+        // pair (tn even = lower half). Which one finishes, with no waiting: each tile has a
+        // flag bit. A tile that finds its partner's bit set adds the partner's published
+        // (rotated, unscaled) values and finishes both halves; otherwise it publishes its own,
+        // sets its bit, and finishes only if the partner's bit appeared meanwhile (the partner
+        // then saw no bit and published instead of finishing). Exactly one tile finishes; the
+        // finisher clears the flag. Values move with device-coherent (sc1) buffer stores and
+        // loads: the stores are complete (s_waitcnt) before the flag's atomic, and the loads
+        // issue after it, so no cache-wide writeback or invalidate is needed.
+        __shared__ int s_state;
+        constexpr int SLOT = NT * 4 * NJ * 8 * 4;    // bytes of one published tile
+        constexpr int kDeviceScope = 16;              // cache policy: sc1
+        const int half = tn & 1;
+        const int64_t pair_id = static_cast<int64_t>(tm) * (tiles_n >> 1) + (tn >> 1);
+        const __amdgpu_buffer_rsrc_t rsp = __builtin_amdgcn_make_buffer_rsrc(
+            g.pair_part + pair_id * 2 * (SLOT / 4), 0, 2 * SLOT, kBufferFlags);
+        const int mybit = 1 << half, otherbit = 1 << (half ^ 1);
+        int* flag = &g.pair_cnt[pair_id];
+        auto slot = [&](int part, int cc, int jj, int k) {
+          return part * SLOT + (((cc * NJ + jj) * 2 + k) * NT + t) * 16;
+        };
+        __syncthreads();
+        if (t == 0) s_state = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        bool finish = (s_state & otherbit) != 0;
+        if (!finish) {
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+            for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+              for (int k = 0; k < 2; ++k) {
+                const float4 f = {res[cc][jj][4 * k], res[cc][jj][4 * k + 1], res[cc][jj][4 * k + 2],
+                                  res[cc][jj][4 * k + 3]};
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, f), rsp,
+                                                       slot(half, cc, jj, k), 0, kDeviceScope);
+              }
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          __syncthreads();
+          if (t == 0)
+            s_state = __hip_atomic_fetch_or(flag, mybit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __syncthreads();
+          finish = (s_state & otherbit) != 0;
+          if (!finish) return;
+        }
+        // finisher: lower half = own + partner (or partner + own), upper = lower-half value
+        // minus upper-half value; both halves of the 256-column block are stored here
+        const float sgn_own = half ? -1.0f : 1.0f;
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          float lo[NJ][8], up[NJ][8];
+#pragma unroll
+          for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+              const float4 f = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                  rsp, slot(half ^ 1, cc, jj, k), 0, kDeviceScope));
+              const float pv[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float own = res[cc][jj][4 * k + e];
+                lo[jj][4 * k + e] = own + pv[e];
+                up[jj][4 * k + e] = __builtin_fmaf(own, sgn_own, -sgn_own * pv[e]);
+              }
+            }
+          store_rows(cc, lo, -BN * half);
+          store_rows(cc, up, BN * (1 - half));
+        }
+        if (t == 0) __hip_atomic_store(flag, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
 }
 
-template <int BN, class Out, int EPI, int KM, int KN, bool TRANS, bool SPLIT = false>
+template <int BN, class Out, int EPI, int KM, int KN, bool TRANS, bool PAIR = false>
 static hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
   const int64_t tiles = ((a.M + GBM - 1) / GBM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_i8_kernel<BN, Out, EPI, KM, KN, TRANS, SPLIT>),
-                     dim3(static_cast<int>(SPLIT ? 2 * tiles : tiles)), dim3(GemmShape<BN>::NT), 0, st, a);
+  hipLaunchKernelGGL((gemm_i8_kernel<BN, Out, EPI, KM, KN, TRANS, PAIR>),
+                     dim3(static_cast<int>(tiles)), dim3(GemmShape<BN>::NT), 0, st, a);
   return hipGetLastError();
 }
 
@@ -608,14 +621,17 @@ static hipError_t launch_out(const GemmPass& p, const GemmArgs& a, hipStream_t s
   }
   if (p.km == 1 && p.kn == 1) return launch_gemm<BN, Out, EPI_SCALE, 1, 1, false>(a, st);
   if (p.km != p.kn) return hipErrorInvalidValue;
-  if constexpr (BN == 256) {
-    if (a.split_part) {
-      switch (p.km) {
-#define HQ_S(KK) case KK: return launch_gemm<BN, Out, EPI_SCALE, KK, KK, false, true>(a, st);
-        HQ_S(2) HQ_S(4) HQ_S(8) HQ_S(16) HQ_S(32) HQ_S(64) HQ_S(128) HQ_S(256)
-#undef HQ_S
-      }
+  if constexpr (BN == 128) {
+    // column blocks up to 128 wide rotate inside the tile; 256-wide ones span a tile pair
+    switch (p.km) {
+#define HQ_B(KK) case KK: return launch_gemm<BN, Out, EPI_SCALE, KK, KK, false>(a, st);
+      HQ_B(2) HQ_B(4) HQ_B(8) HQ_B(16) HQ_B(32) HQ_B(64) HQ_B(128)
+#undef HQ_B
+      case 256:
+        if (!a.pair_part) return hipErrorInvalidValue;
+        return launch_gemm<BN, Out, EPI_SCALE, 256, 256, false, true>(a, st);
     }
+  } else {
     switch (p.km) {
 #define HQ_B(KK) case KK: return launch_gemm<BN, Out, EPI_SCALE, KK, KK, false>(a, st);
       HQ_B(2) HQ_B(4) HQ_B(8) HQ_B(16) HQ_B(32) HQ_B(64) HQ_B(128) HQ_B(256)
@@ -625,38 +641,47 @@ static hipError_t launch_out(const GemmPass& p, const GemmArgs& a, hipStream_t s
   return hipErrorInvalidValue;
 }
 
-int64_t gemm_split_tiles(int64_t M, int64_t N, int64_t K, int epi, int km, int kn, bool trans_out) {
-  if (epi != EPI_SCALE || trans_out || km <= 1 || kn <= 1 || K < 1024) return 0;
-  const int64_t tiles = ((M + GBM - 1) / GBM) * ((N + 255) / 256);
-  return tiles < 256 ? tiles : 0;
+// 128-wide tiles when 256-wide ones would leave most CUs idle and every rotation fits: rows
+// always (a tile holds 256 rows), columns when the block is at most 128 wide or, for 256, by
+// pairing the two tiles of a block (N is then a multiple of 256: the rotated axis is a whole
+// number of blocks).
+static bool use_narrow(int64_t M, int64_t N, int kn, bool trans_out) {
+  const int64_t tiles256 = ((M + GBM - 1) / GBM) * ((N + 255) / 256);
+  if (tiles256 >= 256) return false;
+  return kn <= 128 || (kn == 256 && !trans_out && N % 256 == 0);
 }
 
-size_t gemm_split_bytes(int64_t tiles) {
-  // counters (rounded to 256 B), then two partial tiles of 512 threads x 128 int32 per tile
-  return static_cast<size_t>((tiles * 4 + 255) / 256 * 256) +
-         static_cast<size_t>(tiles) * 2 * 512 * 128 * 4;
+int64_t gemm_split_tiles(int64_t M, int64_t N, int64_t K, int epi, int km, int kn, bool trans_out) {
+  (void)K;
+  (void)km;
+  if (epi != EPI_SCALE || kn != 256 || !use_narrow(M, N, kn, trans_out)) return 0;
+  return ((M + GBM - 1) / GBM) * (N / 256);   // tile pairs
+}
+
+size_t gemm_split_bytes(int64_t pairs) {
+  // arrival flags (rounded to 256 B), then two published tiles of 512 threads x 64 fp32 per pair
+  return static_cast<size_t>((pairs * 4 + 255) / 256 * 256) +
+         static_cast<size_t>(pairs) * 2 * 512 * 64 * 4;
 }
 
 hipError_t gemm_pass(const GemmPass& p, hipStream_t st) {
   GemmArgs a{p.a, p.lda, p.b, p.ldb, p.M, p.N, p.K, p.c, p.ldc, p.sa, p.sb, p.kmul,
              nullptr, nullptr};
   if (p.M == 0 || p.N == 0) return hipSuccess;
-  const int64_t split = gemm_split_tiles(p.M, p.N, p.K, p.epi, p.km, p.kn, p.trans_out);
-  if (split > 0) {
+  const int64_t pairs = gemm_split_tiles(p.M, p.N, p.K, p.epi, p.km, p.kn, p.trans_out);
+  if (pairs > 0) {
     if (!p.split_ws) return hipErrorInvalidValue;
-    a.split_cnt = static_cast<int32_t*>(p.split_ws);
-    a.split_part = reinterpret_cast<int32_t*>(static_cast<char*>(p.split_ws) + (split * 4 + 255) / 256 * 256);
+    a.pair_cnt = static_cast<int32_t*>(p.split_ws);
+    a.pair_part = reinterpret_cast<float*>(static_cast<char*>(p.split_ws) + (pairs * 4 + 255) / 256 * 256);
     if (!p.split_cnt_zeroed) {
-      const hipError_t e = zero_i32(a.split_cnt, split, st);
+      const hipError_t e = zero_i32(a.pair_cnt, pairs, st);
       if (e != hipSuccess) return e;
     }
   }
   // a tile's rows must be addressable by 32-bit buffer offsets
   if (static_cast<int64_t>(GBM) * p.lda >= kOutOfRange || 256 * p.ldb >= kOutOfRange)
     return hipErrorInvalidValue;
-  // 256-wide tiles unless that leaves most CUs idle and no column rotation needs the width
-  const int64_t tiles256 = ((p.M + GBM - 1) / GBM) * ((p.N + 255) / 256);
-  const bool narrow = p.kn <= 1 && tiles256 < 256;
+  const bool narrow = use_narrow(p.M, p.N, p.epi == EPI_I32 ? 1 : p.kn, p.trans_out);
   const int tok = prof_begin(K_GEMM, 2.0 * p.M * p.N * p.K, st);
   hipError_t e = hipErrorInvalidValue;
   if (p.epi == EPI_I32) {

@@ -103,15 +103,15 @@ struct GemmPass {
   int km = 1;              // EPI_SCALE: inverse rotation block along M (rows), 1 = none
   int kn = 1;              // EPI_SCALE: along N (columns); km == kn when both are set
   bool trans_out = false;  // EPI_SCALE: store c^T (N x M, pitch ldc); requires kn == 1
-  void* split_ws = nullptr;       // split-K workspace (gemm_split_bytes) when the split applies
-  bool split_cnt_zeroed = false;  // its counters were zeroed by an earlier launch on the stream
+  void* split_ws = nullptr;       // tile-pair workspace (gemm_split_bytes) when pairing applies
+  bool split_cnt_zeroed = false;  // its arrival flags were zeroed by an earlier launch on the stream
 };
 hipError_t gemm_pass(const GemmPass& p, hipStream_t st);
-// Number of 256 x 256 tiles of a GEMM that runs as two K halves (0: no split). The split is
-// taken when the output rotates along both axes (so tiles stay 256 x 256) and the tiles alone
-// would leave most CUs idle.
+// Number of tile pairs of a GEMM whose 256-wide column rotation spans two 256 x 128 tiles
+// (0: none). Pairing is taken when 256-wide tiles would leave most CUs idle; the two tiles of a
+// pair exchange their rotated values through the workspace and one of them finishes both.
 int64_t gemm_split_tiles(int64_t M, int64_t N, int64_t K, int epi, int km, int kn, bool trans_out);
-size_t gemm_split_bytes(int64_t tiles);
+size_t gemm_split_bytes(int64_t pairs);
 hipError_t zero_i32(int32_t* p, int64_t n, hipStream_t st);
 
 // Launch instrumentation (hq_profile.cpp): returns a token, or -1 when not recording.

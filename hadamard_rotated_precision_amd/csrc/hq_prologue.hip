@@ -477,6 +477,146 @@ __global__ __launch_bounds__(LT_THREADS) void left_kernel(ProArgs a) {
   }
 }
 
+// ================================================================ left rotation, full tiles
+// Used when rows are whole 256-row tiles and columns whole 64-column tiles of 16-bit inputs
+// with 16-byte aligned rows. Persistent workgroups walk 256 x 64 tiles; the raw bytes of the
+// next tile are loaded into registers before the current tile is worked on. A tile is staged
+// in LDS as fp32 (column index XOR-swizzled by 16 * (row / 64), so the column reads below are
+// conflict-free); thread (column c, part p) then takes the 64 consecutive tokens 64 p + [0, 64)
+// of column c: token strides 1..32 are in-register butterflies, 64 and 128 are one-instruction
+// quad DPP stages (v_fmac_dpp, the upper lane's sign folded into the quantizer).
+// Transposed codes leave directly as 64 consecutive tokens; row-major codes are transposed as
+// 4 x 4 byte blocks across the lanes of four neighbouring columns (DPP + v_perm) and
+// assembled in LDS into 64-byte rows.
+constexpr int LF_ROWS = 256, LF_COLS = 64, LF_THREADS = 256, LF_PITCH = LF_COLS + 4, LF_GRID = 512;
+
+// Dword slot swizzle of the 256 x 64-byte code tile: a row's sixteen 4-column groups are
+// permuted so that both the transposed writes (rows 64 p + 4 g + b) and the row reads meet
+// distinct banks.
+__device__ inline int lf_swz(int row) { return (row & 15) ^ ((row >> 4) & 3) ^ (4 * ((row >> 6) & 3)); }
+
+__host__ __device__ inline bool left_fast_ok(int64_t rows, int64_t cols, bool vec, int in_bytes) {
+  return vec && in_bytes == 2 && rows > 0 && cols > 0 && rows % LF_ROWS == 0 && cols % LF_COLS == 0 &&
+         (rows / LF_ROWS) * (cols / LF_COLS) < (int64_t(1) << 31);
+}
+
+template <class In, int K, int OP>
+__global__ __launch_bounds__(LF_THREADS, 2) void left_fast_kernel(ProArgs a) {
+  if constexpr (In::bytes != 2) {
+    return;   // never launched: left_fast_ok admits 16-bit inputs only
+  } else {
+  __shared__ __attribute__((aligned(16))) float tile[LF_ROWS * LF_PITCH];
+  __shared__ float red[32];
+  const int t = threadIdx.x, lane = t & 63;
+  const int c = t >> 2, p = t & 3;              // column of the tile, 64-token part
+  const uint32_t nct = static_cast<uint32_t>(a.cols / LF_COLS);
+  const uint32_t tiles = static_cast<uint32_t>(a.rows / LF_ROWS) * nct;   // < 2^31 (host checks)
+  float sc = 0.0f, rinv = 0.0f;
+  if constexpr (OP == OP_QUANT) {
+    tensor_scale(a.part_in, a.nparts, a.step, a.qp, red, sc, rinv);
+    zero_side(a);
+    if (blockIdx.x == 0 && t == 0) *a.scale_out = sc;
+  }
+  constexpr int XMASK = K > 128 ? 3 : (K > 64 ? 1 : 0);
+  const float rr = (__builtin_popcount(lane & XMASK) & 1) ? -rinv : rinv;
+  const float lo = qlo(a.qp), hi = qhi(a.qp);
+  const float sg1 = (lane & 1) ? -1.0f : 1.0f, sg2 = (lane & 2) ? -1.0f : 1.0f;
+  const char* src = static_cast<const char*>(a.src);
+  // global loads: eight 16-byte chunks per thread, row 32 q + t / 8, columns 8 (t % 8) + [0, 8)
+  const int lr = t >> 3, lc = 8 * (t & 7);
+  auto issue = [&](uint32_t tl, uint4 (&raw)[8]) {
+    const uint32_t tr = tl / nct;
+    const int64_t row = static_cast<int64_t>(tr) * LF_ROWS + lr;
+    const int64_t col = static_cast<int64_t>(tl - tr * nct) * LF_COLS + lc;
+    const char* q0 = src + (row * a.cols + col) * 2;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) raw[q] = *reinterpret_cast<const uint4*>(q0 + static_cast<int64_t>(32 * q) * a.cols * 2);
+  };
+  const int rbase = 64 * p * LF_PITCH + (c ^ (16 * p));   // this thread's column in part p
+  uint4 raw[8];
+  uint32_t tl = blockIdx.x;
+  if (tl < tiles) issue(tl, raw);
+  float amax = 0.0f;
+  for (; tl < tiles; tl += gridDim.x) {
+    uint4 cur[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) cur[q] = raw[q];
+    issue(tl + gridDim.x < tiles ? tl + gridDim.x : tl, raw);   // unconditional: the last re-reads
+    __syncthreads();   // the previous tile's readers of the LDS tile are done
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int row = 32 * q + lr;
+      const uint32_t w[4] = {cur[q].x, cur[q].y, cur[q].z, cur[q].w};
+      float f[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f[2 * j] = In::from_bits(static_cast<uint16_t>(w[j] & 0xFFFFu));
+        f[2 * j + 1] = In::from_bits(static_cast<uint16_t>(w[j] >> 16));
+      }
+      float* d = &tile[row * LF_PITCH + (lc ^ (16 * (row >> 6)))];
+      *reinterpret_cast<float4*>(d) = make_float4(f[0], f[1], f[2], f[3]);
+      *reinterpret_cast<float4*>(d + 4) = make_float4(f[4], f[5], f[6], f[7]);
+    }
+    __syncthreads();
+    float v[64];
+#pragma unroll
+    for (int i = 0; i < 64; ++i) v[i] = tile[rbase + i * LF_PITCH];
+    fwht_inreg<K, 64>(v);
+    if constexpr (K > 64) xstage_signed<1>(v, sg1);
+    if constexpr (K > 128) xstage_signed<2>(v, sg2);
+    if constexpr (OP == OP_ABSMAX) {
+#pragma unroll
+      for (int i = 0; i < 64; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    } else {
+      uint32_t d[16];   // d[g]: tokens 64 p + 4 g + [0, 4) of column c
+#pragma unroll
+      for (int g = 0; g < 16; ++g)
+        d[g] = qpack4(qbits(v[4 * g], rr, lo, hi), qbits(v[4 * g + 1], rr, lo, hi),
+                      qbits(v[4 * g + 2], rr, lo, hi), qbits(v[4 * g + 3], rr, lo, hi));
+      const uint32_t tr = tl / nct;
+      const int64_t row0 = static_cast<int64_t>(tr) * LF_ROWS;
+      const int64_t col0 = static_cast<int64_t>(tl - tr * nct) * LF_COLS;
+      if (a.codes_t) {
+        uint4* dst = reinterpret_cast<uint4*>(a.codes_t + (col0 + c) * a.ld_t + row0 + 64 * p);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dst[j] = make_uint4(d[4 * j], d[4 * j + 1], d[4 * j + 2], d[4 * j + 3]);
+      }
+      if (a.codes) {
+        // 4 x 4 byte transpose across the lanes of columns 4m .. 4m+3 (lane bits 2, 3): lane
+        // b = (lane >> 2) & 3 ends with the codes of columns 4m .. 4m+3 of token 4 g + b
+        const int b = (lane >> 2) & 3;
+        const uint32_t selA = (b < 2) ? 0x05040100u : 0x03020706u;
+        const uint32_t selB = (b & 1) ? 0x03070105u : 0x06020400u;
+        uint32_t* ct = reinterpret_cast<uint32_t*>(tile);   // code tile: 256 rows x 64 bytes
+        __syncthreads();   // every thread has read its column of the fp32 tile
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+          const uint32_t pv = __builtin_amdgcn_update_dpp(0u, d[g], 0x128, 0xF, 0xF, false);   // lane ^ 8
+          const uint32_t x = __builtin_amdgcn_perm(pv, d[g], selA);
+          uint32_t q = __builtin_amdgcn_update_dpp(0u, x, 0x104, 0xF, 0x5, false);           // lane + 4
+          q = __builtin_amdgcn_update_dpp(q, x, 0x114, 0xF, 0xA, false);                     // lane - 4
+          const uint32_t e = __builtin_amdgcn_perm(q, x, selB);
+          const int row = 64 * p + 4 * g + b;
+          ct[row * 16 + ((c >> 2) ^ lf_swz(row))] = e;
+        }
+        __syncthreads();
+        // thread t: tile row t, 64 bytes
+        uint32_t e[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) e[j] = ct[t * 16 + (j ^ lf_swz(t))];
+        uint4* dst = reinterpret_cast<uint4*>(a.codes + (row0 + t) * a.ld + col0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dst[j] = make_uint4(e[4 * j], e[4 * j + 1], e[4 * j + 2], e[4 * j + 3]);
+      }
+    }
+  }
+  if constexpr (OP == OP_ABSMAX) {
+    amax = block_max(amax, red);
+    if (t == 0) a.partials[blockIdx.x] = amax;
+  }
+  }
+}
+
 // ================================================================ both (X under HALO-2)
 constexpr int BT = 256, BT_THREADS = 512, BT_HALF = 128, BT_PITCH = BT_HALF + 4;
 
@@ -728,6 +868,7 @@ struct Launch;
 HQ_PRO_DISPATCH(right_kernel, RT_THREADS)
 HQ_PRO_DISPATCH(right_fast_kernel, RF_THREADS)
 HQ_PRO_DISPATCH(left_kernel, LT_THREADS)
+HQ_PRO_DISPATCH(left_fast_kernel, LF_THREADS)
 HQ_PRO_DISPATCH(both_kernel, BT_THREADS)
 #undef HQ_PRO_DISPATCH
 
@@ -764,6 +905,8 @@ int pro_grid(const ProPass& p) {
       return grid_cap((p.rows / RF_ROWS) * (p.cols / RF_COLS), RF_GRID);
     tiles = ((p.rows + RT_ROWS - 1) / RT_ROWS) * ((p.cols + RT_COLS - 1) / RT_COLS);
   } else if (p.kind == PRO_LEFT) {
+    if (left_fast_ok(p.rows, p.cols, pro_args(p).vec, dtb(p.in_dt)))
+      return grid_cap((p.rows / LF_ROWS) * (p.cols / LF_COLS), LF_GRID);
     const int tr = p.k > 64 ? p.k : 64, tc = LT_ELEMS / tr;
     tiles = ((p.rows + tr - 1) / tr) * ((p.cols + tc - 1) / tc);
   } else {
@@ -785,6 +928,8 @@ hipError_t pro_pass(const ProPass& p, int op, hipStream_t st) {
   if (p.kind == PRO_RIGHT && right_fast_ok(p.rows, p.cols, a.vec))
     e = right_fast_kernel_launch(p.in_dt, op, p.k, a, grid, st);
   else if (p.kind == PRO_RIGHT) e = right_kernel_launch(p.in_dt, op, p.k, a, grid, st);
+  else if (p.kind == PRO_LEFT && left_fast_ok(p.rows, p.cols, a.vec, dtb(p.in_dt)))
+    e = left_fast_kernel_launch(p.in_dt, op, p.k, a, grid, st);
   else if (p.kind == PRO_LEFT) e = left_kernel_launch(p.in_dt, op, p.k, a, grid, st);
   else e = both_kernel_launch(p.in_dt, op, p.k, a, grid, st);
   prof_end(tok, st);

@@ -123,6 +123,9 @@ def _rq(V_bits, dt, rows, cols, rot, k, bits, mode, step=None, codes=True, codes
     (B.HQ_ROT_LEFT, 16, 48, 200),
     (B.HQ_ROT_LEFT, 8, 24, 100),
     (B.HQ_ROT_LEFT, 128, 256, 64),
+    (B.HQ_ROT_LEFT, 256, 512, 192),      # whole 256 x 64 tiles: the persistent kernel
+    (B.HQ_ROT_LEFT, 64, 768, 128),
+    (B.HQ_ROT_LEFT, 2, 256, 64),
     (B.HQ_ROT_BOTH, 256, 512, 512),
     (B.HQ_ROT_BOTH, 128, 256, 384),
     (B.HQ_ROT_BOTH, 16, 64, 48),
@@ -261,14 +264,16 @@ def test_layer_variants_and_k(variant, k):
     compare_layer(cfg, h, ora, cfg["out_dtype"])
 
 
-@pytest.mark.parametrize("k,N,C,D", [(256, 256, 512, 1024), (16, 256, 512, 1040), (128, 512, 768, 2048)])
-def test_layer_split_k_dx(k, N, C, D):
-    """HALO-2 dX with few 256 x 256 tiles and K >= 1024 runs as two K halves (the second to
-    finish adds the partner's partial); a ragged K puts a short last step in the second
-    half. Two layers in a row also check that the arrival counters are left at zero."""
+@pytest.mark.parametrize("k,N,C,D", [(256, 256, 512, 1024), (256, 512, 1024, 776),
+                                     (16, 256, 512, 1040), (128, 512, 768, 2048)])
+def test_layer_narrow_dx(k, N, C, D):
+    """HALO-2 dX with few 256 x 256 tiles runs on 256 x 128 tiles; with k = 256 the column
+    rotation spans a pair of tiles, which exchange their rotated values and one of them
+    finishes both (k <= 128 rotates inside a tile). A ragged K puts a short last K step in
+    every tile. Two layers in a row also check that the pair flags are left at zero."""
     for rep in range(2):
         cfg = WL.config(2, N=N, C=C, D=D, k=k)
-        banner("split-k", k, N, C, D, rep)
+        banner("narrow-dx", k, N, C, D, rep)
         inputs = WL.make_inputs(cfg)
         res = run_gpu(cfg, inputs, out_dt=O.F32)
         h = host(res, O.F32)
