@@ -7,10 +7,11 @@ GEMMs with dequantization, and the output-side inverse rotations. Inputs are see
 tensors with the workload's shapes and distributions, resident in HBM before timing starts.
 
 Printed (one JSON line): effective TOPS = sum of 2*M*N*K over the three products / step
-time; the percentage of the INT8 MFMA peak; the roofline of the dominant kernel (the GEMM,
-timed with HIP events recorded on its own launch stream inside the timed region); the
-rotate+quantize bandwidth; an unrotated bf16 GEMM baseline of the same three products; and
-the CPU oracle timed on a bounded sample of the same workload.
+time of an uninstrumented timed region; the percentage of the INT8 MFMA peak; the roofline of
+the dominant kernel (the GEMM, its launches stamped with HIP events on their own stream during
+a second pass of the same steps); the rotate+quantize bandwidth; an unrotated bf16 GEMM
+baseline of the same three products; the step of the Llama-7B-shaped layer against its bf16
+baseline; and the CPU oracle timed on a bounded sample of the same workload.
 """
 import argparse
 import hashlib
@@ -109,16 +110,62 @@ def bf16_baseline(cfg, steps, warmup, library):
     return s.elapsed_time(e) / steps
 
 
+def layer_vs_bf16(cfg_id, steps, warmup):
+    """The HQ-MM step of another workload (inputs resident, no instrumentation) next to the
+    three unrotated bf16 GEMMs of the same shapes: the comparison the target names for the
+    Llama-7B-shaped MLP layer."""
+    import torch
+    from hadamard_rotated_precision_amd import tensors as T
+    from hadamard_rotated_precision_amd import workloads as WL
+    cfg = WL.config(cfg_id)
+    N, C, D = cfg["N"], cfg["C"], cfg["D"]
+    inputs = WL.make_inputs(cfg)
+    dev = "cuda"
+    in_dt, out_dt = cfg["in_dtype"], cfg["out_dtype"]
+    x = T.device_tensor_from_bits(inputs["x"], in_dt, dev)
+    w = T.device_tensor_from_bits(inputs["w"], in_dt, dev)
+    dy = T.device_tensor_from_bits(inputs["dy"], in_dt, dev)
+    layer = T.Layer(N, C, D, cfg["k"], cfg["bits"], cfg["mode"], cfg["variant"], device=dev)
+    odt = T.TORCH_DT[out_dt]
+    y = torch.empty((N, D), dtype=odt, device=dev)
+    dx = torch.empty((N, C), dtype=odt, device=dev)
+    dw = torch.empty((D, C), dtype=odt, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        layer.fwd(x, w, y, None, stream)
+        layer.bwd_input(dy, dx, None, stream)
+        layer.bwd_weight(dw, stream)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    del x, w, dy, y, dx, dw, layer
+    ms_rb = bf16_baseline(cfg, steps, warmup, "cublas")
+    ms_lt = bf16_baseline(cfg, steps, warmup, "cublaslt")
+    return {"workload": cfg["name"], "hq_ms_per_step": round(ms, 4),
+            "hq_tops": round(layer_ops(cfg) / (ms * 1e-3) / 1e12, 1),
+            "bf16_ms_rocblas": round(ms_rb, 4), "bf16_ms_hipblaslt": round(ms_lt, 4),
+            "speedup_vs_rocblas": round(ms_rb / ms, 3), "speedup_vs_hipblaslt": round(ms_lt / ms, 3)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2,
                     help="workload id (default 2: HALO-2 step, 2048 x 4096 x 4096, k=256)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--check-config", type=int, default=4,
+                    help="also time this workload's step against three bf16 GEMMs (default 4: "
+                         "the Llama-7B-shaped MLP layer); 0 to skip")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="before the steps, copy a buffer of this many MiB three times with a "
                          "plain device copy (reference dispatches for HBM byte counters)")
@@ -180,22 +227,32 @@ def main():
     torch.cuda.synchronize()
     print("[bench] warmup done", file=sys.stderr, flush=True)
 
-    # ---- timed region: K steps; the GEMM launches are bracketed by HIP events on the stream
-    B.check(B.hq_profile_start(1 << B.HQ_KIND_GEMM), "profile")
+    # ---- timed region: K steps, uninstrumented (per-launch events cost several us per launch)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    prof = B.profile_stop_dict()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     ops = layer_ops(cfg)
     eff_tops = ops / (ms_per_step * 1e-3) / 1e12
+    print("[bench] timed region done: %.3f ms/step" % ms_per_step, file=sys.stderr, flush=True)
+
+    # ---- roofline pass: the same K steps again, each GEMM launch stamped with HIP events on
+    # its own launch stream (hipExtLaunchKernel records the kernel's start and end)
+    B.check(B.hq_profile_start(1 << B.HQ_KIND_GEMM), "profile")
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t3 = time.perf_counter()
+    prof = B.profile_stop_dict()
+    ms_instr = (t3 - t2) * 1e3 / args.steps
     gcount, gms, gunits = prof["gemm"]
     gemm_tops = gunits / (gms * 1e-3) / 1e12 if gms > 0 else None
     gemm_avg_us = gms * 1e3 / gcount if gcount else None
-    print("[bench] timed region done: %.3f ms/step" % ms_per_step, file=sys.stderr, flush=True)
 
     # ---- per-kind breakdown of the same step (all kinds bracketed; a separate pass)
     B.check(B.hq_profile_start((1 << B.HQ_KIND_COUNT) - 1), "profile")
@@ -253,6 +310,9 @@ def main():
             "launches": gcount,
             "avg_launch_us": None if gemm_avg_us is None else round(gemm_avg_us, 2),
             "ops_per_launch": None if not gcount else gunits / gcount,
+            "timing": "HIP events stamped by hipExtLaunchKernel on each GEMM launch, over a "
+                      "second pass of the same %d steps (%.4f ms/step with the events)"
+                      % (args.steps, ms_instr),
         },
         "breakdown_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in breakdown.items()},
     }
@@ -267,6 +327,13 @@ def main():
                 "speedup_vs_hipblaslt": round(ms_lt / ms_per_step, 3)}
         except Exception as exc:  # report, do not fail the benchmark line
             result["bf16_baseline"] = {"error": str(exc)}
+    if args.check_config and args.check_config != args.config:
+        print("[bench] step vs bf16 on config %d" % args.check_config, file=sys.stderr, flush=True)
+        try:
+            result["layer_vs_bf16"] = layer_vs_bf16(args.check_config, max(5, args.steps // 5),
+                                                    max(2, args.warmup // 2))
+        except Exception as exc:  # report, do not fail the benchmark line
+            result["layer_vs_bf16"] = {"error": str(exc)}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(args.config, args.cpu_sample_tokens)

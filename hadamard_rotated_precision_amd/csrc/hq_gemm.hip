@@ -528,8 +528,8 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs 
       }
       if constexpr (PAIR) {
         // Column stride 128 of a 256-column rotation block spans the two 256 x 128 tiles of a
-        // pair (tn even = lower half). Which one finishes, with no waiting: each tile has a
-        // flag bit. A tile that finds its partner's bit set adds the partner's published
+        // pair (tn even = lower half). Which one finishes: each tile has a flag bit. A tile
+        // that finds its partner's bit set adds the partner's published
         // (rotated, unscaled) values and finishes both halves; otherwise it publishes its own,
         // sets its bit, and finishes only if the partner's bit appeared meanwhile (the partner
         // then saw no bit and published instead of finishing). Exactly one tile finishes; the
@@ -549,7 +549,19 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs 
           return part * SLOT + (((cc * NJ + jj) * 2 + k) * NT + t) * 16;
         };
         __syncthreads();
-        if (t == 0) s_state = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (t == 0) {
+          // The lower tile first waits a bounded time (about 20 us) for the upper tile's
+          // publication, so that normally one tile publishes and the other finishes; after the
+          // bound it falls back to the wait-free rule below, so no tile ever waits on a
+          // partner that is not running.
+          int st = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (half == 0)
+            for (int i = 0; i < 40 && !(st & otherbit); ++i) {
+              __builtin_amdgcn_s_sleep(16);
+              st = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+          s_state = st;
+        }
         __syncthreads();
         bool finish = (s_state & otherbit) != 0;
         if (!finish) {
@@ -602,38 +614,37 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs 
 }
 
 template <int BN, class Out, int EPI, int KM, int KN, bool TRANS, bool PAIR = false>
-static hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
+static hipError_t launch_gemm(const GemmArgs& a, hipStream_t st, int tok) {
   const int64_t tiles = ((a.M + GBM - 1) / GBM) * ((a.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_i8_kernel<BN, Out, EPI, KM, KN, TRANS, PAIR>),
-                     dim3(static_cast<int>(tiles)), dim3(GemmShape<BN>::NT), 0, st, a);
-  return hipGetLastError();
+  return launch_k(gemm_i8_kernel<BN, Out, EPI, KM, KN, TRANS, PAIR>, dim3(static_cast<int>(tiles)),
+                  dim3(GemmShape<BN>::NT), st, tok, a);
 }
 
 template <int BN, class Out>
-static hipError_t launch_out(const GemmPass& p, const GemmArgs& a, hipStream_t st) {
+static hipError_t launch_out(const GemmPass& p, const GemmArgs& a, hipStream_t st, int tok) {
   if (p.trans_out) {
     switch (p.km) {
-#define HQ_T(KK) case KK: return launch_gemm<BN, Out, EPI_SCALE, KK, 1, true>(a, st);
+#define HQ_T(KK) case KK: return launch_gemm<BN, Out, EPI_SCALE, KK, 1, true>(a, st, tok);
       HQ_T(1) HQ_T(2) HQ_T(4) HQ_T(8) HQ_T(16) HQ_T(32) HQ_T(64) HQ_T(128) HQ_T(256)
 #undef HQ_T
     }
     return hipErrorInvalidValue;
   }
-  if (p.km == 1 && p.kn == 1) return launch_gemm<BN, Out, EPI_SCALE, 1, 1, false>(a, st);
+  if (p.km == 1 && p.kn == 1) return launch_gemm<BN, Out, EPI_SCALE, 1, 1, false>(a, st, tok);
   if (p.km != p.kn) return hipErrorInvalidValue;
   if constexpr (BN == 128) {
     // column blocks up to 128 wide rotate inside the tile; 256-wide ones span a tile pair
     switch (p.km) {
-#define HQ_B(KK) case KK: return launch_gemm<BN, Out, EPI_SCALE, KK, KK, false>(a, st);
+#define HQ_B(KK) case KK: return launch_gemm<BN, Out, EPI_SCALE, KK, KK, false>(a, st, tok);
       HQ_B(2) HQ_B(4) HQ_B(8) HQ_B(16) HQ_B(32) HQ_B(64) HQ_B(128)
 #undef HQ_B
       case 256:
         if (!a.pair_part) return hipErrorInvalidValue;
-        return launch_gemm<BN, Out, EPI_SCALE, 256, 256, false, true>(a, st);
+        return launch_gemm<BN, Out, EPI_SCALE, 256, 256, false, true>(a, st, tok);
     }
   } else {
     switch (p.km) {
-#define HQ_B(KK) case KK: return launch_gemm<BN, Out, EPI_SCALE, KK, KK, false>(a, st);
+#define HQ_B(KK) case KK: return launch_gemm<BN, Out, EPI_SCALE, KK, KK, false>(a, st, tok);
       HQ_B(2) HQ_B(4) HQ_B(8) HQ_B(16) HQ_B(32) HQ_B(64) HQ_B(128) HQ_B(256)
 #undef HQ_B
     }
@@ -682,19 +693,18 @@ hipError_t gemm_pass(const GemmPass& p, hipStream_t st) {
   if (static_cast<int64_t>(GBM) * p.lda >= kOutOfRange || 256 * p.ldb >= kOutOfRange)
     return hipErrorInvalidValue;
   const bool narrow = use_narrow(p.M, p.N, p.epi == EPI_I32 ? 1 : p.kn, p.trans_out);
-  const int tok = prof_begin(K_GEMM, 2.0 * p.M * p.N * p.K, st);
+  const int tok = prof_open(K_GEMM, 2.0 * p.M * p.N * p.K);
   hipError_t e = hipErrorInvalidValue;
   if (p.epi == EPI_I32) {
-    e = narrow ? launch_gemm<128, F32, EPI_I32, 1, 1, false>(a, st)
-               : launch_gemm<256, F32, EPI_I32, 1, 1, false>(a, st);
+    e = narrow ? launch_gemm<128, F32, EPI_I32, 1, 1, false>(a, st, tok)
+               : launch_gemm<256, F32, EPI_I32, 1, 1, false>(a, st, tok);
   } else {
     switch (p.out_dt) {
-      case DT_F32: e = narrow ? launch_out<128, F32>(p, a, st) : launch_out<256, F32>(p, a, st); break;
-      case DT_F16: e = narrow ? launch_out<128, F16>(p, a, st) : launch_out<256, F16>(p, a, st); break;
-      case DT_BF16: e = narrow ? launch_out<128, BF16>(p, a, st) : launch_out<256, BF16>(p, a, st); break;
+      case DT_F32: e = narrow ? launch_out<128, F32>(p, a, st, tok) : launch_out<256, F32>(p, a, st, tok); break;
+      case DT_F16: e = narrow ? launch_out<128, F16>(p, a, st, tok) : launch_out<256, F16>(p, a, st, tok); break;
+      case DT_BF16: e = narrow ? launch_out<128, BF16>(p, a, st, tok) : launch_out<256, BF16>(p, a, st, tok); break;
     }
   }
-  prof_end(tok, st);
   return e;
 }
 

@@ -1,6 +1,7 @@
 // hq_internal.hpp — launchers shared between the kernel files and the C-ABI layer of libhq.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -115,8 +116,22 @@ size_t gemm_split_bytes(int64_t pairs);
 hipError_t zero_i32(int32_t* p, int64_t n, hipStream_t st);
 
 // Launch instrumentation (hq_profile.cpp): returns a token, or -1 when not recording.
+// prof_begin / prof_end bracket a launch with two event records on the stream; prof_open
+// only takes the two events, which launch_k passes to hipExtLaunchKernel.
 int prof_begin(int kind, double units, hipStream_t st);
 void prof_end(int token, hipStream_t st);
+int prof_open(int kind, double units);
+void prof_events(int token, hipEvent_t* start, hipEvent_t* stop);
+
+// Launch a kernel; with a recording token its events take the kernel's start and end times.
+template <class K, class... A>
+inline hipError_t launch_k(K kernel, dim3 grid, dim3 block, hipStream_t st, int tok, A... args) {
+  hipEvent_t e0, e1;
+  prof_events(tok, &e0, &e1);
+  if (e0) hipExtLaunchKernelGGL(kernel, grid, block, 0, st, e0, e1, 0, args...);
+  else hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+  return hipGetLastError();
+}
 enum Kind : int { K_GEMM = 0, K_ROT_ABSMAX = 1, K_ROT_QUANT = 2, K_ROT_STORE = 3,
                   K_TRANSPOSE = 4, K_MISC = 5 };
 

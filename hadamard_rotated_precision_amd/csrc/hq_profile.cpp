@@ -1,7 +1,9 @@
 // hq_profile.cpp — optional launch instrumentation of libhq: when enabled for a set of kernel
-// kinds, each launch of those kinds is bracketed by two HIP events recorded on the launch's
-// own stream, and its algorithmic work (ops for the GEMM, bytes for streaming kernels) is
-// recorded with it. Nothing is recorded while disabled (the default).
+// kinds, each launch of those kinds gets two HIP events and its algorithmic work (ops for the
+// GEMM, bytes for streaming kernels). The GEMM and prologue kernels hand the events to
+// hipExtLaunchKernel, which stamps them with the kernel's own start and end on its stream
+// (no extra packets between launches); other launches are bracketed by two event records on
+// the launch's stream. Nothing is recorded while disabled (the default).
 #include "../../include/hq.h"
 
 #include <hip/hip_runtime.h>
@@ -45,6 +47,25 @@ int prof_begin(int kind, double units, hipStream_t st) {
   if (!r.a || !r.b || hipEventRecord(r.a, st) != hipSuccess) return -1;
   g_recs.push_back(r);
   return static_cast<int>(g_recs.size() - 1);
+}
+
+int prof_open(int kind, double units) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_on || !(g_mask & (1u << kind))) return -1;
+  Rec r{kind, units, take_event(), take_event()};
+  if (!r.a || !r.b) return -1;
+  g_recs.push_back(r);
+  return static_cast<int>(g_recs.size() - 1);
+}
+
+void prof_events(int idx, hipEvent_t* a, hipEvent_t* b) {
+  *a = *b = nullptr;
+  if (idx < 0) return;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (idx < static_cast<int>(g_recs.size())) {
+    *a = g_recs[idx].a;
+    *b = g_recs[idx].b;
+  }
 }
 
 void prof_end(int idx, hipStream_t st) {

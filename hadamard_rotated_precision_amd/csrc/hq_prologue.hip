@@ -832,34 +832,33 @@ struct Launch;
 
 #define HQ_PRO_DISPATCH(NAME, THREADS)                                                         \
   template <class In, int OP>                                                                  \
-  static hipError_t NAME##_k(int k, const ProArgs& a, int grid, hipStream_t st) {             \
+  static hipError_t NAME##_k(int k, const ProArgs& a, int grid, hipStream_t st, int tok) {    \
     switch (k) {                                                                               \
-      case 1: hipLaunchKernelGGL((NAME<In, 1, OP>), dim3(grid), dim3(THREADS), 0, st, a); break;     \
-      case 2: hipLaunchKernelGGL((NAME<In, 2, OP>), dim3(grid), dim3(THREADS), 0, st, a); break;     \
-      case 4: hipLaunchKernelGGL((NAME<In, 4, OP>), dim3(grid), dim3(THREADS), 0, st, a); break;     \
-      case 8: hipLaunchKernelGGL((NAME<In, 8, OP>), dim3(grid), dim3(THREADS), 0, st, a); break;     \
-      case 16: hipLaunchKernelGGL((NAME<In, 16, OP>), dim3(grid), dim3(THREADS), 0, st, a); break;   \
-      case 32: hipLaunchKernelGGL((NAME<In, 32, OP>), dim3(grid), dim3(THREADS), 0, st, a); break;   \
-      case 64: hipLaunchKernelGGL((NAME<In, 64, OP>), dim3(grid), dim3(THREADS), 0, st, a); break;   \
-      case 128: hipLaunchKernelGGL((NAME<In, 128, OP>), dim3(grid), dim3(THREADS), 0, st, a); break; \
-      case 256: hipLaunchKernelGGL((NAME<In, 256, OP>), dim3(grid), dim3(THREADS), 0, st, a); break; \
+      case 1: return launch_k(NAME<In, 1, OP>, dim3(grid), dim3(THREADS), st, tok, a);           \
+      case 2: return launch_k(NAME<In, 2, OP>, dim3(grid), dim3(THREADS), st, tok, a);           \
+      case 4: return launch_k(NAME<In, 4, OP>, dim3(grid), dim3(THREADS), st, tok, a);           \
+      case 8: return launch_k(NAME<In, 8, OP>, dim3(grid), dim3(THREADS), st, tok, a);           \
+      case 16: return launch_k(NAME<In, 16, OP>, dim3(grid), dim3(THREADS), st, tok, a);         \
+      case 32: return launch_k(NAME<In, 32, OP>, dim3(grid), dim3(THREADS), st, tok, a);         \
+      case 64: return launch_k(NAME<In, 64, OP>, dim3(grid), dim3(THREADS), st, tok, a);         \
+      case 128: return launch_k(NAME<In, 128, OP>, dim3(grid), dim3(THREADS), st, tok, a);       \
+      case 256: return launch_k(NAME<In, 256, OP>, dim3(grid), dim3(THREADS), st, tok, a);       \
       default: return hipErrorInvalidValue;                                                    \
     }                                                                                          \
-    return hipGetLastError();                                                                  \
   }                                                                                            \
   static hipError_t NAME##_launch(int in_dt, int op, int k, const ProArgs& a, int grid,        \
-                                  hipStream_t st) {                                            \
+                                  hipStream_t st, int tok) {                                   \
     if (op == OP_ABSMAX) {                                                                     \
       switch (in_dt) {                                                                         \
-        case DT_F32: return NAME##_k<F32, OP_ABSMAX>(k, a, grid, st);                          \
-        case DT_F16: return NAME##_k<F16, OP_ABSMAX>(k, a, grid, st);                          \
-        case DT_BF16: return NAME##_k<BF16, OP_ABSMAX>(k, a, grid, st);                        \
+        case DT_F32: return NAME##_k<F32, OP_ABSMAX>(k, a, grid, st, tok);                          \
+        case DT_F16: return NAME##_k<F16, OP_ABSMAX>(k, a, grid, st, tok);                          \
+        case DT_BF16: return NAME##_k<BF16, OP_ABSMAX>(k, a, grid, st, tok);                        \
       }                                                                                        \
     } else {                                                                                   \
       switch (in_dt) {                                                                         \
-        case DT_F32: return NAME##_k<F32, OP_QUANT>(k, a, grid, st);                           \
-        case DT_F16: return NAME##_k<F16, OP_QUANT>(k, a, grid, st);                           \
-        case DT_BF16: return NAME##_k<BF16, OP_QUANT>(k, a, grid, st);                         \
+        case DT_F32: return NAME##_k<F32, OP_QUANT>(k, a, grid, st, tok);                           \
+        case DT_F16: return NAME##_k<F16, OP_QUANT>(k, a, grid, st, tok);                           \
+        case DT_BF16: return NAME##_k<BF16, OP_QUANT>(k, a, grid, st, tok);                         \
       }                                                                                        \
     }                                                                                          \
     return hipErrorInvalidValue;                                                               \
@@ -923,16 +922,15 @@ hipError_t pro_pass(const ProPass& p, int op, hipStream_t st) {
   const double inb = elems * dtb(p.in_dt);
   double outb = 0.0;
   if (op == OP_QUANT) outb = elems * ((p.codes ? 1 : 0) + (p.codes_t ? 1 : 0));
-  const int tok = prof_begin(op == OP_ABSMAX ? K_ROT_ABSMAX : K_ROT_QUANT, inb + outb, st);
+  const int tok = prof_open(op == OP_ABSMAX ? K_ROT_ABSMAX : K_ROT_QUANT, inb + outb);
   hipError_t e = hipErrorInvalidValue;
   if (p.kind == PRO_RIGHT && right_fast_ok(p.rows, p.cols, a.vec))
-    e = right_fast_kernel_launch(p.in_dt, op, p.k, a, grid, st);
-  else if (p.kind == PRO_RIGHT) e = right_kernel_launch(p.in_dt, op, p.k, a, grid, st);
+    e = right_fast_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
+  else if (p.kind == PRO_RIGHT) e = right_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
   else if (p.kind == PRO_LEFT && left_fast_ok(p.rows, p.cols, a.vec, dtb(p.in_dt)))
-    e = left_fast_kernel_launch(p.in_dt, op, p.k, a, grid, st);
-  else if (p.kind == PRO_LEFT) e = left_kernel_launch(p.in_dt, op, p.k, a, grid, st);
-  else e = both_kernel_launch(p.in_dt, op, p.k, a, grid, st);
-  prof_end(tok, st);
+    e = left_fast_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
+  else if (p.kind == PRO_LEFT) e = left_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
+  else e = both_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
   return e;
 }
 
