@@ -189,10 +189,10 @@ __device__ inline void fwht_xlane(float (&v)[N], int lane, int m) {
 
 // Value of lane (lane ^ 1) / (lane ^ 2) within a quad, through DPP quad permutes.
 __device__ inline float quad_xor1(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
 }
 __device__ inline float quad_xor2(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
 }
 
 // Butterfly stage across the lanes of a quad (m = 1 or 2): the lane with bit m clear keeps

@@ -498,7 +498,7 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs 
 #pragma unroll
             for (int q = 0; q < 8 * NJ; ++q) {
               const uint32_t xv = __float_as_uint(f[q]);
-              uint32_t pv = __builtin_amdgcn_update_dpp(0u, xv, 0x104, 0xF, 0x5, false);   // lane + 4
+              uint32_t pv = __builtin_amdgcn_mov_dpp(xv, 0x104, 0xF, 0x5, false);   // lane + 4
               pv = __builtin_amdgcn_update_dpp(pv, xv, 0x114, 0xF, 0xA, false);            // lane - 4
               f[q] = __builtin_fmaf(f[q], sg, __uint_as_float(pv));
             }

@@ -310,15 +310,12 @@ __global__ __launch_bounds__(RF_THREADS) void right_fast_kernel(ProArgs a) {
     for (int q = 0; q < NQ; ++q)   // chunk q: columns 32*(q*PER/8) + 8s + (q*PER)%8 ...
       raw[q] = *reinterpret_cast<const uint4*>(p + (32 * ((q * PER) / 8) + (q * PER) % 8) * In::bytes);
   };
-  uint4 raw[NQ];
+  uint4 rawA[NQ], rawB[NQ];
   uint32_t tl = blockIdx.x;
-  if (tl < tiles) issue(tl, raw);
+  if (tl < tiles) issue(tl, rawA);
   float amax = 0.0f;
-  for (; tl < tiles; tl += gridDim.x) {
-    uint4 cur[NQ];
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) cur[q] = raw[q];
-    issue(tl + gridDim.x < tiles ? tl + gridDim.x : tl, raw);   // unconditional: the last re-reads
+  // one tile in registers while the next one loads: two register sets, alternating
+  auto body = [&](const uint32_t tl, const uint4 (&cur)[NQ]) {
     float v[64];
     unpack64<In, K>(cur, v);
     right_stages<K>(v, sg1, sg2);
@@ -346,9 +343,9 @@ __global__ __launch_bounds__(RF_THREADS) void right_fast_kernel(ProArgs a) {
         __syncthreads();   // the previous tile's readers of tc are done
 #pragma unroll
         for (int g = 0; g < 16; ++g) {
-          const uint32_t p = __builtin_amdgcn_update_dpp(0u, d[g], 0x128, 0xF, 0xF, false);   // lane ^ 8
+          const uint32_t p = __builtin_amdgcn_mov_dpp(d[g], 0x128, 0xF, 0xF, false);   // lane ^ 8
           const uint32_t x = __builtin_amdgcn_perm(p, d[g], selA);
-          uint32_t q = __builtin_amdgcn_update_dpp(0u, x, 0x104, 0xF, 0x5, false);           // lane + 4
+          uint32_t q = __builtin_amdgcn_mov_dpp(x, 0x104, 0xF, 0x5, false);           // lane + 4
           q = __builtin_amdgcn_update_dpp(q, x, 0x114, 0xF, 0xA, false);                     // lane - 4
           const uint32_t e = __builtin_amdgcn_perm(q, x, selB);
           const int c = 32 * (g >> 1) + 8 * s + 4 * (g & 1) + b;
@@ -362,6 +359,16 @@ __global__ __launch_bounds__(RF_THREADS) void right_fast_kernel(ProArgs a) {
         for (int j = 0; j < 4; ++j) dst[j] = sp[j ^ x];
       }
     }
+    };
+  while (tl < tiles) {
+    const uint32_t t1 = tl + gridDim.x;
+    issue(t1 < tiles ? t1 : tl, rawB);   // unconditional: the last re-reads
+    body(tl, rawA);
+    if (t1 >= tiles) break;
+    const uint32_t t2 = t1 + gridDim.x;
+    issue(t2 < tiles ? t2 : t1, rawA);
+    body(t1, rawB);
+    tl = t2;
   }
   if constexpr (OP == OP_ABSMAX) {
     amax = block_max(amax, red);
@@ -533,15 +540,12 @@ __global__ __launch_bounds__(LF_THREADS, 2) void left_fast_kernel(ProArgs a) {
     for (int q = 0; q < 8; ++q) raw[q] = *reinterpret_cast<const uint4*>(q0 + static_cast<int64_t>(32 * q) * a.cols * 2);
   };
   const int rbase = 64 * p * LF_PITCH + (c ^ (16 * p));   // this thread's column in part p
-  uint4 raw[8];
+  uint4 rawA[8], rawB[8];
   uint32_t tl = blockIdx.x;
-  if (tl < tiles) issue(tl, raw);
+  if (tl < tiles) issue(tl, rawA);
   float amax = 0.0f;
-  for (; tl < tiles; tl += gridDim.x) {
-    uint4 cur[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) cur[q] = raw[q];
-    issue(tl + gridDim.x < tiles ? tl + gridDim.x : tl, raw);   // unconditional: the last re-reads
+  // one tile in registers while the next one loads: two register sets, alternating
+  auto body = [&](const uint32_t tl, const uint4 (&cur)[8]) {
     __syncthreads();   // the previous tile's readers of the LDS tile are done
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -591,9 +595,9 @@ __global__ __launch_bounds__(LF_THREADS, 2) void left_fast_kernel(ProArgs a) {
         __syncthreads();   // every thread has read its column of the fp32 tile
 #pragma unroll
         for (int g = 0; g < 16; ++g) {
-          const uint32_t pv = __builtin_amdgcn_update_dpp(0u, d[g], 0x128, 0xF, 0xF, false);   // lane ^ 8
+          const uint32_t pv = __builtin_amdgcn_mov_dpp(d[g], 0x128, 0xF, 0xF, false);   // lane ^ 8
           const uint32_t x = __builtin_amdgcn_perm(pv, d[g], selA);
-          uint32_t q = __builtin_amdgcn_update_dpp(0u, x, 0x104, 0xF, 0x5, false);           // lane + 4
+          uint32_t q = __builtin_amdgcn_mov_dpp(x, 0x104, 0xF, 0x5, false);           // lane + 4
           q = __builtin_amdgcn_update_dpp(q, x, 0x114, 0xF, 0xA, false);                     // lane - 4
           const uint32_t e = __builtin_amdgcn_perm(q, x, selB);
           const int row = 64 * p + 4 * g + b;
@@ -609,6 +613,16 @@ __global__ __launch_bounds__(LF_THREADS, 2) void left_fast_kernel(ProArgs a) {
         for (int j = 0; j < 4; ++j) dst[j] = make_uint4(e[4 * j], e[4 * j + 1], e[4 * j + 2], e[4 * j + 3]);
       }
     }
+    };
+  while (tl < tiles) {
+    const uint32_t t1 = tl + gridDim.x;
+    issue(t1 < tiles ? t1 : tl, rawB);   // unconditional: the last re-reads
+    body(tl, rawA);
+    if (t1 >= tiles) break;
+    const uint32_t t2 = t1 + gridDim.x;
+    issue(t2 < tiles ? t2 : t1, rawA);
+    body(t1, rawB);
+    tl = t2;
   }
   if constexpr (OP == OP_ABSMAX) {
     amax = block_max(amax, red);
@@ -662,8 +676,8 @@ __device__ inline void quad_stage_f64(double (&u)[N], int lane) {
   for (int i = 0; i < N; ++i) {
     const uint64_t b = __builtin_bit_cast(uint64_t, u[i]);
     const int lo = static_cast<int>(b), hi = static_cast<int>(b >> 32);
-    const int plo = __builtin_amdgcn_update_dpp(0, lo, ctrl, 0xF, 0xF, false);
-    const int phi = __builtin_amdgcn_update_dpp(0, hi, ctrl, 0xF, 0xF, false);
+    const int plo = __builtin_amdgcn_mov_dpp(lo, ctrl, 0xF, 0xF, false);
+    const int phi = __builtin_amdgcn_mov_dpp(hi, ctrl, 0xF, 0xF, false);
     const double p = __builtin_bit_cast(double, (static_cast<uint64_t>(static_cast<uint32_t>(phi)) << 32) |
                                                     static_cast<uint32_t>(plo));
     u[i] = __builtin_fma(u[i], sgn, p);
@@ -680,7 +694,8 @@ __host__ __device__ inline int64_t both_items(int64_t rows, int64_t cols) {
 // Per item: the tile rows rotated along the feature axis (X B in fp32, exact for 16-bit inputs;
 // with k = 256 both halves of a row are needed, otherwise only the item's own half is read) give
 // the row-major codes of X B; the item's half of X B is then staged through LDS (16-column
-// blocks XOR-swizzled by row / 64, so the column reads are conflict-free) and rotated along the
+// blocks XOR-swizzled by row / 64 and the 64-column half, so both the row-wise 16-byte writes
+// and the column reads are conflict-free) and rotated along the
 // token axis in fp64, where sums of fp32 values are exact, so B X B is rounded to fp32 once, as
 // the exact sum would be, before its scale and codes are taken.
 template <class In, int K, int OP>
@@ -774,7 +789,7 @@ __global__ __launch_bounds__(BT_THREADS) void both_kernel(ProArgs a) {
     __syncthreads();
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) {
-      float* dst = &half[r * BT_PITCH + ((64 * s2 + 16 * jb) ^ (16 * (r >> 6)))];
+      float* dst = &half[r * BT_PITCH + ((64 * s2 + 16 * jb) ^ (16 * (r >> 6)) ^ (32 * s2))];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         *reinterpret_cast<float4*>(dst + 4 * q) =
@@ -782,7 +797,7 @@ __global__ __launch_bounds__(BT_THREADS) void both_kernel(ProArgs a) {
     }
     __syncthreads();
     double u[64];
-    const float* col = &half[64 * pp * BT_PITCH + (cp ^ (16 * pp))];
+    const float* col = &half[64 * pp * BT_PITCH + (cp ^ (16 * pp) ^ (32 * (cp >> 6)))];
 #pragma unroll
     for (int i = 0; i < 64; ++i) u[i] = static_cast<double>(col[i * BT_PITCH]);
     fwht_from<1, K, 64>(u);
