@@ -14,6 +14,7 @@ enum DType : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 
 // ----------------------------------------------------------------- element formats
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct F32 {
   using storage = float;

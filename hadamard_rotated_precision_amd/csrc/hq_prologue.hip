@@ -11,6 +11,9 @@
 // the next pass, so no atomics and an order-independent result) and a quantize pass that
 // recomputes the rotation and writes codes. In STEP mode only the quantize pass runs.
 //
+//   right_mma_kernel : rotation along the contiguous axis of 16-bit tensors of whole 64 x 256
+//                  tiles, as a +-1 contraction on the matrix cores (blocks up to 64 columns)
+//                  plus in-register butterflies for the strides 64 and 128.
 //   right_kernel : rotation along the contiguous axis. Tile 64 rows x 256 columns; four lanes
 //                  share a row, each owning 64 consecutive columns, so strides < 64 are
 //                  in-register butterflies and strides 64, 128 are quad-lane DPP exchanges.
@@ -373,6 +376,208 @@ __global__ __launch_bounds__(RF_THREADS) void right_fast_kernel(ProArgs a) {
   if constexpr (OP == OP_ABSMAX) {
     amax = block_max(amax, red);
     if (t == 0) a.partials[blockIdx.x] = amax;
+  }
+}
+
+// ================================================================ right rotation on the matrix cores
+// The row-axis rotation is the product X_tile . blockdiag(H_k): a dense contraction with +-1
+// weights, run here on the 16-bit MFMA (v_mfma_f32_16x16x32_bf16 / _f16: exact products, fp32
+// accumulation) so the VALU only quantizes and lays out codes. Used for 16-bit inputs, k >= 16,
+// and tensors of whole 64 x 256 tiles with 16-byte aligned rows (right_fast_ok).
+//
+// Tile 64 x 256, four waves; wave w owns rows 16w .. 16w+15. K slice ks (32 columns) of the A
+// operand: lane l holds row l%16, columns 32ks + 8(l/16) + [0, 8), so each load instruction reads
+// 64 contiguous bytes per row. The B operand for output columns 16nb + [0, 16) is H_k restricted
+// to that slice. With column c = 16c1 + c0, H_256 = H_16 (x) H_16 gives
+// h(c, c') = h16(c1, c1') h16(c0, c0'); in a B fragment c0 and c0' depend on the lane and register
+// only (lane l, element j: c0 = 8((l/16)%2) + j, c0' = l%16), and h16(c1, c1') with
+// c1 = 2ks + l/32 splits into the compile-time sign h16(2ks, nb) times (-1)^((l/32) nb), so every
+// fragment is one of four per-lane constants (G0, G1 = G0 with lanes 32..63 negated, and their
+// negations). The matrix cores take blocks of at most 64 columns (c1, c1' modulo 4, slices
+// outside the block skipped; k = 16 keeps only the lanes with l/32 = nb%2); for k = 128 and 256
+// the column strides 64 and 128 are in-register butterflies between the nb blocks, which keeps
+// the MFMA work at 32 instructions per wave and tile, below the VALU and memory time.
+//
+// Output of a 16 x 16 block: lane l holds rows 4(l/16) + [0, 4) of column 16nb + l%16, so four
+// codes along a column pack into one dword of the transposed codes. Row-major codes come from a
+// 4 x 4 byte transpose across the lanes of a quad (columns 4m + [0, 4), DPP quad_perm + v_perm).
+// Both code tiles go through LDS as dwords, XOR-swizzled so that the dword writes and the 16-byte
+// reads are conflict-free, and leave in 64-byte (transposed) and 256-byte (row-major) runs.
+constexpr int RM_ROWS = 64, RM_COLS = 256, RM_THREADS = 256, RM_GRID = 512;
+
+__host__ __device__ inline bool right_mma_ok(int64_t rows, int64_t cols, bool vec, int in_bytes,
+                                             int k) {
+  return in_bytes == 2 && k >= 16 && k <= RM_COLS && right_fast_ok(rows, cols, vec);
+}
+
+template <class In>
+__device__ inline f32x4 mma16(const uint4& a, const uint4& b, const f32x4& c) {
+  if constexpr (In::is_bf16) {
+    typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8, a), __builtin_bit_cast(v8, b),
+                                                    c, 0, 0, 0);
+  } else {
+    typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8, a), __builtin_bit_cast(v8, b),
+                                                   c, 0, 0, 0);
+  }
+}
+
+template <class In, int K, int OP>
+__global__ __launch_bounds__(RM_THREADS, 2) void right_mma_kernel(ProArgs a) {
+  if constexpr (In::bytes != 2 || K < 16) {
+    return;
+  } else {
+    __shared__ __attribute__((aligned(16))) uint32_t tcode[RM_COLS * 16];   // [column][64 rows]
+    __shared__ __attribute__((aligned(16))) uint32_t rcode[RM_ROWS * 64];   // [row][256 columns]
+    __shared__ float red[32];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int n0 = lane & 15, lg = lane >> 4;
+    const uint32_t nct = static_cast<uint32_t>(a.cols / RM_COLS);
+    const uint32_t tiles = static_cast<uint32_t>(a.rows / RM_ROWS) * nct;   // < 2^31 (host checks)
+    float sc = 0.0f, rinv = 0.0f;
+    if constexpr (OP == OP_QUANT) {
+      tensor_scale(a.part_in, a.nparts, a.step, a.qp, red, sc, rinv);
+      zero_side(a);
+      if (blockIdx.x == 0 && t == 0) *a.scale_out = sc;
+    }
+    const float lo = qlo(a.qp), hi = qhi(a.qp);
+    // B fragments: G0 (element j of lane l is h16(8((l/16)%2) + j, l%16)), G1, and negations.
+    constexpr uint32_t ONE = In::is_bf16 ? 0x3F80u : 0x3C00u, SGN = 0x80008000u;
+    uint32_t g0[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ca = 8 * (lg & 1) + 2 * i;
+      const uint32_t e0 = ONE | ((__builtin_popcount(ca & n0) & 1) << 15);
+      const uint32_t e1 = ONE | ((__builtin_popcount((ca + 1) & n0) & 1) << 15);
+      g0[i] = e0 | (e1 << 16);
+    }
+    const uint32_t hiflip = (lane >> 5) ? SGN : 0u;
+    uint4 G[4];   // [sign][nb % 2]
+    if constexpr (K == 16) {
+      const uint32_t m0 = (lane >> 5) ? 0u : ~0u;
+      G[0] = make_uint4(g0[0] & m0, g0[1] & m0, g0[2] & m0, g0[3] & m0);
+      G[1] = make_uint4(g0[0] & ~m0, g0[1] & ~m0, g0[2] & ~m0, g0[3] & ~m0);
+      G[2] = G[0];
+      G[3] = G[1];
+    } else {
+      G[0] = make_uint4(g0[0], g0[1], g0[2], g0[3]);
+      G[1] = make_uint4(g0[0] ^ hiflip, g0[1] ^ hiflip, g0[2] ^ hiflip, g0[3] ^ hiflip);
+      G[2] = make_uint4(G[0].x ^ SGN, G[0].y ^ SGN, G[0].z ^ SGN, G[0].w ^ SGN);
+      G[3] = make_uint4(G[1].x ^ SGN, G[1].y ^ SGN, G[1].z ^ SGN, G[1].w ^ SGN);
+    }
+    const char* src = static_cast<const char*>(a.src);
+    auto issue = [&](uint32_t tl, uint4 (&raw)[8]) {
+      const uint32_t tr = tl / nct;
+      const int64_t row = static_cast<int64_t>(tr) * RM_ROWS + 16 * w + n0;
+      const int64_t col = static_cast<int64_t>(tl - tr * nct) * RM_COLS + 8 * lg;
+      const char* p = src + (row * a.cols + col) * 2;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) raw[ks] = *reinterpret_cast<const uint4*>(p + 64 * ks);
+    };
+    uint4 rawA[8], rawB[8];
+    uint32_t tl = blockIdx.x;
+    if (tl < tiles) issue(tl, rawA);
+    float amax = 0.0f;
+    constexpr int KM = K < 64 ? K : 64;     // block size of the matrix-core contraction
+    constexpr int KB = KM >= 32 ? KM : 32;  // columns of one K block of the contraction
+    auto body = [&](const uint32_t tl, const uint4 (&x)[8]) {
+      f32x4 acc[16];
+#pragma unroll
+      for (int nb = 0; nb < 16; ++nb) acc[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+        for (int nb = 0; nb < 16; ++nb) {
+          if ((32 * ks) / KB != (16 * nb) / KB) continue;   // outside the diagonal block
+          const int sg = (KM == 16) ? 0 : (__builtin_popcount((2 * ks) & nb & (KM / 16 - 1)) & 1);
+          acc[nb] = mma16<In>(x[ks], G[2 * sg + (nb & 1)], acc[nb]);
+        }
+      }
+      // column strides 64 and 128 (bits 2 and 3 of nb): H_2m = [[H_m, H_m], [H_m, -H_m]] as
+      // in-register butterflies between the 64-column blocks
+#pragma unroll
+      for (int hb = 4; hb <= 8; hb <<= 1) {
+        if (16 * hb < K) {
+#pragma unroll
+          for (int nb = 0; nb < 16; ++nb)
+            if ((nb & hb) == 0) {
+              const f32x4 u = acc[nb], v = acc[nb + hb];
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                acc[nb][j] = u[j] + v[j];
+                acc[nb + hb][j] = u[j] - v[j];
+              }
+            }
+        }
+      }
+      if constexpr (OP == OP_ABSMAX) {
+#pragma unroll
+        for (int nb = 0; nb < 16; ++nb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(acc[nb][j]));
+      } else {
+        uint32_t d[16];   // rows 4lg + [0, 4) of column 16nb + n0
+#pragma unroll
+        for (int nb = 0; nb < 16; ++nb)
+          d[nb] = qpack4(qbits(acc[nb][0], rinv, lo, hi), qbits(acc[nb][1], rinv, lo, hi),
+                         qbits(acc[nb][2], rinv, lo, hi), qbits(acc[nb][3], rinv, lo, hi));
+        const uint32_t tr = tl / nct;
+        const int64_t row0 = static_cast<int64_t>(tr) * RM_ROWS;
+        const int64_t col0 = static_cast<int64_t>(tl - tr * nct) * RM_COLS;
+        __syncthreads();   // the previous tile's readers of the code tiles are done
+        if (a.codes_t) {
+#pragma unroll
+          for (int nb = 0; nb < 16; ++nb) {
+            const int c = 16 * nb + n0;
+            tcode[c * 16 + ((4 * w + lg) ^ (4 * ((c >> 2) & 3)))] = d[nb];
+          }
+        }
+        if (a.codes) {
+          const int i = n0 & 3, m = n0 >> 2, row = 16 * w + 4 * lg + i;
+          const uint32_t selA = (i < 2) ? 0x05040100u : 0x03020706u;
+          const uint32_t selB = (i & 1) ? 0x03070105u : 0x06020400u;
+#pragma unroll
+          for (int nb = 0; nb < 16; ++nb) {
+            const uint32_t p = __builtin_amdgcn_mov_dpp(d[nb], 0x4E, 0xF, 0xF, false);   // lane ^ 2
+            const uint32_t xx = __builtin_amdgcn_perm(p, d[nb], selA);
+            const uint32_t q = __builtin_amdgcn_mov_dpp(xx, 0xB1, 0xF, 0xF, false);      // lane ^ 1
+            rcode[row * 64 + ((4 * nb + m) ^ (4 * (row & 15)))] = __builtin_amdgcn_perm(q, xx, selB);
+          }
+        }
+        __syncthreads();
+        if (a.codes_t) {
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const int idx = 256 * p + t, c = idx >> 2, q = idx & 3;
+            *reinterpret_cast<uint4*>(a.codes_t + (col0 + c) * a.ld_t + row0 + 16 * q) =
+                *reinterpret_cast<const uint4*>(&tcode[c * 16 + 4 * (q ^ ((c >> 2) & 3))]);
+          }
+        }
+        if (a.codes) {
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const int idx = 256 * p + t, row = idx >> 4, cc = idx & 15;
+            *reinterpret_cast<uint4*>(a.codes + (row0 + row) * a.ld + col0 + 16 * cc) =
+                *reinterpret_cast<const uint4*>(&rcode[row * 64 + 4 * (cc ^ (row & 15))]);
+          }
+        }
+      }
+    };
+    while (tl < tiles) {
+      const uint32_t t1 = tl + gridDim.x;
+      issue(t1 < tiles ? t1 : tl, rawB);   // unconditional: the last re-reads
+      body(tl, rawA);
+      if (t1 >= tiles) break;
+      const uint32_t t2 = t1 + gridDim.x;
+      issue(t2 < tiles ? t2 : t1, rawA);
+      body(t1, rawB);
+      tl = t2;
+    }
+    if constexpr (OP == OP_ABSMAX) {
+      amax = block_max(amax, red);
+      if (t == 0) a.partials[blockIdx.x] = amax;
+    }
   }
 }
 
@@ -881,6 +1086,7 @@ struct Launch;
 
 HQ_PRO_DISPATCH(right_kernel, RT_THREADS)
 HQ_PRO_DISPATCH(right_fast_kernel, RF_THREADS)
+HQ_PRO_DISPATCH(right_mma_kernel, RM_THREADS)
 HQ_PRO_DISPATCH(left_kernel, LT_THREADS)
 HQ_PRO_DISPATCH(left_fast_kernel, LF_THREADS)
 HQ_PRO_DISPATCH(both_kernel, BT_THREADS)
@@ -915,6 +1121,8 @@ static ProArgs pro_args(const ProPass& p) {
 int pro_grid(const ProPass& p) {
   int64_t tiles;
   if (p.kind == PRO_RIGHT) {
+    if (right_mma_ok(p.rows, p.cols, pro_args(p).vec, dtb(p.in_dt), p.k))
+      return grid_cap((p.rows / RM_ROWS) * (p.cols / RM_COLS), RM_GRID);
     if (right_fast_ok(p.rows, p.cols, pro_args(p).vec))
       return grid_cap((p.rows / RF_ROWS) * (p.cols / RF_COLS), RF_GRID);
     tiles = ((p.rows + RT_ROWS - 1) / RT_ROWS) * ((p.cols + RT_COLS - 1) / RT_COLS);
@@ -939,7 +1147,9 @@ hipError_t pro_pass(const ProPass& p, int op, hipStream_t st) {
   if (op == OP_QUANT) outb = elems * ((p.codes ? 1 : 0) + (p.codes_t ? 1 : 0));
   const int tok = prof_open(op == OP_ABSMAX ? K_ROT_ABSMAX : K_ROT_QUANT, inb + outb);
   hipError_t e = hipErrorInvalidValue;
-  if (p.kind == PRO_RIGHT && right_fast_ok(p.rows, p.cols, a.vec))
+  if (p.kind == PRO_RIGHT && right_mma_ok(p.rows, p.cols, a.vec, dtb(p.in_dt), p.k))
+    e = right_mma_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
+  else if (p.kind == PRO_RIGHT && right_fast_ok(p.rows, p.cols, a.vec))
     e = right_fast_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
   else if (p.kind == PRO_RIGHT) e = right_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
   else if (p.kind == PRO_LEFT && left_fast_ok(p.rows, p.cols, a.vec, dtb(p.in_dt)))

@@ -118,6 +118,8 @@ def _rq(V_bits, dt, rows, cols, rot, k, bits, mode, step=None, codes=True, codes
     (B.HQ_ROT_RIGHT, 256, 128, 512),     # whole 64 x 256 tiles: the persistent kernel
     (B.HQ_ROT_RIGHT, 128, 192, 1024),
     (B.HQ_ROT_RIGHT, 64, 64, 256),
+    (B.HQ_ROT_RIGHT, 16, 64, 512),       # matrix-core rotation, k = 16 and 32 blocks
+    (B.HQ_ROT_RIGHT, 32, 128, 768),
     (B.HQ_ROT_NONE, 1, 64, 512),
     (B.HQ_ROT_LEFT, 256, 512, 300),
     (B.HQ_ROT_LEFT, 16, 48, 200),
