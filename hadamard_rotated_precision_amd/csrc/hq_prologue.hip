@@ -21,6 +21,8 @@
 //   left_kernel  : rotation along rows (the token axis). The tile (TR x 16384/TR) is staged in
 //                  LDS as fp32 with a column swizzle; a thread then owns 64 consecutive rows of
 //                  one column (in-register butterflies) and four lanes share a column.
+//   both_mma_kernel : X under HALO-2 for 16-bit inputs and whole 256 x 256 tiles: the row phase
+//                  of both_kernel on the matrix cores, the half tile staged column-major.
 //   both_kernel  : X under HALO-2, 256 x 256 tiles, 512 threads: the right rotation (two rows
 //                  per thread) feeds the row-major codes of Q(X B); the same registers, staged
 //                  through LDS in two 128-column halves, feed the token-axis rotation (64 rows of
@@ -423,6 +425,87 @@ __device__ inline f32x4 mma16(const uint4& a, const uint4& b, const f32x4& c) {
   }
 }
 
+// B fragments of the +-1 contraction with blocks of KM <= 64 columns, G[2 * sign + nb % 2]:
+// element j of lane l in G0 is h16(8((l/16)%2) + j, l%16); G1 negates lanes 32..63 (the factor
+// (-1)^((l/32) nb) of h16(c1, c1')); G[2], G[3] are the negations. For KM = 16 the fragments
+// keep only the lanes whose column block c1 = 2ks + l/32 is the output block nb.
+template <class In, int KM>
+__device__ inline void hfrags(int lane, uint4 (&G)[4]) {
+  constexpr uint32_t ONE = In::is_bf16 ? 0x3F80u : 0x3C00u, SGN = 0x80008000u;
+  const int n0 = lane & 15, lg = lane >> 4;
+  uint32_t g0[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ca = 8 * (lg & 1) + 2 * i;
+    const uint32_t e0 = ONE | ((__builtin_popcount(ca & n0) & 1) << 15);
+    const uint32_t e1 = ONE | ((__builtin_popcount((ca + 1) & n0) & 1) << 15);
+    g0[i] = e0 | (e1 << 16);
+  }
+  if constexpr (KM == 16) {
+    const uint32_t m0 = (lane >> 5) ? 0u : ~0u;
+    G[0] = make_uint4(g0[0] & m0, g0[1] & m0, g0[2] & m0, g0[3] & m0);
+    G[1] = make_uint4(g0[0] & ~m0, g0[1] & ~m0, g0[2] & ~m0, g0[3] & ~m0);
+    G[2] = G[0];
+    G[3] = G[1];
+  } else {
+    const uint32_t hiflip = (lane >> 5) ? SGN : 0u;
+    G[0] = make_uint4(g0[0], g0[1], g0[2], g0[3]);
+    G[1] = make_uint4(g0[0] ^ hiflip, g0[1] ^ hiflip, g0[2] ^ hiflip, g0[3] ^ hiflip);
+    G[2] = make_uint4(G[0].x ^ SGN, G[0].y ^ SGN, G[0].z ^ SGN, G[0].w ^ SGN);
+    G[3] = make_uint4(G[1].x ^ SGN, G[1].y ^ SGN, G[1].z ^ SGN, G[1].w ^ SGN);
+  }
+}
+
+// acc[nb] = 16 rows x columns 16nb + [0, 16) of x . blockdiag(H_KM), where x[ks] is the A
+// fragment of columns 32ks + [0, 32) (lane l: row l%16, columns 32ks + 8(l/16) + [0, 8)).
+template <class In, int KM, int NKS, int NNB>
+__device__ inline void mma_rows(const uint4 (&x)[NKS], const uint4 (&G)[4], f32x4 (&acc)[NNB]) {
+  constexpr int KB = KM >= 32 ? KM : 32;   // columns of one K block of the contraction
+#pragma unroll
+  for (int nb = 0; nb < NNB; ++nb) acc[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+    for (int nb = 0; nb < NNB; ++nb) {
+      if ((32 * ks) / KB != (16 * nb) / KB) continue;   // outside the diagonal block
+      const int sg = (KM == 16) ? 0 : (__builtin_popcount((2 * ks) & nb & (KM / 16 - 1)) & 1);
+      acc[nb] = mma16<In>(x[ks], G[2 * sg + (nb & 1)], acc[nb]);
+    }
+  }
+}
+
+// Column strides 64 and 128 below min(K, LIM) (bits 2 and 3 of nb): H_2m = [[H_m, H_m],
+// [H_m, -H_m]] as in-register butterflies between the 64-column blocks.
+template <int K, int NNB, int LIM>
+__device__ inline void mma_high_stages(f32x4 (&acc)[NNB]) {
+#pragma unroll
+  for (int hb = 4; hb <= 8; hb <<= 1) {
+    if (16 * hb < K && 16 * hb < LIM && hb < NNB) {
+#pragma unroll
+      for (int nb = 0; nb < NNB; ++nb)
+        if ((nb & hb) == 0) {
+          const f32x4 u = acc[nb], v = acc[nb + hb];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc[nb][j] = u[j] + v[j];
+            acc[nb + hb][j] = u[j] - v[j];
+          }
+        }
+    }
+  }
+}
+
+// 4 x 4 byte transpose across the lanes of a quad: lane i of the quad holds bytes (row j, column
+// 4m + i) for j < 4 and returns bytes (row i, column 4m + j).
+__device__ inline uint32_t quad_byte_transpose(uint32_t d, int i) {
+  const uint32_t selA = (i < 2) ? 0x05040100u : 0x03020706u;
+  const uint32_t selB = (i & 1) ? 0x03070105u : 0x06020400u;
+  const uint32_t p = __builtin_amdgcn_mov_dpp(d, 0x4E, 0xF, 0xF, false);   // lane ^ 2
+  const uint32_t x = __builtin_amdgcn_perm(p, d, selA);
+  const uint32_t q = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);   // lane ^ 1
+  return __builtin_amdgcn_perm(q, x, selB);
+}
+
 template <class In, int K, int OP>
 __global__ __launch_bounds__(RM_THREADS, 2) void right_mma_kernel(ProArgs a) {
   if constexpr (In::bytes != 2 || K < 16) {
@@ -442,30 +525,8 @@ __global__ __launch_bounds__(RM_THREADS, 2) void right_mma_kernel(ProArgs a) {
       if (blockIdx.x == 0 && t == 0) *a.scale_out = sc;
     }
     const float lo = qlo(a.qp), hi = qhi(a.qp);
-    // B fragments: G0 (element j of lane l is h16(8((l/16)%2) + j, l%16)), G1, and negations.
-    constexpr uint32_t ONE = In::is_bf16 ? 0x3F80u : 0x3C00u, SGN = 0x80008000u;
-    uint32_t g0[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ca = 8 * (lg & 1) + 2 * i;
-      const uint32_t e0 = ONE | ((__builtin_popcount(ca & n0) & 1) << 15);
-      const uint32_t e1 = ONE | ((__builtin_popcount((ca + 1) & n0) & 1) << 15);
-      g0[i] = e0 | (e1 << 16);
-    }
-    const uint32_t hiflip = (lane >> 5) ? SGN : 0u;
-    uint4 G[4];   // [sign][nb % 2]
-    if constexpr (K == 16) {
-      const uint32_t m0 = (lane >> 5) ? 0u : ~0u;
-      G[0] = make_uint4(g0[0] & m0, g0[1] & m0, g0[2] & m0, g0[3] & m0);
-      G[1] = make_uint4(g0[0] & ~m0, g0[1] & ~m0, g0[2] & ~m0, g0[3] & ~m0);
-      G[2] = G[0];
-      G[3] = G[1];
-    } else {
-      G[0] = make_uint4(g0[0], g0[1], g0[2], g0[3]);
-      G[1] = make_uint4(g0[0] ^ hiflip, g0[1] ^ hiflip, g0[2] ^ hiflip, g0[3] ^ hiflip);
-      G[2] = make_uint4(G[0].x ^ SGN, G[0].y ^ SGN, G[0].z ^ SGN, G[0].w ^ SGN);
-      G[3] = make_uint4(G[1].x ^ SGN, G[1].y ^ SGN, G[1].z ^ SGN, G[1].w ^ SGN);
-    }
+    uint4 G[4];
+    hfrags<In, (K < 64 ? K : 64)>(lane, G);
     const char* src = static_cast<const char*>(a.src);
     auto issue = [&](uint32_t tl, uint4 (&raw)[8]) {
       const uint32_t tr = tl / nct;
@@ -479,38 +540,10 @@ __global__ __launch_bounds__(RM_THREADS, 2) void right_mma_kernel(ProArgs a) {
     uint32_t tl = blockIdx.x;
     if (tl < tiles) issue(tl, rawA);
     float amax = 0.0f;
-    constexpr int KM = K < 64 ? K : 64;     // block size of the matrix-core contraction
-    constexpr int KB = KM >= 32 ? KM : 32;  // columns of one K block of the contraction
     auto body = [&](const uint32_t tl, const uint4 (&x)[8]) {
       f32x4 acc[16];
-#pragma unroll
-      for (int nb = 0; nb < 16; ++nb) acc[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-#pragma unroll
-        for (int nb = 0; nb < 16; ++nb) {
-          if ((32 * ks) / KB != (16 * nb) / KB) continue;   // outside the diagonal block
-          const int sg = (KM == 16) ? 0 : (__builtin_popcount((2 * ks) & nb & (KM / 16 - 1)) & 1);
-          acc[nb] = mma16<In>(x[ks], G[2 * sg + (nb & 1)], acc[nb]);
-        }
-      }
-      // column strides 64 and 128 (bits 2 and 3 of nb): H_2m = [[H_m, H_m], [H_m, -H_m]] as
-      // in-register butterflies between the 64-column blocks
-#pragma unroll
-      for (int hb = 4; hb <= 8; hb <<= 1) {
-        if (16 * hb < K) {
-#pragma unroll
-          for (int nb = 0; nb < 16; ++nb)
-            if ((nb & hb) == 0) {
-              const f32x4 u = acc[nb], v = acc[nb + hb];
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                acc[nb][j] = u[j] + v[j];
-                acc[nb + hb][j] = u[j] - v[j];
-              }
-            }
-        }
-      }
+      mma_rows<In, (K < 64 ? K : 64), 8, 16>(x, G, acc);
+      mma_high_stages<K, 16, 256>(acc);
       if constexpr (OP == OP_ABSMAX) {
 #pragma unroll
         for (int nb = 0; nb < 16; ++nb)
@@ -535,15 +568,9 @@ __global__ __launch_bounds__(RM_THREADS, 2) void right_mma_kernel(ProArgs a) {
         }
         if (a.codes) {
           const int i = n0 & 3, m = n0 >> 2, row = 16 * w + 4 * lg + i;
-          const uint32_t selA = (i < 2) ? 0x05040100u : 0x03020706u;
-          const uint32_t selB = (i & 1) ? 0x03070105u : 0x06020400u;
 #pragma unroll
-          for (int nb = 0; nb < 16; ++nb) {
-            const uint32_t p = __builtin_amdgcn_mov_dpp(d[nb], 0x4E, 0xF, 0xF, false);   // lane ^ 2
-            const uint32_t xx = __builtin_amdgcn_perm(p, d[nb], selA);
-            const uint32_t q = __builtin_amdgcn_mov_dpp(xx, 0xB1, 0xF, 0xF, false);      // lane ^ 1
-            rcode[row * 64 + ((4 * nb + m) ^ (4 * (row & 15)))] = __builtin_amdgcn_perm(q, xx, selB);
-          }
+          for (int nb = 0; nb < 16; ++nb)
+            rcode[row * 64 + ((4 * nb + m) ^ (4 * (row & 15)))] = quad_byte_transpose(d[nb], i);
         }
         __syncthreads();
         if (a.codes_t) {
@@ -1041,6 +1068,162 @@ __global__ __launch_bounds__(BT_THREADS) void both_kernel(ProArgs a) {
   }
 }
 
+// ================================================================ both, row phase on the matrix cores
+// X under HALO-2 for 16-bit inputs and whole 256 x 256 tiles. Work items as both_kernel (the
+// 128-column half h of a tile, halves 8 items apart). Row phase: wave w rotates tile rows
+// 32w + [0, 32) as two 16-row blocks on the matrix cores (mma_rows; for k = 256 all sixteen
+// 16-column blocks of the row, the stride-64 butterfly on both halves, then the stride-128 stage
+// for this half only, lower half x + y, upper half x - y). Its output (lane l: rows 4(l/16) + [0, 4)
+// of column 16nb + l%16) gives the row-major codes of X B through the quad byte transpose, and goes
+// to LDS column-major as one 16-byte write per lane and block: the half tile is
+// [128 columns][256 rows] fp32, 16-byte row chunk c4 of column c stored at chunk
+// c4 ^ (c % 16) ^ 4((c4 / 16) % 4), so the writes (16 columns per 16 lanes) and the column
+// phase's reads (4 columns x 4 row quarters per 16 lanes) are conflict-free. Column phase as
+// both_kernel: lane (column cp, quarter pp) rotates rows 64pp + [0, 64) in fp64.
+constexpr int BM_THREADS = 512;
+
+__host__ __device__ inline bool both_mma_ok(int64_t rows, int64_t cols, bool vec, int in_bytes,
+                                            int k) {
+  return vec && in_bytes == 2 && k >= 16 && k <= BT && rows > 0 && cols > 0 && rows % BT == 0 &&
+         cols % BT == 0;
+}
+
+__device__ inline int bm_chunk(int c, int c4) { return c4 ^ (c & 15) ^ (4 * ((c4 >> 4) & 3)); }
+
+template <class In, int K, int OP>
+__global__ __launch_bounds__(BM_THREADS) void both_mma_kernel(ProArgs a) {
+  if constexpr (In::bytes != 2 || K < 16) {
+    return;
+  } else {
+    __shared__ __attribute__((aligned(16))) float half[BT_HALF * BT];   // [column][row], swizzled
+    __shared__ float red[32];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int n0 = lane & 15, lg = lane >> 4;
+    const int cp = t >> 2, pp = t & 3;     // column phase: column cp of the half, rows 64pp + [0, 64)
+    const int64_t nct = a.cols / BT;
+    const int64_t items = both_items(a.rows, a.cols);
+    float s1 = 0.0f, r1 = 0.0f, sc2 = 0.0f, r2 = 0.0f;
+    if constexpr (OP == OP_QUANT) {
+      tensor_scale(a.part_in, a.nparts, a.step, a.qp, red, s1, r1);
+      tensor_scale(a.part_in2, a.nparts, a.step2, a.qp, red, sc2, r2);
+      zero_side(a);
+      if (blockIdx.x == 0 && t == 0) {
+        *a.scale_out = s1;
+        *a.scale_out2 = sc2;
+      }
+    }
+    const float lo = qlo(a.qp), hi = qhi(a.qp);
+    constexpr int KM = K < 64 ? K : 64;
+    constexpr int NKS = K > 128 ? 8 : 4;    // 32-column slices read per row block
+    constexpr int NNB = K > 128 ? 16 : 8;   // 16-column output blocks computed
+    uint4 G[4];
+    hfrags<In, KM>(lane, G);
+    const char* src = static_cast<const char*>(a.src);
+    float amax1 = 0.0f, amax2 = 0.0f;
+    for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+      const int64_t full = items / 16 * 16;
+      int64_t tl;
+      int h;
+      if (it < full) {
+        tl = (it / 16) * 8 + (it % 8);
+        h = static_cast<int>((it / 8) & 1);
+      } else {
+        tl = full / 2 + (it - full) / 2;
+        h = static_cast<int>((it - full) & 1);
+      }
+      const int64_t row0 = (tl / nct) * BT, col0 = (tl % nct) * BT;
+      const int64_t ccol = col0 + (NKS == 8 ? 0 : BT_HALF * h);   // first column read
+      __syncthreads();   // the previous item's column phase is done with the half tile
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int rloc = 32 * w + 16 * rb;   // first tile row of this block
+        const char* p = src + ((row0 + rloc + n0) * a.cols + ccol + 8 * lg) * 2;
+        uint4 x[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) x[ks] = *reinterpret_cast<const uint4*>(p + 64 * ks);
+        f32x4 acc[NNB];
+        mma_rows<In, KM, NKS, NNB>(x, G, acc);
+        mma_high_stages<K, NNB, 128>(acc);
+        f32x4 y[8];
+        if constexpr (K > 128) {
+          const float sg = h ? -1.0f : 1.0f;
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) y[nb][j] = __builtin_fmaf(acc[nb + 8][j], sg, acc[nb][j]);
+        } else {
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb) y[nb] = acc[nb];
+        }
+        if constexpr (OP == OP_ABSMAX) {
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) amax1 = fmaxf(amax1, fabsf(y[nb][j]));
+        } else if (a.codes) {
+          const int i = n0 & 3, m = n0 >> 2;
+          int8_t* dst = a.codes + (row0 + rloc + 4 * lg + i) * a.ld + col0 + BT_HALF * h + 4 * m;
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb) {
+            const uint32_t d = qpack4(qbits(y[nb][0], r1, lo, hi), qbits(y[nb][1], r1, lo, hi),
+                                      qbits(y[nb][2], r1, lo, hi), qbits(y[nb][3], r1, lo, hi));
+            *reinterpret_cast<uint32_t*>(dst + 16 * nb) = quad_byte_transpose(d, i);
+          }
+        }
+        const int c4 = (rloc >> 2) + lg;
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+          const int c = 16 * nb + n0;
+          *reinterpret_cast<float4*>(&half[c * BT + 4 * bm_chunk(c, c4)]) =
+              make_float4(y[nb][0], y[nb][1], y[nb][2], y[nb][3]);
+        }
+      }
+      __syncthreads();
+      // ---- column phase: the token-axis rotation of this half, in fp64
+      double u[64];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float4 f = *reinterpret_cast<const float4*>(&half[cp * BT + 4 * bm_chunk(cp, 16 * pp + i)]);
+        u[4 * i] = f.x;
+        u[4 * i + 1] = f.y;
+        u[4 * i + 2] = f.z;
+        u[4 * i + 3] = f.w;
+      }
+      fwht_from<1, K, 64>(u);
+      if constexpr (K > 64) quad_stage_f64<1, 64>(u, lane);
+      if constexpr (K > 128) quad_stage_f64<2, 64>(u, lane);
+      const int64_t gcol = col0 + BT_HALF * h + cp;
+      if constexpr (OP == OP_ABSMAX) {
+#pragma unroll
+        for (int i = 0; i < 64; ++i) amax2 = fmaxf(amax2, fabsf(static_cast<float>(u[i])));
+      } else {
+        int8_t* dst = a.codes_t + gcol * a.ld_t + row0 + 64 * pp;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t xq[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int i = 16 * q + 4 * j;
+            xq[j] = qpack4(qbits(static_cast<float>(u[i]), r2, lo, hi),
+                           qbits(static_cast<float>(u[i + 1]), r2, lo, hi),
+                           qbits(static_cast<float>(u[i + 2]), r2, lo, hi),
+                           qbits(static_cast<float>(u[i + 3]), r2, lo, hi));
+          }
+          *reinterpret_cast<uint4*>(dst + 16 * q) = make_uint4(xq[0], xq[1], xq[2], xq[3]);
+        }
+      }
+    }
+    if constexpr (OP == OP_ABSMAX) {
+      amax1 = block_max(amax1, red);
+      amax2 = block_max(amax2, red);
+      if (t == 0) {
+        a.partials[blockIdx.x] = amax1;
+        a.partials[gridDim.x + blockIdx.x] = amax2;
+      }
+    }
+  }
+}
+
 // ================================================================ launchers
 static int grid_cap(int64_t tiles, int cap) {
   if (tiles < 1) tiles = 1;
@@ -1090,6 +1273,7 @@ HQ_PRO_DISPATCH(right_mma_kernel, RM_THREADS)
 HQ_PRO_DISPATCH(left_kernel, LT_THREADS)
 HQ_PRO_DISPATCH(left_fast_kernel, LF_THREADS)
 HQ_PRO_DISPATCH(both_kernel, BT_THREADS)
+HQ_PRO_DISPATCH(both_mma_kernel, BM_THREADS)
 #undef HQ_PRO_DISPATCH
 
 static int dtb(int dt) { return dt == DT_F32 ? 4 : 2; }
@@ -1155,6 +1339,8 @@ hipError_t pro_pass(const ProPass& p, int op, hipStream_t st) {
   else if (p.kind == PRO_LEFT && left_fast_ok(p.rows, p.cols, a.vec, dtb(p.in_dt)))
     e = left_fast_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
   else if (p.kind == PRO_LEFT) e = left_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
+  else if (both_mma_ok(p.rows, p.cols, a.vec, dtb(p.in_dt), p.k))
+    e = both_mma_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
   else e = both_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
   return e;
 }

@@ -131,6 +131,9 @@ def _rq(V_bits, dt, rows, cols, rot, k, bits, mode, step=None, codes=True, codes
     (B.HQ_ROT_BOTH, 256, 512, 512),
     (B.HQ_ROT_BOTH, 128, 256, 384),
     (B.HQ_ROT_BOTH, 16, 64, 48),
+    (B.HQ_ROT_BOTH, 128, 256, 512),      # whole 256 x 256 tiles: matrix-core row phase
+    (B.HQ_ROT_BOTH, 16, 256, 256),
+    (B.HQ_ROT_BOTH, 64, 512, 768),
 ])
 @pytest.mark.parametrize("bits,mode", [(8, B.HQ_SCALE_ABSMAX), (4, B.HQ_SCALE_STEP)])
 @pytest.mark.parametrize("dt", [B.HQ_BF16, B.HQ_F16, B.HQ_F32])
