@@ -18,6 +18,8 @@
 //                  share a row, each owning 64 consecutive columns, so strides < 64 are
 //                  in-register butterflies and strides 64, 128 are quad-lane DPP exchanges.
 //                  Transposed codes go through LDS as bytes and leave as 64-byte rows.
+//   left_mma_kernel : token-axis rotation of 16-bit tensors of whole 256 x 64 tiles on the matrix
+//                  cores (H fragments as the A operand, the tile's columns read from LDS as B).
 //   left_kernel  : rotation along rows (the token axis). The tile (TR x 16384/TR) is staged in
 //                  LDS as fp32 with a column swizzle; a thread then owns 64 consecutive rows of
 //                  one column (in-register butterflies) and four lanes share a column.
@@ -863,6 +865,171 @@ __global__ __launch_bounds__(LF_THREADS, 2) void left_fast_kernel(ProArgs a) {
   }
 }
 
+// ================================================================ left rotation on the matrix cores
+// Token-axis rotation of 16-bit tensors of whole 256 x 64 tiles (dY under HALO-2) as the product
+// blockdiag(H_k) . Y_tile on the matrix cores. H is symmetric, so its A fragments are the B
+// fragments of mma_rows with the output block nb read as the output row block mb. The tile is
+// staged in LDS as raw 16-bit values, rows of 128 bytes whose 16-byte chunk c sits at
+// c ^ 2((row / 8) % 4); wave w takes columns 16w + [0, 16) and builds its B fragments (lane l:
+// column l%16, rows 32ks + 8(l/16) + [0, 8)) from 16-bit reads that meet distinct banks. The output
+// (lane l: rows 16mb + 4(l/16) + [0, 4) of column 16w + l%16) leaves as in right_mma_kernel:
+// dwords of the transposed codes directly, row-major codes through the quad byte transpose, both
+// through XOR-swizzled LDS tiles with conflict-free dword writes and 16-byte reads.
+constexpr int LM_ROWS = 256, LM_COLS = 64, LM_THREADS = 256, LM_GRID = 512;
+
+__host__ __device__ inline bool left_mma_ok(int64_t rows, int64_t cols, bool vec, int in_bytes,
+                                            int k) {
+  return k >= 16 && k <= LM_ROWS && left_fast_ok(rows, cols, vec, in_bytes);
+}
+
+// acc[mb] = output rows 16mb + [0, 16) of blockdiag(H_KM) . y for the wave's 16 columns, where
+// y[ks] is the B fragment of rows 32ks + [0, 32).
+template <class In, int KM, int NKS, int NMB>
+__device__ inline void mma_cols(const uint4 (&G)[4], const uint4 (&y)[NKS], f32x4 (&acc)[NMB]) {
+  constexpr int KB = KM >= 32 ? KM : 32;
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) acc[mb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      if ((32 * ks) / KB != (16 * mb) / KB) continue;
+      const int sg = (KM == 16) ? 0 : (__builtin_popcount((2 * ks) & mb & (KM / 16 - 1)) & 1);
+      acc[mb] = mma16<In>(G[2 * sg + (mb & 1)], y[ks], acc[mb]);
+    }
+  }
+}
+
+template <class In, int K, int OP>
+__global__ __launch_bounds__(LM_THREADS, 2) void left_mma_kernel(ProArgs a) {
+  if constexpr (In::bytes != 2 || K < 16) {
+    return;
+  } else {
+    __shared__ __attribute__((aligned(16))) uint4 tile[LM_ROWS * 8];         // [row][8 chunks]
+    __shared__ __attribute__((aligned(16))) uint32_t tcode[LM_COLS * 64];    // [column][256 rows]
+    __shared__ __attribute__((aligned(16))) uint32_t rcode[LM_ROWS * 16];    // [row][64 columns]
+    __shared__ float red[32];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int n0 = lane & 15, lg = lane >> 4;
+    const uint32_t nct = static_cast<uint32_t>(a.cols / LM_COLS);
+    const uint32_t tiles = static_cast<uint32_t>(a.rows / LM_ROWS) * nct;   // < 2^31 (host checks)
+    float sc = 0.0f, rinv = 0.0f;
+    if constexpr (OP == OP_QUANT) {
+      tensor_scale(a.part_in, a.nparts, a.step, a.qp, red, sc, rinv);
+      zero_side(a);
+      if (blockIdx.x == 0 && t == 0) *a.scale_out = sc;
+    }
+    const float lo = qlo(a.qp), hi = qhi(a.qp);
+    uint4 G[4];
+    hfrags<In, (K < 64 ? K : 64)>(lane, G);
+    const char* src = static_cast<const char*>(a.src);
+    // thread t loads chunks 256p + t: row (256p + t) / 8, 8 columns from 8((256p + t) % 8)
+    auto issue = [&](uint32_t tl, uint4 (&raw)[8]) {
+      const uint32_t tr = tl / nct;
+      const int64_t row = static_cast<int64_t>(tr) * LM_ROWS + (t >> 3);
+      const int64_t col = static_cast<int64_t>(tl - tr * nct) * LM_COLS + 8 * (t & 7);
+      const uint4* p = reinterpret_cast<const uint4*>(src + (row * a.cols + col) * 2);
+      const int64_t step = a.cols * 4;   // 32 rows, in uint4
+#pragma unroll
+      for (int q = 0; q < 8; ++q) raw[q] = p[q * step];
+    };
+    const uint16_t* th = reinterpret_cast<const uint16_t*>(tile);
+    uint4 rawA[8], rawB[8];
+    uint32_t tl = blockIdx.x;
+    if (tl < tiles) issue(tl, rawA);
+    float amax = 0.0f;
+    auto body = [&](const uint32_t tl, const uint4 (&raw)[8]) {
+      __syncthreads();   // the previous tile's readers of the LDS tiles are done
+      {
+        // chunk q of this thread: row 32q + t/8 (same (row / 8) % 4 for every q), chunk t % 8
+        const int rr = t >> 3;
+        uint4* tp = tile + rr * 8 + ((t & 7) ^ (2 * ((rr >> 3) & 3)));
+        const uint4 r0 = raw[0], r1 = raw[1], r2 = raw[2], r3 = raw[3];
+        const uint4 r4 = raw[4], r5 = raw[5], r6 = raw[6], r7 = raw[7];
+        tp[0] = r0; tp[256] = r1; tp[512] = r2; tp[768] = r3;
+        tp[1024] = r4; tp[1280] = r5; tp[1536] = r6; tp[1792] = r7;
+      }
+      __syncthreads();
+      uint4 y[8];
+      {
+        const int c = 2 * w + (n0 >> 3), e = n0 & 7;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const int r0 = 32 * ks + 8 * lg;   // (r0 / 8) % 4 == lg
+          const uint16_t* p = th + r0 * 64 + 8 * (c ^ (2 * lg)) + e;
+          uint32_t v[4];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            v[jj] = static_cast<uint32_t>(p[(2 * jj) * 64]) | (static_cast<uint32_t>(p[(2 * jj + 1) * 64]) << 16);
+          y[ks] = make_uint4(v[0], v[1], v[2], v[3]);
+        }
+      }
+      f32x4 acc[16];
+      mma_cols<In, (K < 64 ? K : 64), 8, 16>(G, y, acc);
+      mma_high_stages<K, 16, 256>(acc);
+      if constexpr (OP == OP_ABSMAX) {
+#pragma unroll
+        for (int mb = 0; mb < 16; ++mb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(acc[mb][j]));
+      } else {
+        uint32_t d[16];   // rows 16mb + 4lg + [0, 4) of column 16w + n0
+#pragma unroll
+        for (int mb = 0; mb < 16; ++mb)
+          d[mb] = qpack4(qbits(acc[mb][0], rinv, lo, hi), qbits(acc[mb][1], rinv, lo, hi),
+                         qbits(acc[mb][2], rinv, lo, hi), qbits(acc[mb][3], rinv, lo, hi));
+        const uint32_t tr = tl / nct;
+        const int64_t row0 = static_cast<int64_t>(tr) * LM_ROWS;
+        const int64_t col0 = static_cast<int64_t>(tl - tr * nct) * LM_COLS;
+        if (a.codes_t) {
+          const int c = 16 * w + n0;
+#pragma unroll
+          for (int mb = 0; mb < 16; ++mb) tcode[c * 64 + ((4 * mb + lg) ^ (4 * n0))] = d[mb];
+        }
+        if (a.codes) {
+          const int i = n0 & 3, m = n0 >> 2;
+#pragma unroll
+          for (int mb = 0; mb < 16; ++mb) {
+            const int row = 16 * mb + 4 * lg + i;   // (row / 4) % 4 == lg
+            rcode[row * 16 + ((4 * w + m) ^ (4 * lg))] = quad_byte_transpose(d[mb], i);
+          }
+        }
+        __syncthreads();
+        if (a.codes_t) {
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const int idx = 256 * p + t, c = idx >> 4, q = idx & 15;
+            *reinterpret_cast<uint4*>(a.codes_t + (col0 + c) * a.ld_t + row0 + 16 * q) =
+                *reinterpret_cast<const uint4*>(&tcode[c * 64 + 4 * (q ^ (c & 15))]);
+          }
+        }
+        if (a.codes) {
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const int idx = 256 * p + t, row = idx >> 2, q = idx & 3;
+            *reinterpret_cast<uint4*>(a.codes + (row0 + row) * a.ld + col0 + 16 * q) =
+                *reinterpret_cast<const uint4*>(&rcode[row * 16 + 4 * (q ^ ((row >> 2) & 3))]);
+          }
+        }
+      }
+    };
+    while (tl < tiles) {
+      const uint32_t t1 = tl + gridDim.x;
+      issue(t1 < tiles ? t1 : tl, rawB);   // unconditional: the last re-reads
+      body(tl, rawA);
+      if (t1 >= tiles) break;
+      const uint32_t t2 = t1 + gridDim.x;
+      issue(t2 < tiles ? t2 : t1, rawA);
+      body(t1, rawB);
+      tl = t2;
+    }
+    if constexpr (OP == OP_ABSMAX) {
+      amax = block_max(amax, red);
+      if (t == 0) a.partials[blockIdx.x] = amax;
+    }
+  }
+}
+
 // ================================================================ both (X under HALO-2)
 constexpr int BT = 256, BT_THREADS = 512, BT_HALF = 128, BT_PITCH = BT_HALF + 4;
 
@@ -1272,6 +1439,7 @@ HQ_PRO_DISPATCH(right_fast_kernel, RF_THREADS)
 HQ_PRO_DISPATCH(right_mma_kernel, RM_THREADS)
 HQ_PRO_DISPATCH(left_kernel, LT_THREADS)
 HQ_PRO_DISPATCH(left_fast_kernel, LF_THREADS)
+HQ_PRO_DISPATCH(left_mma_kernel, LM_THREADS)
 HQ_PRO_DISPATCH(both_kernel, BT_THREADS)
 HQ_PRO_DISPATCH(both_mma_kernel, BM_THREADS)
 #undef HQ_PRO_DISPATCH
@@ -1311,6 +1479,8 @@ int pro_grid(const ProPass& p) {
       return grid_cap((p.rows / RF_ROWS) * (p.cols / RF_COLS), RF_GRID);
     tiles = ((p.rows + RT_ROWS - 1) / RT_ROWS) * ((p.cols + RT_COLS - 1) / RT_COLS);
   } else if (p.kind == PRO_LEFT) {
+    if (left_mma_ok(p.rows, p.cols, pro_args(p).vec, dtb(p.in_dt), p.k))
+      return grid_cap((p.rows / LM_ROWS) * (p.cols / LM_COLS), LM_GRID);
     if (left_fast_ok(p.rows, p.cols, pro_args(p).vec, dtb(p.in_dt)))
       return grid_cap((p.rows / LF_ROWS) * (p.cols / LF_COLS), LF_GRID);
     const int tr = p.k > 64 ? p.k : 64, tc = LT_ELEMS / tr;
@@ -1336,6 +1506,8 @@ hipError_t pro_pass(const ProPass& p, int op, hipStream_t st) {
   else if (p.kind == PRO_RIGHT && right_fast_ok(p.rows, p.cols, a.vec))
     e = right_fast_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
   else if (p.kind == PRO_RIGHT) e = right_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
+  else if (p.kind == PRO_LEFT && left_mma_ok(p.rows, p.cols, a.vec, dtb(p.in_dt), p.k))
+    e = left_mma_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
   else if (p.kind == PRO_LEFT && left_fast_ok(p.rows, p.cols, a.vec, dtb(p.in_dt)))
     e = left_fast_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
   else if (p.kind == PRO_LEFT) e = left_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);

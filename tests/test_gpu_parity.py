@@ -128,6 +128,8 @@ def _rq(V_bits, dt, rows, cols, rot, k, bits, mode, step=None, codes=True, codes
     (B.HQ_ROT_LEFT, 256, 512, 192),      # whole 256 x 64 tiles: the persistent kernel
     (B.HQ_ROT_LEFT, 64, 768, 128),
     (B.HQ_ROT_LEFT, 2, 256, 64),
+    (B.HQ_ROT_LEFT, 16, 256, 128),       # matrix-core token-axis rotation, k = 16 and 32
+    (B.HQ_ROT_LEFT, 32, 512, 64),
     (B.HQ_ROT_BOTH, 256, 512, 512),
     (B.HQ_ROT_BOTH, 128, 256, 384),
     (B.HQ_ROT_BOTH, 16, 64, 48),
