@@ -31,6 +31,9 @@
 //     output dtype happen in a row-contiguous thread layout, and stores are coalesced; TRANS
 //     mode stores the transpose (the caller computes the transposed product when only the
 //     rows need rotating, which keeps that rotation in registers).
+#include <algorithm>
+#include <cstdlib>
+
 #include "hq_device.hpp"
 #include "hq_internal.hpp"
 
@@ -58,7 +61,8 @@ struct GemmArgs {
   const float* sb;
   float kmul;
   float* pair_part;      // PAIR: 2 fp32 partial tiles per pair of 256 x 128 tiles
-  int32_t* pair_cnt;     // PAIR: arrival flags per pair (zero on entry, left zero)
+  int32_t* pair_cnt;     // PAIR: arrival flags per pair (zero on entry, left set)
+  int pair_spin;         // PAIR: polls of the partner's flag before the wait-free fallback
 };
 
 // One 16-byte buffer load per lane straight into LDS: lane l's bytes land at lds + 16 l
@@ -456,6 +460,29 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs 
         }
       };
       float res[PAIR ? 4 : 1][NJ][8];   // PAIR: this tile's rotated values, kept for the exchange
+      // PAIR: the tile's column half, and its published values (device-coherent sc1 stores)
+      const int half = tn & 1;
+      constexpr int SLOT = NT * 4 * NJ * 8 * 4;    // bytes of one published tile
+      constexpr int kDeviceScope = 16;              // cache policy: sc1
+      const int64_t pair_id = static_cast<int64_t>(tm) * (tiles_n >> 1) + (tn >> 1);
+      auto pair_rsrc = [&]() {
+        return __builtin_amdgcn_make_buffer_rsrc(g.pair_part + pair_id * 2 * (SLOT / 4), 0, 2 * SLOT,
+                                                 kBufferFlags);
+      };
+      auto slot = [&](int part, int cc, int jj, int k) {
+        return part * SLOT + (((cc * NJ + jj) * 2 + k) * NT + t) * 16;
+      };
+      auto publish = [&](const __amdgpu_buffer_rsrc_t& rsp, int cc) {
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const float4 f = {res[cc][jj][4 * k], res[cc][jj][4 * k + 1], res[cc][jj][4 * k + 2],
+                              res[cc][jj][4 * k + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, f), rsp, slot(half, cc, jj, k),
+                                                   0, kDeviceScope);
+          }
+      };
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
         __syncthreads();
@@ -522,92 +549,80 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs 
           for (int jj = 0; jj < NJ; ++jj)
 #pragma unroll
             for (int q = 0; q < 8; ++q) res[cc][jj][q] = u[jj][q];
+          if (hh != half) publish(pair_rsrc(), cc);   // rows the partner finishes, sent at once
         } else {
           store_rows(cc, u, 0);
         }
       }
       if constexpr (PAIR) {
         // Column stride 128 of a 256-column rotation block spans the two 256 x 128 tiles of a
-        // pair (tn even = lower half). Which one finishes: each tile has a flag bit. A tile
-        // that finds its partner's bit set adds the partner's published
-        // (rotated, unscaled) values and finishes both halves; otherwise it publishes its own,
-        // sets its bit, and finishes only if the partner's bit appeared meanwhile (the partner
-        // then saw no bit and published instead of finishing). Exactly one tile finishes; the
-        // finisher clears the flag. Values move with device-coherent (sc1) buffer stores and
-        // loads: the stores are complete (s_waitcnt) before the flag's atomic, and the loads
-        // issue after it, so no cache-wide writeback or invalidate is needed.
+        // pair (tn even = lower column half). The tile of column half h finishes tile rows
+        // 128h + [0, 128) of both column halves (its lanes with hh == h): lower half = sum of
+        // the two tiles' values, upper half = lower-half tile's minus upper-half tile's. Each
+        // tile published, during the rounds above, its values of the rows its partner finishes.
+        // Flag bits: P_h (tile h published those rows), F_h (tile h published all rows and
+        // left). A tile sets P, then waits a bounded time (pair_spin polls, ~0.5 us each) for
+        // the partner's P; normally both see both bits and each finishes its own rows. After
+        // the bound (the partner may not be running yet) it publishes its remaining rows, sets
+        // F and leaves, unless the partner's P appeared meanwhile; a tile that finds the
+        // partner's F set finishes all rows. No tile waits without bound, and every output is
+        // written (twice, with equal values, in the narrow race where both finish all). Values
+        // move with device-coherent (sc1) buffer stores and loads: the stores are complete
+        // (s_waitcnt) before the flag's atomic and the loads issue after the partner's bit is
+        // seen, so no cache-wide writeback or invalidate is needed. The flags start at zero
+        // (cleared by the launch before on the stream) and are left set: a tile still polling
+        // must not see its partner's bit disappear.
         __shared__ int s_state;
-        constexpr int SLOT = NT * 4 * NJ * 8 * 4;    // bytes of one published tile
-        constexpr int kDeviceScope = 16;              // cache policy: sc1
-        const int half = tn & 1;
-        const int64_t pair_id = static_cast<int64_t>(tm) * (tiles_n >> 1) + (tn >> 1);
-        const __amdgpu_buffer_rsrc_t rsp = __builtin_amdgcn_make_buffer_rsrc(
-            g.pair_part + pair_id * 2 * (SLOT / 4), 0, 2 * SLOT, kBufferFlags);
-        const int mybit = 1 << half, otherbit = 1 << (half ^ 1);
+        const __amdgpu_buffer_rsrc_t rsp = pair_rsrc();
+        const int pme = 1 << half, pother = 1 << (half ^ 1), fme = 4 << half, fother = 4 << (half ^ 1);
         int* flag = &g.pair_cnt[pair_id];
-        auto slot = [&](int part, int cc, int jj, int k) {
-          return part * SLOT + (((cc * NJ + jj) * 2 + k) * NT + t) * 16;
-        };
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (t == 0) {
-          // The lower tile first waits a bounded time (about 20 us) for the upper tile's
-          // publication, so that normally one tile publishes and the other finishes; after the
-          // bound it falls back to the wait-free rule below, so no tile ever waits on a
-          // partner that is not running.
-          int st = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if (half == 0)
-            for (int i = 0; i < 40 && !(st & otherbit); ++i) {
-              __builtin_amdgcn_s_sleep(16);
-              st = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+          int st = __hip_atomic_fetch_or(flag, pme, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          for (int i = 0; i < g.pair_spin && !(st & pother); ++i) {
+            __builtin_amdgcn_s_sleep(16);
+            st = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
           s_state = st;
         }
         __syncthreads();
-        bool finish = (s_state & otherbit) != 0;
-        if (!finish) {
+        int st = s_state;
+        if (!(st & pother)) {
+          if (hh == half) {
 #pragma unroll
-          for (int cc = 0; cc < 4; ++cc)
+            for (int cc = 0; cc < 4; ++cc) publish(rsp, cc);
+          }
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          __syncthreads();
+          if (t == 0) s_state = __hip_atomic_fetch_or(flag, fme, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __syncthreads();
+          st = s_state;
+          if (!(st & pother)) return;
+        }
+        if (hh == half || (st & fother)) {
+          const float sgn_own = half ? -1.0f : 1.0f;
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) {
+            float lo[NJ][8], up[NJ][8];
 #pragma unroll
             for (int jj = 0; jj < NJ; ++jj)
 #pragma unroll
               for (int k = 0; k < 2; ++k) {
-                const float4 f = {res[cc][jj][4 * k], res[cc][jj][4 * k + 1], res[cc][jj][4 * k + 2],
-                                  res[cc][jj][4 * k + 3]};
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, f), rsp,
-                                                       slot(half, cc, jj, k), 0, kDeviceScope);
+                const float4 f = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                    rsp, slot(half ^ 1, cc, jj, k), 0, kDeviceScope));
+                const float pv[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const float own = res[cc][jj][4 * k + e];
+                  lo[jj][4 * k + e] = own + pv[e];
+                  up[jj][4 * k + e] = __builtin_fmaf(own, sgn_own, -sgn_own * pv[e]);
+                }
               }
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-          __syncthreads();
-          if (t == 0)
-            s_state = __hip_atomic_fetch_or(flag, mybit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __syncthreads();
-          finish = (s_state & otherbit) != 0;
-          if (!finish) return;
+            store_rows(cc, lo, -BN * half);
+            store_rows(cc, up, BN * (1 - half));
+          }
         }
-        // finisher: lower half = own + partner (or partner + own), upper = lower-half value
-        // minus upper-half value; both halves of the 256-column block are stored here
-        const float sgn_own = half ? -1.0f : 1.0f;
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          float lo[NJ][8], up[NJ][8];
-#pragma unroll
-          for (int jj = 0; jj < NJ; ++jj)
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-              const float4 f = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
-                  rsp, slot(half ^ 1, cc, jj, k), 0, kDeviceScope));
-              const float pv[4] = {f.x, f.y, f.z, f.w};
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float own = res[cc][jj][4 * k + e];
-                lo[jj][4 * k + e] = own + pv[e];
-                up[jj][4 * k + e] = __builtin_fmaf(own, sgn_own, -sgn_own * pv[e]);
-              }
-            }
-          store_rows(cc, lo, -BN * half);
-          store_rows(cc, up, BN * (1 - half));
-        }
-        if (t == 0) __hip_atomic_store(flag, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
@@ -677,7 +692,10 @@ size_t gemm_split_bytes(int64_t pairs) {
 
 hipError_t gemm_pass(const GemmPass& p, hipStream_t st) {
   GemmArgs a{p.a, p.lda, p.b, p.ldb, p.M, p.N, p.K, p.c, p.ldc, p.sa, p.sb, p.kmul,
-             nullptr, nullptr};
+             nullptr, nullptr, 40};
+  // Test hook: HQ_PAIR_SPIN bounds the tile-pair wait (40 polls of ~0.5 us by default); 0 makes
+  // every early tile take the wait-free fallback, which tests use to cover that path.
+  if (const char* e = std::getenv("HQ_PAIR_SPIN")) a.pair_spin = std::max(0, std::atoi(e));
   if (p.M == 0 || p.N == 0) return hipSuccess;
   const int64_t pairs = gemm_split_tiles(p.M, p.N, p.K, p.epi, p.km, p.kn, p.trans_out);
   if (pairs > 0) {

@@ -275,12 +275,30 @@ def test_layer_variants_and_k(variant, k):
                                      (16, 256, 512, 1040), (128, 512, 768, 2048)])
 def test_layer_narrow_dx(k, N, C, D):
     """HALO-2 dX with few 256 x 256 tiles runs on 256 x 128 tiles; with k = 256 the column
-    rotation spans a pair of tiles, which exchange their rotated values and one of them
-    finishes both (k <= 128 rotates inside a tile). A ragged K puts a short last K step in
-    every tile. Two layers in a row also check that the pair flags are left at zero."""
+    rotation spans a pair of tiles, which exchange their rotated values and each finish half
+    of the rows (k <= 128 rotates inside a tile). A ragged K puts a short last K step in every
+    tile. Two layers in a row also check that the pair flags are cleared before each use."""
     for rep in range(2):
         cfg = WL.config(2, N=N, C=C, D=D, k=k)
         banner("narrow-dx", k, N, C, D, rep)
+        inputs = WL.make_inputs(cfg)
+        res = run_gpu(cfg, inputs, out_dt=O.F32)
+        h = host(res, O.F32)
+        for name, ref in outputs_from_gpu_codes(cfg, h).items():
+            err = rel_fro(h[name], ref)
+            assert err <= 1e-5, (name, err)
+
+
+@pytest.mark.parametrize("N,C,D", [(256, 512, 1024), (512, 1024, 776)])
+def test_layer_narrow_dx_fallback(N, C, D, monkeypatch):
+    """The wait-free fallback of the tile pairs: with no polling, a tile that arrives before
+    its partner publishes all its rows and leaves, and the partner finishes the whole block
+    (or both finish their own rows when they meet). Forced from the host through the
+    HQ_PAIR_SPIN hook; every kernel still ends normally."""
+    monkeypatch.setenv("HQ_PAIR_SPIN", "0")
+    for rep in range(2):
+        cfg = WL.config(2, N=N, C=C, D=D, k=256)
+        banner("narrow-dx-fallback", N, C, D, rep)
         inputs = WL.make_inputs(cfg)
         res = run_gpu(cfg, inputs, out_dt=O.F32)
         h = host(res, O.F32)
