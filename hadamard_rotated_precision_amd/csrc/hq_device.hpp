@@ -208,6 +208,16 @@ __device__ inline void quad_stage(float (&v)[N], int lane, int m) {
   }
 }
 
+// ---------------------------------------------------------------- direct-to-LDS loads
+constexpr int kBufferFlags = 0x00020000;   // raw untyped buffer, 32-bit records
+
+// One 16-byte buffer load per lane straight into LDS: lane l's bytes land at lds + 16 l
+// (the LDS base is wave-uniform and goes through M0).
+__device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t rs, int8_t* lds, int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voffset, 0, 0, 0);
+}
+
 // ---------------------------------------------------------------- reductions
 __device__ inline float wave_max(float x) {
 #pragma unroll

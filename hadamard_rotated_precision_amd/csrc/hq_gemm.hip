@@ -46,7 +46,6 @@ typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 constexpr int GBM = 256;
 constexpr int kGroupM = 8;
-constexpr int kBufferFlags = 0x00020000;   // raw untyped buffer, 32-bit records
 constexpr int kOutOfRange = 0x7FFFFFF0;    // an offset past any descriptor: the load reads 0
 
 struct GemmArgs {
@@ -65,12 +64,6 @@ struct GemmArgs {
   int pair_spin;         // PAIR: polls of the partner's flag before the wait-free fallback
 };
 
-// One 16-byte buffer load per lane straight into LDS: lane l's bytes land at lds + 16 l
-// (the LDS base is wave-uniform and goes through M0).
-__device__ inline void lds_dma16(__amdgpu_buffer_rsrc_t rs, int8_t* lds, int voffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16,
-                                           voffset, 0, 0, 0);
-}
 
 // LDS layout of an operand stage: rows of KB bytes (KB = K bytes per step), the 16-byte chunk
 // index XOR-swizzled so that the 128-bit fragment reads of 16 consecutive rows hit 16

@@ -1252,16 +1252,20 @@ constexpr int BM_THREADS = 512;
 __host__ __device__ inline bool both_mma_ok(int64_t rows, int64_t cols, bool vec, int in_bytes,
                                             int k) {
   return vec && in_bytes == 2 && k >= 16 && k <= BT && rows > 0 && cols > 0 && rows % BT == 0 &&
-         cols % BT == 0;
+         cols % BT == 0 && cols <= (int64_t(1) << 22);   // 256 rows stay 32-bit addressable
 }
 
 __device__ inline int bm_chunk(int c, int c4) { return c4 ^ (c & 15) ^ (4 * ((c4 >> 4) & 3)); }
 
-template <class In, int K, int OP>
-__global__ __launch_bounds__(BM_THREADS) void both_mma_kernel(ProArgs a) {
-  if constexpr (In::bytes != 2 || K < 16) {
-    return;
-  } else {
+// PIPE (a workgroup has several items): the item's raw 16-bit rows (all 256 columns for k = 256,
+// else the item's 128) are brought into the half-tile buffer by direct-to-LDS buffer loads,
+// issued as soon as the previous item's column phase has read its values out of LDS, so they
+// land while that item's fp64 rotation runs. Rows of RAWB bytes, 16-byte chunk c of row r at
+// c ^ (r % 16): the fragment reads of 16 consecutive rows meet distinct bank groups. Each wave
+// reads its A fragments from there, and after a barrier the buffer takes the fp32 half tile.
+template <class In, int K, int OP, bool PIPE>
+__device__ inline void both_mma_body(const ProArgs& a) {
+  {
     __shared__ __attribute__((aligned(16))) float half[BT_HALF * BT];   // [column][row], swizzled
     __shared__ float red[32];
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -1287,10 +1291,9 @@ __global__ __launch_bounds__(BM_THREADS) void both_mma_kernel(ProArgs a) {
     hfrags<In, KM>(lane, G);
     const char* src = static_cast<const char*>(a.src);
     float amax1 = 0.0f, amax2 = 0.0f;
-    for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-      const int64_t full = items / 16 * 16;
+    const int64_t full = items / 16 * 16;
+    auto decode = [&](int64_t it, int64_t& row0, int64_t& col0, int& h) {
       int64_t tl;
-      int h;
       if (it < full) {
         tl = (it / 16) * 8 + (it % 8);
         h = static_cast<int>((it / 8) & 1);
@@ -1298,16 +1301,61 @@ __global__ __launch_bounds__(BM_THREADS) void both_mma_kernel(ProArgs a) {
         tl = full / 2 + (it - full) / 2;
         h = static_cast<int>((it - full) & 1);
       }
-      const int64_t row0 = (tl / nct) * BT, col0 = (tl % nct) * BT;
+      row0 = (tl / nct) * BT;
+      col0 = (tl % nct) * BT;
+    };
+    constexpr int RAWB = 2 * 32 * NKS;      // bytes of one raw row in LDS (512 or 256)
+    constexpr int NCH = RAWB / 16, RPK = 1024 / RAWB;
+    int8_t* const raw = reinterpret_cast<int8_t*>(half);
+    // direct-to-LDS loads of item it's raw rows: 1 KB blocks w + 8i, lane l -> row
+    // RPK (w + 8i) + l / NCH, slot l % NCH = chunk (l % NCH) ^ (row % 16)
+    auto issue_raw = [&](int64_t it) {
+      int64_t row0, col0;
+      int h;
+      decode(it, row0, col0, h);
+      const int64_t ccol = col0 + (NKS == 8 ? 0 : BT_HALF * h);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(src + (row0 * a.cols + ccol) * 2), 0, static_cast<int>(BT * a.cols * 2),
+          kBufferFlags);
+#pragma unroll
+      for (int i = 0; i < BT / RPK / 8; ++i) {
+        const int b = w + 8 * i, r = RPK * b + lane / NCH, c = (lane % NCH) ^ (r & 15);
+        lds_dma16(rs, raw + b * 1024, r * static_cast<int>(a.cols) * 2 + 16 * c);
+      }
+    };
+    if constexpr (PIPE) {
+      if (static_cast<int64_t>(blockIdx.x) < items) issue_raw(blockIdx.x);
+    }
+    for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+      int64_t row0, col0;
+      int h;
+      decode(it, row0, col0, h);
       const int64_t ccol = col0 + (NKS == 8 ? 0 : BT_HALF * h);   // first column read
-      __syncthreads();   // the previous item's column phase is done with the half tile
+      uint4 xr[PIPE ? 2 : 1][NKS];
+      if constexpr (PIPE) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's raw loads landed
+        __syncthreads();                                    // and every wave's
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const int r = 32 * w + 16 * rb + n0;
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks)
+            xr[rb][ks] = *reinterpret_cast<const uint4*>(raw + r * RAWB + 16 * ((4 * ks + lg) ^ (r & 15)));
+        }
+      }
+      __syncthreads();   // the half tile is free: raw rows read, or the previous column phase done
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         const int rloc = 32 * w + 16 * rb;   // first tile row of this block
-        const char* p = src + ((row0 + rloc + n0) * a.cols + ccol + 8 * lg) * 2;
         uint4 x[NKS];
+        if constexpr (PIPE) {
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) x[ks] = *reinterpret_cast<const uint4*>(p + 64 * ks);
+          for (int ks = 0; ks < NKS; ++ks) x[ks] = xr[rb][ks];
+        } else {
+          const char* p = src + ((row0 + rloc + n0) * a.cols + ccol + 8 * lg) * 2;
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) x[ks] = *reinterpret_cast<const uint4*>(p + 64 * ks);
+        }
         f32x4 acc[NNB];
         mma_rows<In, KM, NKS, NNB>(x, G, acc);
         mma_high_stages<K, NNB, 128>(acc);
@@ -1356,6 +1404,10 @@ __global__ __launch_bounds__(BM_THREADS) void both_mma_kernel(ProArgs a) {
         u[4 * i + 2] = f.z;
         u[4 * i + 3] = f.w;
       }
+      if constexpr (PIPE) {
+        __syncthreads();   // every wave has its column values: the buffer takes the next raw rows
+        if (it + gridDim.x < items) issue_raw(it + gridDim.x);
+      }
       fwht_from<1, K, 64>(u);
       if constexpr (K > 64) quad_stage_f64<1, 64>(u, lane);
       if constexpr (K > 128) quad_stage_f64<2, 64>(u, lane);
@@ -1389,6 +1441,16 @@ __global__ __launch_bounds__(BM_THREADS) void both_mma_kernel(ProArgs a) {
       }
     }
   }
+}
+
+template <class In, int K, int OP>
+__global__ __launch_bounds__(BM_THREADS) void both_mma_kernel(ProArgs a) {
+  if constexpr (In::bytes == 2 && K >= 16) both_mma_body<In, K, OP, false>(a);
+}
+
+template <class In, int K, int OP>
+__global__ __launch_bounds__(BM_THREADS) void both_pipe_kernel(ProArgs a) {
+  if constexpr (In::bytes == 2 && K >= 16) both_mma_body<In, K, OP, true>(a);
 }
 
 // ================================================================ launchers
@@ -1442,6 +1504,7 @@ HQ_PRO_DISPATCH(left_fast_kernel, LF_THREADS)
 HQ_PRO_DISPATCH(left_mma_kernel, LM_THREADS)
 HQ_PRO_DISPATCH(both_kernel, BT_THREADS)
 HQ_PRO_DISPATCH(both_mma_kernel, BM_THREADS)
+HQ_PRO_DISPATCH(both_pipe_kernel, BM_THREADS)
 #undef HQ_PRO_DISPATCH
 
 static int dtb(int dt) { return dt == DT_F32 ? 4 : 2; }
@@ -1511,6 +1574,8 @@ hipError_t pro_pass(const ProPass& p, int op, hipStream_t st) {
   else if (p.kind == PRO_LEFT && left_fast_ok(p.rows, p.cols, a.vec, dtb(p.in_dt)))
     e = left_fast_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
   else if (p.kind == PRO_LEFT) e = left_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
+  else if (both_mma_ok(p.rows, p.cols, a.vec, dtb(p.in_dt), p.k) && both_items(p.rows, p.cols) > grid)
+    e = both_pipe_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
   else if (both_mma_ok(p.rows, p.cols, a.vec, dtb(p.in_dt), p.k))
     e = both_mma_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
   else e = both_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);

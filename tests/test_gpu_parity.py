@@ -136,6 +136,7 @@ def _rq(V_bits, dt, rows, cols, rot, k, bits, mode, step=None, codes=True, codes
     (B.HQ_ROT_BOTH, 128, 256, 512),      # whole 256 x 256 tiles: matrix-core row phase
     (B.HQ_ROT_BOTH, 16, 256, 256),
     (B.HQ_ROT_BOTH, 64, 512, 768),
+    (B.HQ_ROT_BOTH, 16, 2048, 4352),     # 272 items on 256 workgroups: pipelined raw loads
 ])
 @pytest.mark.parametrize("bits,mode", [(8, B.HQ_SCALE_ABSMAX), (4, B.HQ_SCALE_STEP)])
 @pytest.mark.parametrize("dt", [B.HQ_BF16, B.HQ_F16, B.HQ_F32])
