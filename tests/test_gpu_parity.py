@@ -168,6 +168,21 @@ def test_rotate_quantize_parity(rot, k, rows, cols, bits, mode, dt):
     assert q.st.rows == rows and q.st.cols == cols and q.st.rot == rot and q.st.k == k
 
 
+@pytest.mark.parametrize("k,rows,cols", [(256, 1024, 8448), (128, 2048, 4352)])
+def test_rotate_quantize_both_pipelined(k, rows, cols):
+    """X B and B X B with more items than workgroups (264 and 272 half tiles on 256): the
+    next item's raw rows load into LDS during the current item's fp64 column phase."""
+    banner("rq-both-pipe", k, rows, cols)
+    rng = np.random.default_rng(rows + cols + k)
+    V = rng.standard_normal((rows, cols))
+    V[:, rng.choice(cols, 8, replace=False)] *= 40.0
+    vb = WL.to_dtype_bits(V, B.HQ_BF16)
+    q = _rq(vb, B.HQ_BF16, rows, cols, B.HQ_ROT_BOTH, k, 8, B.HQ_SCALE_ABSMAX, codes=False)
+    ref_codes, ref_s = O.quantize_tensor(O.decode(vb, B.HQ_BF16), B.HQ_ROT_BOTH, k, 8, O.ABSMAX)
+    assert_codes(q.codes_t_view().cpu().numpy().T, ref_codes, "codes_t")
+    assert_scale(float(q.scale.cpu()[0]), ref_s, "scale")
+
+
 @pytest.mark.parametrize("rot", [B.HQ_ROT_RIGHT, B.HQ_ROT_LEFT])
 def test_rotate_quantize_single_layout(rot):
     """Only one code layout requested (the other is staged in the workspace)."""
