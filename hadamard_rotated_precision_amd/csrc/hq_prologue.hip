@@ -11,20 +11,23 @@
 // the next pass, so no atomics and an order-independent result) and a quantize pass that
 // recomputes the rotation and writes codes. In STEP mode only the quantize pass runs.
 //
-//   right_mma_kernel : rotation along the contiguous axis of 16-bit tensors of whole 64 x 256
-//                  tiles, as a +-1 contraction on the matrix cores (blocks up to 64 columns)
-//                  plus in-register butterflies for the strides 64 and 128.
-//   right_kernel : rotation along the contiguous axis. Tile 64 rows x 256 columns; four lanes
-//                  share a row, each owning 64 consecutive columns, so strides < 64 are
-//                  in-register butterflies and strides 64, 128 are quad-lane DPP exchanges.
-//                  Transposed codes go through LDS as bytes and leave as 64-byte rows.
-//   left_mma_kernel : token-axis rotation of 16-bit tensors of whole 256 x 64 tiles on the matrix
-//                  cores (H fragments as the A operand, the tile's columns read from LDS as B).
-//   left_kernel  : rotation along rows (the token axis). The tile (TR x 16384/TR) is staged in
+// Matrix-core kernels (16-bit inputs of whole tiles, k >= 16): the rotation is the product with
+// blockdiag(H_k) on v_mfma_f32_16x16x32_{bf16,f16} in blocks of up to 64, plus in-register
+// butterflies for the strides 64 and 128.
+//   right_mma_kernel : along the contiguous axis (W; X under HQ), 64 x 256 tiles.
+//   left_mma_kernel  : along the token axis (dY under HALO-2), 256 x 64 tiles staged raw in LDS,
+//                      H fragments as the A operand.
+//   both_mma_kernel  : X under HALO-2, 256 x 256 tiles: the row phase on the matrix cores, the
+//                      half tile staged column-major, the token phase in fp64;
+//                      both_pipe_kernel is the same with the next item's raw rows loaded into
+//                      LDS during the current item's token phase (several items per workgroup).
+// VALU kernels (every other shape: fp32 inputs, k < 16, ragged tiles, unaligned pitches):
+//   right_fast_kernel / right_kernel : rotation along the contiguous axis. Tile 64 rows x 256
+//                  columns; four lanes share a row, so strides < 64 are in-register butterflies
+//                  and the rest DPP exchanges. Transposed codes go through LDS.
+//   left_fast_kernel / left_kernel : rotation along rows (the token axis). The tile is staged in
 //                  LDS as fp32 with a column swizzle; a thread then owns 64 consecutive rows of
 //                  one column (in-register butterflies) and four lanes share a column.
-//   both_mma_kernel : X under HALO-2 for 16-bit inputs and whole 256 x 256 tiles: the row phase
-//                  of both_kernel on the matrix cores, the half tile staged column-major.
 //   both_kernel  : X under HALO-2, 256 x 256 tiles, 512 threads: the right rotation (two rows
 //                  per thread) feeds the row-major codes of Q(X B); the same registers, staged
 //                  through LDS in two 128-column halves, feed the token-axis rotation (64 rows of
