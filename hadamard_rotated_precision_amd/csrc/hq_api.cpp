@@ -19,6 +19,7 @@ using hq::RowPass;
 
 constexpr size_t kPartialBytes = 4 * hq::kMaxPartials * sizeof(float);   // 4 partial arrays
 constexpr size_t kAlign = 256;
+constexpr size_t kBarBytes = hq::kBarWordsInts * sizeof(int32_t);          // grid-barrier words
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int64_t pitch16(int64_t n) { return (n + 15) / 16 * 16; }
@@ -36,9 +37,10 @@ hq_status check_cfg(const hq_config* cfg) {
   return HQ_OK;
 }
 
-// Workspace: the absmax partial arrays plus one spare device float, then (when the dX product
-// of a HALO-2 layer runs on paired 256 x 128 tiles) the pair flags and published tiles.
-size_t ws_need() { return kPartialBytes + kAlign; }
+// Workspace: the absmax partial arrays, one spare device float, the grid-barrier words of the
+// single-pass two-sided kernel, then (when the dX product of a HALO-2 layer runs on paired
+// 256 x 128 tiles) the pair flags and published tiles.
+size_t ws_need() { return kPartialBytes + kAlign + kBarBytes; }
 
 int64_t dx_split_tiles(const hq_config* cfg, int64_t N, int64_t C, int64_t D) {
   if (cfg->variant != HQ_VARIANT_HALO2 || cfg->k <= 1) return 0;
@@ -60,11 +62,13 @@ hq_status check_ws(void* ws, size_t ws_bytes, size_t need) {
 struct Ws {
   float* part[4];
   float* spare;
-  void* split;   // split-K area (only as large as the call's hq_workspace_bytes allows)
+  int32_t* bar;  // grid-barrier words (kBarWordsInts)
+  void* split;   // tile-pair area (only as large as the call's hq_workspace_bytes allows)
   explicit Ws(void* base) {
     char* b = static_cast<char*>(base);
     for (int i = 0; i < 4; ++i) part[i] = reinterpret_cast<float*>(b + i * hq::kMaxPartials * 4);
     spare = reinterpret_cast<float*>(b + kPartialBytes);
+    bar = reinterpret_cast<int32_t*>(b + kPartialBytes + kAlign);
     split = b + ws_need();
   }
 };
@@ -136,15 +140,10 @@ hq_status quantize_tensor(const void* src, int32_t dt, int64_t rows, int64_t col
   return HQ_OK;
 }
 
-// X under HALO-2: one pass pair writes Q(X B) row-major and Q(B X B) transposed.
-hq_status quantize_x_both(const void* src, int32_t dt, int64_t rows, int64_t cols, int32_t k,
-                          int32_t bits, const float* step_x, const float* step_xt,
-                          hq_qtensor* qx, hq_qtensor* qxt, const Ws& ws, hipStream_t st) {
-  if (rows * cols == 0) {
-    HQ_TRY(hq::write_scale(qx->scale, step_x, st));
-    HQ_TRY(hq::write_scale(qxt->scale, step_xt, st));
-    return HQ_OK;
-  }
+// The two-sided pass of X under HALO-2: Q(X B) row-major and Q(B X B) transposed.
+hq::ProPass x_both_pass(const void* src, int32_t dt, int64_t rows, int64_t cols, int32_t k,
+                        int32_t bits, const float* step_x, const float* step_xt, hq_qtensor* qx,
+                        hq_qtensor* qxt, const Ws& ws) {
   hq::ProPass p;
   p.kind = hq::PRO_BOTH;
   p.src = src;
@@ -162,6 +161,19 @@ hq_status quantize_x_both(const void* src, int32_t dt, int64_t rows, int64_t col
   p.ld = qx->ld;
   p.codes_t = qxt->codes_t;
   p.ld_t = qxt->ld_t;
+  return p;
+}
+
+// X under HALO-2: one pass pair writes Q(X B) row-major and Q(B X B) transposed.
+hq_status quantize_x_both(const void* src, int32_t dt, int64_t rows, int64_t cols, int32_t k,
+                          int32_t bits, const float* step_x, const float* step_xt,
+                          hq_qtensor* qx, hq_qtensor* qxt, const Ws& ws, hipStream_t st) {
+  if (rows * cols == 0) {
+    HQ_TRY(hq::write_scale(qx->scale, step_x, st));
+    HQ_TRY(hq::write_scale(qxt->scale, step_xt, st));
+    return HQ_OK;
+  }
+  hq::ProPass p = x_both_pass(src, dt, rows, cols, k, bits, step_x, step_xt, qx, qxt, ws);
   if (!step_x) {
     p.nparts = hq::pro_grid(p);
     HQ_TRY(hq::pro_pass(p, hq::OP_ABSMAX, st));
@@ -307,7 +319,25 @@ hq_status hq_linear_fwd(const void* x, const void* w, int32_t in_dtype, int64_t 
   hipStream_t st = static_cast<hipStream_t>(stream);
   Ws wsp(ws);
   const int32_t rx = x_rot(v);
-  if (want_xt && !save_x->codes_t && !save_xt->codes && k > 1) {
+  const bool two_sided = want_xt && !save_x->codes_t && !save_xt->codes && k > 1;
+  // X's two-sided pass runs in a single launch over a grid barrier when it is small enough;
+  // W's quantize pass, launched just before, zeroes the barrier words
+  hq::ProPass px;
+  bool single = false;
+  if (two_sided && !stepm && N * C > 0) {
+    px = x_both_pass(x, in_dtype, N, C, k, cfg->bits, nullptr, nullptr, save_x, save_xt, wsp);
+    single = hq::pro_single_ok(px) && D * C > 0;
+  }
+  HQ_CHECK(quantize_tensor(w, in_dtype, D, C, rx, k, cfg->bits, stepm ? step_w : nullptr,
+                           save_w->codes, save_w->ld, save_w->codes_t, save_w->ld_t,
+                           save_w->scale, wsp, 2, st, single ? wsp.bar : nullptr,
+                           single ? hq::kBarWordsInts : 0));
+  fill_meta(save_w, D, C, k, cfg->bits, rx);
+  if (single) {
+    px.nparts = hq::pro_grid(px);
+    HQ_TRY(hq::pro_single_pass(px, wsp.bar, st));
+    HQ_TRY(hq::pro_fixup_pass(px, wsp.bar, st));
+  } else if (two_sided) {
     HQ_CHECK(quantize_x_both(x, in_dtype, N, C, k, cfg->bits, stepm ? step_x : nullptr,
                              stepm ? step_xt : nullptr, save_x, save_xt, wsp, st));
   } else {
@@ -322,10 +352,6 @@ hq_status hq_linear_fwd(const void* x, const void* w, int32_t in_dtype, int64_t 
   }
   fill_meta(save_x, N, C, k, cfg->bits, rx);
   if (want_xt) fill_meta(save_xt, N, C, k, cfg->bits, HQ_ROT_BOTH);
-  HQ_CHECK(quantize_tensor(w, in_dtype, D, C, rx, k, cfg->bits, stepm ? step_w : nullptr,
-                           save_w->codes, save_w->ld, save_w->codes_t, save_w->ld_t,
-                           save_w->scale, wsp, 2, st));
-  fill_meta(save_w, D, C, k, cfg->bits, rx);
   GemmPass g;
   g.a = save_x->codes;
   g.lda = save_x->ld;

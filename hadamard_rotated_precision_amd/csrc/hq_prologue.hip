@@ -32,6 +32,9 @@
 //                  per thread) feeds the row-major codes of Q(X B); the same registers, staged
 //                  through LDS in two 128-column halves, feed the token-axis rotation (64 rows of
 //                  one column per thread) whose codes Q(B X B) are written transposed.
+#include <algorithm>
+#include <cstdlib>
+
 #include "hq_device.hpp"
 #include "hq_internal.hpp"
 
@@ -78,7 +81,16 @@ struct ProArgs {
   int64_t ld_t;
   int32_t* zero_ptr;        // QUANT: block 0 zeroes these ints for a later launch
   int64_t zero_n;
+  int32_t* bar;             // both_single_kernel: barrier words (zeroed by the launch before);
+                            // a QUANT pass given bar runs only if the single pass aborted
+  int spin;                 // both_single_kernel: polls of the barrier before giving up
 };
+
+// Barrier words of the single-pass two-sided kernel: arrival counters of eight workgroup groups
+// (128 bytes apart), the group-completion counter and the state word (0 open, 1 released,
+// 2 aborted).
+constexpr int kBarGroups = 8, kBarStride = 32, kGroupDone = 256, kReleaseWord = 288,
+              kStateAborted = 2;
 
 // Counters a later launch on the stream needs at zero (the split-K arrivals of the GEMM).
 __device__ inline void zero_side(const ProArgs& a) {
@@ -1278,6 +1290,10 @@ __device__ inline void both_mma_body(const ProArgs& a) {
     const int64_t items = both_items(a.rows, a.cols);
     float s1 = 0.0f, r1 = 0.0f, sc2 = 0.0f, r2 = 0.0f;
     if constexpr (OP == OP_QUANT) {
+      // the fallback pass after the single-pass kernel: nothing to do unless it aborted
+      if (a.bar != nullptr && __hip_atomic_load(&a.bar[kReleaseWord], __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT) != kStateAborted)
+        return;
       tensor_scale(a.part_in, a.nparts, a.step, a.qp, red, s1, r1);
       tensor_scale(a.part_in2, a.nparts, a.step2, a.qp, red, sc2, r2);
       zero_side(a);
@@ -1456,6 +1472,230 @@ __global__ __launch_bounds__(BM_THREADS) void both_pipe_kernel(ProArgs a) {
   if constexpr (In::bytes == 2 && K >= 16) both_mma_body<In, K, OP, true>(a);
 }
 
+// ================================================================ both, single pass
+// X under HALO-2 in ABSMAX mode when every workgroup has exactly one item (2048 x 4096 and
+// smaller): the two passes in one launch. Each workgroup computes X B (kept in LDS, column-major
+// as in both_mma) and B X B (kept in registers as fp32), publishes its two partial maxima with
+// device-coherent stores, and arrives at a grid barrier: per-group arrival counters (eight
+// groups), then a group-completion counter whose last arrival moves the state word from open to
+// released with a compare-and-swap. Relaxed atomics only, so no cache-wide writeback is needed:
+// the only data crossing workgroups are the partials, written and read at device scope. The
+// others wait for the release a bounded time (a.spin polls), then read all partials, form both
+// scales exactly as the two-pass kernels do, and write the codes of X B and B X B from what they
+// kept. A workgroup whose wait runs out (some workgroup of the grid is not running yet) moves
+// the state to aborted (unless it was released meanwhile) and leaves without writing codes;
+// after an abort nobody writes codes, and the both_mma QUANT pass launched next on the stream
+// (given a.bar) recomputes them all from the partials, which every workgroup publishes before
+// it waits. Without an abort that pass returns at once. No wait is unbounded. The barrier words
+// are zeroed by the launch before on the stream.
+// One item of the single-pass kernel: compute() puts X B of the item in the LDS half tile (and
+// returns this thread's maxima) and B X B of this thread's column segment in v2; emit() writes
+// the item's codes from those with the given reciprocal scales.
+template <class In, int K>
+struct BothItem {
+  static constexpr int KM = K < 64 ? K : 64, NKS = K > 128 ? 8 : 4, NNB = K > 128 ? 16 : 8;
+  const ProArgs& a;
+  float* half;
+  int t, lane, w, n0, lg, cp, pp;
+  int64_t nct, items, full;
+  uint4 G[4];
+  float v2[64];
+  __device__ BothItem(const ProArgs& args, float* h) : a(args), half(h) {
+    t = threadIdx.x;
+    lane = t & 63;
+    w = t >> 6;
+    n0 = lane & 15;
+    lg = lane >> 4;
+    cp = t >> 2;
+    pp = t & 3;
+    nct = a.cols / BT;
+    items = both_items(a.rows, a.cols);
+    full = items / 16 * 16;
+    hfrags<In, KM>(lane, G);
+  }
+  __device__ void decode(int64_t it, int64_t& row0, int64_t& col0, int& h) const {
+    int64_t tl;
+    if (it < full) {
+      tl = (it / 16) * 8 + (it % 8);
+      h = static_cast<int>((it / 8) & 1);
+    } else {
+      tl = full / 2 + (it - full) / 2;
+      h = static_cast<int>((it - full) & 1);
+    }
+    row0 = (tl / nct) * BT;
+    col0 = (tl % nct) * BT;
+  }
+  __device__ void compute(int64_t it, float& m1, float& m2) {
+    int64_t row0, col0;
+    int h;
+    decode(it, row0, col0, h);
+    const int64_t ccol = col0 + (NKS == 8 ? 0 : BT_HALF * h);
+    const char* src = static_cast<const char*>(a.src);
+    __syncthreads();   // the previous item's readers of the half tile are done
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int rloc = 32 * w + 16 * rb;
+      const char* p = src + ((row0 + rloc + n0) * a.cols + ccol + 8 * lg) * 2;
+      uint4 x[NKS];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) x[ks] = *reinterpret_cast<const uint4*>(p + 64 * ks);
+      f32x4 acc[NNB];
+      mma_rows<In, KM, NKS, NNB>(x, G, acc);
+      mma_high_stages<K, NNB, 128>(acc);
+      f32x4 y[8];
+      if constexpr (K > 128) {
+        const float sg = h ? -1.0f : 1.0f;
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) y[nb][j] = __builtin_fmaf(acc[nb + 8][j], sg, acc[nb][j]);
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) y[nb] = acc[nb];
+      }
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) m1 = fmaxf(m1, fabsf(y[nb][j]));
+      const int c4 = (rloc >> 2) + lg;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const int c = 16 * nb + n0;
+        *reinterpret_cast<float4*>(&half[c * BT + 4 * bm_chunk(c, c4)]) =
+            make_float4(y[nb][0], y[nb][1], y[nb][2], y[nb][3]);
+      }
+    }
+    __syncthreads();
+    double u[64];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float4 f = *reinterpret_cast<const float4*>(&half[cp * BT + 4 * bm_chunk(cp, 16 * pp + i)]);
+      u[4 * i] = f.x;
+      u[4 * i + 1] = f.y;
+      u[4 * i + 2] = f.z;
+      u[4 * i + 3] = f.w;
+    }
+    fwht_from<1, K, 64>(u);
+    if constexpr (K > 64) quad_stage_f64<1, 64>(u, lane);
+    if constexpr (K > 128) quad_stage_f64<2, 64>(u, lane);
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      v2[i] = static_cast<float>(u[i]);
+      m2 = fmaxf(m2, fabsf(v2[i]));
+    }
+  }
+  __device__ void emit(int64_t it, float r1, float r2) const {
+    int64_t row0, col0;
+    int h;
+    decode(it, row0, col0, h);
+    const float lo = qlo(a.qp), hi = qhi(a.qp);
+    if (a.codes) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int rloc = 32 * w + 16 * rb, c4 = (rloc >> 2) + lg;
+        const int i = n0 & 3, m = n0 >> 2;
+        int8_t* dst = a.codes + (row0 + rloc + 4 * lg + i) * a.ld + col0 + BT_HALF * h + 4 * m;
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+          const int c = 16 * nb + n0;
+          const float4 y = *reinterpret_cast<const float4*>(&half[c * BT + 4 * bm_chunk(c, c4)]);
+          const uint32_t d = qpack4(qbits(y.x, r1, lo, hi), qbits(y.y, r1, lo, hi),
+                                    qbits(y.z, r1, lo, hi), qbits(y.w, r1, lo, hi));
+          *reinterpret_cast<uint32_t*>(dst + 16 * nb) = quad_byte_transpose(d, i);
+        }
+      }
+    }
+    int8_t* dst = a.codes_t + (col0 + BT_HALF * h + cp) * a.ld_t + row0 + 64 * pp;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t xq[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 16 * q + 4 * j;
+        xq[j] = qpack4(qbits(v2[i], r2, lo, hi), qbits(v2[i + 1], r2, lo, hi),
+                       qbits(v2[i + 2], r2, lo, hi), qbits(v2[i + 3], r2, lo, hi));
+      }
+      *reinterpret_cast<uint4*>(dst + 16 * q) = make_uint4(xq[0], xq[1], xq[2], xq[3]);
+    }
+  }
+};
+
+template <class In, int K>
+__global__ __launch_bounds__(BM_THREADS) void both_single_kernel(ProArgs a) {
+  if constexpr (In::bytes != 2 || K < 16) {
+    return;
+  } else {
+    __shared__ __attribute__((aligned(16))) float half[BT_HALF * BT];   // [column][row], swizzled
+    __shared__ float red[32];
+    __shared__ int s_state;
+    constexpr int OPEN = 0, RELEASED = 1, ABORTED = 2;
+    const int t = threadIdx.x, wg = blockIdx.x, nwg = gridDim.x;   // nwg == items (host checks)
+    BothItem<In, K> b(a, half);
+    float amax1 = 0.0f, amax2 = 0.0f;
+    b.compute(wg, amax1, amax2);
+    // ---- partial maxima, grid barrier
+    amax1 = block_max(amax1, red);
+    amax2 = block_max(amax2, red);
+    if (t == 0) {
+      __hip_atomic_store(reinterpret_cast<int*>(a.partials) + wg, __float_as_int(amax1),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(reinterpret_cast<int*>(a.partials) + nwg + wg, __float_as_int(amax2),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      int* const state = &a.bar[kReleaseWord];
+      const int grp = wg % kBarGroups, gsize = (nwg - grp + kBarGroups - 1) / kBarGroups;
+      const int old = __hip_atomic_fetch_add(&a.bar[kBarStride * grp], 1, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+      bool last = false;
+      if (old == gsize - 1)
+        last = __hip_atomic_fetch_add(&a.bar[kGroupDone], 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) == kBarGroups - 1;
+      int st;
+      if (last) {
+        // release; a failed swap means some workgroup gave up: the fallback pass redoes it all
+        int expect = OPEN;
+        st = __hip_atomic_compare_exchange_strong(state, &expect, RELEASED, __ATOMIC_RELAXED,
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                 ? RELEASED
+                 : ABORTED;
+      } else {
+        st = OPEN;
+        for (int i = 0; i <= a.spin && st == OPEN; ++i) {
+          st = __hip_atomic_load(state, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (st == OPEN && i < a.spin) __builtin_amdgcn_s_sleep(1);
+        }
+        if (st == OPEN) {
+          int expect = OPEN;
+          st = __hip_atomic_compare_exchange_strong(state, &expect, ABORTED, __ATOMIC_RELAXED,
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                   ? ABORTED
+                   : expect;
+        }
+      }
+      s_state = st;
+    }
+    __syncthreads();
+    if (s_state != RELEASED) return;
+    // ---- scales from every partial (as tensor_scale), then the codes
+    float p1 = 0.0f, p2 = 0.0f;
+    for (int i = t; i < nwg; i += BM_THREADS) {
+      p1 = fmaxf(p1, __int_as_float(__hip_atomic_load(reinterpret_cast<int*>(a.partials) + i,
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
+      p2 = fmaxf(p2, __int_as_float(__hip_atomic_load(reinterpret_cast<int*>(a.partials) + nwg + i,
+                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
+    }
+    p1 = block_max(p1, red);
+    p2 = block_max(p2, red);
+    const float s1 = p1 / static_cast<float>(a.qp), s2 = p2 / static_cast<float>(a.qp);
+    const float r1 = (s1 > 0.0f) ? 1.0f / s1 : 0.0f, r2 = (s2 > 0.0f) ? 1.0f / s2 : 0.0f;
+    if (wg == 0 && t == 0) {
+      *a.scale_out = s1;
+      *a.scale_out2 = s2;
+    }
+    b.emit(wg, r1, r2);
+  }
+}
+
 // ================================================================ launchers
 static int grid_cap(int64_t tiles, int cap) {
   if (tiles < 1) tiles = 1;
@@ -1509,6 +1749,17 @@ HQ_PRO_DISPATCH(both_kernel, BT_THREADS)
 HQ_PRO_DISPATCH(both_mma_kernel, BM_THREADS)
 HQ_PRO_DISPATCH(both_pipe_kernel, BM_THREADS)
 #undef HQ_PRO_DISPATCH
+
+template <class In>
+static hipError_t both_single_k(int k, const ProArgs& a, int grid, hipStream_t st, int tok) {
+  switch (k) {
+#define HQ_BS(KK) \
+  case KK: return launch_k(both_single_kernel<In, KK>, dim3(grid), dim3(BM_THREADS), st, tok, a);
+    HQ_BS(16) HQ_BS(32) HQ_BS(64) HQ_BS(128) HQ_BS(256)
+#undef HQ_BS
+  }
+  return hipErrorInvalidValue;
+}
 
 static int dtb(int dt) { return dt == DT_F32 ? 4 : 2; }
 
@@ -1583,6 +1834,33 @@ hipError_t pro_pass(const ProPass& p, int op, hipStream_t st) {
     e = both_mma_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
   else e = both_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
   return e;
+}
+
+bool pro_single_ok(const ProPass& p) {
+  const ProArgs a = pro_args(p);
+  return p.kind == PRO_BOTH && p.step == nullptr && both_mma_ok(p.rows, p.cols, a.vec, dtb(p.in_dt), p.k) &&
+         both_items(p.rows, p.cols) <= 256;
+}
+
+hipError_t pro_single_pass(const ProPass& p, int32_t* bar, hipStream_t st) {
+  ProArgs a = pro_args(p);
+  a.bar = bar;
+  a.spin = 40000;   // polls of ~30 ns: about 1 ms before the fallback takes over
+  if (const char* e = std::getenv("HQ_SINGLE_SPIN")) a.spin = std::max(0, std::atoi(e));
+  const int grid = static_cast<int>(both_items(p.rows, p.cols));
+  const double elems = static_cast<double>(p.rows) * p.cols;
+  const int tok = prof_open(K_ROT_ABSMAX, elems * (2.0 + (p.codes ? 1 : 0) + (p.codes_t ? 1 : 0)));
+  return p.in_dt == DT_F16 ? both_single_k<F16>(p.k, a, grid, st, tok)
+                           : both_single_k<BF16>(p.k, a, grid, st, tok);
+}
+
+hipError_t pro_fixup_pass(const ProPass& p, int32_t* bar, hipStream_t st) {
+  ProArgs a = pro_args(p);
+  a.bar = bar;
+  const int grid = pro_grid(p);
+  const double elems = static_cast<double>(p.rows) * p.cols;
+  const int tok = prof_open(K_ROT_QUANT, elems * ((p.codes ? 1 : 0) + (p.codes_t ? 1 : 0)));
+  return both_mma_kernel_launch(p.in_dt, OP_QUANT, p.k, a, grid, st, tok);
 }
 
 }  // namespace hq

@@ -323,6 +323,24 @@ def test_layer_narrow_dx_fallback(N, C, D, monkeypatch):
             assert err <= 1e-5, (name, err)
 
 
+@pytest.mark.parametrize("spin", ["0", "40000"])
+def test_layer_single_pass_x(spin, monkeypatch):
+    """X under HALO-2 in one launch over a grid barrier (one half-tile item per workgroup).
+    With no polling every workgroup but the last gives up, leaves its codes unwritten, and the
+    quantize pass launched after it recomputes them from the published partials; with the
+    default bound the single pass writes them. Forced from the host through HQ_SINGLE_SPIN;
+    every kernel ends normally either way."""
+    monkeypatch.setenv("HQ_SINGLE_SPIN", spin)
+    for rep in range(2):
+        cfg = WL.config(2, N=512, C=768, D=512)
+        banner("single-pass-x", spin, rep)
+        inputs = WL.make_inputs(cfg)
+        res = run_gpu(cfg, inputs)
+        h = host(res, cfg["out_dtype"])
+        ora = run_oracle(cfg, inputs)
+        compare_layer(cfg, h, ora, cfg["out_dtype"])
+
+
 def test_layer_deterministic():
     cfg = WL.config(2, N=512, C=512, D=512)
     inputs = WL.make_inputs(cfg)
