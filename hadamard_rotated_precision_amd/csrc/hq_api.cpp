@@ -73,18 +73,27 @@ struct Ws {
   }
 };
 
-hq_status device_ok() {
+// Properties of the device current at the first call, read once.
+struct DeviceInfo {
+  hq_status st = HQ_ERR_DEVICE;
+  int cus = 0;   // compute units visible to this process
+};
+
+const DeviceInfo& device_info() {
   static std::once_flag once;
-  static hq_status st = HQ_ERR_DEVICE;
+  static DeviceInfo info;
   std::call_once(once, [] {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return;
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return;
-    if (strncmp(prop.gcnArchName, "gfx950", 6) == 0) st = HQ_OK;
+    if (strncmp(prop.gcnArchName, "gfx950", 6) == 0) info.st = HQ_OK;
+    info.cus = prop.multiProcessorCount;
   });
-  return st;
+  return info;
 }
+
+hq_status device_ok() { return device_info().st; }
 
 #define HQ_TRY(expr)                                  \
   do {                                                \
@@ -326,7 +335,7 @@ hq_status hq_linear_fwd(const void* x, const void* w, int32_t in_dtype, int64_t 
   bool single = false;
   if (two_sided && !stepm && N * C > 0) {
     px = x_both_pass(x, in_dtype, N, C, k, cfg->bits, nullptr, nullptr, save_x, save_xt, wsp);
-    single = hq::pro_single_ok(px) && D * C > 0;
+    single = hq::pro_single_ok(px, device_info().cus) && D * C > 0;
   }
   HQ_CHECK(quantize_tensor(w, in_dtype, D, C, rx, k, cfg->bits, stepm ? step_w : nullptr,
                            save_w->codes, save_w->ld, save_w->codes_t, save_w->ld_t,

@@ -9,25 +9,28 @@
 // c[m][n] = sum_k a[m][k] * b[n][k];  a: M x K, b: N x K, int8, K-contiguous.
 //
 // Main loop (CDNA4):
-//   - workgroup tile 256 x BN (BN = 256 or 128) from waves of 128 x 64 in a 2 x (BN/64) grid
-//     (8 or 4 wave64s), each built from 2 x 4 v_mfma_i32_32x32x32_i8 tiles with 128 int32
-//     accumulators in AGPRs, so two waves share each SIMD and one wave's LDS and memory waits
-//     are covered by the other's MFMAs;
-//   - K advances 64 bytes per step through three LDS buffers with one barrier per step; global
-//     loads run three steps ahead through two register stages, and the first fragments of the
-//     next step are read before the barrier, so the matrix pipe keeps busy across it;
-//   - LDS rows are 64 bytes; the 16-byte chunk index is XOR-swizzled with (row / 4) % 4 so the
-//     128-bit fragment reads of 16 consecutive rows touch 16 distinct bank groups;
+//   - workgroup tile 256 x BN (BN = 256 or 128) from eight wave64s of 128 x BN/4 in a 2 x 4
+//     grid, two waves per SIMD; a wave holds 4 x BN/128 v_mfma_i32_32x32x32_i8 tiles (128 or 64
+//     int32 accumulators in AGPRs), so one wave's LDS and memory waits are covered by the other
+//     wave's MFMAs;
+//   - K advances 128 bytes per step. Operands go from memory straight into LDS (buffer loads
+//     with the lds bit): two 64 KB stages for 256-wide tiles (loads one step ahead), three
+//     48 KB stages for 128-wide ones (two steps ahead). One barrier per step; the first
+//     fragments of the next step are read right after it, before the current step's last
+//     MFMAs, so the matrix pipe keeps busy across it;
+//   - LDS rows are 128 bytes; the 16-byte chunk index is XOR-swizzled with (row / 2) % 8 so the
+//     128-bit fragment reads of 16 consecutive rows cover the 64 banks once;
 //   - workgroups are remapped so consecutive tiles land on one XCD (blocks are dispatched
 //     round-robin over the 8 XCDs) and a group of tiles shares A rows in that XCD's L2.
 //
-// Epilogue (EPI_OUT): acc -> fp32, then
+// Epilogue (EPI_SCALE): acc -> fp32, then
 //   - rotation along M (rows) in registers: in the 32x32 accumulator layout a lane holds 16 rows
 //     of each of its 4 row blocks, so row bits 0,1,3,4 (register index) and 5,6 (block index) are
 //     in-lane butterflies, bit 2 is the lane half (v_permlane32_swap), bit 7 is the wave row
 //     (done in the LDS phase below);
-//   - the tile is staged through LDS 64 rows at a time (rows x and x+128 of the tile together,
-//     so the bit-7 butterfly is local), where the column rotation (along N) and the cast to the
+//   - the tile is staged through LDS in rounds that hold the same rows of both wave rows (rows
+//     x and x+128 of the tile together, so the bit-7 butterfly is local): four rounds of 2 x 32
+//     rows, two of 2 x 64 in TRANS mode. There the column rotation (along N) and the cast to the
 //     output dtype happen in a row-contiguous thread layout, and stores are coalesced; TRANS
 //     mode stores the transpose (the caller computes the transposed product when only the
 //     rows need rotating, which keeps that rotation in registers).

@@ -75,13 +75,14 @@ struct ProPass {
 };
 int pro_grid(const ProPass& p);
 hipError_t pro_pass(const ProPass& p, int op, hipStream_t st);
-// Single-pass two-sided quantization (PRO_BOTH, ABSMAX mode, at most 256 half-tile items):
-// pro_single_pass does both passes in one launch over a grid barrier in `bar` (kBarWordsInts
+// Single-pass two-sided quantization (PRO_BOTH, ABSMAX mode, at most 256 half-tile items and
+// no more than the device's `cus` compute units, since each item's workgroup takes a whole
+// CU and all of them must be resident at once): pro_single_pass does both passes in one launch over a grid barrier in `bar` (kBarWordsInts
 // ints, zeroed by an earlier launch on the stream); pro_fixup_pass, launched right after,
 // recomputes the codes only if the single pass gave up waiting, and otherwise returns at once.
 // The partials go to p.partials (2 x items floats); p.nparts must be pro_grid(p) (= items).
 constexpr int kBarWordsInts = 512;
-bool pro_single_ok(const ProPass& p);
+bool pro_single_ok(const ProPass& p, int cus);
 hipError_t pro_single_pass(const ProPass& p, int32_t* bar, hipStream_t st);
 hipError_t pro_fixup_pass(const ProPass& p, int32_t* bar, hipStream_t st);
 

@@ -1836,10 +1836,10 @@ hipError_t pro_pass(const ProPass& p, int op, hipStream_t st) {
   return e;
 }
 
-bool pro_single_ok(const ProPass& p) {
+bool pro_single_ok(const ProPass& p, int cus) {
   const ProArgs a = pro_args(p);
   return p.kind == PRO_BOTH && p.step == nullptr && both_mma_ok(p.rows, p.cols, a.vec, dtb(p.in_dt), p.k) &&
-         both_items(p.rows, p.cols) <= 256;
+         both_items(p.rows, p.cols) <= std::min(256, cus);
 }
 
 hipError_t pro_single_pass(const ProPass& p, int32_t* bar, hipStream_t st) {
