@@ -110,6 +110,37 @@ def bf16_baseline(cfg, steps, warmup, library):
     return s.elapsed_time(e) / steps
 
 
+def fwht_bandwidth(reps=20, rows=8192, cols=13824, k=128):
+    """hq_fwht on its own (bf16 in, bf16 out), RIGHT and LEFT, on the largest operand shape of
+    the workloads (X of the 8192 x 13824 x 5120 layer, k = 128): algorithmic bytes = 2 B read
+    + 2 B written per element, over the mean launch time (events on the launch stream)."""
+    import torch
+    from hadamard_rotated_precision_amd import binding as B
+    from hadamard_rotated_precision_amd import tensors as T
+    src = torch.randn((rows, cols), dtype=torch.float32, device="cuda").to(torch.bfloat16)
+    dst = torch.empty_like(src)
+    res = {"shape": "%dx%d bf16 -> bf16" % (rows, cols), "k": k,
+           "bytes_per_launch": 4 * rows * cols}
+    for name, rot in (("right", B.HQ_ROT_RIGHT), ("left", B.HQ_ROT_LEFT)):
+        def run():
+            B.check(B.hq_fwht(src.data_ptr(), B.HQ_BF16, dst.data_ptr(), B.HQ_BF16, rows, cols,
+                              rot, k, T.stream_ptr()), "fwht")
+        for _ in range(3):
+            run()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        gbs = 4.0 * rows * cols / (us * 1e-6) / 1e9
+        res[name] = {"us": round(us, 2), "gbps": round(gbs, 1),
+                     "pct_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 1)}
+    return res
+
+
 def layer_vs_bf16(cfg_id, steps, warmup):
     """The HQ-MM step of another workload (inputs resident, no instrumentation) next to the
     three unrotated bf16 GEMMs of the same shapes: the comparison the target names for the
@@ -166,6 +197,8 @@ def main():
     ap.add_argument("--check-config", type=int, default=4,
                     help="also time this workload's step against three bf16 GEMMs (default 4: "
                          "the Llama-7B-shaped MLP layer); 0 to skip")
+    ap.add_argument("--no-fwht", action="store_true",
+                    help="skip the standalone hq_fwht bandwidth figure")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="before the steps, copy a buffer of this many MiB three times with a "
                          "plain device copy (reference dispatches for HBM byte counters)")
@@ -334,6 +367,12 @@ def main():
                                                     max(2, args.warmup // 2))
         except Exception as exc:  # report, do not fail the benchmark line
             result["layer_vs_bf16"] = {"error": str(exc)}
+    if not args.no_fwht:
+        print("[bench] hq_fwht bandwidth", file=sys.stderr, flush=True)
+        try:
+            result["fwht"] = fwht_bandwidth()
+        except Exception as exc:  # report, do not fail the benchmark line
+            result["fwht"] = {"error": str(exc)}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(args.config, args.cpu_sample_tokens)

@@ -517,7 +517,6 @@ hq_status hq_fwht(const void* src, int32_t src_dtype, void* dst, int32_t dst_dty
     c.rows = rows;
     c.cols = cols;
     c.k = k;
-    c.op = hq::OP_STORE;
     c.dst = dst;
     c.out_dt = dst_dtype;
     HQ_TRY(hq::cols_pass(c, st));
@@ -529,7 +528,6 @@ hq_status hq_fwht(const void* src, int32_t src_dtype, void* dst, int32_t dst_dty
   r.rows = rows;
   r.cols = cols;
   r.k = (rot == HQ_ROT_RIGHT) ? k : 1;
-  r.op = hq::OP_STORE;
   r.dst = dst;
   r.out_dt = dst_dtype;
   HQ_TRY(hq::rows_pass(r, st));

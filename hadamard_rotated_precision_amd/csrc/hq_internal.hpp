@@ -7,46 +7,28 @@
 
 namespace hq {
 
-enum Op : int { OP_ABSMAX = 0, OP_QUANT = 1, OP_STORE = 2 };
+enum Op : int { OP_ABSMAX = 0, OP_QUANT = 1 };
 
 // Most partial maxima one absmax pass writes (its grid is capped to this).
 constexpr int kMaxPartials = 1024;
 
-// One pass of the row-axis (RIGHT / NONE) transform over a rows x cols matrix.
+// The standalone transform (hq_rotate.hip): rotate a rows x cols matrix along the contiguous
+// axis (rows_pass; k = 1 copies with a dtype conversion) or along the row axis in k-row blocks
+// (cols_pass), writing the rotated values in out_dt.
 struct RowPass {
   const void* src = nullptr;
   int in_dt = 0;
   int64_t rows = 0, cols = 0;
   int k = 1;            // 1 = no rotation
-  int op = OP_ABSMAX;
-  float* partials = nullptr;        // ABSMAX out
-  const float* part_in = nullptr;   // QUANT in
-  int nparts = 0;
-  const float* step = nullptr;      // QUANT, STEP mode
-  int qp = 127;
-  float* scale_out = nullptr;
-  int8_t* codes = nullptr;          // QUANT out, pitch ld
-  int64_t ld = 0;
-  void* dst = nullptr;              // STORE out
+  void* dst = nullptr;
   int out_dt = 0;
 };
 
-// One pass of the row-axis-mixing (LEFT, token-axis) transform; QUANT writes the codes
-// transposed (cols x rows, pitch ld_t).
 struct ColPass {
   const void* src = nullptr;
   int in_dt = 0;
-  int64_t rows = 0, cols = 0;
+  int64_t rows = 0, cols = 0;   // rows % k == 0
   int k = 2;
-  int op = OP_ABSMAX;
-  float* partials = nullptr;
-  const float* part_in = nullptr;
-  int nparts = 0;
-  const float* step = nullptr;
-  int qp = 127;
-  float* scale_out = nullptr;
-  int8_t* codes_t = nullptr;
-  int64_t ld_t = 0;
   void* dst = nullptr;
   int out_dt = 0;
 };
@@ -87,14 +69,8 @@ hipError_t pro_single_pass(const ProPass& p, int32_t* bar, hipStream_t st);
 hipError_t pro_fixup_pass(const ProPass& p, int32_t* bar, hipStream_t st);
 
 hipError_t rows_pass(const RowPass& p, hipStream_t st);
-int rows_pass_grid(const RowPass& p);   // grid (= partial count) of the ABSMAX pass
 hipError_t cols_pass(const ColPass& p, hipStream_t st);
-int cols_pass_grid(const ColPass& p);
-hipError_t transpose_i8(const int8_t* src, int64_t ld_src, int8_t* dst, int64_t ld_dst,
-                        int64_t rows, int64_t cols, hipStream_t st);
 hipError_t write_scale(float* scale, const float* step, hipStream_t st);
-hipError_t zero_pad(int8_t* p, int64_t nrows, int64_t ld, int64_t from, int64_t to,
-                    hipStream_t st);
 
 // Integer GEMM c = a * b^T (a: M x K, b: N x K, int8, K-contiguous) with int32 accumulation.
 enum Epi : int { EPI_I32 = 0, EPI_SCALE = 1 };

@@ -81,6 +81,31 @@ def test_fwht_exact_on_small_integers(k, rot, dt):
     np.testing.assert_array_equal(dst.cpu().numpy().astype(np.float64), ref)
 
 
+@pytest.mark.parametrize("k", [4, 16, 64, 256])
+@pytest.mark.parametrize("rot", [B.HQ_ROT_RIGHT, B.HQ_ROT_LEFT])
+@pytest.mark.parametrize("dt", [B.HQ_BF16, B.HQ_F16])
+@pytest.mark.parametrize("ragged", [False, True])
+def test_fwht_16bit_output_exact(k, rot, dt, ragged):
+    """16-bit outputs, whole aligned runs (vector stores) and partial or unaligned ones (element
+    stores: rows of 8 columns at k = 4, rows of 197 columns): with small-integer inputs the fp32 sums are exact, so each output must be the exact rotation
+    rounded once to the dtype (nearest even), bit for bit. At k = 256 the bf16 rounding is
+    active (sums up to 2048 need 12 bits)."""
+    banner("fwht16", k, rot, dt, ragged)
+    rng = np.random.default_rng(7 * k + rot + 31 * dt + 5 * ragged)
+    if rot == B.HQ_ROT_RIGHT:
+        rows, cols = (37 if ragged else 64), 2 * k
+    else:
+        rows, cols = 2 * k, (3 * 64 + 5 if ragged else 3 * 64)
+    V = rng.integers(-8, 9, size=(rows, cols)).astype(np.float64)
+    src = torch.from_numpy(V.astype(np.float32)).to(DEV)
+    dst = torch.empty((rows, cols), dtype=T.TORCH_DT[dt], device=DEV)
+    B.check(B.hq_fwht(src.data_ptr(), B.HQ_F32, dst.data_ptr(), dt, rows, cols, rot, k,
+                      T.stream_ptr()), "fwht")
+    torch.cuda.synchronize()
+    expect = WL.to_dtype_bits(O.rotate(V, rot, k), dt)
+    np.testing.assert_array_equal(T.bits_of(dst), expect)
+
+
 def test_fwht_output_dtypes():
     rng = np.random.default_rng(3)
     V = rng.standard_normal((64, 256)).astype(np.float32)
