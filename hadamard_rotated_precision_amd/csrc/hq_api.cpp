@@ -510,6 +510,11 @@ hq_status hq_fwht(const void* src, int32_t src_dtype, void* dst, int32_t dst_dty
   if (rows * cols == 0) return HQ_OK;
   HQ_CHECK(device_ok());
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (rot == HQ_ROT_LEFT && k > 1 &&
+      hq::fwht_left_mma_ok(src, src_dtype, dst, dst_dtype, rows, cols, k)) {
+    HQ_TRY(hq::fwht_left_mma(src, src_dtype, rows, cols, k, dst, st));
+    return HQ_OK;
+  }
   if (rot == HQ_ROT_LEFT && k > 1) {
     ColPass c;
     c.src = src;

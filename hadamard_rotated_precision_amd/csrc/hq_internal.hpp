@@ -7,7 +7,8 @@
 
 namespace hq {
 
-enum Op : int { OP_ABSMAX = 0, OP_QUANT = 1 };
+// OP_STORE: the transform alone, rotated values written in the input dtype (hq_fwht).
+enum Op : int { OP_ABSMAX = 0, OP_QUANT = 1, OP_STORE = 2 };
 
 // Most partial maxima one absmax pass writes (its grid is capped to this).
 constexpr int kMaxPartials = 1024;
@@ -68,6 +69,12 @@ bool pro_single_ok(const ProPass& p, int cus);
 hipError_t pro_single_pass(const ProPass& p, int32_t* bar, hipStream_t st);
 hipError_t pro_fixup_pass(const ProPass& p, int32_t* bar, hipStream_t st);
 
+// hq_fwht's token-axis (LEFT) transform on the matrix cores, 16-bit in = out dtype: when
+// fwht_left_mma_ok, one launch of the left prologue kernel in OP_STORE mode.
+bool fwht_left_mma_ok(const void* src, int dt, const void* dst, int out_dt, int64_t rows,
+                      int64_t cols, int k);
+hipError_t fwht_left_mma(const void* src, int dt, int64_t rows, int64_t cols, int k, void* dst,
+                         hipStream_t st);
 hipError_t rows_pass(const RowPass& p, hipStream_t st);
 hipError_t cols_pass(const ColPass& p, hipStream_t st);
 hipError_t write_scale(float* scale, const float* step, hipStream_t st);

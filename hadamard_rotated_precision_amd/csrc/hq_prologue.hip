@@ -84,6 +84,7 @@ struct ProArgs {
   int32_t* bar;             // both_single_kernel: barrier words (zeroed by the launch before);
                             // a QUANT pass given bar runs only if the single pass aborted
   int spin;                 // both_single_kernel: polls of the barrier before giving up
+  void* dst;                // left_mma_kernel OP_STORE: rotated values, rows x cols, input dtype
 };
 
 // Barrier words of the single-pass two-sided kernel: arrival counters of eight workgroup groups
@@ -987,6 +988,44 @@ __global__ __launch_bounds__(LM_THREADS, 2) void left_mma_kernel(ProArgs a) {
         for (int mb = 0; mb < 16; ++mb)
 #pragma unroll
           for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(acc[mb][j]));
+      } else if constexpr (OP == OP_STORE) {
+        // The rotated tile in the input dtype goes back through the raw buffer (every wave has
+        // read its fragments once all pass the barrier), row-major with 128-byte rows. Lanes
+        // n0 and n0 ^ 1 hold columns c and c ^ 1 of rows 16mb + 4lg + [0, 4); after a DPP swap
+        // the even lane packs rows +0, +1 and the odd lane rows +3, +2 of the column pair, so
+        // one instruction's rows alternate in parity and, with the 16-byte chunk XOR-swizzled
+        // by 2 ((row / 4) % 4), its 64 dword writes meet 64 distinct banks.
+        __syncthreads();
+        uint32_t* const to = reinterpret_cast<uint32_t*>(tile);
+        const bool odd = (n0 & 1) != 0;
+        const int cp = 8 * w + (n0 >> 1);   // column pair (16w + n0) / 2
+#pragma unroll
+        for (int mb = 0; mb < 16; ++mb) {
+          float v[4], pv[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            v[j] = acc[mb][j];
+            pv[j] = quad_xor1(v[j]);
+          }
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const int row = 16 * mb + 4 * lg + (odd ? 3 - jj : jj);
+            const float lo = odd ? pv[3 - jj] : v[jj];
+            const float hi = odd ? v[3 - jj] : pv[jj];
+            to[row * 32 + 4 * ((cp >> 2) ^ (2 * ((row >> 2) & 3))) + (cp & 3)] = In::pack2(lo, hi);
+          }
+        }
+        __syncthreads();
+        const uint32_t tr = tl / nct;
+        const int64_t row0 = static_cast<int64_t>(tr) * LM_ROWS;
+        const int64_t col0 = static_cast<int64_t>(tl - tr * nct) * LM_COLS;
+        char* const dst = static_cast<char*>(a.dst);
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          const int idx = 256 * p + t, row = idx >> 3, q = idx & 7;
+          *reinterpret_cast<uint4*>(dst + ((row0 + row) * a.cols + col0 + 8 * q) * 2) =
+              tile[row * 8 + (q ^ (2 * ((row >> 2) & 3)))];
+        }
       } else {
         uint32_t d[16];   // rows 16mb + 4lg + [0, 4) of column 16w + n0
 #pragma unroll
@@ -1834,6 +1873,28 @@ hipError_t pro_pass(const ProPass& p, int op, hipStream_t st) {
     e = both_mma_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
   else e = both_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
   return e;
+}
+
+bool fwht_left_mma_ok(const void* src, int dt, const void* dst, int out_dt, int64_t rows,
+                      int64_t cols, int k) {
+  const bool al = (reinterpret_cast<uintptr_t>(src) & 15u) == 0 &&
+                  (reinterpret_cast<uintptr_t>(dst) & 15u) == 0;
+  return dt == out_dt && (dt == DT_F16 || dt == DT_BF16) && al &&
+         left_mma_ok(rows, cols, (cols * 2) % 16 == 0, 2, k);
+}
+
+hipError_t fwht_left_mma(const void* src, int dt, int64_t rows, int64_t cols, int k, void* dst,
+                         hipStream_t st) {
+  ProArgs a{};
+  a.src = src;
+  a.rows = rows;
+  a.cols = cols;
+  a.vec = true;
+  a.dst = dst;
+  const int grid = grid_cap((rows / LM_ROWS) * (cols / LM_COLS), LM_GRID);
+  const int tok = prof_open(K_ROT_STORE, 4.0 * static_cast<double>(rows) * cols);
+  return dt == DT_F16 ? left_mma_kernel_k<F16, OP_STORE>(k, a, grid, st, tok)
+                      : left_mma_kernel_k<BF16, OP_STORE>(k, a, grid, st, tok);
 }
 
 bool pro_single_ok(const ProPass& p, int cus) {
