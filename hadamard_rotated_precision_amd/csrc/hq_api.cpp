@@ -527,6 +527,11 @@ hq_status hq_fwht(const void* src, int32_t src_dtype, void* dst, int32_t dst_dty
     HQ_TRY(hq::cols_pass(c, st));
     return HQ_OK;
   }
+  if (rot == HQ_ROT_RIGHT && k > 1 &&
+      hq::fwht_right_mma_ok(src, src_dtype, dst, dst_dtype, rows, cols, k)) {
+    HQ_TRY(hq::fwht_right_mma(src, src_dtype, rows, cols, k, dst, st));
+    return HQ_OK;
+  }
   RowPass r;
   r.src = src;
   r.in_dt = src_dtype;

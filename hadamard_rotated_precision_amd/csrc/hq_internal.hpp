@@ -69,8 +69,12 @@ bool pro_single_ok(const ProPass& p, int cus);
 hipError_t pro_single_pass(const ProPass& p, int32_t* bar, hipStream_t st);
 hipError_t pro_fixup_pass(const ProPass& p, int32_t* bar, hipStream_t st);
 
-// hq_fwht's token-axis (LEFT) transform on the matrix cores, 16-bit in = out dtype: when
-// fwht_left_mma_ok, one launch of the left prologue kernel in OP_STORE mode.
+// hq_fwht on the matrix cores, 16-bit in = out dtype: when fwht_right_mma_ok /
+// fwht_left_mma_ok, one launch of the right / left prologue kernel in OP_STORE mode.
+bool fwht_right_mma_ok(const void* src, int dt, const void* dst, int out_dt, int64_t rows,
+                       int64_t cols, int k);
+hipError_t fwht_right_mma(const void* src, int dt, int64_t rows, int64_t cols, int k, void* dst,
+                          hipStream_t st);
 bool fwht_left_mma_ok(const void* src, int dt, const void* dst, int out_dt, int64_t rows,
                       int64_t cols, int k);
 hipError_t fwht_left_mma(const void* src, int dt, int64_t rows, int64_t cols, int k, void* dst,

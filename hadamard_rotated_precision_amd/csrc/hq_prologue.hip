@@ -84,7 +84,7 @@ struct ProArgs {
   int32_t* bar;             // both_single_kernel: barrier words (zeroed by the launch before);
                             // a QUANT pass given bar runs only if the single pass aborted
   int spin;                 // both_single_kernel: polls of the barrier before giving up
-  void* dst;                // left_mma_kernel OP_STORE: rotated values, rows x cols, input dtype
+  void* dst;                // right/left_mma_kernel OP_STORE: rotated values, rows x cols, input dtype
 };
 
 // Barrier words of the single-pass two-sided kernel: arrival counters of eight workgroup groups
@@ -567,6 +567,46 @@ __global__ __launch_bounds__(RM_THREADS, 2) void right_mma_kernel(ProArgs a) {
         for (int nb = 0; nb < 16; ++nb)
 #pragma unroll
           for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(acc[nb][j]));
+      } else if constexpr (OP == OP_STORE) {
+        // The rotated 64 x 256 tile in the input dtype goes through the two code buffers (rows
+        // 0-31 in tcode, 32-63 in rcode; 512-byte rows), as packed column pairs: lanes n0 and
+        // n0 ^ 1 hold columns c and c ^ 1 of rows 4lg + [0, 4); after a DPP swap the even lane
+        // packs rows +0, +1 and the odd lane rows +3, +2. With the 16-byte chunk XOR-swizzled
+        // by 4 ((row / 4) % 4) + 2 (row % 2), one instruction's 64 dword writes meet 64
+        // distinct banks.
+        const uint32_t tr = tl / nct;
+        const int64_t row0 = static_cast<int64_t>(tr) * RM_ROWS;
+        const int64_t col0 = static_cast<int64_t>(tl - tr * nct) * RM_COLS;
+        auto swz = [](int r) { return 4 * ((r >> 2) & 3) + 2 * (r & 1); };
+        __syncthreads();   // the previous tile's readers of the buffers are done
+        uint32_t* const half = (w >> 1) ? rcode : tcode;
+        const bool odd = (n0 & 1) != 0;
+#pragma unroll
+        for (int nb = 0; nb < 16; ++nb) {
+          float v[4], pv[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            v[j] = acc[nb][j];
+            pv[j] = quad_xor1(v[j]);
+          }
+          const int cp = 8 * nb + (n0 >> 1);   // column pair (16nb + n0) / 2
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const int rl = 16 * (w & 1) + 4 * lg + (odd ? 3 - jj : jj);
+            const float lo = odd ? pv[3 - jj] : v[jj];
+            const float hi = odd ? v[3 - jj] : pv[jj];
+            half[rl * 128 + 4 * ((cp >> 2) ^ swz(rl)) + (cp & 3)] = In::pack2(lo, hi);
+          }
+        }
+        __syncthreads();
+        char* const dst = static_cast<char*>(a.dst);
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          const int idx = 256 * p + t, row = idx >> 5, q = idx & 31, rl = row & 31;
+          const uint32_t* hb = (row >> 5) ? rcode : tcode;
+          *reinterpret_cast<uint4*>(dst + ((row0 + row) * a.cols + col0 + 8 * q) * 2) =
+              *reinterpret_cast<const uint4*>(&hb[rl * 128 + 4 * (q ^ swz(rl))]);
+        }
       } else {
         uint32_t d[16];   // rows 4lg + [0, 4) of column 16nb + n0
 #pragma unroll
@@ -1873,6 +1913,31 @@ hipError_t pro_pass(const ProPass& p, int op, hipStream_t st) {
     e = both_mma_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
   else e = both_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
   return e;
+}
+
+// Blocks of 128 and 256 only: for k <= 64 the VALU rows kernel streams as fast or faster
+// (it needs at most two lane-exchange stages there), measured on bf16 shapes from 2048 x 4096
+// to 8192 x 13824.
+bool fwht_right_mma_ok(const void* src, int dt, const void* dst, int out_dt, int64_t rows,
+                       int64_t cols, int k) {
+  const bool al = (reinterpret_cast<uintptr_t>(src) & 15u) == 0 &&
+                  (reinterpret_cast<uintptr_t>(dst) & 15u) == 0;
+  return k >= 128 && dt == out_dt && (dt == DT_F16 || dt == DT_BF16) && al &&
+         right_mma_ok(rows, cols, (cols * 2) % 16 == 0, 2, k);
+}
+
+hipError_t fwht_right_mma(const void* src, int dt, int64_t rows, int64_t cols, int k, void* dst,
+                          hipStream_t st) {
+  ProArgs a{};
+  a.src = src;
+  a.rows = rows;
+  a.cols = cols;
+  a.vec = true;
+  a.dst = dst;
+  const int grid = grid_cap((rows / RM_ROWS) * (cols / RM_COLS), RM_GRID);
+  const int tok = prof_open(K_ROT_STORE, 4.0 * static_cast<double>(rows) * cols);
+  return dt == DT_F16 ? right_mma_kernel_k<F16, OP_STORE>(k, a, grid, st, tok)
+                      : right_mma_kernel_k<BF16, OP_STORE>(k, a, grid, st, tok);
 }
 
 bool fwht_left_mma_ok(const void* src, int dt, const void* dst, int out_dt, int64_t rows,

@@ -108,45 +108,52 @@ def test_fwht_16bit_output_exact(k, rot, dt, ragged):
 
 @pytest.mark.parametrize("k", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("dt", [B.HQ_BF16, B.HQ_F16])
-def test_fwht_left_matrix_core_exact(k, dt):
-    """16-bit in = out, whole 256 x 64 tiles: the token-axis transform runs on the matrix cores
-    (exact +-1 products, fp32 sums) and goes back through LDS. Small integers keep the sums
-    exact, so every output is the exact rotation rounded once, bit for bit."""
-    banner("fwht-left-mma", k, dt)
-    rng = np.random.default_rng(11 * k + dt)
-    rows, cols = 512, 192
+@pytest.mark.parametrize("rot", [B.HQ_ROT_RIGHT, B.HQ_ROT_LEFT])
+def test_fwht_matrix_core_exact(rot, k, dt):
+    """16-bit in = out on whole tiles (64 x 256 RIGHT, 256 x 64 LEFT): the transform runs on the
+    matrix cores (exact +-1 products, fp32 sums; RIGHT only for k >= 128, the VALU kernel
+    otherwise) and goes back through LDS. Small integers keep the sums exact, so every output is
+    the exact rotation rounded once, bit for bit."""
+    banner("fwht-mma", rot, k, dt)
+    rng = np.random.default_rng(11 * k + dt + 3 * rot)
+    rows, cols = (128, 512) if rot == B.HQ_ROT_RIGHT else (512, 192)
     V = rng.integers(-8, 9, size=(rows, cols)).astype(np.float64)
     src = T.device_tensor_from_bits(WL.to_dtype_bits(V, dt), dt, DEV)
     dst = torch.full((rows, cols), 7.0, dtype=T.TORCH_DT[dt], device=DEV)
-    B.check(B.hq_fwht(src.data_ptr(), dt, dst.data_ptr(), dt, rows, cols, B.HQ_ROT_LEFT, k,
+    B.check(B.hq_fwht(src.data_ptr(), dt, dst.data_ptr(), dt, rows, cols, rot, k,
                       T.stream_ptr()), "fwht")
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(T.bits_of(dst), WL.to_dtype_bits(O.rotate(V, B.HQ_ROT_LEFT, k), dt))
+    np.testing.assert_array_equal(T.bits_of(dst), WL.to_dtype_bits(O.rotate(V, rot, k), dt))
 
 
 @pytest.mark.parametrize("dt", [B.HQ_BF16, B.HQ_F16])
-def test_fwht_left_matrix_core_random(dt):
-    """Normal inputs on the matrix-core token-axis transform (k = 128, several tiles per
-    workgroup): within the 16-bit rounding of the exact rotation."""
-    rng = np.random.default_rng(5 + dt)
-    rows, cols = 2048, 4096
+@pytest.mark.parametrize("rot", [B.HQ_ROT_RIGHT, B.HQ_ROT_LEFT])
+def test_fwht_matrix_core_random(rot, dt):
+    """Normal inputs on the matrix-core transforms (k = 128, several tiles per workgroup):
+    within the 16-bit rounding of the exact rotation."""
+    banner("fwht-mma-random", rot, dt)
+    rng = np.random.default_rng(5 + dt + 7 * rot)
+    rows, cols, k = 2048, 4096, 128
     V = rng.standard_normal((rows, cols))
     bits = WL.to_dtype_bits(V, dt)
     src = T.device_tensor_from_bits(bits, dt, DEV)
     dst = torch.empty((rows, cols), dtype=T.TORCH_DT[dt], device=DEV)
-    B.check(B.hq_fwht(src.data_ptr(), dt, dst.data_ptr(), dt, rows, cols, B.HQ_ROT_LEFT, 128,
+    B.check(B.hq_fwht(src.data_ptr(), dt, dst.data_ptr(), dt, rows, cols, rot, k,
                       T.stream_ptr()), "fwht")
     torch.cuda.synchronize()
-    ref = O.rotate(O.decode(bits, dt), B.HQ_ROT_LEFT, 128)
+    ref = O.rotate(O.decode(bits, dt), rot, k)
     got = O.decode(T.bits_of(dst), dt)
     assert rel_fro(got, rounded(ref, dt)) < 1e-4
     # per element: one ulp of the dtype (the final rounding) plus the fp32 summation error of
-    # the 128 terms, bounded by 2^-20 of the block's sum of |input| (this matters where the
+    # the k terms, bounded by 2^-20 of the block's sum of |input| (this matters where the
     # terms cancel)
     mant, emin = (7, -126) if dt == B.HQ_BF16 else (10, -14)
     e = np.maximum(np.floor(np.log2(np.maximum(np.abs(ref), 1e-300))), emin)
-    absum = np.repeat(np.abs(O.decode(bits, dt)).reshape(rows // 128, 128, cols).sum(axis=1),
-                      128, axis=0)
+    a = np.abs(O.decode(bits, dt))
+    if rot == B.HQ_ROT_LEFT:
+        absum = np.repeat(a.reshape(rows // k, k, cols).sum(axis=1), k, axis=0)
+    else:
+        absum = np.repeat(a.reshape(rows, cols // k, k).sum(axis=2), k, axis=1)
     assert np.all(np.abs(got - ref) <= 2.0 ** (e - mant) + 2.0 ** -20 * absum)
 
 
