@@ -186,7 +186,12 @@ hq_status hq_linear_bwd_weight(const hq_qtensor *saved_g, const hq_qtensor *save
 
 /* Standalone block-diagonal Walsh-Hadamard transform (unnormalized): dst = rotation of src
  * (INT4 page §3.3). rows x cols row-major; rotated dims divisible by k; rot != BOTH
- * for this entry point; src and dst must not overlap. */
+ * for this entry point; src and dst must not overlap. Sums are formed in fp32 and rounded once
+ * to dst_dtype (nearest even): exact whenever the fp32 sums are, else within the fp32
+ * summation error of that. With 16-bit src_dtype == dst_dtype, 16-byte aligned pointers and
+ * whole tiles (RIGHT: rows % 64 == 0, cols % 256 == 0, k >= 128; LEFT: rows % 256 == 0,
+ * cols % 64 == 0, k >= 16) the sums run on the matrix cores, in another order than the VALU
+ * butterflies of the other cases. */
 hq_status hq_fwht(const void *src, int32_t src_dtype, void *dst, int32_t dst_dtype,
                   int64_t rows, int64_t cols, int32_t rot, int32_t k, void *stream);
 
