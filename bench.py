@@ -303,13 +303,26 @@ def main():
     pro_ms_step = pro_ms / args.steps
     rq_gbs = pro_bytes / (pro_ms_step * 1e-3) / 1e9 if pro_ms_step > 0 else None
 
+    # counted bytes (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated) from profiles/, used only
+    # while the sources they were taken from are unchanged
     traffic = None
+    rq_counted = None
     if os.path.exists(TRAFFIC_FILE):
+        from hadamard_rotated_precision_amd.prof_summary import prologue_source_hash
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        if tr.get("gemm_source_sha256_16") == gemm_source_hash() and \
-                tr.get("workload") == cfg["name"]:
-            traffic = tr.get("bytes_per_launch")
+        if tr.get("workload") == cfg["name"]:
+            if tr.get("gemm_source_sha256_16") == gemm_source_hash():
+                traffic = tr.get("bytes_per_launch")
+            pb = tr.get("prologue_bytes_per_step")
+            if pb and pro_ms_step > 0 and \
+                    tr.get("prologue_source_sha256_16") == prologue_source_hash():
+                gbs = pb / (pro_ms_step * 1e-3) / 1e9
+                rq_counted = {"bytes_per_step": pb, "gbps": round(gbs, 1),
+                              "pct_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 1),
+                              "source": "rocprofv3 FETCH_SIZE + WRITE_SIZE of every prologue "
+                                        "dispatch, calibrated on a 1 GiB device copy "
+                                        "(profiles/gemm_hbm_traffic.json)"}
 
     result = {
         "metric": "HQ-MM fwd+bwd effective TOPS and % of INT8 MFMA peak; rotate+quant GB/s",
@@ -332,6 +345,7 @@ def main():
         "gemm_tops": None if gemm_tops is None else round(gemm_tops, 1),
         "rotate_quant_gbps": None if rq_gbs is None else round(rq_gbs, 1),
         "rotate_quant_pct_hbm": None if rq_gbs is None else round(100 * rq_gbs / PEAK_HBM_GBS, 1),
+        "rotate_quant_counted": rq_counted,
         "roofline": {
             "kernel": "gemm_i8_kernel (int8 MFMA GEMM + dequant epilogue)",
             "bound": "mfma",

@@ -5,8 +5,8 @@
 
   python -m hadamard_rotated_precision_amd.prof_summary traffic FETCH_DIR WRITE_DIR \
       --copy-bytes B --workload NAME --json OUT.json --md OUT.md --cmd "..."
-      HBM bytes per GEMM launch from two --pmc runs (FETCH_SIZE, then WRITE_SIZE, KiB per
-      dispatch). Each counter is scaled by what it reads for the plain device copies of B
+      HBM bytes per GEMM launch, and of the prologue kernels per step, from two --pmc runs
+      (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch). Each counter is scaled by what it reads for the plain device copies of B
       bytes the same run made (read B, write B), so the figure is in bytes of the copy's
       own accounting.
 """
@@ -21,6 +21,23 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 GEMM_SOURCE = os.path.join(HERE, "csrc", "hq_gemm.hip")
+# the rotate -> quantize prologue: its kernels and the host code that picks them
+PROLOGUE_SOURCES = [os.path.join(HERE, "csrc", f) for f in ("hq_prologue.hip", "hq_api.cpp")]
+PROLOGUE_KERNELS = ("right_mma_kernel", "left_mma_kernel", "both_mma_kernel", "both_pipe_kernel",
+                    "both_single_kernel", "right_fast_kernel", "right_kernel", "left_fast_kernel",
+                    "left_kernel", "both_kernel")
+
+
+def prologue_source_hash():
+    h = hashlib.sha256()
+    for path in PROLOGUE_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _is_prologue(key):
+    return key.split("<")[0] in PROLOGUE_KERNELS
 
 
 def _one(pattern):
@@ -98,11 +115,19 @@ def cmd_traffic(args):
         raise SystemExit("no GEMM dispatches found")
     fpl = sum(gemm_f) / len(gemm_f)
     wpl = sum(gemm_w) / len(gemm_w)
+    # prologue bytes per step: every prologue dispatch of the run over the number of steps
+    steps = len(gemm_f) / args.gemms_per_step
+    pro_f = sum(v for k, vs in kf.items() if _is_prologue(k) for v in vs) / steps
+    pro_w = sum(v for k, vs in kw.items() if _is_prologue(k) for v in vs) / steps
     with open(GEMM_SOURCE, "rb") as f:
         src_hash = hashlib.sha256(f.read()).hexdigest()[:16]
     doc = {"workload": args.workload, "gemm_source_sha256_16": src_hash,
            "bytes_per_launch": round(fpl + wpl), "fetch_bytes_per_launch": round(fpl),
            "write_bytes_per_launch": round(wpl), "gemm_launches_counted": len(gemm_f),
+           "prologue_source_sha256_16": prologue_source_hash(),
+           "prologue_bytes_per_step": round(pro_f + pro_w),
+           "prologue_fetch_bytes_per_step": round(pro_f),
+           "prologue_write_bytes_per_step": round(pro_w),
            "calibration": {"copy_bytes": args.copy_bytes,
                            "fetch_kib_per_copy": sum(cf) / len(cf),
                            "write_kib_per_copy": sum(cw) / len(cw),
@@ -120,7 +145,10 @@ def cmd_traffic(args):
         w = kw.get(k, [0.0])
         out.append("| `%s` | %d | %.2f | %.2f |" % (k, len(f), sum(f) / len(f) / 1e6, sum(w) / len(w) / 1e6))
     out += ["", "GEMM average per launch: read %.2f MB, written %.2f MB, total %.2f MB "
-            "(source hash %s)." % (fpl / 1e6, wpl / 1e6, (fpl + wpl) / 1e6, src_hash)]
+            "(source hash %s)." % (fpl / 1e6, wpl / 1e6, (fpl + wpl) / 1e6, src_hash),
+            "", "Prologue (rotate -> quantize kernels) per step: read %.2f MB, written %.2f MB, "
+            "total %.2f MB (source hash %s)." % (pro_f / 1e6, pro_w / 1e6, (pro_f + pro_w) / 1e6,
+                                                 prologue_source_hash())]
     open(args.md, "w").write("\n".join(out) + "\n")
     print("\n".join(out))
 
@@ -141,6 +169,8 @@ def main(argv=None):
     t.add_argument("--json", required=True)
     t.add_argument("--md", required=True)
     t.add_argument("--cmd", required=True)
+    t.add_argument("--gemms-per-step", type=int, default=3,
+                   help="GEMM launches per step of the workload (fwd + dX + dW = 3)")
     args = ap.parse_args(argv)
     if args.what == "stats":
         cmd_stats(args)
