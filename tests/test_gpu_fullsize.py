@@ -96,3 +96,34 @@ def test_fullsize_sampled(cid):
         err = rel_fro(got, rounded(ref, out_dt))
         print("dW block", r0, c0, "rel fro", err, flush=True)
         assert err <= 1e-3
+
+
+@pytest.mark.parametrize("rot", [1, 2])
+def test_fwht_fullsize_sampled(rot):
+    """hq_fwht at the size bench.py measures (8192 x 13824 bf16 -> bf16, k = 128, the X operand
+    of the largest workload), on small-integer inputs so that every output is the exact
+    rotation rounded once: sampled rows (RIGHT rotates within rows) or sampled k-row blocks on
+    sampled column windows (LEFT mixes only within a block), bit for bit."""
+    import torch
+    from hadamard_rotated_precision_amd import binding as B
+    rows, cols, k = 8192, 13824, 128
+    print("[case] fwht fullsize rot", rot, flush=True)
+    rng = np.random.default_rng(40 + rot)
+    V = rng.integers(-8, 9, size=(rows, cols)).astype(np.float32)
+    src = torch.from_numpy(V).to("cuda").to(torch.bfloat16)   # exact: |v| <= 8
+    dst = torch.empty_like(src)
+    B.check(B.hq_fwht(src.data_ptr(), B.HQ_BF16, dst.data_ptr(), B.HQ_BF16, rows, cols, rot, k,
+                      T.stream_ptr()), "fwht")
+    torch.cuda.synchronize()
+    if rot == 1:
+        for r in rng.choice(rows, 12, replace=False):
+            got = T.bits_of(dst[int(r):int(r) + 1])
+            ref = O.rotate(V[int(r):int(r) + 1].astype(np.float64), 1, k)
+            np.testing.assert_array_equal(got, WL.to_dtype_bits(ref, WL.BF16))
+    else:
+        for b in rng.choice(rows // k, 6, replace=False):
+            r0 = int(b) * k
+            c0 = int(rng.integers(0, cols - 512))
+            got = T.bits_of(dst[r0:r0 + k, c0:c0 + 512].contiguous())
+            ref = O.rotate(V[r0:r0 + k, c0:c0 + 512].astype(np.float64), 2, k)
+            np.testing.assert_array_equal(got, WL.to_dtype_bits(ref, WL.BF16))
