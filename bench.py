@@ -117,7 +117,9 @@ def fwht_bandwidth(reps=20, rows=8192, cols=13824, k=128):
     import torch
     from hadamard_rotated_precision_amd import binding as B
     from hadamard_rotated_precision_amd import tensors as T
-    src = torch.randn((rows, cols), dtype=torch.float32, device="cuda").to(torch.bfloat16)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(106)
+    src = torch.randn((rows, cols), dtype=torch.float32, device="cuda", generator=gen).to(torch.bfloat16)
     dst = torch.empty_like(src)
     res = {"shape": "%dx%d bf16 -> bf16" % (rows, cols), "k": k,
            "bytes_per_launch": 4 * rows * cols}
