@@ -362,6 +362,7 @@ hq_status hq_linear_fwd(const void* x, const void* w, int32_t in_dtype, int64_t 
   fill_meta(save_x, N, C, k, cfg->bits, rx);
   if (want_xt) fill_meta(save_xt, N, C, k, cfg->bits, HQ_ROT_BOTH);
   GemmPass g;
+  g.cus = device_info().cus;
   g.a = save_x->codes;
   g.lda = save_x->ld;
   g.b = save_w->codes;
@@ -410,6 +411,7 @@ hq_status hq_linear_bwd_input(const void* dy, int32_t dy_dtype, int64_t N, int64
   fill_meta(save_g, N, D, k, cfg->bits, rg);
   // dX = [B_N] (qG qW) [B_C] sG sW / k^e, dequantized and inverse-rotated in the GEMM epilogue.
   GemmPass g;
+  g.cus = device_info().cus;
   g.epi = hq::EPI_SCALE;
   g.sa = save_g->scale;
   g.sb = saved_w->scale;
@@ -469,6 +471,7 @@ hq_status hq_linear_bwd_weight(const hq_qtensor* saved_g, const hq_qtensor* save
   // dW = (qG^T qX') [B_C] sG sX' / k^e. When C rotates, compute dW^T = qX'^T qG so C is the
   // tile's row axis (rotated in registers) and store it transposed.
   GemmPass g;
+  g.cus = device_info().cus;
   g.epi = hq::EPI_SCALE;
   g.sa = saved_g->scale;
   g.sb = saved_x->scale;
@@ -553,6 +556,7 @@ hq_status hq_gemm_i8_i32(const int8_t* a, int64_t lda, const int8_t* b_t, int64_
   if (M * N == 0) return HQ_OK;
   HQ_CHECK(device_ok());
   GemmPass g;
+  g.cus = device_info().cus;
   g.a = a;
   g.lda = lda;
   g.b = b_t;

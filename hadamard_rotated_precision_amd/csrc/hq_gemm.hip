@@ -184,8 +184,10 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs 
   const int tiles_m = static_cast<int>((g.M + GBM - 1) / GBM);
   const int tiles_n = static_cast<int>((g.N + BN - 1) / BN);
   const int ntiles = tiles_m * tiles_n;
-  int pid = blockIdx.x;
-  if ((ntiles & 7) == 0) pid = (pid & 7) * (ntiles >> 3) + (pid >> 3);   // XCD-contiguous
+  // XCD-contiguous order: block b runs on XCD b % 8, which takes blocks x, x + 8, ... (q or
+  // q + 1 of them for ntiles = 8q + r); they get consecutive logical tiles from x q + min(x, r)
+  const int xcd = blockIdx.x & 7, q8 = ntiles >> 3, r8 = ntiles & 7;
+  const int pid = xcd * q8 + min(xcd, r8) + (blockIdx.x >> 3);
   const int group = pid / (kGroupM * tiles_n);
   const int first_m = group * kGroupM;
   const int gsize = min(tiles_m - first_m, kGroupM);
@@ -673,6 +675,25 @@ static bool use_narrow(int64_t M, int64_t N, int kn, bool trans_out) {
   return kn <= 128 || (kn == 256 && !trans_out && N % 256 == 0);
 }
 
+// 256-wide tile columns to run before a second launch of 128-wide tiles over the rest of N,
+// or tn for one launch. When the 256-wide grid leaves its last round of workgroups partly
+// filled, a tail of 128-wide tiles can fill whole rounds instead: a 256 x 128 tile takes about
+// 0.6 of a 256 x 256 tile's time at the same K (measured K-loop rates 2.6 and 3.1 POP/s), and
+// the extra launch about 0.05 of a round. The tail needs no tile pairs (kn <= 128).
+static int64_t wide_cols_before_tail(int64_t tm, int64_t tn, int cus) {
+  auto rounds = [cus](int64_t tiles) { return static_cast<double>((tiles + cus - 1) / cus); };
+  double best = rounds(tm * tn);
+  int64_t best_n1 = tn;
+  for (int64_t n1 = 1; n1 < tn; ++n1) {
+    const double c = rounds(tm * n1) + 0.6 * rounds(tm * 2 * (tn - n1)) + 0.05;
+    if (c < best - 1e-9) {
+      best = c;
+      best_n1 = n1;
+    }
+  }
+  return best_n1;
+}
+
 int64_t gemm_split_tiles(int64_t M, int64_t N, int64_t K, int epi, int km, int kn, bool trans_out) {
   (void)K;
   (void)km;
@@ -706,20 +727,39 @@ hipError_t gemm_pass(const GemmPass& p, hipStream_t st) {
   // a tile's rows must be addressable by 32-bit buffer offsets
   if (static_cast<int64_t>(GBM) * p.lda >= kOutOfRange || 256 * p.ldb >= kOutOfRange)
     return hipErrorInvalidValue;
-  const bool narrow = use_narrow(p.M, p.N, p.epi == EPI_I32 ? 1 : p.kn, p.trans_out);
-  const int tok = prof_open(K_GEMM, 2.0 * p.M * p.N * p.K);
-  hipError_t e = hipErrorInvalidValue;
-  if (p.epi == EPI_I32) {
-    e = narrow ? launch_gemm<128, F32, EPI_I32, 1, 1, false>(a, st, tok)
-               : launch_gemm<256, F32, EPI_I32, 1, 1, false>(a, st, tok);
-  } else {
+  const int kn = p.epi == EPI_I32 ? 1 : p.kn;
+  const bool narrow = use_narrow(p.M, p.N, kn, p.trans_out);
+  auto launch = [&](bool nar, const GemmArgs& g) {
+    const int tok = prof_open(K_GEMM, 2.0 * g.M * g.N * g.K);
+    if (p.epi == EPI_I32)
+      return nar ? launch_gemm<128, F32, EPI_I32, 1, 1, false>(g, st, tok)
+                 : launch_gemm<256, F32, EPI_I32, 1, 1, false>(g, st, tok);
     switch (p.out_dt) {
-      case DT_F32: e = narrow ? launch_out<128, F32>(p, a, st, tok) : launch_out<256, F32>(p, a, st, tok); break;
-      case DT_F16: e = narrow ? launch_out<128, F16>(p, a, st, tok) : launch_out<256, F16>(p, a, st, tok); break;
-      case DT_BF16: e = narrow ? launch_out<128, BF16>(p, a, st, tok) : launch_out<256, BF16>(p, a, st, tok); break;
+      case DT_F32: return nar ? launch_out<128, F32>(p, g, st, tok) : launch_out<256, F32>(p, g, st, tok);
+      case DT_F16: return nar ? launch_out<128, F16>(p, g, st, tok) : launch_out<256, F16>(p, g, st, tok);
+      case DT_BF16: return nar ? launch_out<128, BF16>(p, g, st, tok) : launch_out<256, BF16>(p, g, st, tok);
+    }
+    return hipErrorInvalidValue;
+  };
+  if (!narrow && kn <= 128) {
+    // 256-wide tiles over columns [0, N1), then 128-wide ones over [N1, N) when that fills the
+    // rounds better (N1 is a multiple of 256, so rotation blocks stay whole in each part)
+    const int64_t tm = (p.M + GBM - 1) / GBM, tn = (p.N + 255) / 256;
+    const int64_t n1 = wide_cols_before_tail(tm, tn, p.cus > 0 ? p.cus : 256) * 256;
+    if (n1 < p.N) {
+      const size_t esz = p.epi == EPI_I32 ? 4 : (p.out_dt == DT_F32 ? 4 : 2);
+      GemmArgs head = a, tail = a;
+      head.N = n1;
+      tail.N = p.N - n1;
+      tail.b = p.b + n1 * p.ldb;
+      // c is M x N (pitch ldc), or N x M when the transpose is stored
+      tail.c = static_cast<char*>(p.c) + static_cast<size_t>(p.trans_out ? n1 * p.ldc : n1) * esz;
+      const hipError_t e = launch(false, head);
+      if (e != hipSuccess) return e;
+      return launch(true, tail);
     }
   }
-  return e;
+  return launch(narrow, a);
 }
 
 }  // namespace hq

@@ -103,6 +103,7 @@ struct GemmPass {
   bool trans_out = false;  // EPI_SCALE: store c^T (N x M, pitch ldc); requires kn == 1
   void* split_ws = nullptr;       // tile-pair workspace (gemm_split_bytes) when pairing applies
   bool split_cnt_zeroed = false;  // its arrival flags were zeroed by an earlier launch on the stream
+  int cus = 0;             // compute units of the device (0: assume 256), for the tile rounds
 };
 hipError_t gemm_pass(const GemmPass& p, hipStream_t st);
 // Number of tile pairs of a GEMM whose 256-wide column rotation spans two 256 x 128 tiles

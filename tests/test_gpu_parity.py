@@ -44,6 +44,25 @@ def test_gemm_i8_i32_bitexact(M, N, K):
     np.testing.assert_array_equal(c.cpu().numpy().astype(np.int64), ref)
 
 
+@pytest.mark.parametrize("M,N,K", [(8192, 5120, 64), (4000, 5000, 48), (12288, 3072, 32)])
+def test_gemm_i8_i32_wide_then_narrow(M, N, K):
+    """Shapes whose 256 x 256 tile grid would leave the last round of workgroups partly filled:
+    256-wide tiles cover the leading columns and a second launch of 128-wide tiles the rest
+    (8192 x 5120: 4096 + 1024 columns; ragged rows and a ragged tail at 4000 x 5000). Every entry, bit for bit (the reference product is
+    exact in float64 at these magnitudes)."""
+    banner("gemm-tail", M, N, K)
+    rng = np.random.default_rng(M + N + K)
+    A = rng.integers(-128, 128, size=(M, K)).astype(np.int8)
+    Bt = rng.integers(-128, 128, size=(N, K)).astype(np.int8)
+    a, b = torch.from_numpy(A).to(DEV), torch.from_numpy(Bt).to(DEV)
+    c = torch.full((M, N), 12345, dtype=torch.int32, device=DEV)
+    B.check(B.hq_gemm_i8_i32(a.data_ptr(), K, b.data_ptr(), K, c.data_ptr(), M, N, K,
+                             T.stream_ptr()), "gemm")
+    torch.cuda.synchronize()
+    ref = A.astype(np.float64) @ Bt.astype(np.float64).T
+    np.testing.assert_array_equal(c.cpu().numpy().astype(np.float64), ref)
+
+
 def test_gemm_extremes_fit_int32():
     """All -128 / 127 operands at the largest contraction of the workloads (13824)."""
     K, M, N = 13824, 64, 64
