@@ -677,11 +677,15 @@ static bool use_narrow(int64_t M, int64_t N, int kn, bool trans_out) {
 
 // 256-wide tile columns to run before a second launch of 128-wide tiles over the rest of N,
 // or tn for one launch. When the 256-wide grid leaves its last round of workgroups partly
-// filled, a tail of 128-wide tiles can fill whole rounds instead: a 256 x 128 tile takes about
-// 0.6 of a 256 x 256 tile's time at the same K (measured K-loop rates 2.6 and 3.1 POP/s), and
-// the extra launch about 0.05 of a round. The tail needs no tile pairs (kn <= 128).
+// filled, a tail of 128-wide tiles can fill whole rounds instead. Estimated cost in rounds of
+// 256 x 256 tiles: a full round 1, a round filled to a fraction f about 0.6 + 0.4 f (fewer
+// workgroups share the memory system), a round of 256 x 128 tiles 0.6 of that (measured
+// K-loop rates 2.6 and 3.1 POP/s), the extra launch 0.05. The tail needs no tile pairs.
 static int64_t wide_cols_before_tail(int64_t tm, int64_t tn, int cus) {
-  auto rounds = [cus](int64_t tiles) { return static_cast<double>((tiles + cus - 1) / cus); };
+  auto rounds = [cus](int64_t tiles) {
+    const int64_t full = tiles / cus, rem = tiles % cus;
+    return static_cast<double>(full) + (rem ? 0.6 + 0.4 * static_cast<double>(rem) / cus : 0.0);
+  };
   double best = rounds(tm * tn);
   int64_t best_n1 = tn;
   for (int64_t n1 = 1; n1 < tn; ++n1) {
