@@ -201,6 +201,8 @@ def main():
                          "the Llama-7B-shaped MLP layer); 0 to skip")
     ap.add_argument("--no-fwht", action="store_true",
                     help="skip the standalone hq_fwht bandwidth figure")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache prologue pass (kernel traces of the warm step)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="before the steps, copy a buffer of this many MiB three times with a "
                          "plain device copy (reference dispatches for HBM byte counters)")
@@ -305,6 +307,29 @@ def main():
     pro_ms_step = pro_ms / args.steps
     rq_gbs = pro_bytes / (pro_ms_step * 1e-3) / 1e9 if pro_ms_step > 0 else None
 
+    # ---- the same with cold caches: before each step a 512 MB buffer is written, which evicts
+    # the inputs from L2 and the 256 MB MALL, so the prologue reads them from HBM
+    rq_cold = None
+    pro_cold_ms = 0.0
+    if not args.no_cold:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold_steps = max(5, min(args.steps, 20))
+        B.check(B.hq_profile_start((1 << B.HQ_KIND_ROT_ABSMAX) | (1 << B.HQ_KIND_ROT_QUANT)),
+                "profile")
+        for _ in range(cold_steps):
+            flush.fill_(1)
+            step()
+        torch.cuda.synchronize()
+        cold = B.profile_stop_dict()
+        del flush
+        pro_cold_ms = (cold["rot_absmax"][1] + cold["rot_quant"][1]) / cold_steps
+    if pro_cold_ms > 0:
+        gbs = pro_bytes / (pro_cold_ms * 1e-3) / 1e9
+        rq_cold = {"ms_per_step": round(pro_cold_ms, 4), "gbps": round(gbs, 1),
+                   "pct_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 1),
+                   "what": "prologue algorithmic bytes over the prologue kernels' event time, "
+                           "a 512 MB buffer written before each of %d steps" % cold_steps}
+
     # counted bytes (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated) from profiles/, used only
     # while the sources they were taken from are unchanged
     traffic = None
@@ -348,6 +373,7 @@ def main():
         "rotate_quant_gbps": None if rq_gbs is None else round(rq_gbs, 1),
         "rotate_quant_pct_hbm": None if rq_gbs is None else round(100 * rq_gbs / PEAK_HBM_GBS, 1),
         "rotate_quant_counted": rq_counted,
+        "rotate_quant_cold": rq_cold,
         "roofline": {
             "kernel": "gemm_i8_kernel (int8 MFMA GEMM + dequant epilogue)",
             "bound": "mfma",
