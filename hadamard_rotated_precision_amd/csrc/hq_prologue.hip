@@ -1663,38 +1663,66 @@ struct BothItem {
       m2 = fmaxf(m2, fabsf(v2[i]));
     }
   }
+  // Codes of the item: quantized into registers, then staged back through the half-tile
+  // buffer (its fp32 values are no longer needed) so that both layouts leave as 16-byte stores
+  // covering whole lines: the row-major X B codes as a 256 x 128-byte tile (dword d of row r
+  // at d ^ 4((r / 2) % 8): the accumulator-layout writes meet 64 distinct banks), the B X B
+  // codes_t as a 128 x 256-byte tile (16-byte chunk k of row r at k ^ (r % 16)).
   __device__ void emit(int64_t it, float r1, float r2) const {
     int64_t row0, col0;
     int h;
     decode(it, row0, col0, h);
     const float lo = qlo(a.qp), hi = qhi(a.qp);
+    const int i = n0 & 3, m = n0 >> 2;
+    uint32_t rc[2][8];
     if (a.codes) {
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        const int rloc = 32 * w + 16 * rb, c4 = (rloc >> 2) + lg;
-        const int i = n0 & 3, m = n0 >> 2;
-        int8_t* dst = a.codes + (row0 + rloc + 4 * lg + i) * a.ld + col0 + BT_HALF * h + 4 * m;
+        const int c4 = ((32 * w + 16 * rb) >> 2) + lg;
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) {
           const int c = 16 * nb + n0;
           const float4 y = *reinterpret_cast<const float4*>(&half[c * BT + 4 * bm_chunk(c, c4)]);
           const uint32_t d = qpack4(qbits(y.x, r1, lo, hi), qbits(y.y, r1, lo, hi),
                                     qbits(y.z, r1, lo, hi), qbits(y.w, r1, lo, hi));
-          *reinterpret_cast<uint32_t*>(dst + 16 * nb) = quad_byte_transpose(d, i);
+          rc[rb][nb] = quad_byte_transpose(d, i);
         }
       }
     }
-    int8_t* dst = a.codes_t + (col0 + BT_HALF * h + cp) * a.ld_t + row0 + 64 * pp;
+    uint32_t tc[16];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t xq[4];
+    for (int j = 0; j < 16; ++j)
+      tc[j] = qpack4(qbits(v2[4 * j], r2, lo, hi), qbits(v2[4 * j + 1], r2, lo, hi),
+                     qbits(v2[4 * j + 2], r2, lo, hi), qbits(v2[4 * j + 3], r2, lo, hi));
+    __syncthreads();   // every thread has read its values out of the half tile
+    uint32_t* const rt = reinterpret_cast<uint32_t*>(half);   // [256 rows][32 dwords]
+    uint32_t* const ct = rt + 256 * 32;                       // [128 columns][64 dwords]
+    if (a.codes) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = 16 * q + 4 * j;
-        xq[j] = qpack4(qbits(v2[i], r2, lo, hi), qbits(v2[i + 1], r2, lo, hi),
-                       qbits(v2[i + 2], r2, lo, hi), qbits(v2[i + 3], r2, lo, hi));
+      for (int rb = 0; rb < 2; ++rb) {
+        const int row = 32 * w + 16 * rb + 4 * lg + i;
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) rt[row * 32 + ((4 * nb + m) ^ (4 * ((row >> 1) & 7)))] = rc[rb][nb];
       }
-      *reinterpret_cast<uint4*>(dst + 16 * q) = make_uint4(xq[0], xq[1], xq[2], xq[3]);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<uint4*>(&ct[cp * 64 + 4 * ((4 * pp + q) ^ (cp & 15))]) =
+          make_uint4(tc[4 * q], tc[4 * q + 1], tc[4 * q + 2], tc[4 * q + 3]);
+    __syncthreads();
+    if (a.codes) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int idx = BM_THREADS * p + t, row = idx >> 3, c = idx & 7;
+        *reinterpret_cast<uint4*>(a.codes + (row0 + row) * a.ld + col0 + BT_HALF * h + 16 * c) =
+            *reinterpret_cast<const uint4*>(&rt[row * 32 + 4 * (c ^ ((row >> 1) & 7))]);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int idx = BM_THREADS * p + t, rr = idx >> 4, k = idx & 15;
+      *reinterpret_cast<uint4*>(a.codes_t + (col0 + BT_HALF * h + rr) * a.ld_t + row0 + 16 * k) =
+          *reinterpret_cast<const uint4*>(&ct[rr * 64 + 4 * (k ^ (rr & 15))]);
     }
   }
 };
