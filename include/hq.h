@@ -23,7 +23,8 @@
  *
  * Conventions that hold for every entry point:
  *   - Pointers are DEVICE pointers unless a comment says otherwise; device pointers must be
- *     16-byte aligned (HQ_ERR_ALIGN otherwise).
+ *     16-byte aligned (HQ_ERR_ALIGN otherwise), except hq_fwht's src and dst, which need only
+ *     the alignment of their element type.
  *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*; NULL is the
  *     default stream). Scales stay on the device; no call synchronizes with the host.
  *   - Ownership: the caller allocates every buffer (codes, scales, outputs, workspace).

@@ -145,6 +145,30 @@ def test_fwht_matrix_core_exact(rot, k, dt):
     np.testing.assert_array_equal(T.bits_of(dst), WL.to_dtype_bits(O.rotate(V, rot, k), dt))
 
 
+@pytest.mark.parametrize("which", ["src", "dst"])
+@pytest.mark.parametrize("rot", [B.HQ_ROT_RIGHT, B.HQ_ROT_LEFT])
+def test_fwht_unaligned_pointers(rot, which):
+    """Whole tiles but a source or destination 2 bytes past a 16-byte boundary: the transform
+    takes the element-access path of the VALU kernels instead of the matrix cores, with the
+    same exact result."""
+    banner("fwht-unaligned", rot, which)
+    dt, k = B.HQ_BF16, 128
+    rng = np.random.default_rng(71 + rot)
+    rows, cols = (128, 512) if rot == B.HQ_ROT_RIGHT else (512, 192)
+    V = rng.integers(-8, 9, size=(rows, cols)).astype(np.float64)
+    bits = WL.to_dtype_bits(V, dt)
+    sbuf = torch.zeros(rows * cols + 8, dtype=torch.bfloat16, device=DEV)
+    dbuf = torch.zeros(rows * cols + 8, dtype=torch.bfloat16, device=DEV)
+    so = 1 if which == "src" else 0
+    do = 1 if which == "dst" else 0
+    sbuf[so:so + rows * cols] = T.device_tensor_from_bits(bits, dt, DEV).reshape(-1)
+    B.check(B.hq_fwht(sbuf[so:].data_ptr(), dt, dbuf[do:].data_ptr(), dt, rows, cols, rot, k,
+                      T.stream_ptr()), "fwht")
+    torch.cuda.synchronize()
+    got = T.bits_of(dbuf[do:do + rows * cols].reshape(rows, cols))
+    np.testing.assert_array_equal(got, WL.to_dtype_bits(O.rotate(V, rot, k), dt))
+
+
 @pytest.mark.parametrize("dt", [B.HQ_BF16, B.HQ_F16])
 @pytest.mark.parametrize("rot", [B.HQ_ROT_RIGHT, B.HQ_ROT_LEFT])
 def test_fwht_matrix_core_random(rot, dt):
