@@ -29,7 +29,20 @@ def _dec(t, dt, rows=None, cols=None):
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
 def test_fullsize_sampled(cid):
-    cfg = WL.config(cid)
+    _check_sampled(WL.config(cid), 1000 + cid)
+
+
+@pytest.mark.timeout(900)
+def test_split_launch_with_column_rotation():
+    """HALO-2 at k = 128 with 8192 tokens and C = 5120: the dX product (8192 x 5120, column
+    rotation 128 wide) runs as 256-wide tiles over columns [0, 4096) and a second launch of
+    128-wide tiles over [4096, 5120). Blocks on both sides of the seam and at the end are
+    compared, besides the random samples."""
+    _check_sampled(WL.config(5, N=8192, C=5120, D=256), 77,
+                   dx_cols=[0, 4096 - 128, 4096, 5120 - 128])
+
+
+def _check_sampled(cfg, seed, dx_cols=()):
     N, C, D, k, v = cfg["N"], cfg["C"], cfg["D"], cfg["k"], cfg["variant"]
     out_dt = cfg["out_dtype"]
     print("[case] fullsize", cfg["name"], flush=True)
@@ -56,7 +69,7 @@ def test_fullsize_sampled(cid):
     assert_scale(float(L.qw.scale.cpu()[0]), sw, "sW")
     print("[step] forward codes compared", flush=True)
 
-    rng = np.random.default_rng(1000 + cid)
+    rng = np.random.default_rng(seed)
     rs = np.sort(rng.choice(N, min(N, 128), replace=False))
     cs = np.sort(rng.choice(D, min(D, 128), replace=False))
     y_ref = O.fwd_from_codes(qx, sx, qw, sw, k, v, rows=rs, cols=cs)
@@ -75,9 +88,10 @@ def test_fullsize_sampled(cid):
     print("[step] gradient codes compared", flush=True)
 
     kb = max(k, 16)
-    for _ in range(2):
-        r0 = int(rng.integers(0, N // kb)) * kb
-        c0 = int(rng.integers(0, C // kb)) * kb
+    blocks = [(int(rng.integers(0, N // kb)) * kb, int(rng.integers(0, C // kb)) * kb)
+              for _ in range(2)]
+    blocks += [(int(rng.integers(0, N // kb)) * kb, c) for c in dx_cols]
+    for r0, c0 in blocks:
         ref = O.bwd_input_from_codes(qg, sg, qw, sw, k, v, row_block=(r0, kb), col_block=(c0, kb))
         got = _dec(res["dx"][r0:r0 + kb, c0:c0 + kb], out_dt)
         err = rel_fro(got, rounded(ref, out_dt))
