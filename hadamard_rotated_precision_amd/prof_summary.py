@@ -3,6 +3,9 @@
   python -m hadamard_rotated_precision_amd.prof_summary stats DIR OUT.md --cmd "..."
       per-kernel table from DIR/*kernel_stats.csv (calls, average and total duration).
 
+  python -m hadamard_rotated_precision_amd.prof_summary mfma DIR OUT.md --cmd "..."
+      matrix-core counters per kernel (int8 MFMA ops, MFMA busy cycles, busy fraction).
+
   python -m hadamard_rotated_precision_amd.prof_summary traffic FETCH_DIR WRITE_DIR \
       --copy-bytes B --workload NAME --json OUT.json --md OUT.md --cmd "..."
       HBM bytes per GEMM launch, and of the prologue kernels per step, from two --pmc runs
@@ -153,6 +156,37 @@ def cmd_traffic(args):
     print("\n".join(out))
 
 
+def cmd_mfma(args):
+    """Matrix-core counters per kernel: int8 MFMA ops (SQ_INSTS_VALU_MFMA_MOPS_I8 x 512),
+    MFMA busy cycles, and the busy fraction of all SIMDs over the kernel's active cycles."""
+    path = _one(os.path.join(args.dir, "**", "*counter_collection.csv"))
+    acc = {}
+    for r in csv.DictReader(open(path)):
+        if "hq::" not in r["Kernel_Name"]:
+            continue
+        acc.setdefault(short_name(r["Kernel_Name"]), {}).setdefault(r["Counter_Name"], []).append(
+            float(r["Counter_Value"]))
+    out = ["# Matrix-core counters: %s" % args.title, "",
+           "One rocprofv3 --pmc run; values are per dispatch, averaged over the dispatches of each",
+           "kernel. GRBM_GUI_ACTIVE comes summed over the %d XCDs (per XCD it matches the kernel's" % args.xcds,
+           "duration times the clock), so MFMA busy %% = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE /",
+           "%d x %d SIMDs). int8 ops = SQ_INSTS_VALU_MFMA_MOPS_I8 x 512." % (args.xcds, args.simds), "",
+           "Command (from the repository root, rocprofv3 run in /tmp):", "", "```", args.cmd, "```", "",
+           "| kernel | dispatches | int8 MFMA ops | MFMA busy cycles | active cycles per XCD | MFMA busy % |",
+           "|---|---:|---:|---:|---:|---:|"]
+    for k in sorted(acc):
+        c = acc[k]
+        avg = {n: sum(v) / len(v) for n, v in c.items()}
+        n = len(next(iter(c.values())))
+        gui = avg.get("GRBM_GUI_ACTIVE", 0.0) / args.xcds
+        busy = avg.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        ops = avg.get("SQ_INSTS_VALU_MFMA_MOPS_I8", 0.0) * 512
+        util = 100.0 * busy / (gui * args.simds) if gui > 0 else 0.0
+        out.append("| `%s` | %d | %.4g | %.4g | %.4g | %.1f |" % (k, n, ops, busy, gui, util))
+    open(args.out, "w").write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = ap.add_subparsers(dest="what", required=True)
@@ -169,11 +203,20 @@ def main(argv=None):
     t.add_argument("--json", required=True)
     t.add_argument("--md", required=True)
     t.add_argument("--cmd", required=True)
+    mm = sub.add_parser("mfma")
+    mm.add_argument("dir")
+    mm.add_argument("out")
+    mm.add_argument("--cmd", required=True)
+    mm.add_argument("--title", default="")
+    mm.add_argument("--xcds", type=int, default=8)
+    mm.add_argument("--simds", type=int, default=1024)
     t.add_argument("--gemms-per-step", type=int, default=3,
                    help="GEMM launches per step of the workload (fwd + dX + dW = 3)")
     args = ap.parse_args(argv)
     if args.what == "stats":
         cmd_stats(args)
+    elif args.what == "mfma":
+        cmd_mfma(args)
     else:
         cmd_traffic(args)
     return 0
