@@ -3,6 +3,9 @@
   python -m hadamard_rotated_precision_amd.prof_summary stats DIR OUT.md --cmd "..."
       per-kernel table from DIR/*kernel_stats.csv (calls, average and total duration).
 
+  python -m hadamard_rotated_precision_amd.prof_summary counters DIR OUT.md --cmd "..." [--ratio A/B]
+      any --pmc counters per kernel, averaged over its dispatches.
+
   python -m hadamard_rotated_precision_amd.prof_summary mfma DIR OUT.md --cmd "..."
       matrix-core counters per kernel (int8 MFMA ops, MFMA busy cycles, busy fraction).
 
@@ -187,6 +190,32 @@ def cmd_mfma(args):
     print("\n".join(out))
 
 
+def cmd_counters(args):
+    """Any --pmc counters per kernel: the value per dispatch (as rocprofv3 reports it for the
+    device), averaged over the dispatches of each kernel; --ratio A/B adds a column A / B."""
+    path = _one(os.path.join(args.dir, "**", "*counter_collection.csv"))
+    acc = {}
+    for r in csv.DictReader(open(path)):
+        if "hq::" not in r["Kernel_Name"]:
+            continue
+        acc.setdefault(short_name(r["Kernel_Name"]), {}).setdefault(r["Counter_Name"], []).append(
+            float(r["Counter_Value"]))
+    names = sorted({n for c in acc.values() for n in c})
+    ratios = [tuple(x.split("/")) for x in args.ratio]
+    out = ["# Counters: %s" % args.title, "", args.note, "",
+           "Command (from the repository root, rocprofv3 run in /tmp):", "", "```", args.cmd, "```", "",
+           "| kernel | " + " | ".join(names + ["%s / %s" % r for r in ratios]) + " |",
+           "|---|" + "---:|" * (len(names) + len(ratios))]
+    for k in sorted(acc):
+        avg = {n: sum(v) / len(v) for n, v in acc[k].items()}
+        cells = ["%.4g" % avg.get(n, 0.0) for n in names]
+        for a, b in ratios:
+            cells.append("%.1f %%" % (100.0 * avg.get(a, 0.0) / avg[b]) if avg.get(b) else "-")
+        out.append("| `%s` | %s |" % (k, " | ".join(cells)))
+    open(args.out, "w").write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = ap.add_subparsers(dest="what", required=True)
@@ -203,6 +232,13 @@ def main(argv=None):
     t.add_argument("--json", required=True)
     t.add_argument("--md", required=True)
     t.add_argument("--cmd", required=True)
+    cc = sub.add_parser("counters")
+    cc.add_argument("dir")
+    cc.add_argument("out")
+    cc.add_argument("--cmd", required=True)
+    cc.add_argument("--title", default="")
+    cc.add_argument("--note", default="")
+    cc.add_argument("--ratio", action="append", default=[])
     mm = sub.add_parser("mfma")
     mm.add_argument("dir")
     mm.add_argument("out")
@@ -217,6 +253,8 @@ def main(argv=None):
         cmd_stats(args)
     elif args.what == "mfma":
         cmd_mfma(args)
+    elif args.what == "counters":
+        cmd_counters(args)
     else:
         cmd_traffic(args)
     return 0
