@@ -5,13 +5,20 @@ HALO-2 rotations, tensor-wise INT8) on one MI355X, through the C ABI of libhq.
 A step is the whole hot path on one batch: rotate+quantize X, W and dY, the three INT8 MFMA
 GEMMs with dequantization, and the output-side inverse rotations. Inputs are seeded synthetic
 tensors with the workload's shapes and distributions, resident in HBM before timing starts.
+The default workload is the largest one, the Qwen-14B-shaped down projection
+(8192 x 13824 x 5120, k = 128, HALO-2, bf16).
 
 Printed (one JSON line): effective TOPS = sum of 2*M*N*K over the three products / step
 time of an uninstrumented timed region; the percentage of the INT8 MFMA peak; the roofline of
 the dominant kernel (the GEMM, its launches stamped with HIP events on their own stream during
-a second pass of the same steps); the rotate+quantize bandwidth; an unrotated bf16 GEMM
-baseline of the same three products; the step of the Llama-7B-shaped layer against its bf16
-baseline; and the CPU oracle timed on a bounded sample of the same workload.
+a second pass of the same steps, per product and overall); the rotate+quantize bandwidth; an
+unrotated bf16 GEMM baseline of the same three products; the steps of the Llama-7B-shaped
+layer and of the 2048 x 4096 x 4096 layer against their bf16 baselines; hq_fwht through the
+butterfly and matrix-core paths; and the CPU oracle timed on a bounded sample of the same
+workload.
+
+Step comparisons against bf16 use one method on both sides: an event pair on the stream around
+each step, 5 warm-up steps, then the median of 20.
 """
 import argparse
 import hashlib
@@ -58,8 +65,20 @@ def prologue_bytes(cfg, in_bytes):
     return b
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg_id, tokens):
-    """The oracle (plain C, OpenMP) on a bounded sample: the same workload with fewer tokens."""
+    """The oracle (plain C, OpenMP over output rows) on a bounded sample: the same workload
+    with fewer tokens (the weight tensor is still rotated and quantized whole)."""
     import oracle as O
     from hadamard_rotated_precision_amd import workloads as WL
     cfg = WL.config(cfg_id)
@@ -76,16 +95,35 @@ def cpu_baseline(cfg_id, tokens):
              cfg["passes"])
     dt_s = time.perf_counter() - t0
     ops = layer_ops(cfg)
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": ops / dt_s / 1e12, "unit": "TOPS", "cores": cores, "kind": "oracle",
-            "sample": "%s with N=%d tokens (same C, D, k, distributions): rotate, quantize, "
-                      "int64 GEMMs, exact inverse rotations, dequantize for %s; %.2f s"
+    return {"value": ops / dt_s / 1e12, "unit": "TOPS", "cores": O.threads(), "kind": "oracle",
+            "cpu": cpu_model(),
+            "sample": "%s with N=%d tokens (same C, D, k, distributions; W rotated and "
+                      "quantized whole): rotate, quantize, int64 GEMMs, exact inverse rotations, "
+                      "dequantize for %s; %.2f s"
                       % (cfg["name"], tokens, "+".join(cfg["passes"]), dt_s),
             "seconds": dt_s}
 
 
-def bf16_baseline(cfg, steps, warmup, library):
-    """Three unrotated bf16 GEMMs of the same shapes (timing context only)."""
+def event_median_ms(fn, warmup=5, reps=20):
+    """GPU time of fn() on the current stream: an event pair around each call, after `warmup`
+    calls; the median of `reps` calls in ms."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for e0, e1 in evs:
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    times = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+    return times[len(times) // 2]
+
+
+def bf16_baseline(cfg, library):
+    """Three unrotated bf16 GEMMs of the same shapes (timing context only): event median."""
     import torch
     torch.backends.cuda.preferred_blas_library(library)
     N, C, D = cfg["N"], cfg["C"], cfg["D"]
@@ -98,22 +136,16 @@ def bf16_baseline(cfg, steps, warmup, library):
         torch.mm(x, w.t())
         torch.mm(dy, w)
         torch.mm(dy.t(), x)
-    for _ in range(warmup):
-        run()
-    torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    for _ in range(steps):
-        run()
-    e.record()
-    torch.cuda.synchronize()
-    return s.elapsed_time(e) / steps
+    ms = event_median_ms(run)
+    torch.backends.cuda.preferred_blas_library("default")
+    return ms
 
 
-def fwht_bandwidth(reps=20, rows=8192, cols=13824, k=128):
+def fwht_bandwidth(reps=20, rows=8192, cols=13824, ks=(16, 64, 128, 256)):
     """hq_fwht on its own (bf16 in, bf16 out), RIGHT and LEFT, on the largest operand shape of
-    the workloads (X of the 8192 x 13824 x 5120 layer, k = 128): algorithmic bytes = 2 B read
-    + 2 B written per element, over the mean launch time (events on the launch stream)."""
+    the workloads (X of the 8192 x 13824 x 5120 layer), through the VALU butterflies and the
+    matrix cores at each k: algorithmic bytes = 2 B read + 2 B written per element, over the
+    mean launch time (events on the launch stream). `auto` names the path hq_fwht takes."""
     import torch
     from hadamard_rotated_precision_amd import binding as B
     from hadamard_rotated_precision_amd import tensors as T
@@ -121,32 +153,38 @@ def fwht_bandwidth(reps=20, rows=8192, cols=13824, k=128):
     gen.manual_seed(106)
     src = torch.randn((rows, cols), dtype=torch.float32, device="cuda", generator=gen).to(torch.bfloat16)
     dst = torch.empty_like(src)
-    res = {"shape": "%dx%d bf16 -> bf16" % (rows, cols), "k": k,
-           "bytes_per_launch": 4 * rows * cols}
+    res = {"shape": "%dx%d bf16 -> bf16" % (rows, cols), "bytes_per_launch": 4 * rows * cols}
     for name, rot in (("right", B.HQ_ROT_RIGHT), ("left", B.HQ_ROT_LEFT)):
-        def run():
-            B.check(B.hq_fwht(src.data_ptr(), B.HQ_BF16, dst.data_ptr(), B.HQ_BF16, rows, cols,
-                              rot, k, T.stream_ptr()), "fwht")
-        for _ in range(3):
-            run()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(reps):
-            run()
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
-        gbs = 4.0 * rows * cols / (us * 1e-6) / 1e9
-        res[name] = {"us": round(us, 2), "gbps": round(gbs, 1),
-                     "pct_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 1)}
+        res[name] = {}
+        for k in ks:
+            row = {}
+            for pname, path in (("butterfly", B.HQ_FWHT_BUTTERFLY), ("matrix", B.HQ_FWHT_MATRIX)):
+                def run():
+                    B.check(B.hq_fwht_path(src.data_ptr(), B.HQ_BF16, dst.data_ptr(), B.HQ_BF16,
+                                           rows, cols, rot, k, path, T.stream_ptr()), "fwht")
+                for _ in range(3):
+                    run()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record()
+                for _ in range(reps):
+                    run()
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / reps
+                gbs = 4.0 * rows * cols / (us * 1e-6) / 1e9
+                row[pname] = {"us": round(us, 2), "gbps": round(gbs, 1),
+                              "pct_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 1)}
+            auto_matrix = rot == B.HQ_ROT_LEFT or k >= 128
+            row["auto"] = "matrix" if auto_matrix else "butterfly"
+            res[name]["k%d" % k] = row
     return res
 
 
-def layer_vs_bf16(cfg_id, steps, warmup):
-    """The HQ-MM step of another workload (inputs resident, no instrumentation) next to the
-    three unrotated bf16 GEMMs of the same shapes: the comparison the target names for the
-    Llama-7B-shaped MLP layer."""
+def layer_vs_bf16(cfg_id):
+    """The HQ-MM step of a workload (inputs resident, no instrumentation) next to the three
+    unrotated bf16 GEMMs of the same shapes, both timed by event_median_ms: the comparison the
+    target names for the Llama-7B-shaped MLP layer."""
     import torch
     from hadamard_rotated_precision_amd import tensors as T
     from hadamard_rotated_precision_amd import workloads as WL
@@ -169,36 +207,33 @@ def layer_vs_bf16(cfg_id, steps, warmup):
         layer.fwd(x, w, y, None, stream)
         layer.bwd_input(dy, dx, None, stream)
         layer.bwd_weight(dw, stream)
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / steps
+    ms = event_median_ms(step)
     del x, w, dy, y, dx, dw, layer
-    ms_rb = bf16_baseline(cfg, steps, warmup, "cublas")
-    ms_lt = bf16_baseline(cfg, steps, warmup, "cublaslt")
+    ms_rb = bf16_baseline(cfg, "cublas")
+    ms_lt = bf16_baseline(cfg, "cublaslt")
     return {"workload": cfg["name"], "hq_ms_per_step": round(ms, 4),
             "hq_tops": round(layer_ops(cfg) / (ms * 1e-3) / 1e12, 1),
             "bf16_ms_rocblas": round(ms_rb, 4), "bf16_ms_hipblaslt": round(ms_lt, 4),
-            "speedup_vs_rocblas": round(ms_rb / ms, 3), "speedup_vs_hipblaslt": round(ms_lt / ms, 3)}
+            "speedup_vs_rocblas": round(ms_rb / ms, 3), "speedup_vs_hipblaslt": round(ms_lt / ms, 3),
+            "timing": "event pair around each step on the stream, 5 warm-ups, median of 20 "
+                      "(the same for the bf16 GEMMs)"}
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2,
-                    help="workload id (default 2: HALO-2 step, 2048 x 4096 x 4096, k=256)")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=5,
+                    help="workload id (default 5: HALO-2 step, 8192 x 13824 x 5120, k=128, the "
+                         "largest layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
-    ap.add_argument("--check-config", type=int, default=4,
-                    help="also time this workload's step against three bf16 GEMMs (default 4: "
-                         "the Llama-7B-shaped MLP layer); 0 to skip")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=128)
+    ap.add_argument("--check-configs", type=str, default="4,2",
+                    help="also time these workloads' steps against three bf16 GEMMs (default "
+                         "4,2: the Llama-7B-shaped MLP layer and the 2048 x 4096 x 4096 layer); "
+                         "empty to skip")
     ap.add_argument("--no-fwht", action="store_true",
                     help="skip the standalone hq_fwht bandwidth figure")
     ap.add_argument("--no-cold", action="store_true",
@@ -276,6 +311,21 @@ def main():
     eff_tops = ops / (ms_per_step * 1e-3) / 1e12
     print("[bench] timed region done: %.3f ms/step" % ms_per_step, file=sys.stderr, flush=True)
 
+    ms_events = event_median_ms(step, warmup=2, reps=max(5, args.steps))
+
+    # GEMM launches of each call of the step (one, or a head and a tail launch)
+    per_call = []
+    for name, call in (("fwd", lambda: layer.fwd(x, w, y, steps_t, stream)),
+                       ("dx", (lambda: layer.bwd_input(dy, dx, steps_t, stream)) if dx is not None else None),
+                       ("dw", (lambda: layer.bwd_weight(dw, stream)) if dw is not None else None)):
+        if call is None:
+            continue
+        B.check(B.hq_profile_start(1 << B.HQ_KIND_GEMM), "profile")
+        call()
+        torch.cuda.synchronize()
+        B.profile_stop_dict()
+        per_call.append((name, len(B.profile_records())))
+
     # ---- roofline pass: the same K steps again, each GEMM launch stamped with HIP events on
     # its own launch stream (hipExtLaunchKernel records the kernel's start and end)
     B.check(B.hq_profile_start(1 << B.HQ_KIND_GEMM), "profile")
@@ -286,10 +336,27 @@ def main():
     torch.cuda.synchronize()
     t3 = time.perf_counter()
     prof = B.profile_stop_dict()
+    recs = B.profile_records()
     ms_instr = (t3 - t2) * 1e3 / args.steps
     gcount, gms, gunits = prof["gemm"]
     gemm_tops = gunits / (gms * 1e-3) / 1e12 if gms > 0 else None
     gemm_avg_us = gms * 1e3 / gcount if gcount else None
+    per_step = sum(n for _, n in per_call)
+    products = {}
+    if per_step and len(recs) == per_step * args.steps:
+        pos = 0
+        for name, n in per_call:
+            for j in range(n):
+                sel = [recs[st * per_step + pos + j] for st in range(args.steps)]
+                ms_sum = sum(r[1] for r in sel)
+                units = sum(r[2] for r in sel)
+                label = name if n == 1 else "%s_%s" % (name, "head" if j == 0 else "tail")
+                tops = units / (ms_sum * 1e-3) / 1e12
+                products[label] = {"avg_us": round(ms_sum * 1e3 / len(sel), 2),
+                                   "ops_per_launch": units / len(sel),
+                                   "tops": round(tops, 1),
+                                   "frac": round(tops / PEAK_INT8_TOPS, 4)}
+            pos += n
 
     # ---- per-kind breakdown of the same step (all kinds bracketed; a separate pass)
     B.check(B.hq_profile_start((1 << B.HQ_KIND_COUNT) - 1), "profile")
@@ -359,6 +426,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_event_median": round(ms_events, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -385,30 +453,34 @@ def main():
             "launches": gcount,
             "avg_launch_us": None if gemm_avg_us is None else round(gemm_avg_us, 2),
             "ops_per_launch": None if not gcount else gunits / gcount,
+            "products": products,
             "timing": "HIP events stamped by hipExtLaunchKernel on each GEMM launch, over a "
-                      "second pass of the same %d steps (%.4f ms/step with the events)"
-                      % (args.steps, ms_instr),
+                      "second pass of the same %d steps (%.4f ms/step with the events); "
+                      "achieved = all GEMM ops / all GEMM launch time" % (args.steps, ms_instr),
         },
         "breakdown_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in breakdown.items()},
     }
     if not args.no_bf16_baseline:
         try:
-            ms_rb = bf16_baseline(cfg, args.steps, args.warmup, "cublas")
-            ms_lt = bf16_baseline(cfg, args.steps, args.warmup, "cublaslt")
+            ms_rb = bf16_baseline(cfg, "cublas")
+            ms_lt = bf16_baseline(cfg, "cublaslt")
             result["bf16_baseline"] = {
-                "what": "three unrotated bf16 torch.mm of the same shapes (Y, dX, dW)",
+                "what": "three unrotated bf16 torch.mm of the same shapes (Y, dX, dW), event "
+                        "median of 20 after 5 warm-ups, against the HQ-MM step's event median",
                 "ms_rocblas": round(ms_rb, 4), "ms_hipblaslt": round(ms_lt, 4),
-                "speedup_vs_rocblas": round(ms_rb / ms_per_step, 3),
-                "speedup_vs_hipblaslt": round(ms_lt / ms_per_step, 3)}
+                "speedup_vs_rocblas": round(ms_rb / ms_events, 3),
+                "speedup_vs_hipblaslt": round(ms_lt / ms_events, 3)}
         except Exception as exc:  # report, do not fail the benchmark line
             result["bf16_baseline"] = {"error": str(exc)}
-    if args.check_config and args.check_config != args.config:
-        print("[bench] step vs bf16 on config %d" % args.check_config, file=sys.stderr, flush=True)
+    checks = [int(c) for c in args.check_configs.split(",") if c.strip()]
+    for cid in checks:
+        if cid == args.config:
+            continue
+        print("[bench] step vs bf16 on config %d" % cid, file=sys.stderr, flush=True)
         try:
-            result["layer_vs_bf16"] = layer_vs_bf16(args.check_config, max(5, args.steps // 5),
-                                                    max(2, args.warmup // 2))
+            result.setdefault("layer_vs_bf16", {})["config%d" % cid] = layer_vs_bf16(cid)
         except Exception as exc:  # report, do not fail the benchmark line
-            result["layer_vs_bf16"] = {"error": str(exc)}
+            result.setdefault("layer_vs_bf16", {})["config%d" % cid] = {"error": str(exc)}
     if not args.no_fwht:
         print("[bench] hq_fwht bandwidth", file=sys.stderr, flush=True)
         try:

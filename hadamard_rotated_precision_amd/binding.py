@@ -19,10 +19,12 @@ HQ_F32, HQ_F16, HQ_BF16 = 0, 1, 2
 HQ_ROT_NONE, HQ_ROT_RIGHT, HQ_ROT_LEFT, HQ_ROT_BOTH = 0, 1, 2, 3
 HQ_SCALE_ABSMAX, HQ_SCALE_STEP = 0, 1
 HQ_VARIANT_HALO0, HQ_VARIANT_HQ, HQ_VARIANT_HALO2 = 0, 1, 2
+HQ_FWHT_AUTO, HQ_FWHT_BUTTERFLY, HQ_FWHT_MATRIX = 0, 1, 2
 
 EXPORTS = ["hq_abi_version", "hq_status_string", "hq_code_pitch", "hq_workspace_bytes",
            "hq_rotate_quantize", "hq_linear_fwd", "hq_linear_bwd_input", "hq_linear_bwd_weight",
-           "hq_fwht", "hq_gemm_i8_i32", "hq_profile_start", "hq_profile_stop"]
+           "hq_fwht", "hq_fwht_path", "hq_gemm_i8_i32", "hq_profile_start", "hq_profile_stop",
+           "hq_profile_records"]
 HQ_KIND_GEMM, HQ_KIND_ROT_ABSMAX, HQ_KIND_ROT_QUANT, HQ_KIND_ROT_STORE = 0, 1, 2, 3
 HQ_KIND_TRANSPOSE, HQ_KIND_MISC, HQ_KIND_COUNT = 4, 5, 6
 KIND_NAMES = ["gemm", "rot_absmax", "rot_quant", "rot_store", "transpose", "misc"]
@@ -43,6 +45,11 @@ class hq_qtensor(ctypes.Structure):
 class hq_profile_stat(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("count", ctypes.c_int32),
                 ("total_ms", ctypes.c_double), ("units", ctypes.c_double)]
+
+
+class hq_profile_record(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("ms", ctypes.c_double), ("units", ctypes.c_double)]
 
 
 class HQError(RuntimeError):
@@ -95,12 +102,16 @@ def load(build_if_missing=True):
                                          P(hq_config), vp, i32, vp, sz, vp]
     lib.hq_fwht.restype = i32
     lib.hq_fwht.argtypes = [vp, i32, vp, i32, i64, i64, i32, i32, vp]
+    lib.hq_fwht_path.restype = i32
+    lib.hq_fwht_path.argtypes = [vp, i32, vp, i32, i64, i64, i32, i32, i32, vp]
     lib.hq_gemm_i8_i32.restype = i32
     lib.hq_gemm_i8_i32.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, vp]
     lib.hq_profile_start.restype = i32
     lib.hq_profile_start.argtypes = [ctypes.c_uint32]
     lib.hq_profile_stop.restype = i32
     lib.hq_profile_stop.argtypes = [P(hq_profile_stat), i32]
+    lib.hq_profile_records.restype = i32
+    lib.hq_profile_records.argtypes = [P(hq_profile_record), i32]
     _lib = lib
     return lib
 
@@ -153,6 +164,10 @@ def hq_fwht(src, src_dtype, dst, dst_dtype, rows, cols, rot, k, stream):
     return load().hq_fwht(src, src_dtype, dst, dst_dtype, rows, cols, rot, k, stream)
 
 
+def hq_fwht_path(src, src_dtype, dst, dst_dtype, rows, cols, rot, k, path, stream):
+    return load().hq_fwht_path(src, src_dtype, dst, dst_dtype, rows, cols, rot, k, path, stream)
+
+
 def hq_gemm_i8_i32(a, lda, b_t, ldb, c, M, N, K, stream):
     return load().hq_gemm_i8_i32(a, lda, b_t, ldb, c, M, N, K, stream)
 
@@ -163,6 +178,18 @@ def hq_profile_start(kind_mask):
 
 def hq_profile_stop(stats, n_stats):
     return load().hq_profile_stop(stats, n_stats)
+
+
+def hq_profile_records(out, cap):
+    return load().hq_profile_records(out, cap)
+
+
+def profile_records():
+    """The per-launch records of the last hq_profile_stop: a list of (kind name, ms, units)."""
+    n = hq_profile_records(None, 0)
+    arr = (hq_profile_record * max(n, 1))()
+    n = hq_profile_records(arr, n)
+    return [(KIND_NAMES[arr[i].kind], arr[i].ms, arr[i].units) for i in range(n)]
 
 
 def profile_stop_dict():

@@ -501,21 +501,38 @@ hq_status hq_linear_bwd_weight(const hq_qtensor* saved_g, const hq_qtensor* save
   return HQ_OK;
 }
 
-hq_status hq_fwht(const void* src, int32_t src_dtype, void* dst, int32_t dst_dtype, int64_t rows,
-                  int64_t cols, int32_t rot, int32_t k, void* stream) {
+hq_status hq_fwht_path(const void* src, int32_t src_dtype, void* dst, int32_t dst_dtype,
+                       int64_t rows, int64_t cols, int32_t rot, int32_t k, int32_t path,
+                       void* stream) {
   if (!valid_dt(src_dtype) || !valid_dt(dst_dtype)) return HQ_ERR_DTYPE;
   if (!is_pow2_k(k)) return HQ_ERR_K;
   if (rot != HQ_ROT_NONE && rot != HQ_ROT_RIGHT && rot != HQ_ROT_LEFT) return HQ_ERR_MODE;
+  if (path != HQ_FWHT_AUTO && path != HQ_FWHT_BUTTERFLY && path != HQ_FWHT_MATRIX)
+    return HQ_ERR_MODE;
   if (rows < 0 || cols < 0) return HQ_ERR_SHAPE;
   if (rot == HQ_ROT_RIGHT && cols % k) return HQ_ERR_SHAPE;
   if (rot == HQ_ROT_LEFT && rows % k) return HQ_ERR_SHAPE;
   if (rows * cols > 0 && (!src || !dst)) return HQ_ERR_NULL;
+  // the matrix-core store kernels cover whole tiles of 16-bit data only (see hq.h)
+  const bool left_mma = rot == HQ_ROT_LEFT && k >= 16 &&
+                        hq::fwht_left_mma_ok(src, src_dtype, dst, dst_dtype, rows, cols, k);
+  const bool right_mma = rot == HQ_ROT_RIGHT && k >= 16 &&
+                         hq::fwht_right_mma_ok(src, src_dtype, dst, dst_dtype, rows, cols, k);
+  if (path == HQ_FWHT_MATRIX && !left_mma && !right_mma) return HQ_ERR_MODE;
   if (rows * cols == 0) return HQ_OK;
   HQ_CHECK(device_ok());
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (rot == HQ_ROT_LEFT && k > 1 &&
-      hq::fwht_left_mma_ok(src, src_dtype, dst, dst_dtype, rows, cols, k)) {
+  // AUTO: the matrix cores for every token-axis (LEFT) rotation they cover, and for RIGHT at
+  // k >= 128, where they were measured faster than the butterflies; butterflies elsewhere
+  const bool use_left_mma = left_mma && path != HQ_FWHT_BUTTERFLY;
+  const bool use_right_mma =
+      right_mma && (path == HQ_FWHT_MATRIX || (path == HQ_FWHT_AUTO && k >= 128));
+  if (use_left_mma) {
     HQ_TRY(hq::fwht_left_mma(src, src_dtype, rows, cols, k, dst, st));
+    return HQ_OK;
+  }
+  if (use_right_mma) {
+    HQ_TRY(hq::fwht_right_mma(src, src_dtype, rows, cols, k, dst, st));
     return HQ_OK;
   }
   if (rot == HQ_ROT_LEFT && k > 1) {
@@ -530,11 +547,6 @@ hq_status hq_fwht(const void* src, int32_t src_dtype, void* dst, int32_t dst_dty
     HQ_TRY(hq::cols_pass(c, st));
     return HQ_OK;
   }
-  if (rot == HQ_ROT_RIGHT && k > 1 &&
-      hq::fwht_right_mma_ok(src, src_dtype, dst, dst_dtype, rows, cols, k)) {
-    HQ_TRY(hq::fwht_right_mma(src, src_dtype, rows, cols, k, dst, st));
-    return HQ_OK;
-  }
   RowPass r;
   r.src = src;
   r.in_dt = src_dtype;
@@ -545,6 +557,11 @@ hq_status hq_fwht(const void* src, int32_t src_dtype, void* dst, int32_t dst_dty
   r.out_dt = dst_dtype;
   HQ_TRY(hq::rows_pass(r, st));
   return HQ_OK;
+}
+
+hq_status hq_fwht(const void* src, int32_t src_dtype, void* dst, int32_t dst_dtype, int64_t rows,
+                  int64_t cols, int32_t rot, int32_t k, void* stream) {
+  return hq_fwht_path(src, src_dtype, dst, dst_dtype, rows, cols, rot, k, HQ_FWHT_AUTO, stream);
 }
 
 hq_status hq_gemm_i8_i32(const int8_t* a, int64_t lda, const int8_t* b_t, int64_t ldb,

@@ -26,6 +26,7 @@ std::mutex g_mu;
 bool g_on = false;
 uint32_t g_mask = 0;
 std::vector<Rec> g_recs;
+std::vector<hq_profile_record> g_done;   // per-launch results of the last hq_profile_stop
 std::vector<hipEvent_t> g_pool;
 size_t g_next = 0;
 
@@ -81,6 +82,7 @@ extern "C" {
 hq_status hq_profile_start(uint32_t kind_mask) {
   std::lock_guard<std::mutex> lk(hq::g_mu);
   hq::g_recs.clear();
+  hq::g_done.clear();
   hq::g_next = 0;
   hq::g_mask = kind_mask;
   hq::g_on = kind_mask != 0;
@@ -98,12 +100,14 @@ hq_status hq_profile_stop(hq_profile_stat* stats, int32_t n_stats) {
     stats[i].units = 0.0;
   }
   hq_status st = HQ_OK;
+  hq::g_done.clear();
   for (const auto& r : hq::g_recs) {
     float ms = 0.0f;
     if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
       st = HQ_ERR_LAUNCH;
       continue;
     }
+    hq::g_done.push_back(hq_profile_record{r.kind, 0, static_cast<double>(ms), r.units});
     if (r.kind < n_stats) {
       stats[r.kind].count += 1;
       stats[r.kind].total_ms += ms;
@@ -113,6 +117,14 @@ hq_status hq_profile_stop(hq_profile_stat* stats, int32_t n_stats) {
   hq::g_recs.clear();
   hq::g_next = 0;
   return st;
+}
+
+int32_t hq_profile_records(hq_profile_record* out, int32_t cap) {
+  std::lock_guard<std::mutex> lk(hq::g_mu);
+  const int32_t n = static_cast<int32_t>(hq::g_done.size());
+  if (out)
+    for (int32_t i = 0; i < n && i < cap; ++i) out[i] = hq::g_done[i];
+  return n;
 }
 
 }  // extern "C"

@@ -1950,7 +1950,7 @@ bool fwht_right_mma_ok(const void* src, int dt, const void* dst, int out_dt, int
                        int64_t cols, int k) {
   const bool al = (reinterpret_cast<uintptr_t>(src) & 15u) == 0 &&
                   (reinterpret_cast<uintptr_t>(dst) & 15u) == 0;
-  return k >= 128 && dt == out_dt && (dt == DT_F16 || dt == DT_BF16) && al &&
+  return dt == out_dt && (dt == DT_F16 || dt == DT_BF16) && al &&
          right_mma_ok(rows, cols, (cols * 2) % 16 == 0, 2, k);
 }
 

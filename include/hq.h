@@ -196,6 +196,23 @@ hq_status hq_linear_bwd_weight(const hq_qtensor *saved_g, const hq_qtensor *save
 hq_status hq_fwht(const void *src, int32_t src_dtype, void *dst, int32_t dst_dtype,
                   int64_t rows, int64_t cols, int32_t rot, int32_t k, void *stream);
 
+/* hq_fwht with the implementation named (for measuring one against the other; the results
+ * agree to the fp32 summation order). path:
+ *   HQ_FWHT_AUTO       what hq_fwht picks: the matrix cores for LEFT whenever they cover the
+ *                      call, and for RIGHT at k >= 128; the VALU butterflies otherwise;
+ *   HQ_FWHT_BUTTERFLY  the VALU butterflies (log2 k add/sub stages per element), any shape;
+ *   HQ_FWHT_MATRIX     the matrix cores (a dense +-1 contraction in 16-bit MFMA, exact
+ *                      products, fp32 sums); HQ_ERR_MODE unless the call has 16-bit
+ *                      src_dtype == dst_dtype, 16-byte aligned pointers, k >= 16 and whole
+ *                      tiles (RIGHT: rows % 64 == 0, cols % 256 == 0; LEFT: rows % 256 == 0,
+ *                      cols % 64 == 0).
+ * Other arguments and errors as hq_fwht. */
+typedef enum { HQ_FWHT_AUTO = 0, HQ_FWHT_BUTTERFLY = 1, HQ_FWHT_MATRIX = 2 } hq_fwht_impl;
+
+hq_status hq_fwht_path(const void *src, int32_t src_dtype, void *dst, int32_t dst_dtype,
+                       int64_t rows, int64_t cols, int32_t rot, int32_t k, int32_t path,
+                       void *stream);
+
 /* Standalone integer GEMM with int32 accumulation (INT4 page §3.1, §A.6):
  *   c[m][n] = sum_k a[m][k] * b_t[n][k];  a: M x K (pitch lda), b_t: N x K (pitch ldb),
  *   c: M x N int32 (pitch N elements). lda, ldb multiples of 16 and >= K; bytes of a row
@@ -230,6 +247,19 @@ typedef struct {
 
 hq_status hq_profile_start(uint32_t kind_mask);
 hq_status hq_profile_stop(hq_profile_stat *stats, int32_t n_stats);
+
+/* The launches recorded between the last hq_profile_start and hq_profile_stop, one record
+ * each in launch order (kind, event time in ms, algorithmic units; `reserved` is 0). Copies
+ * at most `cap` records into `out` (host memory; may be NULL when cap is 0) and returns how
+ * many there are. Valid until the next hq_profile_start. */
+typedef struct {
+  int32_t kind;
+  int32_t reserved;
+  double ms;
+  double units;
+} hq_profile_record;
+
+int32_t hq_profile_records(hq_profile_record *out, int32_t cap);
 
 #ifdef __cplusplus
 }

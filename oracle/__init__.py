@@ -50,6 +50,7 @@ def _load():
     lib = ctypes.CDLL(LIB_PATH)
     i64, i32, vp, f32 = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_float
     lib.hqo_version.restype = i32
+    lib.hqo_threads.restype = i32
     lib.hqo_hadamard.argtypes = [i32, vp]
     lib.hqo_hadamard.restype = i32
     lib.hqo_decode.argtypes = [vp, i32, i64, vp]
@@ -70,6 +71,11 @@ def _load():
     lib.hqo_round.restype = i32
     _lib = lib
     return lib
+
+
+def threads():
+    """OpenMP threads the oracle's loops run on."""
+    return int(_load().hqo_threads())
 
 
 def _p(a):

@@ -31,9 +31,11 @@
  *     h(i,j) = (-1)^popcount(i & j); the 1/k factors go into the dequantization scalar.
  *   - Symmetric integer grid: codes in [-Qp, Qp], Qp = 127 (8 bit) or 7 (4-bit range).
  *   - Round to nearest, ties to even.
- *   - The code decision is taken in fp32, the precision the GPU kernel decides in:
- *       v32 = fp32(v) (v the rotated value), a32 = max |v32|, s = fp32(a32 / Qp),
- *       r = fp32(1 / s), q = clamp(RNE(v32 * r), -Qp, Qp) with the product exact.
+ *   - The scale and the code are the plain definitions, taken exactly from the rotated value R
+ *     (summed in long double, exact for the 16-bit inputs used here):
+ *       a = max |R|,  s = a / Qp rounded once to fp32 (the scale is stored as one fp32),
+ *       q = clamp(RNE(R / s), -Qp, Qp), the quotient compared exactly against the midpoints
+ *       (q +- 1/2) * s, so no intermediate rounding can move a code.
  *     A zero tensor gets s = 0 and all-zero codes.
  */
 #include <stdint.h>
@@ -41,6 +43,9 @@
 #include <string.h>
 #include <math.h>
 #include <fenv.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define HQO_F32 0
 #define HQO_F16 1
@@ -52,6 +57,15 @@
 #define HQO_ROT_BOTH 3
 
 int hqo_version(void) { return 1; }
+
+/* Threads the OpenMP loops of this library run on (1 when built without OpenMP). */
+int hqo_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
 
 static int is_pow2_le256(int k) { return k >= 1 && k <= 256 && (k & (k - 1)) == 0; }
 
@@ -163,40 +177,69 @@ int hqo_rotate(const double *V, int64_t rows, int64_t cols, int rot, int k, doub
   return 0;
 }
 
-/* [HALO Approach; INT4 §3.1] Tensor-wise scale, one per tensor.
- * ABSMAX: the value is rounded to fp32 first (the precision of the code decision), then
- *         a32 = max|v32| and s = fp32(a32 / Qp). Zero tensor -> 0.
- * The division is done in double and rounded once to fp32, which equals the correctly
- * rounded fp32 quotient of the two fp32 operands. */
-float hqo_absmax_scale(const double *R, int64_t n, int qp) {
-  float a32 = 0.0f;
-  for (int64_t i = 0; i < n; ++i) {
-    float v32 = (float)R[i];
-    float m = fabsf(v32);
-    if (m > a32) a32 = m;
+static int f32_odd(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return (int)(u & 1u);
+}
+
+/* Correctly rounded fp32 value of the exact quotient a / d (a >= 0 finite, d a small positive
+ * integer). Start from the double quotient rounded to fp32, then move to a neighbour while the
+ * exact quotient lies beyond the midpoint towards it (on the midpoint: to the even
+ * significand). A midpoint of two fp32 values has 25 significant bits, so midpoint * d is
+ * exact in double and every comparison is exact. */
+static float div_to_f32(double a, int d) {
+  float f = (float)(a / (double)d);
+  for (;;) {
+    const float up = nextafterf(f, INFINITY), dn = nextafterf(f, 0.0f);
+    const double hi = ((double)f + (double)up) * 0.5 * d;
+    const double lo = ((double)f + (double)dn) * 0.5 * d;
+    if (a > hi || (a == hi && f32_odd(f))) { f = up; continue; }
+    if (f > 0.0f && (a < lo || (a == lo && f32_odd(f)))) { f = dn; continue; }
+    return f;
   }
-  return (float)((double)a32 / (double)qp);
+}
+
+/* [HALO Approach; INT4 §3.1] Tensor-wise scale, one per tensor: a = max |R| over the exact
+ * rotated values, s = a / Qp correctly rounded to fp32. Zero tensor -> 0. */
+float hqo_absmax_scale(const double *R, int64_t n, int qp) {
+  double a = 0.0;
+  for (int64_t i = 0; i < n; ++i)
+    if (fabs(R[i]) > a) a = fabs(R[i]);
+  return div_to_f32(a, qp);
 }
 
 /* [INT4 §3.1; HALO Limitations] Round-to-nearest quantizer onto the symmetric grid [-Qp, Qp]:
- *   q = clamp(RNE(v32 * r), -Qp, Qp), r = fp32(1/s), product taken exactly (two fp32 values
- * multiply exactly in double). s == 0 gives all-zero codes. Returns 0. */
+ *   q = clamp(RNE(R / s), -Qp, Qp).
+ * The quotient is never rounded: for |R| < (Qp + 1) s the code q is found by exact
+ * comparisons of R against the midpoints (q - 1/2) s and (q + 1/2) s (each a product of a
+ * short dyadic and an fp32 value, exact in double); a value on a midpoint goes to the even
+ * neighbour. Beyond that range the clamp decides. s == 0 gives all-zero codes. Returns 0. */
 int hqo_quantize(const double *R, int64_t n, float scale, int qp, int8_t *q) {
   if (scale == 0.0f) {
     memset(q, 0, (size_t)n);
     return 0;
   }
-  float r = (float)(1.0 / (double)scale);
-  int old = fegetround();
-  fesetround(FE_TONEAREST);
+  const double s = (double)scale;
+  const double lim = ((double)qp + 1.0) * s;
   for (int64_t i = 0; i < n; ++i) {
-    float v32 = (float)R[i];
-    double t = nearbyint((double)v32 * (double)r);
-    if (t > qp) t = qp;
-    if (t < -qp) t = -qp;
-    q[i] = (int8_t)t;
+    const double v = R[i];
+    int c;
+    if (v >= lim) {
+      c = qp;
+    } else if (v <= -lim) {
+      c = -qp;
+    } else {
+      c = (int)(v / s);                                /* a start near the answer */
+      while (v > ((double)c + 0.5) * s) ++c;           /* now v <= (c + 1/2) s */
+      while (v < ((double)c - 0.5) * s) --c;           /* now (c - 1/2) s <= v <= (c + 1/2) s */
+      if (v == ((double)c + 0.5) * s && (c & 1)) ++c;  /* midpoint: the even neighbour */
+      if (v == ((double)c - 0.5) * s && (c & 1)) --c;
+      if (c > qp) c = qp;
+      if (c < -qp) c = -qp;
+    }
+    q[i] = (int8_t)c;
   }
-  fesetround(old);
   return 0;
 }
 

@@ -215,6 +215,24 @@ def test_fwht_validation(kw, expect):
 
 
 @pytest.mark.parametrize("kw,expect", [
+    (dict(path=3), "HQ_ERR_MODE"),
+    (dict(path=B.HQ_FWHT_MATRIX), "HQ_ERR_MODE"),                       # fp32: no matrix path
+    (dict(path=B.HQ_FWHT_MATRIX, src_dtype=B.HQ_BF16, dst_dtype=B.HQ_BF16, rows=64,
+          cols=512, k=8), "HQ_ERR_MODE"),                              # k < 16
+    (dict(path=B.HQ_FWHT_MATRIX, src_dtype=B.HQ_BF16, dst_dtype=B.HQ_BF16, rows=64,
+          cols=500, k=4), "HQ_ERR_MODE"),                              # partial tile
+    (dict(path=B.HQ_FWHT_MATRIX, src_dtype=B.HQ_BF16, dst_dtype=B.HQ_BF16, rows=64,
+          cols=512, k=32, src=FAKE + 2), "HQ_ERR_MODE"),               # unaligned
+    (dict(path=B.HQ_FWHT_BUTTERFLY, k=6), "HQ_ERR_K"),
+])
+def test_fwht_path_validation(kw, expect):
+    args = dict(src=FAKE, src_dtype=B.HQ_F32, dst=FAKE, dst_dtype=B.HQ_F32, rows=32, cols=64,
+                rot=B.HQ_ROT_RIGHT, k=32, path=B.HQ_FWHT_AUTO, stream=None)
+    args.update(kw)
+    assert B.STATUS_NAMES[B.hq_fwht_path(**args)] == expect
+
+
+@pytest.mark.parametrize("kw,expect", [
     (dict(lda=8), "HQ_ERR_SHAPE"),
     (dict(lda=72, K=64), "HQ_ERR_ALIGN"),
     (dict(a=FAKE_MIS), "HQ_ERR_ALIGN"),

@@ -125,22 +125,23 @@ def test_fwht_16bit_output_exact(k, rot, dt, ragged):
     np.testing.assert_array_equal(T.bits_of(dst), expect)
 
 
+@pytest.mark.parametrize("path", [B.HQ_FWHT_AUTO, B.HQ_FWHT_BUTTERFLY, B.HQ_FWHT_MATRIX])
 @pytest.mark.parametrize("k", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("dt", [B.HQ_BF16, B.HQ_F16])
 @pytest.mark.parametrize("rot", [B.HQ_ROT_RIGHT, B.HQ_ROT_LEFT])
-def test_fwht_matrix_core_exact(rot, k, dt):
-    """16-bit in = out on whole tiles (64 x 256 RIGHT, 256 x 64 LEFT): the transform runs on the
-    matrix cores (exact +-1 products, fp32 sums; RIGHT only for k >= 128, the VALU kernel
-    otherwise) and goes back through LDS. Small integers keep the sums exact, so every output is
-    the exact rotation rounded once, bit for bit."""
-    banner("fwht-mma", rot, k, dt)
+def test_fwht_matrix_core_exact(rot, k, dt, path):
+    """16-bit in = out on whole tiles (64 x 256 RIGHT, 256 x 64 LEFT), through each path of
+    hq_fwht_path: the matrix cores (exact +-1 products, fp32 sums, back through LDS), the VALU
+    butterflies, and the automatic choice. Small integers keep the sums exact, so every
+    output is the exact rotation rounded once, bit for bit, whichever path runs."""
+    banner("fwht-path", rot, k, dt, path)
     rng = np.random.default_rng(11 * k + dt + 3 * rot)
     rows, cols = (128, 512) if rot == B.HQ_ROT_RIGHT else (512, 192)
     V = rng.integers(-8, 9, size=(rows, cols)).astype(np.float64)
     src = T.device_tensor_from_bits(WL.to_dtype_bits(V, dt), dt, DEV)
     dst = torch.full((rows, cols), 7.0, dtype=T.TORCH_DT[dt], device=DEV)
-    B.check(B.hq_fwht(src.data_ptr(), dt, dst.data_ptr(), dt, rows, cols, rot, k,
-                      T.stream_ptr()), "fwht")
+    B.check(B.hq_fwht_path(src.data_ptr(), dt, dst.data_ptr(), dt, rows, cols, rot, k, path,
+                           T.stream_ptr()), "fwht")
     torch.cuda.synchronize()
     np.testing.assert_array_equal(T.bits_of(dst), WL.to_dtype_bits(O.rotate(V, rot, k), dt))
 
@@ -484,3 +485,90 @@ def test_layer_empty_tokens():
     layer.bwd_weight(dw)
     torch.cuda.synchronize()
     assert float(dw.abs().max()) == 0.0
+
+
+# ------------------------------------------- grid-aligned inputs: exact end to end
+def _blockdiag_h(n, k):
+    return np.kron(np.eye(n // k, dtype=np.int64), O.hadamard(k).astype(np.int64))
+
+
+def _ternary(rng, shape, density):
+    """Entries in {-1, 0, 1}, nonzero with the given probability."""
+    return rng.choice([-1, 0, 1], size=shape, p=[density / 2, 1 - density, density / 2])
+
+
+def _run_exact_layer(cfg, xv, wv, gv, dt):
+    """One layer step on exactly representable inputs (values given as float64), fp32 outputs."""
+    inputs = {"x": WL.to_dtype_bits(xv, dt), "w": WL.to_dtype_bits(wv, dt),
+              "dy": WL.to_dtype_bits(gv, dt)}
+    for name, v in (("x", xv), ("w", wv), ("dy", gv)):
+        np.testing.assert_array_equal(O.decode(inputs[name], dt), v)   # exact in the dtype
+    cfg = dict(cfg, in_dtype=dt)
+    res = run_gpu(cfg, inputs, out_dt=O.F32)
+    return host(res, O.F32)
+
+
+@pytest.mark.parametrize("k", [16, 128])
+@pytest.mark.parametrize("dt", [B.HQ_BF16, B.HQ_F32])
+def test_grid_aligned_hq_step_exact(k, dt):
+    """HQ (right rotations, dY unrotated) on inputs built so that every rotated value is an
+    integer and max |X B| = max |W B| = max |dY| = Qp: rotation -> absmax -> quantize must give
+    those integers with s = 1 exactly (bit for bit), and since H H^T = k I, Y = X W^T,
+    dX = dY W and dW = dY^T X exactly (INT4 page, §3.3). X and W are ternary, plus one k-block
+    of 127/k per tensor, which rotates to 127 e_0; all sums stay far below 2^24, so the fp32
+    sums of the kernels are exact. bf16 inputs take the matrix-core prologue, fp32 the VALU one."""
+    banner("grid-aligned-hq", k, dt)
+    rng = np.random.default_rng(900 + k + dt)
+    N, C, D = 512, 512, 256
+    X = _ternary(rng, (N, C), 0.3).astype(np.float64)
+    W = _ternary(rng, (D, C), 0.3).astype(np.float64)
+    G = rng.integers(-3, 4, size=(N, D)).astype(np.float64)
+    X[0, :k] = 127.0 / k
+    W[3, k:2 * k] = -127.0 / k
+    G[5, 7] = 127.0
+    Hc = _blockdiag_h(C, k)
+    A, Bm = X @ Hc, W @ Hc                       # integer rotated values
+    assert np.abs(A).max() == 127 and np.abs(Bm).max() == 127
+    cfg = WL.config(2, N=N, C=C, D=D, k=k, variant=B.HQ_VARIANT_HQ)
+    h = _run_exact_layer(cfg, X, W, G, dt)
+    np.testing.assert_array_equal(h["qx"], A)
+    np.testing.assert_array_equal(h["qw"], Bm)
+    np.testing.assert_array_equal(h["qg"], G)
+    assert h["sx"] == h["sw"] == h["sg"] == 1.0
+    np.testing.assert_array_equal(h["y"], X @ W.T)
+    np.testing.assert_array_equal(h["dx"], G @ W)
+    np.testing.assert_array_equal(h["dw"], G.T @ X)
+
+
+@pytest.mark.parametrize("k", [16, 64])
+@pytest.mark.parametrize("dt", [B.HQ_BF16, B.HQ_F32])
+def test_grid_aligned_halo2_backward_exact(k, dt):
+    """HALO-2 backward on inputs whose rotated values are integers with max Qp: qG = Q(B_N dY),
+    qXt = Q(B_N X B_C) and qW = Q(W B_C) are those integers with s = 1 (bit for bit), and the
+    two backward products come out exactly: dX = B_N (qG qW) B_C / k^2 = dY W and
+    dW = (qG^T qXt) B_C / k^2 = dY^T X (HALO page, Approach; INT4 page, §3.3). The forward
+    output is checked against the oracle as usual."""
+    banner("grid-aligned-halo2", k, dt)
+    rng = np.random.default_rng(950 + k + dt)
+    N, C, D = 512, 512, 256
+    X = _ternary(rng, (N, C), min(0.2, 3.0 / k)).astype(np.float64)
+    W = _ternary(rng, (D, C), 0.3).astype(np.float64)
+    G = _ternary(rng, (N, D), 0.3).astype(np.float64)
+    X[:k, :k] = 127.0 / (k * k)                  # B X B = 127 e_0 e_0^T on this block
+    W[3, k:2 * k] = -127.0 / k
+    G[k:2 * k, 9] = 127.0 / k                    # B G = 127 at row k, column 9
+    Hn, Hc = _blockdiag_h(N, k), _blockdiag_h(C, k)
+    Axt, Ag, Aw = Hn @ X @ Hc, Hn @ G, W @ Hc
+    for a in (Axt, Ag, Aw):
+        assert np.abs(a).max() == 127
+    cfg = WL.config(2, N=N, C=C, D=D, k=k)
+    h = _run_exact_layer(cfg, X, W, G, dt)
+    np.testing.assert_array_equal(h["qxt_t"].T, Axt)
+    np.testing.assert_array_equal(h["qg"], Ag)
+    np.testing.assert_array_equal(h["qw"], Aw)
+    assert h["sxt"] == h["sg"] == h["sw"] == 1.0
+    np.testing.assert_array_equal(h["dx"], G @ W)
+    np.testing.assert_array_equal(h["dw"], G.T @ X)
+    ora = O.linear(X, W, G, k, 8, O.HALO2)
+    assert_codes(h["qx"], ora["qx"], "qX")
+    assert rel_fro(h["y"], ora["y"]) <= 1e-3

@@ -177,6 +177,41 @@ def test_quantizer_step_golden(golden):
     assert s == np.float32(ex["step"])
 
 
+def test_quantizer_exact_division_near_tie_golden(golden):
+    """Codes are RNE of the exact quotient V/s, not of V times a rounded reciprocal: the
+    hand-derived case has s = 3 and exact midpoints that fp32(1/3) would push up."""
+    g = golden["near_tie_exact_division_k2"]
+    X = np.array(g["x"], dtype=np.float64)
+    R = O.rotate(X, O.ROT_RIGHT, g["k"])
+    np.testing.assert_array_equal(R, np.array(g["xb"], dtype=np.float64))
+    q, s = O.quantize_tensor(X, O.ROT_RIGHT, g["k"], g["bits"])
+    assert s == np.float32(g["s"])
+    np.testing.assert_array_equal(q, np.array(g["qx"]))
+    sc = g["step_case"]
+    v = np.array(sc["v"], dtype=np.float64)[None, :]
+    q, s = O.quantize_tensor(v, O.ROT_NONE, 1, sc["bits"], O.STEP, sc["step"])
+    np.testing.assert_array_equal(q[0], np.array(sc["codes"]))
+
+
+def test_absmax_scale_correctly_rounded():
+    """s = a/Qp rounded once to fp32, checked against exact Fractions on values whose
+    quotient lands near an fp32 midpoint (where rounding through double could slip)."""
+    from fractions import Fraction
+    rng = np.random.default_rng(5)
+    for _ in range(300):
+        f = np.float32(rng.uniform(0.5, 2.0)) * np.float32(2.0 ** rng.integers(-20, 20))
+        up = np.nextafter(f, np.float32(np.inf))
+        mid = (Fraction(float(f)) + Fraction(float(up))) / 2
+        qp = int(rng.choice([7, 127]))
+        a = float(mid * qp)   # the double nearest a midpoint times Qp
+        s = O.absmax_scale(np.array([[a, -a / 3]]), qp)
+        exact = Fraction(a) / qp
+        cands = [f, up, np.nextafter(f, np.float32(0)), np.nextafter(up, np.float32(np.inf))]
+        best = min(cands, key=lambda c: (abs(Fraction(float(c)) - exact),
+                                         int(np.array(c).view(np.uint32)) & 1))
+        assert s == best, (a, qp, s, best)
+
+
 def test_quantizer_ties_to_even():
     v = np.array([2.5, 3.5, -2.5, 0.5, -0.5, 1.5, 126.5, -126.5])
     q = O.quantize(v, 1.0, 127)
@@ -300,12 +335,19 @@ def test_brute_force_pipeline_tiny():
     wr = [[sum(Fraction(W[i, t]) * int(Hb[t, j]) for t in range(C)) for j in range(C)]
           for i in range(D)]
 
+    def f32_nearest(q):
+        """Correctly rounded fp32 value of the Fraction q >= 0, by brute force over the
+        neighbours of a first guess (ties to the even significand)."""
+        f0 = np.float32(float(q))
+        cands = [np.nextafter(f0, np.float32(-1)), f0, np.nextafter(f0, np.float32(np.inf))]
+        return min(cands, key=lambda f: (abs(Fraction(float(f)) - q),
+                                         int(np.array(f).view(np.uint32)) & 1))
+
     def codes(R):
-        a = max(abs(np.float32(float(v))) for row in R for v in row)
-        s = np.float32(float(a) / 127)
-        r = np.float32(1.0 / float(s))
-        q = [[int(np.clip(round(Fraction(float(np.float32(float(v)))) * Fraction(float(r))),
-                          -127, 127)) for v in row] for row in R]
+        a = max(abs(v) for row in R for v in row)          # exact max |R|
+        s = f32_nearest(a / 127)                           # s = a / Qp, one fp32 rounding
+        q = [[int(np.clip(round(v / Fraction(float(s))), -127, 127)) for v in row]
+             for row in R]                                 # RNE of the exact quotient
         return np.array(q), s
 
     qx, sx = codes(xr)
