@@ -229,7 +229,7 @@ def main():
                          "largest layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=128)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=768)
     ap.add_argument("--check-configs", type=str, default="4,2",
                     help="also time these workloads' steps against three bf16 GEMMs (default "
                          "4,2: the Llama-7B-shaped MLP layer and the 2048 x 4096 x 4096 layer); "
