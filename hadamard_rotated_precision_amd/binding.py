@@ -22,9 +22,9 @@ HQ_VARIANT_HALO0, HQ_VARIANT_HQ, HQ_VARIANT_HALO2 = 0, 1, 2
 HQ_FWHT_AUTO, HQ_FWHT_BUTTERFLY, HQ_FWHT_MATRIX = 0, 1, 2
 
 EXPORTS = ["hq_abi_version", "hq_status_string", "hq_code_pitch", "hq_workspace_bytes",
-           "hq_rotate_quantize", "hq_linear_fwd", "hq_linear_bwd_input", "hq_linear_bwd_weight",
-           "hq_fwht", "hq_fwht_path", "hq_gemm_i8_i32", "hq_profile_start", "hq_profile_stop",
-           "hq_profile_records"]
+           "hq_rotate_quantize", "hq_linear_fwd", "hq_linear_fwd_noalloc", "hq_linear_bwd_input",
+           "hq_linear_bwd_weight", "hq_fwht", "hq_fwht_path", "hq_gemm_i8_i32",
+           "hq_profile_start", "hq_profile_stop", "hq_profile_records"]
 HQ_KIND_GEMM, HQ_KIND_ROT_ABSMAX, HQ_KIND_ROT_QUANT, HQ_KIND_ROT_STORE = 0, 1, 2, 3
 HQ_KIND_TRANSPOSE, HQ_KIND_MISC, HQ_KIND_COUNT = 4, 5, 6
 KIND_NAMES = ["gemm", "rot_absmax", "rot_quant", "rot_store", "transpose", "misc"]
@@ -94,6 +94,9 @@ def load(build_if_missing=True):
     lib.hq_linear_fwd.restype = i32
     lib.hq_linear_fwd.argtypes = [vp, vp, i32, i64, i64, i64, P(hq_config), vp, vp, vp, vp, i32,
                                   P(hq_qtensor), P(hq_qtensor), P(hq_qtensor), vp, sz, vp]
+    lib.hq_linear_fwd_noalloc.restype = i32
+    lib.hq_linear_fwd_noalloc.argtypes = [vp, vp, i32, i64, i64, i64, P(hq_config), vp, vp, vp,
+                                          vp, i32, P(hq_qtensor), P(hq_qtensor), P(hq_qtensor), vp]
     lib.hq_linear_bwd_input.restype = i32
     lib.hq_linear_bwd_input.argtypes = [vp, i32, i64, i64, i64, P(hq_config), vp, P(hq_qtensor),
                                         vp, i32, P(hq_qtensor), vp, sz, vp]
@@ -147,6 +150,13 @@ def hq_linear_fwd(x, w, in_dtype, N, C, D, cfg, step_x, step_w, step_xt, y, y_dt
     return load().hq_linear_fwd(x, w, in_dtype, N, C, D, _ref(cfg), step_x, step_w, step_xt, y,
                                 y_dtype, _ref(save_x), _ref(save_xt), _ref(save_w), ws,
                                 ws_bytes, stream)
+
+
+def hq_linear_fwd_noalloc(x, w, in_dtype, N, C, D, cfg, step_x, step_w, step_xt, y, y_dtype,
+                          save_x, save_xt, save_w, stream):
+    return load().hq_linear_fwd_noalloc(x, w, in_dtype, N, C, D, _ref(cfg), step_x, step_w,
+                                        step_xt, y, y_dtype, _ref(save_x), _ref(save_xt),
+                                        _ref(save_w), stream)
 
 
 def hq_linear_bwd_input(dy, dy_dtype, N, C, D, cfg, step_g, saved_w, dx, dx_dtype, save_g, ws,

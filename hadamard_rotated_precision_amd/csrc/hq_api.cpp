@@ -300,11 +300,18 @@ hq_status hq_rotate_quantize(const void* src, int32_t src_dtype, int64_t rows, i
   return HQ_OK;
 }
 
-hq_status hq_linear_fwd(const void* x, const void* w, int32_t in_dtype, int64_t N, int64_t C,
-                        int64_t D, const hq_config* cfg, const float* step_x,
-                        const float* step_w, const float* step_xt, void* y, int32_t y_dtype,
-                        hq_qtensor* save_x, hq_qtensor* save_xt, hq_qtensor* save_w, void* ws,
-                        size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace hq {
+
+size_t fwd_workspace_bytes() { return ws_need(); }
+
+// Argument checks of hq_linear_fwd (all but the workspace), before any HIP call.
+hq_status fwd_validate(const void* x, const void* w, int32_t in_dtype, int64_t N, int64_t C,
+                       int64_t D, const hq_config* cfg, const float* step_x,
+                       const float* step_w, const float* step_xt, const void* y,
+                       int32_t y_dtype, const hq_qtensor* save_x, const hq_qtensor* save_xt,
+                       const hq_qtensor* save_w) {
   HQ_CHECK(check_cfg(cfg));
   if (!valid_dt(in_dtype) || !valid_dt(y_dtype)) return HQ_ERR_DTYPE;
   if (N < 0 || C < 0 || D < 0) return HQ_ERR_SHAPE;
@@ -323,8 +330,17 @@ hq_status hq_linear_fwd(const void* x, const void* w, int32_t in_dtype, int64_t 
     if (!save_xt->scale || (!save_xt->codes_t && N * C > 0)) return HQ_ERR_NULL;
     HQ_CHECK(check_pitches(save_xt, N, C));
   }
-  HQ_CHECK(check_ws(ws, ws_bytes, hq_workspace_bytes(cfg, N, C, D)));
-  HQ_CHECK(device_ok());
+  return HQ_OK;
+}
+
+// The launches of the forward on a validated call; ws holds at least fwd_workspace_bytes().
+hq_status fwd_run(const void* x, const void* w, int32_t in_dtype, int64_t N, int64_t C,
+                  int64_t D, const hq_config* cfg, const float* step_x, const float* step_w,
+                  const float* step_xt, void* y, int32_t y_dtype, hq_qtensor* save_x,
+                  hq_qtensor* save_xt, hq_qtensor* save_w, void* ws, void* stream) {
+  const int32_t v = cfg->variant, k = cfg->k;
+  const bool want_xt = (v == HQ_VARIANT_HALO2) && save_xt != nullptr;
+  const bool stepm = cfg->scale_mode == HQ_SCALE_STEP;
   hipStream_t st = static_cast<hipStream_t>(stream);
   Ws wsp(ws);
   const int32_t rx = x_rot(v);
@@ -379,6 +395,25 @@ hq_status hq_linear_fwd(const void* x, const void* w, int32_t in_dtype, int64_t 
   g.kmul = (v == HQ_VARIANT_HALO0) ? 1.0f : 1.0f / static_cast<float>(k);
   HQ_TRY(hq::gemm_pass(g, st));
   return HQ_OK;
+}
+
+hq_status device_ready() { return device_ok(); }
+
+}  // namespace hq
+
+extern "C" {
+
+hq_status hq_linear_fwd(const void* x, const void* w, int32_t in_dtype, int64_t N, int64_t C,
+                        int64_t D, const hq_config* cfg, const float* step_x,
+                        const float* step_w, const float* step_xt, void* y, int32_t y_dtype,
+                        hq_qtensor* save_x, hq_qtensor* save_xt, hq_qtensor* save_w, void* ws,
+                        size_t ws_bytes, void* stream) {
+  HQ_CHECK(hq::fwd_validate(x, w, in_dtype, N, C, D, cfg, step_x, step_w, step_xt, y, y_dtype,
+                            save_x, save_xt, save_w));
+  HQ_CHECK(check_ws(ws, ws_bytes, hq_workspace_bytes(cfg, N, C, D)));
+  HQ_CHECK(device_ok());
+  return hq::fwd_run(x, w, in_dtype, N, C, D, cfg, step_x, step_w, step_xt, y, y_dtype, save_x,
+                     save_xt, save_w, ws, stream);
 }
 
 hq_status hq_linear_bwd_input(const void* dy, int32_t dy_dtype, int64_t N, int64_t C, int64_t D,

@@ -5,7 +5,25 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/hq.h"
+
 namespace hq {
+
+// The forward of hq_linear_fwd in two halves (hq_api.cpp), shared with the entry point that
+// brings its own scratch: fwd_validate runs every argument check except the workspace's;
+// fwd_run launches the passes on a validated call with a workspace of at least
+// fwd_workspace_bytes() bytes. device_ready: HQ_OK when the current device is usable.
+size_t fwd_workspace_bytes();
+hq_status fwd_validate(const void* x, const void* w, int32_t in_dtype, int64_t N, int64_t C,
+                       int64_t D, const hq_config* cfg, const float* step_x,
+                       const float* step_w, const float* step_xt, const void* y,
+                       int32_t y_dtype, const hq_qtensor* save_x, const hq_qtensor* save_xt,
+                       const hq_qtensor* save_w);
+hq_status fwd_run(const void* x, const void* w, int32_t in_dtype, int64_t N, int64_t C,
+                  int64_t D, const hq_config* cfg, const float* step_x, const float* step_w,
+                  const float* step_xt, void* y, int32_t y_dtype, hq_qtensor* save_x,
+                  hq_qtensor* save_xt, hq_qtensor* save_w, void* ws, void* stream);
+hq_status device_ready();
 
 // OP_STORE: the transform alone, rotated values written in the input dtype (hq_fwht).
 enum Op : int { OP_ABSMAX = 0, OP_QUANT = 1, OP_STORE = 2 };

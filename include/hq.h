@@ -162,6 +162,22 @@ hq_status hq_linear_fwd(const void *x, const void *w, int32_t in_dtype, int64_t 
                         hq_qtensor *save_x, hq_qtensor *save_xt, hq_qtensor *save_w,
                         void *ws, size_t ws_bytes, void *stream);
 
+/* hq_linear_fwd without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * Arguments, results and errors are those of hq_linear_fwd, whose kernels it runs; the
+ * forward's scratch (absmax partials and grid-barrier words, under 20 KiB for any shape) lives
+ * in a fixed device array of this library, one per GPU, held until the process ends. The first
+ * call on a device looks the array's address up (no allocation); no call allocates or frees.
+ * HQ_ERR_WORKSPACE if the forward ever needed more scratch than the array holds.
+ * Calls that overlap on one GPU share that array and race: serialize them (one stream, or
+ * events between streams). The array keeps the last call's contents; every call writes the
+ * parts it reads before reading them. */
+hq_status hq_linear_fwd_noalloc(const void *x, const void *w, int32_t in_dtype, int64_t N,
+                                int64_t C, int64_t D, const hq_config *cfg,
+                                const float *step_x, const float *step_w, const float *step_xt,
+                                void *y, int32_t y_dtype, hq_qtensor *save_x,
+                                hq_qtensor *save_xt, hq_qtensor *save_w, void *stream);
+
 /* Input gradient dX = dY W (INT4 page §4; HALO page, Approach).
  *   dy        N x D, dtype dy_dtype
  *   step_g    STEP mode: device float

@@ -143,6 +143,23 @@ def test_linear_fwd_validation(kw, expect):
     assert B.STATUS_NAMES[fwd(**kw)] == expect
 
 
+@pytest.mark.parametrize("kw,expect", [
+    (dict(C=48), "HQ_ERR_SHAPE"),
+    (dict(y_dtype=5), "HQ_ERR_DTYPE"),
+    (dict(save_x=None), "HQ_ERR_NULL"),
+    (dict(cfg=cfg(k=12)), "HQ_ERR_K"),
+    (dict(save_w=qt(96, 64, ld_t=72)), "HQ_ERR_ALIGN"),
+])
+def test_linear_fwd_noalloc_validation(kw, expect):
+    """The no-allocation forward runs the same argument checks, before it looks up its
+    scratch array or touches the device."""
+    args = dict(x=FAKE, w=FAKE, in_dtype=B.HQ_BF16, N=64, C=64, D=96, cfg=cfg(), step_x=None,
+                step_w=None, step_xt=None, y=FAKE, y_dtype=B.HQ_BF16, save_x=qt(64, 64),
+                save_xt=qt(64, 64, rot=B.HQ_ROT_BOTH), save_w=qt(96, 64), stream=None)
+    args.update(kw)
+    assert B.STATUS_NAMES[B.hq_linear_fwd_noalloc(**args)] == expect
+
+
 def test_linear_fwd_halo2_without_xt_is_allowed_before_device():
     # N = 48 is fine when the weight-gradient codes are not requested; the call then reaches
     # the device check, which fails on a machine without a gfx950 GPU.
