@@ -15,6 +15,10 @@ layer, in the order the pages give them:
   in forward, left rotation on output gradients in backward = HALO-2, tensor-wise scales,
   reuse of quantized rotated tensors).
 
+Code formats: INT (integers on [-Qp, Qp], Qp = 127 or 7) and E4M3 (FP8 codes, the HALO
+page's lower-precision variants: s = max|R| / 448, nearest E4M3 value of R / s, ties to even,
+saturating; products exact in int64 units of 2^-18).
+
 Variants (names follow the HALO page):
   HALO0: no rotation.
   HQ   : X, W rotated on the right; dY quantized unrotated; backward reuses qW and qX.
@@ -36,6 +40,9 @@ F32, F16, BF16 = 0, 1, 2
 ROT_NONE, ROT_RIGHT, ROT_LEFT, ROT_BOTH = 0, 1, 2, 3
 HALO0, HQ, HALO2 = 0, 1, 2
 ABSMAX, STEP = 0, 1
+INT, E4M3 = 0, 1          # code formats: integers on [-Qp, Qp], or FP8 E4M3 values
+E4M3_MAX = 448            # largest finite E4M3 value: the grid bound of the FP8 format
+E4M3_UNIT_EXP = 18        # an FP8 product is an integer number of 2^-18
 
 _lib = None
 
@@ -65,10 +72,16 @@ def _load():
     lib.hqo_gemm_i8.restype = i32
     lib.hqo_rotate_i64.argtypes = [vp, i64, i64, i32, i32, vp]
     lib.hqo_rotate_i64.restype = i32
-    lib.hqo_dequant.argtypes = [vp, i64, f32, f32, i32, vp]
+    lib.hqo_dequant.argtypes = [vp, i64, f32, f32, ctypes.c_double, vp]
     lib.hqo_dequant.restype = None
     lib.hqo_round.argtypes = [vp, i64, i32, vp]
     lib.hqo_round.restype = i32
+    lib.hqo_decode_e4m3.argtypes = [vp, i64, vp]
+    lib.hqo_decode_e4m3.restype = None
+    lib.hqo_quantize_e4m3.argtypes = [vp, i64, f32, vp]
+    lib.hqo_quantize_e4m3.restype = i32
+    lib.hqo_gemm_f8.argtypes = [vp, i64, i64, vp, i64, i64, i64, i64, i64, vp]
+    lib.hqo_gemm_f8.restype = i32
     _lib = lib
     return lib
 
@@ -82,8 +95,13 @@ def _p(a):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
-def qmax(bits):
-    """Symmetric grid bound: 127 for INT8, 7 for the INT4 range (INT4 page, §3.1)."""
+def qmax(bits, fmt=INT):
+    """Symmetric grid bound: 127 for INT8, 7 for the INT4 range (INT4 page, §3.1), 448 for
+    FP8 E4M3 codes."""
+    if fmt == E4M3:
+        if bits != 8:
+            raise ValueError("E4M3 codes are 8 bits")
+        return E4M3_MAX
     if bits == 8:
         return 127
     if bits == 4:
@@ -147,12 +165,43 @@ def rotate_i64(T, rot, k):
     return R
 
 
-def dequant(T, s_a, s_b, k_pow_e):
+def dequant(T, s_a, s_b, k_pow_e, fmt=INT):
+    """T * s_a * s_b / k^e (FP8 sums are in units of 2^-18: that factor is applied too)."""
     T = np.ascontiguousarray(T, dtype=np.int64)
     out = np.empty(T.shape, dtype=np.float64)
-    _load().hqo_dequant(_p(T), T.size, float(np.float32(s_a)), float(np.float32(s_b)),
-                        int(k_pow_e), _p(out))
+    div = float(k_pow_e) * (2.0 ** E4M3_UNIT_EXP if fmt == E4M3 else 1.0)
+    _load().hqo_dequant(_p(T), T.size, float(np.float32(s_a)), float(np.float32(s_b)), div,
+                        _p(out))
     return out
+
+
+def decode_e4m3(q):
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    out = np.empty(q.shape, dtype=np.float64)
+    _load().hqo_decode_e4m3(_p(q), q.size, _p(out))
+    return out
+
+
+def quantize_e4m3(R, scale):
+    """E4M3 codes (uint8) nearest to R / scale, ties to even, saturating at +-448."""
+    R = np.ascontiguousarray(R, dtype=np.float64)
+    q = np.empty(R.shape, dtype=np.uint8)
+    _load().hqo_quantize_e4m3(_p(R), R.size, float(np.float32(scale)), _p(q))
+    return q
+
+
+def gemm_f8(A, sam, sak, B, sbk, sbn, M, N, K):
+    """Exact product of E4M3 code matrices in int64 units of 2^-18 (same index maps as
+    gemm_i8)."""
+    A = np.ascontiguousarray(A, dtype=np.uint8)
+    B = np.ascontiguousarray(B, dtype=np.uint8)
+    C = np.empty((M, N), dtype=np.int64)
+    _load().hqo_gemm_f8(_p(A), sam, sak, _p(B), sbk, sbn, M, N, K, _p(C))
+    return C
+
+
+def _gemm(fmt, *args):
+    return gemm_f8(*args) if fmt == E4M3 else gemm_i8(*args)
 
 
 def round_to(vals, dtype):
@@ -165,10 +214,10 @@ def round_to(vals, dtype):
 
 
 # ------------------------------------------------------------ composed steps
-def quantize_tensor(V, rot, k, bits, mode=ABSMAX, step=None):
+def quantize_tensor(V, rot, k, bits, mode=ABSMAX, step=None, fmt=INT):
     """Rotate -> tensor-wise scale -> codes. V is float64 (already decoded).
-    Returns (codes int8, scale float32)."""
-    qp = qmax(bits)
+    Returns (codes: int8, or uint8 E4M3 codes for fmt E4M3; scale: float32)."""
+    qp = qmax(bits, fmt)
     R = rotate(V, rot, k)
     if mode == ABSMAX:
         s = absmax_scale(R, qp)
@@ -178,6 +227,8 @@ def quantize_tensor(V, rot, k, bits, mode=ABSMAX, step=None):
         s = np.float32(step)
     else:
         raise ValueError("bad scale mode")
+    if fmt == E4M3:
+        return quantize_e4m3(R, s), s
     return quantize(R, s, qp), s
 
 
@@ -192,28 +243,28 @@ def _rots(variant):
     raise ValueError("bad variant")
 
 
-def quantize_x(X, k, bits, variant, mode=ABSMAX, step=None, step_xt=None):
+def quantize_x(X, k, bits, variant, mode=ABSMAX, step=None, step_xt=None, fmt=INT):
     """Forward-pass codes of X: qX (forward operand) and, for the weight gradient, the codes
     of X in the rotation that product needs (qXt under HALO2, qX otherwise)."""
     rx, _, rxt = _rots(variant)
-    qx, sx = quantize_tensor(X, rx, k, bits, mode, step)
+    qx, sx = quantize_tensor(X, rx, k, bits, mode, step, fmt)
     if rxt == rx:
         return qx, sx, qx, sx
-    qxt, sxt = quantize_tensor(X, rxt, k, bits, mode, step if step_xt is None else step_xt)
+    qxt, sxt = quantize_tensor(X, rxt, k, bits, mode, step if step_xt is None else step_xt, fmt)
     return qx, sx, qxt, sxt
 
 
-def quantize_w(W, k, bits, variant, mode=ABSMAX, step=None):
+def quantize_w(W, k, bits, variant, mode=ABSMAX, step=None, fmt=INT):
     rx, _, _ = _rots(variant)
-    return quantize_tensor(W, rx, k, bits, mode, step)
+    return quantize_tensor(W, rx, k, bits, mode, step, fmt)
 
 
-def quantize_g(G, k, bits, variant, mode=ABSMAX, step=None):
+def quantize_g(G, k, bits, variant, mode=ABSMAX, step=None, fmt=INT):
     _, rg, _ = _rots(variant)
-    return quantize_tensor(G, rg, k, bits, mode, step)
+    return quantize_tensor(G, rg, k, bits, mode, step, fmt)
 
 
-def fwd_from_codes(qx, sx, qw, sw, k, variant, rows=None, cols=None):
+def fwd_from_codes(qx, sx, qw, sw, k, variant, rows=None, cols=None, fmt=INT):
     """Y[rows][cols] = (qX qW^T) sX sW / k^e in double. rows/cols: optional index ranges
     (slices) for a sampled block."""
     e = 0 if variant == HALO0 else 1
@@ -223,11 +274,11 @@ def fwd_from_codes(qx, sx, qw, sw, k, variant, rows=None, cols=None):
     B = np.ascontiguousarray(qw[cols])
     M, K = A.shape
     N = B.shape[0]
-    T = gemm_i8(A, K, 1, B, 1, K, M, N, K)
-    return dequant(T, sx, sw, k ** e)
+    T = _gemm(fmt, A, K, 1, B, 1, K, M, N, K)
+    return dequant(T, sx, sw, k ** e, fmt)
 
 
-def bwd_input_from_codes(qg, sg, qw, sw, k, variant, row_block=None, col_block=None):
+def bwd_input_from_codes(qg, sg, qw, sw, k, variant, row_block=None, col_block=None, fmt=INT):
     """dX = [B_N] (qG qW) [B_C] sG sW / k^e in double. row_block/col_block: optional
     (start, length) ranges aligned to k for a sampled block (the inverse rotations only
     mix within k-blocks, so an aligned block is self-contained)."""
@@ -237,7 +288,7 @@ def bwd_input_from_codes(qg, sg, qw, sw, k, variant, row_block=None, col_block=N
     c0, cl = (0, C) if col_block is None else col_block
     A = np.ascontiguousarray(qg[r0:r0 + rl])
     Bm = np.ascontiguousarray(qw[:, c0:c0 + cl])
-    T = gemm_i8(A, D, 1, Bm, cl, 1, rl, cl, D)
+    T = _gemm(fmt, A, D, 1, Bm, cl, 1, rl, cl, D)
     if variant == HALO2:
         T = rotate_i64(T, ROT_BOTH, k)
         e = 2
@@ -246,10 +297,10 @@ def bwd_input_from_codes(qg, sg, qw, sw, k, variant, row_block=None, col_block=N
         e = 1
     else:
         e = 0
-    return dequant(T, sg, sw, k ** e)
+    return dequant(T, sg, sw, k ** e, fmt)
 
 
-def bwd_weight_from_codes(qg, sg, qxt, sxt, k, variant, row_block=None, col_block=None):
+def bwd_weight_from_codes(qg, sg, qxt, sxt, k, variant, row_block=None, col_block=None, fmt=INT):
     """dW = (qG^T qXt) [B_C] sG sXt / k^e in double (qXt = Q(B_N X B_C) under HALO2,
     qX = Q(X B_C) under HQ, Q(X) under HALO0)."""
     N, D = qg.shape
@@ -258,7 +309,7 @@ def bwd_weight_from_codes(qg, sg, qxt, sxt, k, variant, row_block=None, col_bloc
     c0, cl = (0, C) if col_block is None else col_block
     A = np.ascontiguousarray(qg[:, r0:r0 + rl])   # N x rl, contraction over tokens
     Bm = np.ascontiguousarray(qxt[:, c0:c0 + cl])  # N x cl
-    T = gemm_i8(A, 1, rl, Bm, cl, 1, rl, cl, N)
+    T = _gemm(fmt, A, 1, rl, Bm, cl, 1, rl, cl, N)
     if variant == HALO2:
         T = rotate_i64(T, ROT_RIGHT, k)
         e = 2
@@ -267,24 +318,26 @@ def bwd_weight_from_codes(qg, sg, qxt, sxt, k, variant, row_block=None, col_bloc
         e = 1
     else:
         e = 0
-    return dequant(T, sg, sxt, k ** e)
+    return dequant(T, sg, sxt, k ** e, fmt)
 
 
-def linear(X, W, dY, k, bits, variant, mode=ABSMAX, steps=None, passes=("fwd", "dx", "dw")):
+def linear(X, W, dY, k, bits, variant, mode=ABSMAX, steps=None, passes=("fwd", "dx", "dw"),
+           fmt=INT):
     """Whole linear layer from decoded float64 inputs. steps: dict with 'x', 'w', 'g' (and
-    'xt') steps for STEP mode. Returns a dict of codes, scales and double outputs."""
+    'xt') steps for STEP mode. fmt: INT codes or FP8 E4M3 codes. Returns a dict of codes,
+    scales and double outputs."""
     steps = steps or {}
     out = {}
-    qx, sx, qxt, sxt = quantize_x(X, k, bits, variant, mode, steps.get("x"), steps.get("xt"))
-    qw, sw = quantize_w(W, k, bits, variant, mode, steps.get("w"))
+    qx, sx, qxt, sxt = quantize_x(X, k, bits, variant, mode, steps.get("x"), steps.get("xt"), fmt)
+    qw, sw = quantize_w(W, k, bits, variant, mode, steps.get("w"), fmt)
     out.update(qx=qx, sx=sx, qxt=qxt, sxt=sxt, qw=qw, sw=sw)
     if "fwd" in passes:
-        out["y"] = fwd_from_codes(qx, sx, qw, sw, k, variant)
+        out["y"] = fwd_from_codes(qx, sx, qw, sw, k, variant, fmt=fmt)
     if dY is not None and ("dx" in passes or "dw" in passes):
-        qg, sg = quantize_g(dY, k, bits, variant, mode, steps.get("g"))
+        qg, sg = quantize_g(dY, k, bits, variant, mode, steps.get("g"), fmt)
         out.update(qg=qg, sg=sg)
         if "dx" in passes:
-            out["dx"] = bwd_input_from_codes(qg, sg, qw, sw, k, variant)
+            out["dx"] = bwd_input_from_codes(qg, sg, qw, sw, k, variant, fmt=fmt)
         if "dw" in passes:
-            out["dw"] = bwd_weight_from_codes(qg, sg, qxt, sxt, k, variant)
+            out["dw"] = bwd_weight_from_codes(qg, sg, qxt, sxt, k, variant, fmt=fmt)
     return out

@@ -37,6 +37,14 @@
  *       q = clamp(RNE(R / s), -Qp, Qp), the quotient compared exactly against the midpoints
  *       (q +- 1/2) * s, so no intermediate rounding can move a code.
  *     A zero tensor gets s = 0 and all-zero codes.
+ *   - FP8 codes (HALO page: the variants that run all three matmuls in FP8/FP6; an FP8 grid is
+ *     used where FP6 hardware is missing, Limitations) are the OCP E4M3 format: sign, 4-bit
+ *     exponent with bias 7, 3-bit mantissa, subnormals m * 2^-9, largest finite value 448, and
+ *     the code 0x7F / 0xFF reserved (not a number). The tensor-wise scale is s = max|R| / 448 and
+ *     a code is the E4M3 value nearest to R / s, ties to the even mantissa, saturating at
+ *     +-448; a value that rounds to zero keeps its sign bit. Every E4M3 value is an integer
+ *     multiple of 2^-9, so products of two codes are exact integers in units of 2^-18 and the
+ *     integer product below accumulates them exactly in int64.
  */
 #include <stdint.h>
 #include <stdlib.h>
@@ -262,8 +270,74 @@ int hqo_gemm_i8(const int8_t *A, int64_t sam, int64_t sak, const int8_t *B, int6
   return overflow ? -1 : 0;
 }
 
+/* ---------------------------------------------------------------- FP8 (E4M3) codes
+ * Value of an E4M3 code in units of 2^-9 (an integer): subnormal (exponent field 0) m, normal
+ * (8 + m) * 2^(e - 1). Returns 0 for the two reserved codes, which the quantizer never writes. */
+static int64_t e4m3_units(uint8_t c) {
+  const int e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return 0;
+  const int64_t mag = (e == 0) ? m : (int64_t)(8 + m) << (e - 1);
+  return (c & 0x80) ? -mag : mag;
+}
+
+/* Decode E4M3 codes to double (exact). */
+void hqo_decode_e4m3(const uint8_t *q, int64_t n, double *out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = ldexp((double)e4m3_units(q[i]), -9);
+}
+
+/* [HALO summary page, Key results / Limitations: FP8 as the lower-precision grid]
+ * q = the E4M3 code nearest to R / s (ties to the even mantissa, saturating at +-448).
+ * Magnitude codes 0..126 are the non-negative grid in increasing order (code 126 = 448). The
+ * code is found by exact comparisons of |R| against g(c) * s and against the midpoints
+ * (g(c) + g(c + 1)) / 2 * s, where g(c) has at most 4 significant bits, so every product with
+ * the fp32 step is exact in double. s == 0 gives all-zero codes. Returns 0. */
+int hqo_quantize_e4m3(const double *R, int64_t n, float scale, uint8_t *q) {
+  if (scale == 0.0f) {
+    memset(q, 0, (size_t)n);
+    return 0;
+  }
+  const double s = (double)scale;
+  for (int64_t i = 0; i < n; ++i) {
+    const double a = fabs(R[i]);
+    int c = 0;
+    /* largest magnitude code whose value times s is <= |R| (binary search over 0..126) */
+    int lo = 0, hi = 126;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) / 2;
+      if (ldexp((double)e4m3_units((uint8_t)mid), -9) * s <= a) lo = mid;
+      else hi = mid - 1;
+    }
+    c = lo;
+    if (c < 126) {
+      const double g0 = ldexp((double)e4m3_units((uint8_t)c), -9);
+      const double g1 = ldexp((double)e4m3_units((uint8_t)(c + 1)), -9);
+      const double midv = (g0 + g1) * 0.5 * s;
+      if (a > midv || (a == midv && (c & 1))) ++c;   /* nearest; a tie goes to the even code */
+    }
+    q[i] = (uint8_t)(c | (R[i] < 0 ? 0x80 : 0));
+  }
+  return 0;
+}
+
+/* [INT4 §3.1, §A.6 with FP8 codes] Exact product of two E4M3 code matrices, in units of 2^-18:
+ *   C[m*N + n] = sum_k A[m*sam + k*sak] * B[k*sbk + n*sbn] (code values times 2^9 each).
+ * |A B| <= 448^2 2^18 K stays far inside int64 for every K used here. Returns 0. */
+int hqo_gemm_f8(const uint8_t *A, int64_t sam, int64_t sak, const uint8_t *B, int64_t sbk,
+                int64_t sbn, int64_t M, int64_t N, int64_t K, int64_t *C) {
+#pragma omp parallel for schedule(static)
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t n = 0; n < N; ++n) {
+      int64_t acc = 0;
+      for (int64_t k = 0; k < K; ++k)
+        acc += e4m3_units(A[m * sam + k * sak]) * e4m3_units(B[k * sbk + n * sbn]);
+      C[m * N + n] = acc;
+    }
+  return 0;
+}
+
 /* [INT4 §3.3] Inverse rotation of an integer product, exact in int64 (the same explicit H;
- * H^-1 = H/k and the 1/k goes to the dequantization scalar). Same index maps as hqo_rotate. */
+ * H^-1 = H/k and the 1/k goes to the dequantization scalar). Same index maps as hqo_rotate.
+ * Returns -1 if a sum would leave the int64 range. */
 int hqo_rotate_i64(const int64_t *T, int64_t rows, int64_t cols, int rot, int k, int64_t *R) {
   if (!is_pow2_le256(k) || rows < 0 || cols < 0) return -1;
   if ((rot == HQO_ROT_RIGHT || rot == HQO_ROT_BOTH) && cols % k) return -1;
@@ -271,20 +345,23 @@ int hqo_rotate_i64(const int64_t *T, int64_t rows, int64_t cols, int rot, int k,
   int8_t *H = (int8_t *)malloc((size_t)k * k);
   if (!H) return -1;
   hqo_hadamard(k, H);
+  int overflow = 0;   /* a sum left the int64 range (never for the products used here) */
   if (rot == HQO_ROT_NONE) {
     memcpy(R, T, sizeof(int64_t) * (size_t)(rows * cols));
   } else if (rot == HQO_ROT_RIGHT) {
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) reduction(| : overflow)
     for (int64_t i = 0; i < rows; ++i)
       for (int64_t b = 0; b < cols / k; ++b)
         for (int j = 0; j < k; ++j) {
           int64_t acc = 0;
-          for (int t = 0; t < k; ++t) acc += T[i * cols + b * k + t] * (int64_t)H[t * k + j];
+          for (int t = 0; t < k; ++t)
+            if (__builtin_add_overflow(acc, T[i * cols + b * k + t] * (int64_t)H[t * k + j], &acc))
+              overflow = 1;
           R[i * cols + b * k + j] = acc;
         }
   } else if (rot == HQO_ROT_LEFT) {
     /* R[b*k+i][j] = sum_t h(i,t) T[b*k+t][j] (exact integers; rows read contiguously) */
-#pragma omp parallel for schedule(static) collapse(2)
+#pragma omp parallel for schedule(static) collapse(2) reduction(| : overflow)
     for (int64_t b = 0; b < rows / k; ++b)
       for (int i = 0; i < k; ++i) {
         int64_t *out = R + (b * k + i) * cols;
@@ -292,7 +369,8 @@ int hqo_rotate_i64(const int64_t *T, int64_t rows, int64_t cols, int rot, int k,
         for (int t = 0; t < k; ++t) {
           const int64_t h = (int64_t)H[i * k + t];
           const int64_t *trow = T + (b * k + t) * cols;
-          for (int64_t j = 0; j < cols; ++j) out[j] += h * trow[j];
+          for (int64_t j = 0; j < cols; ++j)
+            if (__builtin_add_overflow(out[j], h * trow[j], &out[j])) overflow = 1;
         }
       }
   } else if (rot == HQO_ROT_BOTH) {
@@ -308,12 +386,13 @@ int hqo_rotate_i64(const int64_t *T, int64_t rows, int64_t cols, int rot, int k,
     return -1;
   }
   free(H);
-  return 0;
+  return overflow ? -1 : 0;
 }
 
-/* [INT4 §3.1] Dequantization: out = T * s_a * s_b / k^e in double. */
-void hqo_dequant(const int64_t *T, int64_t n, float s_a, float s_b, int k_pow_e, double *out) {
-  double alpha = (double)s_a * (double)s_b / (double)k_pow_e;
+/* [INT4 §3.1] Dequantization: out = T * s_a * s_b / div in double, div = k^e (a power of two;
+ * for FP8 products also times 2^18, the unit of the exact FP8 sums). */
+void hqo_dequant(const int64_t *T, int64_t n, float s_a, float s_b, double div, double *out) {
+  double alpha = (double)s_a * (double)s_b / div;
   for (int64_t i = 0; i < n; ++i) out[i] = (double)T[i] * alpha;
 }
 
