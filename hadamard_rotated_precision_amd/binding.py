@@ -20,10 +20,11 @@ HQ_ROT_NONE, HQ_ROT_RIGHT, HQ_ROT_LEFT, HQ_ROT_BOTH = 0, 1, 2, 3
 HQ_SCALE_ABSMAX, HQ_SCALE_STEP = 0, 1
 HQ_VARIANT_HALO0, HQ_VARIANT_HQ, HQ_VARIANT_HALO2 = 0, 1, 2
 HQ_FWHT_AUTO, HQ_FWHT_BUTTERFLY, HQ_FWHT_MATRIX = 0, 1, 2
+HQ_FMT_INT, HQ_FMT_E4M3 = 0, 1
 
 EXPORTS = ["hq_abi_version", "hq_status_string", "hq_code_pitch", "hq_workspace_bytes",
            "hq_rotate_quantize", "hq_linear_fwd", "hq_linear_fwd_noalloc", "hq_linear_bwd_input",
-           "hq_linear_bwd_weight", "hq_fwht", "hq_fwht_path", "hq_gemm_i8_i32",
+           "hq_linear_bwd_weight", "hq_fwht", "hq_fwht_path", "hq_gemm_i8_i32", "hq_gemm_f8_f32",
            "hq_profile_start", "hq_profile_stop", "hq_profile_records"]
 HQ_KIND_GEMM, HQ_KIND_ROT_ABSMAX, HQ_KIND_ROT_QUANT, HQ_KIND_ROT_STORE = 0, 1, 2, 3
 HQ_KIND_TRANSPOSE, HQ_KIND_MISC, HQ_KIND_COUNT = 4, 5, 6
@@ -32,14 +33,15 @@ KIND_NAMES = ["gemm", "rot_absmax", "rot_quant", "rot_store", "transpose", "misc
 
 class hq_config(ctypes.Structure):
     _fields_ = [("k", ctypes.c_int32), ("bits", ctypes.c_int32),
-                ("scale_mode", ctypes.c_int32), ("variant", ctypes.c_int32)]
+                ("scale_mode", ctypes.c_int32), ("variant", ctypes.c_int32),
+                ("format", ctypes.c_int32)]
 
 
 class hq_qtensor(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("codes_t", ctypes.c_void_p),
                 ("scale", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
                 ("ld", ctypes.c_int64), ("ld_t", ctypes.c_int64), ("k", ctypes.c_int32),
-                ("bits", ctypes.c_int32), ("rot", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("bits", ctypes.c_int32), ("rot", ctypes.c_int32), ("format", ctypes.c_int32)]
 
 
 class hq_profile_stat(ctypes.Structure):
@@ -105,6 +107,8 @@ def load(build_if_missing=True):
                                          P(hq_config), vp, i32, vp, sz, vp]
     lib.hq_fwht.restype = i32
     lib.hq_fwht.argtypes = [vp, i32, vp, i32, i64, i64, i32, i32, vp]
+    lib.hq_gemm_f8_f32.restype = i32
+    lib.hq_gemm_f8_f32.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, vp]
     lib.hq_fwht_path.restype = i32
     lib.hq_fwht_path.argtypes = [vp, i32, vp, i32, i64, i64, i32, i32, i32, vp]
     lib.hq_gemm_i8_i32.restype = i32
@@ -180,6 +184,10 @@ def hq_fwht_path(src, src_dtype, dst, dst_dtype, rows, cols, rot, k, path, strea
 
 def hq_gemm_i8_i32(a, lda, b_t, ldb, c, M, N, K, stream):
     return load().hq_gemm_i8_i32(a, lda, b_t, ldb, c, M, N, K, stream)
+
+
+def hq_gemm_f8_f32(a, lda, b_t, ldb, c, M, N, K, stream):
+    return load().hq_gemm_f8_f32(a, lda, b_t, ldb, c, M, N, K, stream)
 
 
 def hq_profile_start(kind_mask):

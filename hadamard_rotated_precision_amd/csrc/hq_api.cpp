@@ -26,12 +26,16 @@ int64_t pitch16(int64_t n) { return (n + 15) / 16 * 16; }
 bool is_pow2_k(int32_t k) { return k >= 1 && k <= 256 && (k & (k - 1)) == 0; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool valid_dt(int32_t dt) { return dt == HQ_F32 || dt == HQ_F16 || dt == HQ_BF16; }
-int qmax(int32_t bits) { return bits == 4 ? 7 : 127; }
+bool is_f8(const hq_config* cfg) { return cfg->format == HQ_FMT_E4M3; }
+// grid bound of the codes: 448 (the largest E4M3 value) or the integer Qp
+int qmax(const hq_config* cfg) { return is_f8(cfg) ? 448 : (cfg->bits == 4 ? 7 : 127); }
 
 hq_status check_cfg(const hq_config* cfg) {
   if (!cfg) return HQ_ERR_NULL;
   if (!is_pow2_k(cfg->k)) return HQ_ERR_K;
+  if (cfg->format != HQ_FMT_INT && cfg->format != HQ_FMT_E4M3) return HQ_ERR_MODE;
   if (cfg->bits != 4 && cfg->bits != 8) return HQ_ERR_BITS;
+  if (is_f8(cfg) && cfg->bits != 8) return HQ_ERR_BITS;
   if (cfg->scale_mode != HQ_SCALE_ABSMAX && cfg->scale_mode != HQ_SCALE_STEP) return HQ_ERR_MODE;
   if (cfg->variant < HQ_VARIANT_HALO0 || cfg->variant > HQ_VARIANT_HALO2) return HQ_ERR_MODE;
   return HQ_OK;
@@ -103,7 +107,7 @@ hq_status device_ok() { return device_info().st; }
 // Rotate -> scale -> quantize one tensor into row-major and/or transposed codes (one absmax
 // pass unless a step is given, then one quantize pass that writes both layouts).
 hq_status quantize_tensor(const void* src, int32_t dt, int64_t rows, int64_t cols, int32_t rot,
-                          int32_t k, int32_t bits, const float* step, int8_t* codes, int64_t ld,
+                          int32_t k, const hq_config* cfg, const float* step, int8_t* codes, int64_t ld,
                           int8_t* codes_t, int64_t ld_t, float* scale, const Ws& ws,
                           int part_slot, hipStream_t st, int32_t* zero_ptr = nullptr,
                           int64_t zero_n = 0) {
@@ -117,7 +121,8 @@ hq_status quantize_tensor(const void* src, int32_t dt, int64_t rows, int64_t col
   p.in_dt = dt;
   p.rows = rows;
   p.cols = cols;
-  p.qp = qmax(bits);
+  p.qp = qmax(cfg);
+  p.f8 = is_f8(cfg);
   p.partials = ws.part[part_slot];
   p.step = step;
   p.zero_ptr = zero_ptr;
@@ -151,8 +156,8 @@ hq_status quantize_tensor(const void* src, int32_t dt, int64_t rows, int64_t col
 
 // The two-sided pass of X under HALO-2: Q(X B) row-major and Q(B X B) transposed.
 hq::ProPass x_both_pass(const void* src, int32_t dt, int64_t rows, int64_t cols, int32_t k,
-                        int32_t bits, const float* step_x, const float* step_xt, hq_qtensor* qx,
-                        hq_qtensor* qxt, const Ws& ws) {
+                        const hq_config* cfg, const float* step_x, const float* step_xt,
+                        hq_qtensor* qx, hq_qtensor* qxt, const Ws& ws) {
   hq::ProPass p;
   p.kind = hq::PRO_BOTH;
   p.src = src;
@@ -160,7 +165,8 @@ hq::ProPass x_both_pass(const void* src, int32_t dt, int64_t rows, int64_t cols,
   p.rows = rows;
   p.cols = cols;
   p.k = k;
-  p.qp = qmax(bits);
+  p.qp = qmax(cfg);
+  p.f8 = is_f8(cfg);
   p.partials = ws.part[0];
   p.step = step_x;
   p.step2 = step_xt;
@@ -175,14 +181,14 @@ hq::ProPass x_both_pass(const void* src, int32_t dt, int64_t rows, int64_t cols,
 
 // X under HALO-2: one pass pair writes Q(X B) row-major and Q(B X B) transposed.
 hq_status quantize_x_both(const void* src, int32_t dt, int64_t rows, int64_t cols, int32_t k,
-                          int32_t bits, const float* step_x, const float* step_xt,
+                          const hq_config* cfg, const float* step_x, const float* step_xt,
                           hq_qtensor* qx, hq_qtensor* qxt, const Ws& ws, hipStream_t st) {
   if (rows * cols == 0) {
     HQ_TRY(hq::write_scale(qx->scale, step_x, st));
     HQ_TRY(hq::write_scale(qxt->scale, step_xt, st));
     return HQ_OK;
   }
-  hq::ProPass p = x_both_pass(src, dt, rows, cols, k, bits, step_x, step_xt, qx, qxt, ws);
+  hq::ProPass p = x_both_pass(src, dt, rows, cols, k, cfg, step_x, step_xt, qx, qxt, ws);
   if (!step_x) {
     p.nparts = hq::pro_grid(p);
     HQ_TRY(hq::pro_pass(p, hq::OP_ABSMAX, st));
@@ -212,19 +218,20 @@ hq_status check_pitches(const hq_qtensor* q, int64_t rows, int64_t cols) {
   return HQ_OK;
 }
 
-void fill_meta(hq_qtensor* q, int64_t rows, int64_t cols, int32_t k, int32_t bits, int32_t rot) {
+void fill_meta(hq_qtensor* q, int64_t rows, int64_t cols, const hq_config* cfg, int32_t rot) {
   q->rows = rows;
   q->cols = cols;
-  q->k = k;
-  q->bits = bits;
+  q->k = cfg->k;
+  q->bits = cfg->bits;
   q->rot = rot;
+  q->format = cfg->format;
 }
 
 hq_status check_saved(const hq_qtensor* q, int64_t rows, int64_t cols, const hq_config* cfg,
                       int32_t rot) {
   if (!q || !q->scale || (!q->codes_t && rows * cols > 0)) return HQ_ERR_NULL;
   if (q->rows != rows || q->cols != cols || q->k != cfg->k || q->bits != cfg->bits ||
-      q->rot != rot)
+      q->rot != rot || q->format != cfg->format)
     return HQ_ERR_MISMATCH;
   if (!aligned16(q->codes_t) || q->ld_t % 16 != 0) return HQ_ERR_ALIGN;
   if (q->ld_t < rows) return HQ_ERR_SHAPE;
@@ -255,9 +262,9 @@ const char* hq_status_string(int32_t s) {
     case HQ_ERR_NULL: return "a required pointer is NULL";
     case HQ_ERR_SHAPE: return "bad shape (negative, not divisible by k, or mismatched pitch)";
     case HQ_ERR_K: return "k must be a power of two in [1, 256]";
-    case HQ_ERR_BITS: return "bits must be 4 or 8";
+    case HQ_ERR_BITS: return "bits must be 4 or 8 (8 for E4M3 codes)";
     case HQ_ERR_DTYPE: return "unsupported dtype";
-    case HQ_ERR_MODE: return "bad rotation, scale mode or variant";
+    case HQ_ERR_MODE: return "bad rotation, scale mode, variant or code format";
     case HQ_ERR_WORKSPACE: return "workspace missing or too small";
     case HQ_ERR_MISMATCH: return "saved quantized tensor does not match this call";
     case HQ_ERR_DEVICE: return "no usable gfx950 device";
@@ -293,10 +300,10 @@ hq_status hq_rotate_quantize(const void* src, int32_t src_dtype, int64_t rows, i
   HQ_CHECK(device_ok());
   hipStream_t st = static_cast<hipStream_t>(stream);
   Ws w(ws);
-  HQ_CHECK(quantize_tensor(src, src_dtype, rows, cols, rot, cfg->k, cfg->bits,
+  HQ_CHECK(quantize_tensor(src, src_dtype, rows, cols, rot, cfg->k, cfg,
                            cfg->scale_mode == HQ_SCALE_STEP ? step : nullptr, out->codes,
                            out->ld, out->codes_t, out->ld_t, out->scale, w, 0, st));
-  fill_meta(out, rows, cols, cfg->k, cfg->bits, rot);
+  fill_meta(out, rows, cols, cfg, rot);
   return HQ_OK;
 }
 
@@ -350,35 +357,36 @@ hq_status fwd_run(const void* x, const void* w, int32_t in_dtype, int64_t N, int
   hq::ProPass px;
   bool single = false;
   if (two_sided && !stepm && N * C > 0) {
-    px = x_both_pass(x, in_dtype, N, C, k, cfg->bits, nullptr, nullptr, save_x, save_xt, wsp);
+    px = x_both_pass(x, in_dtype, N, C, k, cfg, nullptr, nullptr, save_x, save_xt, wsp);
     single = hq::pro_single_ok(px, device_info().cus) && D * C > 0;
   }
-  HQ_CHECK(quantize_tensor(w, in_dtype, D, C, rx, k, cfg->bits, stepm ? step_w : nullptr,
+  HQ_CHECK(quantize_tensor(w, in_dtype, D, C, rx, k, cfg, stepm ? step_w : nullptr,
                            save_w->codes, save_w->ld, save_w->codes_t, save_w->ld_t,
                            save_w->scale, wsp, 2, st, single ? wsp.bar : nullptr,
                            single ? hq::kBarWordsInts : 0));
-  fill_meta(save_w, D, C, k, cfg->bits, rx);
+  fill_meta(save_w, D, C, cfg, rx);
   if (single) {
     px.nparts = hq::pro_grid(px);
     HQ_TRY(hq::pro_single_pass(px, wsp.bar, st));
     HQ_TRY(hq::pro_fixup_pass(px, wsp.bar, st));
   } else if (two_sided) {
-    HQ_CHECK(quantize_x_both(x, in_dtype, N, C, k, cfg->bits, stepm ? step_x : nullptr,
+    HQ_CHECK(quantize_x_both(x, in_dtype, N, C, k, cfg, stepm ? step_x : nullptr,
                              stepm ? step_xt : nullptr, save_x, save_xt, wsp, st));
   } else {
-    HQ_CHECK(quantize_tensor(x, in_dtype, N, C, rx, k, cfg->bits, stepm ? step_x : nullptr,
+    HQ_CHECK(quantize_tensor(x, in_dtype, N, C, rx, k, cfg, stepm ? step_x : nullptr,
                              save_x->codes, save_x->ld, save_x->codes_t, save_x->ld_t,
                              save_x->scale, wsp, 0, st));
     if (want_xt)
-      HQ_CHECK(quantize_tensor(x, in_dtype, N, C, HQ_ROT_BOTH, k, cfg->bits,
+      HQ_CHECK(quantize_tensor(x, in_dtype, N, C, HQ_ROT_BOTH, k, cfg,
                                stepm ? step_xt : nullptr, k > 1 ? nullptr : save_xt->codes,
                                save_xt->ld, save_xt->codes_t, save_xt->ld_t, save_xt->scale,
                                wsp, 1, st));
   }
-  fill_meta(save_x, N, C, k, cfg->bits, rx);
-  if (want_xt) fill_meta(save_xt, N, C, k, cfg->bits, HQ_ROT_BOTH);
+  fill_meta(save_x, N, C, cfg, rx);
+  if (want_xt) fill_meta(save_xt, N, C, cfg, HQ_ROT_BOTH);
   GemmPass g;
   g.cus = device_info().cus;
+  g.f8 = is_f8(cfg);
   g.a = save_x->codes;
   g.lda = save_x->ld;
   g.b = save_w->codes;
@@ -439,14 +447,15 @@ hq_status hq_linear_bwd_input(const void* dy, int32_t dy_dtype, int64_t N, int64
   const int32_t rg = g_rot(v);
   // paired dX tiles need their arrival flags at zero: the quantize pass clears them
   const int64_t split = dx_split_tiles(cfg, N, C, D);
-  HQ_CHECK(quantize_tensor(dy, dy_dtype, N, D, rg, k, cfg->bits, stepm ? step_g : nullptr,
+  HQ_CHECK(quantize_tensor(dy, dy_dtype, N, D, rg, k, cfg, stepm ? step_g : nullptr,
                            save_g->codes, save_g->ld, save_g->codes_t, save_g->ld_t,
                            save_g->scale, wsp, 0, st,
                            split > 0 ? static_cast<int32_t*>(wsp.split) : nullptr, split));
-  fill_meta(save_g, N, D, k, cfg->bits, rg);
+  fill_meta(save_g, N, D, cfg, rg);
   // dX = [B_N] (qG qW) [B_C] sG sW / k^e, dequantized and inverse-rotated in the GEMM epilogue.
   GemmPass g;
   g.cus = device_info().cus;
+  g.f8 = is_f8(cfg);
   g.epi = hq::EPI_SCALE;
   g.sa = save_g->scale;
   g.sb = saved_w->scale;
@@ -507,6 +516,7 @@ hq_status hq_linear_bwd_weight(const hq_qtensor* saved_g, const hq_qtensor* save
   // tile's row axis (rotated in registers) and store it transposed.
   GemmPass g;
   g.cus = device_info().cus;
+  g.f8 = is_f8(cfg);
   g.epi = hq::EPI_SCALE;
   g.sa = saved_g->scale;
   g.sb = saved_x->scale;
@@ -599,8 +609,9 @@ hq_status hq_fwht(const void* src, int32_t src_dtype, void* dst, int32_t dst_dty
   return hq_fwht_path(src, src_dtype, dst, dst_dtype, rows, cols, rot, k, HQ_FWHT_AUTO, stream);
 }
 
-hq_status hq_gemm_i8_i32(const int8_t* a, int64_t lda, const int8_t* b_t, int64_t ldb,
-                         int32_t* c, int64_t M, int64_t N, int64_t K, void* stream) {
+namespace {
+hq_status gemm_plain(const void* a, int64_t lda, const void* b_t, int64_t ldb, void* c,
+                     int64_t M, int64_t N, int64_t K, bool f8, void* stream) {
   if (M < 0 || N < 0 || K < 0) return HQ_ERR_SHAPE;
   if ((M * K > 0 && !a) || (N * K > 0 && !b_t) || (M * N > 0 && !c)) return HQ_ERR_NULL;
   if (lda < K || ldb < K) return HQ_ERR_SHAPE;
@@ -609,9 +620,10 @@ hq_status hq_gemm_i8_i32(const int8_t* a, int64_t lda, const int8_t* b_t, int64_
   HQ_CHECK(device_ok());
   GemmPass g;
   g.cus = device_info().cus;
-  g.a = a;
+  g.f8 = f8;
+  g.a = static_cast<const int8_t*>(a);
   g.lda = lda;
-  g.b = b_t;
+  g.b = static_cast<const int8_t*>(b_t);
   g.ldb = ldb;
   g.M = M;
   g.N = N;
@@ -621,6 +633,17 @@ hq_status hq_gemm_i8_i32(const int8_t* a, int64_t lda, const int8_t* b_t, int64_
   g.ldc = N;
   HQ_TRY(hq::gemm_pass(g, static_cast<hipStream_t>(stream)));
   return HQ_OK;
+}
+}  // namespace
+
+hq_status hq_gemm_f8_f32(const uint8_t* a, int64_t lda, const uint8_t* b_t, int64_t ldb, float* c,
+                         int64_t M, int64_t N, int64_t K, void* stream) {
+  return gemm_plain(a, lda, b_t, ldb, c, M, N, K, true, stream);
+}
+
+hq_status hq_gemm_i8_i32(const int8_t* a, int64_t lda, const int8_t* b_t, int64_t ldb,
+                         int32_t* c, int64_t M, int64_t N, int64_t K, void* stream) {
+  return gemm_plain(a, lda, b_t, ldb, c, M, N, K, false, stream);
 }
 
 }  // extern "C"

@@ -278,6 +278,36 @@ __device__ inline uint32_t qpack4(uint32_t x0, uint32_t x1, uint32_t x2, uint32_
   return __builtin_amdgcn_perm(x1, x0, 0x0c0c0400u) | __builtin_amdgcn_perm(x3, x2, 0x04000c0cu);
 }
 
+// FP8 (OCP E4M3) codes: v * r clamped to [-448, 448] with med3, then the hardware conversion,
+// which rounds to nearest even on the E4M3 grid (subnormals included) but turns values past
+// 464 into the reserved code; the clamp makes it the saturating quantizer.
+constexpr float kE4M3Max = 448.0f;
+
+__device__ inline uint32_t e4m3_pack4(float v0, float v1, float v2, float v3, float r) {
+  const float x0 = __builtin_amdgcn_fmed3f(v0 * r, -kE4M3Max, kE4M3Max);
+  const float x1 = __builtin_amdgcn_fmed3f(v1 * r, -kE4M3Max, kE4M3Max);
+  const float x2 = __builtin_amdgcn_fmed3f(v2 * r, -kE4M3Max, kE4M3Max);
+  const float x3 = __builtin_amdgcn_fmed3f(v3 * r, -kE4M3Max, kE4M3Max);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
+  return static_cast<uint32_t>(w);
+}
+
+// Four codes of either format packed little-endian into one dword: integer codes through
+// qbits (lo, hi from qlo / qhi) or E4M3 codes (f8; lo and hi unused). f8 is uniform.
+__device__ inline uint32_t quant4(float v0, float v1, float v2, float v3, float r, float lo,
+                                  float hi, bool f8) {
+  if (f8) return e4m3_pack4(v0, v1, v2, v3, r);
+  return qpack4(qbits(v0, r, lo, hi), qbits(v1, r, lo, hi), qbits(v2, r, lo, hi),
+                qbits(v3, r, lo, hi));
+}
+
+// One code byte of either format (two's complement integer, or E4M3).
+__device__ inline int quant_byte(float v, float r, int qp, bool f8) {
+  if (f8) return static_cast<int>(e4m3_pack4(v, 0.0f, 0.0f, 0.0f, r) & 0xFFu);
+  return quant_code(v, r, qp);
+}
+
 // Pack 4 codes (already in [-127, 127]) into one little-endian dword.
 __device__ inline uint32_t pack4(int a, int b, int c, int d) {
   return (static_cast<uint32_t>(a) & 0xFFu) | ((static_cast<uint32_t>(b) & 0xFFu) << 8) |

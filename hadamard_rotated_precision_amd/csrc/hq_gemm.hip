@@ -1,5 +1,9 @@
 // hq_gemm.hip — INT8 x INT8 -> INT32 GEMM on gfx950 matrix cores with a fused epilogue that
-// dequantizes, applies the output-side inverse Walsh-Hadamard rotations and stores.
+// dequantizes, applies the output-side inverse Walsh-Hadamard rotations and stores. The same
+// kernel also multiplies FP8 (OCP E4M3) codes with fp32 accumulation (F8: the HALO page's FP8
+// variant of the three matmuls): v_mfma_f32_32x32x64_f8f6f4 takes 32 K bytes per lane; a lane
+// reads the same two 16-byte chunks of its A row and of its B row, so the products the
+// instruction pairs up share their K index whatever its internal byte order.
 //
 // "Training Transformers with 4-bit Integers", §3.1 (integer product accumulated in INT32,
 // dequantized back to floating point), §3.3 (the block-diagonal H_k transforms cancel, so the
@@ -36,6 +40,7 @@
 //     rows need rotating, which keeps that rotation in registers).
 #include <algorithm>
 #include <cstdlib>
+#include <type_traits>
 
 #include "hq_device.hpp"
 #include "hq_internal.hpp"
@@ -43,6 +48,7 @@
 namespace hq {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
@@ -158,7 +164,7 @@ template <int BN> struct GemmShape {
   static constexpr int NT = 64 * NW;
 };
 
-template <int BN, class Out, int EPI, int KM, int KN, bool TRANS, bool PAIR>
+template <int BN, class Out, int EPI, int KM, int KN, bool TRANS, bool PAIR, bool F8>
 __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs g) {
   constexpr int NT = GemmShape<BN>::NT;   // 512: two waves per SIMD
   constexpr int NW = GemmShape<BN>::NW;
@@ -169,7 +175,8 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs 
   // three 48 KB stages for 128-wide ones (one barrier per 32 or 16 MFMAs per wave)
   constexpr int GBK = 128;
   constexpr int NST = BN == 256 ? 2 : 3;
-  constexpr int KS = GBK / 32;        // 32-byte K slices per step (one MFMA group each)
+  // K slices per step, one MFMA group each: 32 bytes (int8) or 64 bytes (FP8)
+  constexpr int KS = F8 ? GBK / 64 : GBK / 32;
   constexpr int KC = GBK / 16;        // 16-byte chunks per LDS row
   constexpr int RPB = 1024 / GBK;     // rows per 1 KB direct-to-LDS block
   constexpr int A_BYTES = GBM * GBK, B_BYTES = BN * GBK, STAGE = A_BYTES + B_BYTES;
@@ -199,7 +206,9 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs 
   const int lane = t & 63, w = t >> 6;
   const int wm = w / WCOLS, wn = w % WCOLS;
 
-  v16i acc[4][NB];
+  using AccV = typename std::conditional<F8, v16f, v16i>::type;   // fp32 or int32 accumulators
+  using FragV = typename std::conditional<F8, v8i, v4i>::type;    // 32 or 16 K bytes per lane
+  AccV acc[4][NB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -251,24 +260,51 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs 
     for (int i = 0; i < BBLK; ++i)
       lds_dma16(rsb, stg + A_BYTES + (w + NW * i) * 1024, (k0 + kb[i] < kend) ? ob[i] + k0 : kOutOfRange);
   };
-  // fragment registers: two sets (ping-pong between the two 32-byte halves of a K step)
-  v4i af[2][4], bf[2][NB];
+  // fragment registers. Slice ks of a 128-byte step: int8, lane half h reads chunk 2 ks + h
+  // (16 bytes), in two sets (ping-pong between slices); FP8, chunks 4 ks + h and 4 ks + 2 + h
+  // (32 bytes), the same two for A and B, in one set (two would not fit beside the 128
+  // accumulators: the slice's MFMAs are issued before the next slice's reads).
+  constexpr int NSET = F8 ? 1 : 2;
+  FragV af[NSET][4], bf[NSET][NB];
   auto frag = [&](int set, const int8_t* sa, int ks) {
     const int8_t* sb = sa + A_BYTES;
-    const int ch = 2 * ks + (lane >> 5);
+    if constexpr (F8) {
+      const int c0 = 4 * ks + (lane >> 5), c1 = c0 + 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      af[set][i] = *reinterpret_cast<const v4i*>(sa + lds_off<GBK>(wm * 128 + i * 32 + (lane & 31), ch));
+      for (int i = 0; i < 4; ++i) {
+        const int row = wm * 128 + i * 32 + (lane & 31);
+        const v4i lo = *reinterpret_cast<const v4i*>(sa + lds_off<GBK>(row, c0));
+        const v4i hi = *reinterpret_cast<const v4i*>(sa + lds_off<GBK>(row, c1));
+        af[set][i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
-      bf[set][j] = *reinterpret_cast<const v4i*>(sb + lds_off<GBK>(wn * WN + j * 32 + (lane & 31), ch));
+      for (int j = 0; j < NB; ++j) {
+        const int row = wn * WN + j * 32 + (lane & 31);
+        const v4i lo = *reinterpret_cast<const v4i*>(sb + lds_off<GBK>(row, c0));
+        const v4i hi = *reinterpret_cast<const v4i*>(sb + lds_off<GBK>(row, c1));
+        bf[set][j] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+    } else {
+      const int ch = 2 * ks + (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[set][i] = *reinterpret_cast<const v4i*>(sa + lds_off<GBK>(wm * 128 + i * 32 + (lane & 31), ch));
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        bf[set][j] = *reinterpret_cast<const v4i*>(sb + lds_off<GBK>(wn * WN + j * 32 + (lane & 31), ch));
+    }
   };
   auto mfma = [&](int set) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[set][i], bf[set][j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < NB; ++j) {
+        if constexpr (F8)   // format 0 for both operands: FP8 E4M3; no block scales
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[set][i], bf[set][j],
+                                                                      acc[i][j], 0, 0, 0, 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[set][i], bf[set][j], acc[i][j], 0, 0, 0);
+      }
   };
 
   // Pipeline, one barrier per K step. At the start of step k, stage k is complete and
@@ -287,28 +323,53 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs 
   };
   auto step = [&](int k, int8_t* cur, int8_t* nxt, int8_t* far) {
     dma(k + NST - 1, NST == 2 ? nxt : far);
+    if constexpr (F8) {
 #pragma unroll
-    for (int ks = 1; ks < KS; ++ks) {
-      frag(ks & 1, cur, ks);
+      for (int ks = 1; ks < KS; ++ks) {
+        mfma(0);
+        __builtin_amdgcn_sched_barrier(0);
+        frag(0, cur, ks);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      mfma(0);
       __builtin_amdgcn_sched_barrier(0);
-      mfma((ks - 1) & 1);
+      wait_next();
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      frag(0, nxt, 0);
+    } else {
+#pragma unroll
+      for (int ks = 1; ks < KS; ++ks) {
+        frag(ks & 1, cur, ks);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma((ks - 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      wait_next();
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      frag(0, nxt, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma((KS - 1) & 1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    wait_next();
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    frag(0, nxt, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    mfma((KS - 1) & 1);
-    __builtin_amdgcn_sched_barrier(0);
   };
   auto last = [&](const int8_t* cur) {
+    if constexpr (F8) {
 #pragma unroll
-    for (int ks = 1; ks < KS; ++ks) {
-      frag(ks & 1, cur, ks);
-      mfma((ks - 1) & 1);
+      for (int ks = 1; ks < KS; ++ks) {
+        mfma(0);
+        frag(0, cur, ks);
+      }
+      mfma(0);
+    } else {
+#pragma unroll
+      for (int ks = 1; ks < KS; ++ks) {
+        frag(ks & 1, cur, ks);
+        mfma((ks - 1) & 1);
+      }
+      mfma((KS - 1) & 1);
     }
-    mfma((KS - 1) & 1);
   };
 
   if (KT > 0) {
@@ -351,7 +412,10 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs 
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          if (row < g.M && col < g.N) static_cast<int32_t*>(g.c)[row * g.ldc + col] = acc[i][j][r];
+          if (row < g.M && col < g.N) {
+            if constexpr (F8) static_cast<float*>(g.c)[row * g.ldc + col] = acc[i][j][r];
+            else static_cast<int32_t*>(g.c)[row * g.ldc + col] = acc[i][j][r];
+          }
         }
       }
     return;
@@ -362,7 +426,10 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs 
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < NB; ++j) fa[i][j] = __builtin_convertvector(acc[i][j], v16f);
+      for (int j = 0; j < NB; ++j) {
+        if constexpr (F8) fa[i][j] = acc[i][j];
+        else fa[i][j] = __builtin_convertvector(acc[i][j], v16f);
+      }
     if constexpr (KM > 1) {
       rows_fwht_inlane<KM, NB>(fa);
       if constexpr (KM > 4) rows_fwht_lanehalf<NB>(fa, lane);
@@ -626,38 +693,38 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs 
   }
 }
 
-template <int BN, class Out, int EPI, int KM, int KN, bool TRANS, bool PAIR = false>
+template <int BN, class Out, int EPI, int KM, int KN, bool TRANS, bool PAIR, bool F8>
 static hipError_t launch_gemm(const GemmArgs& a, hipStream_t st, int tok) {
   const int64_t tiles = ((a.M + GBM - 1) / GBM) * ((a.N + BN - 1) / BN);
-  return launch_k(gemm_i8_kernel<BN, Out, EPI, KM, KN, TRANS, PAIR>, dim3(static_cast<int>(tiles)),
-                  dim3(GemmShape<BN>::NT), st, tok, a);
+  return launch_k(gemm_i8_kernel<BN, Out, EPI, KM, KN, TRANS, PAIR, F8>,
+                  dim3(static_cast<int>(tiles)), dim3(GemmShape<BN>::NT), st, tok, a);
 }
 
-template <int BN, class Out>
+template <int BN, class Out, bool F8>
 static hipError_t launch_out(const GemmPass& p, const GemmArgs& a, hipStream_t st, int tok) {
   if (p.trans_out) {
     switch (p.km) {
-#define HQ_T(KK) case KK: return launch_gemm<BN, Out, EPI_SCALE, KK, 1, true>(a, st, tok);
+#define HQ_T(KK) case KK: return launch_gemm<BN, Out, EPI_SCALE, KK, 1, true, false, F8>(a, st, tok);
       HQ_T(1) HQ_T(2) HQ_T(4) HQ_T(8) HQ_T(16) HQ_T(32) HQ_T(64) HQ_T(128) HQ_T(256)
 #undef HQ_T
     }
     return hipErrorInvalidValue;
   }
-  if (p.km == 1 && p.kn == 1) return launch_gemm<BN, Out, EPI_SCALE, 1, 1, false>(a, st, tok);
+  if (p.km == 1 && p.kn == 1) return launch_gemm<BN, Out, EPI_SCALE, 1, 1, false, false, F8>(a, st, tok);
   if (p.km != p.kn) return hipErrorInvalidValue;
   if constexpr (BN == 128) {
     // column blocks up to 128 wide rotate inside the tile; 256-wide ones span a tile pair
     switch (p.km) {
-#define HQ_B(KK) case KK: return launch_gemm<BN, Out, EPI_SCALE, KK, KK, false>(a, st, tok);
+#define HQ_B(KK) case KK: return launch_gemm<BN, Out, EPI_SCALE, KK, KK, false, false, F8>(a, st, tok);
       HQ_B(2) HQ_B(4) HQ_B(8) HQ_B(16) HQ_B(32) HQ_B(64) HQ_B(128)
 #undef HQ_B
       case 256:
         if (!a.pair_part) return hipErrorInvalidValue;
-        return launch_gemm<BN, Out, EPI_SCALE, 256, 256, false, true>(a, st, tok);
+        return launch_gemm<BN, Out, EPI_SCALE, 256, 256, false, true, F8>(a, st, tok);
     }
   } else {
     switch (p.km) {
-#define HQ_B(KK) case KK: return launch_gemm<BN, Out, EPI_SCALE, KK, KK, false>(a, st, tok);
+#define HQ_B(KK) case KK: return launch_gemm<BN, Out, EPI_SCALE, KK, KK, false, false, F8>(a, st, tok);
       HQ_B(2) HQ_B(4) HQ_B(8) HQ_B(16) HQ_B(32) HQ_B(64) HQ_B(128) HQ_B(256)
 #undef HQ_B
     }
@@ -733,17 +800,21 @@ hipError_t gemm_pass(const GemmPass& p, hipStream_t st) {
     return hipErrorInvalidValue;
   const int kn = p.epi == EPI_I32 ? 1 : p.kn;
   const bool narrow = use_narrow(p.M, p.N, kn, p.trans_out);
-  auto launch = [&](bool nar, const GemmArgs& g) {
+  auto launch_fmt = [&](bool nar, const GemmArgs& g, auto f8) -> hipError_t {
+    constexpr bool F8 = decltype(f8)::value;
     const int tok = prof_open(K_GEMM, 2.0 * g.M * g.N * g.K);
     if (p.epi == EPI_I32)
-      return nar ? launch_gemm<128, F32, EPI_I32, 1, 1, false>(g, st, tok)
-                 : launch_gemm<256, F32, EPI_I32, 1, 1, false>(g, st, tok);
+      return nar ? launch_gemm<128, F32, EPI_I32, 1, 1, false, false, F8>(g, st, tok)
+                 : launch_gemm<256, F32, EPI_I32, 1, 1, false, false, F8>(g, st, tok);
     switch (p.out_dt) {
-      case DT_F32: return nar ? launch_out<128, F32>(p, g, st, tok) : launch_out<256, F32>(p, g, st, tok);
-      case DT_F16: return nar ? launch_out<128, F16>(p, g, st, tok) : launch_out<256, F16>(p, g, st, tok);
-      case DT_BF16: return nar ? launch_out<128, BF16>(p, g, st, tok) : launch_out<256, BF16>(p, g, st, tok);
+      case DT_F32: return nar ? launch_out<128, F32, F8>(p, g, st, tok) : launch_out<256, F32, F8>(p, g, st, tok);
+      case DT_F16: return nar ? launch_out<128, F16, F8>(p, g, st, tok) : launch_out<256, F16, F8>(p, g, st, tok);
+      case DT_BF16: return nar ? launch_out<128, BF16, F8>(p, g, st, tok) : launch_out<256, BF16, F8>(p, g, st, tok);
     }
     return hipErrorInvalidValue;
+  };
+  auto launch = [&](bool nar, const GemmArgs& g) {
+    return p.f8 ? launch_fmt(nar, g, std::true_type{}) : launch_fmt(nar, g, std::false_type{});
   };
   if (!narrow && kn <= 128) {
     // 256-wide tiles over columns [0, N1), then 128-wide ones over [N1, N) when that fills the

@@ -60,7 +60,8 @@ struct ProPass {
   int in_dt = 0;
   int64_t rows = 0, cols = 0;
   int k = 1;                         // 1 with PRO_RIGHT = no rotation
-  int qp = 127;
+  int qp = 127;                      // grid bound (448 for E4M3 codes)
+  bool f8 = false;                   // FP8 E4M3 codes instead of integer codes
   float* partials = nullptr;         // kMaxPartials floats
   int nparts = 0;                    // QUANT: grid of the ABSMAX pass (pro_grid)
   const float* step = nullptr;       // STEP mode (PRO_BOTH: step of X B)
@@ -101,7 +102,8 @@ hipError_t rows_pass(const RowPass& p, hipStream_t st);
 hipError_t cols_pass(const ColPass& p, hipStream_t st);
 hipError_t write_scale(float* scale, const float* step, hipStream_t st);
 
-// Integer GEMM c = a * b^T (a: M x K, b: N x K, int8, K-contiguous) with int32 accumulation.
+// Integer GEMM c = a * b^T (a: M x K, b: N x K, int8, K-contiguous) with int32 accumulation,
+// or (f8) the product of FP8 E4M3 code matrices with fp32 accumulation.
 enum Epi : int { EPI_I32 = 0, EPI_SCALE = 1 };
 struct GemmPass {
   const int8_t* a = nullptr;
@@ -122,6 +124,7 @@ struct GemmPass {
   void* split_ws = nullptr;       // tile-pair workspace (gemm_split_bytes) when pairing applies
   bool split_cnt_zeroed = false;  // its arrival flags were zeroed by an earlier launch on the stream
   int cus = 0;             // compute units of the device (0: assume 256), for the tile rounds
+  bool f8 = false;         // operands are FP8 E4M3 codes (fp32 accumulation; EPI_I32 stores fp32)
 };
 hipError_t gemm_pass(const GemmPass& p, hipStream_t st);
 // Number of tile pairs of a GEMM whose 256-wide column rotation spans two 256 x 128 tiles

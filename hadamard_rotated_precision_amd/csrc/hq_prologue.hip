@@ -52,13 +52,14 @@ __device__ inline void load64(const void* row, int64_t c0, int64_t n, bool vec, 
   }
 }
 
-// Pack 16 codes starting at v[i0] into a uint4.
-__device__ inline uint4 pack16(const float (&v)[64], int i0, float r, int qp) {
+// Pack 16 codes starting at v[i0] into a uint4 (integer codes, or E4M3 codes when f8).
+__device__ inline uint4 pack16(const float (&v)[64], int i0, float r, int qp, bool f8) {
   uint32_t w[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    w[j] = pack4(quant_code(v[i0 + 4 * j], r, qp), quant_code(v[i0 + 4 * j + 1], r, qp),
-                 quant_code(v[i0 + 4 * j + 2], r, qp), quant_code(v[i0 + 4 * j + 3], r, qp));
+    w[j] = f8 ? e4m3_pack4(v[i0 + 4 * j], v[i0 + 4 * j + 1], v[i0 + 4 * j + 2], v[i0 + 4 * j + 3], r)
+              : pack4(quant_code(v[i0 + 4 * j], r, qp), quant_code(v[i0 + 4 * j + 1], r, qp),
+                      quant_code(v[i0 + 4 * j + 2], r, qp), quant_code(v[i0 + 4 * j + 3], r, qp));
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
@@ -72,7 +73,8 @@ struct ProArgs {
   int nparts;
   const float* step;        // QUANT, STEP mode (right / left rotation, or X B for both_kernel)
   const float* step2;       // both_kernel, STEP mode: step of B X B
-  int qp;
+  int qp;                   // grid bound: 127 / 7 for integer codes, 448 for E4M3 codes
+  bool f8;                  // codes are FP8 E4M3 (quant4 / quant_byte), else integers
   float* scale_out;
   float* scale_out2;        // both_kernel: scale of B X B
   int8_t* codes;            // row-major codes (pitch ld) or nullptr
@@ -141,13 +143,13 @@ __global__ __launch_bounds__(RT_THREADS) void right_kernel(ProArgs a) {
         const int64_t cpad = (a.cols + 15) / 16 * 16;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          if (gc + 16 * q < cpad) *reinterpret_cast<uint4*>(dst + 16 * q) = pack16(v, 16 * q, rinv, a.qp);
+          if (gc + 16 * q < cpad) *reinterpret_cast<uint4*>(dst + 16 * q) = pack16(v, 16 * q, rinv, a.qp, a.f8);
       }
       if (a.codes_t) {
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < 64; ++j)
-          tcodes[64 * s + j][r] = static_cast<int8_t>(quant_code(v[j], rinv, a.qp));
+          tcodes[64 * s + j][r] = static_cast<int8_t>(quant_byte(v[j], rinv, a.qp, a.f8));
         __syncthreads();
         // thread t writes transposed row col0 + t: 64 bytes = tile rows row0 .. row0+63
         const int64_t orow = col0 + t;
@@ -349,8 +351,7 @@ __global__ __launch_bounds__(RF_THREADS) void right_fast_kernel(ProArgs a) {
       uint32_t d[16];   // d[g]: columns 32(g/2) + 8s + 4(g%2) + 0..3
 #pragma unroll
       for (int g = 0; g < 16; ++g)
-        d[g] = qpack4(qbits(v[4 * g], rr, lo, hi), qbits(v[4 * g + 1], rr, lo, hi),
-                      qbits(v[4 * g + 2], rr, lo, hi), qbits(v[4 * g + 3], rr, lo, hi));
+        d[g] = quant4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3], rr, lo, hi, a.f8);
       const uint32_t tr = tl / nct;
       const int64_t row0 = static_cast<int64_t>(tr) * RF_ROWS;
       const int64_t col0 = static_cast<int64_t>(tl - tr * nct) * RF_COLS;
@@ -611,8 +612,7 @@ __global__ __launch_bounds__(RM_THREADS, 2) void right_mma_kernel(ProArgs a) {
         uint32_t d[16];   // rows 4lg + [0, 4) of column 16nb + n0
 #pragma unroll
         for (int nb = 0; nb < 16; ++nb)
-          d[nb] = qpack4(qbits(acc[nb][0], rinv, lo, hi), qbits(acc[nb][1], rinv, lo, hi),
-                         qbits(acc[nb][2], rinv, lo, hi), qbits(acc[nb][3], rinv, lo, hi));
+          d[nb] = quant4(acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3], rinv, lo, hi, a.f8);
         const uint32_t tr = tl / nct;
         const int64_t row0 = static_cast<int64_t>(tr) * RM_ROWS;
         const int64_t col0 = static_cast<int64_t>(tl - tr * nct) * RM_COLS;
@@ -750,13 +750,13 @@ __global__ __launch_bounds__(LT_THREADS) void left_kernel(ProArgs a) {
         int8_t* dst = a.codes_t + gcol * a.ld_t + row0 + 64 * p;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          if (row0 + 64 * p + 16 * q < rpad) *reinterpret_cast<uint4*>(dst + 16 * q) = pack16(v, 16 * q, rinv, a.qp);
+          if (row0 + 64 * p + 16 * q < rpad) *reinterpret_cast<uint4*>(dst + 16 * q) = pack16(v, 16 * q, rinv, a.qp, a.f8);
       }
       if (a.codes) {
         __syncthreads();   // the fp32 tile is dead: reuse it for the byte transpose
 #pragma unroll
         for (int i = 0; i < 64; ++i)
-          bcodes[(64 * p + i) * BP + c] = static_cast<int8_t>(quant_code(v[i], rinv, a.qp));
+          bcodes[(64 * p + i) * BP + c] = static_cast<int8_t>(quant_byte(v[i], rinv, a.qp, a.f8));
         __syncthreads();
         for (int q = t; q < TR * TC / 16; q += LT_THREADS) {
           const int row = q / (TC / 16), cc = 16 * (q % (TC / 16));
@@ -865,8 +865,7 @@ __global__ __launch_bounds__(LF_THREADS, 2) void left_fast_kernel(ProArgs a) {
       uint32_t d[16];   // d[g]: tokens 64 p + 4 g + [0, 4) of column c
 #pragma unroll
       for (int g = 0; g < 16; ++g)
-        d[g] = qpack4(qbits(v[4 * g], rr, lo, hi), qbits(v[4 * g + 1], rr, lo, hi),
-                      qbits(v[4 * g + 2], rr, lo, hi), qbits(v[4 * g + 3], rr, lo, hi));
+        d[g] = quant4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3], rr, lo, hi, a.f8);
       const uint32_t tr = tl / nct;
       const int64_t row0 = static_cast<int64_t>(tr) * LF_ROWS;
       const int64_t col0 = static_cast<int64_t>(tl - tr * nct) * LF_COLS;
@@ -1070,8 +1069,7 @@ __global__ __launch_bounds__(LM_THREADS, 2) void left_mma_kernel(ProArgs a) {
         uint32_t d[16];   // rows 16mb + 4lg + [0, 4) of column 16w + n0
 #pragma unroll
         for (int mb = 0; mb < 16; ++mb)
-          d[mb] = qpack4(qbits(acc[mb][0], rinv, lo, hi), qbits(acc[mb][1], rinv, lo, hi),
-                         qbits(acc[mb][2], rinv, lo, hi), qbits(acc[mb][3], rinv, lo, hi));
+          d[mb] = quant4(acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3], rinv, lo, hi, a.f8);
         const uint32_t tr = tl / nct;
         const int64_t row0 = static_cast<int64_t>(tr) * LM_ROWS;
         const int64_t col0 = static_cast<int64_t>(tl - tr * nct) * LM_COLS;
@@ -1271,8 +1269,7 @@ __global__ __launch_bounds__(BT_THREADS) void both_kernel(ProArgs a) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int i = 16 * q + 4 * j;
-            x[j] = qpack4(qbits(w[i], r1, lo, hi), qbits(w[i + 1], r1, lo, hi),
-                          qbits(w[i + 2], r1, lo, hi), qbits(w[i + 3], r1, lo, hi));
+            x[j] = quant4(w[i], w[i + 1], w[i + 2], w[i + 3], r1, lo, hi, a.f8);
           }
           *reinterpret_cast<uint4*>(dst + 16 * q) = make_uint4(x[0], x[1], x[2], x[3]);
         }
@@ -1309,10 +1306,9 @@ __global__ __launch_bounds__(BT_THREADS) void both_kernel(ProArgs a) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int i = 16 * q + 4 * j;
-            x[j] = qpack4(qbits(static_cast<float>(u[i]), r2, lo, hi),
-                          qbits(static_cast<float>(u[i + 1]), r2, lo, hi),
-                          qbits(static_cast<float>(u[i + 2]), r2, lo, hi),
-                          qbits(static_cast<float>(u[i + 3]), r2, lo, hi));
+            x[j] = quant4(static_cast<float>(u[i]), static_cast<float>(u[i + 1]),
+                          static_cast<float>(u[i + 2]), static_cast<float>(u[i + 3]), r2, lo, hi,
+                          a.f8);
           }
           *reinterpret_cast<uint4*>(dst + 16 * q) = make_uint4(x[0], x[1], x[2], x[3]);
         }
@@ -1478,8 +1474,7 @@ __device__ inline void both_mma_body(const ProArgs& a) {
           int8_t* dst = a.codes + (row0 + rloc + 4 * lg + i) * a.ld + col0 + BT_HALF * h + 4 * m;
 #pragma unroll
           for (int nb = 0; nb < 8; ++nb) {
-            const uint32_t d = qpack4(qbits(y[nb][0], r1, lo, hi), qbits(y[nb][1], r1, lo, hi),
-                                      qbits(y[nb][2], r1, lo, hi), qbits(y[nb][3], r1, lo, hi));
+            const uint32_t d = quant4(y[nb][0], y[nb][1], y[nb][2], y[nb][3], r1, lo, hi, a.f8);
             *reinterpret_cast<uint32_t*>(dst + 16 * nb) = quad_byte_transpose(d, i);
           }
         }
@@ -1521,10 +1516,9 @@ __device__ inline void both_mma_body(const ProArgs& a) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int i = 16 * q + 4 * j;
-            xq[j] = qpack4(qbits(static_cast<float>(u[i]), r2, lo, hi),
-                           qbits(static_cast<float>(u[i + 1]), r2, lo, hi),
-                           qbits(static_cast<float>(u[i + 2]), r2, lo, hi),
-                           qbits(static_cast<float>(u[i + 3]), r2, lo, hi));
+            xq[j] = quant4(static_cast<float>(u[i]), static_cast<float>(u[i + 1]),
+                           static_cast<float>(u[i + 2]), static_cast<float>(u[i + 3]), r2, lo, hi,
+                           a.f8);
           }
           *reinterpret_cast<uint4*>(dst + 16 * q) = make_uint4(xq[0], xq[1], xq[2], xq[3]);
         }
@@ -1683,8 +1677,7 @@ struct BothItem {
         for (int nb = 0; nb < 8; ++nb) {
           const int c = 16 * nb + n0;
           const float4 y = *reinterpret_cast<const float4*>(&half[c * BT + 4 * bm_chunk(c, c4)]);
-          const uint32_t d = qpack4(qbits(y.x, r1, lo, hi), qbits(y.y, r1, lo, hi),
-                                    qbits(y.z, r1, lo, hi), qbits(y.w, r1, lo, hi));
+          const uint32_t d = quant4(y.x, y.y, y.z, y.w, r1, lo, hi, a.f8);
           rc[rb][nb] = quad_byte_transpose(d, i);
         }
       }
@@ -1692,8 +1685,7 @@ struct BothItem {
     uint32_t tc[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j)
-      tc[j] = qpack4(qbits(v2[4 * j], r2, lo, hi), qbits(v2[4 * j + 1], r2, lo, hi),
-                     qbits(v2[4 * j + 2], r2, lo, hi), qbits(v2[4 * j + 3], r2, lo, hi));
+      tc[j] = quant4(v2[4 * j], v2[4 * j + 1], v2[4 * j + 2], v2[4 * j + 3], r2, lo, hi, a.f8);
     __syncthreads();   // every thread has read its values out of the half tile
     uint32_t* const rt = reinterpret_cast<uint32_t*>(half);   // [256 rows][32 dwords]
     uint32_t* const ct = rt + 256 * 32;                       // [128 columns][64 dwords]
@@ -1883,6 +1875,7 @@ static ProArgs pro_args(const ProPass& p) {
   a.step = p.step;
   a.step2 = p.step2;
   a.qp = p.qp;
+  a.f8 = p.f8;
   a.scale_out = p.scale_out;
   a.scale_out2 = p.scale_out2;
   a.codes = p.codes;

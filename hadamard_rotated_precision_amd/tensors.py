@@ -64,18 +64,18 @@ class QTensor:
         return None if self.codes_t is None else self.codes_t[:, :self.rows]
 
 
-def config(k, bits, scale_mode, variant):
+def config(k, bits, scale_mode, variant, fmt=B.HQ_FMT_INT):
     c = B.hq_config()
-    c.k, c.bits, c.scale_mode, c.variant = k, bits, scale_mode, variant
+    c.k, c.bits, c.scale_mode, c.variant, c.format = k, bits, scale_mode, variant, fmt
     return c
 
 
 class Layer:
     """Buffers for one linear layer (N tokens, C in, D out) and the three HQ-MM calls."""
 
-    def __init__(self, N, C, D, k, bits, scale_mode, variant, device="cuda"):
+    def __init__(self, N, C, D, k, bits, scale_mode, variant, device="cuda", fmt=B.HQ_FMT_INT):
         self.N, self.C, self.D = N, C, D
-        self.cfg = config(k, bits, scale_mode, variant)
+        self.cfg = config(k, bits, scale_mode, variant, fmt)
         self.variant = variant
         self.ws_bytes = B.hq_workspace_bytes(self.cfg, N, C, D)
         self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=device)

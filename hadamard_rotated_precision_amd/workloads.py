@@ -20,6 +20,7 @@ import numpy as np
 F32, F16, BF16 = 0, 1, 2
 HALO0, HQ, HALO2 = 0, 1, 2
 ABSMAX, STEP = 0, 1
+INT, E4M3 = 0, 1                 # code formats
 DTYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16"}
 
 
@@ -63,10 +64,17 @@ CONFIGS = {
 
 def config(cfg_id, **overrides):
     """A copy of a workload definition; shape keys (N, C, D) may be overridden to draw a
-    smaller tensor with the same distributions."""
+    smaller tensor with the same distributions, and fmt=E4M3 gives the same layer with FP8
+    codes (its name then says fp8)."""
     cfg = dict(CONFIGS[cfg_id])
     cfg["id"] = cfg_id
+    cfg["fmt"] = INT
     cfg.update(overrides)
+    if cfg["fmt"] == E4M3:
+        if cfg["bits"] != 8 or cfg["mode"] != ABSMAX:
+            raise ValueError("FP8 codes are defined for the 8-bit absmax workloads")
+        base = CONFIGS[cfg_id]["name"]
+        cfg["name"] = base.replace("halo2_", "halo2_fp8_").replace("hqmm_", "hqmm_fp8_")
     return cfg
 
 

@@ -40,8 +40,9 @@
  *     Rotations are computed in fp32, except the token-axis rotation of the two-sided
  *     transform (rot BOTH), which sums the fp32 values of V B exactly in fp64 and rounds the
  *     result to fp32 once. Quantization: s = absmax/Qp (fp32) or the given step,
- *     code = clamp(RNE(v * fp32(1/s)), -Qp, Qp), Qp = 127 (bits 8) or 7 (bits 4); a zero
- *     tensor gets s = 0 and all-zero codes. Integer GEMMs accumulate exactly in int32.
+ *     code = clamp(RNE(v * fp32(1/s)), -Qp, Qp), Qp = 127 (bits 8) or 7 (bits 4), or for E4M3
+ *     codes the nearest E4M3 value of v * fp32(1/s) with s = absmax/448; a zero tensor gets
+ *     s = 0 and all-zero codes. Integer GEMMs accumulate exactly in int32, FP8 GEMMs in fp32.
  *     Outputs are rounded to their dtype with round-to-nearest-even.
  */
 #ifndef HQ_H
@@ -54,18 +55,18 @@
 extern "C" {
 #endif
 
-#define HQ_ABI_VERSION 1
+#define HQ_ABI_VERSION 2
 
 typedef enum {
   HQ_OK = 0,
   HQ_ERR_NULL = 1,      /* a required pointer is NULL */
   HQ_ERR_SHAPE = 2,     /* negative dim, or a rotated dim not divisible by k, or shape mismatch */
   HQ_ERR_K = 3,         /* k is not a power of two in [1, 256] */
-  HQ_ERR_BITS = 4,      /* bits is not 4 or 8 */
+  HQ_ERR_BITS = 4,      /* bits is not 4 or 8 (or not 8 for E4M3 codes) */
   HQ_ERR_DTYPE = 5,     /* unsupported dtype */
-  HQ_ERR_MODE = 6,      /* bad rotation, scale mode or variant */
+  HQ_ERR_MODE = 6,      /* bad rotation, scale mode, variant or code format */
   HQ_ERR_WORKSPACE = 7, /* workspace missing or smaller than hq_workspace_bytes() */
-  HQ_ERR_MISMATCH = 8,  /* a saved qtensor does not match the call (k, bits, rot, shape) */
+  HQ_ERR_MISMATCH = 8,  /* a saved qtensor does not match the call (k, bits, rot, format, shape) */
   HQ_ERR_DEVICE = 9,    /* no usable gfx950 device */
   HQ_ERR_LAUNCH = 10,   /* a kernel launch failed */
   HQ_ERR_ALIGN = 11     /* a device pointer or code row pitch is not 16-byte aligned */
@@ -92,27 +93,40 @@ typedef enum { HQ_SCALE_ABSMAX = 0, HQ_SCALE_STEP = 1 } hq_scale_mode;
  *          dW = (qG^T qXt) B_C sG sXt / k^2,   qXt = Q(B_N X B_C) */
 typedef enum { HQ_VARIANT_HALO0 = 0, HQ_VARIANT_HQ = 1, HQ_VARIANT_HALO2 = 2 } hq_variant;
 
+/* Code format (HALO page: the three matmuls run in INT8 or in a floating-point format such as
+ * FP8; an FP8 grid stands in where FP6 hardware is missing, Limitations):
+ * INT:  integer codes on [-Qp, Qp] (bits 8: Qp = 127; bits 4: Qp = 7), integer GEMM with exact
+ *       int32 accumulation;
+ * E4M3: FP8 codes in the OCP E4M3 format (sign, 4-bit exponent with bias 7, 3-bit mantissa,
+ *       subnormals, largest value 448, 0x7F/0xFF unused); bits must be 8. ABSMAX: s =
+ *       absmax/448; a code is the E4M3 value nearest to v * fp32(1/s) (ties to even), saturating
+ *       at +-448. The GEMM multiplies the codes on the matrix cores with fp32 accumulation. */
+typedef enum { HQ_FMT_INT = 0, HQ_FMT_E4M3 = 1 } hq_format;
+
 typedef struct {
   int32_t k;          /* Hadamard block size, power of two in [1, 256] (16..256 in practice) */
-  int32_t bits;       /* 8 (INT8, Qp = 127) or 4 (INT4 range [-7, 7], stored as int8) */
+  int32_t bits;       /* 8 (INT8, Qp = 127; or E4M3) or 4 (INT4 range [-7, 7], stored as int8) */
   int32_t scale_mode; /* hq_scale_mode */
   int32_t variant;    /* hq_variant */
+  int32_t format;     /* hq_format */
 } hq_config;
 
-/* A quantized tensor: int8 codes of a rows x cols matrix plus its device scale.
+/* A quantized tensor: 8-bit codes (int8, or E4M3 bytes) of a rows x cols matrix plus its
+ * device scale.
  * codes   : rows x cols, row pitch `ld` bytes (ld >= cols, ld % 16 == 0), or NULL.
  * codes_t : the transpose (cols x rows), row pitch `ld_t` bytes (ld_t >= rows,
  *           ld_t % 16 == 0), or NULL. It is the K-contiguous copy a backward product
  *           reads (INT4 page §A.6: the integer GEMM wants both operands K-contiguous).
  * Producers write zeros into the pitch padding, so consumers can read whole 16-byte rows.
- * rows, cols, k, bits, rot are written by the producer and checked by every consumer. */
+ * rows, cols, k, bits, rot, format are written by the producer and checked by every
+ * consumer. */
 typedef struct {
   int8_t *codes;
   int8_t *codes_t;
   float *scale; /* one float on the device */
   int64_t rows, cols;
   int64_t ld, ld_t;
-  int32_t k, bits, rot, reserved;
+  int32_t k, bits, rot, format;
 } hq_qtensor;
 
 /* Version of this ABI (HQ_ABI_VERSION). */
@@ -235,6 +249,14 @@ hq_status hq_fwht_path(const void *src, int32_t src_dtype, void *dst, int32_t ds
  *   between K and the next multiple of 16 must be zero. */
 hq_status hq_gemm_i8_i32(const int8_t *a, int64_t lda, const int8_t *b_t, int64_t ldb,
                          int32_t *c, int64_t M, int64_t N, int64_t K, void *stream);
+
+/* Standalone FP8 GEMM with fp32 accumulation (HALO page: FP8 matmuls; INT4 page §A.6 layouts):
+ *   c[m][n] = sum_k a[m][k] * b_t[n][k] over E4M3 codes; a: M x K (pitch lda), b_t: N x K
+ *   (pitch ldb), c: M x N fp32 (pitch N elements). lda, ldb multiples of 16 and >= K; bytes of a
+ *   row between K and the next multiple of 16 must be zero. The products are exact; the sums
+ *   are formed by the matrix cores in fp32 (not bit-reproducible against a sequential sum). */
+hq_status hq_gemm_f8_f32(const uint8_t *a, int64_t lda, const uint8_t *b_t, int64_t ldb,
+                         float *c, int64_t M, int64_t N, int64_t K, void *stream);
 
 /* ---------------------------------------------------------------- instrumentation
  * Optional timing of the library's own kernel launches, for benchmarks (no compute).

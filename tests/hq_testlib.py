@@ -38,13 +38,23 @@ def rel_fro(a, b):
     return float(np.linalg.norm(a - b) / nb)
 
 
-def code_diff(gpu, ref):
-    d = np.abs(gpu.astype(np.int16) - ref.astype(np.int16))
+def code_steps(codes, fmt=O.INT):
+    """Codes as positions on their grid: the integer itself, or for E4M3 bytes the signed
+    magnitude code (adjacent grid values are one apart; +0 and -0 are both 0)."""
+    if fmt == O.E4M3:
+        c = np.asarray(codes).view(np.uint8).astype(np.int16)
+        mag = c & 0x7F
+        return np.where(c & 0x80, -mag, mag)
+    return np.asarray(codes).astype(np.int16)
+
+
+def code_diff(gpu, ref, fmt=O.INT):
+    d = np.abs(code_steps(gpu, fmt) - code_steps(ref, fmt))
     return float((d != 0).mean()) if d.size else 0.0, int(d.max()) if d.size else 0
 
 
-def assert_codes(gpu, ref, what):
-    frac, mx = code_diff(gpu, ref)
+def assert_codes(gpu, ref, what, fmt=O.INT):
+    frac, mx = code_diff(gpu, ref, fmt)
     print("[codes] %s mismatch fraction %.3g (max |diff| %d, %d entries)"
           % (what, frac, mx, gpu.size), flush=True)
     assert mx <= 1 and frac <= CODE_FRAC, "%s: mismatch frac %.3g max %d" % (what, frac, mx)
@@ -109,7 +119,8 @@ def run_gpu(cfg, inputs, out_dt=None):
     N, C, D = cfg["N"], cfg["C"], cfg["D"]
     in_dt = cfg["in_dtype"]
     out_dt = cfg["out_dtype"] if out_dt is None else out_dt
-    layer = T.Layer(N, C, D, cfg["k"], cfg["bits"], cfg["mode"], cfg["variant"], device=dev)
+    layer = T.Layer(N, C, D, cfg["k"], cfg["bits"], cfg["mode"], cfg["variant"], device=dev,
+                    fmt=cfg.get("fmt", O.INT))
     x = T.device_tensor_from_bits(inputs["x"], in_dt, dev)
     w = T.device_tensor_from_bits(inputs["w"], in_dt, dev)
     steps = None
@@ -166,24 +177,26 @@ def run_oracle(cfg, inputs):
     dY = O.decode(inputs["dy"], in_dt) if inputs.get("dy") is not None else None
     steps = inputs.get("steps")
     passes = cfg["passes"]
-    return O.linear(X, W, dY, cfg["k"], cfg["bits"], cfg["variant"], cfg["mode"], steps, passes)
+    return O.linear(X, W, dY, cfg["k"], cfg["bits"], cfg["variant"], cfg["mode"], steps, passes,
+                    fmt=cfg.get("fmt", O.INT))
 
 
 def compare_layer(cfg, h, ora, out_dt):
     """Full comparison of a (small) layer; returns a dict of measured figures."""
     stats = {}
-    stats["qx"] = assert_codes(h["qx"], ora["qx"], "qX")
+    fmt = cfg.get("fmt", O.INT)
+    stats["qx"] = assert_codes(h["qx"], ora["qx"], "qX", fmt)
     assert_scale(h["sx"], ora["sx"], "sX")
-    stats["qw"] = assert_codes(h["qw"], ora["qw"], "qW")
+    stats["qw"] = assert_codes(h["qw"], ora["qw"], "qW", fmt)
     assert_scale(h["sw"], ora["sw"], "sW")
     np.testing.assert_array_equal(h["qw_t"], h["qw"].T)   # both layouts carry the same codes
     if "qx_t" in h:
         np.testing.assert_array_equal(h["qx_t"], h["qx"].T)
     if "qxt_t" in h:
-        stats["qxt"] = assert_codes(h["qxt_t"].T, ora["qxt"], "qXt")
+        stats["qxt"] = assert_codes(h["qxt_t"].T, ora["qxt"], "qXt", fmt)
         assert_scale(h["sxt"], ora["sxt"], "sXt")
     if "qg" in h:
-        stats["qg"] = assert_codes(h["qg"], ora["qg"], "qG")
+        stats["qg"] = assert_codes(h["qg"], ora["qg"], "qG", fmt)
         assert_scale(h["sg"], ora["sg"], "sG")
         np.testing.assert_array_equal(h["qg_t"], h["qg"].T)
     for name in ("y", "dx", "dw"):
@@ -195,14 +208,18 @@ def compare_layer(cfg, h, ora, out_dt):
 def outputs_from_gpu_codes(cfg, h):
     """The oracle's products evaluated on the GPU's own codes and scales (isolates the
     GEMM + epilogue from code flips)."""
-    k, v = cfg["k"], cfg["variant"]
-    out = {"y": O.fwd_from_codes(h["qx"], h["sx"], h["qw"], h["sw"], k, v)}
+    k, v, f = cfg["k"], cfg["variant"], cfg.get("fmt", O.INT)
+    cv = (lambda q: np.asarray(q).view(np.uint8)) if f == O.E4M3 else (lambda q: q)
+    out = {"y": O.fwd_from_codes(cv(h["qx"]), h["sx"], cv(h["qw"]), h["sw"], k, v, fmt=f)}
     if "qg" in h:
         if "dx" in h:
-            out["dx"] = O.bwd_input_from_codes(h["qg"], h["sg"], h["qw"], h["sw"], k, v)
+            out["dx"] = O.bwd_input_from_codes(cv(h["qg"]), h["sg"], cv(h["qw"]), h["sw"], k, v,
+                                               fmt=f)
         if "dw" in h:
             if v == O.HALO2:
-                out["dw"] = O.bwd_weight_from_codes(h["qg"], h["sg"], h["qxt_t"].T, h["sxt"], k, v)
+                out["dw"] = O.bwd_weight_from_codes(cv(h["qg"]), h["sg"], cv(h["qxt_t"].T),
+                                                    h["sxt"], k, v, fmt=f)
             else:
-                out["dw"] = O.bwd_weight_from_codes(h["qg"], h["sg"], h["qx"], h["sx"], k, v)
+                out["dw"] = O.bwd_weight_from_codes(cv(h["qg"]), h["sg"], cv(h["qx"]), h["sx"],
+                                                    k, v, fmt=f)
     return out

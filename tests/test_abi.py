@@ -45,7 +45,7 @@ def test_one_hip_runtime_in_process():
 
 
 def test_version_status_pitch():
-    assert B.hq_abi_version() == 1
+    assert B.hq_abi_version() == 2
     for code in range(12):
         assert isinstance(B.hq_status_string(code), str) and B.hq_status_string(code)
     assert B.hq_status_string(999) == "unknown status"
