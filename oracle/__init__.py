@@ -341,3 +341,37 @@ def linear(X, W, dY, k, bits, variant, mode=ABSMAX, steps=None, passes=("fwd", "
         if "dw" in passes:
             out["dw"] = bwd_weight_from_codes(qg, sg, qxt, sxt, k, variant, fmt=fmt)
     return out
+
+
+# ------------------------------------------------------------ batched products
+def linear_batched(X, W, dY, k, bits, variant, mode=ABSMAX, steps=None,
+                   passes=("fwd", "dx", "dw"), fmt=INT):
+    """Batched HQ-MM ("Training Transformers with 4-bit Integers", §A.1: the batched matmuls of
+    attention use the same quantizers as ordinary ones). X: batch x N x C, W: batch x D x C,
+    dY: batch x N x D (float64). Each batched tensor is quantized as one tensor, stacked along
+    its rows (one scale; right rotations act within rows, token blocks of k rows stay inside a
+    batch since N % k == 0); batch b's products use batch b's codes. Returns stacked codes,
+    scales and per-batch double outputs (batch x ... arrays)."""
+    nb, N, C = X.shape
+    D = W.shape[1]
+    steps = steps or {}
+    out = {}
+    qx, sx, qxt, sxt = quantize_x(X.reshape(nb * N, C), k, bits, variant, mode, steps.get("x"),
+                                  steps.get("xt"), fmt)
+    qw, sw = quantize_w(W.reshape(nb * D, C), k, bits, variant, mode, steps.get("w"), fmt)
+    out.update(qx=qx, sx=sx, qxt=qxt, sxt=sxt, qw=qw, sw=sw)
+    xs = [slice(b * N, (b + 1) * N) for b in range(nb)]
+    ws = [slice(b * D, (b + 1) * D) for b in range(nb)]
+    if "fwd" in passes:
+        out["y"] = np.stack([fwd_from_codes(qx[xs[b]], sx, qw[ws[b]], sw, k, variant, fmt=fmt)
+                             for b in range(nb)])
+    if dY is not None and ("dx" in passes or "dw" in passes):
+        qg, sg = quantize_g(dY.reshape(nb * N, D), k, bits, variant, mode, steps.get("g"), fmt)
+        out.update(qg=qg, sg=sg)
+        if "dx" in passes:
+            out["dx"] = np.stack([bwd_input_from_codes(qg[xs[b]], sg, qw[ws[b]], sw, k, variant,
+                                                       fmt=fmt) for b in range(nb)])
+        if "dw" in passes:
+            out["dw"] = np.stack([bwd_weight_from_codes(qg[xs[b]], sg, qxt[xs[b]], sxt, k,
+                                                        variant, fmt=fmt) for b in range(nb)])
+    return out
