@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_INT8_TOPS = 5000.0     # MI355X dense INT8 MFMA, 5.0 POP/s
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense FP8 MFMA, 5.0 PFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_hbm_traffic.json")
 GEMM_SOURCE = os.path.join(ROOT, "hadamard_rotated_precision_amd", "csrc", "hq_gemm.hip")
 
@@ -141,7 +142,7 @@ def bf16_baseline(cfg, library):
     return ms
 
 
-def fwht_bandwidth(reps=20, rows=8192, cols=13824, ks=(16, 64, 128, 256)):
+def fwht_bandwidth(reps=20, rows=8192, cols=13824, ks=(16, 32, 64, 128, 256)):
     """hq_fwht on its own (bf16 in, bf16 out), RIGHT and LEFT, on the largest operand shape of
     the workloads (X of the 8192 x 13824 x 5120 layer), through the VALU butterflies and the
     matrix cores at each k: algorithmic bytes = 2 B read + 2 B written per element, over the
@@ -175,7 +176,7 @@ def fwht_bandwidth(reps=20, rows=8192, cols=13824, ks=(16, 64, 128, 256)):
                 gbs = 4.0 * rows * cols / (us * 1e-6) / 1e9
                 row[pname] = {"us": round(us, 2), "gbps": round(gbs, 1),
                               "pct_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 1)}
-            auto_matrix = rot == B.HQ_ROT_LEFT or k >= 128
+            auto_matrix = k >= 256 if rot == B.HQ_ROT_RIGHT else k not in (32, 64)
             row["auto"] = "matrix" if auto_matrix else "butterfly"
             res[name]["k%d" % k] = row
     return res
@@ -219,6 +220,89 @@ def layer_vs_bf16(cfg_id):
                       "(the same for the bf16 GEMMs)"}
 
 
+def fp8_step(cfg_id, steps=20):
+    """The same layer step with FP8 (E4M3) codes (HALO page: the FP8 variant of the three
+    matmuls): step time by event median, and the FP8 GEMM's roofline against the 5.0 PFLOP/s
+    dense FP8 peak (algorithmic 2*M*N*K flops per launch over kernel-stamped launch times)."""
+    import torch
+    from hadamard_rotated_precision_amd import binding as B
+    from hadamard_rotated_precision_amd import tensors as T
+    from hadamard_rotated_precision_amd import workloads as WL
+    cfg = WL.config(cfg_id, fmt=WL.E4M3)
+    N, C, D = cfg["N"], cfg["C"], cfg["D"]
+    inputs = WL.make_inputs(cfg)
+    dev = "cuda"
+    in_dt, out_dt = cfg["in_dtype"], cfg["out_dtype"]
+    x = T.device_tensor_from_bits(inputs["x"], in_dt, dev)
+    w = T.device_tensor_from_bits(inputs["w"], in_dt, dev)
+    dy = T.device_tensor_from_bits(inputs["dy"], in_dt, dev)
+    layer = T.Layer(N, C, D, cfg["k"], cfg["bits"], cfg["mode"], cfg["variant"], device=dev,
+                    fmt=B.HQ_FMT_E4M3)
+    odt = T.TORCH_DT[out_dt]
+    y = torch.empty((N, D), dtype=odt, device=dev)
+    dx = torch.empty((N, C), dtype=odt, device=dev)
+    dw = torch.empty((D, C), dtype=odt, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        layer.fwd(x, w, y, None, stream)
+        layer.bwd_input(dy, dx, None, stream)
+        layer.bwd_weight(dw, stream)
+    ms = event_median_ms(step)
+    B.check(B.hq_profile_start(1 << B.HQ_KIND_GEMM), "profile")
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    _, gms, gunits = B.profile_stop_dict()["gemm"]
+    tf = gunits / (gms * 1e-3) / 1e12
+    return {"workload": cfg["name"], "ms_per_step": round(ms, 4),
+            "tflops": round(layer_ops(cfg) / (ms * 1e-3) / 1e12, 1),
+            "gemm_roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_FP8_TFLOPS,
+                              "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4)},
+            "timing": "event median of 20 steps after 5 warm-ups; GEMM launches stamped by "
+                      "hipExtLaunchKernel over %d further steps" % steps}
+
+
+def bmm_step(steps=20):
+    """The batched HQ-MM of attention scores (INT4 page §A.1): S = Q K^T with its two
+    gradients for a Llama-7B-shaped attention layer (4 x 32 heads, 1024 tokens, head_dim 128,
+    k = 128, HALO-2, bf16): step time by event median, effective TOPS and the GEMM roofline."""
+    import torch
+    from hadamard_rotated_precision_amd import binding as B
+    from hadamard_rotated_precision_amd import tensors as T
+    from hadamard_rotated_precision_amd import workloads as WL
+    cfg = WL.attention_config()
+    nb, N, C, D = cfg["batch"], cfg["N"], cfg["C"], cfg["D"]
+    inputs = WL.make_batched_inputs(cfg)
+    dt = cfg["in_dtype"]
+    x = T.device_tensor_from_bits(inputs["x"], dt)
+    w = T.device_tensor_from_bits(inputs["w"], dt)
+    dy = T.device_tensor_from_bits(inputs["dy"], dt)
+    L = T.BatchedLayer(nb, N, C, D, cfg["k"], cfg["bits"], cfg["mode"], cfg["variant"])
+    odt = T.TORCH_DT[cfg["out_dtype"]]
+    y = torch.empty((nb, N, D), dtype=odt, device="cuda")
+    dx = torch.empty((nb, N, C), dtype=odt, device="cuda")
+    dw = torch.empty((nb, D, C), dtype=odt, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        L.fwd(x, w, y, None, stream)
+        L.bwd_input(dy, dx, None, stream)
+        L.bwd_weight(dw, stream)
+    ms = event_median_ms(step)
+    B.check(B.hq_profile_start(1 << B.HQ_KIND_GEMM), "profile")
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    _, gms, gunits = B.profile_stop_dict()["gemm"]
+    tops = gunits / (gms * 1e-3) / 1e12
+    ops = 3 * 2 * nb * N * C * D
+    return {"workload": cfg["name"], "ms_per_step": round(ms, 4),
+            "tops": round(ops / (ms * 1e-3) / 1e12, 1),
+            "gemm_roofline": {"bound": "mfma", "achieved": round(tops, 1), "peak": PEAK_INT8_TOPS,
+                              "unit": "TOP/s", "frac": round(tops / PEAK_INT8_TOPS, 4)}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -234,6 +318,10 @@ def main():
                     help="also time these workloads' steps against three bf16 GEMMs (default "
                          "4,2: the Llama-7B-shaped MLP layer and the 2048 x 4096 x 4096 layer); "
                          "empty to skip")
+    ap.add_argument("--no-bmm", action="store_true",
+                    help="skip the batched (attention) product")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the FP8 (E4M3) step of the same layer")
     ap.add_argument("--no-fwht", action="store_true",
                     help="skip the standalone hq_fwht bandwidth figure")
     ap.add_argument("--no-cold", action="store_true",
@@ -481,6 +569,18 @@ def main():
             result.setdefault("layer_vs_bf16", {})["config%d" % cid] = layer_vs_bf16(cid)
         except Exception as exc:  # report, do not fail the benchmark line
             result.setdefault("layer_vs_bf16", {})["config%d" % cid] = {"error": str(exc)}
+    if not args.no_fp8 and cfg["bits"] == 8 and cfg["mode"] == WL.ABSMAX:
+        print("[bench] fp8 step", file=sys.stderr, flush=True)
+        try:
+            result["fp8_step"] = fp8_step(args.config)
+        except Exception as exc:  # report, do not fail the benchmark line
+            result["fp8_step"] = {"error": str(exc)}
+    if not args.no_bmm:
+        print("[bench] batched attention product", file=sys.stderr, flush=True)
+        try:
+            result["bmm_step"] = bmm_step()
+        except Exception as exc:  # report, do not fail the benchmark line
+            result["bmm_step"] = {"error": str(exc)}
     if not args.no_fwht:
         print("[bench] hq_fwht bandwidth", file=sys.stderr, flush=True)
         try:

@@ -25,7 +25,8 @@ HQ_FMT_INT, HQ_FMT_E4M3 = 0, 1
 EXPORTS = ["hq_abi_version", "hq_status_string", "hq_code_pitch", "hq_workspace_bytes",
            "hq_rotate_quantize", "hq_linear_fwd", "hq_linear_fwd_noalloc", "hq_linear_bwd_input",
            "hq_linear_bwd_weight", "hq_fwht", "hq_fwht_path", "hq_gemm_i8_i32", "hq_gemm_f8_f32",
-           "hq_profile_start", "hq_profile_stop", "hq_profile_records"]
+           "hq_profile_start", "hq_profile_stop", "hq_profile_records",
+           "hq_bmm_workspace_bytes", "hq_bmm_fwd", "hq_bmm_bwd_input", "hq_bmm_bwd_weight"]
 HQ_KIND_GEMM, HQ_KIND_ROT_ABSMAX, HQ_KIND_ROT_QUANT, HQ_KIND_ROT_STORE = 0, 1, 2, 3
 HQ_KIND_TRANSPOSE, HQ_KIND_MISC, HQ_KIND_COUNT = 4, 5, 6
 KIND_NAMES = ["gemm", "rot_absmax", "rot_quant", "rot_store", "transpose", "misc"]
@@ -107,6 +108,17 @@ def load(build_if_missing=True):
                                          P(hq_config), vp, i32, vp, sz, vp]
     lib.hq_fwht.restype = i32
     lib.hq_fwht.argtypes = [vp, i32, vp, i32, i64, i64, i32, i32, vp]
+    lib.hq_bmm_workspace_bytes.restype = sz
+    lib.hq_bmm_workspace_bytes.argtypes = [P(hq_config)]
+    lib.hq_bmm_fwd.restype = i32
+    lib.hq_bmm_fwd.argtypes = [vp, vp, i32, i64, i64, i64, i64, P(hq_config), vp, vp, vp, vp, i32,
+                               P(hq_qtensor), P(hq_qtensor), P(hq_qtensor), vp, sz, vp]
+    lib.hq_bmm_bwd_input.restype = i32
+    lib.hq_bmm_bwd_input.argtypes = [vp, i32, i64, i64, i64, i64, P(hq_config), vp, P(hq_qtensor),
+                                     vp, i32, P(hq_qtensor), vp, sz, vp]
+    lib.hq_bmm_bwd_weight.restype = i32
+    lib.hq_bmm_bwd_weight.argtypes = [P(hq_qtensor), P(hq_qtensor), i64, i64, i64, i64,
+                                      P(hq_config), vp, i32, vp, sz, vp]
     lib.hq_gemm_f8_f32.restype = i32
     lib.hq_gemm_f8_f32.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, vp]
     lib.hq_fwht_path.restype = i32
@@ -184,6 +196,28 @@ def hq_fwht_path(src, src_dtype, dst, dst_dtype, rows, cols, rot, k, path, strea
 
 def hq_gemm_i8_i32(a, lda, b_t, ldb, c, M, N, K, stream):
     return load().hq_gemm_i8_i32(a, lda, b_t, ldb, c, M, N, K, stream)
+
+
+def hq_bmm_workspace_bytes(cfg):
+    return load().hq_bmm_workspace_bytes(ctypes.byref(cfg))
+
+
+def hq_bmm_fwd(x, w, in_dtype, batch, N, C, D, cfg, step_x, step_w, step_xt, y, y_dtype, save_x,
+               save_xt, save_w, ws, ws_bytes, stream):
+    return load().hq_bmm_fwd(x, w, in_dtype, batch, N, C, D, _ref(cfg), step_x, step_w, step_xt,
+                             y, y_dtype, _ref(save_x), _ref(save_xt), _ref(save_w), ws, ws_bytes,
+                             stream)
+
+
+def hq_bmm_bwd_input(dy, dy_dtype, batch, N, C, D, cfg, step_g, saved_w, dx, dx_dtype, save_g, ws,
+                     ws_bytes, stream):
+    return load().hq_bmm_bwd_input(dy, dy_dtype, batch, N, C, D, _ref(cfg), step_g,
+                                   _ref(saved_w), dx, dx_dtype, _ref(save_g), ws, ws_bytes, stream)
+
+
+def hq_bmm_bwd_weight(saved_g, saved_x, batch, N, C, D, cfg, dw, dw_dtype, ws, ws_bytes, stream):
+    return load().hq_bmm_bwd_weight(_ref(saved_g), _ref(saved_x), batch, N, C, D, _ref(cfg), dw,
+                                    dw_dtype, ws, ws_bytes, stream)
 
 
 def hq_gemm_f8_f32(a, lda, b_t, ldb, c, M, N, K, stream):

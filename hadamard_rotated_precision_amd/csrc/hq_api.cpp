@@ -313,38 +313,48 @@ namespace hq {
 
 size_t fwd_workspace_bytes() { return ws_need(); }
 
-// Argument checks of hq_linear_fwd (all but the workspace), before any HIP call.
-hq_status fwd_validate(const void* x, const void* w, int32_t in_dtype, int64_t N, int64_t C,
-                       int64_t D, const hq_config* cfg, const float* step_x,
+// Argument checks of hq_linear_fwd (all but the workspace), before any HIP call. With
+// batch > 1 (hq_bmm_fwd) X, W and Y are batch stacked N x C, D x C and N x D matrices: the
+// codes describe the stacked (batch N) x C and (batch D) x C matrices, N and D must be
+// multiples of 16 so that every batch's block of the transposed code layouts starts on a
+// 16-byte boundary.
+hq_status fwd_validate(const void* x, const void* w, int32_t in_dtype, int64_t batch, int64_t N,
+                       int64_t C, int64_t D, const hq_config* cfg, const float* step_x,
                        const float* step_w, const float* step_xt, const void* y,
                        int32_t y_dtype, const hq_qtensor* save_x, const hq_qtensor* save_xt,
                        const hq_qtensor* save_w) {
   HQ_CHECK(check_cfg(cfg));
   if (!valid_dt(in_dtype) || !valid_dt(y_dtype)) return HQ_ERR_DTYPE;
-  if (N < 0 || C < 0 || D < 0) return HQ_ERR_SHAPE;
+  if (N < 0 || C < 0 || D < 0 || batch < 1 || batch > 65535) return HQ_ERR_SHAPE;
+  if (batch > 1 && (N % 16 || D % 16)) return HQ_ERR_SHAPE;
+  const int64_t NB = batch * N, DB = batch * D;
   const int32_t v = cfg->variant, k = cfg->k;
   if (v != HQ_VARIANT_HALO0 && C % k) return HQ_ERR_SHAPE;
   const bool want_xt = (v == HQ_VARIANT_HALO2) && save_xt != nullptr;
   if (want_xt && N % k) return HQ_ERR_SHAPE;
   const bool stepm = cfg->scale_mode == HQ_SCALE_STEP;
   if (stepm && (!step_x || !step_w || (want_xt && !step_xt))) return HQ_ERR_NULL;
-  if ((N * C > 0 && !x) || (D * C > 0 && !w) || (N * D > 0 && !y)) return HQ_ERR_NULL;
-  HQ_CHECK(check_qt_out(save_x, true, true, N * C));
-  HQ_CHECK(check_qt_out(save_w, true, true, D * C));
-  HQ_CHECK(check_pitches(save_x, N, C));
-  HQ_CHECK(check_pitches(save_w, D, C));
+  if ((NB * C > 0 && !x) || (DB * C > 0 && !w) || (NB * D > 0 && !y)) return HQ_ERR_NULL;
+  HQ_CHECK(check_qt_out(save_x, true, true, NB * C));
+  HQ_CHECK(check_qt_out(save_w, true, true, DB * C));
+  HQ_CHECK(check_pitches(save_x, NB, C));
+  HQ_CHECK(check_pitches(save_w, DB, C));
   if (want_xt) {
-    if (!save_xt->scale || (!save_xt->codes_t && N * C > 0)) return HQ_ERR_NULL;
-    HQ_CHECK(check_pitches(save_xt, N, C));
+    if (!save_xt->scale || (!save_xt->codes_t && NB * C > 0)) return HQ_ERR_NULL;
+    HQ_CHECK(check_pitches(save_xt, NB, C));
   }
   return HQ_OK;
 }
 
 // The launches of the forward on a validated call; ws holds at least fwd_workspace_bytes().
-hq_status fwd_run(const void* x, const void* w, int32_t in_dtype, int64_t N, int64_t C,
-                  int64_t D, const hq_config* cfg, const float* step_x, const float* step_w,
-                  const float* step_xt, void* y, int32_t y_dtype, hq_qtensor* save_x,
-                  hq_qtensor* save_xt, hq_qtensor* save_w, void* ws, void* stream) {
+hq_status fwd_run(const void* x, const void* w, int32_t in_dtype, int64_t batch, int64_t Nb,
+                  int64_t C, int64_t Db, const hq_config* cfg, const float* step_x,
+                  const float* step_w, const float* step_xt, void* y, int32_t y_dtype,
+                  hq_qtensor* save_x, hq_qtensor* save_xt, hq_qtensor* save_w, void* ws,
+                  void* stream) {
+  // the prologue quantizes the stacked matrices (one scale per batched tensor; right rotations
+  // act within rows and token blocks of k rows never cross a batch); the product is batched
+  const int64_t N = batch * Nb, D = batch * Db;
   const int32_t v = cfg->variant, k = cfg->k;
   const bool want_xt = (v == HQ_VARIANT_HALO2) && save_xt != nullptr;
   const bool stepm = cfg->scale_mode == HQ_SCALE_STEP;
@@ -391,12 +401,16 @@ hq_status fwd_run(const void* x, const void* w, int32_t in_dtype, int64_t N, int
   g.lda = save_x->ld;
   g.b = save_w->codes;
   g.ldb = save_w->ld;
-  g.M = N;
-  g.N = D;
+  g.M = Nb;
+  g.N = Db;
   g.K = C;
+  g.batch = static_cast<int>(batch);
+  g.a_bstride = Nb * save_x->ld;
+  g.b_bstride = Db * save_w->ld;
+  g.c_bstride = Nb * Db;
   g.epi = hq::EPI_SCALE;
   g.c = y;
-  g.ldc = D;
+  g.ldc = Db;
   g.out_dt = y_dtype;
   g.sa = save_x->scale;
   g.sb = save_w->scale;
@@ -416,42 +430,52 @@ hq_status hq_linear_fwd(const void* x, const void* w, int32_t in_dtype, int64_t 
                         const float* step_w, const float* step_xt, void* y, int32_t y_dtype,
                         hq_qtensor* save_x, hq_qtensor* save_xt, hq_qtensor* save_w, void* ws,
                         size_t ws_bytes, void* stream) {
-  HQ_CHECK(hq::fwd_validate(x, w, in_dtype, N, C, D, cfg, step_x, step_w, step_xt, y, y_dtype,
-                            save_x, save_xt, save_w));
+  HQ_CHECK(hq::fwd_validate(x, w, in_dtype, 1, N, C, D, cfg, step_x, step_w, step_xt, y,
+                            y_dtype, save_x, save_xt, save_w));
   HQ_CHECK(check_ws(ws, ws_bytes, hq_workspace_bytes(cfg, N, C, D)));
   HQ_CHECK(device_ok());
-  return hq::fwd_run(x, w, in_dtype, N, C, D, cfg, step_x, step_w, step_xt, y, y_dtype, save_x,
-                     save_xt, save_w, ws, stream);
+  return hq::fwd_run(x, w, in_dtype, 1, N, C, D, cfg, step_x, step_w, step_xt, y, y_dtype,
+                     save_x, save_xt, save_w, ws, stream);
 }
 
-hq_status hq_linear_bwd_input(const void* dy, int32_t dy_dtype, int64_t N, int64_t C, int64_t D,
-                              const hq_config* cfg, const float* step_g,
-                              const hq_qtensor* saved_w, void* dx, int32_t dx_dtype,
-                              hq_qtensor* save_g, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The input gradient of a layer (batch == 1) or of a batched product: dY is batch stacked
+// N x D matrices, its codes describe the stacked (batch N) x D matrix, and the product runs per
+// batch against the stacked transposed codes of W (batch D columns).
+hq_status bwd_input_impl(const void* dy, int32_t dy_dtype, int64_t batch, int64_t N, int64_t C,
+                         int64_t D, const hq_config* cfg, const float* step_g,
+                         const hq_qtensor* saved_w, void* dx, int32_t dx_dtype,
+                         hq_qtensor* save_g, void* ws, size_t ws_bytes, size_t ws_min,
+                         void* stream) {
   HQ_CHECK(check_cfg(cfg));
   if (!valid_dt(dy_dtype) || !valid_dt(dx_dtype)) return HQ_ERR_DTYPE;
-  if (N < 0 || C < 0 || D < 0) return HQ_ERR_SHAPE;
+  if (N < 0 || C < 0 || D < 0 || batch < 1 || batch > 65535) return HQ_ERR_SHAPE;
+  if (batch > 1 && (N % 16 || D % 16)) return HQ_ERR_SHAPE;
+  const int64_t NB = batch * N, DB = batch * D;
   const int32_t v = cfg->variant, k = cfg->k;
   if (v != HQ_VARIANT_HALO0 && C % k) return HQ_ERR_SHAPE;
   if (v == HQ_VARIANT_HALO2 && N % k) return HQ_ERR_SHAPE;
   const bool stepm = cfg->scale_mode == HQ_SCALE_STEP;
   if (stepm && !step_g) return HQ_ERR_NULL;
-  if ((N * D > 0 && !dy) || (N * C > 0 && !dx)) return HQ_ERR_NULL;
-  HQ_CHECK(check_saved(saved_w, D, C, cfg, x_rot(v)));
-  HQ_CHECK(check_qt_out(save_g, true, true, N * D));
-  HQ_CHECK(check_pitches(save_g, N, D));
-  HQ_CHECK(check_ws(ws, ws_bytes, hq_workspace_bytes(cfg, N, C, D)));
+  if ((NB * D > 0 && !dy) || (NB * C > 0 && !dx)) return HQ_ERR_NULL;
+  HQ_CHECK(check_saved(saved_w, DB, C, cfg, x_rot(v)));
+  HQ_CHECK(check_qt_out(save_g, true, true, NB * D));
+  HQ_CHECK(check_pitches(save_g, NB, D));
+  HQ_CHECK(check_ws(ws, ws_bytes, ws_min));
   HQ_CHECK(device_ok());
   hipStream_t st = static_cast<hipStream_t>(stream);
   Ws wsp(ws);
   const int32_t rg = g_rot(v);
   // paired dX tiles need their arrival flags at zero: the quantize pass clears them
-  const int64_t split = dx_split_tiles(cfg, N, C, D);
-  HQ_CHECK(quantize_tensor(dy, dy_dtype, N, D, rg, k, cfg, stepm ? step_g : nullptr,
+  const int64_t split = batch == 1 ? dx_split_tiles(cfg, N, C, D) : 0;
+  HQ_CHECK(quantize_tensor(dy, dy_dtype, NB, D, rg, k, cfg, stepm ? step_g : nullptr,
                            save_g->codes, save_g->ld, save_g->codes_t, save_g->ld_t,
                            save_g->scale, wsp, 0, st,
                            split > 0 ? static_cast<int32_t*>(wsp.split) : nullptr, split));
-  fill_meta(save_g, N, D, cfg, rg);
+  fill_meta(save_g, NB, D, cfg, rg);
   // dX = [B_N] (qG qW) [B_C] sG sW / k^e, dequantized and inverse-rotated in the GEMM epilogue.
   GemmPass g;
   g.cus = device_info().cus;
@@ -463,13 +487,17 @@ hq_status hq_linear_bwd_input(const void* dy, int32_t dy_dtype, int64_t N, int64
   g.out_dt = dx_dtype;
   g.ldc = C;
   g.K = D;
+  g.batch = static_cast<int>(batch);
+  g.c_bstride = N * C;
   if (v == HQ_VARIANT_HQ) {
     // only the columns (C) rotate: compute dX^T = qW^T qG^T so C is the tile's row axis,
     // where the epilogue rotates in registers, and store it transposed
     g.a = saved_w->codes_t;
     g.lda = saved_w->ld_t;
+    g.a_bstride = D;                     // batch b: columns b D + [0, D) of the stacked qW^T
     g.b = save_g->codes;
     g.ldb = save_g->ld;
+    g.b_bstride = N * save_g->ld;
     g.M = C;
     g.N = N;
     g.km = k;
@@ -478,8 +506,10 @@ hq_status hq_linear_bwd_input(const void* dy, int32_t dy_dtype, int64_t N, int64
   } else {
     g.a = save_g->codes;
     g.lda = save_g->ld;
+    g.a_bstride = N * save_g->ld;
     g.b = saved_w->codes_t;
     g.ldb = saved_w->ld_t;
+    g.b_bstride = D;
     g.M = N;
     g.N = C;
     if (v == HQ_VARIANT_HALO2) {   // rows (tokens) and columns (C) both rotate
@@ -496,22 +526,26 @@ hq_status hq_linear_bwd_input(const void* dy, int32_t dy_dtype, int64_t N, int64
   return HQ_OK;
 }
 
-hq_status hq_linear_bwd_weight(const hq_qtensor* saved_g, const hq_qtensor* saved_x, int64_t N,
-                               int64_t C, int64_t D, const hq_config* cfg, void* dw,
-                               int32_t dw_dtype, void* ws, size_t ws_bytes, void* stream) {
+// The weight gradient from saved codes only, of a layer or a batched product (the codes of
+// dY and X describe stacked matrices; batch b contracts over its own N tokens).
+hq_status bwd_weight_impl(const hq_qtensor* saved_g, const hq_qtensor* saved_x, int64_t batch,
+                          int64_t N, int64_t C, int64_t D, const hq_config* cfg, void* dw,
+                          int32_t dw_dtype, void* ws, size_t ws_bytes, size_t ws_min,
+                          void* stream) {
   HQ_CHECK(check_cfg(cfg));
   if (!valid_dt(dw_dtype)) return HQ_ERR_DTYPE;
-  if (N < 0 || C < 0 || D < 0) return HQ_ERR_SHAPE;
+  if (N < 0 || C < 0 || D < 0 || batch < 1 || batch > 65535) return HQ_ERR_SHAPE;
+  if (batch > 1 && (N % 16 || D % 16)) return HQ_ERR_SHAPE;
+  const int64_t NB = batch * N;
   const int32_t v = cfg->variant, k = cfg->k;
   if (v != HQ_VARIANT_HALO0 && C % k) return HQ_ERR_SHAPE;
   if (v == HQ_VARIANT_HALO2 && N % k) return HQ_ERR_SHAPE;
-  if (D * C > 0 && !dw) return HQ_ERR_NULL;
-  HQ_CHECK(check_saved(saved_g, N, D, cfg, g_rot(v)));
-  HQ_CHECK(check_saved(saved_x, N, C, cfg, xt_rot(v)));
-  HQ_CHECK(check_ws(ws, ws_bytes, hq_workspace_bytes(cfg, N, C, D)));
+  if (batch * D * C > 0 && !dw) return HQ_ERR_NULL;
+  HQ_CHECK(check_saved(saved_g, NB, D, cfg, g_rot(v)));
+  HQ_CHECK(check_saved(saved_x, NB, C, cfg, xt_rot(v)));
+  HQ_CHECK(check_ws(ws, ws_bytes, ws_min));
   HQ_CHECK(device_ok());
   hipStream_t st = static_cast<hipStream_t>(stream);
-  Ws wsp(ws);
   // dW = (qG^T qX') [B_C] sG sX' / k^e. When C rotates, compute dW^T = qX'^T qG so C is the
   // tile's row axis (rotated in registers) and store it transposed.
   GemmPass g;
@@ -524,6 +558,10 @@ hq_status hq_linear_bwd_weight(const hq_qtensor* saved_g, const hq_qtensor* save
   g.out_dt = dw_dtype;
   g.ldc = C;
   g.K = N;
+  g.batch = static_cast<int>(batch);
+  g.a_bstride = N;                       // batch b: columns b N + [0, N) of both operands
+  g.b_bstride = N;
+  g.c_bstride = D * C;
   if (v == HQ_VARIANT_HALO0) {
     g.a = saved_g->codes_t;
     g.lda = saved_g->ld_t;
@@ -544,6 +582,60 @@ hq_status hq_linear_bwd_weight(const hq_qtensor* saved_g, const hq_qtensor* save
   }
   HQ_TRY(hq::gemm_pass(g, st));
   return HQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hq_status hq_linear_bwd_input(const void* dy, int32_t dy_dtype, int64_t N, int64_t C, int64_t D,
+                              const hq_config* cfg, const float* step_g,
+                              const hq_qtensor* saved_w, void* dx, int32_t dx_dtype,
+                              hq_qtensor* save_g, void* ws, size_t ws_bytes, void* stream) {
+  const size_t need = cfg ? hq_workspace_bytes(cfg, N, C, D) : 0;
+  return bwd_input_impl(dy, dy_dtype, 1, N, C, D, cfg, step_g, saved_w, dx, dx_dtype, save_g, ws,
+                        ws_bytes, need, stream);
+}
+
+hq_status hq_linear_bwd_weight(const hq_qtensor* saved_g, const hq_qtensor* saved_x, int64_t N,
+                               int64_t C, int64_t D, const hq_config* cfg, void* dw,
+                               int32_t dw_dtype, void* ws, size_t ws_bytes, void* stream) {
+  const size_t need = cfg ? hq_workspace_bytes(cfg, N, C, D) : 0;
+  return bwd_weight_impl(saved_g, saved_x, 1, N, C, D, cfg, dw, dw_dtype, ws, ws_bytes, need,
+                         stream);
+}
+
+size_t hq_bmm_workspace_bytes(const hq_config* cfg) {
+  if (check_cfg(cfg) != HQ_OK) return 0;
+  return ws_need();
+}
+
+hq_status hq_bmm_fwd(const void* x, const void* w, int32_t in_dtype, int64_t batch, int64_t N,
+                     int64_t C, int64_t D, const hq_config* cfg, const float* step_x,
+                     const float* step_w, const float* step_xt, void* y, int32_t y_dtype,
+                     hq_qtensor* save_x, hq_qtensor* save_xt, hq_qtensor* save_w, void* ws,
+                     size_t ws_bytes, void* stream) {
+  HQ_CHECK(hq::fwd_validate(x, w, in_dtype, batch, N, C, D, cfg, step_x, step_w, step_xt, y,
+                            y_dtype, save_x, save_xt, save_w));
+  HQ_CHECK(check_ws(ws, ws_bytes, ws_need()));
+  HQ_CHECK(device_ok());
+  return hq::fwd_run(x, w, in_dtype, batch, N, C, D, cfg, step_x, step_w, step_xt, y, y_dtype,
+                     save_x, save_xt, save_w, ws, stream);
+}
+
+hq_status hq_bmm_bwd_input(const void* dy, int32_t dy_dtype, int64_t batch, int64_t N, int64_t C,
+                           int64_t D, const hq_config* cfg, const float* step_g,
+                           const hq_qtensor* saved_w, void* dx, int32_t dx_dtype,
+                           hq_qtensor* save_g, void* ws, size_t ws_bytes, void* stream) {
+  return bwd_input_impl(dy, dy_dtype, batch, N, C, D, cfg, step_g, saved_w, dx, dx_dtype, save_g,
+                        ws, ws_bytes, ws_need(), stream);
+}
+
+hq_status hq_bmm_bwd_weight(const hq_qtensor* saved_g, const hq_qtensor* saved_x, int64_t batch,
+                            int64_t N, int64_t C, int64_t D, const hq_config* cfg, void* dw,
+                            int32_t dw_dtype, void* ws, size_t ws_bytes, void* stream) {
+  return bwd_weight_impl(saved_g, saved_x, batch, N, C, D, cfg, dw, dw_dtype, ws, ws_bytes,
+                         ws_need(), stream);
 }
 
 hq_status hq_fwht_path(const void* src, int32_t src_dtype, void* dst, int32_t dst_dtype,
@@ -567,11 +659,15 @@ hq_status hq_fwht_path(const void* src, int32_t src_dtype, void* dst, int32_t ds
   if (rows * cols == 0) return HQ_OK;
   HQ_CHECK(device_ok());
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // AUTO: the matrix cores for every token-axis (LEFT) rotation they cover, and for RIGHT at
-  // k >= 128, where they were measured faster than the butterflies; butterflies elsewhere
-  const bool use_left_mma = left_mma && path != HQ_FWHT_BUTTERFLY;
+  // AUTO follows the measured 8192 x 13824 bf16 transforms: the butterflies wherever they are
+  // within 5 % of the matrix cores (RIGHT up to k = 128, LEFT at k = 32 and 64), the matrix
+  // cores otherwise (RIGHT k = 256: 8 % faster; LEFT k = 16, 128, 256: 23-44 % faster)
+  const bool auto_left_mma = k != 32 && k != 64;
+  const bool auto_right_mma = k >= 256;
+  const bool use_left_mma =
+      left_mma && (path == HQ_FWHT_MATRIX || (path == HQ_FWHT_AUTO && auto_left_mma));
   const bool use_right_mma =
-      right_mma && (path == HQ_FWHT_MATRIX || (path == HQ_FWHT_AUTO && k >= 128));
+      right_mma && (path == HQ_FWHT_MATRIX || (path == HQ_FWHT_AUTO && auto_right_mma));
   if (use_left_mma) {
     HQ_TRY(hq::fwht_left_mma(src, src_dtype, rows, cols, k, dst, st));
     return HQ_OK;

@@ -71,6 +71,9 @@ struct GemmArgs {
   float* pair_part;      // PAIR: 2 fp32 partial tiles per pair of 256 x 128 tiles
   int32_t* pair_cnt;     // PAIR: arrival flags per pair (zero on entry, left set)
   int pair_spin;         // PAIR: polls of the partner's flag before the wait-free fallback
+  // batched products (grid.y = batch index): offsets of a batch's a and b (bytes) and c
+  // (elements); the scales are shared (one per batched tensor)
+  int64_t a_bstride, b_bstride, c_bstride;
 };
 
 
@@ -166,6 +169,12 @@ template <int BN> struct GemmShape {
 
 template <int BN, class Out, int EPI, int KM, int KN, bool TRANS, bool PAIR, bool F8>
 __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs g) {
+  if (blockIdx.y > 0) {   // batch blockIdx.y of a batched product (never with tile pairs)
+    g.a += blockIdx.y * g.a_bstride;
+    g.b += blockIdx.y * g.b_bstride;
+    const size_t esz = (EPI == EPI_I32) ? 4 : Out::bytes;
+    g.c = static_cast<char*>(g.c) + static_cast<size_t>(blockIdx.y) * g.c_bstride * esz;
+  }
   constexpr int NT = GemmShape<BN>::NT;   // 512: two waves per SIMD
   constexpr int NW = GemmShape<BN>::NW;
   constexpr int WN = GemmShape<BN>::WN;   // wave tile columns
@@ -694,37 +703,37 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs 
 }
 
 template <int BN, class Out, int EPI, int KM, int KN, bool TRANS, bool PAIR, bool F8>
-static hipError_t launch_gemm(const GemmArgs& a, hipStream_t st, int tok) {
+static hipError_t launch_gemm(const GemmArgs& a, hipStream_t st, int tok, int batch) {
   const int64_t tiles = ((a.M + GBM - 1) / GBM) * ((a.N + BN - 1) / BN);
   return launch_k(gemm_i8_kernel<BN, Out, EPI, KM, KN, TRANS, PAIR, F8>,
-                  dim3(static_cast<int>(tiles)), dim3(GemmShape<BN>::NT), st, tok, a);
+                  dim3(static_cast<int>(tiles), batch), dim3(GemmShape<BN>::NT), st, tok, a);
 }
 
 template <int BN, class Out, bool F8>
 static hipError_t launch_out(const GemmPass& p, const GemmArgs& a, hipStream_t st, int tok) {
   if (p.trans_out) {
     switch (p.km) {
-#define HQ_T(KK) case KK: return launch_gemm<BN, Out, EPI_SCALE, KK, 1, true, false, F8>(a, st, tok);
+#define HQ_T(KK) case KK: return launch_gemm<BN, Out, EPI_SCALE, KK, 1, true, false, F8>(a, st, tok, p.batch);
       HQ_T(1) HQ_T(2) HQ_T(4) HQ_T(8) HQ_T(16) HQ_T(32) HQ_T(64) HQ_T(128) HQ_T(256)
 #undef HQ_T
     }
     return hipErrorInvalidValue;
   }
-  if (p.km == 1 && p.kn == 1) return launch_gemm<BN, Out, EPI_SCALE, 1, 1, false, false, F8>(a, st, tok);
+  if (p.km == 1 && p.kn == 1) return launch_gemm<BN, Out, EPI_SCALE, 1, 1, false, false, F8>(a, st, tok, p.batch);
   if (p.km != p.kn) return hipErrorInvalidValue;
   if constexpr (BN == 128) {
     // column blocks up to 128 wide rotate inside the tile; 256-wide ones span a tile pair
     switch (p.km) {
-#define HQ_B(KK) case KK: return launch_gemm<BN, Out, EPI_SCALE, KK, KK, false, false, F8>(a, st, tok);
+#define HQ_B(KK) case KK: return launch_gemm<BN, Out, EPI_SCALE, KK, KK, false, false, F8>(a, st, tok, p.batch);
       HQ_B(2) HQ_B(4) HQ_B(8) HQ_B(16) HQ_B(32) HQ_B(64) HQ_B(128)
 #undef HQ_B
       case 256:
         if (!a.pair_part) return hipErrorInvalidValue;
-        return launch_gemm<BN, Out, EPI_SCALE, 256, 256, false, true, F8>(a, st, tok);
+        return launch_gemm<BN, Out, EPI_SCALE, 256, 256, false, true, F8>(a, st, tok, p.batch);
     }
   } else {
     switch (p.km) {
-#define HQ_B(KK) case KK: return launch_gemm<BN, Out, EPI_SCALE, KK, KK, false, false, F8>(a, st, tok);
+#define HQ_B(KK) case KK: return launch_gemm<BN, Out, EPI_SCALE, KK, KK, false, false, F8>(a, st, tok, p.batch);
       HQ_B(2) HQ_B(4) HQ_B(8) HQ_B(16) HQ_B(32) HQ_B(64) HQ_B(128) HQ_B(256)
 #undef HQ_B
     }
@@ -780,12 +789,14 @@ size_t gemm_split_bytes(int64_t pairs) {
 
 hipError_t gemm_pass(const GemmPass& p, hipStream_t st) {
   GemmArgs a{p.a, p.lda, p.b, p.ldb, p.M, p.N, p.K, p.c, p.ldc, p.sa, p.sb, p.kmul,
-             nullptr, nullptr, 40};
+             nullptr, nullptr, 40, p.a_bstride, p.b_bstride, p.c_bstride};
+  if (p.batch < 1 || p.batch > 65535) return hipErrorInvalidValue;
   // Test hook: HQ_PAIR_SPIN bounds the tile-pair wait (40 polls of ~0.5 us by default); 0 makes
   // every early tile take the wait-free fallback, which tests use to cover that path.
   if (const char* e = std::getenv("HQ_PAIR_SPIN")) a.pair_spin = std::max(0, std::atoi(e));
   if (p.M == 0 || p.N == 0) return hipSuccess;
-  const int64_t pairs = gemm_split_tiles(p.M, p.N, p.K, p.epi, p.km, p.kn, p.trans_out);
+  const int64_t pairs =
+      p.batch > 1 ? 0 : gemm_split_tiles(p.M, p.N, p.K, p.epi, p.km, p.kn, p.trans_out);
   if (pairs > 0) {
     if (!p.split_ws) return hipErrorInvalidValue;
     a.pair_cnt = static_cast<int32_t*>(p.split_ws);
@@ -799,13 +810,17 @@ hipError_t gemm_pass(const GemmPass& p, hipStream_t st) {
   if (static_cast<int64_t>(GBM) * p.lda >= kOutOfRange || 256 * p.ldb >= kOutOfRange)
     return hipErrorInvalidValue;
   const int kn = p.epi == EPI_I32 ? 1 : p.kn;
-  const bool narrow = use_narrow(p.M, p.N, kn, p.trans_out);
+  // batched: every batch's tiles count towards filling the device; 256-wide column blocks
+  // stay inside one tile (no tile pairs across a batch), and there is no tail launch
+  const bool narrow = p.batch > 1
+                          ? (((p.M + GBM - 1) / GBM) * ((p.N + 255) / 256) * p.batch < 256 && kn <= 128)
+                          : use_narrow(p.M, p.N, kn, p.trans_out);
   auto launch_fmt = [&](bool nar, const GemmArgs& g, auto f8) -> hipError_t {
     constexpr bool F8 = decltype(f8)::value;
-    const int tok = prof_open(K_GEMM, 2.0 * g.M * g.N * g.K);
+    const int tok = prof_open(K_GEMM, 2.0 * g.M * g.N * g.K * p.batch);
     if (p.epi == EPI_I32)
-      return nar ? launch_gemm<128, F32, EPI_I32, 1, 1, false, false, F8>(g, st, tok)
-                 : launch_gemm<256, F32, EPI_I32, 1, 1, false, false, F8>(g, st, tok);
+      return nar ? launch_gemm<128, F32, EPI_I32, 1, 1, false, false, F8>(g, st, tok, p.batch)
+                 : launch_gemm<256, F32, EPI_I32, 1, 1, false, false, F8>(g, st, tok, p.batch);
     switch (p.out_dt) {
       case DT_F32: return nar ? launch_out<128, F32, F8>(p, g, st, tok) : launch_out<256, F32, F8>(p, g, st, tok);
       case DT_F16: return nar ? launch_out<128, F16, F8>(p, g, st, tok) : launch_out<256, F16, F8>(p, g, st, tok);
@@ -816,7 +831,7 @@ hipError_t gemm_pass(const GemmPass& p, hipStream_t st) {
   auto launch = [&](bool nar, const GemmArgs& g) {
     return p.f8 ? launch_fmt(nar, g, std::true_type{}) : launch_fmt(nar, g, std::false_type{});
   };
-  if (!narrow && kn <= 128) {
+  if (!narrow && kn <= 128 && p.batch == 1) {
     // 256-wide tiles over columns [0, N1), then 128-wide ones over [N1, N) when that fills the
     // rounds better (N1 is a multiple of 256, so rotation blocks stay whole in each part)
     const int64_t tm = (p.M + GBM - 1) / GBM, tn = (p.N + 255) / 256;

@@ -13,20 +13,24 @@ namespace hq {
 // brings its own scratch: fwd_validate runs every argument check except the workspace's;
 // fwd_run launches the passes on a validated call with a workspace of at least
 // fwd_workspace_bytes() bytes. device_ready: HQ_OK when the current device is usable.
+// batch > 1: the batched product of hq_bmm_fwd (N and D per batch).
 size_t fwd_workspace_bytes();
-hq_status fwd_validate(const void* x, const void* w, int32_t in_dtype, int64_t N, int64_t C,
-                       int64_t D, const hq_config* cfg, const float* step_x,
+hq_status fwd_validate(const void* x, const void* w, int32_t in_dtype, int64_t batch, int64_t N,
+                       int64_t C, int64_t D, const hq_config* cfg, const float* step_x,
                        const float* step_w, const float* step_xt, const void* y,
                        int32_t y_dtype, const hq_qtensor* save_x, const hq_qtensor* save_xt,
                        const hq_qtensor* save_w);
-hq_status fwd_run(const void* x, const void* w, int32_t in_dtype, int64_t N, int64_t C,
-                  int64_t D, const hq_config* cfg, const float* step_x, const float* step_w,
-                  const float* step_xt, void* y, int32_t y_dtype, hq_qtensor* save_x,
-                  hq_qtensor* save_xt, hq_qtensor* save_w, void* ws, void* stream);
+hq_status fwd_run(const void* x, const void* w, int32_t in_dtype, int64_t batch, int64_t N,
+                  int64_t C, int64_t D, const hq_config* cfg, const float* step_x,
+                  const float* step_w, const float* step_xt, void* y, int32_t y_dtype,
+                  hq_qtensor* save_x, hq_qtensor* save_xt, hq_qtensor* save_w, void* ws,
+                  void* stream);
 hq_status device_ready();
 
 // OP_STORE: the transform alone, rotated values written in the input dtype (hq_fwht).
-enum Op : int { OP_ABSMAX = 0, OP_QUANT = 1, OP_STORE = 2 };
+// OP_QUANT_F8: the quantize pass writing FP8 E4M3 codes (pro_pass picks it from ProPass::f8);
+// the format is a compile-time choice so each kernel carries one quantizer.
+enum Op : int { OP_ABSMAX = 0, OP_QUANT = 1, OP_STORE = 2, OP_QUANT_F8 = 3 };
 
 // Most partial maxima one absmax pass writes (its grid is capped to this).
 constexpr int kMaxPartials = 1024;
@@ -125,6 +129,9 @@ struct GemmPass {
   bool split_cnt_zeroed = false;  // its arrival flags were zeroed by an earlier launch on the stream
   int cus = 0;             // compute units of the device (0: assume 256), for the tile rounds
   bool f8 = false;         // operands are FP8 E4M3 codes (fp32 accumulation; EPI_I32 stores fp32)
+  int batch = 1;           // batched product: batch b reads a + b a_bstride, b + b b_bstride
+  int64_t a_bstride = 0, b_bstride = 0;   // (bytes) and writes c + b c_bstride (elements)
+  int64_t c_bstride = 0;
 };
 hipError_t gemm_pass(const GemmPass& p, hipStream_t st);
 // Number of tile pairs of a GEMM whose 256-wide column rotation spans two 256 x 128 tiles

@@ -74,7 +74,6 @@ struct ProArgs {
   const float* step;        // QUANT, STEP mode (right / left rotation, or X B for both_kernel)
   const float* step2;       // both_kernel, STEP mode: step of B X B
   int qp;                   // grid bound: 127 / 7 for integer codes, 448 for E4M3 codes
-  bool f8;                  // codes are FP8 E4M3 (quant4 / quant_byte), else integers
   float* scale_out;
   float* scale_out2;        // both_kernel: scale of B X B
   int8_t* codes;            // row-major codes (pitch ld) or nullptr
@@ -95,6 +94,9 @@ struct ProArgs {
 constexpr int kBarGroups = 8, kBarStride = 32, kGroupDone = 256, kReleaseWord = 288,
               kStateAborted = 2;
 
+// A quantize pass (integer or FP8 codes).
+__host__ __device__ constexpr bool quant_op(int op) { return op == OP_QUANT || op == OP_QUANT_F8; }
+
 // Counters a later launch on the stream needs at zero (the split-K arrivals of the GEMM).
 __device__ inline void zero_side(const ProArgs& a) {
   if (a.zero_n > 0 && blockIdx.x == 0)
@@ -113,7 +115,7 @@ __global__ __launch_bounds__(RT_THREADS) void right_kernel(ProArgs a) {
   const int64_t nrt = (a.rows + RT_ROWS - 1) / RT_ROWS, nct = (a.cols + RT_COLS - 1) / RT_COLS;
   const int64_t tiles = nrt * nct;
   float sc = 0.0f, rinv = 0.0f;
-  if constexpr (OP == OP_QUANT) {
+  if constexpr (quant_op(OP)) {
     tensor_scale(a.part_in, a.nparts, a.step, a.qp, red, sc, rinv);
     zero_side(a);
     if (blockIdx.x == 0 && t == 0) *a.scale_out = sc;
@@ -143,13 +145,13 @@ __global__ __launch_bounds__(RT_THREADS) void right_kernel(ProArgs a) {
         const int64_t cpad = (a.cols + 15) / 16 * 16;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          if (gc + 16 * q < cpad) *reinterpret_cast<uint4*>(dst + 16 * q) = pack16(v, 16 * q, rinv, a.qp, a.f8);
+          if (gc + 16 * q < cpad) *reinterpret_cast<uint4*>(dst + 16 * q) = pack16(v, 16 * q, rinv, a.qp, (OP == OP_QUANT_F8));
       }
       if (a.codes_t) {
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < 64; ++j)
-          tcodes[64 * s + j][r] = static_cast<int8_t>(quant_byte(v[j], rinv, a.qp, a.f8));
+          tcodes[64 * s + j][r] = static_cast<int8_t>(quant_byte(v[j], rinv, a.qp, (OP == OP_QUANT_F8)));
         __syncthreads();
         // thread t writes transposed row col0 + t: 64 bytes = tile rows row0 .. row0+63
         const int64_t orow = col0 + t;
@@ -314,7 +316,7 @@ __global__ __launch_bounds__(RF_THREADS) void right_fast_kernel(ProArgs a) {
   const uint32_t nct = static_cast<uint32_t>(a.cols / RF_COLS);
   const uint32_t tiles = static_cast<uint32_t>(a.rows / RF_ROWS) * nct;   // < 2^31 (host checks)
   float sc = 0.0f, rinv = 0.0f;
-  if constexpr (OP == OP_QUANT) {
+  if constexpr (quant_op(OP)) {
     tensor_scale(a.part_in, a.nparts, a.step, a.qp, red, sc, rinv);
     zero_side(a);
     if (blockIdx.x == 0 && t == 0) *a.scale_out = sc;
@@ -351,7 +353,7 @@ __global__ __launch_bounds__(RF_THREADS) void right_fast_kernel(ProArgs a) {
       uint32_t d[16];   // d[g]: columns 32(g/2) + 8s + 4(g%2) + 0..3
 #pragma unroll
       for (int g = 0; g < 16; ++g)
-        d[g] = quant4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3], rr, lo, hi, a.f8);
+        d[g] = quant4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3], rr, lo, hi, (OP == OP_QUANT_F8));
       const uint32_t tr = tl / nct;
       const int64_t row0 = static_cast<int64_t>(tr) * RF_ROWS;
       const int64_t col0 = static_cast<int64_t>(tl - tr * nct) * RF_COLS;
@@ -538,7 +540,7 @@ __global__ __launch_bounds__(RM_THREADS, 2) void right_mma_kernel(ProArgs a) {
     const uint32_t nct = static_cast<uint32_t>(a.cols / RM_COLS);
     const uint32_t tiles = static_cast<uint32_t>(a.rows / RM_ROWS) * nct;   // < 2^31 (host checks)
     float sc = 0.0f, rinv = 0.0f;
-    if constexpr (OP == OP_QUANT) {
+    if constexpr (quant_op(OP)) {
       tensor_scale(a.part_in, a.nparts, a.step, a.qp, red, sc, rinv);
       zero_side(a);
       if (blockIdx.x == 0 && t == 0) *a.scale_out = sc;
@@ -612,7 +614,7 @@ __global__ __launch_bounds__(RM_THREADS, 2) void right_mma_kernel(ProArgs a) {
         uint32_t d[16];   // rows 4lg + [0, 4) of column 16nb + n0
 #pragma unroll
         for (int nb = 0; nb < 16; ++nb)
-          d[nb] = quant4(acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3], rinv, lo, hi, a.f8);
+          d[nb] = quant4(acc[nb][0], acc[nb][1], acc[nb][2], acc[nb][3], rinv, lo, hi, (OP == OP_QUANT_F8));
         const uint32_t tr = tl / nct;
         const int64_t row0 = static_cast<int64_t>(tr) * RM_ROWS;
         const int64_t col0 = static_cast<int64_t>(tl - tr * nct) * RM_COLS;
@@ -689,7 +691,7 @@ __global__ __launch_bounds__(LT_THREADS) void left_kernel(ProArgs a) {
   const int64_t nrt = (a.rows + TR - 1) / TR, nct = (a.cols + TC - 1) / TC;
   const int64_t tiles = nrt * nct;
   float sc = 0.0f, rinv = 0.0f;
-  if constexpr (OP == OP_QUANT) {
+  if constexpr (quant_op(OP)) {
     tensor_scale(a.part_in, a.nparts, a.step, a.qp, red, sc, rinv);
     zero_side(a);
     if (blockIdx.x == 0 && t == 0) *a.scale_out = sc;
@@ -750,13 +752,13 @@ __global__ __launch_bounds__(LT_THREADS) void left_kernel(ProArgs a) {
         int8_t* dst = a.codes_t + gcol * a.ld_t + row0 + 64 * p;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          if (row0 + 64 * p + 16 * q < rpad) *reinterpret_cast<uint4*>(dst + 16 * q) = pack16(v, 16 * q, rinv, a.qp, a.f8);
+          if (row0 + 64 * p + 16 * q < rpad) *reinterpret_cast<uint4*>(dst + 16 * q) = pack16(v, 16 * q, rinv, a.qp, (OP == OP_QUANT_F8));
       }
       if (a.codes) {
         __syncthreads();   // the fp32 tile is dead: reuse it for the byte transpose
 #pragma unroll
         for (int i = 0; i < 64; ++i)
-          bcodes[(64 * p + i) * BP + c] = static_cast<int8_t>(quant_byte(v[i], rinv, a.qp, a.f8));
+          bcodes[(64 * p + i) * BP + c] = static_cast<int8_t>(quant_byte(v[i], rinv, a.qp, (OP == OP_QUANT_F8)));
         __syncthreads();
         for (int q = t; q < TR * TC / 16; q += LT_THREADS) {
           const int row = q / (TC / 16), cc = 16 * (q % (TC / 16));
@@ -809,7 +811,7 @@ __global__ __launch_bounds__(LF_THREADS, 2) void left_fast_kernel(ProArgs a) {
   const uint32_t nct = static_cast<uint32_t>(a.cols / LF_COLS);
   const uint32_t tiles = static_cast<uint32_t>(a.rows / LF_ROWS) * nct;   // < 2^31 (host checks)
   float sc = 0.0f, rinv = 0.0f;
-  if constexpr (OP == OP_QUANT) {
+  if constexpr (quant_op(OP)) {
     tensor_scale(a.part_in, a.nparts, a.step, a.qp, red, sc, rinv);
     zero_side(a);
     if (blockIdx.x == 0 && t == 0) *a.scale_out = sc;
@@ -865,7 +867,7 @@ __global__ __launch_bounds__(LF_THREADS, 2) void left_fast_kernel(ProArgs a) {
       uint32_t d[16];   // d[g]: tokens 64 p + 4 g + [0, 4) of column c
 #pragma unroll
       for (int g = 0; g < 16; ++g)
-        d[g] = quant4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3], rr, lo, hi, a.f8);
+        d[g] = quant4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3], rr, lo, hi, (OP == OP_QUANT_F8));
       const uint32_t tr = tl / nct;
       const int64_t row0 = static_cast<int64_t>(tr) * LF_ROWS;
       const int64_t col0 = static_cast<int64_t>(tl - tr * nct) * LF_COLS;
@@ -969,7 +971,7 @@ __global__ __launch_bounds__(LM_THREADS, 2) void left_mma_kernel(ProArgs a) {
     const uint32_t nct = static_cast<uint32_t>(a.cols / LM_COLS);
     const uint32_t tiles = static_cast<uint32_t>(a.rows / LM_ROWS) * nct;   // < 2^31 (host checks)
     float sc = 0.0f, rinv = 0.0f;
-    if constexpr (OP == OP_QUANT) {
+    if constexpr (quant_op(OP)) {
       tensor_scale(a.part_in, a.nparts, a.step, a.qp, red, sc, rinv);
       zero_side(a);
       if (blockIdx.x == 0 && t == 0) *a.scale_out = sc;
@@ -1069,7 +1071,7 @@ __global__ __launch_bounds__(LM_THREADS, 2) void left_mma_kernel(ProArgs a) {
         uint32_t d[16];   // rows 16mb + 4lg + [0, 4) of column 16w + n0
 #pragma unroll
         for (int mb = 0; mb < 16; ++mb)
-          d[mb] = quant4(acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3], rinv, lo, hi, a.f8);
+          d[mb] = quant4(acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3], rinv, lo, hi, (OP == OP_QUANT_F8));
         const uint32_t tr = tl / nct;
         const int64_t row0 = static_cast<int64_t>(tr) * LM_ROWS;
         const int64_t col0 = static_cast<int64_t>(tl - tr * nct) * LM_COLS;
@@ -1199,7 +1201,7 @@ __global__ __launch_bounds__(BT_THREADS) void both_kernel(ProArgs a) {
   const int64_t nct = (a.cols + BT - 1) / BT;
   const int64_t items = both_items(a.rows, a.cols);
   float s1 = 0.0f, r1 = 0.0f, sc2 = 0.0f, r2 = 0.0f;
-  if constexpr (OP == OP_QUANT) {
+  if constexpr (quant_op(OP)) {
     tensor_scale(a.part_in, a.nparts, a.step, a.qp, red, s1, r1);
     tensor_scale(a.part_in2, a.nparts, a.step2, a.qp, red, sc2, r2);
     zero_side(a);
@@ -1269,7 +1271,7 @@ __global__ __launch_bounds__(BT_THREADS) void both_kernel(ProArgs a) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int i = 16 * q + 4 * j;
-            x[j] = quant4(w[i], w[i + 1], w[i + 2], w[i + 3], r1, lo, hi, a.f8);
+            x[j] = quant4(w[i], w[i + 1], w[i + 2], w[i + 3], r1, lo, hi, (OP == OP_QUANT_F8));
           }
           *reinterpret_cast<uint4*>(dst + 16 * q) = make_uint4(x[0], x[1], x[2], x[3]);
         }
@@ -1308,7 +1310,7 @@ __global__ __launch_bounds__(BT_THREADS) void both_kernel(ProArgs a) {
             const int i = 16 * q + 4 * j;
             x[j] = quant4(static_cast<float>(u[i]), static_cast<float>(u[i + 1]),
                           static_cast<float>(u[i + 2]), static_cast<float>(u[i + 3]), r2, lo, hi,
-                          a.f8);
+                          (OP == OP_QUANT_F8));
           }
           *reinterpret_cast<uint4*>(dst + 16 * q) = make_uint4(x[0], x[1], x[2], x[3]);
         }
@@ -1364,7 +1366,7 @@ __device__ inline void both_mma_body(const ProArgs& a) {
     const int64_t nct = a.cols / BT;
     const int64_t items = both_items(a.rows, a.cols);
     float s1 = 0.0f, r1 = 0.0f, sc2 = 0.0f, r2 = 0.0f;
-    if constexpr (OP == OP_QUANT) {
+    if constexpr (quant_op(OP)) {
       // the fallback pass after the single-pass kernel: nothing to do unless it aborted
       if (a.bar != nullptr && __hip_atomic_load(&a.bar[kReleaseWord], __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_AGENT) != kStateAborted)
@@ -1474,7 +1476,7 @@ __device__ inline void both_mma_body(const ProArgs& a) {
           int8_t* dst = a.codes + (row0 + rloc + 4 * lg + i) * a.ld + col0 + BT_HALF * h + 4 * m;
 #pragma unroll
           for (int nb = 0; nb < 8; ++nb) {
-            const uint32_t d = quant4(y[nb][0], y[nb][1], y[nb][2], y[nb][3], r1, lo, hi, a.f8);
+            const uint32_t d = quant4(y[nb][0], y[nb][1], y[nb][2], y[nb][3], r1, lo, hi, (OP == OP_QUANT_F8));
             *reinterpret_cast<uint32_t*>(dst + 16 * nb) = quad_byte_transpose(d, i);
           }
         }
@@ -1518,7 +1520,7 @@ __device__ inline void both_mma_body(const ProArgs& a) {
             const int i = 16 * q + 4 * j;
             xq[j] = quant4(static_cast<float>(u[i]), static_cast<float>(u[i + 1]),
                            static_cast<float>(u[i + 2]), static_cast<float>(u[i + 3]), r2, lo, hi,
-                           a.f8);
+                           (OP == OP_QUANT_F8));
           }
           *reinterpret_cast<uint4*>(dst + 16 * q) = make_uint4(xq[0], xq[1], xq[2], xq[3]);
         }
@@ -1564,7 +1566,7 @@ __global__ __launch_bounds__(BM_THREADS) void both_pipe_kernel(ProArgs a) {
 // One item of the single-pass kernel: compute() puts X B of the item in the LDS half tile (and
 // returns this thread's maxima) and B X B of this thread's column segment in v2; emit() writes
 // the item's codes from those with the given reciprocal scales.
-template <class In, int K>
+template <class In, int K, bool F8>
 struct BothItem {
   static constexpr int KM = K < 64 ? K : 64, NKS = K > 128 ? 8 : 4, NNB = K > 128 ? 16 : 8;
   const ProArgs& a;
@@ -1677,7 +1679,7 @@ struct BothItem {
         for (int nb = 0; nb < 8; ++nb) {
           const int c = 16 * nb + n0;
           const float4 y = *reinterpret_cast<const float4*>(&half[c * BT + 4 * bm_chunk(c, c4)]);
-          const uint32_t d = quant4(y.x, y.y, y.z, y.w, r1, lo, hi, a.f8);
+          const uint32_t d = quant4(y.x, y.y, y.z, y.w, r1, lo, hi, F8);
           rc[rb][nb] = quad_byte_transpose(d, i);
         }
       }
@@ -1685,7 +1687,7 @@ struct BothItem {
     uint32_t tc[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j)
-      tc[j] = quant4(v2[4 * j], v2[4 * j + 1], v2[4 * j + 2], v2[4 * j + 3], r2, lo, hi, a.f8);
+      tc[j] = quant4(v2[4 * j], v2[4 * j + 1], v2[4 * j + 2], v2[4 * j + 3], r2, lo, hi, F8);
     __syncthreads();   // every thread has read its values out of the half tile
     uint32_t* const rt = reinterpret_cast<uint32_t*>(half);   // [256 rows][32 dwords]
     uint32_t* const ct = rt + 256 * 32;                       // [128 columns][64 dwords]
@@ -1719,7 +1721,7 @@ struct BothItem {
   }
 };
 
-template <class In, int K>
+template <class In, int K, bool F8>
 __global__ __launch_bounds__(BM_THREADS) void both_single_kernel(ProArgs a) {
   if constexpr (In::bytes != 2 || K < 16) {
     return;
@@ -1729,7 +1731,7 @@ __global__ __launch_bounds__(BM_THREADS) void both_single_kernel(ProArgs a) {
     __shared__ int s_state;
     constexpr int OPEN = 0, RELEASED = 1, ABORTED = 2;
     const int t = threadIdx.x, wg = blockIdx.x, nwg = gridDim.x;   // nwg == items (host checks)
-    BothItem<In, K> b(a, half);
+    BothItem<In, K, F8> b(a, half);
     float amax1 = 0.0f, amax2 = 0.0f;
     b.compute(wg, amax1, amax2);
     // ---- partial maxima, grid barrier
@@ -1828,11 +1830,17 @@ struct Launch;
         case DT_F16: return NAME##_k<F16, OP_ABSMAX>(k, a, grid, st, tok);                          \
         case DT_BF16: return NAME##_k<BF16, OP_ABSMAX>(k, a, grid, st, tok);                        \
       }                                                                                        \
-    } else {                                                                                   \
+    } else if (op == OP_QUANT) {                                                               \
       switch (in_dt) {                                                                         \
         case DT_F32: return NAME##_k<F32, OP_QUANT>(k, a, grid, st, tok);                           \
         case DT_F16: return NAME##_k<F16, OP_QUANT>(k, a, grid, st, tok);                           \
         case DT_BF16: return NAME##_k<BF16, OP_QUANT>(k, a, grid, st, tok);                         \
+      }                                                                                        \
+    } else if (op == OP_QUANT_F8) {                                                            \
+      switch (in_dt) {                                                                         \
+        case DT_F32: return NAME##_k<F32, OP_QUANT_F8>(k, a, grid, st, tok);                        \
+        case DT_F16: return NAME##_k<F16, OP_QUANT_F8>(k, a, grid, st, tok);                        \
+        case DT_BF16: return NAME##_k<BF16, OP_QUANT_F8>(k, a, grid, st, tok);                      \
       }                                                                                        \
     }                                                                                          \
     return hipErrorInvalidValue;                                                               \
@@ -1849,11 +1857,11 @@ HQ_PRO_DISPATCH(both_mma_kernel, BM_THREADS)
 HQ_PRO_DISPATCH(both_pipe_kernel, BM_THREADS)
 #undef HQ_PRO_DISPATCH
 
-template <class In>
+template <class In, bool F8>
 static hipError_t both_single_k(int k, const ProArgs& a, int grid, hipStream_t st, int tok) {
   switch (k) {
 #define HQ_BS(KK) \
-  case KK: return launch_k(both_single_kernel<In, KK>, dim3(grid), dim3(BM_THREADS), st, tok, a);
+  case KK: return launch_k(both_single_kernel<In, KK, F8>, dim3(grid), dim3(BM_THREADS), st, tok, a);
     HQ_BS(16) HQ_BS(32) HQ_BS(64) HQ_BS(128) HQ_BS(256)
 #undef HQ_BS
   }
@@ -1875,7 +1883,6 @@ static ProArgs pro_args(const ProPass& p) {
   a.step = p.step;
   a.step2 = p.step2;
   a.qp = p.qp;
-  a.f8 = p.f8;
   a.scale_out = p.scale_out;
   a.scale_out2 = p.scale_out2;
   a.codes = p.codes;
@@ -1910,12 +1917,13 @@ int pro_grid(const ProPass& p) {
 }
 
 hipError_t pro_pass(const ProPass& p, int op, hipStream_t st) {
+  if (op == OP_QUANT && p.f8) op = OP_QUANT_F8;   // the quantize pass writing E4M3 codes
   ProArgs a = pro_args(p);
   const int grid = pro_grid(p);
   const double elems = static_cast<double>(p.rows) * p.cols;
   const double inb = elems * dtb(p.in_dt);
   double outb = 0.0;
-  if (op == OP_QUANT) outb = elems * ((p.codes ? 1 : 0) + (p.codes_t ? 1 : 0));
+  if (quant_op(op)) outb = elems * ((p.codes ? 1 : 0) + (p.codes_t ? 1 : 0));
   const int tok = prof_open(op == OP_ABSMAX ? K_ROT_ABSMAX : K_ROT_QUANT, inb + outb);
   hipError_t e = hipErrorInvalidValue;
   if (p.kind == PRO_RIGHT && right_mma_ok(p.rows, p.cols, a.vec, dtb(p.in_dt), p.k))
@@ -1997,8 +2005,11 @@ hipError_t pro_single_pass(const ProPass& p, int32_t* bar, hipStream_t st) {
   const int grid = static_cast<int>(both_items(p.rows, p.cols));
   const double elems = static_cast<double>(p.rows) * p.cols;
   const int tok = prof_open(K_ROT_ABSMAX, elems * (2.0 + (p.codes ? 1 : 0) + (p.codes_t ? 1 : 0)));
-  return p.in_dt == DT_F16 ? both_single_k<F16>(p.k, a, grid, st, tok)
-                           : both_single_k<BF16>(p.k, a, grid, st, tok);
+  if (p.f8)
+    return p.in_dt == DT_F16 ? both_single_k<F16, true>(p.k, a, grid, st, tok)
+                             : both_single_k<BF16, true>(p.k, a, grid, st, tok);
+  return p.in_dt == DT_F16 ? both_single_k<F16, false>(p.k, a, grid, st, tok)
+                           : both_single_k<BF16, false>(p.k, a, grid, st, tok);
 }
 
 hipError_t pro_fixup_pass(const ProPass& p, int32_t* bar, hipStream_t st) {
@@ -2007,7 +2018,7 @@ hipError_t pro_fixup_pass(const ProPass& p, int32_t* bar, hipStream_t st) {
   const int grid = pro_grid(p);
   const double elems = static_cast<double>(p.rows) * p.cols;
   const int tok = prof_open(K_ROT_QUANT, elems * ((p.codes ? 1 : 0) + (p.codes_t ? 1 : 0)));
-  return both_mma_kernel_launch(p.in_dt, OP_QUANT, p.k, a, grid, st, tok);
+  return both_mma_kernel_launch(p.in_dt, p.f8 ? OP_QUANT_F8 : OP_QUANT, p.k, a, grid, st, tok);
 }
 
 }  // namespace hq

@@ -50,7 +50,7 @@ extern "C" hq_status hq_linear_fwd_noalloc(const void* x, const void* w, int32_t
                                            int32_t y_dtype, hq_qtensor* save_x,
                                            hq_qtensor* save_xt, hq_qtensor* save_w,
                                            void* stream) {
-  hq_status s = hq::fwd_validate(x, w, in_dtype, N, C, D, cfg, step_x, step_w, step_xt, y,
+  hq_status s = hq::fwd_validate(x, w, in_dtype, 1, N, C, D, cfg, step_x, step_w, step_xt, y,
                                  y_dtype, save_x, save_xt, save_w);
   if (s != HQ_OK) return s;
   if (hq::fwd_workspace_bytes() > kScratchBytes) return HQ_ERR_WORKSPACE;
@@ -59,6 +59,6 @@ extern "C" hq_status hq_linear_fwd_noalloc(const void* x, const void* w, int32_t
   void* ws = nullptr;
   s = scratch_on_current_device(&ws);
   if (s != HQ_OK) return s;
-  return hq::fwd_run(x, w, in_dtype, N, C, D, cfg, step_x, step_w, step_xt, y, y_dtype, save_x,
-                     save_xt, save_w, ws, stream);
+  return hq::fwd_run(x, w, in_dtype, 1, N, C, D, cfg, step_x, step_w, step_xt, y, y_dtype,
+                     save_x, save_xt, save_w, ws, stream);
 }

@@ -105,3 +105,43 @@ class Layer:
         B.check(B.hq_linear_bwd_weight(
             self.qg.st, qx.st, self.N, self.C, self.D, self.cfg, ptr(dw), HQ_DT[dw.dtype],
             ptr(self.ws), self.ws_bytes, stream_ptr(stream)), "hq_linear_bwd_weight")
+
+
+class BatchedLayer:
+    """Buffers for a batched product (batch x (N x C) by batch x (D x C), e.g. attention
+    heads) and the three batched calls; codes describe the stacked matrices."""
+
+    def __init__(self, batch, N, C, D, k, bits, scale_mode, variant, device="cuda",
+                 fmt=B.HQ_FMT_INT):
+        self.batch, self.N, self.C, self.D = batch, N, C, D
+        self.cfg = config(k, bits, scale_mode, variant, fmt)
+        self.variant = variant
+        self.ws_bytes = B.hq_bmm_workspace_bytes(self.cfg)
+        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=device)
+        halo2 = variant == B.HQ_VARIANT_HALO2
+        NB, DB = batch * N, batch * D
+        self.qx = QTensor(NB, C, codes=True, codes_t=not halo2, device=device)
+        self.qxt = QTensor(NB, C, codes=False, codes_t=True, device=device) if halo2 else None
+        self.qw = QTensor(DB, C, codes=True, codes_t=True, device=device)
+        self.qg = QTensor(NB, D, codes=True, codes_t=True, device=device)
+
+    def fwd(self, x, w, y, steps=None, stream=None):
+        steps = steps or {}
+        B.check(B.hq_bmm_fwd(
+            ptr(x), ptr(w), HQ_DT[x.dtype], self.batch, self.N, self.C, self.D, self.cfg,
+            ptr(steps.get("x")), ptr(steps.get("w")), ptr(steps.get("xt", steps.get("x"))),
+            ptr(y), HQ_DT[y.dtype], self.qx.st, None if self.qxt is None else self.qxt.st,
+            self.qw.st, ptr(self.ws), self.ws_bytes, stream_ptr(stream)), "hq_bmm_fwd")
+
+    def bwd_input(self, dy, dx, steps=None, stream=None):
+        steps = steps or {}
+        B.check(B.hq_bmm_bwd_input(
+            ptr(dy), HQ_DT[dy.dtype], self.batch, self.N, self.C, self.D, self.cfg,
+            ptr(steps.get("g")), self.qw.st, ptr(dx), HQ_DT[dx.dtype], self.qg.st, ptr(self.ws),
+            self.ws_bytes, stream_ptr(stream)), "hq_bmm_bwd_input")
+
+    def bwd_weight(self, dw, stream=None):
+        qx = self.qxt if self.qxt is not None else self.qx
+        B.check(B.hq_bmm_bwd_weight(
+            self.qg.st, qx.st, self.batch, self.N, self.C, self.D, self.cfg, ptr(dw),
+            HQ_DT[dw.dtype], ptr(self.ws), self.ws_bytes, stream_ptr(stream)), "hq_bmm_bwd_weight")

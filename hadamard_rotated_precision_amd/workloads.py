@@ -62,6 +62,46 @@ CONFIGS = {
 }
 
 
+# Batched products of attention (INT4 page §A.1): the scores S = Q K^T of a Llama-7B-shaped
+# attention layer, batch = 4 sequences x 32 heads, 1024 tokens, head_dim 128 (rotated, k = 128),
+# HALO-2 (dQ = dS K, dK = dS^T Q). Q and K ~ N(0,1) with 2 head-dim channels x 20 (the outlier
+# channels seen in query / key projections); dS = 1e-3 t3.
+ATTENTION = {
+    "qk": dict(name="halo2_attn_scores_llama7b_128x1024x128x1024_k128", batch=128, N=1024,
+               C=128, D=1024, k=128, bits=8, mode=ABSMAX, variant=HALO2, in_dtype=BF16,
+               out_dtype=BF16, passes=("fwd", "dx", "dw"), seed=201,
+               x=("normal", 1.0), x_outliers=(2, 20.0), w=("normal", 1.0), dy=("t3", 1e-3)),
+}
+
+
+def attention_config(name="qk", **overrides):
+    """A copy of a batched (attention) workload; shapes may be overridden."""
+    cfg = dict(ATTENTION[name])
+    cfg["fmt"] = INT
+    cfg.update(overrides)
+    return cfg
+
+
+def make_batched_inputs(cfg):
+    """Draw X (batch x N x C), W (batch x D x C) and dY (batch x N x D) for a batched workload,
+    as bit arrays of the input dtype; the outlier channels (of C) are shared by all batches
+    and by W, as the channels of a head are."""
+    rng = np.random.Generator(np.random.PCG64(cfg["seed"]))
+    nb, N, C, D = cfg["batch"], cfg["N"], cfg["C"], cfg["D"]
+    X = _draw(rng, cfg["x"], (nb, N, C))
+    W = _draw(rng, cfg["w"], (nb, D, C))
+    outliers = np.zeros(0, dtype=np.int64)
+    if cfg.get("x_outliers"):
+        n_out, mult = _outlier_count(cfg["x_outliers"], C)
+        outliers = rng.choice(C, n_out, replace=False)
+        X[:, :, outliers] *= mult
+        W[:, :, outliers] *= mult
+    dY = _draw(rng, cfg["dy"], (nb, N, D))
+    dt = cfg["in_dtype"]
+    return dict(x=to_dtype_bits(X, dt), w=to_dtype_bits(W, dt), dy=to_dtype_bits(dY, dt),
+                outliers=outliers)
+
+
 def config(cfg_id, **overrides):
     """A copy of a workload definition; shape keys (N, C, D) may be overridden to draw a
     smaller tensor with the same distributions, and fmt=E4M3 gives the same layer with FP8

@@ -215,21 +215,53 @@ hq_status hq_linear_bwd_weight(const hq_qtensor *saved_g, const hq_qtensor *save
                                void *dw, int32_t dw_dtype, void *ws, size_t ws_bytes,
                                void *stream);
 
+/* ---------------------------------------------------------------- batched products
+ * Batched HQ-MM for the batched matmuls of attention (INT4 page §A.1: the same quantizers
+ * apply to BMMs as to ordinary matrix multiplications). A batched operand is `batch` row-major
+ * matrices stored one after another (e.g. heads x tokens x head_dim); batch b computes
+ *   Y_b = X_b W_b^T (N x D),  dX_b = dY_b W_b (N x C),  dW_b = dY_b^T X_b (D x C)
+ * with the rotations, variants and formats of the layer calls (e.g. scores S = Q K^T: X = Q,
+ * W = K, C = head_dim; P V: X = P, W = V^T, C = key tokens). Each batched tensor is quantized
+ * as one tensor: one scale for all batches, codes of the stacked (batch N) x C, (batch D) x C
+ * and (batch N) x D matrices in the quantized-tensor structs, whose rows count every batch.
+ * Right rotations act within rows and the token-axis blocks (N % k == 0 under HALO2) never
+ * cross a batch, so the stacked codes are those of every batch. N and D must be multiples of
+ * 16 when batch > 1 (HQ_ERR_SHAPE), batch at most 65535. Workspace: hq_bmm_workspace_bytes(cfg) bytes, for any
+ * shape. Otherwise as hq_linear_fwd / hq_linear_bwd_input / hq_linear_bwd_weight. */
+size_t hq_bmm_workspace_bytes(const hq_config *cfg);
+
+hq_status hq_bmm_fwd(const void *x, const void *w, int32_t in_dtype, int64_t batch, int64_t N,
+                     int64_t C, int64_t D, const hq_config *cfg, const float *step_x,
+                     const float *step_w, const float *step_xt, void *y, int32_t y_dtype,
+                     hq_qtensor *save_x, hq_qtensor *save_xt, hq_qtensor *save_w, void *ws,
+                     size_t ws_bytes, void *stream);
+
+hq_status hq_bmm_bwd_input(const void *dy, int32_t dy_dtype, int64_t batch, int64_t N,
+                           int64_t C, int64_t D, const hq_config *cfg, const float *step_g,
+                           const hq_qtensor *saved_w, void *dx, int32_t dx_dtype,
+                           hq_qtensor *save_g, void *ws, size_t ws_bytes, void *stream);
+
+hq_status hq_bmm_bwd_weight(const hq_qtensor *saved_g, const hq_qtensor *saved_x, int64_t batch,
+                            int64_t N, int64_t C, int64_t D, const hq_config *cfg, void *dw,
+                            int32_t dw_dtype, void *ws, size_t ws_bytes, void *stream);
+
 /* Standalone block-diagonal Walsh-Hadamard transform (unnormalized): dst = rotation of src
  * (INT4 page §3.3). rows x cols row-major; rotated dims divisible by k; rot != BOTH
  * for this entry point; src and dst must not overlap. Sums are formed in fp32 and rounded once
  * to dst_dtype (nearest even): exact whenever the fp32 sums are, else within the fp32
- * summation error of that. With 16-bit src_dtype == dst_dtype, 16-byte aligned pointers and
- * whole tiles (RIGHT: rows % 64 == 0, cols % 256 == 0, k >= 128; LEFT: rows % 256 == 0,
- * cols % 64 == 0, k >= 16) the sums run on the matrix cores, in another order than the VALU
+ * summation error of that. The implementation is hq_fwht_path's HQ_FWHT_AUTO choice: with
+ * 16-bit src_dtype == dst_dtype, 16-byte aligned pointers and whole tiles (RIGHT: rows % 64
+ * == 0, cols % 256 == 0; LEFT: rows % 256 == 0, cols % 64 == 0) the sums run on the matrix
+ * cores for RIGHT at k = 256 and LEFT at k = 16, 128, 256, in another order than the VALU
  * butterflies of the other cases. */
 hq_status hq_fwht(const void *src, int32_t src_dtype, void *dst, int32_t dst_dtype,
                   int64_t rows, int64_t cols, int32_t rot, int32_t k, void *stream);
 
 /* hq_fwht with the implementation named (for measuring one against the other; the results
  * agree to the fp32 summation order). path:
- *   HQ_FWHT_AUTO       what hq_fwht picks: the matrix cores for LEFT whenever they cover the
- *                      call, and for RIGHT at k >= 128; the VALU butterflies otherwise;
+ *   HQ_FWHT_AUTO       what hq_fwht picks: the matrix cores where they cover the call and
+ *                      were measured more than 5 % faster (RIGHT at k = 256; LEFT at
+ *                      k = 16, 128, 256), the VALU butterflies otherwise;
  *   HQ_FWHT_BUTTERFLY  the VALU butterflies (log2 k add/sub stages per element), any shape;
  *   HQ_FWHT_MATRIX     the matrix cores (a dense +-1 contraction in 16-bit MFMA, exact
  *                      products, fp32 sums); HQ_ERR_MODE unless the call has 16-bit
