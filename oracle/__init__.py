@@ -375,3 +375,69 @@ def linear_batched(X, W, dY, k, bits, variant, mode=ABSMAX, steps=None,
             out["dw"] = np.stack([bwd_weight_from_codes(qg[xs[b]], sg, qxt[xs[b]], sxt, k,
                                                         variant, fmt=fmt) for b in range(nb)])
     return out
+
+
+# ------------------------------------------------ quantizer parameters (LSQ step machinery)
+def lsq_step_derivative(R, scale, qp):
+    """d v_hat / d s for v_hat = s * clamp(RNE(v / s), -Qp, Qp) with the straight-through
+    rounding of learned step size quantization ("Training Transformers with 4-bit Integers",
+    §3.1 learned step, §A.3 step gradients by the chain rule): q - v/s inside the grid, and
+    the clipped level (+-Qp) outside it. The quotient is exact (double of an exact R over an
+    fp32 s); the codes are the oracle's quantizer."""
+    R = np.ascontiguousarray(R, dtype=np.float64)
+    q = quantize(R, scale, qp).astype(np.float64)
+    x = R / float(np.float32(scale))
+    return np.where(np.abs(x) >= qp, np.sign(x) * qp, q - x)
+
+
+def rotated_stats(V, G, rot, k, bits, scale, fmt=INT):
+    """The three statistics of a rotated tensor R = rotation(V) that set quantizer parameters
+    (INT4 page §A.3-§A.5), each the plain sum over all entries, in double:
+      abs_sum  = sum |R|                                   (cold-start step)
+      qerr     = sum (R - s * value(code(R)))^2              (Hadamard-size selection)
+      lsq      = sum (rotation(G) / k)_i * d v_hat_i / d s   (LSQ step gradient; G the gradient
+                 of the loss with respect to the unrotated tensor, so rotation(G) / k is the
+                 gradient with respect to R since V = R B / k)
+    lsq is None when G is None; INT codes only for lsq."""
+    R = rotate(V, rot, k)
+    out = {"abs_sum": float(np.sum(np.abs(R)))}
+    qp = qmax(bits, fmt)
+    if fmt == E4M3:
+        rec = decode_e4m3(quantize_e4m3(R, scale)) * float(np.float32(scale))
+    else:
+        rec = quantize(R, scale, qp).astype(np.float64) * float(np.float32(scale))
+    out["qerr"] = float(np.sum((R - rec) ** 2))
+    if G is not None:
+        kk = k if rot != ROT_NONE else 1
+        Gr = rotate(G, rot, k) / kk
+        out["lsq"] = float(np.sum(Gr * lsq_step_derivative(R, scale, qp)))
+    return out
+
+
+def cold_start_step(V, rot, k, bits):
+    """Cold-start step of a tensor (INT4 page §A.4: while steps are not yet learned, a
+    heuristic sets them from the tensor; the page does not give it). Reading taken: the
+    learned-step initialisation 2 * mean|R| / sqrt(Qp) of the rotated tensor, rounded once to
+    fp32."""
+    R = rotate(V, rot, k)
+    return np.float32(2.0 * float(np.mean(np.abs(R))) / np.sqrt(qmax(bits)))
+
+
+def choose_hadamard_k(X, W, candidates, bits, fmt=INT):
+    """Hadamard size selection (INT4 page §A.5): the candidate k minimising the product of the
+    activation and weight quantization errors, the rotated tensors standing for X and W:
+    err(V, k) = ||V - s Q(V B) B / k||_F^2 = sum (R - s q)^2 / k (B B = k I), with the tensor-
+    wise absmax scale of R = V B. Returns (best k, {k: (err_x, err_w)}); ties go to the smaller
+    k."""
+    errs = {}
+    best = None
+    for k in candidates:
+        e = []
+        for V in (X, W):
+            R = rotate(V, ROT_RIGHT, k)
+            s = absmax_scale(R, qmax(bits, fmt))
+            e.append(rotated_stats(V, None, ROT_RIGHT, k, bits, s, fmt)["qerr"] / k)
+        errs[k] = tuple(e)
+        if best is None or e[0] * e[1] < errs[best][0] * errs[best][1]:
+            best = k
+    return best, errs
