@@ -303,6 +303,66 @@ def bmm_step(steps=20):
                               "unit": "TOP/s", "frac": round(tops / PEAK_INT8_TOPS, 4)}}
 
 
+def qparam_stats(reps=10):
+    """Quantizer-parameter statistics (INT4 page §A.3-§A.5) on X of the 8192 x 13824 x 5120
+    layer (bf16, k = 128): the LSQ step gradient (reads X and a gradient of the same shape,
+    2 x 226 MB), the cold-start step and the quantization error (X only), each one streaming
+    pass: GB/s over the mean event time; and hq_select_hadamard_k over k = 16..256 for that
+    layer's X and W (a synchronous setup call: wall time)."""
+    import ctypes
+    import torch
+    from hadamard_rotated_precision_amd import binding as B
+    from hadamard_rotated_precision_amd import tensors as T
+    rows, cols, k, D = 8192, 13824, 128, 5120
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(107)
+    x = torch.randn((rows, cols), dtype=torch.float32, device="cuda", generator=gen).to(torch.bfloat16)
+    g = (torch.randn((rows, cols), dtype=torch.float32, device="cuda", generator=gen) * 1e-3).to(torch.bfloat16)
+    w = (torch.randn((D, cols), dtype=torch.float32, device="cuda", generator=gen) * 0.015).to(torch.bfloat16)
+    cfg = T.config(k, 8, B.HQ_SCALE_ABSMAX, B.HQ_VARIANT_HQ)
+    nws = B.hq_workspace_bytes(cfg, 1, 16, 1)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    sc = torch.tensor([0.05], dtype=torch.float32, device="cuda")
+    out = torch.zeros(1, dtype=torch.float64, device="cuda")
+    step = torch.zeros(1, dtype=torch.float32, device="cuda")
+    res = {"shape": "%dx%d bf16, k=%d" % (rows, cols, k)}
+
+    def timed(fn, nbytes):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        gbs = nbytes / (us * 1e-6) / 1e9
+        return {"us": round(us, 2), "gbps": round(gbs, 1), "pct_hbm": round(100 * gbs / PEAK_HBM_GBS, 1)}
+    n2 = 2 * rows * cols
+    res["lsq_grad"] = timed(lambda: B.check(B.hq_rotated_stat(
+        x.data_ptr(), g.data_ptr(), B.HQ_BF16, rows, cols, B.HQ_ROT_RIGHT, cfg, B.HQ_STAT_LSQ_GRAD,
+        sc.data_ptr(), out.data_ptr(), ws.data_ptr(), nws, T.stream_ptr()), "lsq"), 2 * n2)
+    res["qerr"] = timed(lambda: B.check(B.hq_rotated_stat(
+        x.data_ptr(), None, B.HQ_BF16, rows, cols, B.HQ_ROT_RIGHT, cfg, B.HQ_STAT_QERR,
+        sc.data_ptr(), out.data_ptr(), ws.data_ptr(), nws, T.stream_ptr()), "qerr"), n2)
+    res["cold_start_step"] = timed(lambda: B.check(B.hq_cold_start_step(
+        x.data_ptr(), B.HQ_BF16, rows, cols, B.HQ_ROT_RIGHT, cfg, step.data_ptr(), ws.data_ptr(),
+        nws, T.stream_ptr()), "cold"), n2)
+    cands = [16, 32, 64, 128, 256]
+    carr = (ctypes.c_int32 * len(cands))(*cands)
+    kb = ctypes.c_int32(0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    B.check(B.hq_select_hadamard_k(x.data_ptr(), w.data_ptr(), B.HQ_BF16, rows, cols, D, cfg, carr,
+                                   len(cands), kb, None, ws.data_ptr(), nws, T.stream_ptr()), "sel")
+    res["select_k"] = {"candidates": cands, "chosen": kb.value,
+                       "ms": round((time.perf_counter() - t0) * 1e3, 2),
+                       "what": "absmax and error passes over X and W per candidate, synchronous"}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -318,6 +378,8 @@ def main():
                     help="also time these workloads' steps against three bf16 GEMMs (default "
                          "4,2: the Llama-7B-shaped MLP layer and the 2048 x 4096 x 4096 layer); "
                          "empty to skip")
+    ap.add_argument("--no-qparams", action="store_true",
+                    help="skip the quantizer-parameter statistics")
     ap.add_argument("--no-bmm", action="store_true",
                     help="skip the batched (attention) product")
     ap.add_argument("--no-fp8", action="store_true",
@@ -575,6 +637,12 @@ def main():
             result["fp8_step"] = fp8_step(args.config)
         except Exception as exc:  # report, do not fail the benchmark line
             result["fp8_step"] = {"error": str(exc)}
+    if not args.no_qparams:
+        print("[bench] quantizer-parameter statistics", file=sys.stderr, flush=True)
+        try:
+            result["qparams"] = qparam_stats()
+        except Exception as exc:  # report, do not fail the benchmark line
+            result["qparams"] = {"error": str(exc)}
     if not args.no_bmm:
         print("[bench] batched attention product", file=sys.stderr, flush=True)
         try:

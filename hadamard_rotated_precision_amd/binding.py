@@ -26,7 +26,10 @@ EXPORTS = ["hq_abi_version", "hq_status_string", "hq_code_pitch", "hq_workspace_
            "hq_rotate_quantize", "hq_linear_fwd", "hq_linear_fwd_noalloc", "hq_linear_bwd_input",
            "hq_linear_bwd_weight", "hq_fwht", "hq_fwht_path", "hq_gemm_i8_i32", "hq_gemm_f8_f32",
            "hq_profile_start", "hq_profile_stop", "hq_profile_records",
-           "hq_bmm_workspace_bytes", "hq_bmm_fwd", "hq_bmm_bwd_input", "hq_bmm_bwd_weight"]
+           "hq_bmm_workspace_bytes", "hq_bmm_fwd", "hq_bmm_bwd_input", "hq_bmm_bwd_weight",
+           "hq_rotated_stat", "hq_cold_start_step", "hq_select_hadamard_k"]
+HQ_STAT_ABS_SUM, HQ_STAT_QERR, HQ_STAT_LSQ_GRAD = 0, 1, 2
+HQ_MAX_K_CANDIDATES = 16
 HQ_KIND_GEMM, HQ_KIND_ROT_ABSMAX, HQ_KIND_ROT_QUANT, HQ_KIND_ROT_STORE = 0, 1, 2, 3
 HQ_KIND_TRANSPOSE, HQ_KIND_MISC, HQ_KIND_COUNT = 4, 5, 6
 KIND_NAMES = ["gemm", "rot_absmax", "rot_quant", "rot_store", "transpose", "misc"]
@@ -119,6 +122,14 @@ def load(build_if_missing=True):
     lib.hq_bmm_bwd_weight.restype = i32
     lib.hq_bmm_bwd_weight.argtypes = [P(hq_qtensor), P(hq_qtensor), i64, i64, i64, i64,
                                       P(hq_config), vp, i32, vp, sz, vp]
+    lib.hq_rotated_stat.restype = i32
+    lib.hq_rotated_stat.argtypes = [vp, vp, i32, i64, i64, i32, P(hq_config), i32, vp, vp, vp,
+                                    sz, vp]
+    lib.hq_cold_start_step.restype = i32
+    lib.hq_cold_start_step.argtypes = [vp, i32, i64, i64, i32, P(hq_config), vp, vp, sz, vp]
+    lib.hq_select_hadamard_k.restype = i32
+    lib.hq_select_hadamard_k.argtypes = [vp, vp, i32, i64, i64, i64, P(hq_config), vp, i32, vp,
+                                         vp, vp, sz, vp]
     lib.hq_gemm_f8_f32.restype = i32
     lib.hq_gemm_f8_f32.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, vp]
     lib.hq_fwht_path.restype = i32
@@ -218,6 +229,26 @@ def hq_bmm_bwd_input(dy, dy_dtype, batch, N, C, D, cfg, step_g, saved_w, dx, dx_
 def hq_bmm_bwd_weight(saved_g, saved_x, batch, N, C, D, cfg, dw, dw_dtype, ws, ws_bytes, stream):
     return load().hq_bmm_bwd_weight(_ref(saved_g), _ref(saved_x), batch, N, C, D, _ref(cfg), dw,
                                     dw_dtype, ws, ws_bytes, stream)
+
+
+def hq_rotated_stat(src, grad, dtype, rows, cols, rot, cfg, stat, scale, out, ws, ws_bytes,
+                    stream):
+    return load().hq_rotated_stat(src, grad, dtype, rows, cols, rot, _ref(cfg), stat, scale, out,
+                                  ws, ws_bytes, stream)
+
+
+def hq_cold_start_step(src, dtype, rows, cols, rot, cfg, step, ws, ws_bytes, stream):
+    return load().hq_cold_start_step(src, dtype, rows, cols, rot, _ref(cfg), step, ws, ws_bytes,
+                                     stream)
+
+
+def hq_select_hadamard_k(x, w, dtype, N, C, D, cfg, candidates, n_candidates, k_best, errors, ws,
+                         ws_bytes, stream):
+    """candidates: a ctypes int32 array; k_best: a ctypes int32; errors: a ctypes double array
+    of 2 * n_candidates, or None (host memory)."""
+    return load().hq_select_hadamard_k(x, w, dtype, N, C, D, _ref(cfg), candidates, n_candidates,
+                                       ctypes.byref(k_best),
+                                       None if errors is None else errors, ws, ws_bytes, stream)
 
 
 def hq_gemm_f8_f32(a, lda, b_t, ldb, c, M, N, K, stream):

@@ -638,6 +638,136 @@ hq_status hq_bmm_bwd_weight(const hq_qtensor* saved_g, const hq_qtensor* saved_x
                          ws_need(), stream);
 }
 
+}  // extern "C"
+
+namespace {
+hq_status check_stat_args(const void* src, const void* grad, int32_t dtype, int64_t rows,
+                          int64_t cols, int32_t rot, const hq_config* cfg) {
+  HQ_CHECK(check_cfg(cfg));
+  if (!valid_dt(dtype)) return HQ_ERR_DTYPE;
+  if (rot != HQ_ROT_NONE && rot != HQ_ROT_RIGHT) return HQ_ERR_MODE;
+  if (rows < 0 || cols < 0) return HQ_ERR_SHAPE;
+  if (rot == HQ_ROT_RIGHT && cols % cfg->k) return HQ_ERR_SHAPE;
+  if (rows * cols > 0 && !src) return HQ_ERR_NULL;
+  (void)grad;
+  return HQ_OK;
+}
+
+hq::StatPass stat_pass_for(const void* src, const void* grad, int32_t dtype, int64_t rows,
+                           int64_t cols, int32_t rot, const hq_config* cfg, int mode,
+                           const Ws& w) {
+  hq::StatPass p;
+  p.src = src;
+  p.grad = grad;
+  p.dt = dtype;
+  p.rows = rows;
+  p.cols = cols;
+  p.k = rot == HQ_ROT_RIGHT ? cfg->k : 1;
+  p.mode = mode;
+  p.f8 = is_f8(cfg);
+  p.qp = qmax(cfg);
+  p.partials = reinterpret_cast<double*>(w.part[0]);   // part[0..1]: kStatMaxParts doubles
+  return p;
+}
+}  // namespace
+
+extern "C" {
+
+hq_status hq_rotated_stat(const void* src, const void* grad, int32_t dtype, int64_t rows,
+                          int64_t cols, int32_t rot, const hq_config* cfg, int32_t stat,
+                          const float* scale, double* out, void* ws, size_t ws_bytes,
+                          void* stream) {
+  HQ_CHECK(check_stat_args(src, grad, dtype, rows, cols, rot, cfg));
+  if (stat != HQ_STAT_ABS_SUM && stat != HQ_STAT_QERR && stat != HQ_STAT_LSQ_GRAD)
+    return HQ_ERR_MODE;
+  if (stat == HQ_STAT_LSQ_GRAD && is_f8(cfg)) return HQ_ERR_MODE;
+  if (stat == HQ_STAT_LSQ_GRAD && rows * cols > 0 && !grad) return HQ_ERR_NULL;
+  if (stat != HQ_STAT_ABS_SUM && !scale) return HQ_ERR_NULL;
+  if (!out) return HQ_ERR_NULL;
+  HQ_CHECK(check_ws(ws, ws_bytes, ws_need()));
+  HQ_CHECK(device_ok());
+  Ws w(ws);
+  hq::StatPass p = stat_pass_for(src, grad, dtype, rows, cols, rot, cfg, stat, w);
+  p.scale = scale;
+  p.out = out;
+  HQ_TRY(hq::stat_pass(p, static_cast<hipStream_t>(stream)));
+  return HQ_OK;
+}
+
+hq_status hq_cold_start_step(const void* src, int32_t dtype, int64_t rows, int64_t cols,
+                             int32_t rot, const hq_config* cfg, float* step, void* ws,
+                             size_t ws_bytes, void* stream) {
+  HQ_CHECK(check_stat_args(src, nullptr, dtype, rows, cols, rot, cfg));
+  if (is_f8(cfg)) return HQ_ERR_MODE;
+  if (!step) return HQ_ERR_NULL;
+  if (rows * cols == 0) return HQ_ERR_SHAPE;   // no entries: no mean to set a step from
+  HQ_CHECK(check_ws(ws, ws_bytes, ws_need()));
+  HQ_CHECK(device_ok());
+  Ws w(ws);
+  hq::StatPass p = stat_pass_for(src, nullptr, dtype, rows, cols, rot, cfg, HQ_STAT_ABS_SUM, w);
+  p.finish = 2;
+  p.fout = step;
+  HQ_TRY(hq::stat_pass(p, static_cast<hipStream_t>(stream)));
+  return HQ_OK;
+}
+
+hq_status hq_select_hadamard_k(const void* x, const void* w, int32_t dtype, int64_t N, int64_t C,
+                               int64_t D, const hq_config* cfg, const int32_t* candidates,
+                               int32_t n_candidates, int32_t* k_best, double* errors, void* ws,
+                               size_t ws_bytes, void* stream) {
+  HQ_CHECK(check_cfg(cfg));
+  if (!valid_dt(dtype)) return HQ_ERR_DTYPE;
+  if (N <= 0 || C <= 0 || D <= 0) return HQ_ERR_SHAPE;
+  if (!x || !w || !candidates || !k_best) return HQ_ERR_NULL;
+  if (n_candidates < 1 || n_candidates > HQ_MAX_K_CANDIDATES) return HQ_ERR_SHAPE;
+  for (int32_t i = 0; i < n_candidates; ++i) {
+    if (!is_pow2_k(candidates[i])) return HQ_ERR_K;
+    if (C % candidates[i]) return HQ_ERR_SHAPE;
+  }
+  HQ_CHECK(check_ws(ws, ws_bytes, ws_need()));
+  HQ_CHECK(device_ok());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Ws wsp(ws);
+  double* res = reinterpret_cast<double*>(wsp.part[2]);   // 2 doubles per candidate
+  float* sc = wsp.part[3];                                // the two absmax scales
+  hq_config c = *cfg;
+  for (int32_t i = 0; i < n_candidates; ++i) {
+    c.k = candidates[i];
+    for (int t = 0; t < 2; ++t) {
+      const void* src = t == 0 ? x : w;
+      const int64_t rows = t == 0 ? N : D;
+      hq::StatPass p = stat_pass_for(src, nullptr, dtype, rows, C, HQ_ROT_RIGHT, &c,
+                                     hq::STAT_MODE_ABS_MAX, wsp);
+      p.finish = 1;
+      p.fout = sc + t;
+      HQ_TRY(hq::stat_pass(p, st));
+      p = stat_pass_for(src, nullptr, dtype, rows, C, HQ_ROT_RIGHT, &c, HQ_STAT_QERR, wsp);
+      p.scale = sc + t;
+      p.out = res + 2 * i + t;
+      HQ_TRY(hq::stat_pass(p, st));
+    }
+  }
+  double host[2 * HQ_MAX_K_CANDIDATES];
+  HQ_TRY(hipMemcpyAsync(host, res, sizeof(double) * 2 * n_candidates, hipMemcpyDeviceToHost, st));
+  HQ_TRY(hipStreamSynchronize(st));
+  int32_t best = -1;
+  double best_prod = 0.0;
+  for (int32_t i = 0; i < n_candidates; ++i) {
+    // errors in the space of X and W: ||V - s Q(V B) B / k||^2 = sum (v - s q)^2 / k
+    const double ex = host[2 * i] / candidates[i], ew = host[2 * i + 1] / candidates[i];
+    if (errors) {
+      errors[2 * i] = ex;
+      errors[2 * i + 1] = ew;
+    }
+    if (best < 0 || ex * ew < best_prod) {
+      best = i;
+      best_prod = ex * ew;
+    }
+  }
+  *k_best = candidates[best];
+  return HQ_OK;
+}
+
 hq_status hq_fwht_path(const void* src, int32_t src_dtype, void* dst, int32_t dst_dtype,
                        int64_t rows, int64_t cols, int32_t rot, int32_t k, int32_t path,
                        void* stream) {
@@ -705,6 +835,8 @@ hq_status hq_fwht(const void* src, int32_t src_dtype, void* dst, int32_t dst_dty
   return hq_fwht_path(src, src_dtype, dst, dst_dtype, rows, cols, rot, k, HQ_FWHT_AUTO, stream);
 }
 
+}  // extern "C"
+
 namespace {
 hq_status gemm_plain(const void* a, int64_t lda, const void* b_t, int64_t ldb, void* c,
                      int64_t M, int64_t N, int64_t K, bool f8, void* stream) {
@@ -731,6 +863,8 @@ hq_status gemm_plain(const void* a, int64_t lda, const void* b_t, int64_t ldb, v
   return HQ_OK;
 }
 }  // namespace
+
+extern "C" {
 
 hq_status hq_gemm_f8_f32(const uint8_t* a, int64_t lda, const uint8_t* b_t, int64_t ldb, float* c,
                          int64_t M, int64_t N, int64_t K, void* stream) {

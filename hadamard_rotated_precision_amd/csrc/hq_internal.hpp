@@ -103,6 +103,29 @@ bool fwht_left_mma_ok(const void* src, int dt, const void* dst, int out_dt, int6
 hipError_t fwht_left_mma(const void* src, int dt, int64_t rows, int64_t cols, int k, void* dst,
                          hipStream_t st);
 hipError_t rows_pass(const RowPass& p, hipStream_t st);
+
+// Statistics of a right-rotated tensor (hq_rotate.hip, stat_kernel): mode is a StatMode
+// (0 sum |v|, 1 sum (v - s q)^2, 2 LSQ step gradient, 3 max |v|); the reduced value goes to
+// out (device double, or nullptr), and finish 1 / 2 also writes the absmax scale / cold-start
+// step to fout. partials: kStatMaxParts doubles of workspace.
+constexpr int kStatMaxParts = 1024;
+constexpr int STAT_MODE_ABS_MAX = 3;
+struct StatPass {
+  const void* src = nullptr;
+  const void* grad = nullptr;
+  int dt = 0;
+  int64_t rows = 0, cols = 0;
+  int k = 1;
+  int mode = 0;
+  bool f8 = false;
+  int qp = 127;
+  const float* scale = nullptr;
+  double* partials = nullptr;
+  double* out = nullptr;
+  int finish = 0;
+  float* fout = nullptr;
+};
+hipError_t stat_pass(const StatPass& p, hipStream_t st);
 hipError_t cols_pass(const ColPass& p, hipStream_t st);
 hipError_t write_scale(float* scale, const float* step, hipStream_t st);
 

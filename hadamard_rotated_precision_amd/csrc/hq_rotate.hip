@@ -15,6 +15,8 @@
 //                  KL-row tile in LDS (fp32, column-swizzled), each thread owns KL/P consecutive
 //                  rows of one column (in-register stages) and P lanes share a column; the tile
 //                  goes back through LDS so the stores are row-contiguous.
+#include <algorithm>
+
 #include "hq_device.hpp"
 #include "hq_internal.hpp"
 
@@ -59,6 +61,184 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(RowArgs a) {
     // 16-byte stores when the run is whole and aligned, element stores otherwise
     store_run<Out, 16>(a.dst, row * a.cols + c0, a.cols - c0, v, 1.0f);
   }
+}
+
+// ============================================================ rotated statistics
+// One pass over a right-rotated tensor R = V B (and, for the step gradient, the rotated
+// gradient G B) reducing one per-element term ("Training Transformers with 4-bit Integers",
+// §A.3 step gradients from cheap elementwise residuals, §A.4 cold-start steps, §A.5 the
+// Hadamard size minimising the quantization errors):
+//   STAT_ABS_SUM  |v|              STAT_ABS_MAX  max |v| (the absmax of a candidate size)
+//   STAT_QERR     (v - s q(v))^2   q: the library's quantizer (integer or E4M3 codes)
+//   STAT_LSQ      (g / k) dv_hat/ds, dv_hat/ds = q - v/s inside the grid, +-Qp clipped
+// Layout as rows_kernel: a 16-lane group owns a 256-column segment of one row, 16 consecutive
+// elements per lane. Each thread sums in fp64; per-workgroup partials (fp64) are reduced in a
+// fixed order by stat_finish_kernel, so results do not depend on scheduling.
+enum StatMode : int { STAT_ABS_SUM = 0, STAT_QERR = 1, STAT_LSQ = 2, STAT_ABS_MAX = 3 };
+
+struct StatArgs {
+  const void* src;
+  const void* grad;       // STAT_LSQ: gradient with respect to V (same shape and dtype)
+  int64_t rows, cols;
+  bool vec;
+  const float* scale;     // STAT_QERR / STAT_LSQ: the step s
+  int qp;
+  float inv_k;            // STAT_LSQ: 1 / k (the gradient with respect to R is (G B) / k)
+  double* partials;       // one per workgroup
+};
+
+__device__ inline double block_sum_f64(double x, double* red, bool take_max) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const double y = __shfl_xor(x, m, 64);
+    x = take_max ? fmax(x, y) : x + y;
+  }
+  __syncthreads();
+  if (lane == 0) red[wid] = x;
+  __syncthreads();
+  double r = red[0];
+  for (int w = 1; w < nw; ++w) r = take_max ? fmax(r, red[w]) : r + red[w];
+  return r;
+}
+
+template <class In, int KR, int MODE, bool F8>
+__global__ __launch_bounds__(kThreads) void stat_kernel(StatArgs a) {
+  __shared__ double red[kThreads / 64];
+  const int lane = threadIdx.x & 63;
+  const int g = lane & 15;
+  const int group = (blockIdx.x * kThreads + threadIdx.x) >> 4;
+  const int ngroups = (gridDim.x * kThreads) >> 4;
+  const int64_t nseg = (a.cols + 255) / 256;
+  const int64_t items = a.rows * nseg;
+  const int64_t iters = (items + ngroups - 1) / ngroups;
+  float s = 0.0f, r = 0.0f;
+  if constexpr (MODE == STAT_QERR || MODE == STAT_LSQ) {
+    s = *a.scale;
+    r = (s > 0.0f) ? 1.0f / s : 0.0f;
+  }
+  double acc = 0.0;
+  for (int64_t it = 0; it < iters; ++it) {
+    const int64_t item = group + it * ngroups;
+    const bool live = item < items;
+    const int64_t row = live ? item / nseg : 0;
+    const int64_t c0 = live ? (item % nseg) * 256 + 16 * g : a.cols;
+    const bool full = c0 + 16 <= a.cols;
+    float v[16];
+    load16<In>(static_cast<const char*>(a.src) + row * a.cols * In::bytes, c0,
+               live ? a.cols : 0, a.vec && full, v);
+    fwht_inreg<KR, 16>(v);
+#pragma unroll
+    for (int m = 1; 16 * m < KR; m <<= 1) fwht_xlane<16>(v, g, m);
+    float gv[16];
+    if constexpr (MODE == STAT_LSQ) {
+      load16<In>(static_cast<const char*>(a.grad) + row * a.cols * In::bytes, c0,
+                 live ? a.cols : 0, a.vec && full, gv);
+      fwht_inreg<KR, 16>(gv);
+#pragma unroll
+      for (int m = 1; 16 * m < KR; m <<= 1) fwht_xlane<16>(gv, g, m);
+    }
+    if (!live) continue;   // loads past the end read zeros: their terms are zero
+    float part = 0.0f;     // at most 16 terms in fp32, then into the fp64 sum
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if constexpr (MODE == STAT_ABS_SUM) {
+        part += fabsf(v[i]);
+      } else if constexpr (MODE == STAT_ABS_MAX) {
+        part = fmaxf(part, fabsf(v[i]));
+      } else if constexpr (MODE == STAT_QERR) {
+        // the difference in fp64 (s times a code is exact there): it cancels most of v
+        double level;
+        if constexpr (F8) {
+          const uint32_t c = e4m3_pack4(v[i], 0.0f, 0.0f, 0.0f, r);
+          level = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(c), 0);
+        } else {
+          level = quant_code(v[i], r, a.qp);
+        }
+        const double e = static_cast<double>(v[i]) - static_cast<double>(s) * level;
+        acc += e * e;
+      } else {
+        const double x = static_cast<double>(v[i]) / static_cast<double>(s);
+        const double d = fabs(x) >= a.qp ? copysign(static_cast<double>(a.qp), x)
+                                         : static_cast<double>(quant_code(v[i], r, a.qp)) - x;
+        acc += static_cast<double>(gv[i]) * a.inv_k * d;
+      }
+    }
+    if constexpr (MODE == STAT_ABS_SUM) acc += part;
+    if constexpr (MODE == STAT_ABS_MAX) acc = fmax(acc, static_cast<double>(part));
+  }
+  acc = block_sum_f64(acc, red, MODE == STAT_ABS_MAX);
+  if (threadIdx.x == 0) a.partials[blockIdx.x] = acc;
+}
+
+// Reduce the partials in order into out[0]; then, by `finish`: 0 nothing more; 1 the scale
+// max / qp (fp32, for STAT_ABS_MAX: the tensor-wise absmax scale); 2 the cold-start step
+// fp32(2 * (sum / n) / sqrt(qp)) into fout.
+__global__ void stat_finish_kernel(const double* partials, int nparts, bool take_max, double* out,
+                                   int finish, double n, int qp, float* fout) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  double t = 0.0;
+  for (int i = 0; i < nparts; ++i) t = take_max ? fmax(t, partials[i]) : t + partials[i];
+  if (out) *out = t;
+  if (finish == 1) *fout = static_cast<float>(t) / static_cast<float>(qp);
+  if (finish == 2) *fout = static_cast<float>(2.0 * (t / n) / sqrt(static_cast<double>(qp)));
+}
+
+template <class In, int MODE, bool F8>
+static hipError_t stat_launch_k(int k, const StatArgs& a, int grid, hipStream_t st, int tok) {
+  switch (k) {
+#define HQ_SK(KK) \
+  case KK: return launch_k(stat_kernel<In, KK, MODE, F8>, dim3(grid), dim3(kThreads), st, tok, a);
+    HQ_SK(1) HQ_SK(2) HQ_SK(4) HQ_SK(8) HQ_SK(16) HQ_SK(32) HQ_SK(64) HQ_SK(128) HQ_SK(256)
+#undef HQ_SK
+  }
+  return hipErrorInvalidValue;
+}
+
+template <class In>
+static hipError_t stat_launch_in(int k, int mode, bool f8, const StatArgs& a, int grid,
+                                 hipStream_t st, int tok) {
+  switch (mode) {
+    case STAT_ABS_SUM: return stat_launch_k<In, STAT_ABS_SUM, false>(k, a, grid, st, tok);
+    case STAT_ABS_MAX: return stat_launch_k<In, STAT_ABS_MAX, false>(k, a, grid, st, tok);
+    case STAT_QERR:
+      return f8 ? stat_launch_k<In, STAT_QERR, true>(k, a, grid, st, tok)
+                : stat_launch_k<In, STAT_QERR, false>(k, a, grid, st, tok);
+    case STAT_LSQ: return stat_launch_k<In, STAT_LSQ, false>(k, a, grid, st, tok);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t stat_pass(const StatPass& p, hipStream_t st) {
+  StatArgs a{};
+  a.src = p.src;
+  a.grad = p.grad;
+  a.rows = p.rows;
+  a.cols = p.cols;
+  const int eb = p.dt == DT_F32 ? 4 : 2;
+  a.vec = (reinterpret_cast<uintptr_t>(p.src) & 15u) == 0 && (p.cols * eb) % 16 == 0 &&
+          (!p.grad || (reinterpret_cast<uintptr_t>(p.grad) & 15u) == 0);
+  a.scale = p.scale;
+  a.qp = p.qp;
+  a.inv_k = 1.0f / static_cast<float>(p.k);
+  a.partials = p.partials;
+  const int64_t items = p.rows * ((p.cols + 255) / 256);
+  const int64_t groups_per_block = kThreads / 16;
+  int64_t grid = (items + groups_per_block - 1) / groups_per_block;
+  grid = std::max<int64_t>(1, std::min<int64_t>(grid, kStatMaxParts));
+  const double bytes = static_cast<double>(p.rows) * p.cols * eb * (p.grad ? 2 : 1);
+  const int tok = prof_open(K_MISC, bytes);
+  hipError_t e = hipErrorInvalidValue;
+  switch (p.dt) {
+    case DT_F32: e = stat_launch_in<F32>(p.k, p.mode, p.f8, a, static_cast<int>(grid), st, tok); break;
+    case DT_F16: e = stat_launch_in<F16>(p.k, p.mode, p.f8, a, static_cast<int>(grid), st, tok); break;
+    case DT_BF16: e = stat_launch_in<BF16>(p.k, p.mode, p.f8, a, static_cast<int>(grid), st, tok); break;
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(stat_finish_kernel, dim3(1), dim3(64), 0, st, p.partials, static_cast<int>(grid),
+                     p.mode == STAT_ABS_MAX, p.out, p.finish,
+                     static_cast<double>(p.rows) * static_cast<double>(p.cols), p.qp, p.fout);
+  return hipGetLastError();
 }
 
 // ============================================================ cols kernel (LEFT)

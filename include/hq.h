@@ -26,7 +26,8 @@
  *     16-byte aligned (HQ_ERR_ALIGN otherwise), except hq_fwht's src and dst, which need only
  *     the alignment of their element type.
  *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*; NULL is the
- *     default stream). Scales stay on the device; no call synchronizes with the host.
+ *     default stream). Scales stay on the device; no call synchronizes with the host, except
+ *     hq_select_hadamard_k, whose choice is made on the host.
  *   - Ownership: the caller allocates every buffer (codes, scales, outputs, workspace).
  *     The library allocates and frees nothing and keeps no pointer after it returns. Buffers
  *     must stay alive until the stream has reached the work.
@@ -244,6 +245,48 @@ hq_status hq_bmm_bwd_input(const void *dy, int32_t dy_dtype, int64_t batch, int6
 hq_status hq_bmm_bwd_weight(const hq_qtensor *saved_g, const hq_qtensor *saved_x, int64_t batch,
                             int64_t N, int64_t C, int64_t D, const hq_config *cfg, void *dw,
                             int32_t dw_dtype, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------- quantizer parameters
+ * Statistics of a right-rotated tensor R = V B (rot RIGHT, blocks of cfg->k; rot NONE: R = V)
+ * that set the quantizer parameters ("Training Transformers with 4-bit Integers", §3.1 learned
+ * step, §A.3 step gradients by the chain rule from cheap elementwise residuals, §A.4 cold
+ * start, §A.5 Hadamard size):
+ *   HQ_STAT_ABS_SUM   sum |r|
+ *   HQ_STAT_QERR      sum (r - s * value(code(r)))^2, code() the library's quantizer of cfg
+ *                     (integer or E4M3), s = *scale
+ *   HQ_STAT_LSQ_GRAD  sum (G B / k)_i * dv_hat_i/ds: the learned-step gradient of the loss with
+ *                     respect to s, G = dL/dV (rows x cols, same dtype), straight-through
+ *                     rounding: dv_hat/ds = code(r) - r/s inside the grid, +-Qp where clipped
+ *                     (integer codes only; s must be > 0)
+ * The terms are summed in fp64 (per-workgroup partials reduced in a fixed order) into *out
+ * (one device double). The rotation is in fp32 as in hq_fwht. Workspace as hq_rotate_quantize. */
+typedef enum { HQ_STAT_ABS_SUM = 0, HQ_STAT_QERR = 1, HQ_STAT_LSQ_GRAD = 2 } hq_stat_kind;
+
+hq_status hq_rotated_stat(const void *src, const void *grad, int32_t dtype, int64_t rows,
+                          int64_t cols, int32_t rot, const hq_config *cfg, int32_t stat,
+                          const float *scale, double *out, void *ws, size_t ws_bytes,
+                          void *stream);
+
+/* Cold-start step of a tensor (INT4 page §A.4: before steps are learned a heuristic sets
+ * them; the page does not give it, the library takes the learned-step initialisation):
+ * *step = fp32(2 * mean|r| / sqrt(Qp)) over R = V B (or V), written on the device, ready as a
+ * STEP-mode step. Integer codes only; HQ_ERR_SHAPE for an empty tensor. */
+hq_status hq_cold_start_step(const void *src, int32_t dtype, int64_t rows, int64_t cols,
+                             int32_t rot, const hq_config *cfg, float *step, void *ws,
+                             size_t ws_bytes, void *stream);
+
+/* Hadamard size selection (INT4 page §A.5): for each candidate k (powers of two dividing C,
+ * at most HQ_MAX_K_CANDIDATES of them, host array), the quantization errors of X (N x C) and
+ * W (D x C) with the tensor-wise absmax scale of X B_k and W B_k in cfg's format,
+ * err = ||V - s Q(V B) B / k||_F^2 = sum (r - s q)^2 / k; *k_best (host) = the candidate with
+ * the smallest err_X * err_W (ties: the earlier candidate); errors (host, 2 per candidate:
+ * err_X, err_W) may be NULL. Runs on `stream` and WAITS for it (the choice is made on the
+ * host): a setup-time call, not for graph capture. */
+#define HQ_MAX_K_CANDIDATES 16
+hq_status hq_select_hadamard_k(const void *x, const void *w, int32_t dtype, int64_t N,
+                               int64_t C, int64_t D, const hq_config *cfg,
+                               const int32_t *candidates, int32_t n_candidates, int32_t *k_best,
+                               double *errors, void *ws, size_t ws_bytes, void *stream);
 
 /* Standalone block-diagonal Walsh-Hadamard transform (unnormalized): dst = rotation of src
  * (INT4 page §3.3). rows x cols row-major; rotated dims divisible by k; rot != BOTH

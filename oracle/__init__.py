@@ -427,8 +427,8 @@ def choose_hadamard_k(X, W, candidates, bits, fmt=INT):
     """Hadamard size selection (INT4 page §A.5): the candidate k minimising the product of the
     activation and weight quantization errors, the rotated tensors standing for X and W:
     err(V, k) = ||V - s Q(V B) B / k||_F^2 = sum (R - s q)^2 / k (B B = k I), with the tensor-
-    wise absmax scale of R = V B. Returns (best k, {k: (err_x, err_w)}); ties go to the smaller
-    k."""
+    wise absmax scale of R = V B. Returns (best k, {k: (err_x, err_w)}); ties go to the earlier
+    candidate."""
     errs = {}
     best = None
     for k in candidates:
