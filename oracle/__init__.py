@@ -441,3 +441,79 @@ def choose_hadamard_k(X, W, candidates, bits, fmt=INT):
         if best is None or e[0] * e[1] < errs[best][0] * errs[best][1]:
             best = k
     return best, errs
+
+
+# ------------------------------------------------ LSS-MM: the sampled weight gradient
+LSS_HI_QP = 7          # both halves of the bit split are INT4-range codes
+LSS_LO_DIV = 14        # s_lo = s_hi / 14: the smallest step whose [-7, 7] covers a half step
+
+
+def lss_probabilities(scores, budget):
+    """Leverage-score sampling probabilities ("Training Transformers with 4-bit Integers",
+    §4.2 probabilities in proportion to leverage scores, §A.2 the clamp-and-rescale
+    procedure): p = budget * l / sum(l); while some p exceed 1, those are set to 1 and the
+    others rescaled to fill what remains of the budget. Zero scores get p = 0; if the budget
+    covers every nonzero score they all get 1. Double precision, sums in index order."""
+    l = np.asarray(scores, dtype=np.float64)
+    p = np.zeros_like(l)
+    fixed = np.zeros(l.shape, dtype=bool)        # probabilities clamped to 1
+    nonzero = l > 0
+    while True:
+        free = nonzero & ~fixed
+        left = float(budget) - float(np.count_nonzero(fixed))
+        if not free.any() or left <= 0:
+            break
+        tot = 0.0
+        for v in l[free]:                        # the sum in index order
+            tot += float(v)
+        p[free] = left * l[free] / tot
+        over = free & (p > 1.0)
+        if not over.any():
+            break
+        p[over] = 1.0
+        fixed |= over
+    return p
+
+
+def lss_weight_gradient(G, qx, sx, k, budget, uniforms, rot=ROT_RIGHT):
+    """LSS-MM for the weight gradient of the INT4-range HQ layer (INT4 page §4.2 bit splitting
+    and leverage-score sampling, §A.2 probabilities, §A.3 LSS-MM stages, §A.6 INT8 data for the
+    scores and K padding after sampling, §B.2 the unbiased row-sampled estimator):
+      1. scores: q8 = Q(dY) on the INT8 grid (tensor-wise absmax), l_i = |q8_i| |qx_i|
+         (Euclidean norms of integer rows; qx = the forward's codes of X B_C);
+      2. probabilities p = lss_probabilities(l, budget); token i is kept iff u_i < p_i (the
+         uniforms are an input);
+      3. kept rows weighted by 1 / p_i (unbiased: E[sum m_i / p_i g_i x_i] = sum g_i x_i);
+      4. bit split of the kept, weighted rows Gw: s_hi = max|Gw| / 7, hi = Q_7(Gw / s_hi),
+         s_lo = s_hi / 14, lo = Q_7((Gw - s_hi hi) / s_lo); Gw ~ s_lo (14 hi + lo);
+      5. dW = (14 hi + lo)^T qx_kept B_C s_lo sx / k: the two INT4 products (hi, lo) summed
+         exactly as one integer product over the kept tokens, then the inverse rotation.
+    Returns a dict: scores, p, keep (indices), s_hi, s_lo, hi, lo, dw (double, D x C)."""
+    G = np.ascontiguousarray(G, dtype=np.float64)
+    qx = np.ascontiguousarray(qx, dtype=np.int8)
+    N, D = G.shape
+    C = qx.shape[1]
+    s8 = absmax_scale(G, 127)
+    q8 = quantize(G, s8, 127).astype(np.int64)
+    xi = qx.astype(np.int64)
+    scores = np.sqrt((q8 * q8).sum(axis=1).astype(np.float64)) * \
+        np.sqrt((xi * xi).sum(axis=1).astype(np.float64))
+    p = lss_probabilities(scores, budget)
+    keep = np.nonzero(np.asarray(uniforms, dtype=np.float32).astype(np.float64) < p)[0]
+    out = {"scores": scores, "p": p, "keep": keep}
+    Gw = G[keep] / p[keep][:, None]
+    s_hi = absmax_scale(Gw, LSS_HI_QP) if keep.size else np.float32(0)
+    hi = quantize(Gw, s_hi, LSS_HI_QP)
+    s_lo = np.float32(float(s_hi) / LSS_LO_DIV)
+    lo = quantize(Gw - float(s_hi) * hi.astype(np.float64), s_lo, LSS_HI_QP)
+    out.update(s_hi=s_hi, s_lo=s_lo, hi=hi, lo=lo)
+    comb = (LSS_LO_DIV * hi.astype(np.int64) + lo.astype(np.int64)).astype(np.int8)
+    xk = np.ascontiguousarray(qx[keep])
+    K = keep.size
+    T = gemm_i8(comb, 1, D, xk, C, 1, D, C, K) if K else np.zeros((D, C), dtype=np.int64)
+    kk = 1
+    if rot == ROT_RIGHT:
+        T = rotate_i64(T, ROT_RIGHT, k)
+        kk = k
+    out["dw"] = dequant(T, s_lo, sx, kk)
+    return out
