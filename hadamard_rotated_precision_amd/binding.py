@@ -27,7 +27,8 @@ EXPORTS = ["hq_abi_version", "hq_status_string", "hq_code_pitch", "hq_workspace_
            "hq_linear_bwd_weight", "hq_fwht", "hq_fwht_path", "hq_gemm_i8_i32", "hq_gemm_f8_f32",
            "hq_profile_start", "hq_profile_stop", "hq_profile_records",
            "hq_bmm_workspace_bytes", "hq_bmm_fwd", "hq_bmm_bwd_input", "hq_bmm_bwd_weight",
-           "hq_rotated_stat", "hq_cold_start_step", "hq_select_hadamard_k"]
+           "hq_rotated_stat", "hq_cold_start_step", "hq_select_hadamard_k",
+           "hq_lss_workspace_bytes", "hq_lss_bwd_weight"]
 HQ_STAT_ABS_SUM, HQ_STAT_QERR, HQ_STAT_LSQ_GRAD = 0, 1, 2
 HQ_MAX_K_CANDIDATES = 16
 HQ_KIND_GEMM, HQ_KIND_ROT_ABSMAX, HQ_KIND_ROT_QUANT, HQ_KIND_ROT_STORE = 0, 1, 2, 3
@@ -46,6 +47,11 @@ class hq_qtensor(ctypes.Structure):
                 ("scale", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
                 ("ld", ctypes.c_int64), ("ld_t", ctypes.c_int64), ("k", ctypes.c_int32),
                 ("bits", ctypes.c_int32), ("rot", ctypes.c_int32), ("format", ctypes.c_int32)]
+
+
+class hq_lss_stats(ctypes.Structure):
+    _fields_ = [("kept", ctypes.c_int32), ("s8", ctypes.c_float), ("s_hi", ctypes.c_float),
+                ("s_lo", ctypes.c_float)]
 
 
 class hq_profile_stat(ctypes.Structure):
@@ -130,6 +136,11 @@ def load(build_if_missing=True):
     lib.hq_select_hadamard_k.restype = i32
     lib.hq_select_hadamard_k.argtypes = [vp, vp, i32, i64, i64, i64, P(hq_config), vp, i32, vp,
                                          vp, vp, sz, vp]
+    lib.hq_lss_workspace_bytes.restype = sz
+    lib.hq_lss_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.hq_lss_bwd_weight.restype = i32
+    lib.hq_lss_bwd_weight.argtypes = [vp, i32, P(hq_qtensor), i64, i64, i64, P(hq_config),
+                                      ctypes.c_double, vp, vp, i32, vp, vp, vp, vp, sz, vp]
     lib.hq_gemm_f8_f32.restype = i32
     lib.hq_gemm_f8_f32.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, vp]
     lib.hq_fwht_path.restype = i32
@@ -249,6 +260,18 @@ def hq_select_hadamard_k(x, w, dtype, N, C, D, cfg, candidates, n_candidates, k_
     return load().hq_select_hadamard_k(x, w, dtype, N, C, D, _ref(cfg), candidates, n_candidates,
                                        ctypes.byref(k_best),
                                        None if errors is None else errors, ws, ws_bytes, stream)
+
+
+def hq_lss_workspace_bytes(N, C, D):
+    return load().hq_lss_workspace_bytes(N, C, D)
+
+
+def hq_lss_bwd_weight(dy, dy_dtype, saved_x, N, C, D, cfg, budget, uniforms, dw, dw_dtype, probs,
+                      kept_idx, stats, ws, ws_bytes, stream):
+    """probs, kept_idx, stats: device pointers (stats: one hq_lss_stats on the device) or None."""
+    return load().hq_lss_bwd_weight(dy, dy_dtype, _ref(saved_x), N, C, D, _ref(cfg), budget,
+                                    uniforms, dw, dw_dtype, probs, kept_idx, stats, ws, ws_bytes,
+                                    stream)
 
 
 def hq_gemm_f8_f32(a, lda, b_t, ldb, c, M, N, K, stream):

@@ -8,7 +8,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libhq.so")
 
-SOURCES = ["hq_rotate.hip", "hq_prologue.hip", "hq_gemm.hip", "hq_static.hip", "hq_api.cpp",
+SOURCES = ["hq_rotate.hip", "hq_prologue.hip", "hq_gemm.hip", "hq_static.hip", "hq_lss.hip", "hq_api.cpp",
            "hq_profile.cpp"]
 
 # -packed-fp32-ops: hipcc forms packed fp32 ops from plain float code; keep them out.

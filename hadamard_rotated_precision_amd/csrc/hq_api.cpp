@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <mutex>
 #include <string.h>
 
@@ -874,6 +875,146 @@ hq_status hq_gemm_f8_f32(const uint8_t* a, int64_t lda, const uint8_t* b_t, int6
 hq_status hq_gemm_i8_i32(const int8_t* a, int64_t lda, const int8_t* b_t, int64_t ldb,
                          int32_t* c, int64_t M, int64_t N, int64_t K, void* stream) {
   return gemm_plain(a, lda, b_t, ldb, c, M, N, K, false, stream);
+}
+
+}  // extern "C"
+
+namespace {
+// LSS-MM workspace: absmax partials, the stats record, then per-token arrays (row maxima,
+// scores, probabilities, clamp flags, kept list) and the two K-contiguous GEMM operands.
+constexpr int64_t kLssMaxN = int64_t(1) << 21;   // int32 sums of the combined-code product
+constexpr int64_t kLssMaxDim = int64_t(1) << 20;   // pack grid: (C + D) / 64 rows of tiles
+
+struct LssWs {
+  float* partials;
+  hq_lss_stats* stats;
+  float* rowmax;
+  double* scores;
+  double* probs;
+  uint8_t* fixed;
+  int32_t* kept_idx;
+  int8_t* ct;
+  int8_t* xt;
+  int64_t ldk;
+  size_t bytes;
+  LssWs(void* base, int64_t N, int64_t C, int64_t D) {
+    char* b = static_cast<char*>(base);
+    size_t off = 0;
+    auto take = [&](size_t n) {
+      char* p = b ? b + off : nullptr;
+      off = align_up(off + n, kAlign);
+      return p;
+    };
+    ldk = pitch16(N);
+    partials = reinterpret_cast<float*>(take(hq::kMaxPartials * sizeof(float)));
+    stats = reinterpret_cast<hq_lss_stats*>(take(sizeof(hq_lss_stats)));
+    rowmax = reinterpret_cast<float*>(take(N * sizeof(float)));
+    scores = reinterpret_cast<double*>(take(N * sizeof(double)));
+    probs = reinterpret_cast<double*>(take(N * sizeof(double)));
+    fixed = reinterpret_cast<uint8_t*>(take(N));
+    kept_idx = reinterpret_cast<int32_t*>(take(N * sizeof(int32_t)));
+    ct = reinterpret_cast<int8_t*>(take(D * ldk));
+    xt = reinterpret_cast<int8_t*>(take(C * ldk));
+    bytes = off;
+  }
+};
+
+bool lss_dims_ok(int64_t N, int64_t C, int64_t D) {
+  return N >= 0 && C >= 0 && D >= 0 && N <= kLssMaxN && C <= kLssMaxDim && D <= kLssMaxDim;
+}
+}  // namespace
+
+extern "C" {
+
+size_t hq_lss_workspace_bytes(int64_t N, int64_t C, int64_t D) {
+  if (!lss_dims_ok(N, C, D)) return 0;
+  return LssWs(nullptr, N, C, D).bytes;
+}
+
+hq_status hq_lss_bwd_weight(const void* dy, int32_t dy_dtype, const hq_qtensor* saved_x,
+                            int64_t N, int64_t C, int64_t D, const hq_config* cfg, double budget,
+                            const float* uniforms, void* dw, int32_t dw_dtype, double* probs,
+                            int32_t* kept_idx, hq_lss_stats* stats, void* ws, size_t ws_bytes,
+                            void* stream) {
+  HQ_CHECK(check_cfg(cfg));
+  if (cfg->format != HQ_FMT_INT) return HQ_ERR_MODE;
+  if (cfg->bits != 4) return HQ_ERR_BITS;
+  const int32_t v = cfg->variant, k = cfg->k;
+  if (v != HQ_VARIANT_HQ && v != HQ_VARIANT_HALO0) return HQ_ERR_MODE;
+  if (!valid_dt(dy_dtype) || !valid_dt(dw_dtype)) return HQ_ERR_DTYPE;
+  if (!lss_dims_ok(N, C, D)) return HQ_ERR_SHAPE;
+  if (v == HQ_VARIANT_HQ && C % k) return HQ_ERR_SHAPE;
+  if (!std::isfinite(budget)) return HQ_ERR_SHAPE;
+  if (N * D > 0 && !dy) return HQ_ERR_NULL;
+  if (N > 0 && !uniforms) return HQ_ERR_NULL;
+  if (D * C > 0 && !dw) return HQ_ERR_NULL;
+  if (!saved_x || !saved_x->scale || (N * C > 0 && !saved_x->codes)) return HQ_ERR_NULL;
+  if (saved_x->rows != N || saved_x->cols != C || saved_x->k != k || saved_x->bits != cfg->bits ||
+      saved_x->rot != x_rot(v) || saved_x->format != cfg->format)
+    return HQ_ERR_MISMATCH;
+  if (saved_x->codes && (!aligned16(saved_x->codes) || saved_x->ld % 16)) return HQ_ERR_ALIGN;
+  if (saved_x->codes && saved_x->ld < C) return HQ_ERR_SHAPE;
+  if ((probs && !aligned16(probs)) || (kept_idx && !aligned16(kept_idx)) ||
+      (stats && !aligned16(stats)))
+    return HQ_ERR_ALIGN;
+  const LssWs need(nullptr, N, C, D);
+  HQ_CHECK(check_ws(ws, ws_bytes, need.bytes));
+  HQ_CHECK(device_ok());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  LssWs w(ws, N, C, D);
+  hq::LssPass p;
+  p.dy = dy;
+  p.dt = dy_dtype;
+  p.N = N;
+  p.C = C;
+  p.D = D;
+  p.qx = saved_x->codes;
+  p.ldx = saved_x->ld;
+  p.budget = budget;
+  p.uniforms = uniforms;
+  p.partials = w.partials;
+  p.rowmax = w.rowmax;
+  p.scores = w.scores;
+  p.probs = probs ? probs : w.probs;
+  p.fixed = w.fixed;
+  p.kept_idx = kept_idx ? kept_idx : w.kept_idx;
+  p.stats = stats ? stats : w.stats;
+  p.ct = w.ct;
+  p.xt = w.xt;
+  p.ldk = w.ldk;
+  HQ_TRY(hq::lss_pass(p, st));
+  // dW = (14 hi + lo)^T qX_kept [B_C] s_lo sX / k over the K' kept tokens; with B_C the
+  // transpose dW^T = qX_kept^T (14 hi + lo) is formed so C is the tile's rotated row axis
+  GemmPass g;
+  g.cus = device_info().cus;
+  g.epi = hq::EPI_SCALE;
+  g.sa = &p.stats->s_lo;
+  g.sb = saved_x->scale;
+  g.c = dw;
+  g.out_dt = dw_dtype;
+  g.ldc = C;
+  g.K = N;
+  g.k_dev = &p.stats->kept;
+  if (v == HQ_VARIANT_HALO0) {
+    g.a = w.ct;
+    g.lda = w.ldk;
+    g.b = w.xt;
+    g.ldb = w.ldk;
+    g.M = D;
+    g.N = C;
+  } else {
+    g.a = w.xt;
+    g.lda = w.ldk;
+    g.b = w.ct;
+    g.ldb = w.ldk;
+    g.M = C;
+    g.N = D;
+    g.km = k;
+    g.trans_out = true;
+    g.kmul = 1.0f / static_cast<float>(k);
+  }
+  HQ_TRY(hq::gemm_pass(g, st));
+  return HQ_OK;
 }
 
 }  // extern "C"

@@ -74,6 +74,10 @@ struct GemmArgs {
   // batched products (grid.y = batch index): offsets of a batch's a and b (bytes) and c
   // (elements); the scales are shared (one per batched tensor)
   int64_t a_bstride, b_bstride, c_bstride;
+  // when set, the contraction stops at min(K, *k_dev) (a length an earlier kernel on the stream
+  // wrote, e.g. the number of sampled rows); operand bytes from there to the next multiple of
+  // 16 must be zero
+  const int32_t* k_dev;
 };
 
 
@@ -225,7 +229,8 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-  const int kbeg = 0, kend = static_cast<int>(g.K);
+  const int kbeg = 0;
+  const int kend = g.k_dev ? min(static_cast<int>(g.K), max(0, *g.k_dev)) : static_cast<int>(g.K);
   const int KT = (kend - kbeg + GBK - 1) / GBK;
   // Operands go straight from memory into LDS (buffer loads with the lds bit): each wave
   // instruction fills 1 KB of LDS, lane l writing bytes 16l..16l+15, i.e. 16 rows of 64 bytes.
@@ -789,7 +794,7 @@ size_t gemm_split_bytes(int64_t pairs) {
 
 hipError_t gemm_pass(const GemmPass& p, hipStream_t st) {
   GemmArgs a{p.a, p.lda, p.b, p.ldb, p.M, p.N, p.K, p.c, p.ldc, p.sa, p.sb, p.kmul,
-             nullptr, nullptr, 40, p.a_bstride, p.b_bstride, p.c_bstride};
+             nullptr, nullptr, 40, p.a_bstride, p.b_bstride, p.c_bstride, p.k_dev};
   if (p.batch < 1 || p.batch > 65535) return hipErrorInvalidValue;
   // Test hook: HQ_PAIR_SPIN bounds the tile-pair wait (40 polls of ~0.5 us by default); 0 makes
   // every early tile take the wait-free fallback, which tests use to cover that path.

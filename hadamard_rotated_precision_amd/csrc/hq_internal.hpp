@@ -129,6 +129,31 @@ hipError_t stat_pass(const StatPass& p, hipStream_t st);
 hipError_t cols_pass(const ColPass& p, hipStream_t st);
 hipError_t write_scale(float* scale, const float* step, hipStream_t st);
 
+// LSS-MM sampling and bit split (hq_lss.hip): rowmax, score, probability and pack passes, up
+// to the K-contiguous operands of the sampled weight-gradient GEMM (ct: D x ldk split codes,
+// xt: C x ldk gathered X codes, K' = stats->kept columns valid, zeros up to the next multiple
+// of 16). Buffers of N entries each; partials: kMaxPartials floats.
+struct LssPass {
+  const void* dy = nullptr;
+  int dt = 0;
+  int64_t N = 0, C = 0, D = 0;
+  const int8_t* qx = nullptr;   // row-major X codes, pitch ldx
+  int64_t ldx = 0;
+  double budget = 0.0;
+  const float* uniforms = nullptr;
+  float* partials = nullptr;
+  float* rowmax = nullptr;
+  double* scores = nullptr;
+  double* probs = nullptr;
+  uint8_t* fixed = nullptr;
+  int32_t* kept_idx = nullptr;
+  hq_lss_stats* stats = nullptr;
+  int8_t* ct = nullptr;
+  int8_t* xt = nullptr;
+  int64_t ldk = 0;
+};
+hipError_t lss_pass(const LssPass& p, hipStream_t st);
+
 // Integer GEMM c = a * b^T (a: M x K, b: N x K, int8, K-contiguous) with int32 accumulation,
 // or (f8) the product of FP8 E4M3 code matrices with fp32 accumulation.
 enum Epi : int { EPI_I32 = 0, EPI_SCALE = 1 };
@@ -155,6 +180,7 @@ struct GemmPass {
   int batch = 1;           // batched product: batch b reads a + b a_bstride, b + b b_bstride
   int64_t a_bstride = 0, b_bstride = 0;   // (bytes) and writes c + b c_bstride (elements)
   int64_t c_bstride = 0;
+  const int32_t* k_dev = nullptr;   // contraction length written on the device (<= K), or none
 };
 hipError_t gemm_pass(const GemmPass& p, hipStream_t st);
 // Number of tile pairs of a GEMM whose 256-wide column rotation spans two 256 x 128 tiles

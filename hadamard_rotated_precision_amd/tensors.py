@@ -145,3 +145,30 @@ class BatchedLayer:
         B.check(B.hq_bmm_bwd_weight(
             self.qg.st, qx.st, self.batch, self.N, self.C, self.D, self.cfg, ptr(dw),
             HQ_DT[dw.dtype], ptr(self.ws), self.ws_bytes, stream_ptr(stream)), "hq_bmm_bwd_weight")
+
+
+class LssGrad:
+    """Buffers for the sampled weight gradient (hq_lss_bwd_weight) of an N x C -> D layer:
+    workspace, probabilities, kept-token list and the stats record (kept, s8, s_hi, s_lo)."""
+
+    def __init__(self, N, C, D, k, variant=B.HQ_VARIANT_HQ, device="cuda"):
+        self.N, self.C, self.D = N, C, D
+        self.cfg = config(k, 4, B.HQ_SCALE_ABSMAX, variant)
+        self.ws_bytes = B.hq_lss_workspace_bytes(N, C, D)
+        self.ws = torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=device)
+        self.probs = torch.empty(max(N, 1), dtype=torch.float64, device=device)
+        self.kept_idx = torch.empty(max(N, 1), dtype=torch.int32, device=device)
+        self.stats = torch.zeros(4, dtype=torch.int32, device=device)   # one hq_lss_stats
+
+    def __call__(self, dy, saved_x, uniforms, dw, budget, stream=None):
+        B.check(B.hq_lss_bwd_weight(
+            ptr(dy), HQ_DT[dy.dtype], saved_x.st, self.N, self.C, self.D, self.cfg, float(budget),
+            ptr(uniforms), ptr(dw), HQ_DT[dw.dtype], ptr(self.probs), ptr(self.kept_idx),
+            ptr(self.stats), ptr(self.ws), self.ws_bytes, stream_ptr(stream)),
+            "hq_lss_bwd_weight")
+
+    def read_stats(self):
+        """(kept, s8, s_hi, s_lo) on the host."""
+        h = self.stats.cpu().numpy()
+        f = h.view(np.float32)
+        return int(h[0]), np.float32(f[1]), np.float32(f[2]), np.float32(f[3])

@@ -288,6 +288,48 @@ hq_status hq_select_hadamard_k(const void *x, const void *w, int32_t dtype, int6
                                const int32_t *candidates, int32_t n_candidates, int32_t *k_best,
                                double *errors, void *ws, size_t ws_bytes, void *stream);
 
+/* LSS-MM: the weight gradient of the INT4-range HQ layer from a leverage-score sample of the
+ * tokens and a bit split of dY ("Training Transformers with 4-bit Integers": §4.2 bit splitting
+ * and leverage score sampling; §A.2 the probability procedure; §A.6 INT8 data for the scores,
+ * fused high/low quantization, zero padding of K after sampling; §B.2 the unbiased estimator):
+ *   1. q8 = Q(dY) on the INT8 grid with the tensor-wise absmax step s8; the score of token i is
+ *      l_i = ||q8_i|| * ||qX_i||, qX the forward's INT4 codes of X B_C (saved_x->codes);
+ *   2. p = clamp-and-rescale probabilities with sum(p) = budget where possible: p_i =
+ *      budget' l_i / sum_free(l) over the tokens not yet clamped, those above 1 set to 1 and
+ *      the rest rescaled to what the budget leaves, until none exceeds 1 (zero scores: p = 0;
+ *      budget >= the number of nonzero scores keeps every token with a nonzero score, the
+ *      page's practical choice); sums in fp64, in a fixed order;
+ *   3. token i is kept iff uniforms[i] < p_i (uniforms: N device floats in [0, 1), drawn by the
+ *      caller); the K' kept tokens, in increasing order, are weighted by 1 / p_i;
+ *   4. bit split of the kept weighted rows Gw = dY_i / p_i (fp64): s_hi = max|Gw| / 7,
+ *      hi = Q_7(Gw / s_hi), s_lo = s_hi / 14, lo = Q_7((Gw - s_hi hi) / s_lo), codes
+ *      14 hi + lo in [-105, 105];
+ *   5. dW = ((14 hi + lo)^T qX_kept) [B_C] s_lo sX / k, one integer GEMM over the K' kept
+ *      tokens (the page's two INT4 products, hi and lo, summed exactly in int32).
+ * The codes of steps 1 and 4 take the exact rule (round-to-nearest-even of the quotient, ties
+ * decided exactly; fp32 or fp64 products with an exact fallback near ties); steps fp32,
+ * s_hi and s8 the correctly rounded quotients.
+ * cfg: format INT, bits 4, variant HQ (B_C of block size k) or HALO0 (no rotation); saved_x
+ * as hq_linear_fwd writes it (row-major codes required, N x C). dy: N x D in dy_dtype.
+ * Output dw: D x C in dw_dtype. Optional device outputs (NULL: kept in the workspace):
+ * probs (N doubles, p), kept_idx (N int32, the first K' are the kept tokens), stats (one
+ * hq_lss_stats). N <= 2^21 (int32 sums); workspace hq_lss_workspace_bytes(N, C, D).
+ * The probability procedure runs on one workgroup: each round clamps at least one token, so
+ * it ends after at most N rounds (a few for ordinary score spreads). */
+typedef struct {
+  int32_t kept; /* K', the number of sampled tokens */
+  float s8;     /* step of the INT8 codes of dY behind the scores */
+  float s_hi;   /* step of the high part of the bit split */
+  float s_lo;   /* step of the low part (s_hi / 14) */
+} hq_lss_stats;
+
+size_t hq_lss_workspace_bytes(int64_t N, int64_t C, int64_t D);
+hq_status hq_lss_bwd_weight(const void *dy, int32_t dy_dtype, const hq_qtensor *saved_x,
+                            int64_t N, int64_t C, int64_t D, const hq_config *cfg, double budget,
+                            const float *uniforms, void *dw, int32_t dw_dtype, double *probs,
+                            int32_t *kept_idx, hq_lss_stats *stats, void *ws, size_t ws_bytes,
+                            void *stream);
+
 /* Standalone block-diagonal Walsh-Hadamard transform (unnormalized): dst = rotation of src
  * (INT4 page §3.3). rows x cols row-major; rotated dims divisible by k; rot != BOTH
  * for this entry point; src and dst must not overlap. Sums are formed in fp32 and rounded once

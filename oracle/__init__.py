@@ -475,7 +475,7 @@ def lss_probabilities(scores, budget):
     return p
 
 
-def lss_weight_gradient(G, qx, sx, k, budget, uniforms, rot=ROT_RIGHT):
+def lss_weight_gradient(G, qx, sx, k, budget, uniforms, rot=ROT_RIGHT, dw_rows=None):
     """LSS-MM for the weight gradient of the INT4-range HQ layer (INT4 page §4.2 bit splitting
     and leverage-score sampling, §A.2 probabilities, §A.3 LSS-MM stages, §A.6 INT8 data for the
     scores and K padding after sampling, §B.2 the unbiased row-sampled estimator):
@@ -488,7 +488,9 @@ def lss_weight_gradient(G, qx, sx, k, budget, uniforms, rot=ROT_RIGHT):
          s_lo = s_hi / 14, lo = Q_7((Gw - s_hi hi) / s_lo); Gw ~ s_lo (14 hi + lo);
       5. dW = (14 hi + lo)^T qx_kept B_C s_lo sx / k: the two INT4 products (hi, lo) summed
          exactly as one integer product over the kept tokens, then the inverse rotation.
-    Returns a dict: scores, p, keep (indices), s_hi, s_lo, hi, lo, dw (double, D x C)."""
+    dw_rows: optional index array or slice of the rows of dW to form (all by default).
+    Returns a dict: scores, p, keep (indices), s_hi, s_lo, hi, lo, dw (double, D x C, or
+    len(dw_rows) x C)."""
     G = np.ascontiguousarray(G, dtype=np.float64)
     qx = np.ascontiguousarray(qx, dtype=np.int8)
     N, D = G.shape
@@ -508,9 +510,12 @@ def lss_weight_gradient(G, qx, sx, k, budget, uniforms, rot=ROT_RIGHT):
     lo = quantize(Gw - float(s_hi) * hi.astype(np.float64), s_lo, LSS_HI_QP)
     out.update(s_hi=s_hi, s_lo=s_lo, hi=hi, lo=lo)
     comb = (LSS_LO_DIV * hi.astype(np.int64) + lo.astype(np.int64)).astype(np.int8)
+    if dw_rows is not None:
+        comb = np.ascontiguousarray(comb[:, dw_rows])
+    Dr = comb.shape[1]
     xk = np.ascontiguousarray(qx[keep])
     K = keep.size
-    T = gemm_i8(comb, 1, D, xk, C, 1, D, C, K) if K else np.zeros((D, C), dtype=np.int64)
+    T = gemm_i8(comb, 1, Dr, xk, C, 1, Dr, C, K) if K else np.zeros((Dr, C), dtype=np.int64)
     kk = 1
     if rot == ROT_RIGHT:
         T = rotate_i64(T, ROT_RIGHT, k)

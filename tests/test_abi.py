@@ -217,6 +217,69 @@ def test_bwd_weight_validation(kw, expect):
     assert B.STATUS_NAMES[bwd_w(**kw)] == expect
 
 
+def lss(**kw):
+    N, C, D = 64, 64, 96
+    args = dict(dy=FAKE, dy_dtype=B.HQ_BF16, saved_x=qt(N, C, bits=4, k=16), N=N, C=C, D=D,
+                cfg=cfg(k=16, bits=4, variant=B.HQ_VARIANT_HQ), budget=32.0, uniforms=FAKE,
+                dw=FAKE, dw_dtype=B.HQ_F32, probs=None, kept_idx=None, stats=None, ws=FAKE,
+                ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return B.hq_lss_bwd_weight(**args)
+
+
+def test_lss_workspace_bytes():
+    n = B.hq_lss_workspace_bytes(1000, 256, 512)
+    assert n >= (256 + 512) * 1008 + 1000 * (4 + 8 + 8 + 1 + 4)
+    assert B.hq_lss_workspace_bytes(-1, 8, 8) == 0
+    assert B.hq_lss_workspace_bytes((1 << 21) + 1, 8, 8) == 0
+    assert B.hq_lss_workspace_bytes(0, 8, 8) > 0
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(cfg=cfg(k=16, bits=8, variant=B.HQ_VARIANT_HQ)), "HQ_ERR_BITS"),
+    (dict(cfg=cfg(k=16, bits=4, variant=B.HQ_VARIANT_HALO2)), "HQ_ERR_MODE"),
+    (dict(cfg=cfg(k=3, bits=4, variant=B.HQ_VARIANT_HQ)), "HQ_ERR_K"),
+    (dict(dy_dtype=5), "HQ_ERR_DTYPE"),
+    (dict(dw_dtype=5), "HQ_ERR_DTYPE"),
+    (dict(C=40), "HQ_ERR_SHAPE"),                                  # 40 % 16
+    (dict(N=-1), "HQ_ERR_SHAPE"),
+    (dict(N=(1 << 21) + 1), "HQ_ERR_SHAPE"),
+    (dict(budget=float("nan")), "HQ_ERR_SHAPE"),
+    (dict(budget=float("inf")), "HQ_ERR_SHAPE"),
+    (dict(dy=None), "HQ_ERR_NULL"),
+    (dict(uniforms=None), "HQ_ERR_NULL"),
+    (dict(dw=None), "HQ_ERR_NULL"),
+    (dict(saved_x=None), "HQ_ERR_NULL"),
+    (dict(saved_x=qt(64, 64, bits=4, k=16, codes=None)), "HQ_ERR_NULL"),   # row-major codes
+    (dict(saved_x=qt(64, 64, bits=4, k=16, scale=None)), "HQ_ERR_NULL"),
+    (dict(saved_x=qt(64, 64, bits=8, k=16)), "HQ_ERR_MISMATCH"),
+    (dict(saved_x=qt(64, 64, bits=4, k=32)), "HQ_ERR_MISMATCH"),
+    (dict(saved_x=qt(64, 64, bits=4, k=16, rot=B.HQ_ROT_NONE)), "HQ_ERR_MISMATCH"),
+    (dict(saved_x=qt(32, 64, bits=4, k=16)), "HQ_ERR_MISMATCH"),
+    (dict(saved_x=qt(64, 64, bits=4, k=16, codes=FAKE_MIS)), "HQ_ERR_ALIGN"),
+    (dict(saved_x=qt(64, 64, bits=4, k=16, ld=72)), "HQ_ERR_ALIGN"),
+    (dict(saved_x=qt(64, 64, bits=4, k=16, ld=48)), "HQ_ERR_SHAPE"),
+    (dict(probs=FAKE_MIS), "HQ_ERR_ALIGN"),
+    (dict(ws=None), "HQ_ERR_WORKSPACE"),
+    (dict(ws_bytes=1000), "HQ_ERR_WORKSPACE"),
+    (dict(ws=FAKE_MIS), "HQ_ERR_ALIGN"),
+])
+def test_lss_validation(kw, expect):
+    assert B.STATUS_NAMES[lss(**kw)] == expect
+
+
+def test_lss_halo0_takes_unrotated_codes():
+    # HALO0 samples against codes of X itself; with them the call reaches the device check,
+    # which fails on a machine without a gfx950 GPU.
+    import torch
+    c = cfg(k=16, bits=4, variant=B.HQ_VARIANT_HALO0)
+    assert B.STATUS_NAMES[lss(cfg=c)] == "HQ_ERR_MISMATCH"   # these codes carry B_C
+    if torch.cuda.is_available():
+        pytest.skip("only meaningful without a GPU")
+    assert B.STATUS_NAMES[lss(cfg=c, C=40, saved_x=qt(64, 40, bits=4, k=16,
+                                                      rot=B.HQ_ROT_NONE))] == "HQ_ERR_DEVICE"
+
+
 @pytest.mark.parametrize("kw,expect", [
     (dict(k=6), "HQ_ERR_K"),
     (dict(rot=B.HQ_ROT_BOTH), "HQ_ERR_MODE"),

@@ -1,0 +1,237 @@
+"""GPU parity of LSS-MM, the sampled weight gradient of the INT4-range HQ layer (INT4 page
+§4.2, §A.2, §A.6, §B.2), through hq_lss_bwd_weight, against oracle.lss_weight_gradient.
+
+The GPU and the oracle take the same inputs: dY, the oracle's INT4 codes of X B_C and their
+step (uploaded as the saved forward tensor), the budget and the uniforms. Bars:
+  - the kept tokens: identical lists (the decisions compare the same fp32 uniforms with fp64
+    probabilities on both sides);
+  - probabilities: relative 1e-12 (both in fp64; the GPU sums the scores in a tree, the
+    oracle in index order);
+  - steps s8, s_hi, s_lo: equal (correctly rounded quotients on both sides);
+  - dW: the output bound of the dtype against the oracle's unrounded values.
+A last case runs the GPU forward first and samples from its own saved codes; there the
+uniforms are kept 1e-3 (relative) away from the oracle's probabilities, so that a code that
+differs at a rounding tie cannot flip a decision, and dW is held to the relative Frobenius
+bound of the layer outputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from hadamard_rotated_precision_amd import binding as B
+from hadamard_rotated_precision_amd import tensors as T
+from hadamard_rotated_precision_amd import workloads as WL
+from hq_testlib import OUT_REL_FRO, assert_out, check_guards, guarded_empty, rel_fro
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TORCH_OUT = {B.HQ_F32: torch.float32, B.HQ_F16: torch.float16, B.HQ_BF16: torch.bfloat16}
+
+
+def make_case(seed, N, C, D, k, dt, zero_rows=0, spread=1.0):
+    """dY with log-normal row magnitudes (spread: sigma of log|row|), X with outlier channels."""
+    rng = np.random.default_rng(seed)
+    G = rng.standard_t(3, size=(N, D)) * 1e-3 * np.exp(spread * rng.standard_normal((N, 1)))
+    if zero_rows:
+        G[rng.choice(N, zero_rows, replace=False)] = 0.0
+    X = rng.standard_normal((N, C))
+    X[:, rng.choice(C, max(1, C // 64), replace=False)] *= 30.0
+    gb = WL.to_dtype_bits(G, dt)
+    xb = WL.to_dtype_bits(X, dt)
+    u = rng.random(N).astype(np.float32)
+    return gb, O.decode(gb, dt), xb, O.decode(xb, dt), u
+
+
+def saved_codes(qx, sx, k, rot):
+    """The oracle's INT4 codes of X (B_C) as a saved forward tensor on the device."""
+    N, C = qx.shape
+    q = T.QTensor(N, C, codes=True, codes_t=False, device=DEV)
+    pad = np.zeros((N, T.pitch16(C)), dtype=np.int8)
+    pad[:, :C] = qx
+    q.codes.copy_(torch.from_numpy(pad))
+    q.scale.fill_(float(sx))
+    q.st.rows, q.st.cols, q.st.k, q.st.bits = N, C, k, 4
+    q.st.rot, q.st.format = rot, B.HQ_FMT_INT
+    return q
+
+
+def run_lss(gb, dt, q, N, C, D, k, variant, budget, u, out_dt):
+    dy = T.device_tensor_from_bits(gb, dt, DEV)
+    uni = torch.from_numpy(u).to(DEV)
+    lss = T.LssGrad(N, C, D, k, variant, device=DEV)
+    dw, raw = guarded_empty((D, C), TORCH_OUT[out_dt])
+    lss(dy, q, uni, dw, budget)
+    torch.cuda.synchronize()
+    check_guards({"dw": raw})
+    kept, s8, s_hi, s_lo = lss.read_stats()
+    probs = lss.probs.cpu().numpy()[:N]
+    idx = lss.kept_idx.cpu().numpy()[:kept]
+    return dict(kept=kept, s8=s8, s_hi=s_hi, s_lo=s_lo, probs=probs, idx=idx,
+                dw=dw.float().cpu().numpy().astype(np.float64))
+
+
+def check(got, ora, G, out_dt, what, dw_rows=None):
+    print("[lss] %s kept %d (oracle %d), s_hi %r s_lo %r" % (
+        what, got["kept"], ora["keep"].size, got["s_hi"], got["s_lo"]), flush=True)
+    np.testing.assert_array_equal(got["idx"], ora["keep"].astype(np.int32))
+    p = ora["p"]
+    np.testing.assert_allclose(got["probs"], p, rtol=1e-12, atol=0)
+    assert got["s8"] == O.absmax_scale(G, 127), (got["s8"], O.absmax_scale(G, 127))
+    assert got["s_hi"] == ora["s_hi"] and got["s_lo"] == ora["s_lo"]
+    dw = got["dw"] if dw_rows is None else got["dw"][dw_rows]
+    if not np.any(ora["dw"]):
+        assert not np.any(dw), what
+        return
+    assert_out(dw, ora["dw"], out_dt, what)
+
+
+CASES = [
+    # (N, C, D, k, variant, in dtype, out dtype, budget fraction, seed)
+    (300, 96, 200, 16, B.HQ_VARIANT_HQ, B.HQ_BF16, B.HQ_F32, 0.5, 11),
+    (1000, 256, 320, 32, B.HQ_VARIANT_HQ, B.HQ_F16, B.HQ_BF16, 0.3, 12),
+    (257, 64, 130, 16, B.HQ_VARIANT_HALO0, B.HQ_F32, B.HQ_F32, 0.5, 13),
+    (2100, 128, 72, 128, B.HQ_VARIANT_HQ, B.HQ_BF16, B.HQ_F16, 0.25, 14),
+    (33, 16, 16, 16, B.HQ_VARIANT_HQ, B.HQ_BF16, B.HQ_F32, 0.5, 15),
+]
+
+
+@pytest.mark.parametrize("N,C,D,k,variant,dt,out_dt,frac,seed", CASES)
+def test_lss_weight_gradient_matches_oracle(N, C, D, k, variant, dt, out_dt, frac, seed):
+    print("[case] lss", N, C, D, k, variant, dt, out_dt, frac, seed, flush=True)
+    gb, G, _, X, u = make_case(seed, N, C, D, k, dt, zero_rows=N // 20, spread=1.5)
+    rot = O.ROT_RIGHT if variant == B.HQ_VARIANT_HQ else O.ROT_NONE
+    qx, sx = O.quantize_tensor(X, rot, k, 4)
+    budget = frac * N
+    ora = O.lss_weight_gradient(G, qx, sx, k, budget, u, rot=rot)
+    assert (ora["p"] == 1).any() and ((ora["p"] > 0) & (ora["p"] < 1)).any()   # clamp rounds ran
+    got = run_lss(gb, dt, saved_codes(qx, sx, k, rot), N, C, D, k, variant, budget, u, out_dt)
+    check(got, ora, G, out_dt, "N%d C%d D%d k%d" % (N, C, D, k))
+
+
+def test_lss_nonzero_rows_mode_keeps_every_nonzero_token():
+    """budget >= the number of nonzero scores: every token with a nonzero score gets p = 1
+    (INT4 page §A.6: in practice rows with a nonzero norm are sampled)."""
+    N, C, D, k = 200, 64, 96, 16
+    gb, G, _, X, u = make_case(21, N, C, D, k, B.HQ_BF16, zero_rows=30)
+    qx, sx = O.quantize_tensor(X, O.ROT_RIGHT, k, 4)
+    ora = O.lss_weight_gradient(G, qx, sx, k, N, u)
+    # rows whose INT8 codes all round to zero score 0 too, beside the 30 zero rows
+    assert ora["keep"].size == np.count_nonzero(ora["scores"]) <= N - 30
+    got = run_lss(gb, B.HQ_BF16, saved_codes(qx, sx, k, O.ROT_RIGHT), N, C, D, k,
+                  B.HQ_VARIANT_HQ, N, u, B.HQ_F32)
+    check(got, ora, G, B.HQ_F32, "nonzero rows")
+    assert set(np.unique(got["probs"])) <= {0.0, 1.0}
+
+
+@pytest.mark.parametrize("budget", [0.0, -3.0])
+def test_lss_zero_budget_keeps_nothing(budget):
+    N, C, D, k = 100, 32, 48, 16
+    gb, G, _, X, u = make_case(22, N, C, D, k, B.HQ_F16)
+    qx, sx = O.quantize_tensor(X, O.ROT_RIGHT, k, 4)
+    ora = O.lss_weight_gradient(G, qx, sx, k, budget, u)
+    assert ora["keep"].size == 0
+    got = run_lss(gb, B.HQ_F16, saved_codes(qx, sx, k, O.ROT_RIGHT), N, C, D, k,
+                  B.HQ_VARIANT_HQ, budget, u, B.HQ_BF16)
+    assert got["kept"] == 0 and got["s_hi"] == 0 and got["s_lo"] == 0
+    assert not np.any(got["dw"])
+    assert not np.any(got["probs"])
+
+
+def test_lss_zero_gradient():
+    """dY = 0: every score is zero, nothing is kept, dW = 0."""
+    N, C, D, k = 64, 32, 40, 16
+    gb, G, _, X, u = make_case(23, N, C, D, k, B.HQ_BF16)
+    gb = np.zeros_like(gb)
+    qx, sx = O.quantize_tensor(X, O.ROT_RIGHT, k, 4)
+    got = run_lss(gb, B.HQ_BF16, saved_codes(qx, sx, k, O.ROT_RIGHT), N, C, D, k,
+                  B.HQ_VARIANT_HQ, N / 2, u, B.HQ_F32)
+    assert got["kept"] == 0 and got["s8"] == 0 and not np.any(got["dw"])
+
+
+def test_lss_no_tokens():
+    """N = 0: dW is written as zeros."""
+    C, D, k = 32, 48, 16
+    q = T.QTensor(0, C, codes=True, codes_t=False, device=DEV)
+    q.st.rows, q.st.cols, q.st.k, q.st.bits = 0, C, k, 4
+    q.st.rot, q.st.format = O.ROT_RIGHT, B.HQ_FMT_INT
+    lss = T.LssGrad(0, C, D, k, device=DEV)
+    dw = torch.full((D, C), 7.0, dtype=torch.float32, device=DEV)
+    dy = torch.empty(0, dtype=torch.bfloat16, device=DEV)
+    uni = torch.empty(0, dtype=torch.float32, device=DEV)
+    lss(dy, q, uni, dw, 0.0)
+    torch.cuda.synchronize()
+    assert lss.read_stats()[0] == 0
+    assert not bool(dw.any())
+
+
+def test_lss_repeated_calls_reuse_workspace():
+    """Two calls in a row on one workspace, the second with a smaller budget: the second
+    result depends only on its own inputs (every stage writes what it reads)."""
+    N, C, D, k = 400, 64, 128, 16
+    gb, G, _, X, u = make_case(24, N, C, D, k, B.HQ_BF16, spread=1.0)
+    qx, sx = O.quantize_tensor(X, O.ROT_RIGHT, k, 4)
+    q = saved_codes(qx, sx, k, O.ROT_RIGHT)
+    dy = T.device_tensor_from_bits(gb, B.HQ_BF16, DEV)
+    uni = torch.from_numpy(u).to(DEV)
+    lss = T.LssGrad(N, C, D, k, device=DEV)
+    for budget in (0.8 * N, 0.2 * N):
+        dw = torch.empty((D, C), dtype=torch.float32, device=DEV)
+        lss(dy, q, uni, dw, budget)
+        torch.cuda.synchronize()
+        ora = O.lss_weight_gradient(G, qx, sx, k, budget, u)
+        kept = lss.read_stats()[0]
+        np.testing.assert_array_equal(lss.kept_idx.cpu().numpy()[:kept], ora["keep"])
+        assert_out(dw.cpu().numpy().astype(np.float64), ora["dw"], B.HQ_F32,
+                   "budget %.0f" % budget)
+
+
+def test_lss_fullsize_bert_large_ffn():
+    """The BERT-large FFN-up shapes of the INT4 learned-step workload (4096 tokens, 1024 in,
+    4096 out, k = 16, fp16): the whole sample and steps, dW checked on 256 sampled rows."""
+    cfg = WL.config(3)
+    N, C, D, k = cfg["N"], cfg["C"], cfg["D"], cfg["k"]
+    dt = cfg["in_dtype"]
+    inp = WL.make_inputs(cfg)
+    G = O.decode(inp["dy"], dt)
+    X = O.decode(inp["x"], dt)
+    u = np.random.default_rng(cfg["seed"] + 7).random(N).astype(np.float32)
+    qx, sx = O.quantize_tensor(X, O.ROT_RIGHT, k, 4, O.STEP, inp["steps"]["x"])
+    rows = np.sort(np.random.default_rng(5).choice(D, 256, replace=False))
+    ora = O.lss_weight_gradient(G, qx, sx, k, N / 2, u, dw_rows=rows)
+    got = run_lss(inp["dy"], dt, saved_codes(qx, sx, k, O.ROT_RIGHT), N, C, D, k,
+                  B.HQ_VARIANT_HQ, N / 2, u, cfg["out_dtype"])
+    check(got, ora, G, cfg["out_dtype"], "bert-large ffn", dw_rows=rows)
+
+
+def test_lss_after_gpu_forward():
+    """The forward's own saved INT4 codes feed the sample (the path as a layer runs it)."""
+    N, C, D, k = 512, 256, 192, 16
+    dt = B.HQ_BF16
+    gb, G, xb, X, _ = make_case(31, N, C, D, k, dt, spread=1.0)
+    rng = np.random.default_rng(32)
+    W = rng.standard_normal((D, C)) * 0.02
+    wb = WL.to_dtype_bits(W, dt)
+    qx, sx = O.quantize_tensor(X, O.ROT_RIGHT, k, 4)
+    budget = N / 2
+    ora = O.lss_weight_gradient(G, qx, sx, k, budget, np.zeros(N, dtype=np.float32))
+    p = ora["p"]
+    u = rng.random(N).astype(np.float32)
+    near = np.abs(u.astype(np.float64) - p) < 1e-3 * np.maximum(p, 1e-30)
+    u[near] = np.where(p[near] > 0.5, p[near] * 0.98, p[near] * 1.02).astype(np.float32)
+    ora = O.lss_weight_gradient(G, qx, sx, k, budget, u)
+    layer = T.Layer(N, C, D, k, 4, B.HQ_SCALE_ABSMAX, B.HQ_VARIANT_HQ, device=DEV)
+    x = T.device_tensor_from_bits(xb, dt, DEV)
+    w = T.device_tensor_from_bits(wb, dt, DEV)
+    y = torch.empty((N, D), dtype=torch.bfloat16, device=DEV)
+    layer.fwd(x, w, y)
+    dy = T.device_tensor_from_bits(gb, dt, DEV)
+    lss = T.LssGrad(N, C, D, k, device=DEV)
+    dw = torch.empty((D, C), dtype=torch.float32, device=DEV)
+    lss(dy, layer.qx, torch.from_numpy(u).to(DEV), dw, budget)
+    torch.cuda.synchronize()
+    kept = lss.read_stats()[0]
+    np.testing.assert_array_equal(lss.kept_idx.cpu().numpy()[:kept], ora["keep"])
+    err = rel_fro(dw.cpu().numpy(), ora["dw"])
+    print("[lss] after forward: kept %d, dW rel fro %.3g" % (kept, err), flush=True)
+    assert err <= OUT_REL_FRO
