@@ -303,6 +303,75 @@ def bmm_step(steps=20):
                               "unit": "TOP/s", "frac": round(tops / PEAK_INT8_TOPS, 4)}}
 
 
+def lss_step(cfg_id, reps=20):
+    """LSS-MM (INT4 page §4.2, §A.3, §A.6) on a workload's shapes, distributions and k as an
+    INT4 HQ layer (X codes from an absmax INT4 HQ forward): the sampled weight gradient at
+    budget N/2 next to the unsampled INT4 weight gradient of the same layer (event medians),
+    with each stage's launch time (kernel-stamped events over `reps` calls), its algorithmic
+    bytes and GB/s, and the GEMM's ops over the kept tokens."""
+    import torch
+    from hadamard_rotated_precision_amd import binding as B
+    from hadamard_rotated_precision_amd import tensors as T
+    from hadamard_rotated_precision_amd import workloads as WL
+    cfg = WL.config(cfg_id)
+    N, C, D, k = cfg["N"], cfg["C"], cfg["D"], cfg["k"]
+    inputs = WL.make_inputs(cfg)
+    dt = cfg["in_dtype"]
+    x = T.device_tensor_from_bits(inputs["x"], dt)
+    w = T.device_tensor_from_bits(inputs["w"], dt)
+    dy = T.device_tensor_from_bits(inputs["dy"], dt)
+    layer = T.Layer(N, C, D, k, 4, WL.ABSMAX, WL.HQ)
+    odt = T.TORCH_DT[cfg["out_dtype"]]
+    y = torch.empty((N, D), dtype=odt, device="cuda")
+    dx = torch.empty((N, C), dtype=odt, device="cuda")
+    dw_full = torch.empty((D, C), dtype=odt, device="cuda")
+    dw = torch.empty((D, C), dtype=odt, device="cuda")
+    layer.fwd(x, w, y)
+    layer.bwd_input(dy, dx)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(cfg["seed"] + 7)
+    u = torch.rand(N, generator=gen, device="cuda", dtype=torch.float32)
+    lss = T.LssGrad(N, C, D, k)
+    budget = N / 2
+    full_ms = event_median_ms(lambda: layer.bwd_weight(dw_full))
+    lss_ms = event_median_ms(lambda: lss(dy, layer.qx, u, dw, budget))
+    B.check(B.hq_profile_start((1 << B.HQ_KIND_COUNT) - 1), "profile")
+    for _ in range(reps):
+        lss(dy, layer.qx, u, dw, budget)
+    torch.cuda.synchronize()
+    B.profile_stop_dict()
+    recs = B.profile_records()
+    kept = lss.read_stats()[0]
+    kpad = (kept + 15) // 16 * 16
+    eb = 4 if dt == WL.F32 else 2
+    names = ["rowmax", "score", "prob", "pack", "gemm"]
+    nbytes = {"rowmax": N * D * eb + N * 4,
+              "score": N * D * eb + N * C + N * 8,
+              "prob": N * (8 + 4 + 4 + 8 + 1) + kept * 4,
+              "pack": kept * (D * eb + C + 4 + 8) + (D + C) * kpad,
+              "gemm": (D + C) * kpad + D * C * eb}
+    stages = {}
+    per = len(recs) // reps   # four sampling stages, then the GEMM's launch(es)
+    if per >= len(names) and len(recs) == per * reps:
+        for i, nm in enumerate(names):
+            idx = [i] if nm != "gemm" else list(range(len(names) - 1, per))
+            ms = sorted(sum(recs[j * per + q][1] for q in idx) for j in range(reps))[reps // 2]
+            st = {"us": round(ms * 1e3, 2), "bytes": nbytes[nm],
+                  "gbps": round(nbytes[nm] / (ms * 1e-3) / 1e9, 1)}
+            if nm == "gemm":
+                st["launches"] = len(idx)
+            if nm == "gemm":
+                tops = 2.0 * C * D * kept / (ms * 1e-3) / 1e12
+                st["tops"] = round(tops, 1)
+                st["frac_int8_peak"] = round(tops / PEAK_INT8_TOPS, 4)
+            stages[nm] = st
+    return {"workload": "lss_int4_%dx%dx%d_k%d_from_%s" % (N, C, D, k, cfg["name"]), "budget": budget,
+            "kept": kept, "lss_ms": round(lss_ms, 4), "unsampled_int4_dw_ms": round(full_ms, 4),
+            "speedup_vs_unsampled": round(full_ms / lss_ms, 3), "stages_median": stages,
+            "timing": "event median of 20 calls after 5 warm-ups for both; stages: median of "
+                      "%d kernel-stamped launches each" % reps}
+
+
 def qparam_stats(reps=10):
     """Quantizer-parameter statistics (INT4 page §A.3-§A.5) on X of the 8192 x 13824 x 5120
     layer (bf16, k = 128): the LSQ step gradient (reads X and a gradient of the same shape,
@@ -382,6 +451,8 @@ def main():
                     help="skip the quantizer-parameter statistics")
     ap.add_argument("--no-bmm", action="store_true",
                     help="skip the batched (attention) product")
+    ap.add_argument("--no-lss", action="store_true",
+                    help="skip the LSS-MM (sampled weight gradient) measurement")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the FP8 (E4M3) step of the same layer")
     ap.add_argument("--no-fwht", action="store_true",
@@ -643,6 +714,13 @@ def main():
             result["qparams"] = qparam_stats()
         except Exception as exc:  # report, do not fail the benchmark line
             result["qparams"] = {"error": str(exc)}
+    if not args.no_lss:
+        print("[bench] LSS-MM weight gradient", file=sys.stderr, flush=True)
+        for cid in (3, 4, 5):
+            try:
+                result.setdefault("lss_step", []).append(lss_step(cid))
+            except Exception as exc:  # report, do not fail the benchmark line
+                result.setdefault("lss_step", []).append({"config": cid, "error": str(exc)})
     if not args.no_bmm:
         print("[bench] batched attention product", file=sys.stderr, flush=True)
         try:

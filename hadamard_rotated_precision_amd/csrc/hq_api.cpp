@@ -893,6 +893,7 @@ struct LssWs {
   double* probs;
   uint8_t* fixed;
   int32_t* kept_idx;
+  double* kept_p;
   int8_t* ct;
   int8_t* xt;
   int64_t ldk;
@@ -913,6 +914,7 @@ struct LssWs {
     probs = reinterpret_cast<double*>(take(N * sizeof(double)));
     fixed = reinterpret_cast<uint8_t*>(take(N));
     kept_idx = reinterpret_cast<int32_t*>(take(N * sizeof(int32_t)));
+    kept_p = reinterpret_cast<double*>(take(N * sizeof(double)));
     ct = reinterpret_cast<int8_t*>(take(D * ldk));
     xt = reinterpret_cast<int8_t*>(take(C * ldk));
     bytes = off;
@@ -978,6 +980,7 @@ hq_status hq_lss_bwd_weight(const void* dy, int32_t dy_dtype, const hq_qtensor* 
   p.probs = probs ? probs : w.probs;
   p.fixed = w.fixed;
   p.kept_idx = kept_idx ? kept_idx : w.kept_idx;
+  p.kept_p = w.kept_p;
   p.stats = stats ? stats : w.stats;
   p.ct = w.ct;
   p.xt = w.xt;

@@ -147,6 +147,7 @@ struct LssPass {
   double* probs = nullptr;
   uint8_t* fixed = nullptr;
   int32_t* kept_idx = nullptr;
+  double* kept_p = nullptr;     // probability of each kept token, in kept order
   hq_lss_stats* stats = nullptr;
   int8_t* ct = nullptr;
   int8_t* xt = nullptr;

@@ -294,9 +294,10 @@ hq_status hq_select_hadamard_k(const void *x, const void *w, int32_t dtype, int6
  * fused high/low quantization, zero padding of K after sampling; §B.2 the unbiased estimator):
  *   1. q8 = Q(dY) on the INT8 grid with the tensor-wise absmax step s8; the score of token i is
  *      l_i = ||q8_i|| * ||qX_i||, qX the forward's INT4 codes of X B_C (saved_x->codes);
- *   2. p = clamp-and-rescale probabilities with sum(p) = budget where possible: p_i =
- *      budget' l_i / sum_free(l) over the tokens not yet clamped, those above 1 set to 1 and
- *      the rest rescaled to what the budget leaves, until none exceeds 1 (zero scores: p = 0;
+ *   2. p = clamp-and-rescale probabilities with sum(p) = budget where possible: each round
+ *      sets p_i = (budget' / sum_free(l)) l_i for the tokens not yet clamped (budget' = budget
+ *      minus the clamped count), sets those above 1 to 1, and repeats until a round clamps
+ *      none (zero scores: p = 0;
  *      budget >= the number of nonzero scores keeps every token with a nonzero score, the
  *      page's practical choice); sums in fp64, in a fixed order;
  *   3. token i is kept iff uniforms[i] < p_i (uniforms: N device floats in [0, 1), drawn by the
@@ -306,9 +307,9 @@ hq_status hq_select_hadamard_k(const void *x, const void *w, int32_t dtype, int6
  *      14 hi + lo in [-105, 105];
  *   5. dW = ((14 hi + lo)^T qX_kept) [B_C] s_lo sX / k, one integer GEMM over the K' kept
  *      tokens (the page's two INT4 products, hi and lo, summed exactly in int32).
- * The codes of steps 1 and 4 take the exact rule (round-to-nearest-even of the quotient, ties
- * decided exactly; fp32 or fp64 products with an exact fallback near ties); steps fp32,
- * s_hi and s8 the correctly rounded quotients.
+ * The codes of steps 1 and 4 follow the exact rule (round-to-nearest-even of the quotient,
+ * ties decided exactly: fp32 products, with an fp64 fallback near ties). The steps are fp32:
+ * s8 and s_hi are the correctly rounded quotients, s_lo = fp32(s_hi / 14).
  * cfg: format INT, bits 4, variant HQ (B_C of block size k) or HALO0 (no rotation); saved_x
  * as hq_linear_fwd writes it (row-major codes required, N x C). dy: N x D in dy_dtype.
  * Output dw: D x C in dw_dtype. Optional device outputs (NULL: kept in the workspace):

@@ -451,7 +451,7 @@ LSS_LO_DIV = 14        # s_lo = s_hi / 14: the smallest step whose [-7, 7] cover
 def lss_probabilities(scores, budget):
     """Leverage-score sampling probabilities ("Training Transformers with 4-bit Integers",
     §4.2 probabilities in proportion to leverage scores, §A.2 the clamp-and-rescale
-    procedure): p = budget * l / sum(l); while some p exceed 1, those are set to 1 and the
+    procedure): p = (budget / sum(l)) l; while some p exceed 1, those are set to 1 and the
     others rescaled to fill what remains of the budget. Zero scores get p = 0; if the budget
     covers every nonzero score they all get 1. Double precision, sums in index order."""
     l = np.asarray(scores, dtype=np.float64)
@@ -466,7 +466,7 @@ def lss_probabilities(scores, budget):
         tot = 0.0
         for v in l[free]:                        # the sum in index order
             tot += float(v)
-        p[free] = left * l[free] / tot
+        p[free] = (left / tot) * l[free]         # one scale factor per round
         over = free & (p > 1.0)
         if not over.any():
             break

@@ -93,6 +93,8 @@ CASES = [
     (257, 64, 130, 16, B.HQ_VARIANT_HALO0, B.HQ_F32, B.HQ_F32, 0.5, 13),
     (2100, 128, 72, 128, B.HQ_VARIANT_HQ, B.HQ_BF16, B.HQ_F16, 0.25, 14),
     (33, 16, 16, 16, B.HQ_VARIANT_HQ, B.HQ_BF16, B.HQ_F32, 0.5, 15),
+    (20000, 32, 64, 16, B.HQ_VARIANT_HQ, B.HQ_BF16, B.HQ_F32, 0.2, 16),   # > 16384 tokens
+    (9000, 48, 40, 16, B.HQ_VARIANT_HQ, B.HQ_F16, B.HQ_F32, 0.15, 17),
 ]
 
 
