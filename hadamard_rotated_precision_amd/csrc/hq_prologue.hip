@@ -18,7 +18,7 @@
 //   left_mma_kernel  : along the token axis (dY under HALO-2), 256 x 64 tiles staged raw in LDS,
 //                      H fragments as the A operand.
 //   both_mma_kernel  : X under HALO-2, 256 x 256 tiles: the row phase on the matrix cores, the
-//                      half tile staged column-major, the token phase in fp64;
+//                      half tile staged column-major, the token phase in TokenT (fp32);
 //                      both_pipe_kernel is the same with the next item's raw rows loaded into
 //                      LDS during the current item's token phase (several items per workgroup).
 // VALU kernels (every other shape: fp32 inputs, k < 16, ragged tiles, unaligned pitches):
@@ -1178,6 +1178,17 @@ __device__ inline void quad_stage_f64(double (&u)[N], int lane) {
   }
 }
 
+// The token-axis phase of the two-sided transform (B (X B)) sums the fp32 values of X B in
+// fp32 butterflies: log2 k rounded additions per value, within the code and output tolerances
+// (a code may move by one step where B X B lies within that rounding of a midpoint). With
+// TokenT = double the sums are exact and B X B is rounded once.
+using TokenT = float;
+
+template <int M, int N>
+__device__ inline void quad_stage_tok(float (&u)[N], int lane) { quad_stage<N>(u, lane, M); }
+template <int M, int N>
+__device__ inline void quad_stage_tok(double (&u)[N], int lane) { quad_stage_f64<M, N>(u, lane); }
+
 // Work items of both_kernel: 128-column halves of 256 x 256 tiles. The two halves of a tile are
 // 8 items apart, so that they run on one XCD and the second read of the tile hits its L2.
 __host__ __device__ inline int64_t both_items(int64_t rows, int64_t cols) {
@@ -1188,9 +1199,8 @@ __host__ __device__ inline int64_t both_items(int64_t rows, int64_t cols) {
 // with k = 256 both halves of a row are needed, otherwise only the item's own half is read) give
 // the row-major codes of X B; the item's half of X B is then staged through LDS (16-column
 // blocks XOR-swizzled by row / 64 and the 64-column half, so both the row-wise 16-byte writes
-// and the column reads are conflict-free) and rotated along the
-// token axis in fp64, where sums of fp32 values are exact, so B X B is rounded to fp32 once, as
-// the exact sum would be, before its scale and codes are taken.
+// and the column reads are conflict-free) and rotated along the token axis in TokenT before
+// its scale and codes are taken.
 template <class In, int K, int OP>
 __global__ __launch_bounds__(BT_THREADS) void both_kernel(ProArgs a) {
   __shared__ __attribute__((aligned(16))) float half[BT * BT_PITCH];
@@ -1277,7 +1287,7 @@ __global__ __launch_bounds__(BT_THREADS) void both_kernel(ProArgs a) {
         }
       }
     }
-    // ---- column phase: the token-axis rotation of this half, in fp64
+    // ---- column phase: the token-axis rotation of this half, in TokenT
     __syncthreads();
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) {
@@ -1288,13 +1298,13 @@ __global__ __launch_bounds__(BT_THREADS) void both_kernel(ProArgs a) {
             make_float4(w[16 * jb + 4 * q], w[16 * jb + 4 * q + 1], w[16 * jb + 4 * q + 2], w[16 * jb + 4 * q + 3]);
     }
     __syncthreads();
-    double u[64];
+    TokenT u[64];
     const float* col = &half[64 * pp * BT_PITCH + (cp ^ (16 * pp) ^ (32 * (cp >> 6)))];
 #pragma unroll
-    for (int i = 0; i < 64; ++i) u[i] = static_cast<double>(col[i * BT_PITCH]);
+    for (int i = 0; i < 64; ++i) u[i] = static_cast<TokenT>(col[i * BT_PITCH]);
     fwht_from<1, K, 64>(u);
-    if constexpr (K > 64) quad_stage_f64<1, 64>(u, lane);
-    if constexpr (K > 128) quad_stage_f64<2, 64>(u, lane);
+    if constexpr (K > 64) quad_stage_tok<1, 64>(u, lane);
+    if constexpr (K > 128) quad_stage_tok<2, 64>(u, lane);
     const int64_t gcol = col0 + BT_HALF * h + cp;
     if constexpr (OP == OP_ABSMAX) {
 #pragma unroll
@@ -1338,7 +1348,7 @@ __global__ __launch_bounds__(BT_THREADS) void both_kernel(ProArgs a) {
 // [128 columns][256 rows] fp32, 16-byte row chunk c4 of column c stored at chunk
 // c4 ^ (c % 16) ^ 4((c4 / 16) % 4), so the writes (16 columns per 16 lanes) and the column
 // phase's reads (4 columns x 4 row quarters per 16 lanes) are conflict-free. Column phase as
-// both_kernel: lane (column cp, quarter pp) rotates rows 64pp + [0, 64) in fp64.
+// both_kernel: lane (column cp, quarter pp) rotates rows 64pp + [0, 64) in TokenT.
 constexpr int BM_THREADS = 512;
 
 __host__ __device__ inline bool both_mma_ok(int64_t rows, int64_t cols, bool vec, int in_bytes,
@@ -1352,7 +1362,7 @@ __device__ inline int bm_chunk(int c, int c4) { return c4 ^ (c & 15) ^ (4 * ((c4
 // PIPE (a workgroup has several items): the item's raw 16-bit rows (all 256 columns for k = 256,
 // else the item's 128) are brought into the half-tile buffer by direct-to-LDS buffer loads,
 // issued as soon as the previous item's column phase has read its values out of LDS, so they
-// land while that item's fp64 rotation runs. Rows of RAWB bytes, 16-byte chunk c of row r at
+// land while that item's token-axis rotation runs. Rows of RAWB bytes, 16-byte chunk c of row r at
 // c ^ (r % 16): the fragment reads of 16 consecutive rows meet distinct bank groups. Each wave
 // reads its A fragments from there, and after a barrier the buffer takes the fp32 half tile.
 template <class In, int K, int OP, bool PIPE>
@@ -1489,8 +1499,8 @@ __device__ inline void both_mma_body(const ProArgs& a) {
         }
       }
       __syncthreads();
-      // ---- column phase: the token-axis rotation of this half, in fp64
-      double u[64];
+      // ---- column phase: the token-axis rotation of this half, in TokenT
+      TokenT u[64];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float4 f = *reinterpret_cast<const float4*>(&half[cp * BT + 4 * bm_chunk(cp, 16 * pp + i)]);
@@ -1504,8 +1514,8 @@ __device__ inline void both_mma_body(const ProArgs& a) {
         if (it + gridDim.x < items) issue_raw(it + gridDim.x);
       }
       fwht_from<1, K, 64>(u);
-      if constexpr (K > 64) quad_stage_f64<1, 64>(u, lane);
-      if constexpr (K > 128) quad_stage_f64<2, 64>(u, lane);
+      if constexpr (K > 64) quad_stage_tok<1, 64>(u, lane);
+      if constexpr (K > 128) quad_stage_tok<2, 64>(u, lane);
       const int64_t gcol = col0 + BT_HALF * h + cp;
       if constexpr (OP == OP_ABSMAX) {
 #pragma unroll
@@ -1641,7 +1651,7 @@ struct BothItem {
       }
     }
     __syncthreads();
-    double u[64];
+    TokenT u[64];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float4 f = *reinterpret_cast<const float4*>(&half[cp * BT + 4 * bm_chunk(cp, 16 * pp + i)]);
@@ -1651,8 +1661,8 @@ struct BothItem {
       u[4 * i + 3] = f.w;
     }
     fwht_from<1, K, 64>(u);
-    if constexpr (K > 64) quad_stage_f64<1, 64>(u, lane);
-    if constexpr (K > 128) quad_stage_f64<2, 64>(u, lane);
+    if constexpr (K > 64) quad_stage_tok<1, 64>(u, lane);
+    if constexpr (K > 128) quad_stage_tok<2, 64>(u, lane);
 #pragma unroll
     for (int i = 0; i < 64; ++i) {
       v2[i] = static_cast<float>(u[i]);

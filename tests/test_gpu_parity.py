@@ -291,7 +291,7 @@ def test_rotate_quantize_parity(rot, k, rows, cols, bits, mode, dt):
 @pytest.mark.parametrize("k,rows,cols", [(256, 1024, 8448), (128, 2048, 4352)])
 def test_rotate_quantize_both_pipelined(k, rows, cols):
     """X B and B X B with more items than workgroups (264 and 272 half tiles on 256): the
-    next item's raw rows load into LDS during the current item's fp64 column phase."""
+    next item's raw rows load into LDS during the current item's token-axis phase."""
     banner("rq-both-pipe", k, rows, cols)
     rng = np.random.default_rng(rows + cols + k)
     V = rng.standard_normal((rows, cols))
