@@ -18,6 +18,7 @@
 
 #include "hq_device.hpp"
 #include "hq_internal.hpp"
+#include "hq_launch.hpp"
 
 namespace hq {
 namespace {

@@ -19,6 +19,7 @@
 
 #include "hq_device.hpp"
 #include "hq_internal.hpp"
+#include "hq_launch.hpp"
 
 namespace hq {
 

@@ -34,7 +34,8 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libhq_oracle.so")
+# HQ_ORACLE_LIB names another build of the same source (the sanitizer test's)
+LIB_PATH = os.environ.get("HQ_ORACLE_LIB") or os.path.join(HERE, "libhq_oracle.so")
 
 F32, F16, BF16 = 0, 1, 2
 ROT_NONE, ROT_RIGHT, ROT_LEFT, ROT_BOTH = 0, 1, 2, 3
