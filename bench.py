@@ -176,7 +176,8 @@ def fwht_bandwidth(reps=20, rows=8192, cols=13824, ks=(16, 32, 64, 128, 256)):
                 gbs = 4.0 * rows * cols / (us * 1e-6) / 1e9
                 row[pname] = {"us": round(us, 2), "gbps": round(gbs, 1),
                               "pct_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 1)}
-            auto_matrix = k >= 256 if rot == B.HQ_ROT_RIGHT else k not in (32, 64)
+            # hq_fwht's HQ_FWHT_AUTO choice, as its header states it (context for the reader)
+            auto_matrix = rot == B.HQ_ROT_LEFT and k not in (32, 64)
             row["auto"] = "matrix" if auto_matrix else "butterfly"
             res[name]["k%d" % k] = row
     return res

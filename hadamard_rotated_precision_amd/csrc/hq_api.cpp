@@ -667,7 +667,7 @@ hq::StatPass stat_pass_for(const void* src, const void* grad, int32_t dtype, int
   p.mode = mode;
   p.f8 = is_f8(cfg);
   p.qp = qmax(cfg);
-  p.partials = reinterpret_cast<double*>(w.part[0]);   // part[0..1]: kStatMaxParts doubles
+  p.partials = reinterpret_cast<double*>(w.part[0]);   // part[0..3]: kStatMaxParts doubles
   return p;
 }
 }  // namespace
@@ -729,8 +729,11 @@ hq_status hq_select_hadamard_k(const void* x, const void* w, int32_t dtype, int6
   HQ_CHECK(device_ok());
   hipStream_t st = static_cast<hipStream_t>(stream);
   Ws wsp(ws);
-  double* res = reinterpret_cast<double*>(wsp.part[2]);   // 2 doubles per candidate
-  float* sc = wsp.part[3];                                // the two absmax scales
+  // results in the grid-barrier words (unused by these passes; the partials take part[0..3])
+  static_assert(2 * HQ_MAX_K_CANDIDATES * sizeof(double) + 2 * sizeof(float) + kAlign <= kBarBytes,
+                "selection results fit the barrier words");
+  double* res = reinterpret_cast<double*>(wsp.bar);                              // 2 per candidate
+  float* sc = reinterpret_cast<float*>(reinterpret_cast<char*>(wsp.bar) + kAlign);   // 2 scales
   hq_config c = *cfg;
   for (int32_t i = 0; i < n_candidates; ++i) {
     c.k = candidates[i];
@@ -790,11 +793,12 @@ hq_status hq_fwht_path(const void* src, int32_t src_dtype, void* dst, int32_t ds
   if (rows * cols == 0) return HQ_OK;
   HQ_CHECK(device_ok());
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // AUTO follows the measured 8192 x 13824 bf16 transforms: the butterflies wherever they are
-  // within 5 % of the matrix cores (RIGHT up to k = 128, LEFT at k = 32 and 64), the matrix
-  // cores otherwise (RIGHT k = 256: 8 % faster; LEFT k = 16, 128, 256: 23-44 % faster)
+  // AUTO follows the measured bf16 transforms (2048 x 4096 up to 8192 x 13824): the
+  // butterflies wherever they are within 5 % of the matrix cores (RIGHT at every k, with DPP
+  // lane exchanges 1-17 % faster; LEFT at k = 32 and 64), the matrix cores otherwise (LEFT at
+  // k = 16, 128, 256: 13-40 % faster)
   const bool auto_left_mma = k != 32 && k != 64;
-  const bool auto_right_mma = k >= 256;
+  const bool auto_right_mma = false;
   const bool use_left_mma =
       left_mma && (path == HQ_FWHT_MATRIX || (path == HQ_FWHT_AUTO && auto_left_mma));
   const bool use_right_mma =

@@ -176,15 +176,43 @@ __device__ inline float xor_lane(float x, int m) {
   return __shfl_xor(x, m, 64);
 }
 
-// One butterfly stage across lanes: lanes l and l^m hold the same positions of the two
-// halves; the lane with the bit clear keeps a+b, the other keeps a-b.
-template <int N>
-__device__ inline void fwht_xlane(float (&v)[N], int lane, int m) {
-  const bool upper = (lane & m) != 0;
+// One butterfly stage across lanes: lanes l and l^M hold the same positions of the two
+// halves; the lane with the bit clear keeps a+b, the other keeps a-b (as fma(v, -1, p): the
+// same single rounding). Strides inside a 16-lane row move through DPP on the VALU (quad
+// permutes for 1 and 2; for 4 a row shift left into banks 0, 2 and right into banks 1, 3; for
+// 8 a row rotate), wider ones through the LDS permute.
+template <int M, int N>
+__device__ inline void fwht_xlane_c(float (&v)[N], int lane) {
+  const float sgn = (lane & M) ? -1.0f : 1.0f;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    float p = xor_lane(v[i], m);
-    v[i] = upper ? (p - v[i]) : (v[i] + p);
+    const int x = __float_as_int(v[i]);
+    int p;
+    if constexpr (M == 1) {
+      p = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);            // quad_perm 1,0,3,2
+    } else if constexpr (M == 2) {
+      p = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);            // quad_perm 2,3,0,1
+    } else if constexpr (M == 4) {
+      p = __builtin_amdgcn_mov_dpp(x, 0x104, 0xF, 0x5, false);           // row_shl:4 -> l + 4
+      p = __builtin_amdgcn_update_dpp(p, x, 0x114, 0xF, 0xA, false);     // row_shr:4 -> l - 4
+    } else if constexpr (M == 8) {
+      p = __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);           // row_ror:8 -> l ^ 8
+    } else {
+      p = __shfl_xor(x, M, 64);
+    }
+    v[i] = __builtin_fmaf(v[i], sgn, __int_as_float(p));
+  }
+}
+
+template <int N>
+__device__ inline void fwht_xlane(float (&v)[N], int lane, int m) {
+  switch (m) {   // m is a constant after unrolling: one case survives
+    case 1: fwht_xlane_c<1, N>(v, lane); break;
+    case 2: fwht_xlane_c<2, N>(v, lane); break;
+    case 4: fwht_xlane_c<4, N>(v, lane); break;
+    case 8: fwht_xlane_c<8, N>(v, lane); break;
+    case 16: fwht_xlane_c<16, N>(v, lane); break;
+    default: fwht_xlane_c<32, N>(v, lane); break;
   }
 }
 

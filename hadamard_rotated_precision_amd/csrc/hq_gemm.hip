@@ -135,22 +135,28 @@ __device__ inline void rows_fwht_inlane(V (&v)[4][NB]) {
   }
 }
 
-// Row stride 4 <- lane bit 5: the pair lives in lanes l and l^32.
+// Row stride 4 <- lane bit 5: the pair lives in lanes l and l^32. One row block (the stage
+// pairs values within a block, so the row-major epilogue applies it block by block, which
+// keeps the swap results of one block, not of all four, in registers at a time).
 template <int NB, class V>
-__device__ inline void rows_fwht_lanehalf(V (&v)[4][NB], int lane) {
+__device__ inline void rows_fwht_lanehalf_block(V (&v)[NB], int lane) {
   const float sgn = (lane & 32) ? -1.0f : 1.0f;
 #pragma unroll
-  for (int bi = 0; bi < 4; ++bi)
+  for (int bj = 0; bj < NB; ++bj)
 #pragma unroll
-    for (int bj = 0; bj < NB; ++bj)
+    for (int r = 0; r < 16; ++r) {
+      const unsigned x = __float_as_uint(v[bj][r]);
+      // after the swap: .x = value of the lower lane of the pair, .y = of the upper lane
+      auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+      const float lo = __uint_as_float(p[0]), hi = __uint_as_float(p[1]);
+      v[bj][r] = __builtin_fmaf(hi, sgn, lo);   // lower lane: lo+hi, upper: lo-hi
+    }
+}
+
+template <int NB, class V>
+__device__ inline void rows_fwht_lanehalf(V (&v)[4][NB], int lane) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const unsigned x = __float_as_uint(v[bi][bj][r]);
-        // after the swap: .x = value of the lower lane of the pair, .y = of the upper lane
-        auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-        const float lo = __uint_as_float(p[0]), hi = __uint_as_float(p[1]);
-        v[bi][bj][r] = __builtin_fmaf(hi, sgn, lo);   // lower lane: lo+hi, upper: lo-hi
-      }
+  for (int bi = 0; bi < 4; ++bi) rows_fwht_lanehalf_block<NB>(v[bi], lane);
 }
 
 // Butterfly stages over lanes l ^ m (m = 1, 2, 4) for N values.
@@ -447,7 +453,8 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs 
       }
     if constexpr (KM > 1) {
       rows_fwht_inlane<KM, NB>(fa);
-      if constexpr (KM > 4) rows_fwht_lanehalf<NB>(fa, lane);
+      // the row-major rounds apply the lane-half stage to each row block as they reach it
+      if constexpr (KM > 4 && TRANS) rows_fwht_lanehalf<NB>(fa, lane);
     }
     // (2) two rounds through LDS, each holding 64 rows of both wave rows: rows 64 cc + [0, 64)
     // of wave row 0 in stage 0, the same rows of wave row 1 (tile rows + 128) in stage 1.
@@ -565,6 +572,7 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs 
       };
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
+        if constexpr (KM > 4) rows_fwht_lanehalf_block<NB>(fa[cc], lane);
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < NB; ++j) {

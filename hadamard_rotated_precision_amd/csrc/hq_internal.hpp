@@ -107,8 +107,8 @@ hipError_t rows_pass(const RowPass& p, hipStream_t st);
 // Statistics of a right-rotated tensor (hq_rotate.hip, stat_kernel): mode is a StatMode
 // (0 sum |v|, 1 sum (v - s q)^2, 2 LSQ step gradient, 3 max |v|); the reduced value goes to
 // out (device double, or nullptr), and finish 1 / 2 also writes the absmax scale / cold-start
-// step to fout. partials: kStatMaxParts doubles of workspace.
-constexpr int kStatMaxParts = 1024;
+// step to fout. partials: kStatMaxParts doubles of workspace (the 16 KiB of absmax partials).
+constexpr int kStatMaxParts = 2048;
 constexpr int STAT_MODE_ABS_MAX = 3;
 struct StatPass {
   const void* src = nullptr;

@@ -114,32 +114,39 @@ __global__ __launch_bounds__(kThreads) void stat_kernel(StatArgs a) {
   const int64_t items = a.rows * nseg;
   const int64_t iters = (items + ngroups - 1) / ngroups;
   float s = 0.0f, r = 0.0f;
+  double rd = 0.0;
   if constexpr (MODE == STAT_QERR || MODE == STAT_LSQ) {
     s = *a.scale;
     r = (s > 0.0f) ? 1.0f / s : 0.0f;
+    rd = (s > 0.0f) ? 1.0 / static_cast<double>(s) : 0.0;
   }
+  constexpr bool G = MODE == STAT_LSQ;
   double acc = 0.0;
-  for (int64_t it = 0; it < iters; ++it) {
-    const int64_t item = group + it * ngroups;
-    const bool live = item < items;
-    const int64_t row = live ? item / nseg : 0;
-    const int64_t c0 = live ? (item % nseg) * 256 + 16 * g : a.cols;
+  // The segments of this group's iterations, loaded two ahead of their use into alternating
+  // register sets: a segment past the end loads the last one again and is skipped.
+  auto fetch = [&](int64_t it, float (&v)[16], float (&gv)[16]) {
+    int64_t item = group + it * ngroups;
+    if (item >= items) item = items - 1;
+    const int64_t row = item / nseg;
+    const int64_t c0 = (item % nseg) * 256 + 16 * g;
     const bool full = c0 + 16 <= a.cols;
-    float v[16];
-    load16<In>(static_cast<const char*>(a.src) + row * a.cols * In::bytes, c0,
-               live ? a.cols : 0, a.vec && full, v);
+    load16<In>(static_cast<const char*>(a.src) + row * a.cols * In::bytes, c0, a.cols,
+               a.vec && full, v);
+    if constexpr (G)
+      load16<In>(static_cast<const char*>(a.grad) + row * a.cols * In::bytes, c0, a.cols,
+                 a.vec && full, gv);
+  };
+  auto process = [&](int64_t it, float (&v)[16], float (&gv)[16]) {
+    const bool live = group + it * ngroups < items;
     fwht_inreg<KR, 16>(v);
 #pragma unroll
     for (int m = 1; 16 * m < KR; m <<= 1) fwht_xlane<16>(v, g, m);
-    float gv[16];
-    if constexpr (MODE == STAT_LSQ) {
-      load16<In>(static_cast<const char*>(a.grad) + row * a.cols * In::bytes, c0,
-                 live ? a.cols : 0, a.vec && full, gv);
+    if constexpr (G) {
       fwht_inreg<KR, 16>(gv);
 #pragma unroll
       for (int m = 1; 16 * m < KR; m <<= 1) fwht_xlane<16>(gv, g, m);
     }
-    if (!live) continue;   // loads past the end read zeros: their terms are zero
+    if (!live) return;     // a repeated segment: its terms are not counted
     float part = 0.0f;     // at most 16 terms in fp32, then into the fp64 sum
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -159,7 +166,8 @@ __global__ __launch_bounds__(kThreads) void stat_kernel(StatArgs a) {
         const double e = static_cast<double>(v[i]) - static_cast<double>(s) * level;
         acc += e * e;
       } else {
-        const double x = static_cast<double>(v[i]) / static_cast<double>(s);
+        // r / s as a product with the fp64 reciprocal (within 2^-52 of the quotient)
+        const double x = static_cast<double>(v[i]) * rd;
         const double d = fabs(x) >= a.qp ? copysign(static_cast<double>(a.qp), x)
                                          : static_cast<double>(quant_code(v[i], r, a.qp)) - x;
         acc += static_cast<double>(gv[i]) * a.inv_k * d;
@@ -167,19 +175,40 @@ __global__ __launch_bounds__(kThreads) void stat_kernel(StatArgs a) {
     }
     if constexpr (MODE == STAT_ABS_SUM) acc += part;
     if constexpr (MODE == STAT_ABS_MAX) acc = fmax(acc, static_cast<double>(part));
+  };
+  if (items > 0) {
+    float va[16], vb[16], ga[G ? 16 : 1], gb[G ? 16 : 1];
+    float (&gA)[16] = *reinterpret_cast<float(*)[16]>(G ? ga : va);
+    float (&gB)[16] = *reinterpret_cast<float(*)[16]>(G ? gb : vb);
+    fetch(0, va, gA);
+    int64_t it = 0;
+    for (; it + 1 < iters; it += 2) {
+      fetch(it + 1, vb, gB);
+      process(it, va, gA);
+      fetch(it + 2, va, gA);
+      process(it + 1, vb, gB);
+    }
+    if (it < iters) process(it, va, gA);
   }
   acc = block_sum_f64(acc, red, MODE == STAT_ABS_MAX);
   if (threadIdx.x == 0) a.partials[blockIdx.x] = acc;
 }
 
-// Reduce the partials in order into out[0]; then, by `finish`: 0 nothing more; 1 the scale
+// Reduce the partials in a fixed order into out[0]; then, by `finish`: 0 nothing more; 1 the scale
 // max / qp (fp32, for STAT_ABS_MAX: the tensor-wise absmax scale); 2 the cold-start step
 // fp32(2 * (sum / n) / sqrt(qp)) into fout.
-__global__ void stat_finish_kernel(const double* partials, int nparts, bool take_max, double* out,
-                                   int finish, double n, int qp, float* fout) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+constexpr int kFinishThreads = 256;
+
+__global__ __launch_bounds__(kFinishThreads) void stat_finish_kernel(
+    const double* partials, int nparts, bool take_max, double* out, int finish, double n, int qp,
+    float* fout) {
+  __shared__ double red[kFinishThreads / 64];
+  // thread t takes partials t, t + 256, ... in order; then the lane tree and the waves in order
   double t = 0.0;
-  for (int i = 0; i < nparts; ++i) t = take_max ? fmax(t, partials[i]) : t + partials[i];
+  for (int i = threadIdx.x; i < nparts; i += kFinishThreads)
+    t = take_max ? fmax(t, partials[i]) : t + partials[i];
+  t = block_sum_f64(t, red, take_max);
+  if (threadIdx.x != 0) return;
   if (out) *out = t;
   if (finish == 1) *fout = static_cast<float>(t) / static_cast<float>(qp);
   if (finish == 2) *fout = static_cast<float>(2.0 * (t / n) / sqrt(static_cast<double>(qp)));
@@ -236,7 +265,7 @@ hipError_t stat_pass(const StatPass& p, hipStream_t st) {
     case DT_BF16: e = stat_launch_in<BF16>(p.k, p.mode, p.f8, a, static_cast<int>(grid), st, tok); break;
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(stat_finish_kernel, dim3(1), dim3(64), 0, st, p.partials, static_cast<int>(grid),
+  hipLaunchKernelGGL(stat_finish_kernel, dim3(1), dim3(kFinishThreads), 0, st, p.partials, static_cast<int>(grid),
                      p.mode == STAT_ABS_MAX, p.out, p.finish,
                      static_cast<double>(p.rows) * static_cast<double>(p.cols), p.qp, p.fout);
   return hipGetLastError();

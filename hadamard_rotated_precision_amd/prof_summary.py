@@ -140,10 +140,12 @@ def cmd_traffic(args):
                            "fetch_scale": f_scale, "write_scale": w_scale},
            "command": args.cmd}
     json.dump(doc, open(args.json, "w"), indent=1)
-    out = ["# HBM traffic per launch: %s" % args.workload, "",
+    out = ["# Counted memory traffic per launch: %s" % args.workload, "",
            "Two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch). Each counter",
            "is divided by what it reads for a plain device copy of %d bytes in the same run" % args.copy_bytes,
-           "(fetch scale %.4f, write scale %.4f counted bytes per copied byte)." % (f_scale, w_scale), "",
+           "(fetch scale %.4f, write scale %.4f counted bytes per copied byte)." % (f_scale, w_scale),
+           "These counters count bytes between the L2s and the memory fabric, hits in the 256 MB",
+           "MALL included: an upper bound on the HBM bytes, not the HBM bytes themselves.", "",
            "Commands (from the repository root, rocprofv3 run in /tmp):", "", "```", args.cmd, "```", "",
            "| kernel | dispatches | read MB / launch | written MB / launch |", "|---|---:|---:|---:|"]
     for k in sorted(set(kf) | set(kw)):
