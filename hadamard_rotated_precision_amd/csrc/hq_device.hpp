@@ -78,6 +78,46 @@ struct BF16 {
   }
 };
 
+// A compiler-only fence after a prefetch: the loads before it are issued before anything after
+// it. A body that stores nothing (an absmax or a sum pass) would otherwise let the compiler sink
+// the next item's loads down to their first use, which leaves one item's loads in flight and its
+// latency exposed; the scheduling barrier also keeps the body's first instructions from moving
+// above them. No instruction is emitted and no wait: the loads stay in flight across the fence.
+__device__ inline void keep_issued() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// 16 consecutive elements as raw 16-byte chunks (two for 16-bit formats, four for fp32), so a
+// prefetch holds no converted values; unpack16 converts them.
+template <class T>
+__device__ inline void load16_raw(const void* base, int64_t i0, uint4 (&q)[4]) {
+  const uint4* p = reinterpret_cast<const uint4*>(static_cast<const char*>(base) + i0 * T::bytes);
+#pragma unroll
+  for (int j = 0; j < T::bytes; ++j) q[j] = p[j];
+}
+
+template <class T>
+__device__ inline void unpack16(const uint4 (&q)[4], float (&v)[16]) {
+  if constexpr (T::bytes == 4) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[4 * j + 0] = __uint_as_float(q[j].x); v[4 * j + 1] = __uint_as_float(q[j].y);
+      v[4 * j + 2] = __uint_as_float(q[j].z); v[4 * j + 3] = __uint_as_float(q[j].w);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t w[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[8 * j + 2 * i + 0] = T::from_bits(static_cast<uint16_t>(w[i] & 0xFFFFu));
+        v[8 * j + 2 * i + 1] = T::from_bits(static_cast<uint16_t>(w[i] >> 16));
+      }
+    }
+  }
+}
+
 // Load 16 consecutive elements starting at element index i0 of a row whose valid length is
 // n (elements >= n read as 0). `vec` says the row base and i0 are 16-byte aligned and the
 // whole chunk is in bounds, so wide loads can be used.

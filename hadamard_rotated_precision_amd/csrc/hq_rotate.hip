@@ -103,7 +103,10 @@ __device__ inline double block_sum_f64(double x, double* red, bool take_max) {
   return r;
 }
 
-template <class In, int KR, int MODE, bool F8>
+// VEC: every segment is a whole aligned 256-column run (aligned rows, cols % 256 == 0) and there
+// are fewer than 2^31 of them; the segments then stay raw 16-byte chunks while in flight and are
+// converted when processed.
+template <class In, int KR, int MODE, bool F8, bool VEC>
 __global__ __launch_bounds__(kThreads) void stat_kernel(StatArgs a) {
   __shared__ double red[kThreads / 64];
   const int lane = threadIdx.x & 63;
@@ -122,8 +125,10 @@ __global__ __launch_bounds__(kThreads) void stat_kernel(StatArgs a) {
   }
   constexpr bool G = MODE == STAT_LSQ;
   double acc = 0.0;
-  // The segments of this group's iterations, loaded two ahead of their use into alternating
-  // register sets: a segment past the end loads the last one again and is skipped.
+  // The segments of this group's iterations go through rotating register sets: three in the VEC
+  // form, whose raw chunks stay in flight two segments ahead; two in the element form, which
+  // converts on load and so waits for its loads there. A segment past the end loads the last
+  // one again and is skipped.
   auto fetch = [&](int64_t it, float (&v)[16], float (&gv)[16]) {
     int64_t item = group + it * ngroups;
     if (item >= items) item = items - 1;
@@ -176,7 +181,44 @@ __global__ __launch_bounds__(kThreads) void stat_kernel(StatArgs a) {
     if constexpr (MODE == STAT_ABS_SUM) acc += part;
     if constexpr (MODE == STAT_ABS_MAX) acc = fmax(acc, static_cast<double>(part));
   };
-  if (items > 0) {
+  if constexpr (VEC) {
+    // 32-bit index arithmetic (the host takes this form only for items < 2^31): a 64-bit
+    // division would branch, and the compiler waits for the loads in flight at such branches.
+    const uint32_t nseg32 = static_cast<uint32_t>(nseg), last = static_cast<uint32_t>(items - 1);
+    auto fetch_raw = [&](int64_t it, uint4 (&q)[4], uint4 (&gq)[4]) {
+      const int64_t want = group + it * ngroups;
+      const uint32_t item = want < items ? static_cast<uint32_t>(want) : last;
+      const uint32_t row = item / nseg32, seg = item - row * nseg32;
+      const int64_t off = static_cast<int64_t>(row) * a.cols + 256 * seg + 16 * g;
+      load16_raw<In>(a.src, off, q);
+      if constexpr (G) load16_raw<In>(a.grad, off, gq);
+    };
+    auto run = [&](int64_t it, const uint4 (&q)[4], const uint4 (&gq)[4]) {
+      float v[16], gv[16];
+      unpack16<In>(q, v);
+      if constexpr (G) unpack16<In>(gq, gv);
+      process(it, v, gv);
+    };
+    if (items > 0) {   // three register sets: two segments in flight while one is processed
+      uint4 qa[4], qb[4], qc[4], ga[4], gb[4], gc[4];
+      fetch_raw(0, qa, ga);
+      fetch_raw(1, qb, gb);
+      for (int64_t it = 0;; it += 3) {
+        fetch_raw(it + 2, qc, gc);
+        keep_issued();
+        run(it, qa, ga);
+        if (it + 1 >= iters) break;
+        fetch_raw(it + 3, qa, ga);
+        keep_issued();
+        run(it + 1, qb, gb);
+        if (it + 2 >= iters) break;
+        fetch_raw(it + 4, qb, gb);
+        keep_issued();
+        run(it + 2, qc, gc);
+        if (it + 3 >= iters) break;
+      }
+    }
+  } else if (items > 0) {
     float va[16], vb[16], ga[G ? 16 : 1], gb[G ? 16 : 1];
     float (&gA)[16] = *reinterpret_cast<float(*)[16]>(G ? ga : va);
     float (&gB)[16] = *reinterpret_cast<float(*)[16]>(G ? gb : vb);
@@ -216,9 +258,12 @@ __global__ __launch_bounds__(kFinishThreads) void stat_finish_kernel(
 
 template <class In, int MODE, bool F8>
 static hipError_t stat_launch_k(int k, const StatArgs& a, int grid, hipStream_t st, int tok) {
+  const bool vec = a.vec && a.cols % 256 == 0 && a.rows * (a.cols / 256) < (int64_t(1) << 31);
   switch (k) {
 #define HQ_SK(KK) \
-  case KK: return launch_k(stat_kernel<In, KK, MODE, F8>, dim3(grid), dim3(kThreads), st, tok, a);
+  case KK:                                                                                        \
+    return vec ? launch_k(stat_kernel<In, KK, MODE, F8, true>, dim3(grid), dim3(kThreads), st, tok, a) \
+               : launch_k(stat_kernel<In, KK, MODE, F8, false>, dim3(grid), dim3(kThreads), st, tok, a);
     HQ_SK(1) HQ_SK(2) HQ_SK(4) HQ_SK(8) HQ_SK(16) HQ_SK(32) HQ_SK(64) HQ_SK(128) HQ_SK(256)
 #undef HQ_SK
   }

@@ -128,6 +128,25 @@ def test_select_hadamard_k(fmt, bits):
         assert kb.value == best
 
 
+@pytest.mark.parametrize("rows,dt", [(6000, B.HQ_BF16), (8000, B.HQ_BF16), (6000, B.HQ_F32)])
+def test_stats_many_segments(rows, dt):
+    """Shapes with more 256-column segments than one launch has lane groups (2048 workgroups of
+    16 groups), so each group takes three or four segments in turn, the last round only partly
+    live: sum |r| and the quantization error against the oracle."""
+    print("[case] stats many segments", rows, dt, flush=True)
+    rng = np.random.default_rng(rows + dt)
+    cols, k = 4096, 128
+    vb, _, V, _ = _data(rng, rows, cols, dt)
+    R = O.rotate(V, O.ROT_RIGHT, k)
+    scale = O.absmax_scale(R, 127)
+    ora = O.rotated_stats(V, None, O.ROT_RIGHT, k, 8, scale)
+    cfg = T.config(k, 8, B.HQ_SCALE_STEP, B.HQ_VARIANT_HQ)
+    got = gpu_stat(vb, None, dt, rows, cols, B.HQ_ROT_RIGHT, cfg, B.HQ_STAT_ABS_SUM, scale)
+    assert abs(got - ora["abs_sum"]) <= 1e-6 * ora["abs_sum"], (got, ora["abs_sum"])
+    got = gpu_stat(vb, None, dt, rows, cols, B.HQ_ROT_RIGHT, cfg, B.HQ_STAT_QERR, scale)
+    assert abs(got - ora["qerr"]) <= 1e-5 * ora["qerr"], (got, ora["qerr"])
+
+
 @pytest.mark.timeout(600)
 def test_lsq_stat_fullsize_llama7b_x():
     """The LSQ step gradient of X at the Llama-7B MLP shape (4096 x 4096 bf16, heavy-tailed,
