@@ -1955,9 +1955,9 @@ hipError_t pro_pass(const ProPass& p, int op, hipStream_t st) {
   return e;
 }
 
-// Blocks of 128 and 256 only: for k <= 64 the VALU rows kernel streams as fast or faster
-// (it needs at most two lane-exchange stages there), measured on bf16 shapes from 2048 x 4096
-// to 8192 x 13824.
+// The matrix-core store mode covers whole 64 x 256 tiles of 16-bit data for every k >= 16. The
+// automatic choice does not take it for RIGHT: with DPP lane exchanges the VALU rows kernel
+// streams at least as fast at every k (measured on bf16 8192 x 13824).
 bool fwht_right_mma_ok(const void* src, int dt, const void* dst, int out_dt, int64_t rows,
                        int64_t cols, int k) {
   const bool al = (reinterpret_cast<uintptr_t>(src) & 15u) == 0 &&
