@@ -207,6 +207,11 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs 
   __shared__ __attribute__((aligned(16))) int8_t st0[STAGE_ALLOC];
   __shared__ __attribute__((aligned(16))) int8_t st1[STAGE_ALLOC];
   __shared__ __attribute__((aligned(16))) int8_t st2[NST == 3 ? STAGE_ALLOC : 16];
+  // The row-major epilogue with 128- or 256-point row rotations on 256-wide tiles parks the last
+  // round's block of values in LDS while the first rounds run (see STASH below); two of its
+  // eight 16-byte chunks per thread live here, the rest in the unused tails of stages 0 and 1.
+  constexpr bool STASH = BN == 256 && !TRANS && !PAIR && KM >= 128 && EPI != EPI_I32;
+  __shared__ __attribute__((aligned(16))) float4 stash_x[STASH ? 2 * NT : 1];
 
   const int tiles_m = static_cast<int>((g.M + GBM - 1) / GBM);
   const int tiles_n = static_cast<int>((g.N + BN - 1) / BN);
@@ -546,6 +551,29 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs 
           }
         }
       };
+      // STASH: with the two-sided 128- and 256-point rotations, all 128 values of a lane plus a
+      // round's working set do not fit the 256 registers a wave has at two waves per SIMD, and
+      // the compiler would spill about 31 values to scratch memory (written and read back
+      // through the caches for every tile). Instead the last round's block fa[3] (32 values)
+      // goes to LDS once the row stages that mix the blocks are done and comes back when its
+      // round starts: eight 16-byte chunks per thread, three past a round's 32 padded rows in
+      // stage 0, three in stage 1, two in stash_x. Each thread reads only what it wrote, and
+      // the rounds never touch these bytes, so no barrier is involved.
+      constexpr int EP_ROUND = 32 * RP * 4;   // bytes of one round in a stage
+      static_assert(!STASH || (EP_ROUND % 16 == 0 && EP_ROUND + 3 * NT * 16 <= STAGE),
+                    "three stash chunks must fit past a round in each stage");
+      auto stash_at = [&](int c) -> float4* {
+        if (c < 3) return reinterpret_cast<float4*>(st0 + EP_ROUND + c * NT * 16) + t;
+        if (c < 6) return reinterpret_cast<float4*>(st1 + EP_ROUND + (c - 3) * NT * 16) + t;
+        return &stash_x[(c - 6) * NT + t];
+      };
+      if constexpr (STASH) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const int j = c / 4, e = 4 * (c % 4);
+          *stash_at(c) = make_float4(fa[3][j][e], fa[3][j][e + 1], fa[3][j][e + 2], fa[3][j][e + 3]);
+        }
+      }
       float res[PAIR ? 4 : 1][NJ][8];   // PAIR: this tile's rotated values, kept for the exchange
       // PAIR: the tile's column half, and its published values (device-coherent sc1 stores)
       const int half = tn & 1;
@@ -572,6 +600,16 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs 
       };
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
+        if constexpr (STASH) {
+          if (cc == 3) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+              const float4 v = *stash_at(c);
+              const int j = c / 4, e = 4 * (c % 4);
+              fa[3][j][e] = v.x; fa[3][j][e + 1] = v.y; fa[3][j][e + 2] = v.z; fa[3][j][e + 3] = v.w;
+            }
+          }
+        }
         if constexpr (KM > 4) rows_fwht_lanehalf_block<NB>(fa[cc], lane);
         __syncthreads();
 #pragma unroll
