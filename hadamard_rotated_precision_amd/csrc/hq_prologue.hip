@@ -517,6 +517,26 @@ __device__ inline void mma_high_stages(f32x4 (&acc)[NNB]) {
   }
 }
 
+// 4 x 4 dword transpose across lane bits 2 and 3 (lanes 4m + i, m < 4, of each row of 16
+// lanes): lane m's v[c] becomes lane c's v[m]. Bank-masked DPP moves, a lane keeping its own
+// value where the mask leaves it out: lane ^ 8 is a rotation of the row by 8, lane ^ 4 a shift
+// by four lanes in each direction.
+template <int CTRL, int BANKS>
+__device__ inline uint32_t dpp_take(uint32_t old, uint32_t src) {
+  return __builtin_amdgcn_update_dpp(old, src, CTRL, 0xF, BANKS, false);
+}
+__device__ inline void lane4_transpose(uint32_t& v0, uint32_t& v1, uint32_t& v2, uint32_t& v3) {
+  // lane bit 3: positions 0, 1 of lanes 8-15 and 2, 3 of lanes 0-7 come from lane ^ 8
+  const uint32_t a0 = dpp_take<0x128, 0xC>(v0, v2), a2 = dpp_take<0x128, 0x3>(v2, v0);
+  const uint32_t a1 = dpp_take<0x128, 0xC>(v1, v3), a3 = dpp_take<0x128, 0x3>(v3, v1);
+  // lane bit 2: positions 0, 2 of lanes with the bit set come from lane - 4 (row shift right),
+  // positions 1, 3 of the others from lane + 4 (row shift left)
+  v0 = dpp_take<0x114, 0xA>(a0, a1);
+  v1 = dpp_take<0x104, 0x5>(a1, a0);
+  v2 = dpp_take<0x114, 0xA>(a2, a3);
+  v3 = dpp_take<0x104, 0x5>(a3, a2);
+}
+
 // 4 x 4 byte transpose across the lanes of a quad: lane i of the quad holds bytes (row j, column
 // 4m + i) for j < 4 and returns bytes (row i, column 4m + j).
 __device__ inline uint32_t quad_byte_transpose(uint32_t d, int i) {
@@ -1483,13 +1503,22 @@ __device__ inline void both_mma_body(const ProArgs& a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) amax1 = fmaxf(amax1, fabsf(y[nb][j]));
         } else if (a.codes) {
+          // After the byte transpose, lane (n0 = 4m + i, lg) holds the codes of columns
+          // 16nb + 4m + [0, 4) of row 4lg + i; the dword transpose over m then gives lane m all
+          // 16 codes of blocks m and 4 + m, two 16-byte stores (code rows are 16-byte aligned).
+          // One store instruction covers 64 consecutive bytes of 16 rows: 4-byte stores covering
+          // 16 bytes of each row wrote at about half the rate of whole lines.
           const int i = n0 & 3, m = n0 >> 2;
-          int8_t* dst = a.codes + (row0 + rloc + 4 * lg + i) * a.ld + col0 + BT_HALF * h + 4 * m;
+          uint32_t d[8];
 #pragma unroll
-          for (int nb = 0; nb < 8; ++nb) {
-            const uint32_t d = quant4(y[nb][0], y[nb][1], y[nb][2], y[nb][3], r1, lo, hi, (OP == OP_QUANT_F8));
-            *reinterpret_cast<uint32_t*>(dst + 16 * nb) = quad_byte_transpose(d, i);
-          }
+          for (int nb = 0; nb < 8; ++nb)
+            d[nb] = quad_byte_transpose(
+                quant4(y[nb][0], y[nb][1], y[nb][2], y[nb][3], r1, lo, hi, (OP == OP_QUANT_F8)), i);
+          lane4_transpose(d[0], d[1], d[2], d[3]);
+          lane4_transpose(d[4], d[5], d[6], d[7]);
+          int8_t* dst = a.codes + (row0 + rloc + 4 * lg + i) * a.ld + col0 + BT_HALF * h + 16 * m;
+          *reinterpret_cast<uint4*>(dst) = make_uint4(d[0], d[1], d[2], d[3]);
+          *reinterpret_cast<uint4*>(dst + 64) = make_uint4(d[4], d[5], d[6], d[7]);
         }
         const int c4 = (rloc >> 2) + lg;
 #pragma unroll
