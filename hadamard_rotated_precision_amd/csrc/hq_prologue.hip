@@ -537,6 +537,23 @@ __device__ inline void lane4_transpose(uint32_t& v0, uint32_t& v1, uint32_t& v2,
   v3 = dpp_take<0x104, 0x5>(a3, a2);
 }
 
+// 4 x 4 dword transpose across the lanes of a quad (lane p = lane & 3): lane p's v[c] becomes
+// lane c's v[p]. Per lane bit, a quad permute fetches the partner's value and a select keeps it
+// where the position's bit and the lane's bit differ.
+__device__ inline void quad_transpose4(uint32_t (&v)[4], int p) {
+  uint32_t n[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint32_t x = __builtin_amdgcn_mov_dpp(v[c ^ 2], 0x4E, 0xF, 0xF, false);   // lane ^ 2
+    n[c] = (((c ^ p) >> 1) & 1) ? x : v[c];
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint32_t x = __builtin_amdgcn_mov_dpp(n[c ^ 1], 0xB1, 0xF, 0xF, false);   // lane ^ 1
+    v[c] = ((c ^ p) & 1) ? x : n[c];
+  }
+}
+
 // 4 x 4 byte transpose across the lanes of a quad: lane i of the quad holds bytes (row j, column
 // 4m + i) for j < 4 and returns bytes (row i, column 4m + j).
 __device__ inline uint32_t quad_byte_transpose(uint32_t d, int i) {
@@ -1551,19 +1568,32 @@ __device__ inline void both_mma_body(const ProArgs& a) {
 #pragma unroll
         for (int i = 0; i < 64; ++i) amax2 = fmaxf(amax2, fabsf(static_cast<float>(u[i])));
       } else {
-        int8_t* dst = a.codes_t + gcol * a.ld_t + row0 + 64 * pp;
+        // xq[q] holds rows 64pp + 16q + [0, 16) of the column. The quad's four lanes (pp) trade
+        // those chunks, one dword index at a time, so that lane pp ends up with rows
+        // 64q + 16pp + [0, 16): each store instruction then writes 64 consecutive bytes of a
+        // column's code row instead of four 16-byte pieces 64 bytes apart, which wrote at about
+        // half the rate of whole lines.
+        uint32_t xq[4][4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint32_t xq[4];
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int i = 16 * q + 4 * j;
-            xq[j] = quant4(static_cast<float>(u[i]), static_cast<float>(u[i + 1]),
-                           static_cast<float>(u[i + 2]), static_cast<float>(u[i + 3]), r2, lo, hi,
-                           (OP == OP_QUANT_F8));
+            xq[q][j] = quant4(static_cast<float>(u[i]), static_cast<float>(u[i + 1]),
+                              static_cast<float>(u[i + 2]), static_cast<float>(u[i + 3]), r2, lo,
+                              hi, (OP == OP_QUANT_F8));
           }
-          *reinterpret_cast<uint4*>(dst + 16 * q) = make_uint4(xq[0], xq[1], xq[2], xq[3]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t col[4] = {xq[0][j], xq[1][j], xq[2][j], xq[3][j]};
+          quad_transpose4(col, pp);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) xq[q][j] = col[q];
         }
+        int8_t* dst = a.codes_t + gcol * a.ld_t + row0 + 16 * pp;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<uint4*>(dst + 64 * q) = make_uint4(xq[q][0], xq[q][1], xq[q][2], xq[q][3]);
       }
     }
     if constexpr (OP == OP_ABSMAX) {
