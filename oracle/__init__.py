@@ -15,9 +15,11 @@ layer, in the order the pages give them:
   in forward, left rotation on output gradients in backward = HALO-2, tensor-wise scales,
   reuse of quantized rotated tensors).
 
-Code formats: INT (integers on [-Qp, Qp], Qp = 127 or 7) and E4M3 (FP8 codes, the HALO
+Code formats: INT (integers on [-Qp, Qp], Qp = 127 or 7), E4M3 (FP8 codes, the HALO
 page's lower-precision variants: s = max|R| / 448, nearest E4M3 value of R / s, ties to even,
-saturating; products exact in int64 units of 2^-18).
+saturating; products exact in int64 units of 2^-18), and E2M3 / E3M2 (FP6 codes, the same
+page's FP6 variants: s = max|R| / 7.5 or / 28, nearest FP6 value, ties to even, saturating;
+stored as the E4M3 bytes of their values, so the FP8 product and decode serve them).
 
 Variants (names follow the HALO page):
   HALO0: no rotation.
@@ -42,6 +44,8 @@ ROT_NONE, ROT_RIGHT, ROT_LEFT, ROT_BOTH = 0, 1, 2, 3
 HALO0, HQ, HALO2 = 0, 1, 2
 ABSMAX, STEP = 0, 1
 INT, E4M3 = 0, 1          # code formats: integers on [-Qp, Qp], or FP8 E4M3 values
+E2M3, E3M2 = 2, 3         # FP6 code formats (stored as the E4M3 bytes of their values)
+FLOAT_FORMATS = (E4M3, E2M3, E3M2)
 E4M3_MAX = 448            # largest finite E4M3 value: the grid bound of the FP8 format
 E4M3_UNIT_EXP = 18        # an FP8 product is an integer number of 2^-18
 
@@ -83,6 +87,12 @@ def _load():
     lib.hqo_quantize_e4m3.restype = i32
     lib.hqo_gemm_f8.argtypes = [vp, i64, i64, vp, i64, i64, i64, i64, i64, vp]
     lib.hqo_gemm_f8.restype = i32
+    lib.hqo_absmax_scale_d.argtypes = [vp, i64, ctypes.c_double]
+    lib.hqo_absmax_scale_d.restype = f32
+    lib.hqo_fp6_max.argtypes = [i32]
+    lib.hqo_fp6_max.restype = ctypes.c_double
+    lib.hqo_quantize_fp6.argtypes = [vp, i64, f32, i32, vp]
+    lib.hqo_quantize_fp6.restype = i32
     _lib = lib
     return lib
 
@@ -98,11 +108,15 @@ def _p(a):
 
 def qmax(bits, fmt=INT):
     """Symmetric grid bound: 127 for INT8, 7 for the INT4 range (INT4 page, §3.1), 448 for
-    FP8 E4M3 codes."""
+    FP8 E4M3 codes, 7.5 / 28 for FP6 E2M3 / E3M2 codes (the largest value of each format)."""
     if fmt == E4M3:
         if bits != 8:
             raise ValueError("E4M3 codes are 8 bits")
         return E4M3_MAX
+    if fmt in (E2M3, E3M2):
+        if bits != 6:
+            raise ValueError("FP6 codes are 6 bits")
+        return fp6_max(fmt)
     if bits == 8:
         return 127
     if bits == 4:
@@ -137,7 +151,17 @@ def rotate(V, rot, k):
 
 def absmax_scale(R, qp):
     R = np.ascontiguousarray(R, dtype=np.float64)
-    return np.float32(_load().hqo_absmax_scale(_p(R), R.size, qp))
+    if float(qp) != int(qp):   # a grid bound that is not an integer (7.5 for E2M3)
+        return np.float32(_load().hqo_absmax_scale_d(_p(R), R.size, float(qp)))
+    return np.float32(_load().hqo_absmax_scale(_p(R), R.size, int(qp)))
+
+
+def fp6_max(fmt):
+    """Largest value of an FP6 format (E2M3 or E3M2)."""
+    v = _load().hqo_fp6_max(fmt)
+    if v < 0:
+        raise ValueError("not an FP6 format")
+    return v
 
 
 def quantize(R, scale, qp):
@@ -170,7 +194,7 @@ def dequant(T, s_a, s_b, k_pow_e, fmt=INT):
     """T * s_a * s_b / k^e (FP8 sums are in units of 2^-18: that factor is applied too)."""
     T = np.ascontiguousarray(T, dtype=np.int64)
     out = np.empty(T.shape, dtype=np.float64)
-    div = float(k_pow_e) * (2.0 ** E4M3_UNIT_EXP if fmt == E4M3 else 1.0)
+    div = float(k_pow_e) * (2.0 ** E4M3_UNIT_EXP if fmt in FLOAT_FORMATS else 1.0)
     _load().hqo_dequant(_p(T), T.size, float(np.float32(s_a)), float(np.float32(s_b)), div,
                         _p(out))
     return out
@@ -191,6 +215,16 @@ def quantize_e4m3(R, scale):
     return q
 
 
+def quantize_fp6(R, scale, fmt):
+    """FP6 codes (E2M3 or E3M2) nearest to R / scale, ties to even, saturating at the largest
+    value, as the uint8 E4M3 bytes of their values."""
+    R = np.ascontiguousarray(R, dtype=np.float64)
+    q = np.empty(R.shape, dtype=np.uint8)
+    if _load().hqo_quantize_fp6(_p(R), R.size, float(np.float32(scale)), fmt, _p(q)) != 0:
+        raise ValueError("not an FP6 format")
+    return q
+
+
 def gemm_f8(A, sam, sak, B, sbk, sbn, M, N, K):
     """Exact product of E4M3 code matrices in int64 units of 2^-18 (same index maps as
     gemm_i8)."""
@@ -202,7 +236,7 @@ def gemm_f8(A, sam, sak, B, sbk, sbn, M, N, K):
 
 
 def _gemm(fmt, *args):
-    return gemm_f8(*args) if fmt == E4M3 else gemm_i8(*args)
+    return gemm_f8(*args) if fmt in FLOAT_FORMATS else gemm_i8(*args)
 
 
 def round_to(vals, dtype):
@@ -217,7 +251,7 @@ def round_to(vals, dtype):
 # ------------------------------------------------------------ composed steps
 def quantize_tensor(V, rot, k, bits, mode=ABSMAX, step=None, fmt=INT):
     """Rotate -> tensor-wise scale -> codes. V is float64 (already decoded).
-    Returns (codes: int8, or uint8 E4M3 codes for fmt E4M3; scale: float32)."""
+    Returns (codes: int8, or uint8 E4M3 bytes for the float formats; scale: float32)."""
     qp = qmax(bits, fmt)
     R = rotate(V, rot, k)
     if mode == ABSMAX:
@@ -230,6 +264,8 @@ def quantize_tensor(V, rot, k, bits, mode=ABSMAX, step=None, fmt=INT):
         raise ValueError("bad scale mode")
     if fmt == E4M3:
         return quantize_e4m3(R, s), s
+    if fmt in (E2M3, E3M2):
+        return quantize_fp6(R, s, fmt), s
     return quantize(R, s, qp), s
 
 
@@ -405,6 +441,8 @@ def rotated_stats(V, G, rot, k, bits, scale, fmt=INT):
     qp = qmax(bits, fmt)
     if fmt == E4M3:
         rec = decode_e4m3(quantize_e4m3(R, scale)) * float(np.float32(scale))
+    elif fmt in (E2M3, E3M2):
+        rec = decode_e4m3(quantize_fp6(R, scale, fmt)) * float(np.float32(scale))
     else:
         rec = quantize(R, scale, qp).astype(np.float64) * float(np.float32(scale))
     out["qerr"] = float(np.sum((R - rec) ** 2))

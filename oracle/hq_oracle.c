@@ -45,6 +45,10 @@
  *     +-448; a value that rounds to zero keeps its sign bit. Every E4M3 value is an integer
  *     multiple of 2^-9, so products of two codes are exact integers in units of 2^-18 and the
  *     integer product below accumulates them exactly in int64.
+ *   - FP6 codes (the same page's FP6 variants; the layout is not given) are either OCP 6-bit
+ *     format, E2M3 (largest 7.5) or E3M2 (largest 28): s = max|R| / largest value, the
+ *     nearest FP6 value, ties to the even mantissa, saturating. Both grids lie inside E4M3, so
+ *     an FP6 code is kept as the E4M3 byte of its value and the FP8 product serves.
  */
 #include <stdint.h>
 #include <stdlib.h>
@@ -191,12 +195,12 @@ static int f32_odd(float f) {
   return (int)(u & 1u);
 }
 
-/* Correctly rounded fp32 value of the exact quotient a / d (a >= 0 finite, d a small positive
- * integer). Start from the double quotient rounded to fp32, then move to a neighbour while the
+/* Correctly rounded fp32 value of the exact quotient a / d (a >= 0 finite, d > 0 with at most
+ * 7 significant bits: 127, 7, 448, 7.5 or 28). Start from the double quotient rounded to fp32, then move to a neighbour while the
  * exact quotient lies beyond the midpoint towards it (on the midpoint: to the even
  * significand). A midpoint of two fp32 values has 25 significant bits, so midpoint * d is
  * exact in double and every comparison is exact. */
-static float div_to_f32(double a, int d) {
+static float div_to_f32(double a, double d) {
   float f = (float)(a / (double)d);
   for (;;) {
     const float up = nextafterf(f, INFINITY), dn = nextafterf(f, 0.0f);
@@ -214,7 +218,16 @@ float hqo_absmax_scale(const double *R, int64_t n, int qp) {
   double a = 0.0;
   for (int64_t i = 0; i < n; ++i)
     if (fabs(R[i]) > a) a = fabs(R[i]);
-  return div_to_f32(a, qp);
+  return div_to_f32(a, (double)qp);
+}
+
+/* The same with a grid bound that need not be an integer (7.5, the largest E2M3 value): it has
+ * at most 4 significant bits, so midpoint * d stays exact in double. */
+float hqo_absmax_scale_d(const double *R, int64_t n, double qmax) {
+  double a = 0.0;
+  for (int64_t i = 0; i < n; ++i)
+    if (fabs(R[i]) > a) a = fabs(R[i]);
+  return div_to_f32(a, qmax);
 }
 
 /* [INT4 §3.1; HALO Limitations] Round-to-nearest quantizer onto the symmetric grid [-Qp, Qp]:
@@ -315,6 +328,83 @@ int hqo_quantize_e4m3(const double *R, int64_t n, float scale, uint8_t *q) {
       if (a > midv || (a == midv && (c & 1))) ++c;   /* nearest; a tie goes to the even code */
     }
     q[i] = (uint8_t)(c | (R[i] < 0 ? 0x80 : 0));
+  }
+  return 0;
+}
+
+/* ---------------------------------------------------------------- FP6 codes (E2M3, E3M2)
+ * [HALO summary page, Key results (the FP6 variants of the matmuls) and Limitations (tensor-wise
+ * round-to-nearest; FP8 matmuls stood in for FP6 on hardware without FP6)]. The pages do not fix
+ * the layout; both OCP 6-bit formats are provided: sign, E exponent bits with bias
+ * 2^(E-1) - 1, M mantissa bits, subnormals, every pattern finite. E2M3 (E = 2, M = 3) spans
+ * [-7.5, 7.5] in steps of 1/8 near zero; E3M2 (E = 3, M = 2) spans [-28, 28] in steps of 1/16
+ * near zero. Magnitude ordinal c = (e << M) | m, increasing in value: m 2^(1 - bias - M) for
+ * e = 0, (2^M + m) 2^(e - bias - M) otherwise. Every FP6 value of either format is an E4M3
+ * value (at most 3 significant bits, exponents inside E4M3's range), so a code is stored as
+ * the E4M3 byte of its value, and the FP8 product, decode and dequantization apply unchanged.
+ * fmt: 2 = E2M3, 3 = E3M2 (the library's format numbers). */
+static int fp6_layout(int fmt, int *E, int *M) {
+  if (fmt == 2) { *E = 2; *M = 3; return 0; }
+  if (fmt == 3) { *E = 3; *M = 2; return 0; }
+  return -1;
+}
+
+/* Value of FP6 magnitude ordinal c in units of 2^-9 (an integer for both formats). */
+static int64_t fp6_units(int E, int M, int c) {
+  const int bias = (1 << (E - 1)) - 1, e = c >> M, m = c & ((1 << M) - 1);
+  const int64_t mant = (e == 0) ? m : (int64_t)((1 << M) + m);
+  const int ex = (e == 0 ? 1 : e) - bias - M + 9;   /* >= 5 for both formats */
+  return mant << ex;
+}
+
+/* E4M3 byte of a non-negative value given in units of 2^-9 that lies on the E4M3 grid. */
+static int e4m3_code_of(int64_t units) {
+  int lo = 0, hi = 126;
+  while (lo < hi) {
+    const int mid = (lo + hi) / 2;
+    if (e4m3_units((uint8_t)mid) < units) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+/* The largest FP6 value of the format (the grid bound the tensor-wise scale maps max |R| to). */
+double hqo_fp6_max(int fmt) {
+  int E, M;
+  if (fp6_layout(fmt, &E, &M)) return -1.0;
+  return ldexp((double)fp6_units(E, M, (1 << (E + M)) - 1), -9);
+}
+
+/* q = the FP6 value nearest to R / s, ties to the even magnitude ordinal (the even mantissa),
+ * saturating at the largest value, stored as its E4M3 byte; a value that rounds to zero keeps
+ * its sign bit, as for E4M3 codes. The ordinal is found by exact comparisons of |R| against
+ * g(c) s and the midpoints (g(c) + g(c + 1)) / 2 s, each exact in double. s == 0 gives all-zero
+ * codes. Returns -1 for an unknown format, else 0. */
+int hqo_quantize_fp6(const double *R, int64_t n, float scale, int fmt, uint8_t *q) {
+  int E, M;
+  if (fp6_layout(fmt, &E, &M)) return -1;
+  if (scale == 0.0f) {
+    memset(q, 0, (size_t)n);
+    return 0;
+  }
+  const int cmax = (1 << (E + M)) - 1;
+  const double s = (double)scale;
+  for (int64_t i = 0; i < n; ++i) {
+    const double a = fabs(R[i]);
+    int lo = 0, hi = cmax;   /* largest ordinal whose value times s is <= |R| */
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) / 2;
+      if (ldexp((double)fp6_units(E, M, mid), -9) * s <= a) lo = mid;
+      else hi = mid - 1;
+    }
+    int c = lo;
+    if (c < cmax) {
+      const double g0 = ldexp((double)fp6_units(E, M, c), -9);
+      const double g1 = ldexp((double)fp6_units(E, M, c + 1), -9);
+      const double midv = (g0 + g1) * 0.5 * s;
+      if (a > midv || (a == midv && (c & 1))) ++c;   /* nearest; a tie goes to the even ordinal */
+    }
+    q[i] = (uint8_t)(e4m3_code_of(fp6_units(E, M, c)) | (R[i] < 0 ? 0x80 : 0));
   }
   return 0;
 }
