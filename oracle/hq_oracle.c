@@ -327,7 +327,7 @@ int hqo_quantize_e4m3(const double *R, int64_t n, float scale, uint8_t *q) {
       const double midv = (g0 + g1) * 0.5 * s;
       if (a > midv || (a == midv && (c & 1))) ++c;   /* nearest; a tie goes to the even code */
     }
-    q[i] = (uint8_t)(c | (R[i] < 0 ? 0x80 : 0));
+    q[i] = (uint8_t)(c | (signbit(R[i]) ? 0x80 : 0));
   }
   return 0;
 }
@@ -404,7 +404,7 @@ int hqo_quantize_fp6(const double *R, int64_t n, float scale, int fmt, uint8_t *
       const double midv = (g0 + g1) * 0.5 * s;
       if (a > midv || (a == midv && (c & 1))) ++c;   /* nearest; a tie goes to the even ordinal */
     }
-    q[i] = (uint8_t)(e4m3_code_of(fp6_units(E, M, c)) | (R[i] < 0 ? 0x80 : 0));
+    q[i] = (uint8_t)(e4m3_code_of(fp6_units(E, M, c)) | (signbit(R[i]) ? 0x80 : 0));
   }
   return 0;
 }

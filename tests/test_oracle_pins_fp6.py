@@ -146,6 +146,15 @@ def test_fp6_grid_aligned_layer_exact(golden, name, k):
     np.testing.assert_array_equal(out["dw"], G.T @ X)
 
 
+@pytest.mark.parametrize("fmt", [O.E4M3, O.E2M3, O.E3M2])
+def test_zero_codes_keep_the_sign_bit(fmt):
+    """A value that rounds to zero keeps its IEEE sign: -0.0 and tiny negatives give 0x80,
+    +0.0 and tiny positives 0x00."""
+    vals = np.array([0.0, -0.0, 1e-30, -1e-30])
+    q = O.quantize_e4m3(vals, 1.0) if fmt == O.E4M3 else O.quantize_fp6(vals, 1.0, fmt)
+    np.testing.assert_array_equal(q, [0x00, 0x80, 0x00, 0x80])
+
+
 def test_fp6_formats_are_6_bits():
     with pytest.raises(ValueError):
         O.qmax(8, O.E2M3)
