@@ -221,15 +221,18 @@ def layer_vs_bf16(cfg_id):
                       "(the same for the bf16 GEMMs)"}
 
 
-def fp8_step(cfg_id, steps=20):
-    """The same layer step with FP8 (E4M3) codes (HALO page: the FP8 variant of the three
-    matmuls): step time by event median, and the FP8 GEMM's roofline against the 5.0 PFLOP/s
-    dense FP8 peak (algorithmic 2*M*N*K flops per launch over kernel-stamped launch times)."""
+def fp8_step(cfg_id, steps=20, fmt=None):
+    """The same layer step with float codes, FP8 E4M3 by default (HALO page: the FP8 and FP6
+    variants of the three matmuls; FP6 codes, E2M3 or E3M2, are kept as E4M3 bytes and run on
+    the same FP8 matrix-core product, as the page ran FP6 on FP8 hardware): step time by event
+    median, and the GEMM's roofline against the 5.0 PFLOP/s dense FP8 peak (algorithmic
+    2*M*N*K flops per launch over kernel-stamped launch times)."""
     import torch
     from hadamard_rotated_precision_amd import binding as B
     from hadamard_rotated_precision_amd import tensors as T
     from hadamard_rotated_precision_amd import workloads as WL
-    cfg = WL.config(cfg_id, fmt=WL.E4M3)
+    fmt = WL.E4M3 if fmt is None else fmt
+    cfg = WL.config(cfg_id, fmt=fmt)
     N, C, D = cfg["N"], cfg["C"], cfg["D"]
     inputs = WL.make_inputs(cfg)
     dev = "cuda"
@@ -238,7 +241,7 @@ def fp8_step(cfg_id, steps=20):
     w = T.device_tensor_from_bits(inputs["w"], in_dt, dev)
     dy = T.device_tensor_from_bits(inputs["dy"], in_dt, dev)
     layer = T.Layer(N, C, D, cfg["k"], cfg["bits"], cfg["mode"], cfg["variant"], device=dev,
-                    fmt=B.HQ_FMT_E4M3)
+                    fmt=fmt)
     odt = T.TORCH_DT[out_dt]
     y = torch.empty((N, D), dtype=odt, device=dev)
     dx = torch.empty((N, C), dtype=odt, device=dev)
@@ -456,6 +459,8 @@ def main():
                     help="skip the LSS-MM (sampled weight gradient) measurement")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the FP8 (E4M3) step of the same layer")
+    ap.add_argument("--no-fp6", action="store_true",
+                    help="skip the FP6 (E2M3, E3M2) steps of the same layer")
     ap.add_argument("--no-fwht", action="store_true",
                     help="skip the standalone hq_fwht bandwidth figure")
     ap.add_argument("--no-cold", action="store_true",
@@ -709,6 +714,13 @@ def main():
             result["fp8_step"] = fp8_step(args.config)
         except Exception as exc:  # report, do not fail the benchmark line
             result["fp8_step"] = {"error": str(exc)}
+    if not args.no_fp6 and cfg["bits"] == 8 and cfg["mode"] == WL.ABSMAX:
+        print("[bench] fp6 steps", file=sys.stderr, flush=True)
+        for name, f in (("e2m3", WL.E2M3), ("e3m2", WL.E3M2)):
+            try:
+                result.setdefault("fp6_step", {})[name] = fp8_step(args.config, fmt=f)
+            except Exception as exc:  # report, do not fail the benchmark line
+                result.setdefault("fp6_step", {})[name] = {"error": str(exc)}
     if not args.no_qparams:
         print("[bench] quantizer-parameter statistics", file=sys.stderr, flush=True)
         try:

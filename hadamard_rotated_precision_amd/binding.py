@@ -22,7 +22,7 @@ HQ_ROT_NONE, HQ_ROT_RIGHT, HQ_ROT_LEFT, HQ_ROT_BOTH = 0, 1, 2, 3
 HQ_SCALE_ABSMAX, HQ_SCALE_STEP = 0, 1
 HQ_VARIANT_HALO0, HQ_VARIANT_HQ, HQ_VARIANT_HALO2 = 0, 1, 2
 HQ_FWHT_AUTO, HQ_FWHT_BUTTERFLY, HQ_FWHT_MATRIX = 0, 1, 2
-HQ_FMT_INT, HQ_FMT_E4M3 = 0, 1
+HQ_FMT_INT, HQ_FMT_E4M3, HQ_FMT_E2M3, HQ_FMT_E3M2 = 0, 1, 2, 3
 
 EXPORTS = ["hq_abi_version", "hq_status_string", "hq_code_pitch", "hq_workspace_bytes",
            "hq_rotate_quantize", "hq_linear_fwd", "hq_linear_fwd_noalloc", "hq_linear_bwd_input",

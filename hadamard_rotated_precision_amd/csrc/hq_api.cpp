@@ -27,16 +27,34 @@ int64_t pitch16(int64_t n) { return (n + 15) / 16 * 16; }
 bool is_pow2_k(int32_t k) { return k >= 1 && k <= 256 && (k & (k - 1)) == 0; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool valid_dt(int32_t dt) { return dt == HQ_F32 || dt == HQ_F16 || dt == HQ_BF16; }
-bool is_f8(const hq_config* cfg) { return cfg->format == HQ_FMT_E4M3; }
-// grid bound of the codes: 448 (the largest E4M3 value) or the integer Qp
+// Float-format codes (E4M3, or the FP6 formats kept as E4M3 bytes): the FP8 product serves them.
+bool is_f8(const hq_config* cfg) { return cfg->format != HQ_FMT_INT; }
+bool is_fp6(const hq_config* cfg) {
+  return cfg->format == HQ_FMT_E2M3 || cfg->format == HQ_FMT_E3M2;
+}
+// integer grid bound Qp (float formats: 448, only where an integer is needed)
 int qmax(const hq_config* cfg) { return is_f8(cfg) ? 448 : (cfg->bits == 4 ? 7 : 127); }
+// the scale's divisor: Qp, or the format's largest value (E4M3 448, E2M3 7.5, E3M2 28)
+float qmax_f(const hq_config* cfg) {
+  switch (cfg->format) {
+    case HQ_FMT_E4M3: return 448.0f;
+    case HQ_FMT_E2M3: return 7.5f;
+    case HQ_FMT_E3M2: return 28.0f;
+  }
+  return static_cast<float>(qmax(cfg));
+}
+// the prologue's float grid: 0 E4M3, 1 E2M3, 2 E3M2
+int fgrid(const hq_config* cfg) {
+  return cfg->format == HQ_FMT_E2M3 ? 1 : (cfg->format == HQ_FMT_E3M2 ? 2 : 0);
+}
 
 hq_status check_cfg(const hq_config* cfg) {
   if (!cfg) return HQ_ERR_NULL;
   if (!is_pow2_k(cfg->k)) return HQ_ERR_K;
-  if (cfg->format != HQ_FMT_INT && cfg->format != HQ_FMT_E4M3) return HQ_ERR_MODE;
-  if (cfg->bits != 4 && cfg->bits != 8) return HQ_ERR_BITS;
-  if (is_f8(cfg) && cfg->bits != 8) return HQ_ERR_BITS;
+  if (cfg->format != HQ_FMT_INT && cfg->format != HQ_FMT_E4M3 && !is_fp6(cfg)) return HQ_ERR_MODE;
+  if (cfg->format == HQ_FMT_INT && cfg->bits != 4 && cfg->bits != 8) return HQ_ERR_BITS;
+  if (cfg->format == HQ_FMT_E4M3 && cfg->bits != 8) return HQ_ERR_BITS;
+  if (is_fp6(cfg) && cfg->bits != 6) return HQ_ERR_BITS;
   if (cfg->scale_mode != HQ_SCALE_ABSMAX && cfg->scale_mode != HQ_SCALE_STEP) return HQ_ERR_MODE;
   if (cfg->variant < HQ_VARIANT_HALO0 || cfg->variant > HQ_VARIANT_HALO2) return HQ_ERR_MODE;
   return HQ_OK;
@@ -124,6 +142,8 @@ hq_status quantize_tensor(const void* src, int32_t dt, int64_t rows, int64_t col
   p.cols = cols;
   p.qp = qmax(cfg);
   p.f8 = is_f8(cfg);
+  p.qmaxf = qmax_f(cfg);
+  p.fgrid = fgrid(cfg);
   p.partials = ws.part[part_slot];
   p.step = step;
   p.zero_ptr = zero_ptr;
@@ -168,6 +188,8 @@ hq::ProPass x_both_pass(const void* src, int32_t dt, int64_t rows, int64_t cols,
   p.k = k;
   p.qp = qmax(cfg);
   p.f8 = is_f8(cfg);
+  p.qmaxf = qmax_f(cfg);
+  p.fgrid = fgrid(cfg);
   p.partials = ws.part[0];
   p.step = step_x;
   p.step2 = step_xt;
@@ -263,7 +285,7 @@ const char* hq_status_string(int32_t s) {
     case HQ_ERR_NULL: return "a required pointer is NULL";
     case HQ_ERR_SHAPE: return "bad shape (negative, not divisible by k, or mismatched pitch)";
     case HQ_ERR_K: return "k must be a power of two in [1, 256]";
-    case HQ_ERR_BITS: return "bits must be 4 or 8 (8 for E4M3 codes)";
+    case HQ_ERR_BITS: return "bits must be 4 or 8 for integer codes, 8 for E4M3, 6 for E2M3 / E3M2";
     case HQ_ERR_DTYPE: return "unsupported dtype";
     case HQ_ERR_MODE: return "bad rotation, scale mode, variant or code format";
     case HQ_ERR_WORKSPACE: return "workspace missing or too small";
@@ -682,6 +704,7 @@ hq_status hq_rotated_stat(const void* src, const void* grad, int32_t dtype, int6
   if (stat != HQ_STAT_ABS_SUM && stat != HQ_STAT_QERR && stat != HQ_STAT_LSQ_GRAD)
     return HQ_ERR_MODE;
   if (stat == HQ_STAT_LSQ_GRAD && is_f8(cfg)) return HQ_ERR_MODE;
+  if (stat == HQ_STAT_QERR && is_fp6(cfg)) return HQ_ERR_MODE;   // E4M3 and integer grids only
   if (stat == HQ_STAT_LSQ_GRAD && rows * cols > 0 && !grad) return HQ_ERR_NULL;
   if (stat != HQ_STAT_ABS_SUM && !scale) return HQ_ERR_NULL;
   if (!out) return HQ_ERR_NULL;
@@ -717,6 +740,7 @@ hq_status hq_select_hadamard_k(const void* x, const void* w, int32_t dtype, int6
                                int32_t n_candidates, int32_t* k_best, double* errors, void* ws,
                                size_t ws_bytes, void* stream) {
   HQ_CHECK(check_cfg(cfg));
+  if (is_fp6(cfg)) return HQ_ERR_MODE;   // error passes on the E4M3 and integer grids only
   if (!valid_dt(dtype)) return HQ_ERR_DTYPE;
   if (N <= 0 || C <= 0 || D <= 0) return HQ_ERR_SHAPE;
   if (!x || !w || !candidates || !k_best) return HQ_ERR_NULL;

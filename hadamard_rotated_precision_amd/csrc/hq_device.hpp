@@ -306,17 +306,18 @@ __device__ inline float block_max(float x, float* red) {
 }
 
 // ---------------------------------------------------------------- quantizer
-// Scale of a tensor: the given step (STEP mode), or max(partials)/Qp (ABSMAX mode).
+// Scale of a tensor: the given step (STEP mode), or max(partials) / qmax (ABSMAX mode), qmax
+// the grid bound (Qp, or the largest value of a float code format: 448, 7.5, 28).
 // Every thread of the block returns the same (s, r = 1/s, or r = 0 when s == 0).
 __device__ inline void tensor_scale(const float* partials, int nparts, const float* step,
-                                    int qp, float* red, float& s, float& r) {
+                                    float qmax, float* red, float& s, float& r) {
   if (step != nullptr) {
     s = *step;
   } else {
     float a = 0.0f;
     for (int i = threadIdx.x; i < nparts; i += blockDim.x) a = fmaxf(a, partials[i]);
     a = block_max(a, red);
-    s = a / static_cast<float>(qp);   // correctly rounded fp32 division
+    s = a / qmax;   // correctly rounded fp32 division
   }
   r = (s > 0.0f) ? 1.0f / s : 0.0f;
 }
@@ -361,18 +362,64 @@ __device__ inline uint32_t e4m3_pack4(float v0, float v1, float v2, float v3, fl
   return static_cast<uint32_t>(w);
 }
 
-// Four codes of either format packed little-endian into one dword: integer codes through
-// qbits (lo, hi from qlo / qhi) or E4M3 codes (f8; lo and hi unused). f8 is uniform.
+// FP6 codes (OCP E2M3: 3 mantissa bits, smallest normal 1, largest 7.5; E3M2: 2 mantissa bits,
+// smallest normal 1/4, largest 28), kept as the E4M3 bytes of their values. x is already clamped
+// to the format's range; its magnitude is rounded to the grid, ties to even: below the smallest
+// normal a fixed step (1/8 or 1/16, the subnormals; rint is round to nearest even), above it the
+// fp32 significand cut to the format's mantissa bits (add half an ulp minus one plus the kept
+// lowest bit, then clear the dropped bits; a carry moves into the exponent as it should). The
+// result is an E4M3 value, so the hardware conversion that follows is exact.
+__device__ inline float fp6_round(float x, bool e3m2) {
+  const float ax = fabsf(x);
+  const float inv_step = e3m2 ? 16.0f : 8.0f, step = e3m2 ? 0.0625f : 0.125f;
+  const float sub = __builtin_rintf(ax * inv_step) * step;
+  const uint32_t drop = e3m2 ? 21u : 20u;   // 23 - mantissa bits
+  uint32_t u = __float_as_uint(ax);
+  u += ((1u << (drop - 1)) - 1u) + ((u >> drop) & 1u);
+  u &= ~((1u << drop) - 1u);
+  return __builtin_copysignf(ax < (e3m2 ? 0.25f : 1.0f) ? sub : __uint_as_float(u), x);
+}
+
+// Four float-format codes: v * r clamped to [-fmax, fmax], then, for the FP6 grids (grid 1 =
+// E2M3, 2 = E3M2; 0 = E4M3 itself), rounded to the grid before the E4M3 conversion. grid and
+// fmax are uniform.
+__device__ inline uint32_t fcode_pack4(float v0, float v1, float v2, float v3, float r,
+                                       float grid, float fmax) {
+  float x0 = __builtin_amdgcn_fmed3f(v0 * r, -fmax, fmax);
+  float x1 = __builtin_amdgcn_fmed3f(v1 * r, -fmax, fmax);
+  float x2 = __builtin_amdgcn_fmed3f(v2 * r, -fmax, fmax);
+  float x3 = __builtin_amdgcn_fmed3f(v3 * r, -fmax, fmax);
+  if (grid != 0.0f) {
+    const bool e3m2 = grid > 1.5f;
+    x0 = fp6_round(x0, e3m2);
+    x1 = fp6_round(x1, e3m2);
+    x2 = fp6_round(x2, e3m2);
+    x3 = fp6_round(x3, e3m2);
+  }
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
+  return static_cast<uint32_t>(w);
+}
+
+// Four codes of either kind packed little-endian into one dword: integer codes through qbits
+// (lo, hi from qlo / qhi), or float-format codes (f8: lo = the grid, 0 E4M3, 1 E2M3, 2 E3M2;
+// hi = the format's largest value; see float_bounds). f8 is uniform.
 __device__ inline uint32_t quant4(float v0, float v1, float v2, float v3, float r, float lo,
                                   float hi, bool f8) {
-  if (f8) return e4m3_pack4(v0, v1, v2, v3, r);
+  if (f8) return fcode_pack4(v0, v1, v2, v3, r, lo, hi);
   return qpack4(qbits(v0, r, lo, hi), qbits(v1, r, lo, hi), qbits(v2, r, lo, hi),
                 qbits(v3, r, lo, hi));
 }
 
-// One code byte of either format (two's complement integer, or E4M3).
-__device__ inline int quant_byte(float v, float r, int qp, bool f8) {
-  if (f8) return static_cast<int>(e4m3_pack4(v, 0.0f, 0.0f, 0.0f, r) & 0xFFu);
+// The (lo, hi) pair quant4 takes for float-format codes.
+__device__ inline void float_bounds(int grid, float fmax, float& lo, float& hi) {
+  lo = static_cast<float>(grid);
+  hi = fmax;
+}
+
+// One code byte of either kind (two's complement integer, or a float-format code as above).
+__device__ inline int quant_byte(float v, float r, int qp, bool f8, float grid, float fmax) {
+  if (f8) return static_cast<int>(fcode_pack4(v, 0.0f, 0.0f, 0.0f, r, grid, fmax) & 0xFFu);
   return quant_code(v, r, qp);
 }
 

@@ -64,8 +64,10 @@ struct ProPass {
   int in_dt = 0;
   int64_t rows = 0, cols = 0;
   int k = 1;                         // 1 with PRO_RIGHT = no rotation
-  int qp = 127;                      // grid bound (448 for E4M3 codes)
-  bool f8 = false;                   // FP8 E4M3 codes instead of integer codes
+  int qp = 127;                      // integer codes: the grid bound
+  bool f8 = false;                   // float-format codes (E4M3 bytes) instead of integer codes
+  float qmaxf = 127.0f;              // the scale's divisor: Qp, or the format's largest value
+  int fgrid = 0;                     // f8: 0 E4M3, 1 E2M3, 2 E3M2 (FP6 values as E4M3 bytes)
   float* partials = nullptr;         // kMaxPartials floats
   int nparts = 0;                    // QUANT: grid of the ABSMAX pass (pro_grid)
   const float* step = nullptr;       // STEP mode (PRO_BOTH: step of X B)

@@ -54,11 +54,13 @@ __device__ inline void load64(const void* row, int64_t c0, int64_t n, bool vec, 
 }
 
 // Pack 16 codes starting at v[i0] into a uint4 (integer codes, or E4M3 codes when f8).
-__device__ inline uint4 pack16(const float (&v)[64], int i0, float r, int qp, bool f8) {
+__device__ inline uint4 pack16(const float (&v)[64], int i0, float r, int qp, bool f8, float grid,
+                              float fmax) {
   uint32_t w[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    w[j] = f8 ? e4m3_pack4(v[i0 + 4 * j], v[i0 + 4 * j + 1], v[i0 + 4 * j + 2], v[i0 + 4 * j + 3], r)
+    w[j] = f8 ? fcode_pack4(v[i0 + 4 * j], v[i0 + 4 * j + 1], v[i0 + 4 * j + 2], v[i0 + 4 * j + 3], r,
+                            grid, fmax)
               : pack4(quant_code(v[i0 + 4 * j], r, qp), quant_code(v[i0 + 4 * j + 1], r, qp),
                       quant_code(v[i0 + 4 * j + 2], r, qp), quant_code(v[i0 + 4 * j + 3], r, qp));
   return make_uint4(w[0], w[1], w[2], w[3]);
@@ -74,7 +76,9 @@ struct ProArgs {
   int nparts;
   const float* step;        // QUANT, STEP mode (right / left rotation, or X B for both_kernel)
   const float* step2;       // both_kernel, STEP mode: step of B X B
-  int qp;                   // grid bound: 127 / 7 for integer codes, 448 for E4M3 codes
+  int qp;                   // integer codes: the grid bound 127 / 7
+  float qmaxf;              // the scale's divisor: Qp, or the float format's largest value
+  int fgrid;                // float-format codes: 0 E4M3, 1 E2M3, 2 E3M2 (FP6, as E4M3 bytes)
   float* scale_out;
   float* scale_out2;        // both_kernel: scale of B X B
   int8_t* codes;            // row-major codes (pitch ld) or nullptr
@@ -98,6 +102,17 @@ constexpr int kBarGroups = 8, kBarStride = 32, kGroupDone = 256, kReleaseWord = 
 // A quantize pass (integer or FP8 codes).
 __host__ __device__ constexpr bool quant_op(int op) { return op == OP_QUANT || op == OP_QUANT_F8; }
 
+// The (lo, hi) pair quant4 takes: the integer clamp bounds, or for float-format codes the grid
+// and the format's largest value.
+template <int OP>
+__device__ inline float code_lo(const ProArgs& a) {
+  return OP == OP_QUANT_F8 ? static_cast<float>(a.fgrid) : qlo(a.qp);
+}
+template <int OP>
+__device__ inline float code_hi(const ProArgs& a) {
+  return OP == OP_QUANT_F8 ? a.qmaxf : qhi(a.qp);
+}
+
 // Counters a later launch on the stream needs at zero (the split-K arrivals of the GEMM).
 __device__ inline void zero_side(const ProArgs& a) {
   if (a.zero_n > 0 && blockIdx.x == 0)
@@ -117,7 +132,7 @@ __global__ __launch_bounds__(RT_THREADS) void right_kernel(ProArgs a) {
   const int64_t tiles = nrt * nct;
   float sc = 0.0f, rinv = 0.0f;
   if constexpr (quant_op(OP)) {
-    tensor_scale(a.part_in, a.nparts, a.step, a.qp, red, sc, rinv);
+    tensor_scale(a.part_in, a.nparts, a.step, a.qmaxf, red, sc, rinv);
     zero_side(a);
     if (blockIdx.x == 0 && t == 0) *a.scale_out = sc;
   }
@@ -146,13 +161,13 @@ __global__ __launch_bounds__(RT_THREADS) void right_kernel(ProArgs a) {
         const int64_t cpad = (a.cols + 15) / 16 * 16;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          if (gc + 16 * q < cpad) *reinterpret_cast<uint4*>(dst + 16 * q) = pack16(v, 16 * q, rinv, a.qp, (OP == OP_QUANT_F8));
+          if (gc + 16 * q < cpad) *reinterpret_cast<uint4*>(dst + 16 * q) = pack16(v, 16 * q, rinv, a.qp, (OP == OP_QUANT_F8), static_cast<float>(a.fgrid), a.qmaxf);
       }
       if (a.codes_t) {
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < 64; ++j)
-          tcodes[64 * s + j][r] = static_cast<int8_t>(quant_byte(v[j], rinv, a.qp, (OP == OP_QUANT_F8)));
+          tcodes[64 * s + j][r] = static_cast<int8_t>(quant_byte(v[j], rinv, a.qp, (OP == OP_QUANT_F8), static_cast<float>(a.fgrid), a.qmaxf));
         __syncthreads();
         // thread t writes transposed row col0 + t: 64 bytes = tile rows row0 .. row0+63
         const int64_t orow = col0 + t;
@@ -318,13 +333,13 @@ __global__ __launch_bounds__(RF_THREADS) void right_fast_kernel(ProArgs a) {
   const uint32_t tiles = static_cast<uint32_t>(a.rows / RF_ROWS) * nct;   // < 2^31 (host checks)
   float sc = 0.0f, rinv = 0.0f;
   if constexpr (quant_op(OP)) {
-    tensor_scale(a.part_in, a.nparts, a.step, a.qp, red, sc, rinv);
+    tensor_scale(a.part_in, a.nparts, a.step, a.qmaxf, red, sc, rinv);
     zero_side(a);
     if (blockIdx.x == 0 && t == 0) *a.scale_out = sc;
   }
   constexpr int XMASK = K > 16 ? 3 : (K > 8 ? 1 : 0);
   const float rr = (__builtin_popcount(lane & XMASK) & 1) ? -rinv : rinv;
-  const float lo = qlo(a.qp), hi = qhi(a.qp);
+  const float lo = code_lo<OP>(a), hi = code_hi<OP>(a);
   const float sg1 = (lane & 1) ? -1.0f : 1.0f, sg2 = (lane & 2) ? -1.0f : 1.0f;
   constexpr int NQ = 4 * In::bytes;      // 16-byte chunks per thread per tile
   constexpr int PER = 16 / In::bytes;    // elements per chunk
@@ -579,11 +594,11 @@ __global__ __launch_bounds__(RM_THREADS, 2) void right_mma_kernel(ProArgs a) {
     const uint32_t tiles = static_cast<uint32_t>(a.rows / RM_ROWS) * nct;   // < 2^31 (host checks)
     float sc = 0.0f, rinv = 0.0f;
     if constexpr (quant_op(OP)) {
-      tensor_scale(a.part_in, a.nparts, a.step, a.qp, red, sc, rinv);
+      tensor_scale(a.part_in, a.nparts, a.step, a.qmaxf, red, sc, rinv);
       zero_side(a);
       if (blockIdx.x == 0 && t == 0) *a.scale_out = sc;
     }
-    const float lo = qlo(a.qp), hi = qhi(a.qp);
+    const float lo = code_lo<OP>(a), hi = code_hi<OP>(a);
     uint4 G[4];
     hfrags<In, (K < 64 ? K : 64)>(lane, G);
     const char* src = static_cast<const char*>(a.src);
@@ -730,7 +745,7 @@ __global__ __launch_bounds__(LT_THREADS) void left_kernel(ProArgs a) {
   const int64_t tiles = nrt * nct;
   float sc = 0.0f, rinv = 0.0f;
   if constexpr (quant_op(OP)) {
-    tensor_scale(a.part_in, a.nparts, a.step, a.qp, red, sc, rinv);
+    tensor_scale(a.part_in, a.nparts, a.step, a.qmaxf, red, sc, rinv);
     zero_side(a);
     if (blockIdx.x == 0 && t == 0) *a.scale_out = sc;
   }
@@ -790,13 +805,13 @@ __global__ __launch_bounds__(LT_THREADS) void left_kernel(ProArgs a) {
         int8_t* dst = a.codes_t + gcol * a.ld_t + row0 + 64 * p;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          if (row0 + 64 * p + 16 * q < rpad) *reinterpret_cast<uint4*>(dst + 16 * q) = pack16(v, 16 * q, rinv, a.qp, (OP == OP_QUANT_F8));
+          if (row0 + 64 * p + 16 * q < rpad) *reinterpret_cast<uint4*>(dst + 16 * q) = pack16(v, 16 * q, rinv, a.qp, (OP == OP_QUANT_F8), static_cast<float>(a.fgrid), a.qmaxf);
       }
       if (a.codes) {
         __syncthreads();   // the fp32 tile is dead: reuse it for the byte transpose
 #pragma unroll
         for (int i = 0; i < 64; ++i)
-          bcodes[(64 * p + i) * BP + c] = static_cast<int8_t>(quant_byte(v[i], rinv, a.qp, (OP == OP_QUANT_F8)));
+          bcodes[(64 * p + i) * BP + c] = static_cast<int8_t>(quant_byte(v[i], rinv, a.qp, (OP == OP_QUANT_F8), static_cast<float>(a.fgrid), a.qmaxf));
         __syncthreads();
         for (int q = t; q < TR * TC / 16; q += LT_THREADS) {
           const int row = q / (TC / 16), cc = 16 * (q % (TC / 16));
@@ -850,13 +865,13 @@ __global__ __launch_bounds__(LF_THREADS, 2) void left_fast_kernel(ProArgs a) {
   const uint32_t tiles = static_cast<uint32_t>(a.rows / LF_ROWS) * nct;   // < 2^31 (host checks)
   float sc = 0.0f, rinv = 0.0f;
   if constexpr (quant_op(OP)) {
-    tensor_scale(a.part_in, a.nparts, a.step, a.qp, red, sc, rinv);
+    tensor_scale(a.part_in, a.nparts, a.step, a.qmaxf, red, sc, rinv);
     zero_side(a);
     if (blockIdx.x == 0 && t == 0) *a.scale_out = sc;
   }
   constexpr int XMASK = K > 128 ? 3 : (K > 64 ? 1 : 0);
   const float rr = (__builtin_popcount(lane & XMASK) & 1) ? -rinv : rinv;
-  const float lo = qlo(a.qp), hi = qhi(a.qp);
+  const float lo = code_lo<OP>(a), hi = code_hi<OP>(a);
   const float sg1 = (lane & 1) ? -1.0f : 1.0f, sg2 = (lane & 2) ? -1.0f : 1.0f;
   const char* src = static_cast<const char*>(a.src);
   // global loads: eight 16-byte chunks per thread, row 32 q + t / 8, columns 8 (t % 8) + [0, 8)
@@ -1010,11 +1025,11 @@ __global__ __launch_bounds__(LM_THREADS, 2) void left_mma_kernel(ProArgs a) {
     const uint32_t tiles = static_cast<uint32_t>(a.rows / LM_ROWS) * nct;   // < 2^31 (host checks)
     float sc = 0.0f, rinv = 0.0f;
     if constexpr (quant_op(OP)) {
-      tensor_scale(a.part_in, a.nparts, a.step, a.qp, red, sc, rinv);
+      tensor_scale(a.part_in, a.nparts, a.step, a.qmaxf, red, sc, rinv);
       zero_side(a);
       if (blockIdx.x == 0 && t == 0) *a.scale_out = sc;
     }
-    const float lo = qlo(a.qp), hi = qhi(a.qp);
+    const float lo = code_lo<OP>(a), hi = code_hi<OP>(a);
     uint4 G[4];
     hfrags<In, (K < 64 ? K : 64)>(lane, G);
     const char* src = static_cast<const char*>(a.src);
@@ -1250,15 +1265,15 @@ __global__ __launch_bounds__(BT_THREADS) void both_kernel(ProArgs a) {
   const int64_t items = both_items(a.rows, a.cols);
   float s1 = 0.0f, r1 = 0.0f, sc2 = 0.0f, r2 = 0.0f;
   if constexpr (quant_op(OP)) {
-    tensor_scale(a.part_in, a.nparts, a.step, a.qp, red, s1, r1);
-    tensor_scale(a.part_in2, a.nparts, a.step2, a.qp, red, sc2, r2);
+    tensor_scale(a.part_in, a.nparts, a.step, a.qmaxf, red, s1, r1);
+    tensor_scale(a.part_in2, a.nparts, a.step2, a.qmaxf, red, sc2, r2);
     zero_side(a);
     if (blockIdx.x == 0 && t == 0) {
       *a.scale_out = s1;
       *a.scale_out2 = sc2;
     }
   }
-  const float lo = qlo(a.qp), hi = qhi(a.qp);
+  const float lo = code_lo<OP>(a), hi = code_hi<OP>(a);
   const int64_t rpad = (a.rows + 15) / 16 * 16, cpad = (a.cols + 15) / 16 * 16;
   const char* src = static_cast<const char*>(a.src);
   float amax1 = 0.0f, amax2 = 0.0f;
@@ -1419,15 +1434,15 @@ __device__ inline void both_mma_body(const ProArgs& a) {
       if (a.bar != nullptr && __hip_atomic_load(&a.bar[kReleaseWord], __ATOMIC_RELAXED,
                                                 __HIP_MEMORY_SCOPE_AGENT) != kStateAborted)
         return;
-      tensor_scale(a.part_in, a.nparts, a.step, a.qp, red, s1, r1);
-      tensor_scale(a.part_in2, a.nparts, a.step2, a.qp, red, sc2, r2);
+      tensor_scale(a.part_in, a.nparts, a.step, a.qmaxf, red, s1, r1);
+      tensor_scale(a.part_in2, a.nparts, a.step2, a.qmaxf, red, sc2, r2);
       zero_side(a);
       if (blockIdx.x == 0 && t == 0) {
         *a.scale_out = s1;
         *a.scale_out2 = sc2;
       }
     }
-    const float lo = qlo(a.qp), hi = qhi(a.qp);
+    const float lo = code_lo<OP>(a), hi = code_hi<OP>(a);
     constexpr int KM = K < 64 ? K : 64;
     constexpr int NKS = K > 128 ? 8 : 4;    // 32-column slices read per row block
     constexpr int NNB = K > 128 ? 16 : 8;   // 16-column output blocks computed
@@ -1738,7 +1753,7 @@ struct BothItem {
     int64_t row0, col0;
     int h;
     decode(it, row0, col0, h);
-    const float lo = qlo(a.qp), hi = qhi(a.qp);
+    const float lo = code_lo<F8 ? OP_QUANT_F8 : OP_QUANT>(a), hi = code_hi<F8 ? OP_QUANT_F8 : OP_QUANT>(a);
     const int i = n0 & 3, m = n0 >> 2;
     uint32_t rc[2][8];
     if (a.codes) {
@@ -1857,7 +1872,7 @@ __global__ __launch_bounds__(BM_THREADS) void both_single_kernel(ProArgs a) {
     }
     p1 = block_max(p1, red);
     p2 = block_max(p2, red);
-    const float s1 = p1 / static_cast<float>(a.qp), s2 = p2 / static_cast<float>(a.qp);
+    const float s1 = p1 / a.qmaxf, s2 = p2 / a.qmaxf;
     const float r1 = (s1 > 0.0f) ? 1.0f / s1 : 0.0f, r2 = (s2 > 0.0f) ? 1.0f / s2 : 0.0f;
     if (wg == 0 && t == 0) {
       *a.scale_out = s1;
@@ -1953,6 +1968,8 @@ static ProArgs pro_args(const ProPass& p) {
   a.step = p.step;
   a.step2 = p.step2;
   a.qp = p.qp;
+  a.qmaxf = p.qmaxf;
+  a.fgrid = p.fgrid;
   a.scale_out = p.scale_out;
   a.scale_out2 = p.scale_out2;
   a.codes = p.codes;

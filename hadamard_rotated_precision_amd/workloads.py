@@ -20,7 +20,7 @@ import numpy as np
 F32, F16, BF16 = 0, 1, 2
 HALO0, HQ, HALO2 = 0, 1, 2
 ABSMAX, STEP = 0, 1
-INT, E4M3 = 0, 1                 # code formats
+INT, E4M3, E2M3, E3M2 = 0, 1, 2, 3   # code formats (E2M3 / E3M2: FP6)
 DTYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16"}
 
 
@@ -104,17 +104,19 @@ def make_batched_inputs(cfg):
 
 def config(cfg_id, **overrides):
     """A copy of a workload definition; shape keys (N, C, D) may be overridden to draw a
-    smaller tensor with the same distributions, and fmt=E4M3 gives the same layer with FP8
-    codes (its name then says fp8)."""
+    smaller tensor with the same distributions, and fmt=E4M3 / E2M3 / E3M2 gives the same layer
+    with FP8 or FP6 codes (its name then says fp8, fp6e2m3 or fp6e3m2; FP6 codes are 6 bits)."""
     cfg = dict(CONFIGS[cfg_id])
     cfg["id"] = cfg_id
     cfg["fmt"] = INT
     cfg.update(overrides)
-    if cfg["fmt"] == E4M3:
-        if cfg["bits"] != 8 or cfg["mode"] != ABSMAX:
-            raise ValueError("FP8 codes are defined for the 8-bit absmax workloads")
+    if cfg["fmt"] != INT:
+        if CONFIGS[cfg_id]["bits"] != 8 or cfg["mode"] != ABSMAX:
+            raise ValueError("float codes are defined for the 8-bit absmax workloads")
+        tag = {E4M3: "fp8", E2M3: "fp6e2m3", E3M2: "fp6e3m2"}[cfg["fmt"]]
+        cfg["bits"] = 8 if cfg["fmt"] == E4M3 else 6
         base = CONFIGS[cfg_id]["name"]
-        cfg["name"] = base.replace("halo2_", "halo2_fp8_").replace("hqmm_", "hqmm_fp8_")
+        cfg["name"] = base.replace("halo2_", "halo2_%s_" % tag).replace("hqmm_", "hqmm_%s_" % tag)
     return cfg
 
 

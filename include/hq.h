@@ -100,12 +100,21 @@ typedef enum { HQ_VARIANT_HALO0 = 0, HQ_VARIANT_HQ = 1, HQ_VARIANT_HALO2 = 2 } h
  * E4M3: FP8 codes in the OCP E4M3 format (sign, 4-bit exponent with bias 7, 3-bit mantissa,
  *       subnormals, largest value 448, 0x7F/0xFF unused); bits must be 8. ABSMAX: s =
  *       absmax/448; a code is the E4M3 value nearest to v * fp32(1/s) (ties to even), saturating
- *       at +-448. The GEMM multiplies the codes on the matrix cores with fp32 accumulation. */
-typedef enum { HQ_FMT_INT = 0, HQ_FMT_E4M3 = 1 } hq_format;
+ *       at +-448. The GEMM multiplies the codes on the matrix cores with fp32 accumulation.
+ * E2M3, E3M2: FP6 codes (the same page's FP6 variants; it does not give the layout, so both OCP
+ *       6-bit formats): E2M3 has a 2-bit exponent with bias 1 and a 3-bit mantissa, largest
+ *       value 7.5; E3M2 a 3-bit exponent with bias 3 and a 2-bit mantissa, largest value 28;
+ *       both have subnormals and no reserved patterns. bits must be 6. ABSMAX: s = absmax/7.5
+ *       or absmax/28; a code is the FP6 value nearest to v * fp32(1/s) (ties to even),
+ *       saturating. Every FP6 value is an E4M3 value, so a code is stored as the E4M3 byte of
+ *       its value (one byte per code, like E4M3 codes) and the E4M3 GEMM multiplies them
+ *       exactly: the FP8 product stands in for an FP6 one, as on the page. hq_rotated_stat's
+ *       error sum and hq_select_hadamard_k take integer or E4M3 codes only. */
+typedef enum { HQ_FMT_INT = 0, HQ_FMT_E4M3 = 1, HQ_FMT_E2M3 = 2, HQ_FMT_E3M2 = 3 } hq_format;
 
 typedef struct {
   int32_t k;          /* Hadamard block size, power of two in [1, 256] (16..256 in practice) */
-  int32_t bits;       /* 8 (INT8, Qp = 127; or E4M3) or 4 (INT4 range [-7, 7], stored as int8) */
+  int32_t bits;       /* 8 (INT8, Qp = 127; or E4M3), 4 (INT4 range [-7, 7], stored as int8), 6 (FP6) */
   int32_t scale_mode; /* hq_scale_mode */
   int32_t variant;    /* hq_variant */
   int32_t format;     /* hq_format */

@@ -38,13 +38,33 @@ def rel_fro(a, b):
     return float(np.linalg.norm(a - b) / nb)
 
 
+_FP6_GRID = {}
+
+
+def fp6_grid(fmt):
+    """The non-negative values of an FP6 format, increasing (the oracle's grid, pinned against
+    the hand-listed one in the FP6 pins)."""
+    if fmt not in _FP6_GRID:
+        top = O.fp6_max(fmt)
+        sweep = np.linspace(0.0, top, 20001)
+        _FP6_GRID[fmt] = np.unique(O.decode_e4m3(O.quantize_fp6(sweep, 1.0, fmt)))
+    return _FP6_GRID[fmt]
+
+
 def code_steps(codes, fmt=O.INT):
-    """Codes as positions on their grid: the integer itself, or for E4M3 bytes the signed
-    magnitude code (adjacent grid values are one apart; +0 and -0 are both 0)."""
+    """Codes as positions on their grid: the integer itself, for E4M3 bytes the signed
+    magnitude code, for FP6 codes (kept as E4M3 bytes) the signed position on the FP6 grid
+    (adjacent grid values are one apart; +0 and -0 are both 0)."""
     if fmt == O.E4M3:
         c = np.asarray(codes).view(np.uint8).astype(np.int16)
         mag = c & 0x7F
         return np.where(c & 0x80, -mag, mag)
+    if fmt in (O.E2M3, O.E3M2):
+        v = O.decode_e4m3(np.asarray(codes).view(np.uint8))
+        grid = fp6_grid(fmt)
+        pos = np.searchsorted(grid, np.abs(v))
+        assert (grid[np.minimum(pos, grid.size - 1)] == np.abs(v)).all(), "a code off the FP6 grid"
+        return np.where(v < 0, -pos, pos).astype(np.int16)
     return np.asarray(codes).astype(np.int16)
 
 
@@ -209,7 +229,7 @@ def outputs_from_gpu_codes(cfg, h):
     """The oracle's products evaluated on the GPU's own codes and scales (isolates the
     GEMM + epilogue from code flips)."""
     k, v, f = cfg["k"], cfg["variant"], cfg.get("fmt", O.INT)
-    cv = (lambda q: np.asarray(q).view(np.uint8)) if f == O.E4M3 else (lambda q: q)
+    cv = (lambda q: np.asarray(q).view(np.uint8)) if f in O.FLOAT_FORMATS else (lambda q: q)
     out = {"y": O.fwd_from_codes(cv(h["qx"]), h["sx"], cv(h["qw"]), h["sw"], k, v, fmt=f)}
     if "qg" in h:
         if "dx" in h:
@@ -223,3 +243,46 @@ def outputs_from_gpu_codes(cfg, h):
                 out["dw"] = O.bwd_weight_from_codes(cv(h["qg"]), h["sg"], cv(h["qx"]), h["sx"],
                                                     k, v, fmt=f)
     return out
+
+
+def fullsize_sampled(cfg, seed):
+    """A workload's whole step at its full size: codes and scales compared in full against the
+    oracle's, outputs on sampled rows / k-aligned blocks against the oracle's exact values on
+    its own codes. The format and the code width come from cfg."""
+    N, C, D, k, v = cfg["N"], cfg["C"], cfg["D"], cfg["k"], cfg["variant"]
+    bits, f = cfg["bits"], cfg.get("fmt", O.INT)
+    out_dt = cfg["out_dtype"]
+    inputs = WL.make_inputs(cfg)
+    res = run_gpu(cfg, inputs)
+    L = res["layer"]
+    X = O.decode(inputs["x"], cfg["in_dtype"])
+    qx, sx, qxt, sxt = O.quantize_x(X, k, bits, v, fmt=f)
+    del X
+    assert_codes(L.qx.codes_view().cpu().numpy(), qx, "qX", f)
+    assert_scale(float(L.qx.scale.cpu()[0]), sx, "sX")
+    assert_codes(L.qxt.codes_t_view().cpu().numpy().T, qxt, "qXt", f)
+    assert_scale(float(L.qxt.scale.cpu()[0]), sxt, "sXt")
+    W = O.decode(inputs["w"], cfg["in_dtype"])
+    qw, sw = O.quantize_w(W, k, bits, v, fmt=f)
+    del W
+    assert_codes(L.qw.codes_view().cpu().numpy(), qw, "qW", f)
+    G = O.decode(inputs["dy"], cfg["in_dtype"])
+    qg, sg = O.quantize_g(G, k, bits, v, fmt=f)
+    del G
+    assert_codes(L.qg.codes_view().cpu().numpy(), qg, "qG", f)
+    rng = np.random.default_rng(seed)
+    rs = np.sort(rng.choice(N, 128, replace=False))
+    cs = np.sort(rng.choice(D, 128, replace=False))
+    y = O.decode(T.bits_of(res["y"][rs][:, cs].contiguous()), out_dt)
+    assert_out(y, O.fwd_from_codes(qx, sx, qw, sw, k, v, rows=rs, cols=cs, fmt=f), out_dt, "Y")
+    for _ in range(2):
+        r0, c0 = int(rng.integers(0, N // k)) * k, int(rng.integers(0, C // k)) * k
+        ref = O.bwd_input_from_codes(qg, sg, qw, sw, k, v, row_block=(r0, k), col_block=(c0, k),
+                                     fmt=f)
+        got = O.decode(T.bits_of(res["dx"][r0:r0 + k, c0:c0 + k].contiguous()), out_dt)
+        assert_out(got, ref, out_dt, "dX block (%d, %d)" % (r0, c0))
+        r0, c0 = int(rng.integers(0, D - 64 + 1)), int(rng.integers(0, C // k)) * k
+        ref = O.bwd_weight_from_codes(qg, sg, qxt, sxt, k, v, row_block=(r0, 64),
+                                      col_block=(c0, k), fmt=f)
+        got = O.decode(T.bits_of(res["dw"][r0:r0 + 64, c0:c0 + k].contiguous()), out_dt)
+        assert_out(got, ref, out_dt, "dW block (%d, %d)" % (r0, c0))

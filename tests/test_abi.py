@@ -53,9 +53,9 @@ def test_version_status_pitch():
     assert B.hq_code_pitch(33) == 48
 
 
-def cfg(k=32, bits=8, mode=B.HQ_SCALE_ABSMAX, variant=B.HQ_VARIANT_HALO2):
+def cfg(k=32, bits=8, mode=B.HQ_SCALE_ABSMAX, variant=B.HQ_VARIANT_HALO2, fmt=B.HQ_FMT_INT):
     c = B.hq_config()
-    c.k, c.bits, c.scale_mode, c.variant = k, bits, mode, variant
+    c.k, c.bits, c.scale_mode, c.variant, c.format = k, bits, mode, variant, fmt
     return c
 
 
@@ -91,6 +91,11 @@ def rq(**kw):
     (dict(cfg=cfg(k=512)), "HQ_ERR_K"),
     (dict(cfg=cfg(k=0)), "HQ_ERR_K"),
     (dict(cfg=cfg(bits=5)), "HQ_ERR_BITS"),
+    (dict(cfg=cfg(bits=6)), "HQ_ERR_BITS"),                 # 6 bits only for FP6 codes
+    (dict(cfg=cfg(bits=8, fmt=B.HQ_FMT_E2M3)), "HQ_ERR_BITS"),
+    (dict(cfg=cfg(bits=4, fmt=B.HQ_FMT_E3M2)), "HQ_ERR_BITS"),
+    (dict(cfg=cfg(bits=6, fmt=B.HQ_FMT_E4M3)), "HQ_ERR_BITS"),
+    (dict(cfg=cfg(bits=6, fmt=4)), "HQ_ERR_MODE"),
     (dict(cfg=cfg(mode=7)), "HQ_ERR_MODE"),
     (dict(cfg=cfg(variant=3)), "HQ_ERR_MODE"),
     (dict(src_dtype=9), "HQ_ERR_DTYPE"),
@@ -115,6 +120,27 @@ def rq(**kw):
 ])
 def test_rotate_quantize_validation(kw, expect):
     assert B.STATUS_NAMES[rq(**kw)] == expect
+
+
+@pytest.mark.parametrize("fmt", [B.HQ_FMT_E2M3, B.HQ_FMT_E3M2])
+def test_fp6_codes_pass_the_checks(fmt):
+    """FP6 configurations pass every argument check and stop only at the device check."""
+    assert B.STATUS_NAMES[rq(cfg=cfg(bits=6, fmt=fmt))] == "HQ_ERR_DEVICE"
+
+
+@pytest.mark.parametrize("fmt", [B.HQ_FMT_E2M3, B.HQ_FMT_E3M2])
+def test_fp6_statistics_are_refused(fmt):
+    """The error sum and the Hadamard-size selection run on the integer and E4M3 grids only."""
+    c = cfg(k=32, bits=6, fmt=fmt, variant=B.HQ_VARIANT_HQ)
+    out = ctypes.c_double()
+    r = B.hq_rotated_stat(FAKE, None, B.HQ_BF16, 64, 64, B.HQ_ROT_RIGHT, c, B.HQ_STAT_QERR, FAKE,
+                          ctypes.addressof(out), FAKE, 1 << 30, None)
+    assert B.STATUS_NAMES[r] == "HQ_ERR_MODE"
+    carr = (ctypes.c_int32 * 1)(32)
+    kb = ctypes.c_int32(0)
+    r = B.hq_select_hadamard_k(FAKE, FAKE, B.HQ_BF16, 64, 64, 64, c, carr, 1, kb, None, FAKE,
+                               1 << 30, None)
+    assert B.STATUS_NAMES[r] == "HQ_ERR_MODE"
 
 
 def fwd(**kw):

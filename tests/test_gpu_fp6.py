@@ -1,0 +1,119 @@
+"""GPU parity of the FP6 (E2M3, E3M2) variants of the path against the oracle, through the C ABI.
+
+The HALO summary page runs the three matmuls in FP6 as well as FP8 and INT8 (Key results), FP8
+matmuls standing in for FP6 where the hardware has none (Limitations). The library keeps an FP6
+code as the E4M3 byte of its value, so the FP8 GEMM multiplies FP6 codes exactly. Codes: at most
+one FP6 grid step apart on at most 1e-4 of the entries (the GPU decides v * fp32(1/s) and cuts
+the fp32 significand to the format, the oracle compares the exact quotient with the midpoints);
+outputs as for INT8 and FP8 (hq_testlib.out_bound), the products held to the floating-point bound.
+"""
+import numpy as np
+import pytest
+
+import oracle as O
+from hadamard_rotated_precision_amd import binding as B
+from hadamard_rotated_precision_amd import workloads as WL
+
+from hq_testlib import (assert_out, compare_layer, fp6_grid, fullsize_sampled, host,
+                        outputs_from_gpu_codes, rel_fro, run_gpu, run_oracle)
+
+pytestmark = pytest.mark.gpu
+FMTS = {"e2m3": WL.E2M3, "e3m2": WL.E3M2}
+
+REDUCED = {
+    2: dict(N=512, C=1024, D=768),
+    5: dict(N=256, C=1408, D=640),
+}
+
+
+def banner(*a):
+    print("[case]", *a, flush=True)
+
+
+@pytest.mark.parametrize("name", ["e2m3", "e3m2"])
+@pytest.mark.parametrize("cid", [2, 5])
+@pytest.mark.parametrize("out_dt", [None, O.F32])
+def test_fp6_layer_parity_reduced(name, cid, out_dt):
+    cfg = WL.config(cid, fmt=FMTS[name], **REDUCED[cid])
+    odt = cfg["out_dtype"] if out_dt is None else out_dt
+    banner("fp6-layer", cfg["name"], cfg["N"], cfg["C"], cfg["D"], odt)
+    inputs = WL.make_inputs(cfg)
+    res = run_gpu(cfg, inputs, out_dt=odt)
+    h = host(res, odt)
+    ora = run_oracle(cfg, inputs)
+    compare_layer(cfg, h, ora, odt)
+    for out_name, ref in outputs_from_gpu_codes(cfg, h).items():
+        assert_out(h[out_name], ref, odt, out_name + " (GPU codes)")
+
+
+@pytest.mark.parametrize("name", ["e2m3", "e3m2"])
+@pytest.mark.parametrize("k", [16, 64])
+def test_fp6_grid_aligned_codes_exact(name, k):
+    """X = A B_C / k with A on the FP6 grid (one entry at the largest value), given in fp32,
+    which holds X exactly. The forward quantizes X B_C back to A with s = 1 bit for bit,
+    subnormals and ties of the grid included, and Y equals X W^T up to the fp32 summation of the
+    matrix cores."""
+    fmt = FMTS[name]
+    banner("fp6-grid", name, k)
+    rng = np.random.default_rng(70 + k + fmt)
+    N, C, D = 512, 512, 256
+    grid = fp6_grid(fmt)[1:]
+
+    def draw(shape):
+        v = rng.choice(grid, size=shape) * rng.choice([-1.0, 1.0], size=shape)
+        v[0, 0] = grid[-1]
+        return v
+    A, Bm = draw((N, C)), draw((D, C))
+    H = np.kron(np.eye(C // k), O.hadamard(k).astype(np.float64))
+    X, W = A @ H / k, Bm @ H / k
+    cfg = dict(WL.config(2, N=N, C=C, D=D, k=k, variant=B.HQ_VARIANT_HQ, fmt=fmt),
+               in_dtype=WL.F32, passes=("fwd",))
+    inputs = {"x": WL.to_dtype_bits(X, WL.F32), "w": WL.to_dtype_bits(W, WL.F32), "dy": None}
+    np.testing.assert_array_equal(O.decode(inputs["x"], WL.F32), X)
+    res = run_gpu(cfg, inputs, out_dt=O.F32)
+    h = host(res, O.F32)
+    np.testing.assert_array_equal(O.decode_e4m3(h["qx"].view(np.uint8)), A)
+    np.testing.assert_array_equal(O.decode_e4m3(h["qw"].view(np.uint8)), Bm)
+    assert h["sx"] == h["sw"] == 1.0
+    err = rel_fro(h["y"], X @ W.T)
+    print("[fp6-grid] Y rel fro %.3g" % err, flush=True)
+    assert err <= 1e-3
+
+
+@pytest.mark.parametrize("name", ["e2m3", "e3m2"])
+def test_fp6_midpoints_round_to_even(name):
+    """Every midpoint of two neighbouring FP6 values, times a power-of-two step (so v * fp32(1/s)
+    is the exact quotient on the GPU), lands on the even neighbour; the grid values themselves
+    stay put and values beyond the largest one saturate: the codes equal the oracle's one for
+    one, in STEP mode without rotation."""
+    fmt = FMTS[name]
+    banner("fp6-ties", name)
+    grid = fp6_grid(fmt)
+    mids = (grid[:-1] + grid[1:]) / 2
+    vals = np.concatenate([grid, mids, [grid[-1] * 1.01, grid[-1] * 40.0]])
+    vals = np.concatenate([vals, -vals])
+    C = 256
+    V = np.zeros((8, C))
+    V.flat[:vals.size] = vals
+    step = 0.5
+    cfg = dict(WL.config(2, N=8, C=C, D=8, k=1, variant=B.HQ_VARIANT_HALO0, fmt=fmt),
+               in_dtype=WL.F32, passes=("fwd",), mode=WL.STEP)
+    inputs = {"x": WL.to_dtype_bits(V * step, WL.F32),
+              "w": WL.to_dtype_bits(np.eye(8, C), WL.F32), "dy": None,
+              "steps": {"x": step, "w": 1.0}}
+    res = run_gpu(cfg, inputs, out_dt=O.F32)
+    h = host(res, O.F32)
+    assert h["sx"] == step
+    ref = O.quantize_fp6(O.decode(inputs["x"], WL.F32), np.float32(step), fmt)
+    np.testing.assert_array_equal(h["qx"].view(np.uint8), ref)
+    np.testing.assert_array_equal(np.abs(O.decode_e4m3(ref[0, :grid.size])), grid)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["e2m3", "e3m2"])
+def test_fp6_fullsize_2048x4096x4096_sampled(name):
+    """The FP6 HALO-2 step at 2048 x 4096 x 4096 (k = 256): codes and scales in full, outputs on
+    sampled rows / k-aligned blocks against the oracle's exact values."""
+    cfg = WL.config(2, fmt=FMTS[name])
+    banner("fp6-fullsize", cfg["name"])
+    fullsize_sampled(cfg, 3100 + cfg["fmt"])

@@ -16,8 +16,8 @@ from hadamard_rotated_precision_amd import binding as B
 from hadamard_rotated_precision_amd import tensors as T
 from hadamard_rotated_precision_amd import workloads as WL
 
-from hq_testlib import (assert_codes, assert_out, assert_scale, compare_layer, host,
-                        outputs_from_gpu_codes, rel_fro, run_gpu, run_oracle)
+from hq_testlib import (compare_layer, fullsize_sampled, host, outputs_from_gpu_codes, rel_fro,
+                        run_gpu, run_oracle, assert_out)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -119,41 +119,5 @@ def test_fp8_fullsize_2048x4096x4096_sampled():
     """The FP8 HALO-2 step at 2048 x 4096 x 4096 (k = 256): codes and scales in full,
     outputs on sampled rows / k-aligned blocks against the oracle's exact values."""
     cfg = WL.config(2, fmt=WL.E4M3)
-    N, C, D, k, v = cfg["N"], cfg["C"], cfg["D"], cfg["k"], cfg["variant"]
-    out_dt = cfg["out_dtype"]
     banner("fp8-fullsize", cfg["name"])
-    inputs = WL.make_inputs(cfg)
-    res = run_gpu(cfg, inputs)
-    L = res["layer"]
-    f = O.E4M3
-    X = O.decode(inputs["x"], cfg["in_dtype"])
-    qx, sx, qxt, sxt = O.quantize_x(X, k, 8, v, fmt=f)
-    del X
-    assert_codes(L.qx.codes_view().cpu().numpy(), qx, "qX", f)
-    assert_scale(float(L.qx.scale.cpu()[0]), sx, "sX")
-    assert_codes(L.qxt.codes_t_view().cpu().numpy().T, qxt, "qXt", f)
-    assert_scale(float(L.qxt.scale.cpu()[0]), sxt, "sXt")
-    W = O.decode(inputs["w"], cfg["in_dtype"])
-    qw, sw = O.quantize_w(W, k, 8, v, fmt=f)
-    del W
-    assert_codes(L.qw.codes_view().cpu().numpy(), qw, "qW", f)
-    G = O.decode(inputs["dy"], cfg["in_dtype"])
-    qg, sg = O.quantize_g(G, k, 8, v, fmt=f)
-    del G
-    assert_codes(L.qg.codes_view().cpu().numpy(), qg, "qG", f)
-    rng = np.random.default_rng(3000)
-    rs = np.sort(rng.choice(N, 128, replace=False))
-    cs = np.sort(rng.choice(D, 128, replace=False))
-    y = O.decode(T.bits_of(res["y"][rs][:, cs].contiguous()), out_dt)
-    assert_out(y, O.fwd_from_codes(qx, sx, qw, sw, k, v, rows=rs, cols=cs, fmt=f), out_dt, "Y")
-    for _ in range(2):
-        r0, c0 = int(rng.integers(0, N // k)) * k, int(rng.integers(0, C // k)) * k
-        ref = O.bwd_input_from_codes(qg, sg, qw, sw, k, v, row_block=(r0, k), col_block=(c0, k),
-                                     fmt=f)
-        got = O.decode(T.bits_of(res["dx"][r0:r0 + k, c0:c0 + k].contiguous()), out_dt)
-        assert_out(got, ref, out_dt, "dX block (%d, %d)" % (r0, c0))
-        r0, c0 = int(rng.integers(0, D - 64 + 1)), int(rng.integers(0, C // k)) * k
-        ref = O.bwd_weight_from_codes(qg, sg, qxt, sxt, k, v, row_block=(r0, 64),
-                                      col_block=(c0, k), fmt=f)
-        got = O.decode(T.bits_of(res["dw"][r0:r0 + 64, c0:c0 + k].contiguous()), out_dt)
-        assert_out(got, ref, out_dt, "dW block (%d, %d)" % (r0, c0))
+    fullsize_sampled(cfg, 3000)
