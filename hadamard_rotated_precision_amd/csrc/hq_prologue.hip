@@ -21,6 +21,9 @@
 //                      half tile staged column-major, the token phase in TokenT (fp32);
 //                      both_pipe_kernel is the same with the next item's raw rows loaded into
 //                      LDS during the current item's token phase (several items per workgroup).
+//   both_narrow_kernel : the same for k <= 128 on 128 x 128 items: 64 KB of LDS per workgroup of
+//                      four waves, two workgroups per CU (the default where both_pipe_kernel
+//                      would run and k <= 128).
 // VALU kernels (every other shape: fp32 inputs, k < 16, ragged tiles, unaligned pitches):
 //   right_fast_kernel / right_kernel : rotation along the contiguous axis. Tile 64 rows x 256
 //                  columns; four lanes share a row, so strides < 64 are in-register butterflies
@@ -1632,6 +1635,185 @@ __global__ __launch_bounds__(BM_THREADS) void both_pipe_kernel(ProArgs a) {
   if constexpr (In::bytes == 2 && K >= 16) both_mma_body<In, K, OP, true>(a);
 }
 
+// ================================================================ both, narrow items (k <= 128)
+// With k <= 128 a token-axis block spans at most 128 rows and a feature-axis block at most 128
+// columns, so a work item can be a 128 x 128 tile: its fp32 staging takes 64 KB of LDS instead of
+// the 128 KB of a 256-row half tile, and two workgroups of four waves share a CU. Their load,
+// matrix-core, LDS and butterfly phases then overlap, where a single 8-wave workgroup ran them
+// in series. Per item, as both_pipe_kernel:
+//  - the raw 16-bit rows (128 x 256 bytes) come in by direct-to-LDS loads issued during the
+//    previous item's token phase, chunk c of row r at c ^ (r % 16);
+//  - row phase on the matrix cores (wave w: rows 32w + [0, 32)), row-major codes of X B stored
+//    from registers;
+//  - X B staged column-major as fp32, 16-byte row chunk c4 of column c at
+//    c4 ^ (c % 16) ^ 8 (c4 / 16): the 16-lane write groups (one chunk, 16 columns) and the read
+//    groups (8 columns x both row halves) meet 16 distinct 16-byte bank groups;
+//  - token phase: thread (column t / 2, half t % 2) rotates rows 64 (t % 2) + [0, 64) in fp32
+//    registers, the stride-64 stage (k = 128) between the two lanes of a pair;
+//  - transposed codes of B X B go through a 16 KB byte tile in the upper half of the staging
+//    buffer (the raw rows of the next item use the lower half), column c's 16-byte chunk q at
+//    q ^ ((c / 2) % 4), and leave as 16-byte stores of whole 128-byte column runs.
+constexpr int BN_ROWS = 128, BN_COLS = 128, BN_THREADS = 256, BN_GRID = 512;
+
+__host__ __device__ inline int64_t both_narrow_items(int64_t rows, int64_t cols) {
+  return (rows / BN_ROWS) * (cols / BN_COLS);
+}
+
+// The narrow kernel takes the shapes of both_pipe_kernel (several items per workgroup) when
+// k <= 128.
+__host__ __device__ inline bool both_narrow_ok(int64_t rows, int64_t cols, bool vec, int in_bytes,
+                                               int k) {
+  return both_mma_ok(rows, cols, vec, in_bytes, k) && k <= BN_COLS &&
+         both_items(rows, cols) > 256;
+}
+
+__device__ inline int bn_chunk(int c, int c4) { return c4 ^ (c & 15) ^ (8 * ((c4 >> 4) & 1)); }
+
+template <class In, int K, int OP>
+__global__ __launch_bounds__(BN_THREADS, 2) void both_narrow_kernel(ProArgs a) {
+  if constexpr (In::bytes != 2 || K < 16 || K > BN_COLS) {
+    return;
+  } else {
+    __shared__ __attribute__((aligned(16))) float half[BN_COLS * BN_ROWS];   // [column][row]
+    __shared__ float red[32];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int n0 = lane & 15, lg = lane >> 4;
+    const int cp = t >> 1, pp = t & 1;   // token phase: column cp, rows 64pp + [0, 64)
+    const int64_t nct = a.cols / BN_COLS;
+    const int64_t items = both_narrow_items(a.rows, a.cols);
+    float s1 = 0.0f, r1 = 0.0f, sc2 = 0.0f, r2 = 0.0f;
+    if constexpr (quant_op(OP)) {
+      tensor_scale(a.part_in, a.nparts, a.step, a.qmaxf, red, s1, r1);
+      tensor_scale(a.part_in2, a.nparts, a.step2, a.qmaxf, red, sc2, r2);
+      zero_side(a);
+      if (blockIdx.x == 0 && t == 0) {
+        *a.scale_out = s1;
+        *a.scale_out2 = sc2;
+      }
+    }
+    const float lo = code_lo<OP>(a), hi = code_hi<OP>(a);
+    constexpr int KM = K < 64 ? K : 64;
+    constexpr int NKS = 4, NNB = 8;         // 32-column slices, 16-column output blocks
+    constexpr int RAWB = 2 * BN_COLS;       // bytes of one raw row (256)
+    constexpr int NCH = RAWB / 16, RPK = 1024 / RAWB;
+    uint4 G[4];
+    hfrags<In, KM>(lane, G);
+    const char* src = static_cast<const char*>(a.src);
+    int8_t* const raw = reinterpret_cast<int8_t*>(half);                 // bytes [0, 32 KB)
+    uint4* const ctile = reinterpret_cast<uint4*>(half) + 2048;           // bytes [32, 48 KB)
+    float amax1 = 0.0f, amax2 = 0.0f;
+    // direct-to-LDS loads of item it's raw rows: 1 KB blocks w + 4i, lane l -> row
+    // RPK (w + 4i) + l / NCH, slot l % NCH = chunk (l % NCH) ^ (row % 16)
+    auto issue_raw = [&](int64_t it) {
+      const int64_t row0 = (it / nct) * BN_ROWS, col0 = (it % nct) * BN_COLS;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(src + (row0 * a.cols + col0) * 2), 0,
+          static_cast<int>(BN_ROWS * a.cols * 2), kBufferFlags);
+#pragma unroll
+      for (int i = 0; i < BN_ROWS / RPK / 4; ++i) {
+        const int b = w + 4 * i, r = RPK * b + lane / NCH, c = (lane % NCH) ^ (r & 15);
+        lds_dma16(rs, raw + b * 1024, r * static_cast<int>(a.cols) * 2 + 16 * c);
+      }
+    };
+    if (static_cast<int64_t>(blockIdx.x) < items) issue_raw(blockIdx.x);
+    for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+      const int64_t row0 = (it / nct) * BN_ROWS, col0 = (it % nct) * BN_COLS;
+      uint4 xr[2][NKS];
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's raw loads landed
+      __syncthreads();                                    // and every wave's
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int r = 32 * w + 16 * rb + n0;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+          xr[rb][ks] = *reinterpret_cast<const uint4*>(raw + r * RAWB + 16 * ((4 * ks + lg) ^ (r & 15)));
+      }
+      __syncthreads();   // raw rows read by every wave: the buffer takes the fp32 tile
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int rloc = 32 * w + 16 * rb;   // first tile row of this block
+        f32x4 y[NNB];
+        mma_rows<In, KM, NKS, NNB>(xr[rb], G, y);
+        mma_high_stages<K, NNB, 128>(y);
+        if constexpr (OP == OP_ABSMAX) {
+#pragma unroll
+          for (int nb = 0; nb < NNB; ++nb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) amax1 = fmaxf(amax1, fabsf(y[nb][j]));
+        } else if (a.codes) {
+          // as both_mma_body: after the byte and dword transposes lane (n0 = 4m + i, lg) holds
+          // all 16 codes of column blocks m and 4 + m of row 4lg + i
+          const int i = n0 & 3, m = n0 >> 2;
+          uint32_t d[8];
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb)
+            d[nb] = quad_byte_transpose(
+                quant4(y[nb][0], y[nb][1], y[nb][2], y[nb][3], r1, lo, hi, (OP == OP_QUANT_F8)), i);
+          lane4_transpose(d[0], d[1], d[2], d[3]);
+          lane4_transpose(d[4], d[5], d[6], d[7]);
+          int8_t* dst = a.codes + (row0 + rloc + 4 * lg + i) * a.ld + col0 + 16 * m;
+          *reinterpret_cast<uint4*>(dst) = make_uint4(d[0], d[1], d[2], d[3]);
+          *reinterpret_cast<uint4*>(dst + 64) = make_uint4(d[4], d[5], d[6], d[7]);
+        }
+        const int c4 = (rloc >> 2) + lg;
+#pragma unroll
+        for (int nb = 0; nb < NNB; ++nb) {
+          const int c = 16 * nb + n0;
+          *reinterpret_cast<float4*>(&half[c * BN_ROWS + 4 * bn_chunk(c, c4)]) =
+              make_float4(y[nb][0], y[nb][1], y[nb][2], y[nb][3]);
+        }
+      }
+      __syncthreads();
+      // ---- token phase
+      float u[64];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float4 f = *reinterpret_cast<const float4*>(&half[cp * BN_ROWS + 4 * bn_chunk(cp, 16 * pp + i)]);
+        u[4 * i] = f.x;
+        u[4 * i + 1] = f.y;
+        u[4 * i + 2] = f.z;
+        u[4 * i + 3] = f.w;
+      }
+      __syncthreads();   // every wave has its column values: the lower half takes the next raw rows
+      if (it + gridDim.x < items) issue_raw(it + gridDim.x);
+      fwht_from<1, K, 64>(u);
+      if constexpr (K > 64) quad_stage<64>(u, lane, 1);
+      if constexpr (OP == OP_ABSMAX) {
+#pragma unroll
+        for (int i = 0; i < 64; ++i) amax2 = fmaxf(amax2, fabsf(u[i]));
+      } else {
+        // rows 64pp + 16q + [0, 16) of column cp -> chunk 4pp + q of the column's 128-byte run
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t d[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int i = 16 * q + 4 * j;
+            d[j] = quant4(u[i], u[i + 1], u[i + 2], u[i + 3], r2, lo, hi, (OP == OP_QUANT_F8));
+          }
+          ctile[8 * cp + ((4 * pp + q) ^ ((cp >> 1) & 3))] = make_uint4(d[0], d[1], d[2], d[3]);
+        }
+        __syncthreads();
+        // eight lanes per column: store s covers columns 32s + t / 8, chunk t % 8 of each
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int c = 32 * s + (t >> 3), ch = t & 7;
+          const uint4 v = ctile[8 * c + (ch ^ ((c >> 1) & 3))];
+          *reinterpret_cast<uint4*>(a.codes_t + (col0 + c) * a.ld_t + row0 + 16 * ch) = v;
+        }
+      }
+    }
+    if constexpr (OP == OP_ABSMAX) {
+      amax1 = block_max(amax1, red);
+      amax2 = block_max(amax2, red);
+      if (t == 0) {
+        a.partials[blockIdx.x] = amax1;
+        a.partials[gridDim.x + blockIdx.x] = amax2;
+      }
+    }
+  }
+}
+
 // ================================================================ both, single pass
 // X under HALO-2 in ABSMAX mode when every workgroup has exactly one item (2048 x 4096 and
 // smaller): the two passes in one launch. Each workgroup computes X B (kept in LDS, column-major
@@ -1942,6 +2124,32 @@ HQ_PRO_DISPATCH(both_mma_kernel, BM_THREADS)
 HQ_PRO_DISPATCH(both_pipe_kernel, BM_THREADS)
 #undef HQ_PRO_DISPATCH
 
+template <class In, int OP>
+static hipError_t both_narrow_k(int k, const ProArgs& a, int grid, hipStream_t st, int tok) {
+  switch (k) {
+#define HQ_BN(KK) \
+  case KK: return launch_k(both_narrow_kernel<In, KK, OP>, dim3(grid), dim3(BN_THREADS), st, tok, a);
+    HQ_BN(16) HQ_BN(32) HQ_BN(64) HQ_BN(128)
+#undef HQ_BN
+  }
+  return hipErrorInvalidValue;
+}
+
+template <class In>
+static hipError_t both_narrow_op(int op, int k, const ProArgs& a, int grid, hipStream_t st, int tok) {
+  if (op == OP_ABSMAX) return both_narrow_k<In, OP_ABSMAX>(k, a, grid, st, tok);
+  if (op == OP_QUANT) return both_narrow_k<In, OP_QUANT>(k, a, grid, st, tok);
+  if (op == OP_QUANT_F8) return both_narrow_k<In, OP_QUANT_F8>(k, a, grid, st, tok);
+  return hipErrorInvalidValue;
+}
+
+static hipError_t both_narrow_launch(int in_dt, int op, int k, const ProArgs& a, int grid,
+                                     hipStream_t st, int tok) {
+  if (in_dt == DT_F16) return both_narrow_op<F16>(op, k, a, grid, st, tok);
+  if (in_dt == DT_BF16) return both_narrow_op<BF16>(op, k, a, grid, st, tok);
+  return hipErrorInvalidValue;
+}
+
 template <class In, bool F8>
 static hipError_t both_single_k(int k, const ProArgs& a, int grid, hipStream_t st, int tok) {
   switch (k) {
@@ -1954,6 +2162,13 @@ static hipError_t both_single_k(int k, const ProArgs& a, int grid, hipStream_t s
 }
 
 static int dtb(int dt) { return dt == DT_F32 ? 4 : 2; }
+
+// The narrow two-sided kernel is the default where it applies; HQ_BOTH_NARROW=0 selects
+// both_pipe_kernel instead (read on every call, so a test can compare the two).
+static bool both_narrow_on() {
+  const char* e = std::getenv("HQ_BOTH_NARROW");
+  return !(e && e[0] == '0');
+}
 
 static ProArgs pro_args(const ProPass& p) {
   ProArgs a{};
@@ -1997,6 +2212,8 @@ int pro_grid(const ProPass& p) {
     const int tr = p.k > 64 ? p.k : 64, tc = LT_ELEMS / tr;
     tiles = ((p.rows + tr - 1) / tr) * ((p.cols + tc - 1) / tc);
   } else {
+    if (both_narrow_on() && both_narrow_ok(p.rows, p.cols, pro_args(p).vec, dtb(p.in_dt), p.k))
+      return grid_cap(both_narrow_items(p.rows, p.cols), BN_GRID);   // two per CU
     // one 135 KB workgroup per CU: at most one item per CU at a time
     return grid_cap(both_items(p.rows, p.cols), 256);
   }
@@ -2023,6 +2240,8 @@ hipError_t pro_pass(const ProPass& p, int op, hipStream_t st) {
   else if (p.kind == PRO_LEFT && left_fast_ok(p.rows, p.cols, a.vec, dtb(p.in_dt)))
     e = left_fast_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
   else if (p.kind == PRO_LEFT) e = left_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
+  else if (both_narrow_on() && both_narrow_ok(p.rows, p.cols, a.vec, dtb(p.in_dt), p.k))
+    e = both_narrow_launch(p.in_dt, op, p.k, a, grid, st, tok);
   else if (both_mma_ok(p.rows, p.cols, a.vec, dtb(p.in_dt), p.k) && both_items(p.rows, p.cols) > grid)
     e = both_pipe_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
   else if (both_mma_ok(p.rows, p.cols, a.vec, dtb(p.in_dt), p.k))

@@ -30,8 +30,8 @@ GEMM_SOURCE = os.path.join(HERE, "csrc", "hq_gemm.hip")
 # the rotate -> quantize prologue: its kernels and the host code that picks them
 PROLOGUE_SOURCES = [os.path.join(HERE, "csrc", f) for f in ("hq_prologue.hip", "hq_api.cpp")]
 PROLOGUE_KERNELS = ("right_mma_kernel", "left_mma_kernel", "both_mma_kernel", "both_pipe_kernel",
-                    "both_single_kernel", "right_fast_kernel", "right_kernel", "left_fast_kernel",
-                    "left_kernel", "both_kernel")
+                    "both_narrow_kernel", "both_single_kernel", "right_fast_kernel", "right_kernel",
+                    "left_fast_kernel", "left_kernel", "both_kernel")
 
 
 def prologue_source_hash():

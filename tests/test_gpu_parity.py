@@ -303,6 +303,66 @@ def test_rotate_quantize_both_pipelined(k, rows, cols):
     assert_scale(float(q.scale.cpu()[0]), ref_s, "scale")
 
 
+def _rq_both(vb, dt, rows, cols, k, bits, mode, fmt, step):
+    q = T.QTensor(rows, cols, codes=False, codes_t=True)
+    cfg = T.config(k, bits, mode, B.HQ_VARIANT_HQ, fmt)
+    ws_bytes = B.hq_workspace_bytes(cfg, rows, cols, cols)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    src = T.device_tensor_from_bits(vb, dt, DEV)
+    st = None if step is None else torch.tensor([step], dtype=torch.float32, device=DEV)
+    B.check(B.hq_rotate_quantize(src.data_ptr(), dt, rows, cols, B.HQ_ROT_BOTH, cfg, T.ptr(st),
+                                 q.st, ws.data_ptr(), ws_bytes, T.stream_ptr()), "rotate_quantize")
+    torch.cuda.synchronize()
+    return q.codes_t.cpu().numpy(), float(q.scale.cpu()[0])
+
+
+@pytest.mark.parametrize("k", [16, 32, 64, 128])
+@pytest.mark.parametrize("dt,bits,mode,fmt", [
+    (B.HQ_BF16, 8, B.HQ_SCALE_ABSMAX, B.HQ_FMT_INT),
+    (B.HQ_F16, 4, B.HQ_SCALE_STEP, B.HQ_FMT_INT),
+    (B.HQ_BF16, 8, B.HQ_SCALE_ABSMAX, B.HQ_FMT_E4M3),
+])
+def test_both_narrow_items_match_half_tiles(k, dt, bits, mode, fmt, monkeypatch):
+    """B X B with k <= 128 on 128 x 128 items (two workgroups per compute unit; 544 items on 512
+    workgroups, so some take two) against the 256-row half-tile kernel, which HQ_BOTH_NARROW=0
+    selects: the same rotation in the same order, so codes (every byte of the pitched buffer)
+    and scale agree bit for bit; the integer codes are also compared with the oracle."""
+    rows, cols = 2048, 4352
+    banner("both-narrow", k, dt, bits, mode, fmt)
+    rng = np.random.default_rng(900 + k)
+    V = rng.standard_normal((rows, cols))
+    V[:, rng.choice(cols, 8, replace=False)] *= 40.0
+    vb = WL.to_dtype_bits(V, dt)
+    step = float(np.float32(2.0 * k * 0.8 / np.sqrt(7.0))) if mode == B.HQ_SCALE_STEP else None
+    narrow, s_n = _rq_both(vb, dt, rows, cols, k, bits, mode, fmt, step)
+    monkeypatch.setenv("HQ_BOTH_NARROW", "0")
+    halves, s_h = _rq_both(vb, dt, rows, cols, k, bits, mode, fmt, step)
+    np.testing.assert_array_equal(narrow, halves)
+    assert np.float32(s_n).tobytes() == np.float32(s_h).tobytes()
+    if fmt == B.HQ_FMT_INT:
+        ref_codes, ref_s = O.quantize_tensor(O.decode(vb, dt), B.HQ_ROT_BOTH, k, bits,
+                                             O.STEP if step else O.ABSMAX, step)
+        assert_codes(narrow[:, :rows].T, ref_codes, "codes_t")
+        assert_scale(s_n, ref_s, "scale")
+
+
+@pytest.mark.parametrize("k", [64, 128])
+def test_layer_narrow_x_items(k, monkeypatch):
+    """The HALO-2 forward's X pass on 128 x 128 items (X B row-major and B X B transposed codes
+    from one pass pair), at a size with more items than workgroups: the whole layer against the
+    oracle, and codes and outputs bit for bit against the 256-row half-tile kernel."""
+    cfg = WL.config(5, N=2048, C=4352, D=256, k=k)
+    banner("layer-narrow-x", k)
+    inputs = WL.make_inputs(cfg)
+    h = host(run_gpu(cfg, inputs), cfg["out_dtype"])
+    monkeypatch.setenv("HQ_BOTH_NARROW", "0")
+    h0 = host(run_gpu(cfg, inputs), cfg["out_dtype"])
+    for key in h:
+        np.testing.assert_array_equal(h[key], h0[key], err_msg=key)
+    ora = run_oracle(cfg, inputs)
+    compare_layer(cfg, h, ora, cfg["out_dtype"])
+
+
 @pytest.mark.parametrize("rot", [B.HQ_ROT_RIGHT, B.HQ_ROT_LEFT])
 def test_rotate_quantize_single_layout(rot):
     """Only one code layout requested (the other is staged in the workspace)."""
