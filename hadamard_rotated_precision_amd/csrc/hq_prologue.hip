@@ -2170,6 +2170,13 @@ static bool both_narrow_on() {
   return !(e && e[0] == '0');
 }
 
+// The matrix-core kernels are the default for the shapes they take; HQ_PROLOGUE_VALU=1 runs
+// every prologue pass on the VALU butterfly kernels instead, to measure one against the other.
+static bool prologue_mma_on() {
+  const char* e = std::getenv("HQ_PROLOGUE_VALU");
+  return !(e && e[0] == '1');
+}
+
 static ProArgs pro_args(const ProPass& p) {
   ProArgs a{};
   a.src = p.src;
@@ -2198,21 +2205,22 @@ static ProArgs pro_args(const ProPass& p) {
 
 int pro_grid(const ProPass& p) {
   int64_t tiles;
+  const bool mma = prologue_mma_on();
   if (p.kind == PRO_RIGHT) {
-    if (right_mma_ok(p.rows, p.cols, pro_args(p).vec, dtb(p.in_dt), p.k))
+    if (mma && right_mma_ok(p.rows, p.cols, pro_args(p).vec, dtb(p.in_dt), p.k))
       return grid_cap((p.rows / RM_ROWS) * (p.cols / RM_COLS), RM_GRID);
     if (right_fast_ok(p.rows, p.cols, pro_args(p).vec))
       return grid_cap((p.rows / RF_ROWS) * (p.cols / RF_COLS), RF_GRID);
     tiles = ((p.rows + RT_ROWS - 1) / RT_ROWS) * ((p.cols + RT_COLS - 1) / RT_COLS);
   } else if (p.kind == PRO_LEFT) {
-    if (left_mma_ok(p.rows, p.cols, pro_args(p).vec, dtb(p.in_dt), p.k))
+    if (mma && left_mma_ok(p.rows, p.cols, pro_args(p).vec, dtb(p.in_dt), p.k))
       return grid_cap((p.rows / LM_ROWS) * (p.cols / LM_COLS), LM_GRID);
     if (left_fast_ok(p.rows, p.cols, pro_args(p).vec, dtb(p.in_dt)))
       return grid_cap((p.rows / LF_ROWS) * (p.cols / LF_COLS), LF_GRID);
     const int tr = p.k > 64 ? p.k : 64, tc = LT_ELEMS / tr;
     tiles = ((p.rows + tr - 1) / tr) * ((p.cols + tc - 1) / tc);
   } else {
-    if (both_narrow_on() && both_narrow_ok(p.rows, p.cols, pro_args(p).vec, dtb(p.in_dt), p.k))
+    if (mma && both_narrow_on() && both_narrow_ok(p.rows, p.cols, pro_args(p).vec, dtb(p.in_dt), p.k))
       return grid_cap(both_narrow_items(p.rows, p.cols), BN_GRID);   // two per CU
     // one 135 KB workgroup per CU: at most one item per CU at a time
     return grid_cap(both_items(p.rows, p.cols), 256);
@@ -2230,21 +2238,23 @@ hipError_t pro_pass(const ProPass& p, int op, hipStream_t st) {
   if (quant_op(op)) outb = elems * ((p.codes ? 1 : 0) + (p.codes_t ? 1 : 0));
   const int tok = prof_open(op == OP_ABSMAX ? K_ROT_ABSMAX : K_ROT_QUANT, inb + outb);
   hipError_t e = hipErrorInvalidValue;
-  if (p.kind == PRO_RIGHT && right_mma_ok(p.rows, p.cols, a.vec, dtb(p.in_dt), p.k))
+  const bool mma = prologue_mma_on();
+  if (p.kind == PRO_RIGHT && mma && right_mma_ok(p.rows, p.cols, a.vec, dtb(p.in_dt), p.k))
     e = right_mma_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
   else if (p.kind == PRO_RIGHT && right_fast_ok(p.rows, p.cols, a.vec))
     e = right_fast_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
   else if (p.kind == PRO_RIGHT) e = right_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
-  else if (p.kind == PRO_LEFT && left_mma_ok(p.rows, p.cols, a.vec, dtb(p.in_dt), p.k))
+  else if (p.kind == PRO_LEFT && mma && left_mma_ok(p.rows, p.cols, a.vec, dtb(p.in_dt), p.k))
     e = left_mma_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
   else if (p.kind == PRO_LEFT && left_fast_ok(p.rows, p.cols, a.vec, dtb(p.in_dt)))
     e = left_fast_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
   else if (p.kind == PRO_LEFT) e = left_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
-  else if (both_narrow_on() && both_narrow_ok(p.rows, p.cols, a.vec, dtb(p.in_dt), p.k))
+  else if (mma && both_narrow_on() && both_narrow_ok(p.rows, p.cols, a.vec, dtb(p.in_dt), p.k))
     e = both_narrow_launch(p.in_dt, op, p.k, a, grid, st, tok);
-  else if (both_mma_ok(p.rows, p.cols, a.vec, dtb(p.in_dt), p.k) && both_items(p.rows, p.cols) > grid)
+  else if (mma && both_mma_ok(p.rows, p.cols, a.vec, dtb(p.in_dt), p.k) &&
+           both_items(p.rows, p.cols) > grid)
     e = both_pipe_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
-  else if (both_mma_ok(p.rows, p.cols, a.vec, dtb(p.in_dt), p.k))
+  else if (mma && both_mma_ok(p.rows, p.cols, a.vec, dtb(p.in_dt), p.k))
     e = both_mma_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
   else e = both_kernel_launch(p.in_dt, op, p.k, a, grid, st, tok);
   return e;
@@ -2299,7 +2309,8 @@ hipError_t fwht_left_mma(const void* src, int dt, int64_t rows, int64_t cols, in
 
 bool pro_single_ok(const ProPass& p, int cus) {
   const ProArgs a = pro_args(p);
-  return p.kind == PRO_BOTH && p.step == nullptr && both_mma_ok(p.rows, p.cols, a.vec, dtb(p.in_dt), p.k) &&
+  return p.kind == PRO_BOTH && p.step == nullptr && prologue_mma_on() &&
+         both_mma_ok(p.rows, p.cols, a.vec, dtb(p.in_dt), p.k) &&
          both_items(p.rows, p.cols) <= std::min(256, cus);
 }
 

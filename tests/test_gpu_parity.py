@@ -363,6 +363,21 @@ def test_layer_narrow_x_items(k, monkeypatch):
     compare_layer(cfg, h, ora, cfg["out_dtype"])
 
 
+@pytest.mark.parametrize("cid,N,C,D", [(2, 512, 1024, 512), (4, 512, 1024, 768),
+                                     (5, 1024, 2048, 512)])
+def test_layer_prologue_valu_kernels(cid, N, C, D, monkeypatch):
+    """HQ_PROLOGUE_VALU=1 runs every rotate-quantize pass of the layer on the VALU butterfly
+    kernels instead of the matrix-core ones (whole tiles, k = 256 and 128): the layer still
+    matches the oracle within the same bounds."""
+    monkeypatch.setenv("HQ_PROLOGUE_VALU", "1")
+    cfg = WL.config(cid, N=N, C=C, D=D)
+    banner("layer-prologue-valu", cid, N, C, D)
+    inputs = WL.make_inputs(cfg)
+    h = host(run_gpu(cfg, inputs), cfg["out_dtype"])
+    ora = run_oracle(cfg, inputs)
+    compare_layer(cfg, h, ora, cfg["out_dtype"])
+
+
 @pytest.mark.parametrize("rot", [B.HQ_ROT_RIGHT, B.HQ_ROT_LEFT])
 def test_rotate_quantize_single_layout(rot):
     """Only one code layout requested (the other is staged in the workspace)."""
