@@ -819,9 +819,9 @@ hq_status hq_fwht_path(const void* src, int32_t src_dtype, void* dst, int32_t ds
   hipStream_t st = static_cast<hipStream_t>(stream);
   // AUTO follows the measured bf16 transforms (2048 x 4096 up to 8192 x 13824): the
   // butterflies wherever they are within 5 % of the matrix cores (RIGHT at every k, with DPP
-  // lane exchanges 1-17 % faster; LEFT at k = 32 and 64), the matrix cores otherwise (LEFT at
-  // k = 16, 128, 256: 13-40 % faster)
-  const bool auto_left_mma = k != 32 && k != 64;
+  // lane exchanges 1-17 % faster; LEFT at k = 16 with the register kernel, 32 and 64), the
+  // matrix cores otherwise (LEFT at k = 128 and 256: 7-60 % faster)
+  const bool auto_left_mma = k >= 128;
   const bool auto_right_mma = false;
   const bool use_left_mma =
       left_mma && (path == HQ_FWHT_MATRIX || (path == HQ_FWHT_AUTO && auto_left_mma));

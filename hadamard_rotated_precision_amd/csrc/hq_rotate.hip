@@ -17,6 +17,8 @@
 //                  goes back through LDS so the stores are row-contiguous.
 #include <algorithm>
 
+#include <cstdlib>
+
 #include "hq_device.hpp"
 #include "hq_internal.hpp"
 #include "hq_launch.hpp"
@@ -400,6 +402,93 @@ __global__ __launch_bounds__(kThreads) void cols_kernel(ColArgs a) {
   }
 }
 
+// ============================================================ register cols kernel (LEFT, k = 16)
+// k = 16, 16-bit input, row pitch a multiple of 8 elements, 16-byte aligned source and
+// destination. No LDS: a thread holds one whole 16-row block of 8 consecutive columns (one
+// 16-byte load per row) and rotates it in registers; each load or store instruction covers
+// 1 KB of one row. At 8192 x 13824 bf16 it runs in 83.5-86.2 us against 115-117 us for cols_kernel
+// and 96.6 us on the matrix cores. The same layout at k = 32..256 (k/16 lanes per column group,
+// the wider strides as DPP lane exchanges) was slower than cols_kernel at every such k (90.7,
+// 100.2, 109.6, 135.1 against 85.1, 94.3, 103.0, 154.6 us; the matrix cores take 128 and 256),
+// so it is built for k = 16 only.
+constexpr int C16_COLS = 2048;   // columns per tile: 256 threads x 8
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+template <class In, class Out>
+__global__ __launch_bounds__(kThreads, 2) void cols16_kernel(ColArgs a) {
+  if constexpr (In::bytes != 2) {
+    return;
+  } else {
+    constexpr int R = 16;
+    const int t = threadIdx.x;
+    const int64_t nct = (a.cols + C16_COLS - 1) / C16_COLS;
+    const int64_t tiles = (a.rows / R) * nct;
+    for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+      const int64_t rb = (tile / nct) * R;
+      const int64_t c0 = (tile % nct) * C16_COLS + 8 * t;
+      if (c0 >= a.cols) continue;   // cols % 8 == 0: a thread's 8 columns are whole or absent
+      // buffer loads and stores from the block's first row, the row index in the scalar offset
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(static_cast<const uint16_t*>(a.src) + rb * a.cols), 0,
+          static_cast<int>(R * a.cols * 2), kBufferFlags);
+      const int pitch = static_cast<int>(a.cols * 2);
+      v4u x[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+        x[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<int>(c0 * 2), i * pitch, 0);
+      // two halves of four columns keep 64 values live; 16-bit outputs are packed into the input
+      // words they replace, and a row leaves as one 16-byte store at the end
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        float v[4 * R];   // (row i, column 4 hf + j) at v[4 i + j]
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const uint32_t u = x[i][2 * hf + j];
+            v[4 * i + 2 * j] = In::from_bits(static_cast<uint16_t>(u & 0xFFFFu));
+            v[4 * i + 2 * j + 1] = In::from_bits(static_cast<uint16_t>(u >> 16));
+          }
+#pragma unroll
+        for (int h = 1; h < R; h <<= 1)
+#pragma unroll
+          for (int i = 0; i < R; ++i)
+            if ((i & h) == 0)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const float p0 = v[4 * i + j], p1 = v[4 * (i + h) + j];
+                v[4 * i + j] = p0 + p1;
+                v[4 * (i + h) + j] = p0 - p1;
+              }
+        if constexpr (Out::bytes == 2) {
+#pragma unroll
+          for (int i = 0; i < R; ++i) {
+            x[i][2 * hf] = Out::pack2(v[4 * i], v[4 * i + 1]);
+            x[i][2 * hf + 1] = Out::pack2(v[4 * i + 2], v[4 * i + 3]);
+          }
+        } else {
+          const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+              static_cast<float*>(a.dst) + rb * a.cols, 0, static_cast<int>(R * a.cols * 4), kBufferFlags);
+#pragma unroll
+          for (int i = 0; i < R; ++i) {
+            const float4 f = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, f), rd,
+                                                   static_cast<int>((c0 + 4 * hf) * 4), i * 2 * pitch, 0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);   // one half's values live at a time
+      }
+      if constexpr (Out::bytes == 2) {
+        const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(
+            static_cast<uint16_t*>(a.dst) + rb * a.cols, 0, static_cast<int>(R * a.cols * 2), kBufferFlags);
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+          __builtin_amdgcn_raw_buffer_store_b128(x[i], rd, static_cast<int>(c0 * 2), i * pitch, 0);
+      }
+    }
+  }
+}
+
 // ============================================================ fills
 __global__ __launch_bounds__(kThreads) void zero_i32_kernel(int32_t* p, int64_t n) {
   for (int64_t i = blockIdx.x * static_cast<int64_t>(kThreads) + threadIdx.x; i < n;
@@ -456,6 +545,17 @@ static hipError_t rows_out(int out_dt, int k, const RowArgs& a, int grid, hipStr
 }
 
 template <class In>
+static hipError_t cols16_out(int out_dt, const ColArgs& a, int grid, hipStream_t st) {
+  switch (out_dt) {
+    case DT_F32: hipLaunchKernelGGL((cols16_kernel<In, F32>), dim3(grid), dim3(kThreads), 0, st, a); break;
+    case DT_F16: hipLaunchKernelGGL((cols16_kernel<In, F16>), dim3(grid), dim3(kThreads), 0, st, a); break;
+    case DT_BF16: hipLaunchKernelGGL((cols16_kernel<In, BF16>), dim3(grid), dim3(kThreads), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <class In>
 static hipError_t cols_out(int out_dt, int k, const ColArgs& a, int grid, hipStream_t st) {
   switch (out_dt) {
     case DT_F32: return launch_cols_k<In, F32>(k, a, grid, st);
@@ -490,6 +590,13 @@ hipError_t rows_pass(const RowPass& p, hipStream_t st) {
   return e;
 }
 
+// At k = 16 the register kernel is the default where it applies; HQ_COLS_REG=0 selects the
+// LDS-staged cols_kernel instead (read on every call, so the two can be measured side by side).
+static bool cols_reg_on() {
+  const char* e = std::getenv("HQ_COLS_REG");
+  return !(e && e[0] == '0');
+}
+
 hipError_t cols_pass(const ColPass& p, hipStream_t st) {
   ColArgs a{};
   a.src = p.src;
@@ -497,6 +604,18 @@ hipError_t cols_pass(const ColPass& p, hipStream_t st) {
   a.cols = p.cols;
   a.vec = aligned16(p.src) && (p.cols * dt_bytes(p.in_dt)) % 16 == 0;
   a.dst = p.dst;
+  if ((p.in_dt == DT_F16 || p.in_dt == DT_BF16) && p.k == 16 && p.cols % 8 == 0 &&
+      aligned16(p.src) && aligned16(p.dst) && 16 * p.cols * dt_bytes(p.out_dt) < (int64_t(1) << 31) &&
+      cols_reg_on()) {
+    const int64_t tiles = (p.rows / 16) * ((p.cols + C16_COLS - 1) / C16_COLS);
+    const int tok = prof_begin(K_ROT_STORE, static_cast<double>(p.rows) * p.cols *
+                                                (dt_bytes(p.in_dt) + dt_bytes(p.out_dt)), st);
+    const int grid = grid_for(tiles, 1, 1 << 20);
+    const hipError_t e = p.in_dt == DT_F16 ? cols16_out<F16>(p.out_dt, a, grid, st)
+                                           : cols16_out<BF16>(p.out_dt, a, grid, st);
+    prof_end(tok, st);
+    return e;
+  }
   const int nc = kThreads / (p.k >= 4 ? 4 : p.k);   // ColShape<k>::NC
   const int64_t tiles = (p.rows / p.k) * ((p.cols + nc - 1) / nc);
   const int grid = grid_for(tiles, 1, 1 << 20);

@@ -346,7 +346,7 @@ hq_status hq_lss_bwd_weight(const void *dy, int32_t dy_dtype, const hq_qtensor *
  * summation error of that. The implementation is hq_fwht_path's HQ_FWHT_AUTO choice: with
  * 16-bit src_dtype == dst_dtype, 16-byte aligned pointers and whole tiles (RIGHT: rows % 64
  * == 0, cols % 256 == 0; LEFT: rows % 256 == 0, cols % 64 == 0) the sums run on the matrix
- * cores for LEFT at k = 16, 128, 256, in another order than the VALU butterflies of the other
+ * cores for LEFT at k = 128 and 256, in another order than the VALU butterflies of the other
  * cases. */
 hq_status hq_fwht(const void *src, int32_t src_dtype, void *dst, int32_t dst_dtype,
                   int64_t rows, int64_t cols, int32_t rot, int32_t k, void *stream);
@@ -354,7 +354,7 @@ hq_status hq_fwht(const void *src, int32_t src_dtype, void *dst, int32_t dst_dty
 /* hq_fwht with the implementation named (for measuring one against the other; the results
  * agree to the fp32 summation order). path:
  *   HQ_FWHT_AUTO       what hq_fwht picks: the matrix cores where they cover the call and
- *                      were measured more than 5 % faster (LEFT at k = 16, 128, 256), the
+ *                      were measured more than 5 % faster (LEFT at k = 128 and 256), the
  *                      VALU butterflies otherwise;
  *   HQ_FWHT_BUTTERFLY  the VALU butterflies (log2 k add/sub stages per element), any shape;
  *   HQ_FWHT_MATRIX     the matrix cores (a dense +-1 contraction in 16-bit MFMA, exact

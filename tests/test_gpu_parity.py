@@ -201,6 +201,44 @@ def test_fwht_matrix_core_random(rot, dt):
     assert np.all(np.abs(got - ref) <= 2.0 ** (e - mant) + 2.0 ** -20 * absum)
 
 
+@pytest.mark.parametrize("k", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("dt,out", [(B.HQ_BF16, B.HQ_BF16), (B.HQ_F16, B.HQ_F16),
+                                    (B.HQ_BF16, B.HQ_F32)])
+@pytest.mark.parametrize("reg", ["1", "0"])
+def test_fwht_left_butterfly(k, dt, out, reg, monkeypatch):
+    """LEFT on the VALU butterflies, 16-bit input: at k = 16 the register kernel (a 16-row block
+    of 8 columns per lane, no LDS) and, with HQ_COLS_REG=0, the LDS-staged one, which every
+    larger k takes. 2048 x 1000 leaves a partial column tile at every k. Small integers: the
+    exact rotation rounded once, bit for bit; normal inputs: within one unit of the output
+    dtype plus the fp32 summation error."""
+    monkeypatch.setenv("HQ_COLS_REG", reg)
+    banner("fwht-left-butterfly", k, dt, out, reg)
+    rows, cols = 2048, 1000
+    rng = np.random.default_rng(13 * k + dt + 5 * out)
+    for exact in (True, False):
+        V = (rng.integers(-8, 9, size=(rows, cols)).astype(np.float64) if exact
+             else rng.standard_normal((rows, cols)))
+        bits = WL.to_dtype_bits(V, dt)
+        src = T.device_tensor_from_bits(bits, dt, DEV)
+        dst = torch.full((rows, cols), 7.0, dtype=T.TORCH_DT[out], device=DEV)
+        B.check(B.hq_fwht_path(src.data_ptr(), dt, dst.data_ptr(), out, rows, cols,
+                               B.HQ_ROT_LEFT, k, B.HQ_FWHT_BUTTERFLY, T.stream_ptr()), "fwht")
+        torch.cuda.synchronize()
+        ref = O.rotate(O.decode(bits, dt), O.ROT_LEFT, k)
+        if exact:
+            if out == B.HQ_F32:
+                np.testing.assert_array_equal(dst.cpu().numpy().astype(np.float64), ref)
+            else:
+                np.testing.assert_array_equal(T.bits_of(dst), WL.to_dtype_bits(ref, out))
+            continue
+        got = O.decode(T.bits_of(dst), out)
+        mant, emin = {B.HQ_BF16: (7, -126), B.HQ_F16: (10, -14), B.HQ_F32: (23, -126)}[out]
+        e = np.maximum(np.floor(np.log2(np.maximum(np.abs(ref), 1e-300))), emin)
+        absum = np.repeat(np.abs(O.decode(bits, dt)).reshape(rows // k, k, cols).sum(axis=1), k,
+                          axis=0)
+        assert np.all(np.abs(got - ref) <= 2.0 ** (e - mant) + 2.0 ** -20 * absum)
+
+
 def test_fwht_output_dtypes():
     rng = np.random.default_rng(3)
     V = rng.standard_normal((64, 256)).astype(np.float32)
