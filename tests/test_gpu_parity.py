@@ -401,6 +401,23 @@ def test_layer_narrow_x_items(k, monkeypatch):
     compare_layer(cfg, h, ora, cfg["out_dtype"])
 
 
+@pytest.mark.parametrize("cid,N,C,D", [(5, 8192, 8192, 256), (5, 256, 8192, 8192),
+                                     (5, 8192, 256, 8192)])
+def test_layer_quant_order(cid, N, C, D, monkeypatch):
+    """After an absmax pass over an input of 128 MiB or more (X, W and dY in turn) the quantize
+    pass visits tiles last to first (default), or first to last with HQ_QUANT_REVERSE=0: each
+    tile's codes depend only on the tile and the scale, so both orders give the same codes and
+    outputs bit for bit."""
+    cfg = WL.config(cid, N=N, C=C, D=D)
+    banner("layer-quant-order", cid, N, C, D)
+    inputs = WL.make_inputs(cfg)
+    h = host(run_gpu(cfg, inputs), cfg["out_dtype"])
+    monkeypatch.setenv("HQ_QUANT_REVERSE", "0")
+    h0 = host(run_gpu(cfg, inputs), cfg["out_dtype"])
+    for key in h:
+        np.testing.assert_array_equal(h[key], h0[key], err_msg=key)
+
+
 @pytest.mark.parametrize("cid,N,C,D", [(2, 512, 1024, 512), (4, 512, 1024, 768),
                                      (5, 1024, 2048, 512)])
 def test_layer_prologue_valu_kernels(cid, N, C, D, monkeypatch):
