@@ -470,7 +470,7 @@ def main():
                          "plain device copy (reference dispatches for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         return 2
 

@@ -4,7 +4,7 @@ The HALO summary page runs the three matmuls in FP8 as well as INT8 (Key results
 stands in where FP6 hardware is missing, Limitations). Codes: at most one grid step apart on
 at most 1e-4 of the entries (the GPU decides v * fp32(1/s), the oracle the exact quotient).
 The FP8 products are exact, but the matrix cores sum them in fp32 in their own order, so the
-GEMM is held to the benchmark spec's floating-point bound (relative Frobenius 1e-3 against the
+GEMM is held to the floating-point output bound (relative Frobenius 1e-3 against the
 oracle's exact sum) rather than bit-exactness; outputs as for INT8 (hq_testlib.out_bound).
 """
 import numpy as np
