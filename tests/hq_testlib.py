@@ -245,10 +245,11 @@ def outputs_from_gpu_codes(cfg, h):
     return out
 
 
-def fullsize_sampled(cfg, seed):
+def fullsize_sampled(cfg, seed, dw_rows=()):
     """A workload's whole step at its full size: codes and scales compared in full against the
     oracle's, outputs on sampled rows / k-aligned blocks against the oracle's exact values on
-    its own codes. The format and the code width come from cfg."""
+    its own codes (plus 64-row dW blocks at dw_rows). The format and the code width come from
+    cfg."""
     N, C, D, k, v = cfg["N"], cfg["C"], cfg["D"], cfg["k"], cfg["variant"]
     bits, f = cfg["bits"], cfg.get("fmt", O.INT)
     out_dt = cfg["out_dtype"]
@@ -282,6 +283,12 @@ def fullsize_sampled(cfg, seed):
         got = O.decode(T.bits_of(res["dx"][r0:r0 + k, c0:c0 + k].contiguous()), out_dt)
         assert_out(got, ref, out_dt, "dX block (%d, %d)" % (r0, c0))
         r0, c0 = int(rng.integers(0, D - 64 + 1)), int(rng.integers(0, C // k)) * k
+        ref = O.bwd_weight_from_codes(qg, sg, qxt, sxt, k, v, row_block=(r0, 64),
+                                      col_block=(c0, k), fmt=f)
+        got = O.decode(T.bits_of(res["dw"][r0:r0 + 64, c0:c0 + k].contiguous()), out_dt)
+        assert_out(got, ref, out_dt, "dW block (%d, %d)" % (r0, c0))
+    for r0 in dw_rows:
+        c0 = int(rng.integers(0, C // k)) * k
         ref = O.bwd_weight_from_codes(qg, sg, qxt, sxt, k, v, row_block=(r0, 64),
                                       col_block=(c0, k), fmt=f)
         got = O.decode(T.bits_of(res["dw"][r0:r0 + 64, c0:c0 + k].contiguous()), out_dt)

@@ -118,3 +118,37 @@ def test_bmm_equals_layers_with_shared_steps():
         l1.bwd_weight(dw)
         torch.cuda.synchronize()
         assert torch.equal(y, yb[b]) and torch.equal(dx, dxb[b]) and torch.equal(dw, dwb[b]), b
+
+
+@pytest.mark.timeout(900)
+def test_bmm_fullsize_attention_sampled():
+    """The attention-score products at the size bench.py times them (128 batches = 4 sequences
+    x 32 heads, 1024 tokens, head width 128, k = 128, HALO-2): the stacked codes and the shared
+    scales in full, the products of three batches (first, middle, last) against the oracle's
+    exact values on its own codes."""
+    cfg = WL.attention_config()
+    nb, N, C, D, k, v = cfg["batch"], cfg["N"], cfg["C"], cfg["D"], cfg["k"], cfg["variant"]
+    print("[case] bmm fullsize", cfg["name"], flush=True)
+    inputs = WL.make_batched_inputs(cfg)
+    L, outs = run_bmm(cfg, inputs, cfg["out_dtype"])
+    dt, out_dt = cfg["in_dtype"], cfg["out_dtype"]
+    qx, sx, qxt, sxt = O.quantize_x(O.decode(inputs["x"], dt).reshape(nb * N, C), k, cfg["bits"], v)
+    qw, sw = O.quantize_w(O.decode(inputs["w"], dt).reshape(nb * D, C), k, cfg["bits"], v)
+    qg, sg = O.quantize_g(O.decode(inputs["dy"], dt).reshape(nb * N, D), k, cfg["bits"], v)
+    assert_codes(L.qx.codes_view().cpu().numpy(), qx, "qX")
+    assert_scale(float(L.qx.scale.cpu()[0]), sx, "sX")
+    assert_codes(L.qw.codes_view().cpu().numpy(), qw, "qW")
+    assert_scale(float(L.qw.scale.cpu()[0]), sw, "sW")
+    assert_codes(L.qg.codes_view().cpu().numpy(), qg, "qG")
+    assert_scale(float(L.qg.scale.cpu()[0]), sg, "sG")
+    assert_codes(L.qxt.codes_t_view().cpu().numpy().T, qxt, "qXt")
+    assert_scale(float(L.qxt.scale.cpu()[0]), sxt, "sXt")
+    print("[step] codes compared", flush=True)
+    for b in (0, nb // 2 - 7, nb - 1):
+        xs, ws = slice(b * N, (b + 1) * N), slice(b * D, (b + 1) * D)
+        refs = {"y": O.fwd_from_codes(qx[xs], sx, qw[ws], sw, k, v),
+                "dx": O.bwd_input_from_codes(qg[xs], sg, qw[ws], sw, k, v),
+                "dw": O.bwd_weight_from_codes(qg[xs], sg, qxt[xs], sxt, k, v)}
+        for name, ref in refs.items():
+            got = O.decode(T.bits_of(outs[name][b].contiguous()), out_dt)
+            assert_out(got, ref, out_dt, "%s batch %d" % (name, b))

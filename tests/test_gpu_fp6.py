@@ -110,10 +110,14 @@ def test_fp6_midpoints_round_to_even(name):
 
 
 @pytest.mark.timeout(900)
+@pytest.mark.parametrize("cid", [2, 5])
 @pytest.mark.parametrize("name", ["e2m3", "e3m2"])
-def test_fp6_fullsize_2048x4096x4096_sampled(name):
-    """The FP6 HALO-2 step at 2048 x 4096 x 4096 (k = 256): codes and scales in full, outputs on
-    sampled rows / k-aligned blocks against the oracle's exact values."""
-    cfg = WL.config(2, fmt=FMTS[name])
+def test_fp6_fullsize_sampled(name, cid):
+    """The FP6 HALO-2 step at full size, 2048 x 4096 x 4096 (k = 256) and 8192 x 13824 x 5120
+    (k = 128, the size bench.py times it at): codes and scales in full, outputs on sampled
+    rows / k-aligned blocks against the oracle's exact values (at the larger size also dW
+    blocks on both sides of the head / tail launch seam at row 4608, and at the end)."""
+    cfg = WL.config(cid, fmt=FMTS[name])
     banner("fp6-fullsize", cfg["name"])
-    fullsize_sampled(cfg, 3100 + cfg["fmt"])
+    seam = (4608 - 64, 4608, 5120 - 64) if cid == 5 else ()
+    fullsize_sampled(cfg, 3100 + 10 * cid + cfg["fmt"], dw_rows=seam)

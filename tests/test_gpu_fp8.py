@@ -114,10 +114,17 @@ def test_fp8_grid_aligned_codes_exact(k):
     assert err <= 1e-3
 
 
+# dW rows on both sides of the head / tail launch seam at 8192 x 13824 x 5120 (dW computed as
+# dW^T: 256-wide tiles over dW rows [0, 4608), 128-wide ones over [4608, 5120)), and the end
+DW_SEAM = {5: (4608 - 64, 4608, 5120 - 64)}
+
+
 @pytest.mark.timeout(900)
-def test_fp8_fullsize_2048x4096x4096_sampled():
-    """The FP8 HALO-2 step at 2048 x 4096 x 4096 (k = 256): codes and scales in full,
-    outputs on sampled rows / k-aligned blocks against the oracle's exact values."""
-    cfg = WL.config(2, fmt=WL.E4M3)
+@pytest.mark.parametrize("cid", [2, 5])
+def test_fp8_fullsize_sampled(cid):
+    """The FP8 HALO-2 step at full size, 2048 x 4096 x 4096 (k = 256) and 8192 x 13824 x 5120
+    (k = 128, the size bench.py times it at): codes and scales in full, outputs on sampled
+    rows / k-aligned blocks against the oracle's exact values."""
+    cfg = WL.config(cid, fmt=WL.E4M3)
     banner("fp8-fullsize", cfg["name"])
-    fullsize_sampled(cfg, 3000)
+    fullsize_sampled(cfg, 3000 + cid, dw_rows=DW_SEAM.get(cid, ()))

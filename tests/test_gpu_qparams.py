@@ -147,12 +147,14 @@ def test_stats_many_segments(rows, dt):
     assert abs(got - ora["qerr"]) <= 1e-5 * ora["qerr"], (got, ora["qerr"])
 
 
-@pytest.mark.timeout(600)
-def test_lsq_stat_fullsize_llama7b_x():
-    """The LSQ step gradient of X at the Llama-7B MLP shape (4096 x 4096 bf16, heavy-tailed,
-    k = 256) with a synthetic gradient, and sum |r| / the quantization error, against the
-    oracle over the whole tensor."""
-    cfg_w = WL.config(4)
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cid", [4, 5])
+def test_lsq_stat_fullsize_x(cid):
+    """The LSQ step gradient of X at full size with a synthetic gradient, and the quantization
+    error, against the oracle over the whole tensor: the Llama-7B MLP shape (4096 x 4096 bf16,
+    heavy-tailed, k = 256) and the size bench.py times (8192 x 13824 bf16, k = 128)."""
+    cfg_w = WL.config(cid)
+    print("[case] lsq fullsize", cfg_w["name"], flush=True)
     inputs = WL.make_inputs(cfg_w)
     rng = np.random.default_rng(44)
     N, C, k = cfg_w["N"], cfg_w["C"], cfg_w["k"]
