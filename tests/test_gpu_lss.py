@@ -237,3 +237,26 @@ def test_lss_after_gpu_forward():
     err = rel_fro(dw.cpu().numpy(), ora["dw"])
     print("[lss] after forward: kept %d, dW rel fro %.3g" % (kept, err), flush=True)
     assert err <= OUT_REL_FRO
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cid", [4, 5])
+def test_lss_fullsize_halo2_shapes(cid):
+    """LSS-MM at the larger layer shapes bench.py times it at (4096 x 4096 x 11008, k = 256, and
+    8192 x 13824 x 5120, k = 128), as an INT4 absmax HQ layer: the whole sample (kept tokens,
+    probabilities, steps) and dW on 64 sampled rows against the oracle."""
+    cfg = WL.config(cid)
+    N, C, D, k = cfg["N"], cfg["C"], cfg["D"], cfg["k"]
+    dt = cfg["in_dtype"]
+    print("[case] lss fullsize", cfg["name"], flush=True)
+    inp = WL.make_inputs(cfg)
+    G = O.decode(inp["dy"], dt)
+    X = O.decode(inp["x"], dt)
+    u = np.random.default_rng(cfg["seed"] + 70).random(N).astype(np.float32)
+    qx, sx = O.quantize_tensor(X, O.ROT_RIGHT, k, 4)
+    del X
+    rows = np.sort(np.random.default_rng(cid).choice(D, 64, replace=False))
+    ora = O.lss_weight_gradient(G, qx, sx, k, N / 2, u, dw_rows=rows)
+    got = run_lss(inp["dy"], dt, saved_codes(qx, sx, k, O.ROT_RIGHT), N, C, D, k,
+                  B.HQ_VARIANT_HQ, N / 2, u, cfg["out_dtype"])
+    check(got, ora, G, cfg["out_dtype"], cfg["name"], dw_rows=rows)
