@@ -150,9 +150,18 @@ __device__ inline void load16(const void* row, int64_t i0, int64_t n, bool vec, 
   }
 }
 
+// u * alpha, or with PZ u * alpha + 0 (one fma): the same value except that a zero product
+// is +0 whatever the signs of its factors.
+template <bool PZ>
+__device__ inline float scaled(float u, float alpha) {
+  if constexpr (PZ) return __builtin_fmaf(u, alpha, 0.0f);
+  return u * alpha;
+}
+
 // Store u[0..N) * alpha as N consecutive elements starting at element `off` of `base`;
-// only the first `nvalid` are written. Whole aligned runs use 16-byte stores.
-template <class T, int N>
+// only the first `nvalid` are written. Whole aligned runs use 16-byte stores. PZ: zero
+// products are stored as +0 (for callers whose alpha carries a sign per lane).
+template <class T, int N, bool PZ = false>
 __device__ inline void store_run(void* base, int64_t off, int64_t nvalid, const float (&u)[N],
                                  float alpha) {
   char* p = static_cast<char*>(base) + off * T::bytes;
@@ -162,18 +171,20 @@ __device__ inline void store_run(void* base, int64_t off, int64_t nvalid, const 
     for (int q = 0; q < N; q += PER16) {
       if constexpr (T::bytes == 4) {
         *reinterpret_cast<float4*>(p + 4 * q) =
-            make_float4(u[q] * alpha, u[q + 1] * alpha, u[q + 2] * alpha, u[q + 3] * alpha);
+            make_float4(scaled<PZ>(u[q], alpha), scaled<PZ>(u[q + 1], alpha),
+                        scaled<PZ>(u[q + 2], alpha), scaled<PZ>(u[q + 3], alpha));
       } else {
         uint32_t w[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) w[j] = T::pack2(u[q + 2 * j] * alpha, u[q + 2 * j + 1] * alpha);
+        for (int j = 0; j < 4; ++j)
+          w[j] = T::pack2(scaled<PZ>(u[q + 2 * j], alpha), scaled<PZ>(u[q + 2 * j + 1], alpha));
         *reinterpret_cast<uint4*>(p + 2 * q) = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
   } else {
 #pragma unroll
     for (int q = 0; q < N; ++q)
-      if (q < nvalid) T::store(base, off + q, u[q] * alpha);
+      if (q < nvalid) T::store(base, off + q, scaled<PZ>(u[q], alpha));
   }
 }
 
@@ -427,6 +438,74 @@ __device__ inline int quant_byte(float v, float r, int qp, bool f8, float grid, 
 __device__ inline uint32_t pack4(int a, int b, int c, int d) {
   return (static_cast<uint32_t>(a) & 0xFFu) | ((static_cast<uint32_t>(b) & 0xFFu) << 8) |
          ((static_cast<uint32_t>(c) & 0xFFu) << 16) | ((static_cast<uint32_t>(d) & 0xFFu) << 24);
+}
+
+// v += sgn * v[lane ^ M] in one DPP instruction per value (quad permute, M = 1 or 2). With
+// sgn = +1 on the lower lane of each pair and -1 on the upper, the lower lane gets a + b and
+// the upper lane b - a, the negation of its butterfly output: each cross-lane stage flips the
+// sign its upper lanes hold, and the caller folds that sign into the quantizer (a max of
+// magnitudes is unaffected). The s_nop covers the VALU-write -> DPP-read hazard of whatever
+// ran before the block.
+template <int M>
+__device__ inline void xstage8(float& v0, float& v1, float& v2, float& v3, float& v4, float& v5,
+                               float& v6, float& v7, float sgn) {
+  if constexpr (M == 1) {
+    asm("s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %0, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %2, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %3, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %4, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %5, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %6, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, %7, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+        : "+v"(v0), "+v"(v1), "+v"(v2), "+v"(v3), "+v"(v4), "+v"(v5), "+v"(v6), "+v"(v7)
+        : "v"(sgn));
+  } else {
+    asm("s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %0, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %1, %1, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %2, %2, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %3, %3, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %4, %4, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %5, %5, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %6, %6, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+        "v_fmac_f32_dpp %7, %7, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+        : "+v"(v0), "+v"(v1), "+v"(v2), "+v"(v3), "+v"(v4), "+v"(v5), "+v"(v6), "+v"(v7)
+        : "v"(sgn));
+  }
+}
+
+// Butterfly over lanes l and l ^ 4 (lane bit 2, inside a 16-lane row) in two DPP instructions
+// per value: the lower lane of each pair (bit 2 clear, banks 0 and 2) takes a + b through a row
+// shift left by four, the upper lane (banks 1 and 3) a - b through a row shift right by four.
+// Each instruction writes only its banks of the new register and reads the old one, so the
+// halves do not see each other's results. The s_nop covers the VALU-write -> DPP-read hazard
+// of whatever wrote the inputs.
+__device__ inline void xstage4_lane4(float (&v)[8]) {
+  float r[8];
+  asm("s_nop 1\n\t"
+      "v_add_f32_dpp %0, %8, %8 row_shl:4 row_mask:0xf bank_mask:0x5\n\t"
+      "v_sub_f32_dpp %0, %8, %8 row_shr:4 row_mask:0xf bank_mask:0xa\n\t"
+      "v_add_f32_dpp %1, %9, %9 row_shl:4 row_mask:0xf bank_mask:0x5\n\t"
+      "v_sub_f32_dpp %1, %9, %9 row_shr:4 row_mask:0xf bank_mask:0xa\n\t"
+      "v_add_f32_dpp %2, %10, %10 row_shl:4 row_mask:0xf bank_mask:0x5\n\t"
+      "v_sub_f32_dpp %2, %10, %10 row_shr:4 row_mask:0xf bank_mask:0xa\n\t"
+      "v_add_f32_dpp %3, %11, %11 row_shl:4 row_mask:0xf bank_mask:0x5\n\t"
+      "v_sub_f32_dpp %3, %11, %11 row_shr:4 row_mask:0xf bank_mask:0xa\n\t"
+      "v_add_f32_dpp %4, %12, %12 row_shl:4 row_mask:0xf bank_mask:0x5\n\t"
+      "v_sub_f32_dpp %4, %12, %12 row_shr:4 row_mask:0xf bank_mask:0xa\n\t"
+      "v_add_f32_dpp %5, %13, %13 row_shl:4 row_mask:0xf bank_mask:0x5\n\t"
+      "v_sub_f32_dpp %5, %13, %13 row_shr:4 row_mask:0xf bank_mask:0xa\n\t"
+      "v_add_f32_dpp %6, %14, %14 row_shl:4 row_mask:0xf bank_mask:0x5\n\t"
+      "v_sub_f32_dpp %6, %14, %14 row_shr:4 row_mask:0xf bank_mask:0xa\n\t"
+      "v_add_f32_dpp %7, %15, %15 row_shl:4 row_mask:0xf bank_mask:0x5\n\t"
+      "v_sub_f32_dpp %7, %15, %15 row_shr:4 row_mask:0xf bank_mask:0xa"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7])
+      : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = r[i];
 }
 
 }  // namespace hq

@@ -138,18 +138,24 @@ __device__ inline void rows_fwht_inlane(V (&v)[4][NB]) {
 // Row stride 4 <- lane bit 5: the pair lives in lanes l and l^32. One row block (the stage
 // pairs values within a block, so the row-major epilogue applies it block by block, which
 // keeps the swap results of one block, not of all four, in registers at a time).
+// Two values a, b per step: a swap of a's upper half with b's lower half leaves the lower lanes
+// holding both halves of a and the upper lanes both halves of b; each lane forms the sum and
+// the difference of its pair, and a second swap returns sums to the lower lanes and
+// differences to the upper ones, each value in its own register again (two swaps and two
+// adds for two values).
 template <int NB, class V>
 __device__ inline void rows_fwht_lanehalf_block(V (&v)[NB], int lane) {
-  const float sgn = (lane & 32) ? -1.0f : 1.0f;
 #pragma unroll
   for (int bj = 0; bj < NB; ++bj)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const unsigned x = __float_as_uint(v[bj][r]);
-      // after the swap: .x = value of the lower lane of the pair, .y = of the upper lane
-      auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    for (int r = 0; r < 16; r += 2) {
+      auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[bj][r]),
+                                                __float_as_uint(v[bj][r + 1]), false, false);
       const float lo = __uint_as_float(p[0]), hi = __uint_as_float(p[1]);
-      v[bj][r] = __builtin_fmaf(hi, sgn, lo);   // lower lane: lo+hi, upper: lo-hi
+      auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo + hi), __float_as_uint(lo - hi),
+                                                false, false);
+      v[bj][r] = __uint_as_float(q[0]);       // lower lane: a_lo + a_hi, upper: a_lo - a_hi
+      v[bj][r + 1] = __uint_as_float(q[1]);   // the same for b
     }
 }
 
@@ -539,15 +545,20 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs 
       constexpr int RP = BN + 4;           // padded row pitch (floats)
       const int x = 4 * w + (lq >> 3);
       const float* const epr = hh ? ep1 : ep0;
-      const float hsgn = hh ? -1.0f : 1.0f;
       // (store_rows: dn shifts the columns, for the pair finisher's lower / upper halves)
+      // column strides 8 and 16 leave lane l's values multiplied by csgn (lane bits 0 and 1);
+      // the sign goes into the scale of the stores, which negates them back exactly (a zero
+      // is stored as +0, as the unfolded butterflies gave it)
+      const float sg1 = (lane & 1) ? -1.0f : 1.0f, sg2 = (lane & 2) ? -1.0f : 1.0f;
+      const float csgn = (KN > 8 ? sg1 : 1.0f) * (KN > 16 ? sg2 : 1.0f);
+      const float alpha_l = alpha * csgn;
       auto store_rows = [&](int cc, const float (&u)[NJ][8], int dn) {
         const int64_t orow = m0 + 128 * hh + 32 * cc + x;
         if (orow < g.M) {
 #pragma unroll
           for (int jj = 0; jj < NJ; ++jj) {
             const int64_t cb = n0 + dn + 64 * jj + 8 * s8;
-            store_run<Out, 8>(g.c, orow * g.ldc + cb, g.N - cb, u[jj], alpha);
+            store_run<Out, 8, true>(g.c, orow * g.ldc + cb, g.N - cb, u[jj], alpha_l);
           }
         }
       };
@@ -632,29 +643,40 @@ __global__ __launch_bounds__(GemmShape<BN>::NT, 1) void gemm_i8_kernel(GemmArgs 
           }
         float* const f = &u[0][0];
         if constexpr (KM > 128) {
+          // row stride 128 = lane bit 5, two values per pair of swaps as in the row stages
 #pragma unroll
-          for (int q = 0; q < 8 * NJ; ++q) {
-            const unsigned xv = __float_as_uint(f[q]);
-            auto pr = __builtin_amdgcn_permlane32_swap(xv, xv, false, false);
-            f[q] = __builtin_fmaf(__uint_as_float(pr[1]), hsgn, __uint_as_float(pr[0]));
+          for (int q = 0; q < 8 * NJ; q += 2) {
+            auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(f[q]), __float_as_uint(f[q + 1]),
+                                                       false, false);
+            const float lo = __uint_as_float(pr[0]), hi = __uint_as_float(pr[1]);
+            auto qr = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo + hi),
+                                                       __float_as_uint(lo - hi), false, false);
+            f[q] = __uint_as_float(qr[0]);
+            f[q + 1] = __uint_as_float(qr[1]);
           }
         }
         if constexpr (KN > 1) {
 #pragma unroll
           for (int jj = 0; jj < NJ; ++jj) fwht_inreg<KN, 8>(u[jj]);
-          if constexpr (KN > 8) quad_stage<8 * NJ>(*reinterpret_cast<float(*)[8 * NJ]>(f), lane, 1);
-          if constexpr (KN > 16) quad_stage<8 * NJ>(*reinterpret_cast<float(*)[8 * NJ]>(f), lane, 2);
-          if constexpr (KN > 32) {
-            // stride 32 = lane bit 2: the partner is lane ^ 4 (row shifts by four lanes, each
-            // written to the banks whose partner it fetches)
-            const float sg = (lane & 4) ? -1.0f : 1.0f;
+          // strides 8, 16 = lane bits 0, 1: one fused DPP fma per value, the upper lanes left
+          // holding the negated butterfly output (csgn, folded into the store's scale)
+          if constexpr (KN > 8) {
 #pragma unroll
-            for (int q = 0; q < 8 * NJ; ++q) {
-              const uint32_t xv = __float_as_uint(f[q]);
-              uint32_t pv = __builtin_amdgcn_mov_dpp(xv, 0x104, 0xF, 0x5, false);   // lane + 4
-              pv = __builtin_amdgcn_update_dpp(pv, xv, 0x114, 0xF, 0xA, false);            // lane - 4
-              f[q] = __builtin_fmaf(f[q], sg, __uint_as_float(pv));
-            }
+            for (int jj = 0; jj < NJ; ++jj)
+              xstage8<1>(u[jj][0], u[jj][1], u[jj][2], u[jj][3], u[jj][4], u[jj][5], u[jj][6],
+                         u[jj][7], sg1);
+          }
+          if constexpr (KN > 16) {
+#pragma unroll
+            for (int jj = 0; jj < NJ; ++jj)
+              xstage8<2>(u[jj][0], u[jj][1], u[jj][2], u[jj][3], u[jj][4], u[jj][5], u[jj][6],
+                         u[jj][7], sg2);
+          }
+          // stride 32 = lane bit 2: the partner is lane ^ 4 (two bank-masked row shifts); the
+          // lanes of a pair carry the same csgn, so the stage needs no sign of its own
+          if constexpr (KN > 32) {
+#pragma unroll
+            for (int jj = 0; jj < NJ; ++jj) xstage4_lane4(u[jj]);
           }
 #pragma unroll
           for (int hb = 1; hb < NJ; hb <<= 1)

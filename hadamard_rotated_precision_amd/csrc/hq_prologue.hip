@@ -197,42 +197,6 @@ __global__ __launch_bounds__(RT_THREADS) void right_kernel(ProArgs a) {
 // working on the current one, so memory and ALU overlap.
 constexpr int RF_ROWS = 64, RF_COLS = 256, RF_THREADS = 256, RF_GRID = 512;
 
-// v += sgn * v[lane ^ M] in one DPP instruction per value (quad permute, M = 1 or 2). With
-// sgn = +1 on the lower lane of each pair and -1 on the upper, the lower lane gets a + b and
-// the upper lane b - a, the negation of its butterfly output: each cross-lane stage flips the
-// sign its upper lanes hold, and the caller folds that sign into the quantizer (a max of
-// magnitudes is unaffected). The s_nop covers the VALU-write -> DPP-read hazard of whatever
-// ran before the block.
-template <int M>
-__device__ inline void xstage8(float& v0, float& v1, float& v2, float& v3, float& v4, float& v5,
-                               float& v6, float& v7, float sgn) {
-  if constexpr (M == 1) {
-    asm("s_nop 1\n\t"
-        "v_fmac_f32_dpp %0, %0, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %1, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %2, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %3, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %4, %4, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %5, %5, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %6, %6, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %7, %7, %8 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
-        : "+v"(v0), "+v"(v1), "+v"(v2), "+v"(v3), "+v"(v4), "+v"(v5), "+v"(v6), "+v"(v7)
-        : "v"(sgn));
-  } else {
-    asm("s_nop 1\n\t"
-        "v_fmac_f32_dpp %0, %0, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %1, %1, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %2, %2, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %3, %3, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %4, %4, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %5, %5, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %6, %6, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
-        "v_fmac_f32_dpp %7, %7, %8 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
-        : "+v"(v0), "+v"(v1), "+v"(v2), "+v"(v3), "+v"(v4), "+v"(v5), "+v"(v6), "+v"(v7)
-        : "v"(sgn));
-  }
-}
-
 template <int M>
 __device__ inline void xstage_signed(float (&v)[64], float sgn) {
 #pragma unroll
