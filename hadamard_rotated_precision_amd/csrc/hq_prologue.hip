@@ -1744,11 +1744,15 @@ __global__ __launch_bounds__(BN_THREADS, 2) void both_narrow_kernel(ProArgs a) {
       __syncthreads();   // every wave has its column values: the lower half takes the next raw rows
       if (it + gridDim.x < items) issue_raw(it + gridDim.x);
       fwht_from<1, K, 64>(u);
-      if constexpr (K > 64) quad_stage<64>(u, lane, 1);
+      // stride 64 (k = 128): one fused DPP fma per value; the upper lane of each pair (pp = 1)
+      // keeps the negated sums, so its quantizer takes the negated reciprocal (an exact sign)
+      const float tsg = (K > 64 && pp) ? -1.0f : 1.0f;
+      if constexpr (K > 64) xstage_signed<1>(u, tsg);
       if constexpr (OP == OP_ABSMAX) {
 #pragma unroll
         for (int i = 0; i < 64; ++i) amax2 = fmaxf(amax2, fabsf(u[i]));
       } else {
+        const float r2s = r2 * tsg;
         // rows 64pp + 16q + [0, 16) of column cp -> chunk 4pp + q of the column's 128-byte run
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -1756,7 +1760,7 @@ __global__ __launch_bounds__(BN_THREADS, 2) void both_narrow_kernel(ProArgs a) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int i = 16 * q + 4 * j;
-            d[j] = quant4(u[i], u[i + 1], u[i + 2], u[i + 3], r2, lo, hi, (OP == OP_QUANT_F8));
+            d[j] = quant4(u[i], u[i + 1], u[i + 2], u[i + 3], r2s, lo, hi, (OP == OP_QUANT_F8));
           }
           ctile[8 * cp + ((4 * pp + q) ^ ((cp >> 1) & 3))] = make_uint4(d[0], d[1], d[2], d[3]);
         }
