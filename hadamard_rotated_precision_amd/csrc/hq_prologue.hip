@@ -1544,8 +1544,11 @@ __device__ inline void both_mma_body(const ProArgs& a) {
         if (it + gridDim.x < items) issue_raw(it + gridDim.x);
       }
       fwht_from<1, K, 64>(u);
-      if constexpr (K > 64) quad_stage_tok<1, 64>(u, lane);
-      if constexpr (K > 128) quad_stage_tok<2, 64>(u, lane);
+      // strides 64 and 128 across the quad: fused DPP fmas, the upper lanes keeping negated
+      // sums; the sign a lane collects goes into its reciprocal scale (exact)
+      if constexpr (K > 64) xstage_signed<1>(u, (pp & 1) ? -1.0f : 1.0f);
+      if constexpr (K > 128) xstage_signed<2>(u, (pp & 2) ? -1.0f : 1.0f);
+      const float tsg = ((K > 64 && (pp & 1)) ? -1.0f : 1.0f) * ((K > 128 && (pp & 2)) ? -1.0f : 1.0f);
       const int64_t gcol = col0 + BT_HALF * h + cp;
       if constexpr (OP == OP_ABSMAX) {
 #pragma unroll
@@ -1563,8 +1566,8 @@ __device__ inline void both_mma_body(const ProArgs& a) {
           for (int j = 0; j < 4; ++j) {
             const int i = 16 * q + 4 * j;
             xq[q][j] = quant4(static_cast<float>(u[i]), static_cast<float>(u[i + 1]),
-                              static_cast<float>(u[i + 2]), static_cast<float>(u[i + 3]), r2, lo,
-                              hi, (OP == OP_QUANT_F8));
+                              static_cast<float>(u[i + 2]), static_cast<float>(u[i + 3]),
+                              r2 * tsg, lo, hi, (OP == OP_QUANT_F8));
           }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -1889,8 +1892,9 @@ struct BothItem {
       u[4 * i + 3] = f.w;
     }
     fwht_from<1, K, 64>(u);
-    if constexpr (K > 64) quad_stage_tok<1, 64>(u, lane);
-    if constexpr (K > 128) quad_stage_tok<2, 64>(u, lane);
+    // fused DPP fmas, the upper lanes keeping negated sums (emit() folds the sign into r2)
+    if constexpr (K > 64) xstage_signed<1>(u, (pp & 1) ? -1.0f : 1.0f);
+    if constexpr (K > 128) xstage_signed<2>(u, (pp & 2) ? -1.0f : 1.0f);
 #pragma unroll
     for (int i = 0; i < 64; ++i) {
       v2[i] = static_cast<float>(u[i]);
@@ -1923,9 +1927,10 @@ struct BothItem {
       }
     }
     uint32_t tc[16];
+    const float r2s = r2 * ((K > 64 && (pp & 1)) ? -1.0f : 1.0f) * ((K > 128 && (pp & 2)) ? -1.0f : 1.0f);
 #pragma unroll
     for (int j = 0; j < 16; ++j)
-      tc[j] = quant4(v2[4 * j], v2[4 * j + 1], v2[4 * j + 2], v2[4 * j + 3], r2, lo, hi, F8);
+      tc[j] = quant4(v2[4 * j], v2[4 * j + 1], v2[4 * j + 2], v2[4 * j + 3], r2s, lo, hi, F8);
     __syncthreads();   // every thread has read its values out of the half tile
     uint32_t* const rt = reinterpret_cast<uint32_t*>(half);   // [256 rows][32 dwords]
     uint32_t* const ct = rt + 256 * 32;                       // [128 columns][64 dwords]
