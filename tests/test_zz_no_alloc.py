@@ -46,6 +46,9 @@ def _fwd_both_ways(cfg):
 
 
 def test_noalloc_forward_matches_workspace_forward_twice():
+    # HALO-2, k = 128 with more 128 x 128 X items than workgroups (512 workgroups: the
+    # two-sided partials fill the 1024 floats of a partials array)
+    _fwd_both_ways(WL.config(5, N=2048, C=4352, D=256))
     # HALO-2, k = 256 (single-pass X over the grid barrier words in the scratch), then a
     # smaller layer whose X pass takes the two-launch path (absmax partials only)
     _fwd_both_ways(WL.config(2, N=512, C=1024, D=768))
