@@ -38,6 +38,15 @@
  *     workspaces and outputs.
  *   - Numerics: inputs must be finite. H is the unnormalized Sylvester matrix in natural
  *     order, h(i,j) = (-1)^popcount(i&j); its 1/k factors go into the dequantization scalar.
+ *   - Environment switches, read on every call, for measuring one implementation against
+ *     another (the results agree bit for bit unless noted): HQ_PROLOGUE_VALU=1 runs the
+ *     rotate-quantize passes on the VALU butterfly kernels instead of the matrix cores (same
+ *     bounds, another summation order); HQ_BOTH_NARROW=0 runs the two-sided X pass on 256-row
+ *     half tiles at k <= 128; HQ_QUANT_REVERSE=0 keeps the forward tile order in the quantize
+ *     passes of inputs of 128 MiB or more; HQ_COLS_REG=0 runs hq_fwht's LEFT butterflies at
+ *     k = 16 on the LDS-staged kernel (another summation order). HQ_SINGLE_SPIN and
+ *     HQ_PAIR_SPIN bound the polls of the single-pass grid barrier and of the tile-pair
+ *     exchange (0 forces their fallback paths).
  *     Rotations are computed in fp32 (the two-sided transform, rot BOTH, as fp32
  *     butterflies along the token axis over the fp32 values of V B). Quantization: s = absmax/Qp (fp32) or the given step,
  *     code = clamp(RNE(v * fp32(1/s)), -Qp, Qp), Qp = 127 (bits 8) or 7 (bits 4), or for E4M3
