@@ -158,10 +158,20 @@ __device__ inline float scaled(float u, float alpha) {
   return u * alpha;
 }
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// One 16-byte store, with the non-temporal (streaming) hint when NT.
+template <bool NT>
+__device__ inline void store16(char* p, u32x4 v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+  else *reinterpret_cast<u32x4*>(p) = v;
+}
+
 // Store u[0..N) * alpha as N consecutive elements starting at element `off` of `base`;
 // only the first `nvalid` are written. Whole aligned runs use 16-byte stores. PZ: zero
-// products are stored as +0 (for callers whose alpha carries a sign per lane).
-template <class T, int N, bool PZ = false>
+// products are stored as +0 (for callers whose alpha carries a sign per lane). NT: the
+// 16-byte stores carry the non-temporal hint (outputs no later kernel of the call reads).
+template <class T, int N, bool PZ = false, bool NT = false>
 __device__ inline void store_run(void* base, int64_t off, int64_t nvalid, const float (&u)[N],
                                  float alpha) {
   char* p = static_cast<char*>(base) + off * T::bytes;
@@ -170,15 +180,16 @@ __device__ inline void store_run(void* base, int64_t off, int64_t nvalid, const 
 #pragma unroll
     for (int q = 0; q < N; q += PER16) {
       if constexpr (T::bytes == 4) {
-        *reinterpret_cast<float4*>(p + 4 * q) =
-            make_float4(scaled<PZ>(u[q], alpha), scaled<PZ>(u[q + 1], alpha),
-                        scaled<PZ>(u[q + 2], alpha), scaled<PZ>(u[q + 3], alpha));
+        store16<NT>(p + 4 * q, u32x4{__float_as_uint(scaled<PZ>(u[q], alpha)),
+                                     __float_as_uint(scaled<PZ>(u[q + 1], alpha)),
+                                     __float_as_uint(scaled<PZ>(u[q + 2], alpha)),
+                                     __float_as_uint(scaled<PZ>(u[q + 3], alpha))});
       } else {
-        uint32_t w[4];
+        u32x4 w;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           w[j] = T::pack2(scaled<PZ>(u[q + 2 * j], alpha), scaled<PZ>(u[q + 2 * j + 1], alpha));
-        *reinterpret_cast<uint4*>(p + 2 * q) = make_uint4(w[0], w[1], w[2], w[3]);
+        store16<NT>(p + 2 * q, w);
       }
     }
   } else {

@@ -44,7 +44,8 @@
  *     bounds, another summation order); HQ_BOTH_NARROW=0 runs the two-sided X pass on 256-row
  *     half tiles at k <= 128; HQ_QUANT_REVERSE=0 keeps the forward tile order in the quantize
  *     passes of inputs of 128 MiB or more; HQ_COLS_REG=0 runs hq_fwht's LEFT butterflies at
- *     k = 16 on the LDS-staged kernel (another summation order). HQ_SINGLE_SPIN and
+ *     k = 16 on the LDS-staged kernel (another summation order); HQ_GEMM_NT=0 stores the
+ *     products' outputs without the non-temporal hint. HQ_SINGLE_SPIN and
  *     HQ_PAIR_SPIN bound the polls of the single-pass grid barrier and of the tile-pair
  *     exchange (0 forces their fallback paths).
  *     Rotations are computed in fp32 (the two-sided transform, rot BOTH, as fp32

@@ -401,6 +401,21 @@ def test_layer_narrow_x_items(k, monkeypatch):
     compare_layer(cfg, h, ora, cfg["out_dtype"])
 
 
+@pytest.mark.parametrize("cid,N,C,D", [(5, 1024, 2048, 768), (2, 512, 1024, 776), (3, 1000, 1024, 1000)])
+def test_layer_output_store_hint(cid, N, C, D, monkeypatch):
+    """The products store their outputs with the non-temporal hint (default) or without it
+    (HQ_GEMM_NT=0): a cache hint only, so codes and outputs agree bit for bit (the
+    2048 x 4096 x 4096-shaped case also takes the tile-pair exchange)."""
+    cfg = WL.config(cid, N=N, C=C, D=D)
+    banner("layer-store-hint", cid, N, C, D)
+    inputs = WL.make_inputs(cfg)
+    h = host(run_gpu(cfg, inputs), cfg["out_dtype"])
+    monkeypatch.setenv("HQ_GEMM_NT", "0")
+    h0 = host(run_gpu(cfg, inputs), cfg["out_dtype"])
+    for key in h:
+        np.testing.assert_array_equal(h[key], h0[key], err_msg=key)
+
+
 @pytest.mark.parametrize("cid,N,C,D", [(5, 8192, 8192, 256), (5, 256, 8192, 8192),
                                      (5, 8192, 256, 8192)])
 def test_layer_quant_order(cid, N, C, D, monkeypatch):
