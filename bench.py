@@ -177,7 +177,7 @@ def fwht_bandwidth(reps=20, rows=8192, cols=13824, ks=(16, 32, 64, 128, 256)):
                 row[pname] = {"us": round(us, 2), "gbps": round(gbs, 1),
                               "pct_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 1)}
             # hq_fwht's HQ_FWHT_AUTO choice, as its header states it (context for the reader)
-            auto_matrix = rot == B.HQ_ROT_LEFT and k >= 128
+            auto_matrix = rot == B.HQ_ROT_LEFT and k >= 256
             row["auto"] = "matrix" if auto_matrix else "butterfly"
             res[name]["k%d" % k] = row
     return res

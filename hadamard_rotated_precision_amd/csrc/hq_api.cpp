@@ -818,10 +818,10 @@ hq_status hq_fwht_path(const void* src, int32_t src_dtype, void* dst, int32_t ds
   HQ_CHECK(device_ok());
   hipStream_t st = static_cast<hipStream_t>(stream);
   // AUTO follows the measured bf16 transforms (2048 x 4096 up to 8192 x 13824): the
-  // butterflies wherever they are within 5 % of the matrix cores (RIGHT at every k, with DPP
-  // lane exchanges 1-17 % faster; LEFT at k = 16 with the register kernel, 32 and 64), the
-  // matrix cores otherwise (LEFT at k = 128 and 256: 7-60 % faster)
-  const bool auto_left_mma = k >= 128;
+  // butterflies wherever they are within 5 % of the matrix cores (RIGHT at every k; LEFT up
+  // to k = 128, with non-temporal output stores 65-88 us against 97 us), the matrix cores
+  // otherwise (LEFT at k = 256: 97 against 113 us)
+  const bool auto_left_mma = k >= 256;
   const bool auto_right_mma = false;
   const bool use_left_mma =
       left_mma && (path == HQ_FWHT_MATRIX || (path == HQ_FWHT_AUTO && auto_left_mma));

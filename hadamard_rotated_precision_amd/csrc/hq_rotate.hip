@@ -33,6 +33,7 @@ struct RowArgs {
   int64_t rows, cols;   // src is rows x cols, row pitch = cols elements
   bool vec;             // 16-byte loads are legal for every full 16-element chunk
   void* dst;            // rows x cols output (pitch cols)
+  int nt;               // output stores carry the non-temporal hint
 };
 
 template <class In, class Out, int KR>
@@ -62,7 +63,8 @@ __global__ __launch_bounds__(kThreads) void rows_kernel(RowArgs a) {
 
     if (!live || c0 >= a.cols) continue;
     // 16-byte stores when the run is whole and aligned, element stores otherwise
-    store_run<Out, 16>(a.dst, row * a.cols + c0, a.cols - c0, v, 1.0f);
+    if (a.nt) store_run<Out, 16, false, true>(a.dst, row * a.cols + c0, a.cols - c0, v, 1.0f);
+    else store_run<Out, 16>(a.dst, row * a.cols + c0, a.cols - c0, v, 1.0f);
   }
 }
 
@@ -324,6 +326,7 @@ struct ColArgs {
   int64_t rows, cols;   // rows % KL == 0
   bool vec;             // 16-byte loads are aligned (row pitch a multiple of 16 bytes, base aligned)
   void* dst;            // rows x cols output
+  int nt;               // output stores carry the non-temporal hint
 };
 
 template <int KL> struct ColShape {
@@ -397,7 +400,10 @@ __global__ __launch_bounds__(kThreads) void cols_kernel(ColArgs a) {
       const float4 x0 = *reinterpret_cast<const float4*>(&tile[slot(row, cc)]);
       const float4 x1 = *reinterpret_cast<const float4*>(&tile[slot(row, cc + 4)]);
       const float f[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-      store_run<Out, 8>(a.dst, (r0 + row) * a.cols + col0 + cc, a.cols - (col0 + cc), f, 1.0f);
+      if (a.nt)
+        store_run<Out, 8, false, true>(a.dst, (r0 + row) * a.cols + col0 + cc, a.cols - (col0 + cc), f, 1.0f);
+      else
+        store_run<Out, 8>(a.dst, (r0 + row) * a.cols + col0 + cc, a.cols - (col0 + cc), f, 1.0f);
     }
   }
 }
@@ -412,9 +418,10 @@ __global__ __launch_bounds__(kThreads) void cols_kernel(ColArgs a) {
 // 100.2, 109.6, 135.1 against 85.1, 94.3, 103.0, 154.6 us; the matrix cores take 128 and 256),
 // so it is built for k = 16 only.
 constexpr int C16_COLS = 2048;   // columns per tile: 256 threads x 8
+constexpr int kNt = 2;           // buffer-store cache policy: non-temporal
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
-template <class In, class Out>
+template <class In, class Out, bool NT>
 __global__ __launch_bounds__(kThreads, 2) void cols16_kernel(ColArgs a) {
   if constexpr (In::bytes != 2) {
     return;
@@ -473,7 +480,8 @@ __global__ __launch_bounds__(kThreads, 2) void cols16_kernel(ColArgs a) {
           for (int i = 0; i < R; ++i) {
             const float4 f = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, f), rd,
-                                                   static_cast<int>((c0 + 4 * hf) * 4), i * 2 * pitch, 0);
+                                                   static_cast<int>((c0 + 4 * hf) * 4), i * 2 * pitch,
+                                                   NT ? kNt : 0);
           }
         }
         __builtin_amdgcn_sched_barrier(0);   // one half's values live at a time
@@ -483,7 +491,7 @@ __global__ __launch_bounds__(kThreads, 2) void cols16_kernel(ColArgs a) {
             static_cast<uint16_t*>(a.dst) + rb * a.cols, 0, static_cast<int>(R * a.cols * 2), kBufferFlags);
 #pragma unroll
         for (int i = 0; i < R; ++i)
-          __builtin_amdgcn_raw_buffer_store_b128(x[i], rd, static_cast<int>(c0 * 2), i * pitch, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(x[i], rd, static_cast<int>(c0 * 2), i * pitch, NT ? kNt : 0);
       }
     }
   }
@@ -544,15 +552,20 @@ static hipError_t rows_out(int out_dt, int k, const RowArgs& a, int grid, hipStr
   return hipErrorInvalidValue;
 }
 
-template <class In>
-static hipError_t cols16_out(int out_dt, const ColArgs& a, int grid, hipStream_t st) {
+template <class In, bool NT>
+static hipError_t cols16_out_nt(int out_dt, const ColArgs& a, int grid, hipStream_t st) {
   switch (out_dt) {
-    case DT_F32: hipLaunchKernelGGL((cols16_kernel<In, F32>), dim3(grid), dim3(kThreads), 0, st, a); break;
-    case DT_F16: hipLaunchKernelGGL((cols16_kernel<In, F16>), dim3(grid), dim3(kThreads), 0, st, a); break;
-    case DT_BF16: hipLaunchKernelGGL((cols16_kernel<In, BF16>), dim3(grid), dim3(kThreads), 0, st, a); break;
+    case DT_F32: hipLaunchKernelGGL((cols16_kernel<In, F32, NT>), dim3(grid), dim3(kThreads), 0, st, a); break;
+    case DT_F16: hipLaunchKernelGGL((cols16_kernel<In, F16, NT>), dim3(grid), dim3(kThreads), 0, st, a); break;
+    case DT_BF16: hipLaunchKernelGGL((cols16_kernel<In, BF16, NT>), dim3(grid), dim3(kThreads), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <class In>
+static hipError_t cols16_out(int out_dt, const ColArgs& a, int grid, hipStream_t st) {
+  return a.nt ? cols16_out_nt<In, true>(out_dt, a, grid, st) : cols16_out_nt<In, false>(out_dt, a, grid, st);
 }
 
 template <class In>
@@ -569,6 +582,13 @@ static int dt_bytes(int dt) { return dt == DT_F32 ? 4 : 2; }
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// hq_fwht writes its output once and reads nothing back: the stores carry the non-temporal
+// hint unless HQ_FWHT_NT=0.
+static int fwht_nt() {
+  const char* e = std::getenv("HQ_FWHT_NT");
+  return (e && e[0] == '0') ? 0 : 1;
+}
+
 hipError_t rows_pass(const RowPass& p, hipStream_t st) {
   RowArgs a{};
   a.src = p.src;
@@ -576,6 +596,9 @@ hipError_t rows_pass(const RowPass& p, hipStream_t st) {
   a.cols = p.cols;
   a.vec = aligned16(p.src) && (p.cols * dt_bytes(p.in_dt)) % 16 == 0;
   a.dst = p.dst;
+  // measured at 8192 x 13824 bf16: non-temporal stores take k >= 32 from 81-84 to 73-80 us,
+  // but k = 16 (and the unrotated copy) from 82 to 94 us
+  a.nt = p.k >= 32 ? fwht_nt() : 0;
   const int64_t lanes = p.rows * ((p.cols + 255) / 256) * 16;   // one 16-lane group per segment
   const int grid = grid_for(lanes, kThreads, 1 << 20);
   const int tok = prof_begin(K_ROT_STORE, static_cast<double>(p.rows) * p.cols *
@@ -604,6 +627,7 @@ hipError_t cols_pass(const ColPass& p, hipStream_t st) {
   a.cols = p.cols;
   a.vec = aligned16(p.src) && (p.cols * dt_bytes(p.in_dt)) % 16 == 0;
   a.dst = p.dst;
+  a.nt = fwht_nt();
   if ((p.in_dt == DT_F16 || p.in_dt == DT_BF16) && p.k == 16 && p.cols % 8 == 0 &&
       aligned16(p.src) && aligned16(p.dst) && 16 * p.cols * dt_bytes(p.out_dt) < (int64_t(1) << 31) &&
       cols_reg_on()) {

@@ -44,10 +44,10 @@
  *     bounds, another summation order); HQ_BOTH_NARROW=0 runs the two-sided X pass on 256-row
  *     half tiles at k <= 128; HQ_QUANT_REVERSE=0 keeps the forward tile order in the quantize
  *     passes of inputs of 128 MiB or more; HQ_COLS_REG=0 runs hq_fwht's LEFT butterflies at
- *     k = 16 on the LDS-staged kernel (another summation order); HQ_GEMM_NT=0 stores the
- *     products' outputs without the non-temporal hint. HQ_SINGLE_SPIN and
- *     HQ_PAIR_SPIN bound the polls of the single-pass grid barrier and of the tile-pair
- *     exchange (0 forces their fallback paths).
+ *     k = 16 on the LDS-staged kernel (another summation order); HQ_GEMM_NT=0 and
+ *     HQ_FWHT_NT=0 store the products' and hq_fwht's outputs without the non-temporal
+ *     hint. HQ_SINGLE_SPIN and HQ_PAIR_SPIN bound the polls of the single-pass grid barrier
+ *     and of the tile-pair exchange (0 forces their fallback paths).
  *     Rotations are computed in fp32 (the two-sided transform, rot BOTH, as fp32
  *     butterflies along the token axis over the fp32 values of V B). Quantization: s = absmax/Qp (fp32) or the given step,
  *     code = clamp(RNE(v * fp32(1/s)), -Qp, Qp), Qp = 127 (bits 8) or 7 (bits 4), or for E4M3
@@ -356,16 +356,15 @@ hq_status hq_lss_bwd_weight(const void *dy, int32_t dy_dtype, const hq_qtensor *
  * summation error of that. The implementation is hq_fwht_path's HQ_FWHT_AUTO choice: with
  * 16-bit src_dtype == dst_dtype, 16-byte aligned pointers and whole tiles (RIGHT: rows % 64
  * == 0, cols % 256 == 0; LEFT: rows % 256 == 0, cols % 64 == 0) the sums run on the matrix
- * cores for LEFT at k = 128 and 256, in another order than the VALU butterflies of the other
- * cases. */
+ * cores for LEFT at k = 256, in another order than the VALU butterflies of the other cases. */
 hq_status hq_fwht(const void *src, int32_t src_dtype, void *dst, int32_t dst_dtype,
                   int64_t rows, int64_t cols, int32_t rot, int32_t k, void *stream);
 
 /* hq_fwht with the implementation named (for measuring one against the other; the results
  * agree to the fp32 summation order). path:
  *   HQ_FWHT_AUTO       what hq_fwht picks: the matrix cores where they cover the call and
- *                      were measured more than 5 % faster (LEFT at k = 128 and 256), the
- *                      VALU butterflies otherwise;
+ *                      were measured more than 5 % faster (LEFT at k = 256), the VALU
+ *                      butterflies otherwise;
  *   HQ_FWHT_BUTTERFLY  the VALU butterflies (log2 k add/sub stages per element), any shape;
  *   HQ_FWHT_MATRIX     the matrix cores (a dense +-1 contraction in 16-bit MFMA, exact
  *                      products, fp32 sums); HQ_ERR_MODE unless the call has 16-bit
