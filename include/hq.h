@@ -45,8 +45,8 @@
  *     half tiles at k <= 128; HQ_QUANT_REVERSE=0 keeps the forward tile order in the quantize
  *     passes of inputs of 128 MiB or more; HQ_COLS_REG=0 runs hq_fwht's LEFT butterflies at
  *     k = 16 on the LDS-staged kernel (another summation order); HQ_GEMM_NT=0 and
- *     HQ_FWHT_NT=0 store the products' and hq_fwht's outputs without the non-temporal
- *     hint. HQ_SINGLE_SPIN and HQ_PAIR_SPIN bound the polls of the single-pass grid barrier
+ *     HQ_FWHT_NT=0 store the products' and hq_fwht's VALU-kernel outputs without the
+ *     non-temporal hint. HQ_SINGLE_SPIN and HQ_PAIR_SPIN bound the polls of the single-pass grid barrier
  *     and of the tile-pair exchange (0 forces their fallback paths).
  *     Rotations are computed in fp32 (the two-sided transform, rot BOTH, as fp32
  *     butterflies along the token axis over the fp32 values of V B). Quantization: s = absmax/Qp (fp32) or the given step,
